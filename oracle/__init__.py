@@ -1,0 +1,332 @@
+"""Plain CPU oracle of the CLHA calibration path.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+execute this package: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code with the GPU
+library (``gptq_calibration_moe_amd``); the two meet only in the seeded input
+generator ``gen``, which holds none of the method's arithmetic.
+
+Sources.  "CLHA - Cross-Layer Hessian Aggregation for quantizing
+weight-shared MoE transformers" (gist.science summary, Dutch page, with the
+Chinese page as a second witness):
+  * section 2.1 - objective L(W_q) = sum_i alpha_i tr[(W_q-W) H_i (W_q-W)^T],
+    H_i the activation covariance of layer i, alpha_i the routing frequency;
+    Proposition 1: minimising L is GPTQ with H_comb = sum_i alpha_i H_i;
+    PLIC uses the primary layer's H alone.
+  * section 2.2 - collection of per-layer Hessians and token counts for every
+    active expert; aggregation per shared pair with alpha = n_a/(n_a+n_b)
+    ("rt") or alpha = 0.5 ("eq"); quantization by standard GPTQ
+    column-sequential updates on H_comb.
+  * section 2.3 - CLHA-MP: always-active shared experts see all N tokens and
+    get b+1 bits.
+  * section 2.4 - accumulators keyed by layer, not by the shared module.
+The pages leave everything inside "standard GPTQ" open.  Those steps follow
+the published GPTQ algorithm (Frantar et al., ICLR 2023): relative damping,
+the upper Cholesky factor of the inverse Hessian, column-sequential
+quantize-and-propagate with lazy block updates, min-max asymmetric groups.
+
+Precision.  Everything is float64, except the quantizer's integer decisions
+(scale, zero point, code), which are taken in float32 -- the precision the GPU
+kernels take them in -- so a code is decided identically from the same
+weight value on both sides.
+
+Readings of silent points (each is a stated choice, not a page fact):
+  * H_l = S_l / n_l with S_l the raw Gram sum sum_t x_t x_t^T (uncentred,
+    per token); rt aggregation = (S_a + S_b)/(n_a + n_b).
+  * top-K order: larger logit first, ties to the lower expert index.
+  * shared experts: one Hessian slot per layer over all N tokens.
+  * dead columns (H_ii == 0): H_ii := 1 and W[:, i] := 0.
+  * damping: lambda = damp * mean(diag H) after the dead fix.
+  * group statistics computed at each group's first column from the updated
+    weights; natural column order; the group size divides the block size.
+  * quantizer grid: range widened to contain 0, an all-zero group uses
+    (-1, 1); s = (max - min)/maxq, z = rint(-min/s); rint ties to even.
+  * an empty layer (n = 0) drops out of the combination; if every layer is
+    empty the combined Hessian is the identity.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "bf16_to_f64", "route", "bucket", "gram", "layer_hessians", "aggregate",
+    "inverse_cholesky_upper", "quant_params", "quantize", "gptq", "dequantize",
+    "loss", "calibrate_pair",
+]
+
+
+# --------------------------------------------------------------------------- inputs
+
+def bf16_to_f64(bits) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> float64 values (exact widening)."""
+    b = np.asarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+# --------------------------------------------------------------------------- collection
+
+def route(logits, k: int) -> np.ndarray:
+    """Top-K experts per token (CLHA section 2.2, "active experts"; section 2.3,
+    routed experts see a K/E fraction of tokens).
+
+    For each token the experts are ordered by (logit descending, index
+    ascending) and the first K are kept.  Returns [N, K] int32.
+    """
+    lg = np.asarray(logits, dtype=np.float32)
+    n, e = lg.shape
+    if not 1 <= k <= e:
+        raise ValueError("need 1 <= K <= E")
+    if not np.all(np.isfinite(lg)):
+        raise ValueError("non-finite router logit")
+    key_idx = np.broadcast_to(np.arange(e), (n, e))
+    order = np.lexsort((key_idx, -lg.astype(np.float64)), axis=-1)
+    return order[:, :k].astype(np.int32)
+
+
+def bucket(topk, n_experts: int):
+    """Token lists per expert (CLHA section 2.2, per-expert token counts).
+
+    counts[e] = number of tokens that chose e; offsets = exclusive prefix sum;
+    token_ids lists, for each expert in turn, its tokens in ascending order.
+    """
+    tk = np.asarray(topk, dtype=np.int64)
+    n, k = tk.shape
+    flat = tk.ravel()
+    tok = np.repeat(np.arange(n, dtype=np.int64), k)
+    order = np.lexsort((tok, flat))
+    counts = np.bincount(flat, minlength=n_experts).astype(np.int64)
+    offsets = np.zeros(n_experts + 1, np.int64)
+    offsets[1:] = np.cumsum(counts)
+    return counts, offsets, tok[order].astype(np.int32)
+
+
+def gram(x) -> np.ndarray:
+    """S = X^T X in float64 (raw activation Gram sum of one expert's tokens)."""
+    x64 = np.asarray(x, dtype=np.float64)
+    return x64.T @ x64
+
+
+def layer_hessians(x_bits, topk, n_routed: int, n_shared: int, slots=None):
+    """Per-layer Gram sums and token counts (CLHA section 2.2, collection).
+
+    Slots 0..E-1 are the routed experts (their routed tokens); slot E, present
+    when n_shared > 0, is the shared-expert input over all N tokens (section
+    2.3: shared experts receive every token).  Returns ({slot: S}, counts).
+    """
+    x = bf16_to_f64(x_bits)
+    n = x.shape[0]
+    counts, offsets, ids = bucket(topk, n_routed)
+    n_slots = n_routed + (1 if n_shared > 0 else 0)
+    all_counts = np.zeros(n_slots, np.int64)
+    all_counts[:n_routed] = counts
+    if n_shared > 0:
+        all_counts[n_routed] = n
+    if slots is None:
+        slots = range(n_slots)
+    out = {}
+    for s in slots:
+        if s < n_routed:
+            out[s] = gram(x[ids[offsets[s]:offsets[s + 1]]])
+        else:
+            out[s] = gram(x)
+    return out, all_counts
+
+
+def aggregate(S_list, n_list, mode: str, alpha=None):
+    """Combined Hessian of one shared weight (CLHA section 2.1 Proposition 1;
+    section 2.2 aggregation).
+
+    mode 'rt':       H = sum_i S_i / sum_i n_i, i.e. alpha_i = n_i / sum n.
+    mode 'eq':       H = sum_i (1/m) S_i/n_i over the m non-empty layers.
+    mode 'explicit': H = sum_i alpha_i S_i/n_i (alpha renormalised over the
+                     non-empty layers if some weighted layer is empty).
+    A single layer (PLIC) is any mode with one entry: H = S/n.
+    Returns (H, alpha_used).  All layers empty -> (I, zeros).
+    """
+    n = np.asarray(n_list, dtype=np.int64)
+    d = S_list[0].shape[0]
+    m = len(S_list)
+    if n.sum() == 0:
+        return np.eye(d), np.zeros(m)
+    if mode == "rt":
+        total = float(n.sum())
+        H = sum(np.asarray(S, np.float64) for S in S_list) / total
+        return H, n / total
+    if mode == "eq":
+        a = np.where(n > 0, 1.0, 0.0)
+        a = a / a.sum()
+    elif mode == "explicit":
+        a = np.asarray(alpha, np.float64).copy()
+        if a.shape != (m,):
+            raise ValueError("alpha needs one weight per layer")
+        lost = bool(np.any((a != 0.0) & (n == 0)))
+        a = np.where(n > 0, a, 0.0)
+        if lost:
+            if a.sum() == 0.0:
+                return np.eye(d), np.zeros(m)
+            a = a / a.sum()
+    else:
+        raise ValueError(mode)
+    H = np.zeros((d, d))
+    for ai, S, ni in zip(a, S_list, n):
+        if ni > 0 and ai != 0.0:
+            H += ai * (np.asarray(S, np.float64) / float(ni))
+    return H, a
+
+
+# --------------------------------------------------------------------------- GPTQ
+
+def inverse_cholesky_upper(H) -> np.ndarray:
+    """U upper triangular with positive diagonal and U^T U = H^-1 (GPTQ's
+    "Cholesky of H^-1"), written as its definition."""
+    Hinv = np.linalg.inv(np.asarray(H, np.float64))
+    Hinv = 0.5 * (Hinv + Hinv.T)
+    return np.linalg.cholesky(Hinv).T
+
+
+def quant_params(x, maxq: int):
+    """Per-row asymmetric min-max grid of one group, decided in float32.
+
+    x: [rows, g] weights.  Returns (scale, zero) as float32 arrays; zero holds
+    integer values in [0, maxq].
+    """
+    x32 = np.asarray(x, dtype=np.float32)
+    xmin = np.minimum(x32.min(axis=1), np.float32(0))
+    xmax = np.maximum(x32.max(axis=1), np.float32(0))
+    empty = (xmin == 0) & (xmax == 0)
+    xmin = np.where(empty, np.float32(-1), xmin).astype(np.float32)
+    xmax = np.where(empty, np.float32(1), xmax).astype(np.float32)
+    s = ((xmax - xmin) / np.float32(maxq)).astype(np.float32)
+    z = np.rint((-xmin) / s).astype(np.float32)
+    return s, z
+
+
+def quantize(w, s, z, maxq: int) -> np.ndarray:
+    """Codes of one column: clamp(rint(w/s) + z, 0, maxq), decided in float32."""
+    w32 = np.asarray(w, dtype=np.float32)
+    q = np.rint(w32 / s) + z
+    return np.clip(q, np.float32(0), np.float32(maxq)).astype(np.float32)
+
+
+def dequantize(codes, scales, zeros, group: int) -> np.ndarray:
+    """W_q = s (q - z) per group, float64."""
+    c = np.asarray(codes, np.float64)
+    s = np.repeat(np.asarray(scales, np.float64), group, axis=1)
+    z = np.repeat(np.asarray(zeros, np.float64), group, axis=1)
+    return s * (c - z)
+
+
+def gptq(w, H, bits: int, group: int, damp: float = 0.01, block: int = 128) -> dict:
+    """GPTQ on one weight matrix with Hessian H (CLHA section 2.2 step 3,
+    "standard GPTQ column-sequential updates" with H = H_comb).
+
+    w: [r, c] weights, H: [c, c] symmetric PSD (undamped).  Steps:
+      1. dead columns (H_ii == 0): H_ii := 1, W[:, i] := 0;
+      2. lambda = damp * mean(diag H); H += lambda I;
+      3. U = upper Cholesky factor of H^-1;
+      4. blocks of `block` columns; inside a block, column by column:
+         at a group's first column fit (s, z) per row on the group's current
+         weights; quantize the column; err = (w - what)/U_jj; propagate
+         err * U[j, j+1:] into the rest of the block;
+         after the block, propagate the block's errors into all later columns
+         through U[block, later].
+    Returns codes [r,c] uint8, scales [r,c/g] float32, zeros [r,c/g] uint8,
+    obs [r] (sum of err^2 per row), wq [r,c] float64, dead [c] bool, lam.
+    """
+    W = np.array(w, dtype=np.float64)
+    Hd = np.array(H, dtype=np.float64)
+    r, c = W.shape
+    if c % group or block % group:
+        raise ValueError("group must divide the column count and the block size")
+    maxq = (1 << bits) - 1
+    diag = np.diag(Hd).copy()
+    dead = diag == 0
+    Hd[dead, dead] = 1.0
+    W[:, dead] = 0.0
+    lam = damp * float(np.mean(np.diag(Hd)))
+    Hd[np.diag_indices(c)] += lam
+    U = inverse_cholesky_upper(Hd)
+
+    codes = np.zeros((r, c), np.uint8)
+    scales = np.zeros((r, c // group), np.float32)
+    zeros = np.zeros((r, c // group), np.uint8)
+    obs = np.zeros(r)
+    s = z = None
+    for i1 in range(0, c, block):
+        i2 = min(i1 + block, c)
+        W1 = W[:, i1:i2].copy()
+        E1 = np.zeros_like(W1)
+        for j in range(i1, i2):
+            jj = j - i1
+            if j % group == 0:
+                s, z = quant_params(W1[:, jj:jj + group], maxq)
+                scales[:, j // group] = s
+                zeros[:, j // group] = z.astype(np.uint8)
+            wcol = W1[:, jj]
+            q = quantize(wcol, s, z, maxq)
+            codes[:, j] = q.astype(np.uint8)
+            what = s.astype(np.float64) * (q.astype(np.float64) - z.astype(np.float64))
+            err = (wcol - what) / U[j, j]
+            obs += err * err
+            W1[:, jj + 1:] -= np.outer(err, U[j, j + 1:i2])
+            E1[:, jj] = err
+        W[:, i2:] -= E1 @ U[i1:i2, i2:]
+    wq = dequantize(codes, scales, zeros, group)
+    return {"codes": codes, "scales": scales, "zeros": zeros, "obs": obs,
+            "wq": wq, "dead": dead, "lam": lam, "U": U}
+
+
+def loss(w, wq, H) -> float:
+    """tr[(W_q - W) H (W_q - W)^T] = sum over rows of delta_r H delta_r^T
+    (CLHA section 2.1 objective for one layer term)."""
+    delta = np.asarray(wq, np.float64) - np.asarray(w, np.float64)
+    return float(np.sum((delta @ np.asarray(H, np.float64)) * delta))
+
+
+# --------------------------------------------------------------------------- whole pair
+
+def calibrate_pair(x_bits_list, logits_list, jobs: dict, *, n_routed: int, top_k: int,
+                   n_shared: int, mode: str, bits: int, shared_bits: int, group: int,
+                   damp: float = 0.01, block: int = 128, alpha=None,
+                   layer_losses: bool = False) -> dict:
+    """The three CLHA phases on one shared-weight group (section 2.2).
+
+    x_bits_list / logits_list: one entry per layer sharing the experts.
+    jobs: {expert: [r, c] float array} -- the stacked matrices of each expert
+    to quantize.  Routed expert e (< E) uses Hessian slot e; every shared
+    expert (E <= e < E + n_shared) uses slot E, the all-token Hessian, and
+    shared_bits bits (CLHA-MP, section 2.3).
+    Returns routing, counts, per-layer S, H_comb and alpha per slot, GPTQ
+    outputs and the loss under H_comb per expert (and per layer if asked).
+    """
+    def slot_of(e):
+        return e if e < n_routed else n_routed
+
+    slots = sorted({slot_of(e) for e in jobs})
+    out = {"topk": [], "counts": [], "offsets": [], "token_ids": [], "S": [], "n": []}
+    for x_bits, lg in zip(x_bits_list, logits_list):
+        tk = route(lg, top_k)
+        counts, offsets, ids = bucket(tk, n_routed)
+        S, all_counts = layer_hessians(x_bits, tk, n_routed, n_shared, slots=slots)
+        out["topk"].append(tk)
+        out["counts"].append(counts)
+        out["offsets"].append(offsets)
+        out["token_ids"].append(ids)
+        out["S"].append(S)
+        out["n"].append(all_counts)
+    out["H"], out["alpha"] = {}, {}
+    for s in slots:
+        H, a = aggregate([S[s] for S in out["S"]], [n[s] for n in out["n"]], mode, alpha)
+        out["H"][s], out["alpha"][s] = H, a
+    out["gptq"], out["loss"], out["layer_loss"] = {}, {}, {}
+    for e, w in sorted(jobs.items()):
+        s = slot_of(e)
+        b = shared_bits if e >= n_routed else bits
+        g = gptq(w, out["H"][s], b, group, damp, block)
+        out["gptq"][e] = g
+        out["loss"][e] = loss(w, g["wq"], out["H"][s])
+        if layer_losses:
+            out["layer_loss"][e] = [
+                loss(w, g["wq"], S[s] / n[s]) if n[s] > 0 else 0.0
+                for S, n in zip(out["S"], out["n"])]
+    return out
