@@ -1,0 +1,78 @@
+"""CLHA calibration of one group of layers that share their routed experts.
+
+Host-side orchestration of the three phases of the CLHA summary (section 2.2)
+through the C ABI; every arithmetic step runs in the library's kernels.
+  collect(layer, x, logits)   phase 1, per layer and batch (layer-aware, section 2.4)
+  aggregate(mode)             phase 2, H_comb per expert slot
+  quantize(weights, ...)      phase 3, GPTQ per expert on its slot's H_comb,
+                              shared experts at b+1 bits under CLHA-MP (section 2.3)
+"""
+from __future__ import annotations
+
+from typing import Optional, Sequence
+
+import torch
+
+from . import Context
+
+
+class SharedGroupCalibration:
+    """Accumulators of n_layers layers sharing one MoE block's experts."""
+
+    def __init__(self, ctx: Context, layer_ids: Sequence[int]):
+        self.ctx = ctx
+        self.layer_ids = list(layer_ids)
+        self.S, self.counts = {}, {}
+        for l in self.layer_ids:
+            S, n = ctx.new_layer_buffers()
+            ctx.register_layer(l, S, n)
+            self.S[l], self.counts[l] = S, n
+        self.H = torch.empty(ctx.slots, ctx.d, ctx.d, dtype=torch.float32, device=ctx.device)
+        self.alpha = torch.empty(ctx.slots, len(self.layer_ids), dtype=torch.float32, device=ctx.device)
+
+    def reset(self):
+        for l in self.layer_ids:
+            self.S[l].zero_()
+            self.counts[l].zero_()
+
+    def collect(self, layer: int, x: torch.Tensor, logits: torch.Tensor, **kw):
+        self.ctx.collect_hessians(layer, x, logits, **kw)
+
+    def aggregate(self, mode: str, alpha: Optional[Sequence[float]] = None,
+                  layers: Optional[Sequence[int]] = None):
+        ids = self.layer_ids if layers is None else list(layers)
+        alpha_out = self.alpha if len(ids) == len(self.layer_ids) else None
+        self.ctx.aggregate(ids, mode, self.H, alpha=alpha, alpha_out=alpha_out)
+        return self.H
+
+    def slot_of(self, expert: int) -> int:
+        return expert if expert < self.ctx.n_routed else self.ctx.n_routed
+
+    def make_outputs(self, experts: Sequence[int], rows: int, group: int):
+        d, dev = self.ctx.d, self.ctx.device
+        out = {}
+        for e in experts:
+            out[e] = {
+                "codes": torch.empty(rows, d, dtype=torch.uint8, device=dev),
+                "scales": torch.empty(rows, d // group, dtype=torch.float32, device=dev),
+                "zeros": torch.empty(rows, d // group, dtype=torch.uint8, device=dev),
+                "loss": torch.empty(1, dtype=torch.float32, device=dev),
+            }
+        return out
+
+    def quantize(self, weights: dict, bits: int, shared_bits: int, group: int, block: int = 128,
+                 damp: float = 0.01, outputs: Optional[dict] = None, H: Optional[torch.Tensor] = None):
+        """weights: {expert: W [rows, d] float32 or bfloat16}.  Routed expert e uses
+        H[e]; shared experts (e >= E) use H[E] and shared_bits."""
+        H = self.H if H is None else H
+        experts = sorted(weights)
+        rows = weights[experts[0]].shape[0]
+        if outputs is None:
+            outputs = self.make_outputs(experts, rows, group)
+        jobs = []
+        for e in experts:
+            o = outputs[e]
+            jobs.append({"H": H[self.slot_of(e)], "W": weights[e],
+                         "bits": shared_bits if e >= self.ctx.n_routed else bits, **o})
+        self.ctx.gptq_quantize(jobs, self.ctx.d, group, block, damp)
+        return outputs

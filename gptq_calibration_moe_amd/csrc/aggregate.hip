@@ -1,0 +1,130 @@
+// Aggregation phase: combined Hessian of every shared expert slot.
+//
+// CLHA summary, section 2.1 (Proposition 1): minimising the shared weight's
+// total reconstruction error over the layers that use it is GPTQ on
+// H_comb = sum_i alpha_i H_i.  Section 2.2 gives two weightings: routing
+// frequency alpha_i = n_i / sum n ("CLHA-rt") and equal alpha = 0.5 ("CLHA-eq");
+// PLIC (one primary layer) is alpha = (1, 0).
+//
+// With H_i = S_i / n_i, routing-frequency weighting is (sum_i S_i)/(sum_i n_i);
+// that form is used here.  Equal and explicit weights form sum_i a_i (S_i / n_i)
+// with separately rounded products and sums, in layer order, so that a = (1, 0)
+// returns S_a/n_a bit for bit and two identical layers return S/n bit for bit.
+//
+// Each workgroup reads one 64x64 lower-triangular tile of every layer's S and
+// writes the tile and its mirror image, so H comes out full and symmetric.
+#include "kernels.h"
+
+namespace clha {
+
+struct SlotWeights {
+  float a[kMaxLayers];
+  float inv_total;   // routing frequency: 1 / sum n (unused otherwise)
+  int identity;      // no tokens at all: H = I
+  int rt;
+};
+
+__device__ SlotWeights slot_weights(const AggArgs& g, int slot) {
+  SlotWeights w;
+  int64_t n[kMaxLayers];
+  int64_t total = 0;
+  int nonempty = 0;
+  for (int l = 0; l < g.n_layers; ++l) {
+    n[l] = g.counts[l][slot];
+    total += n[l];
+    nonempty += n[l] > 0;
+  }
+  w.identity = total == 0;
+  w.rt = g.mode == 0;
+  w.inv_total = 0.0f;
+  for (int l = 0; l < kMaxLayers; ++l) w.a[l] = 0.0f;
+  if (w.identity) return w;
+  if (g.mode == 0) {
+    for (int l = 0; l < g.n_layers; ++l) w.a[l] = (float)n[l] / (float)total;
+  } else if (g.mode == 1) {
+    const float a = 1.0f / (float)nonempty;
+    for (int l = 0; l < g.n_layers; ++l) w.a[l] = n[l] > 0 ? a : 0.0f;
+  } else {
+    bool lost = false;
+    float sum = 0.0f;
+    for (int l = 0; l < g.n_layers; ++l) {
+      lost |= (g.alpha[l] != 0.0f) && n[l] == 0;
+      w.a[l] = n[l] > 0 ? g.alpha[l] : 0.0f;
+      sum += w.a[l];
+    }
+    if (lost) {
+      if (sum == 0.0f) {
+        w.identity = 1;
+        for (int l = 0; l < kMaxLayers; ++l) w.a[l] = 0.0f;
+        return w;
+      }
+      for (int l = 0; l < g.n_layers; ++l) w.a[l] = w.a[l] / sum;
+    }
+  }
+  return w;
+}
+
+__global__ __launch_bounds__(256) void aggregate_kernel(AggArgs g, float* __restrict__ H,
+                                                        float* __restrict__ alpha_out) {
+  __shared__ float T[64][65];
+  const int slot = blockIdx.y;
+  const int d = g.d;
+  int t = blockIdx.x;
+  int ti = (int)((sqrtf(8.0f * (float)t + 1.0f) - 1.0f) * 0.5f);
+  while ((ti + 1) * (ti + 2) / 2 <= t) ++ti;
+  while (ti * (ti + 1) / 2 > t) --ti;
+  const int tj = t - ti * (ti + 1) / 2;
+  const bool diag = ti == tj;
+  const SlotWeights w = slot_weights(g, slot);
+  if (blockIdx.x == 0 && threadIdx.x < g.n_layers && alpha_out)
+    alpha_out[slot * g.n_layers + threadIdx.x] = w.a[threadIdx.x];
+
+  int64_t n[kMaxLayers];
+  int64_t total = 0;
+  for (int l = 0; l < g.n_layers; ++l) {
+    n[l] = g.counts[l][slot];
+    total += n[l];
+  }
+  const float ftotal = (float)total;
+  float* Hs = H + (int64_t)slot * d * d;
+  const int64_t soff = (int64_t)slot * d * d;
+  for (int idx = threadIdx.x; idx < 64 * 64; idx += 256) {
+    const int r = idx >> 6, c = idx & 63;
+    if (diag && c > r) continue;
+    const int i = ti * 64 + r, j = tj * 64 + c;
+    const int64_t e = (int64_t)i * d + j;
+    float v;
+    if (w.identity) {
+      v = (i == j) ? 1.0f : 0.0f;
+    } else if (w.rt) {
+      float sum = 0.0f;
+      for (int l = 0; l < g.n_layers; ++l) sum = __fadd_rn(sum, g.S[l][soff + e]);
+      v = __fdiv_rn(sum, ftotal);
+    } else {
+      float acc = 0.0f;
+      for (int l = 0; l < g.n_layers; ++l) {
+        if (w.a[l] != 0.0f && n[l] > 0) {
+          const float h = __fdiv_rn(g.S[l][soff + e], (float)n[l]);
+          acc = __fadd_rn(acc, __fmul_rn(w.a[l], h));
+        }
+      }
+      v = acc;
+    }
+    T[r][c] = v;
+    Hs[e] = v;
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < 64 * 64; idx += 256) {
+    const int r = idx >> 6, c = idx & 63;   // writes row tj*64 + r, column ti*64 + c
+    if (diag && c <= r) continue;
+    Hs[(int64_t)(tj * 64 + r) * d + ti * 64 + c] = T[c][r];
+  }
+}
+
+void launch_aggregate(const AggArgs& a, float* H, float* alpha_out, hipStream_t s) {
+  const int nt = a.d / 64;
+  hipLaunchKernelGGL(aggregate_kernel, dim3(nt * (nt + 1) / 2, a.slots), dim3(256), 0, s, a, H,
+                     alpha_out);
+}
+
+}  // namespace clha

@@ -1,0 +1,563 @@
+// Host side of the CLHA C ABI: argument validation, the layer registry that keeps
+// per-layer accumulators apart, workspace carving and the device status latch.
+// All compute is enqueued through the launchers in kernels.h.
+#include "clha.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+
+using clha::AggArgs;
+using clha::CollectPlan;
+using clha::GJob;
+using clha::GptqPlan;
+
+namespace clha {
+size_t gptq_smem_bytes(int block, int group);
+}
+
+struct LayerBufs {
+  float* S;
+  int64_t* counts;
+};
+
+struct clha_ctx {
+  clha_moe_desc desc;
+  int slots;
+  int device;
+  int* status_dev;
+  std::map<int32_t, LayerBufs> layers;
+  std::string err;
+  void* pinned = nullptr;        // staging for job tables (host, page-locked)
+  size_t pinned_bytes = 0;
+  hipEvent_t pinned_done = nullptr;
+  bool pinned_pending = false;
+};
+
+namespace {
+
+clha_status fail(clha_ctx* ctx, clha_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  if (ctx) ctx->err = buf;
+  return st;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+size_t up256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Sequential carve-up of one workspace allocation.
+struct Carver {
+  char* base;
+  size_t off = 0;
+  explicit Carver(void* b) : base(static_cast<char*>(b)) {}
+  template <class T>
+  T* take(size_t count) {
+    T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+    off += up256(count * sizeof(T));
+    return p;
+  }
+};
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+clha_status hip_check(clha_ctx* ctx, const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(ctx, CLHA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return CLHA_OK;
+}
+
+// Copies `bytes` of host data to `dst` on `stream` through the context's pinned
+// staging buffer; waits for the previous staged copy before reusing the buffer.
+clha_status stage_to_device(clha_ctx* ctx, void* dst, const void* src, size_t bytes,
+                            hipStream_t stream) {
+  if (ctx->pinned_pending) {
+    if (hipEventSynchronize(ctx->pinned_done) != hipSuccess)
+      return fail(ctx, CLHA_ERR_HIP, "staging wait failed");
+    ctx->pinned_pending = false;
+  }
+  if (bytes > ctx->pinned_bytes) {
+    if (ctx->pinned) hipHostFree(ctx->pinned);
+    ctx->pinned = nullptr;
+    size_t nb = bytes < 65536 ? 65536 : bytes * 2;
+    if (hipHostMalloc(&ctx->pinned, nb, hipHostMallocDefault) != hipSuccess) {
+      ctx->pinned_bytes = 0;
+      return fail(ctx, CLHA_ERR_HIP, "pinned staging allocation failed");
+    }
+    ctx->pinned_bytes = nb;
+  }
+  std::memcpy(ctx->pinned, src, bytes);
+  if (hipMemcpyAsync(dst, ctx->pinned, bytes, hipMemcpyHostToDevice, stream) != hipSuccess)
+    return fail(ctx, CLHA_ERR_HIP, "staging copy failed");
+  if (hipEventRecord(ctx->pinned_done, stream) != hipSuccess)
+    return fail(ctx, CLHA_ERR_HIP, "staging event failed");
+  ctx->pinned_pending = true;
+  return CLHA_OK;
+}
+
+bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + bn && y < x + an;
+}
+
+// ---------------------------------------------------------------- collection layout
+struct CollectLayout {
+  int32_t* topk;
+  int32_t* blockcounts;
+  int32_t* blockbase;
+  int64_t* offsets;
+  int64_t* pad_off;
+  int32_t* slot_order;
+  int32_t* token_ids;
+  uint16_t* xgT;
+  size_t bytes;
+};
+
+CollectLayout collect_layout(const clha_ctx* ctx, void* ws) {
+  const clha_moe_desc& d = ctx->desc;
+  const int64_t n = d.max_tokens;
+  const int64_t nblk = (n + clha::kBucketTokens - 1) / clha::kBucketTokens;
+  const int64_t xg_tokens = n * d.top_k + (int64_t)clha::kTokPad * d.n_routed +
+                            (d.n_shared > 0 ? n + clha::kTokPad : 0);
+  Carver c(ws);
+  CollectLayout L;
+  L.topk = c.take<int32_t>((size_t)n * d.top_k);
+  L.blockcounts = c.take<int32_t>((size_t)nblk * d.n_routed);
+  L.blockbase = c.take<int32_t>((size_t)nblk * d.n_routed);
+  L.offsets = c.take<int64_t>((size_t)d.n_routed + 1);
+  L.pad_off = c.take<int64_t>((size_t)ctx->slots + 1);
+  L.slot_order = c.take<int32_t>((size_t)ctx->slots);
+  L.token_ids = c.take<int32_t>((size_t)n * d.top_k);
+  L.xgT = c.take<uint16_t>((size_t)xg_tokens * d.d);
+  L.bytes = c.off;
+  return L;
+}
+
+// ---------------------------------------------------------------- GPTQ layout
+struct GptqLayout {
+  GJob* jobs;
+  const float** mats;
+  double* A;
+  double* X;
+  float* U;
+  double* dinv;
+  uint8_t* dead;
+  double* lamd;
+  float* wf;
+  double* partials;
+  size_t bytes;
+};
+
+GptqLayout gptq_layout(void* ws, int n_jobs, int n_mats, int cols, int64_t wf_elems,
+                       int64_t total_slabs, bool need_u, bool need_wf) {
+  Carver c(ws);
+  GptqLayout L;
+  L.jobs = c.take<GJob>((size_t)(n_jobs > 0 ? n_jobs : 1));
+  L.mats = c.take<const float*>((size_t)n_mats);
+  L.A = c.take<double>((size_t)n_mats * cols * cols);
+  L.X = c.take<double>((size_t)n_mats * cols * cols);
+  L.U = need_u ? c.take<float>((size_t)n_mats * cols * cols) : nullptr;
+  L.dinv = c.take<double>((size_t)n_mats * cols * clha::kNb);
+  L.dead = c.take<uint8_t>((size_t)n_mats * cols);
+  L.lamd = c.take<double>((size_t)n_mats);
+  L.wf = need_wf ? c.take<float>((size_t)wf_elems) : nullptr;
+  L.partials = need_wf ? c.take<double>((size_t)2 * (total_slabs > 0 ? total_slabs : 1)) : nullptr;
+  L.bytes = c.off;
+  return L;
+}
+
+struct JobScan {
+  std::vector<const float*> mats;
+  std::vector<int> mat_of;
+  int64_t wf_elems = 0;
+  int64_t total_slabs = 0;
+};
+
+JobScan scan_jobs(int n_jobs, const clha_gptq_job* jobs, int cols) {
+  JobScan s;
+  std::map<const float*, int> ids;
+  for (int i = 0; i < n_jobs; ++i) {
+    auto it = ids.find(jobs[i].H);
+    int id;
+    if (it == ids.end()) {
+      id = (int)s.mats.size();
+      ids[jobs[i].H] = id;
+      s.mats.push_back(jobs[i].H);
+    } else {
+      id = it->second;
+    }
+    s.mat_of.push_back(id);
+    s.wf_elems += (int64_t)jobs[i].rows * cols;
+    s.total_slabs += (jobs[i].rows + clha::kGptqRows - 1) / clha::kGptqRows;
+  }
+  return s;
+}
+
+}  // namespace
+
+extern "C" {
+
+CLHA_API clha_status clha_create(const clha_moe_desc* desc, clha_ctx** out) {
+  if (!desc || !out) return CLHA_ERR_INVALID_ARG;
+  *out = nullptr;
+  const clha_moe_desc& d = *desc;
+  if (d.d < 128 || d.d > 8192 || d.d % 128 != 0) return CLHA_ERR_SHAPE;
+  if (d.n_routed < 1 || d.n_routed > clha::kMaxExperts) return CLHA_ERR_SHAPE;
+  if (d.top_k < 1 || d.top_k > d.n_routed || d.top_k > clha::kMaxTopK) return CLHA_ERR_SHAPE;
+  if (d.n_shared < 0) return CLHA_ERR_SHAPE;
+  if (d.max_tokens < 1 || d.max_tokens > (int64_t)INT32_MAX / d.top_k) return CLHA_ERR_SHAPE;
+  clha_ctx* ctx = new (std::nothrow) clha_ctx();
+  if (!ctx) return CLHA_ERR_INVALID_ARG;
+  ctx->desc = d;
+  ctx->slots = d.n_routed + (d.n_shared > 0 ? 1 : 0);
+  if (hipGetDevice(&ctx->device) != hipSuccess ||
+      hipMalloc(&ctx->status_dev, 64) != hipSuccess ||
+      hipMemset(ctx->status_dev, 0, 64) != hipSuccess ||
+      hipEventCreateWithFlags(&ctx->pinned_done, hipEventDisableTiming) != hipSuccess) {
+    if (ctx->status_dev) hipFree(ctx->status_dev);
+    delete ctx;
+    return CLHA_ERR_HIP;
+  }
+  *out = ctx;
+  return CLHA_OK;
+}
+
+CLHA_API clha_status clha_destroy(clha_ctx* ctx) {
+  if (!ctx) return CLHA_OK;
+  if (ctx->pinned_pending) hipEventSynchronize(ctx->pinned_done);
+  if (ctx->pinned) hipHostFree(ctx->pinned);
+  if (ctx->pinned_done) hipEventDestroy(ctx->pinned_done);
+  if (ctx->status_dev) hipFree(ctx->status_dev);
+  delete ctx;
+  return CLHA_OK;
+}
+
+CLHA_API const char* clha_last_error(const clha_ctx* ctx) {
+  return ctx ? ctx->err.c_str() : "null context";
+}
+
+CLHA_API int32_t clha_num_slots(const clha_ctx* ctx) { return ctx ? ctx->slots : 0; }
+
+CLHA_API clha_status clha_register_layer(clha_ctx* ctx, int32_t layer, float* S, int64_t* counts) {
+  if (!ctx) return CLHA_ERR_INVALID_ARG;
+  if (!S || !counts) return fail(ctx, CLHA_ERR_INVALID_ARG, "register_layer: null buffer");
+  if (!aligned16(S) || !aligned4(counts)) return fail(ctx, CLHA_ERR_ALIGN, "register_layer: misaligned");
+  const size_t sb = (size_t)ctx->slots * ctx->desc.d * ctx->desc.d * sizeof(float);
+  const size_t cb = (size_t)ctx->slots * sizeof(int64_t);
+  for (const auto& kv : ctx->layers) {
+    if (kv.first == layer) continue;
+    const LayerBufs& o = kv.second;
+    if (overlaps(S, sb, o.S, sb) || overlaps(counts, cb, o.counts, cb) ||
+        overlaps(S, sb, o.counts, cb) || overlaps(counts, cb, o.S, sb))
+      return fail(ctx, CLHA_ERR_INVALID_ARG,
+                  "register_layer: layer %d's buffers overlap layer %d's; every layer needs "
+                  "its own Hessian accumulator", layer, kv.first);
+  }
+  if (overlaps(S, sb, counts, cb))
+    return fail(ctx, CLHA_ERR_INVALID_ARG, "register_layer: S and counts overlap");
+  ctx->layers[layer] = LayerBufs{S, counts};
+  return CLHA_OK;
+}
+
+CLHA_API size_t clha_collect_workspace_bytes(const clha_ctx* ctx) {
+  if (!ctx) return 0;
+  return collect_layout(ctx, nullptr).bytes;
+}
+
+CLHA_API clha_status clha_collect_hessians(clha_ctx* ctx, int32_t layer, int64_t n_tokens,
+                                           const uint16_t* x, const float* logits,
+                                           int32_t* topk_out, int64_t* offsets_out,
+                                           int32_t* token_ids_out, void* workspace,
+                                           size_t workspace_bytes, void* stream) {
+  if (!ctx) return CLHA_ERR_INVALID_ARG;
+  auto it = ctx->layers.find(layer);
+  if (it == ctx->layers.end())
+    return fail(ctx, CLHA_ERR_INVALID_ARG, "collect_hessians: layer %d is not registered", layer);
+  if (n_tokens < 0 || n_tokens > ctx->desc.max_tokens)
+    return fail(ctx, CLHA_ERR_SHAPE, "collect_hessians: n_tokens %lld outside 0..%lld",
+                (long long)n_tokens, (long long)ctx->desc.max_tokens);
+  if (!x || !logits || !workspace)
+    return fail(ctx, CLHA_ERR_INVALID_ARG, "collect_hessians: null x, logits or workspace");
+  if (!aligned16(x) || !aligned4(logits) || !aligned16(workspace) ||
+      (topk_out && !aligned4(topk_out)) || (offsets_out && !aligned16(offsets_out)) ||
+      (token_ids_out && !aligned4(token_ids_out)))
+    return fail(ctx, CLHA_ERR_ALIGN, "collect_hessians: misaligned pointer");
+  const CollectLayout need = collect_layout(ctx, nullptr);
+  if (workspace_bytes < need.bytes)
+    return fail(ctx, CLHA_ERR_WORKSPACE, "collect_hessians: workspace %zu < %zu bytes",
+                workspace_bytes, need.bytes);
+  if (n_tokens == 0) return CLHA_OK;
+  const CollectLayout L = collect_layout(ctx, workspace);
+  const clha_moe_desc& d = ctx->desc;
+  CollectPlan p;
+  p.n_tokens = n_tokens;
+  p.d = d.d;
+  p.E = d.n_routed;
+  p.K = d.top_k;
+  p.has_shared = d.n_shared > 0;
+  p.nblk = (int)((n_tokens + clha::kBucketTokens - 1) / clha::kBucketTokens);
+  p.topk = topk_out ? topk_out : L.topk;
+  p.blockcounts = L.blockcounts;
+  p.blockbase = L.blockbase;
+  p.offsets = offsets_out ? offsets_out : L.offsets;
+  p.pad_off = L.pad_off;
+  p.slot_order = L.slot_order;
+  p.token_ids = token_ids_out ? token_ids_out : L.token_ids;
+  p.xgT = L.xgT;
+  p.xg_tiles = (n_tokens * d.top_k + clha::kTokPad - 1) / clha::kTokPad + d.n_routed +
+               (p.has_shared ? (n_tokens + clha::kTokPad - 1) / clha::kTokPad : 0);
+  p.status = ctx->status_dev;
+  const hipStream_t s = as_stream(stream);
+  clha::launch_route(logits, p, s);
+  clha::launch_bucket(p, it->second.counts, s);
+  clha::launch_gather(x, p, s);
+  clha::launch_syrk(p, it->second.S, s);
+  return hip_check(ctx, "collect_hessians");
+}
+
+CLHA_API clha_status clha_aggregate(clha_ctx* ctx, int32_t n_layers, const int32_t* layers,
+                                    clha_alpha_mode mode, const float* alpha, float* H_out,
+                                    float* alpha_out, void* stream) {
+  if (!ctx) return CLHA_ERR_INVALID_ARG;
+  if (n_layers < 1 || n_layers > clha::kMaxLayers || !layers)
+    return fail(ctx, CLHA_ERR_SHAPE, "aggregate: n_layers must be 1..%d", clha::kMaxLayers);
+  if (mode != CLHA_ALPHA_ROUTING_FREQ && mode != CLHA_ALPHA_EQUAL && mode != CLHA_ALPHA_EXPLICIT)
+    return fail(ctx, CLHA_ERR_INVALID_ARG, "aggregate: unknown alpha mode %d", (int)mode);
+  if (!H_out) return fail(ctx, CLHA_ERR_INVALID_ARG, "aggregate: null H_out");
+  if (!aligned16(H_out) || (alpha_out && !aligned4(alpha_out)))
+    return fail(ctx, CLHA_ERR_ALIGN, "aggregate: misaligned output");
+  AggArgs a;
+  std::memset(&a, 0, sizeof a);
+  for (int i = 0; i < n_layers; ++i) {
+    auto it = ctx->layers.find(layers[i]);
+    if (it == ctx->layers.end())
+      return fail(ctx, CLHA_ERR_INVALID_ARG, "aggregate: layer %d is not registered", layers[i]);
+    for (int j = 0; j < i; ++j)
+      if (layers[j] == layers[i])
+        return fail(ctx, CLHA_ERR_INVALID_ARG, "aggregate: layer %d listed twice", layers[i]);
+    a.S[i] = it->second.S;
+    a.counts[i] = it->second.counts;
+    if (mode == CLHA_ALPHA_EXPLICIT) {
+      if (!alpha) return fail(ctx, CLHA_ERR_INVALID_ARG, "aggregate: explicit mode needs alpha");
+      if (!std::isfinite(alpha[i]) || alpha[i] < 0.0f)
+        return fail(ctx, CLHA_ERR_INVALID_ARG, "aggregate: alpha[%d] must be finite and >= 0", i);
+      a.alpha[i] = alpha[i];
+    }
+  }
+  const size_t hb = (size_t)ctx->slots * ctx->desc.d * ctx->desc.d * sizeof(float);
+  for (const auto& kv : ctx->layers)
+    if (overlaps(H_out, hb, kv.second.S, hb))
+      return fail(ctx, CLHA_ERR_INVALID_ARG, "aggregate: H_out overlaps layer %d's S", kv.first);
+  a.n_layers = n_layers;
+  a.mode = (int)mode;
+  a.d = ctx->desc.d;
+  a.slots = ctx->slots;
+  clha::launch_aggregate(a, H_out, alpha_out, as_stream(stream));
+  return hip_check(ctx, "aggregate");
+}
+
+static clha_status check_gptq_args(clha_ctx* ctx, int32_t n_jobs, const clha_gptq_job* jobs,
+                                   int32_t cols, int32_t group, int32_t block, float damp) {
+  if (n_jobs < 1 || !jobs) return fail(ctx, CLHA_ERR_INVALID_ARG, "gptq: no jobs");
+  if (block != 64 && block != 128) return fail(ctx, CLHA_ERR_SHAPE, "gptq: block must be 64 or 128");
+  if (cols < block || cols > 8192 || cols % block != 0)
+    return fail(ctx, CLHA_ERR_SHAPE, "gptq: cols %d must be a multiple of block %d, <= 8192", cols, block);
+  if (group < 4 || group % 4 != 0 || block % group != 0)
+    return fail(ctx, CLHA_ERR_SHAPE, "gptq: group %d must be a multiple of 4 dividing block %d", group, block);
+  if (!std::isfinite(damp) || damp < 0.0f) return fail(ctx, CLHA_ERR_INVALID_ARG, "gptq: bad damp");
+  for (int i = 0; i < n_jobs; ++i) {
+    const clha_gptq_job& j = jobs[i];
+    if (!j.H || !j.W || !j.codes || !j.scales || !j.zeros)
+      return fail(ctx, CLHA_ERR_INVALID_ARG, "gptq: job %d has a null pointer", i);
+    if (j.w_dtype != CLHA_F32 && j.w_dtype != CLHA_BF16)
+      return fail(ctx, CLHA_ERR_INVALID_ARG, "gptq: job %d has an unknown dtype", i);
+    if (j.rows < 1 || j.bits < 2 || j.bits > 8)
+      return fail(ctx, CLHA_ERR_SHAPE, "gptq: job %d needs rows >= 1 and bits in 2..8", i);
+    if (!aligned16(j.H) || !aligned16(j.W) || !aligned16(j.codes) || !aligned4(j.scales) ||
+        (j.loss && !aligned4(j.loss)))
+      return fail(ctx, CLHA_ERR_ALIGN, "gptq: job %d has a misaligned pointer", i);
+  }
+  return CLHA_OK;
+}
+
+CLHA_API size_t clha_gptq_workspace_bytes(const clha_ctx* ctx, int32_t n_jobs,
+                                          const clha_gptq_job* jobs, int32_t cols) {
+  if (!ctx || n_jobs < 1 || !jobs || cols < 1) return 0;
+  const JobScan js = scan_jobs(n_jobs, jobs, cols);
+  return gptq_layout(nullptr, n_jobs, (int)js.mats.size(), cols, js.wf_elems, js.total_slabs, true,
+                     true).bytes;
+}
+
+CLHA_API clha_status clha_gptq_quantize(clha_ctx* ctx, int32_t n_jobs, const clha_gptq_job* jobs,
+                                        int32_t cols, int32_t group, int32_t block, float damp,
+                                        void* workspace, size_t workspace_bytes, void* stream) {
+  if (!ctx) return CLHA_ERR_INVALID_ARG;
+  clha_status st = check_gptq_args(ctx, n_jobs, jobs, cols, group, block, damp);
+  if (st != CLHA_OK) return st;
+  if (!workspace || !aligned16(workspace))
+    return fail(ctx, CLHA_ERR_ALIGN, "gptq: workspace null or misaligned");
+  const JobScan js = scan_jobs(n_jobs, jobs, cols);
+  const int n_mats = (int)js.mats.size();
+  const GptqLayout need = gptq_layout(nullptr, n_jobs, n_mats, cols, js.wf_elems, js.total_slabs,
+                                      true, true);
+  if (workspace_bytes < need.bytes)
+    return fail(ctx, CLHA_ERR_WORKSPACE, "gptq: workspace %zu < %zu bytes", workspace_bytes, need.bytes);
+  if (js.total_slabs > INT32_MAX) return fail(ctx, CLHA_ERR_SHAPE, "gptq: too many rows");
+  const GptqLayout L = gptq_layout(workspace, n_jobs, n_mats, cols, js.wf_elems, js.total_slabs,
+                                   true, true);
+  // host tables: jobs, then the distinct Hessian pointers, staged in one copy
+  std::vector<char> host(up256(sizeof(GJob) * n_jobs) + sizeof(float*) * n_mats);
+  GJob* hj = reinterpret_cast<GJob*>(host.data());
+  int64_t wf_off = 0;
+  int slab_base = 0;
+  for (int i = 0; i < n_jobs; ++i) {
+    const clha_gptq_job& j = jobs[i];
+    GJob g;
+    g.W = j.W;
+    g.codes = j.codes;
+    g.scales = j.scales;
+    g.zeros = j.zeros;
+    g.loss = j.loss;
+    g.wf_off = wf_off;
+    g.dtype = j.w_dtype;
+    g.rows = j.rows;
+    g.bits = j.bits;
+    g.mat = js.mat_of[i];
+    g.slab_base = slab_base;
+    g.n_slabs = (j.rows + clha::kGptqRows - 1) / clha::kGptqRows;
+    hj[i] = g;
+    wf_off += (int64_t)j.rows * cols;
+    slab_base += g.n_slabs;
+  }
+  std::memcpy(host.data() + up256(sizeof(GJob) * n_jobs), js.mats.data(), sizeof(float*) * n_mats);
+  const hipStream_t s = as_stream(stream);
+  // jobs and mats are adjacent in the layout (both carved first)
+  st = stage_to_device(ctx, L.jobs, host.data(), host.size(), s);
+  if (st != CLHA_OK) return st;
+  if (reinterpret_cast<char*>(L.mats) != reinterpret_cast<char*>(L.jobs) + up256(sizeof(GJob) * n_jobs))
+    return fail(ctx, CLHA_ERR_WORKSPACE, "gptq: internal layout mismatch");
+  GptqPlan p;
+  p.n_jobs = n_jobs;
+  p.n_mats = n_mats;
+  p.cols = cols;
+  p.group = group;
+  p.block = block;
+  p.total_slabs = (int)js.total_slabs;
+  p.damp = damp;
+  p.jobs = L.jobs;
+  p.mats = L.mats;
+  p.A = L.A;
+  p.X = L.X;
+  p.U = L.U;
+  p.dinv = L.dinv;
+  p.dead = L.dead;
+  p.lamd = L.lamd;
+  p.lam = nullptr;
+  p.wf = L.wf;
+  p.partials = reinterpret_cast<float*>(L.partials);
+  p.status = ctx->status_dev;
+  clha::launch_inverse_cholesky(p, s);
+  clha::launch_gptq(p, s);
+  return hip_check(ctx, "gptq_quantize");
+}
+
+CLHA_API size_t clha_inverse_cholesky_workspace_bytes(const clha_ctx* ctx, int32_t n, int32_t cols) {
+  if (!ctx || n < 1 || cols < 1) return 0;
+  return gptq_layout(nullptr, 0, n, cols, 0, 0, false, false).bytes;
+}
+
+CLHA_API clha_status clha_inverse_cholesky(clha_ctx* ctx, int32_t n, const float* const* H,
+                                           int32_t cols, float damp, float* U_out,
+                                           float* lambda_out, uint8_t* dead_out, void* workspace,
+                                           size_t workspace_bytes, void* stream) {
+  if (!ctx) return CLHA_ERR_INVALID_ARG;
+  if (n < 1 || !H || !U_out) return fail(ctx, CLHA_ERR_INVALID_ARG, "inverse_cholesky: bad arguments");
+  if (cols < clha::kNb || cols > 8192 || cols % clha::kNb != 0)
+    return fail(ctx, CLHA_ERR_SHAPE, "inverse_cholesky: cols must be a multiple of %d, <= 8192", clha::kNb);
+  if (!std::isfinite(damp) || damp < 0.0f) return fail(ctx, CLHA_ERR_INVALID_ARG, "inverse_cholesky: bad damp");
+  for (int i = 0; i < n; ++i)
+    if (!H[i] || !aligned16(H[i])) return fail(ctx, CLHA_ERR_ALIGN, "inverse_cholesky: H[%d] null or misaligned", i);
+  if (!aligned16(U_out) || !workspace || !aligned16(workspace))
+    return fail(ctx, CLHA_ERR_ALIGN, "inverse_cholesky: misaligned output or workspace");
+  const GptqLayout need = gptq_layout(nullptr, 0, n, cols, 0, 0, false, false);
+  if (workspace_bytes < need.bytes)
+    return fail(ctx, CLHA_ERR_WORKSPACE, "inverse_cholesky: workspace %zu < %zu bytes", workspace_bytes, need.bytes);
+  const GptqLayout L = gptq_layout(workspace, 0, n, cols, 0, 0, false, false);
+  const hipStream_t s = as_stream(stream);
+  clha_status st = stage_to_device(ctx, L.mats, H, sizeof(float*) * n, s);
+  if (st != CLHA_OK) return st;
+  GptqPlan p;
+  std::memset(&p, 0, sizeof p);
+  p.n_mats = n;
+  p.cols = cols;
+  p.damp = damp;
+  p.mats = L.mats;
+  p.A = L.A;
+  p.X = L.X;
+  p.U = U_out;
+  p.dinv = L.dinv;
+  p.dead = dead_out ? dead_out : L.dead;
+  p.lamd = L.lamd;
+  p.lam = lambda_out;
+  p.status = ctx->status_dev;
+  clha::launch_inverse_cholesky(p, s);
+  return hip_check(ctx, "inverse_cholesky");
+}
+
+CLHA_API size_t clha_loss_workspace_bytes(const clha_ctx* ctx, int32_t rows, int32_t cols) {
+  if (!ctx || rows < 1 || cols < 64) return 0;
+  return up256((size_t)clha::loss_partial_count(rows, cols) * sizeof(double));
+}
+
+CLHA_API clha_status clha_loss(clha_ctx* ctx, int32_t rows, int32_t cols, int32_t group,
+                               const void* W, int32_t w_dtype, const uint8_t* codes,
+                               const float* scales, const uint8_t* zeros, const float* H,
+                               float* loss_out, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  if (!ctx) return CLHA_ERR_INVALID_ARG;
+  if (rows < 1 || cols < 64 || cols > 8192 || cols % 64 != 0 || group < 1 || cols % group != 0)
+    return fail(ctx, CLHA_ERR_SHAPE, "loss: bad shape");
+  if (!W || !codes || !scales || !zeros || !H || !loss_out || !workspace)
+    return fail(ctx, CLHA_ERR_INVALID_ARG, "loss: null pointer");
+  if (w_dtype != CLHA_F32 && w_dtype != CLHA_BF16) return fail(ctx, CLHA_ERR_INVALID_ARG, "loss: bad dtype");
+  if (!aligned16(W) || !aligned16(H) || !aligned4(scales) || !aligned4(loss_out) || !aligned16(workspace))
+    return fail(ctx, CLHA_ERR_ALIGN, "loss: misaligned pointer");
+  if (workspace_bytes < clha_loss_workspace_bytes(ctx, rows, cols))
+    return fail(ctx, CLHA_ERR_WORKSPACE, "loss: workspace too small");
+  clha::launch_loss(rows, cols, group, W, w_dtype, codes, scales, zeros, H,
+                    static_cast<float*>(workspace), loss_out, as_stream(stream));
+  return hip_check(ctx, "loss");
+}
+
+CLHA_API clha_status clha_sync(clha_ctx* ctx, void* stream) {
+  if (!ctx) return CLHA_ERR_INVALID_ARG;
+  const hipStream_t s = as_stream(stream);
+  int st = 0;
+  if (hipMemcpyAsync(&st, ctx->status_dev, sizeof(int), hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return fail(ctx, CLHA_ERR_HIP, "sync: %s", hipGetErrorString(hipGetLastError()));
+  if (ctx->pinned_pending) {
+    hipEventSynchronize(ctx->pinned_done);
+    ctx->pinned_pending = false;
+  }
+  if (st == 0) return CLHA_OK;
+  if (hipMemsetAsync(ctx->status_dev, 0, sizeof(int), s) != hipSuccess || hipStreamSynchronize(s) != hipSuccess)
+    return fail(ctx, CLHA_ERR_HIP, "sync: could not clear the status word");
+  if (st & clha::kStatusNonfinite)
+    return fail(ctx, CLHA_ERR_NONFINITE, "a router logit was NaN or infinite");
+  return fail(ctx, CLHA_ERR_NOT_PD, "a damped Hessian is not positive definite");
+}
+
+}  // extern "C"

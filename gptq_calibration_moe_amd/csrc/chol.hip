@@ -1,0 +1,339 @@
+// Inverse-Hessian factor for GPTQ: U upper triangular, positive diagonal,
+// U^T U = Hd^-1, with Hd the damped Hessian.
+//
+// GPTQ (Frantar et al., ICLR 2023, section "Cholesky reformulation") drives its
+// column-sequential updates from the rows of the upper Cholesky factor of the
+// inverse Hessian; the CLHA summary (section 2.2, step 3) runs that standard
+// GPTQ on H_comb.
+//
+// Route (no explicit inverse): with J the index reversal, factor the reversed
+// matrix J Hd J = L L^T (ordinary lower Cholesky).  Then Hd = R R^T with
+// R = J L J upper triangular, Hd^-1 = R^-T R^-1, and U = R^-1 = J L^-1 J.
+// Cost: c^3/3 flops for the factorisation and c^3/3 for the triangular inverse.
+//
+// Precision: the factorisation and the inverse run in fp64 (the fp64 matrix
+// cores, v_mfma_f64_16x16x4f64, run at half the fp32 rate on MI355X).  A
+// right-looking fp32 factorisation rounds each diagonal entry once per block
+// step while it shrinks from H_jj to its Schur complement, which costs about a
+// decimal digit on ill-conditioned Hessians; GPTQ's code decisions inherit that
+// error.  U is rounded to fp32 once, at the end.
+//
+// Every step is batched over all distinct Hessians of one call:
+//   diag_stats      dead columns (H_ii == 0) and lambda = damp * mean(diag),
+//                   taking H_ii := 1 on dead columns first
+//   build_reversed  A = J (H + fixes + lambda I) J, lower triangle, fp64
+//   per 64-column block step k:
+//     potrf_panel   factor the diagonal block (kept only as its inverse) and
+//                   solve the panel below it
+//     chol_update   trailing lower update A[i][j] -= L[i][k] L[j][k]^T
+//   per block row i:
+//     trtri_row     X[i][j] = -Linv_ii sum_m L[i][m] X[m][j] (X = L^-1, fp64),
+//                   and U at the reversed position in fp32
+#include "kernels.h"
+
+namespace clha {
+
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void tri_of(int t, int& i, int& j) {
+  int a = (int)((sqrtf(8.0f * (float)t + 1.0f) - 1.0f) * 0.5f);
+  while ((a + 1) * (a + 2) / 2 <= t) ++a;
+  while (a * (a + 1) / 2 > t) --a;
+  i = a;
+  j = t - a * (a + 1) / 2;
+}
+
+// 64x64 tile product on the fp64 matrix cores: each of the 4 waves owns a 32x32
+// quarter as 2x2 blocks of 16x16.  acc[bi][bj][r] is element
+// (wm*32 + bi*16 + 4*(lane/16) + r, wn*32 + bj*16 + lane%16) of the tile.
+// Operand lanes of v_mfma_f64_16x16x4f64 (measured on gfx950): lane l holds
+// B[k = l/16][j = l%16] and A[i = 4*(l%4) + (l%16)/4][k = l/16].
+struct Tile64 {
+  f64x4 acc[2][2];
+  __device__ void zero() {
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b) acc[a][b] = f64x4{0.0, 0.0, 0.0, 0.0};
+  }
+  // acc += sign * Am[row][k] * Bm[k][col]; Am indexed [row][k], Bm given by
+  // `bk(k, col)` through a [k][col] array or a [col][k] array (transposed)
+  template <bool BT>
+  __device__ void mac(const double (*Am)[kNb + 1], const double (*Bm)[kNb + 1], double sign) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int li = lane & 15, lk = lane >> 4;
+    const int ai = 4 * (li & 3) + (li >> 2);
+#pragma unroll 4
+    for (int k = 0; k < kNb; k += 4) {
+      double a[2], b[2];
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        a[x] = sign * Am[wm * 32 + x * 16 + ai][k + lk];
+        b[x] = BT ? Bm[wn * 32 + x * 16 + li][k + lk] : Bm[k + lk][wn * 32 + x * 16 + li];
+      }
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int y = 0; y < 2; ++y)
+          acc[x][y] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[x], b[y], acc[x][y], 0, 0, 0);
+    }
+  }
+  __device__ static int row(int x, int r) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    return (wave >> 1) * 32 + x * 16 + 4 * (lane >> 4) + r;
+  }
+  __device__ static int col(int y) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    return (wave & 1) * 32 + y * 16 + (lane & 15);
+  }
+};
+
+// ---------------------------------------------------------------- damping
+
+__global__ __launch_bounds__(256) void diag_stats_kernel(const float* const* __restrict__ mats,
+                                                         int c, float damp,
+                                                         uint8_t* __restrict__ dead,
+                                                         double* __restrict__ lamd,
+                                                         float* __restrict__ lam_out) {
+  __shared__ double red[256];
+  const int m = blockIdx.x;
+  const float* H = mats[m];
+  double sum = 0.0;
+  for (int i = threadIdx.x; i < c; i += 256) {
+    const float h = H[(int64_t)i * c + i];
+    const bool z = h == 0.0f;
+    dead[(int64_t)m * c + i] = z;
+    sum += z ? 1.0 : (double)h;
+  }
+  red[threadIdx.x] = sum;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const double l = (double)damp * (red[0] / (double)c);
+    lamd[m] = l;
+    if (lam_out) lam_out[m] = (float)l;
+  }
+}
+
+__global__ __launch_bounds__(256) void build_reversed_kernel(const float* const* __restrict__ mats,
+                                                             int c, const uint8_t* __restrict__ dead,
+                                                             const double* __restrict__ lamd,
+                                                             double* __restrict__ Aall) {
+  const int m = blockIdx.y;
+  int bi, bj;
+  tri_of(blockIdx.x, bi, bj);
+  const float* H = mats[m];
+  double* A = Aall + (int64_t)m * c * c;
+  const double l = lamd[m];
+  for (int idx = threadIdx.x; idx < kNb * kNb; idx += 256) {
+    const int r = idx >> 6, cc = idx & 63;
+    const int i = bi * kNb + r, j = bj * kNb + cc;
+    if (j > i) continue;
+    const int hi = c - 1 - i, hj = c - 1 - j;
+    double v = (double)H[(int64_t)hi * c + hj];
+    if (i == j) v = (dead[(int64_t)m * c + hi] ? 1.0 : v) + l;
+    A[(int64_t)i * c + j] = v;
+  }
+}
+
+// ---------------------------------------------------------------- blocked Cholesky
+
+__device__ void factor_block(double (*L)[kNb + 1], int* status) {
+  for (int j = 0; j < kNb; ++j) {
+    if (threadIdx.x == 0) {
+      double p = L[j][j];
+      if (!(p > 0.0)) {
+        atomicOr(status, kStatusNotPd);
+        p = 1.0;
+      }
+      L[j][j] = sqrt(p);
+    }
+    __syncthreads();
+    if (threadIdx.x > j && threadIdx.x < kNb) L[threadIdx.x][j] = L[threadIdx.x][j] / L[j][j];
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < kNb * kNb; idx += 256) {
+      const int r = idx >> 6, cc = idx & 63;
+      if (cc > j && cc <= r) L[r][cc] -= L[r][j] * L[cc][j];
+    }
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(256) void potrf_panel_kernel(double* __restrict__ Aall, int c, int k,
+                                                          double* __restrict__ dinv,
+                                                          int* __restrict__ status) {
+  __shared__ double L[kNb][kNb + 1];
+  __shared__ double P[kNb][kNb + 1];
+  const int m = blockIdx.y;
+  const int i = k + blockIdx.x;
+  double* A = Aall + (int64_t)m * c * c;
+  const int64_t k0 = (int64_t)k * kNb;
+  for (int idx = threadIdx.x; idx < kNb * kNb; idx += 256) {
+    const int r = idx >> 6, cc = idx & 63;
+    L[r][cc] = cc <= r ? A[(k0 + r) * c + k0 + cc] : 0.0;
+  }
+  __syncthreads();
+  factor_block(L, status);
+  if (i == k) {
+    // The diagonal block of A stays unfactored (other workgroups of this launch
+    // read it); the factor is needed only as its inverse.
+    for (int idx = threadIdx.x; idx < kNb * kNb; idx += 256) P[idx >> 6][idx & 63] = 0.0;
+    __syncthreads();
+    if (threadIdx.x < kNb) {
+      const int j = threadIdx.x;       // column j of L_kk^-1 by forward substitution
+      P[j][j] = 1.0 / L[j][j];
+      for (int r = j + 1; r < kNb; ++r) {
+        double v = 0.0;
+        for (int mm = j; mm < r; ++mm) v += L[r][mm] * P[mm][j];
+        P[r][j] = -v / L[r][r];
+      }
+    }
+    __syncthreads();
+    double* D = dinv + ((int64_t)m * (c / kNb) + k) * kNb * kNb;
+    for (int idx = threadIdx.x; idx < kNb * kNb; idx += 256) D[idx] = P[idx >> 6][idx & 63];
+    return;
+  }
+  const int64_t i0 = (int64_t)i * kNb;
+  for (int idx = threadIdx.x; idx < kNb * kNb; idx += 256) {
+    const int r = idx >> 6, cc = idx & 63;
+    P[r][cc] = A[(i0 + r) * c + k0 + cc];
+  }
+  __syncthreads();
+  if (threadIdx.x < kNb) {
+    const int r = threadIdx.x;         // row r of the panel: x L^T = p
+    for (int j = 0; j < kNb; ++j) {
+      double v = P[r][j];
+      for (int mm = 0; mm < j; ++mm) v -= P[r][mm] * L[j][mm];
+      P[r][j] = v / L[j][j];
+    }
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < kNb * kNb; idx += 256) {
+    const int r = idx >> 6, cc = idx & 63;
+    A[(i0 + r) * c + k0 + cc] = P[r][cc];
+  }
+}
+
+__global__ __launch_bounds__(256) void chol_update_kernel(double* __restrict__ Aall, int c, int k) {
+  __shared__ double Pi[kNb][kNb + 1];
+  __shared__ double Pj[kNb][kNb + 1];
+  const int m = blockIdx.y;
+  int bi, bj;
+  tri_of(blockIdx.x, bi, bj);
+  const int i = k + 1 + bi, j = k + 1 + bj;
+  const bool diag = i == j;
+  double* A = Aall + (int64_t)m * c * c;
+  const int64_t k0 = (int64_t)k * kNb, i0 = (int64_t)i * kNb, j0 = (int64_t)j * kNb;
+  for (int idx = threadIdx.x; idx < kNb * kNb; idx += 256) {
+    const int r = idx >> 6, cc = idx & 63;
+    Pi[r][cc] = A[(i0 + r) * c + k0 + cc];
+    Pj[r][cc] = A[(j0 + r) * c + k0 + cc];
+  }
+  __syncthreads();
+  Tile64 t;
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = Tile64::row(x, r), col = Tile64::col(y);
+        t.acc[x][y][r] = (!diag || col <= row) ? A[(i0 + row) * c + j0 + col] : 0.0;
+      }
+  t.mac<true>(Pi, Pj, -1.0);
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = Tile64::row(x, r), col = Tile64::col(y);
+        if (!diag || col <= row) A[(i0 + row) * c + j0 + col] = t.acc[x][y][r];
+      }
+}
+
+// ---------------------------------------------------------------- triangular inverse
+
+__global__ __launch_bounds__(256) void trtri_row_kernel(const double* __restrict__ Aall, int c, int i,
+                                                        const double* __restrict__ dinv,
+                                                        double* __restrict__ Xall,
+                                                        float* __restrict__ Uall) {
+  __shared__ double Ls[kNb][kNb + 1];
+  __shared__ double Xs[kNb][kNb + 1];
+  const int m = blockIdx.y, j = blockIdx.x;
+  const double* A = Aall + (int64_t)m * c * c;
+  double* X = Xall + (int64_t)m * c * c;
+  float* U = Uall + (int64_t)m * c * c;
+  const double* Di = dinv + ((int64_t)m * (c / kNb) + i) * kNb * kNb;
+  const int64_t i0 = (int64_t)i * kNb, j0 = (int64_t)j * kNb;
+  if (j == i) {
+    for (int idx = threadIdx.x; idx < kNb * kNb; idx += 256) {
+      const int r = idx >> 6, cc = idx & 63;
+      const double v = cc <= r ? Di[idx] : 0.0;
+      X[(i0 + r) * c + j0 + cc] = v;
+      if (cc <= r) U[(c - 1 - (i0 + r)) * c + (c - 1 - (j0 + cc))] = (float)v;
+    }
+    return;
+  }
+  Tile64 t;
+  t.zero();
+  for (int mm = j; mm < i; ++mm) {
+    const int64_t m0 = (int64_t)mm * kNb;
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < kNb * kNb; idx += 256) {
+      const int r = idx >> 6, cc = idx & 63;
+      Ls[r][cc] = A[(i0 + r) * c + m0 + cc];
+      Xs[r][cc] = X[(m0 + r) * c + j0 + cc];
+    }
+    __syncthreads();
+    t.mac<false>(Ls, Xs, 1.0);
+  }
+  // Xs <- T (the sum), Ls <- Linv_ii; then X[i][j] = -Linv_ii T
+  __syncthreads();
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Xs[Tile64::row(x, r)][Tile64::col(y)] = t.acc[x][y][r];
+  for (int idx = threadIdx.x; idx < kNb * kNb; idx += 256) Ls[idx >> 6][idx & 63] = Di[idx];
+  __syncthreads();
+  t.zero();
+  t.mac<false>(Ls, Xs, -1.0);
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = Tile64::row(x, r), col = Tile64::col(y);
+        const double v = t.acc[x][y][r];
+        X[(i0 + row) * c + j0 + col] = v;
+        U[(c - 1 - (i0 + row)) * c + (c - 1 - (j0 + col))] = (float)v;
+      }
+}
+
+void launch_inverse_cholesky(const GptqPlan& p, hipStream_t s) {
+  const int c = p.cols, nbk = c / kNb;
+  hipLaunchKernelGGL(diag_stats_kernel, dim3(p.n_mats), dim3(256), 0, s, p.mats, c, p.damp,
+                     p.dead, p.lamd, p.lam);
+  hipLaunchKernelGGL(build_reversed_kernel, dim3(nbk * (nbk + 1) / 2, p.n_mats), dim3(256), 0, s,
+                     p.mats, c, p.dead, p.lamd, p.A);
+  for (int k = 0; k < nbk; ++k) {
+    hipLaunchKernelGGL(potrf_panel_kernel, dim3(nbk - k, p.n_mats), dim3(256), 0, s, p.A, c, k,
+                       p.dinv, p.status);
+    const int rem = nbk - k - 1;
+    if (rem > 0)
+      hipLaunchKernelGGL(chol_update_kernel, dim3(rem * (rem + 1) / 2, p.n_mats), dim3(256), 0, s,
+                         p.A, c, k);
+  }
+  for (int i = 0; i < nbk; ++i)
+    hipLaunchKernelGGL(trtri_row_kernel, dim3(i + 1, p.n_mats), dim3(256), 0, s, p.A, c, i, p.dinv,
+                       p.X, p.U);
+}
+
+}  // namespace clha

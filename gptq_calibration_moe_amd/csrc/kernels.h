@@ -1,0 +1,102 @@
+// Internal declarations shared by the C-ABI layer (api.cpp) and the HIP kernel
+// sources.  Host-side launchers only; every launcher enqueues on `stream` and
+// returns without synchronising.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace clha {
+
+// ---------------------------------------------------------------- constants
+constexpr int kBucketTokens = 1024;   // tokens per bucketing workgroup (16 groups of 64)
+constexpr int kTokPad = 64;           // expert token lists are padded to this multiple
+constexpr int kMaxExperts = 256;
+constexpr int kMaxTopK = 16;
+constexpr int kMaxLayers = 8;
+constexpr int kSyrkTile = 128;        // Gram-sum output tile
+constexpr int kNb = 64;               // Cholesky / triangular-inverse block
+constexpr int kGptqRows = 64;         // rows per GPTQ workgroup
+
+// status word bits (device, latched; see clha_sync)
+constexpr int kStatusNonfinite = 1;
+constexpr int kStatusNotPd = 2;
+
+// ---------------------------------------------------------------- collection
+struct CollectPlan {
+  int64_t n_tokens;
+  int d, E, K, has_shared;
+  int nblk;              // bucketing workgroups
+  // device buffers (from the caller's workspace or outputs)
+  int32_t* topk;         // [n][K]
+  int32_t* blockcounts;  // [nblk][E]
+  int32_t* blockbase;    // [nblk][E]
+  int64_t* offsets;      // [E+1]
+  int64_t* pad_off;      // [slots+1] padded starts of each slot's token list
+  int32_t* slot_order;   // [slots] slots sorted by padded length, longest first
+  int32_t* token_ids;    // [n*K]
+  uint16_t* xgT;         // feature-major gathered activations
+  int64_t xg_tiles;      // upper bound of 64-token tiles over all slots
+  int* status;
+};
+
+void launch_route(const float* logits, const CollectPlan& p, hipStream_t s);
+void launch_bucket(const CollectPlan& p, int64_t* layer_counts, hipStream_t s);
+void launch_gather(const uint16_t* x, const CollectPlan& p, hipStream_t s);
+void launch_syrk(const CollectPlan& p, float* S, hipStream_t s);
+
+// ---------------------------------------------------------------- aggregation
+struct AggArgs {
+  const float* S[kMaxLayers];
+  const int64_t* counts[kMaxLayers];
+  float alpha[kMaxLayers];
+  int n_layers;
+  int mode;              // clha_alpha_mode
+  int d;
+  int slots;
+};
+void launch_aggregate(const AggArgs& a, float* H, float* alpha_out, hipStream_t s);
+
+// ---------------------------------------------------------------- GPTQ
+struct GJob {
+  const void* W;
+  uint8_t* codes;
+  float* scales;
+  uint8_t* zeros;
+  float* loss;
+  int64_t wf_off;        // offset of the job's fp32 working copy (elements)
+  int32_t dtype;
+  int32_t rows;
+  int32_t bits;
+  int32_t mat;           // index of the job's distinct Hessian
+  int32_t slab_base;     // first global slab of this job
+  int32_t n_slabs;
+};
+
+struct GptqPlan {
+  int n_jobs, n_mats, cols, group, block, total_slabs;
+  float damp;
+  const GJob* jobs;          // device [n_jobs]
+  const float* const* mats;  // device [n_mats] Hessian pointers
+  double* A;                 // device [n_mats][cols][cols]  reversed damped H, then its Cholesky factor
+  double* X;                 // device [n_mats][cols][cols]  inverse of that factor
+  float* U;                  // device [n_mats][cols][cols]  upper factor of Hd^-1 (fp32)
+  double* dinv;              // device [n_mats][cols/kNb][kNb][kNb] inverses of L's diagonal blocks
+  uint8_t* dead;             // device [n_mats][cols]
+  double* lamd;              // device [n_mats] damping lambda
+  float* lam;                // device [n_mats] lambda as float (optional output, may be null)
+  float* wf;                 // device fp32 working copies of all jobs' weights
+  float* partials;           // device [total_slabs][2]
+  int* status;
+};
+void launch_inverse_cholesky(const GptqPlan& p, hipStream_t s);
+void launch_gptq(const GptqPlan& p, hipStream_t s);
+
+// ---------------------------------------------------------------- loss
+void launch_loss(int rows, int cols, int group, const void* W, int dtype, const uint8_t* codes,
+                 const float* scales, const uint8_t* zeros, const float* H, float* partials,
+                 float* loss_out, hipStream_t s);
+int64_t loss_partial_count(int rows, int cols);
+
+}  // namespace clha

@@ -1,0 +1,268 @@
+// Collection phase, first half: top-K routing, per-expert bucketing and the
+// gather of each expert's rows into a feature-major layout.
+//
+// CLHA summary, section 2.2 (collection): per calibration batch, every layer
+// accumulates a Hessian and a token count for each expert that is active for
+// its tokens; section 2.3: routed experts see the K/E fraction of tokens the
+// router sends them, shared experts see all N tokens.
+//
+// Layout produced here (all in the caller's workspace):
+//   topk        int32 [N][K]        experts of each token, larger logit first
+//   offsets     int64 [E+1]         exclusive prefix sum of per-expert counts
+//   token_ids   int32 [N*K]         tokens of expert e at offsets[e].., ascending
+//   pad_off     int64 [slots+1]     start of slot e's token columns in xgT,
+//                                   each slot padded to a multiple of 64 tokens;
+//                                   slot E (if the block has shared experts) holds
+//                                   all N tokens in order
+//   xgT         bf16  per slot e a [d][npad_e] feature-major matrix at
+//                     xgT + pad_off[e]*d; padding columns are zero
+// Feature-major storage puts the Gram sum's contraction index (tokens) in
+// contiguous memory, which is the operand layout the matrix cores read.
+#include "kernels.h"
+
+namespace clha {
+
+// ------------------------------------------------------------------ routing
+
+__global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits, int64_t n,
+                                                    int E, int K, int32_t* __restrict__ topk,
+                                                    int* __restrict__ status) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= n) return;
+  const float* row = logits + t * E;
+  float val[kMaxTopK];
+  int idx[kMaxTopK];
+#pragma unroll
+  for (int p = 0; p < kMaxTopK; ++p) {
+    val[p] = -INFINITY;
+    idx[p] = 0x7fffffff;
+  }
+  bool bad = false;
+  for (int e = 0; e < E; ++e) {
+    float cv = row[e];
+    int ci = e;
+    bad |= !isfinite(cv);
+    // insertion into the list ordered by (logit descending, index ascending);
+    // an element pushed down keeps moving past entries it precedes, so equal
+    // logits always end up in index order
+#pragma unroll
+    for (int p = 0; p < kMaxTopK; ++p) {
+      if (p < K) {
+        const bool gt = cv > val[p] || (cv == val[p] && ci < idx[p]) || idx[p] == 0x7fffffff;
+        const float tv = val[p];
+        const int ti = idx[p];
+        val[p] = gt ? cv : tv;
+        idx[p] = gt ? ci : ti;
+        cv = gt ? tv : cv;
+        ci = gt ? ti : ci;
+      }
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < kMaxTopK; ++p)
+    if (p < K) topk[t * K + p] = idx[p];
+  if (bad) atomicOr(status, kStatusNonfinite);
+}
+
+void launch_route(const float* logits, const CollectPlan& p, hipStream_t s) {
+  const unsigned grid = (unsigned)((p.n_tokens + 255) / 256);
+  hipLaunchKernelGGL(route_kernel, dim3(grid), dim3(256), 0, s, logits, p.n_tokens, p.E, p.K,
+                     p.topk, p.status);
+}
+
+// ------------------------------------------------------------------ bucketing
+// A workgroup owns kBucketTokens consecutive tokens as 16 groups of 64.  For
+// each (group, expert) a 64-bit mask records which tokens of the group chose
+// the expert; popcounts of the masks give per-workgroup counts, and the rank of
+// a token inside its expert list is a popcount of the lower mask bits plus the
+// counts of the earlier groups -- no ordering atomics, so the lists come out
+// sorted by token and identical on every run.
+
+__device__ __forceinline__ void build_masks(const int32_t* __restrict__ topk, int64_t n, int K,
+                                            int E, unsigned long long* mask) {
+  for (int i = threadIdx.x; i < 16 * E; i += 256) mask[i] = 0ull;
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t base = (int64_t)blockIdx.x * kBucketTokens;
+  for (int g = wave; g < 16; g += 4) {
+    const int64_t t = base + g * 64 + lane;
+    if (t < n) {
+      for (int k = 0; k < K; ++k) {
+        const int e = topk[t * K + k];
+        atomicOr(&mask[g * E + e], 1ull << lane);
+      }
+    }
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(256) void bucket_count_kernel(const int32_t* __restrict__ topk,
+                                                           int64_t n, int K, int E,
+                                                           int32_t* __restrict__ blockcounts) {
+  __shared__ unsigned long long mask[16 * kMaxExperts];
+  build_masks(topk, n, K, E, mask);
+  for (int e = threadIdx.x; e < E; e += 256) {
+    int c = 0;
+#pragma unroll
+    for (int g = 0; g < 16; ++g) c += __popcll(mask[g * E + e]);
+    blockcounts[(int64_t)blockIdx.x * E + e] = c;
+  }
+}
+
+// One workgroup: per-expert exclusive scan over bucketing workgroups, expert
+// offsets, padded slot offsets, the longest-first slot order used by the Gram
+// kernel, and the layer's running token counts.
+__global__ __launch_bounds__(256) void bucket_scan_kernel(
+    const int32_t* __restrict__ blockcounts, int nblk, int64_t n, int E, int has_shared,
+    int32_t* __restrict__ blockbase, int64_t* __restrict__ offsets, int64_t* __restrict__ pad_off,
+    int32_t* __restrict__ slot_order, int64_t* __restrict__ layer_counts) {
+  __shared__ int64_t cnt[kMaxExperts + 1];
+  __shared__ int64_t padc[kMaxExperts + 1];
+  const int slots = E + has_shared;
+  for (int e = threadIdx.x; e < E; e += 256) {
+    int64_t run = 0;
+    for (int b = 0; b < nblk; ++b) {
+      const int c = blockcounts[(int64_t)b * E + e];
+      blockbase[(int64_t)b * E + e] = (int32_t)run;
+      run += c;
+    }
+    cnt[e] = run;
+  }
+  if (threadIdx.x == 0 && has_shared) cnt[E] = n;
+  __syncthreads();
+  for (int e = threadIdx.x; e < slots; e += 256) {
+    padc[e] = (cnt[e] + kTokPad - 1) / kTokPad * kTokPad;
+    if (layer_counts) layer_counts[e] += cnt[e];
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int64_t o = 0, po = 0;
+    for (int e = 0; e < E; ++e) {
+      offsets[e] = o;
+      o += cnt[e];
+    }
+    offsets[E] = o;
+    for (int e = 0; e < slots; ++e) {
+      pad_off[e] = po;
+      po += padc[e];
+    }
+    pad_off[slots] = po;
+  }
+  // rank of each slot by (padded length descending, slot ascending)
+  for (int e = threadIdx.x; e < slots; e += 256) {
+    int r = 0;
+    for (int o = 0; o < slots; ++o) r += (padc[o] > padc[e]) || (padc[o] == padc[e] && o < e);
+    slot_order[r] = e;
+  }
+}
+
+__global__ __launch_bounds__(256) void bucket_scatter_kernel(
+    const int32_t* __restrict__ topk, int64_t n, int K, int E,
+    const int32_t* __restrict__ blockbase, const int64_t* __restrict__ offsets,
+    int32_t* __restrict__ token_ids) {
+  __shared__ unsigned long long mask[16 * kMaxExperts];
+  __shared__ int32_t pre[16 * kMaxExperts];
+  build_masks(topk, n, K, E, mask);
+  for (int e = threadIdx.x; e < E; e += 256) {
+    int run = blockbase[(int64_t)blockIdx.x * E + e];
+    for (int g = 0; g < 16; ++g) {
+      pre[g * E + e] = run;
+      run += __popcll(mask[g * E + e]);
+    }
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int64_t base = (int64_t)blockIdx.x * kBucketTokens;
+  for (int g = wave; g < 16; g += 4) {
+    const int64_t t = base + g * 64 + lane;
+    if (t < n) {
+      for (int k = 0; k < K; ++k) {
+        const int e = topk[t * K + k];
+        const int r = pre[g * E + e] + __popcll(mask[g * E + e] & below);
+        token_ids[offsets[e] + r] = (int32_t)t;
+      }
+    }
+  }
+}
+
+void launch_bucket(const CollectPlan& p, int64_t* layer_counts, hipStream_t s) {
+  hipLaunchKernelGGL(bucket_count_kernel, dim3(p.nblk), dim3(256), 0, s, p.topk, p.n_tokens, p.K,
+                     p.E, p.blockcounts);
+  hipLaunchKernelGGL(bucket_scan_kernel, dim3(1), dim3(256), 0, s, p.blockcounts, p.nblk,
+                     p.n_tokens, p.E, p.has_shared, p.blockbase, p.offsets, p.pad_off,
+                     p.slot_order, layer_counts);
+  hipLaunchKernelGGL(bucket_scatter_kernel, dim3(p.nblk), dim3(256), 0, s, p.topk, p.n_tokens,
+                     p.K, p.E, p.blockbase, p.offsets, p.token_ids);
+}
+
+// ------------------------------------------------------------------ gather
+// One workgroup of 128 threads moves a 64-token x 128-feature tile.  Thread
+// (q, fc) reads 8 token rows x 8 features (16 B per row, 256 B contiguous per
+// row across the 16 threads of a token group), transposes the 8x8 bf16 block in
+// registers and writes 8 feature rows x 8 tokens (128 B contiguous per feature
+// across the 8 threads q = 0..7).  Tiles past the last slot exit at once.
+
+__device__ __forceinline__ uint32_t lo_pair(uint32_t a, uint32_t b) {
+  return (a & 0xffffu) | (b << 16);
+}
+__device__ __forceinline__ uint32_t hi_pair(uint32_t a, uint32_t b) {
+  return (a >> 16) | (b & 0xffff0000u);
+}
+
+__global__ __launch_bounds__(128) void gather_kernel(
+    const uint16_t* __restrict__ x, int64_t n, int d, int E, int has_shared,
+    const int64_t* __restrict__ offsets, const int64_t* __restrict__ pad_off,
+    const int32_t* __restrict__ token_ids, uint16_t* __restrict__ xgT) {
+  const int slots = E + has_shared;
+  const int64_t p0 = (int64_t)blockIdx.x * kTokPad;
+  const int64_t total = pad_off[slots];
+  if (p0 >= total) return;
+  int lo = 0, hi = slots;  // pad_off[lo] <= p0 < pad_off[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (pad_off[mid] <= p0) lo = mid; else hi = mid;
+  }
+  const int s = lo;
+  const int64_t npad = pad_off[s + 1] - pad_off[s];
+  const int64_t i0 = p0 - pad_off[s];
+  const bool routed = s < E;
+  const int64_t cnt = routed ? offsets[s + 1] - offsets[s] : n;
+  const int32_t* ids = token_ids + (routed ? offsets[s] : 0);
+  const int q = threadIdx.x & 7;         // token group of 8
+  const int fc = threadIdx.x >> 3;       // feature group of 8 (0..15)
+  const int f0 = blockIdx.y * 128 + fc * 8;
+
+  uint4 in[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int64_t i = i0 + q * 8 + u;
+    in[u] = make_uint4(0, 0, 0, 0);
+    if (i < cnt) {
+      const int64_t tok = routed ? (int64_t)ids[i] : i;
+      in[u] = *reinterpret_cast<const uint4*>(x + tok * d + f0);
+    }
+  }
+  uint16_t* out = xgT + pad_off[s] * d + i0 + q * 8;
+#pragma unroll
+  for (int fp = 0; fp < 4; ++fp) {       // feature pair (2fp, 2fp+1) inside the 8
+    uint32_t a[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) a[u] = (&in[u].x)[fp];
+    uint4 e, o;
+    e.x = lo_pair(a[0], a[1]); e.y = lo_pair(a[2], a[3]);
+    e.z = lo_pair(a[4], a[5]); e.w = lo_pair(a[6], a[7]);
+    o.x = hi_pair(a[0], a[1]); o.y = hi_pair(a[2], a[3]);
+    o.z = hi_pair(a[4], a[5]); o.w = hi_pair(a[6], a[7]);
+    *reinterpret_cast<uint4*>(out + (int64_t)(f0 + 2 * fp) * npad) = e;
+    *reinterpret_cast<uint4*>(out + (int64_t)(f0 + 2 * fp + 1) * npad) = o;
+  }
+}
+
+void launch_gather(const uint16_t* x, const CollectPlan& p, hipStream_t s) {
+  hipLaunchKernelGGL(gather_kernel, dim3((unsigned)p.xg_tiles, p.d / 128), dim3(128), 0, s, x,
+                     p.n_tokens, p.d, p.E, p.has_shared, p.offsets, p.pad_off, p.token_ids,
+                     p.xgT);
+}
+
+}  // namespace clha

@@ -1,0 +1,228 @@
+/*
+ * clha.h - C ABI of the CLHA calibration library for AMD Instinct MI355X (gfx950).
+ *
+ * CLHA (Cross-Layer Hessian Aggregation) calibrates Mixture-of-Experts weights
+ * that adjacent layers share (cross-layer weight sharing, CLWS).  The method,
+ * as the gist.science summary "CLHA - Cross-Layer Hessian Aggregation for
+ * quantizing weight-shared MoE transformers" states it, has three phases
+ * (section 2.2):
+ *   1. collection  - per layer and per active expert, accumulate the Hessian
+ *                    (activation second moment) and the token count;
+ *   2. aggregation - per shared expert, H_comb = sum_i alpha_i H_i with
+ *                    alpha_i = n_i / sum n (routing frequency) or 1/m (equal);
+ *   3. quantization - standard GPTQ column-sequential updates on H_comb, at b
+ *                    bits, or b+1 bits for always-active shared experts
+ *                    (CLHA-MP, section 2.3).
+ * Section 2.4 requires the Hessian accumulators to be keyed by layer, not by
+ * the shared weight module; this ABI makes the layer an explicit argument of
+ * every collection call and rejects two layers that alias one accumulator.
+ *
+ * Conventions
+ *   - Every array argument marked "device" is a pointer into GPU memory that the
+ *     caller allocated and owns.  The library never frees caller memory.  The
+ *     only memory the library allocates itself is a 64-byte device status word
+ *     per context (clha_create) and host-side bookkeeping.
+ *   - `stream` is a hipStream_t passed as void*; NULL means the default stream.
+ *     Every compute call only enqueues work on `stream` and returns; outputs are
+ *     valid once the stream has been synchronised (clha_sync does that).
+ *   - Argument, shape and alignment errors are detected on the host before
+ *     anything is enqueued; the call then returns the error and enqueues
+ *     nothing.  Numerical failures found on the device (non-finite router
+ *     logits, a damped Hessian that is not positive definite) are latched in
+ *     the context's status word and returned by the next clha_sync.
+ *   - Matrices are row-major.  bf16 values are passed as their uint16 bit
+ *     patterns.  Device pointers must be 16-byte aligned.
+ *   - A context is used by one host thread at a time.  No C++ exception crosses
+ *     this interface.
+ */
+#ifndef CLHA_H
+#define CLHA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CLHA_API __attribute__((visibility("default")))
+
+typedef enum clha_status {
+  CLHA_OK = 0,
+  CLHA_ERR_INVALID_ARG = 1,   /* null pointer, unknown layer, aliased buffers, bad enum */
+  CLHA_ERR_SHAPE = 2,         /* a size outside the supported range */
+  CLHA_ERR_ALIGN = 3,         /* a device pointer not 16-byte aligned */
+  CLHA_ERR_HIP = 4,           /* the HIP runtime reported an error */
+  CLHA_ERR_NOT_PD = 5,        /* a damped Hessian is not positive definite */
+  CLHA_ERR_NONFINITE = 6,     /* a router logit is NaN or infinite */
+  CLHA_ERR_WORKSPACE = 7      /* workspace smaller than the matching *_workspace_bytes */
+} clha_status;
+
+typedef enum clha_alpha_mode {
+  CLHA_ALPHA_ROUTING_FREQ = 0, /* alpha_i = n_i / sum_j n_j ("CLHA-rt", section 2.2)      */
+  CLHA_ALPHA_EQUAL = 1,        /* alpha_i = 1/m over the m non-empty layers ("CLHA-eq")    */
+  CLHA_ALPHA_EXPLICIT = 2      /* caller-given alpha_i; alpha = (1, 0) is PLIC (section 2.1) */
+} clha_alpha_mode;
+
+typedef enum clha_dtype { CLHA_F32 = 0, CLHA_BF16 = 1 } clha_dtype;
+
+/* Shape of the MoE block whose routed experts a group of layers shares. */
+typedef struct clha_moe_desc {
+  int32_t d;            /* hidden size; columns of every calibrated matrix; multiple of 128, <= 8192 */
+  int32_t n_routed;     /* E, routed experts; 1..256 */
+  int32_t top_k;        /* K, experts per token; 1..min(E, 16) */
+  int32_t n_shared;     /* always-active shared experts; 0 or more.  They all see the same
+                           input, so one Hessian slot (index E) serves all of them. */
+  int64_t max_tokens;   /* largest n_tokens of one clha_collect_hessians call; >= 1 */
+} clha_moe_desc;
+
+typedef struct clha_ctx clha_ctx;
+
+/* Creates a context for one MoE block shape on the current HIP device.
+ * Errors: INVALID_ARG (null), SHAPE (desc outside the ranges above), HIP. */
+CLHA_API clha_status clha_create(const clha_moe_desc* desc, clha_ctx** out);
+
+/* Frees the context (host bookkeeping and its status word).  Accepts NULL. */
+CLHA_API clha_status clha_destroy(clha_ctx* ctx);
+
+/* Text of the last error on this context (static storage owned by ctx). */
+CLHA_API const char* clha_last_error(const clha_ctx* ctx);
+
+/* Number of Hessian slots per layer: E, plus one when n_shared > 0. */
+CLHA_API int32_t clha_num_slots(const clha_ctx* ctx);
+
+/* Binds the accumulators of one layer (the layer-aware collection of section 2.4).
+ *   S      device, float [slots][d][d]: Gram sums S[e] = sum_t x_t x_t^T over the tokens
+ *          routed to slot e (slot E: all tokens).  Only the lower triangle (i >= j) is
+ *          ever written; the caller zeroes the buffer before the first collection.
+ *   counts device, int64 [slots]: token counts n[e]; zeroed by the caller.
+ * A layer may be registered again (rebinding it).  Registering a buffer range that
+ * overlaps another layer's S or counts returns INVALID_ARG: two layers never share
+ * one accumulator. */
+CLHA_API clha_status clha_register_layer(clha_ctx* ctx, int32_t layer, float* S, int64_t* counts);
+
+/* Device workspace bytes that clha_collect_hessians needs for max_tokens tokens. */
+CLHA_API size_t clha_collect_workspace_bytes(const clha_ctx* ctx);
+
+/* Collection phase for one calibration batch of one layer (section 2.2, phase 1):
+ *   1. routes each token to its top-K experts (larger logit first, ties to the lower index);
+ *   2. buckets tokens per expert (counts, exclusive offsets, token lists ascending);
+ *   3. gathers each expert's rows of X;
+ *   4. S[e] += X_e^T X_e (fp32 accumulation of bf16 products) for every routed expert,
+ *      and S[E] += X^T X over all tokens when the block has shared experts;
+ *      counts[e] += n_e, counts[E] += n_tokens.
+ *   x        device, bf16 bits [n_tokens][d]
+ *   logits   device, float [n_tokens][E]
+ *   topk_out, offsets_out, token_ids_out: optional device outputs of this batch's
+ *            routing (int32 [n_tokens][K], int64 [E+1], int32 [n_tokens*K]); NULL skips.
+ *   workspace device, >= clha_collect_workspace_bytes(ctx) bytes.
+ * Non-finite logits latch CLHA_ERR_NONFINITE (routing of that token is then undefined).
+ * Errors: INVALID_ARG (unregistered layer, null x/logits), SHAPE (n_tokens outside
+ * 0..max_tokens), ALIGN, WORKSPACE.  n_tokens == 0 enqueues nothing. */
+CLHA_API clha_status clha_collect_hessians(clha_ctx* ctx, int32_t layer, int64_t n_tokens,
+                                           const uint16_t* x, const float* logits,
+                                           int32_t* topk_out, int64_t* offsets_out,
+                                           int32_t* token_ids_out,
+                                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Aggregation phase (section 2.1 Proposition 1, section 2.2 phase 2) over the given
+ * layers, for every slot e:
+ *   ROUTING_FREQ: H[e] = (sum_i S_i[e]) / (sum_i n_i[e])
+ *   EQUAL:        H[e] = sum_i (1/m) (S_i[e] / n_i[e]) over the m layers with n_i[e] > 0
+ *   EXPLICIT:     H[e] = sum_i alpha_i (S_i[e] / n_i[e]); layers with n_i[e] == 0 drop out
+ *                 and, if a dropped layer had alpha_i != 0, the rest are renormalised.
+ * A slot with no tokens in any layer gets H[e] = I and alpha 0.
+ *   layers    host, int32 [n_layers]; registered layers; n_layers 1..8
+ *   alpha     host, float [n_layers]; EXPLICIT only, else ignored (may be NULL)
+ *   H_out     device, float [slots][d][d]; full symmetric matrices
+ *   alpha_out device, float [slots][n_layers] (the weights used); may be NULL
+ * Errors: INVALID_ARG, SHAPE, ALIGN. */
+CLHA_API clha_status clha_aggregate(clha_ctx* ctx, int32_t n_layers, const int32_t* layers,
+                                    clha_alpha_mode mode, const float* alpha,
+                                    float* H_out, float* alpha_out, void* stream);
+
+/* One GPTQ job: one weight matrix (e.g. an expert's gate and up stacked row-wise)
+ * and the Hessian it is quantized against. */
+typedef struct clha_gptq_job {
+  const float* H;      /* device, float [cols][cols], symmetric PSD, undamped (e.g. H_comb) */
+  const void* W;       /* device, [rows][cols] row-major, float or bf16 bits (w_dtype) */
+  int32_t w_dtype;     /* clha_dtype */
+  int32_t rows;        /* >= 1 */
+  int32_t bits;        /* 2..8; b, or b+1 for always-active shared experts (CLHA-MP) */
+  int32_t pad_;
+  uint8_t* codes;      /* device out, uint8 [rows][cols]: q in [0, 2^bits - 1] */
+  float* scales;       /* device out, float [rows][cols/group] */
+  uint8_t* zeros;      /* device out, uint8 [rows][cols/group] */
+  float* loss;         /* device out, float [1]: tr[(Wq - W) H (Wq - W)^T]; may be NULL */
+} clha_gptq_job;
+
+/* Device workspace bytes clha_gptq_quantize needs for these jobs. */
+CLHA_API size_t clha_gptq_workspace_bytes(const clha_ctx* ctx, int32_t n_jobs,
+                                          const clha_gptq_job* jobs, int32_t cols);
+
+/* Quantization phase (section 2.2 phase 3, "standard GPTQ") for a batch of jobs.
+ * For every distinct H (jobs sharing an H pointer share one factorisation):
+ *   dead columns (H_ii == 0) get H_ii := 1 and their weights are treated as 0;
+ *   lambda = damp * mean(diag H); Hd = H + lambda I;
+ *   U = upper Cholesky factor of Hd^-1.
+ * Then for each job, blocks of `block` columns, column by column: at each group's first
+ * column fit the per-row asymmetric grid on the group's current weights (range widened
+ * to contain 0; an all-zero group uses (-1, 1); s = (max - min)/maxq; z = rint(-min/s));
+ * q = clamp(rint(w/s) + z, 0, maxq); err = (w - s(q - z))/U_jj; propagate err into the
+ * later columns of the block through row j of U, and after the block into all later
+ * columns.  Codes, scales and zero points are decided in fp32 with IEEE division and
+ * round-half-to-even.  loss = sum_j err_j^2 - lambda ||Wq - W||^2, which equals
+ * tr[(Wq - W) H (Wq - W)^T] on the undamped H.
+ *   cols      columns of every job; multiple of `block`, <= 8192
+ *   group     g; divides block
+ *   block     64 or 128
+ *   damp      relative damping, >= 0 (0.01 is customary)
+ * Errors: INVALID_ARG, SHAPE, ALIGN, WORKSPACE.  A Hessian that is not positive definite
+ * after damping latches CLHA_ERR_NOT_PD (that job's outputs are then undefined). */
+CLHA_API clha_status clha_gptq_quantize(clha_ctx* ctx, int32_t n_jobs, const clha_gptq_job* jobs,
+                                        int32_t cols, int32_t group, int32_t block, float damp,
+                                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Device workspace bytes clha_inverse_cholesky needs for n Hessians of size cols. */
+CLHA_API size_t clha_inverse_cholesky_workspace_bytes(const clha_ctx* ctx, int32_t n, int32_t cols);
+
+/* The damping and factorisation steps of clha_gptq_quantize on their own (GPTQ's
+ * "Cholesky of H^-1"), for inspection: for each of the n Hessians H[i],
+ *   dead columns (H_ii == 0) get H_ii := 1; lambda = damp * mean(diag H);
+ *   U = upper Cholesky factor of (H + lambda I)^-1.
+ *   H          host array of n device pointers, each float [cols][cols] symmetric
+ *   U_out      device float [n][cols][cols]; only the upper triangle (with the
+ *              diagonal) is written
+ *   lambda_out device float [n] (may be NULL); dead_out device uint8 [n][cols] (may be NULL)
+ *   cols       multiple of 64, <= 8192
+ * Errors: INVALID_ARG, SHAPE, ALIGN, WORKSPACE; NOT_PD is latched as in clha_gptq_quantize. */
+CLHA_API clha_status clha_inverse_cholesky(clha_ctx* ctx, int32_t n, const float* const* H,
+                                           int32_t cols, float damp, float* U_out,
+                                           float* lambda_out, uint8_t* dead_out,
+                                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Device workspace bytes clha_loss needs. */
+CLHA_API size_t clha_loss_workspace_bytes(const clha_ctx* ctx, int32_t rows, int32_t cols);
+
+/* Reconstruction loss of a quantized matrix under any Hessian, computed directly:
+ *   loss = sum_r (Wq_r - W_r) H (Wq_r - W_r)^T,  Wq = s (q - z) per group
+ * (the objective of section 2.1 for one layer term; with H = H_a or H_b it is the
+ * per-layer calibration error of a shared weight).
+ *   W device [rows][cols] (w_dtype); codes/scales/zeros as produced by clha_gptq_quantize;
+ *   H device float [cols][cols] symmetric; loss_out device float [1].
+ * Errors: INVALID_ARG, SHAPE, ALIGN, WORKSPACE. */
+CLHA_API clha_status clha_loss(clha_ctx* ctx, int32_t rows, int32_t cols, int32_t group,
+                               const void* W, int32_t w_dtype, const uint8_t* codes,
+                               const float* scales, const uint8_t* zeros, const float* H,
+                               float* loss_out, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/* Waits for `stream`, then returns and clears the first latched device error
+ * (NONFINITE or NOT_PD), or CLHA_OK. */
+CLHA_API clha_status clha_sync(clha_ctx* ctx, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CLHA_H */

@@ -1,0 +1,92 @@
+"""Shared helpers of the GPU parity tests: run the HIP path through the C ABI on
+seeded inputs and compare with the CPU oracle under the stated tolerances."""
+import numpy as np
+import torch
+
+import gen
+
+HESS_TOL = 1e-4        # max |H_gpu - H_ref| / sqrt(H_ref_ii H_ref_jj)
+CODE_AGREE = 0.999     # fraction of identical codes
+LOSS_RTOL = 1e-3       # relative loss difference
+
+
+def dev():
+    return torch.device("cuda", 0)
+
+
+def bits_to_dev(bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev()).view(torch.bfloat16)
+
+
+def to_dev(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev())
+
+
+def weights_to_dev(wl, w: np.ndarray) -> torch.Tensor:
+    return bits_to_dev(w) if wl.w_dtype == "bf16" else to_dev(w.astype(np.float32))
+
+
+def hess_err(G, R) -> float:
+    """Max error over the lower triangle, normalised by sqrt(R_ii R_jj)."""
+    G = np.asarray(G, np.float64)
+    R = np.asarray(R, np.float64)
+    dg = np.sqrt(np.maximum(np.diag(R), 0.0))
+    den = np.outer(dg, dg)
+    low = np.tril(np.ones_like(R, dtype=bool))
+    zero = low & (den == 0)
+    if np.any(G[zero] != 0) and np.any(R[zero] == 0):
+        return float("inf")
+    m = low & (den > 0)
+    if not m.any():
+        return 0.0
+    return float(np.max(np.abs(G - R)[m] / den[m]))
+
+
+def run_group(wl, inputs, jobs, *, mode=None, alpha=None, chunks=1, layers=(0, 1),
+              block=128, keep_routing=True, agg_layers=None):
+    """Runs collection for every layer, aggregation and GPTQ through the ABI.
+    inputs: {"x": [bits per layer], "logits": [...]}; jobs: {expert: stored weights}."""
+    import gptq_calibration_moe_amd as clha
+    from gptq_calibration_moe_amd.calibrate import SharedGroupCalibration
+
+    n = inputs["x"][0].shape[0]
+    ctx = clha.Context(wl.d, wl.n_routed, wl.top_k, wl.n_shared, max_tokens=n, device=dev())
+    cal = SharedGroupCalibration(ctx, list(layers))
+    out = {"topk": [], "offsets": [], "token_ids": []}
+    for li, l in enumerate(layers):
+        x = bits_to_dev(inputs["x"][li])
+        lg = to_dev(inputs["logits"][li])
+        if chunks == 1:
+            tk = torch.empty(n, wl.top_k, dtype=torch.int32, device=dev()) if keep_routing else None
+            of = torch.empty(wl.n_routed + 1, dtype=torch.int64, device=dev()) if keep_routing else None
+            ti = torch.empty(n * wl.top_k, dtype=torch.int32, device=dev()) if keep_routing else None
+            cal.collect(l, x, lg, topk_out=tk, offsets_out=of, token_ids_out=ti)
+            if keep_routing:
+                out["topk"].append(tk)
+                out["offsets"].append(of)
+                out["token_ids"].append(ti)
+        else:
+            bounds = np.linspace(0, n, chunks + 1).astype(int)
+            for a, b in zip(bounds[:-1], bounds[1:]):
+                cal.collect(l, x[a:b], lg[a:b])
+    ctx.sync()
+    res = {"ctx": ctx, "cal": cal}
+    res["S"] = [cal.S[l].cpu().numpy() for l in layers]
+    res["counts"] = [cal.counts[l].cpu().numpy() for l in layers]
+    for k in ("topk", "offsets", "token_ids"):
+        res[k] = [t.cpu().numpy() for t in out[k]]
+    if mode is not None:
+        cal.aggregate(mode, alpha=alpha, layers=agg_layers)
+        ctx.sync()
+        res["H"] = cal.H.cpu().numpy()
+        res["alpha"] = cal.alpha.cpu().numpy()
+    if jobs:
+        wdev = {e: weights_to_dev(wl, w) for e, w in jobs.items()}
+        o = cal.quantize(wdev, wl.bits, wl.shared_bits, wl.group, block=block, damp=wl.damp)
+        ctx.sync()
+        res["gptq"] = {e: {k: v.cpu().numpy() for k, v in d.items()} for e, d in o.items()}
+    return res
+
+
+def agree(a, b) -> float:
+    return float(np.mean(np.asarray(a) == np.asarray(b)))
