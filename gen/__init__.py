@@ -134,6 +134,14 @@ def _haar_orthogonal(rng: np.random.Generator, d: int) -> np.ndarray:
     return q * np.sign(np.diag(r))[None, :]
 
 
+def _student_t_f32(rng, shape, nu: float) -> np.ndarray:
+    """Student-t(nu) in float32 as Z * sqrt(nu / chi2_nu), chi2_nu = 2 Gamma(nu/2)."""
+    z = rng.standard_normal(shape, dtype=np.float32)
+    g = rng.standard_gamma(np.float32(nu / 2.0), shape, dtype=np.float32)
+    z *= np.sqrt(np.float32(nu / 2.0) / g)
+    return z
+
+
 def _normal_f32(rng, shape, scale=1.0) -> np.ndarray:
     x = rng.standard_normal(shape, dtype=np.float32)
     if scale != 1.0:
@@ -160,8 +168,8 @@ def activations(wl: Workload, pair: int = 0, t: Optional[float] = None,
         noise = _normal_f32(_rng(wl, pair, _S_XB), (n, d), 0.3)
         xb = bf16_bits(bf16_value(xa) @ q + noise)
     elif wl.x_kind == "student_t":
-        xa = bf16_bits(_rng(wl, pair, _S_XA).standard_t(4.0, (n, d)).astype(np.float32))
-        xb = bf16_bits(_rng(wl, pair, _S_XB).standard_t(4.0, (n, d)).astype(np.float32))
+        xa = bf16_bits(_student_t_f32(_rng(wl, pair, _S_XA), (n, d), 4.0))
+        xb = bf16_bits(_student_t_f32(_rng(wl, pair, _S_XB), (n, d), 4.0))
     elif wl.x_kind == "drift":
         if t is None:
             raise ValueError("drift workload needs t")

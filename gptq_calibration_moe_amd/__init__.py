@@ -4,8 +4,8 @@ Argument marshalling only: every step of the calibration path runs in the HIP
 kernels behind the C ABI declared in ``include/clha.h``.  PyTorch supplies
 device memory (tensors) and streams; this module checks dtypes, shapes and
 devices, passes raw pointers through ctypes and turns non-zero status codes
-into ``ClhaError``.  The library must be built (``python -m
-gptq_calibration_moe_amd.build``); without it, importing the binding raises.
+into ``ClhaError``.  The library must be built (``python
+gptq_calibration_moe_amd/build.py``); without it, importing the binding raises.
 
 Names follow the C entry points: ``Context.collect_hessians`` calls
 ``clha_collect_hessians`` and so on.
@@ -30,8 +30,10 @@ EXPORTS = (
     "clha_create", "clha_destroy", "clha_last_error", "clha_num_slots", "clha_register_layer",
     "clha_collect_workspace_bytes", "clha_collect_hessians", "clha_aggregate",
     "clha_gptq_workspace_bytes", "clha_gptq_quantize", "clha_inverse_cholesky_workspace_bytes",
-    "clha_inverse_cholesky", "clha_loss_workspace_bytes", "clha_loss", "clha_sync",
+    "clha_inverse_cholesky", "clha_loss_workspace_bytes", "clha_loss", "clha_set_timing",
+    "clha_read_timing", "clha_sync",
 )
+STAGES = ("route", "bucket", "gather", "syrk", "aggregate", "factor", "gptq", "loss")
 
 
 class ClhaError(RuntimeError):
@@ -54,7 +56,7 @@ class GptqJob(C.Structure):
 def _load() -> C.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing; build it with "
-                          "`python -m gptq_calibration_moe_amd.build`")
+                          "`python gptq_calibration_moe_amd/build.py`")
     lib = C.CDLL(LIB_PATH)
     vp, i32, i64, sz, f32 = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t, C.c_float
     sig = {
@@ -72,6 +74,8 @@ def _load() -> C.CDLL:
         "clha_inverse_cholesky": ([vp, i32, C.POINTER(vp), i32, f32, vp, vp, vp, vp, sz, vp], i32),
         "clha_loss_workspace_bytes": ([vp, i32, i32], sz),
         "clha_loss": ([vp, i32, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp], i32),
+        "clha_set_timing": ([vp, i32], i32),
+        "clha_read_timing": ([vp, C.POINTER(C.c_double), C.POINTER(i64), i32], i32),
         "clha_sync": ([vp, vp], i32),
     }
     for name, (args, res) in sig.items():
@@ -227,6 +231,25 @@ class Context:
                              j["loss"].data_ptr() if j.get("loss") is not None else None)
         return arr
 
+    class PreparedGptq:
+        """A checked, marshalled job batch for repeated clha_gptq_quantize calls."""
+
+        def __init__(self, arr, n, cols, ws):
+            self.arr, self.n, self.cols, self.ws = arr, n, cols, ws
+
+    def prepare_gptq(self, jobs, cols: int) -> "Context.PreparedGptq":
+        arr = self._jobs(jobs, cols)
+        need = lib.clha_gptq_workspace_bytes(self._h, len(jobs), arr, cols)
+        ws = torch.empty(max(int(need), 256), dtype=torch.uint8, device=self.device)
+        prep = Context.PreparedGptq(arr, len(jobs), cols, ws)
+        prep.tensors = jobs          # keep the job tensors alive with the pointers
+        return prep
+
+    def run_gptq(self, prep: "Context.PreparedGptq", group: int, block: int = 128,
+                 damp: float = 0.01, stream=None):
+        self._raise(lib.clha_gptq_quantize(self._h, prep.n, prep.arr, prep.cols, group, block,
+                                           damp, _ptr(prep.ws), prep.ws.numel(), _stream(stream)))
+
     def gptq_workspace_bytes(self, jobs, cols: int) -> int:
         arr = self._jobs(jobs, cols)
         return lib.clha_gptq_workspace_bytes(self._h, len(jobs), arr, cols)
@@ -274,6 +297,17 @@ class Context:
                                   BF16 if W.dtype == torch.bfloat16 else F32, _ptr(codes),
                                   _ptr(scales), _ptr(zeros), _ptr(H), _ptr(loss_out), _ptr(ws),
                                   ws.numel(), _stream(stream)))
+
+    def set_timing(self, enable: bool):
+        self._raise(lib.clha_set_timing(self._h, 1 if enable else 0))
+
+    def read_timing(self) -> dict:
+        """{stage: (total ms, calls)} of the stages recorded since the last read."""
+        n = len(STAGES)
+        ms = (C.c_double * n)()
+        calls = (C.c_int64 * n)()
+        self._raise(lib.clha_read_timing(self._h, ms, calls, n))
+        return {name: (ms[i], calls[i]) for i, name in enumerate(STAGES)}
 
     def sync(self, stream=None):
         self._raise(lib.clha_sync(self._h, _stream(stream)))

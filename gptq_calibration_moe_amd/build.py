@@ -2,7 +2,8 @@
 
 hipcc compiles every HIP source for gfx950 (objects under _build/) and links
 them with the C-ABI layer into one shared library.  Packed fp32 instructions
-are disabled for device code.  Run ``python -m gptq_calibration_moe_amd.build``.
+are disabled for device code.  Run ``python gptq_calibration_moe_amd/build.py``
+(this file does not import the package, so it works while no library exists).
 """
 import concurrent.futures as cf
 import os

@@ -60,6 +60,19 @@ class SharedGroupCalibration:
             }
         return out
 
+    def prepare_quantize(self, weights: dict, bits: int, shared_bits: int, group: int,
+                         outputs: Optional[dict] = None, H: Optional[torch.Tensor] = None):
+        """Marshals the GPTQ job batch once; run it with ctx.run_gptq(prep, group, ...)."""
+        H = self.H if H is None else H
+        experts = sorted(weights)
+        rows = weights[experts[0]].shape[0]
+        if outputs is None:
+            outputs = self.make_outputs(experts, rows, group)
+        jobs = [{"H": H[self.slot_of(e)], "W": weights[e],
+                 "bits": shared_bits if e >= self.ctx.n_routed else bits, **outputs[e]}
+                for e in experts]
+        return self.ctx.prepare_gptq(jobs, self.ctx.d), outputs
+
     def quantize(self, weights: dict, bits: int, shared_bits: int, group: int, block: int = 128,
                  damp: float = 0.01, outputs: Optional[dict] = None, H: Optional[torch.Tensor] = None):
         """weights: {expert: W [rows, d] float32 or bfloat16}.  Routed expert e uses

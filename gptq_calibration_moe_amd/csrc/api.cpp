@@ -40,6 +40,14 @@ struct clha_ctx {
   size_t pinned_bytes = 0;
   hipEvent_t pinned_done = nullptr;
   bool pinned_pending = false;
+  // optional per-stage timers
+  bool timing = false;
+  struct Rec {
+    int stage;
+    hipEvent_t a, b;
+  };
+  std::vector<Rec> recs;
+  std::vector<hipEvent_t> free_events;
 };
 
 namespace {
@@ -72,6 +80,40 @@ struct Carver {
 };
 
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+hipEvent_t take_event(clha_ctx* ctx) {
+  if (!ctx->free_events.empty()) {
+    hipEvent_t e = ctx->free_events.back();
+    ctx->free_events.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Records a hipEvent pair around one stage's launches when timing is enabled.
+struct StageTimer {
+  clha_ctx* ctx;
+  int stage;
+  hipStream_t s;
+  hipEvent_t a = nullptr;
+  StageTimer(clha_ctx* c, int st, hipStream_t stream) : ctx(c), stage(st), s(stream) {
+    if (!ctx->timing) return;
+    a = take_event(ctx);
+    if (a) hipEventRecord(a, s);
+  }
+  ~StageTimer() {
+    if (!a) return;
+    hipEvent_t b = take_event(ctx);
+    if (!b) {
+      ctx->free_events.push_back(a);
+      return;
+    }
+    hipEventRecord(b, s);
+    ctx->recs.push_back({stage, a, b});
+  }
+};
 
 clha_status hip_check(clha_ctx* ctx, const char* what) {
   const hipError_t e = hipGetLastError();
@@ -239,6 +281,12 @@ CLHA_API clha_status clha_destroy(clha_ctx* ctx) {
   if (ctx->pinned_pending) hipEventSynchronize(ctx->pinned_done);
   if (ctx->pinned) hipHostFree(ctx->pinned);
   if (ctx->pinned_done) hipEventDestroy(ctx->pinned_done);
+  for (auto& r : ctx->recs) {
+    hipEventSynchronize(r.b);
+    hipEventDestroy(r.a);
+    hipEventDestroy(r.b);
+  }
+  for (auto e : ctx->free_events) hipEventDestroy(e);
   if (ctx->status_dev) hipFree(ctx->status_dev);
   delete ctx;
   return CLHA_OK;
@@ -320,10 +368,22 @@ CLHA_API clha_status clha_collect_hessians(clha_ctx* ctx, int32_t layer, int64_t
                (p.has_shared ? (n_tokens + clha::kTokPad - 1) / clha::kTokPad : 0);
   p.status = ctx->status_dev;
   const hipStream_t s = as_stream(stream);
-  clha::launch_route(logits, p, s);
-  clha::launch_bucket(p, it->second.counts, s);
-  clha::launch_gather(x, p, s);
-  clha::launch_syrk(p, it->second.S, s);
+  {
+    StageTimer t(ctx, CLHA_STAGE_ROUTE, s);
+    clha::launch_route(logits, p, s);
+  }
+  {
+    StageTimer t(ctx, CLHA_STAGE_BUCKET, s);
+    clha::launch_bucket(p, it->second.counts, s);
+  }
+  {
+    StageTimer t(ctx, CLHA_STAGE_GATHER, s);
+    clha::launch_gather(x, p, s);
+  }
+  {
+    StageTimer t(ctx, CLHA_STAGE_SYRK, s);
+    clha::launch_syrk(p, it->second.S, s);
+  }
   return hip_check(ctx, "collect_hessians");
 }
 
@@ -364,7 +424,10 @@ CLHA_API clha_status clha_aggregate(clha_ctx* ctx, int32_t n_layers, const int32
   a.mode = (int)mode;
   a.d = ctx->desc.d;
   a.slots = ctx->slots;
-  clha::launch_aggregate(a, H_out, alpha_out, as_stream(stream));
+  {
+    StageTimer t(ctx, CLHA_STAGE_AGGREGATE, as_stream(stream));
+    clha::launch_aggregate(a, H_out, alpha_out, as_stream(stream));
+  }
   return hip_check(ctx, "aggregate");
 }
 
@@ -468,8 +531,14 @@ CLHA_API clha_status clha_gptq_quantize(clha_ctx* ctx, int32_t n_jobs, const clh
   p.wf = L.wf;
   p.partials = reinterpret_cast<float*>(L.partials);
   p.status = ctx->status_dev;
-  clha::launch_inverse_cholesky(p, s);
-  clha::launch_gptq(p, s);
+  {
+    StageTimer t(ctx, CLHA_STAGE_FACTOR, s);
+    clha::launch_inverse_cholesky(p, s);
+  }
+  {
+    StageTimer t(ctx, CLHA_STAGE_GPTQ, s);
+    clha::launch_gptq(p, s);
+  }
   return hip_check(ctx, "gptq_quantize");
 }
 
@@ -512,7 +581,10 @@ CLHA_API clha_status clha_inverse_cholesky(clha_ctx* ctx, int32_t n, const float
   p.lamd = L.lamd;
   p.lam = lambda_out;
   p.status = ctx->status_dev;
-  clha::launch_inverse_cholesky(p, s);
+  {
+    StageTimer t(ctx, CLHA_STAGE_FACTOR, s);
+    clha::launch_inverse_cholesky(p, s);
+  }
   return hip_check(ctx, "inverse_cholesky");
 }
 
@@ -536,9 +608,37 @@ CLHA_API clha_status clha_loss(clha_ctx* ctx, int32_t rows, int32_t cols, int32_
     return fail(ctx, CLHA_ERR_ALIGN, "loss: misaligned pointer");
   if (workspace_bytes < clha_loss_workspace_bytes(ctx, rows, cols))
     return fail(ctx, CLHA_ERR_WORKSPACE, "loss: workspace too small");
-  clha::launch_loss(rows, cols, group, W, w_dtype, codes, scales, zeros, H,
-                    static_cast<float*>(workspace), loss_out, as_stream(stream));
+  {
+    StageTimer t(ctx, CLHA_STAGE_LOSS, as_stream(stream));
+    clha::launch_loss(rows, cols, group, W, w_dtype, codes, scales, zeros, H,
+                      static_cast<float*>(workspace), loss_out, as_stream(stream));
+  }
   return hip_check(ctx, "loss");
+}
+
+CLHA_API clha_status clha_set_timing(clha_ctx* ctx, int32_t enable) {
+  if (!ctx) return CLHA_ERR_INVALID_ARG;
+  ctx->timing = enable != 0;
+  return CLHA_OK;
+}
+
+CLHA_API clha_status clha_read_timing(clha_ctx* ctx, double* ms_out, int64_t* calls_out, int32_t n) {
+  if (!ctx) return CLHA_ERR_INVALID_ARG;
+  if (n < 0 || n > CLHA_NUM_STAGES) return fail(ctx, CLHA_ERR_SHAPE, "read_timing: n must be 0..%d", CLHA_NUM_STAGES);
+  clha_status st = CLHA_OK;
+  for (auto& r : ctx->recs) {
+    float ms = 0.0f;
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess)
+      st = fail(ctx, CLHA_ERR_HIP, "read_timing: event query failed");
+    if (r.stage < n) {
+      if (ms_out) ms_out[r.stage] += ms;
+      if (calls_out) calls_out[r.stage] += 1;
+    }
+    ctx->free_events.push_back(r.a);
+    ctx->free_events.push_back(r.b);
+  }
+  ctx->recs.clear();
+  return st;
 }
 
 CLHA_API clha_status clha_sync(clha_ctx* ctx, void* stream) {

@@ -217,6 +217,28 @@ CLHA_API clha_status clha_loss(clha_ctx* ctx, int32_t rows, int32_t cols, int32_
                                float* loss_out, void* workspace, size_t workspace_bytes,
                                void* stream);
 
+/* Stages timed by the optional per-stage timers. */
+typedef enum clha_stage {
+  CLHA_STAGE_ROUTE = 0,      /* top-K routing kernel */
+  CLHA_STAGE_BUCKET = 1,     /* histogram, scan and scatter kernels */
+  CLHA_STAGE_GATHER = 2,     /* gather of each expert's rows */
+  CLHA_STAGE_SYRK = 3,       /* Gram-sum kernel (one launch per collect call) */
+  CLHA_STAGE_AGGREGATE = 4,  /* aggregation kernel */
+  CLHA_STAGE_FACTOR = 5,     /* damping, Cholesky and triangular inverse kernels */
+  CLHA_STAGE_GPTQ = 6,       /* GPTQ kernel and its loss reduction */
+  CLHA_STAGE_LOSS = 7,       /* explicit loss kernels */
+  CLHA_NUM_STAGES = 8
+} clha_stage;
+
+/* Enables (1) or disables (0) per-stage timing: each stage of each later call records a
+ * pair of hipEvents on the call's stream around its kernels.  Off by default. */
+CLHA_API clha_status clha_set_timing(clha_ctx* ctx, int32_t enable);
+
+/* Waits for every recorded event pair, adds the elapsed milliseconds of stage s to
+ * ms_out[s] and the number of recorded calls to calls_out[s] (host arrays of n entries,
+ * n <= CLHA_NUM_STAGES; either may be NULL), then forgets the records. */
+CLHA_API clha_status clha_read_timing(clha_ctx* ctx, double* ms_out, int64_t* calls_out, int32_t n);
+
 /* Waits for `stream`, then returns and clears the first latched device error
  * (NONFINITE or NOT_PD), or CLHA_OK. */
 CLHA_API clha_status clha_sync(clha_ctx* ctx, void* stream);
