@@ -21,7 +21,7 @@ using clha::GJob;
 using clha::GptqPlan;
 
 namespace clha {
-size_t gptq_smem_bytes(int block, int group);
+bool gptq_group_supported(int group);
 }
 
 struct LayerBufs {
@@ -194,6 +194,7 @@ struct GptqLayout {
   double* A;
   double* X;
   float* U;
+  float* UT;
   double* dinv;
   uint8_t* dead;
   double* lamd;
@@ -211,6 +212,7 @@ GptqLayout gptq_layout(void* ws, int n_jobs, int n_mats, int cols, int64_t wf_el
   L.A = c.take<double>((size_t)n_mats * cols * cols);
   L.X = c.take<double>((size_t)n_mats * cols * cols);
   L.U = need_u ? c.take<float>((size_t)n_mats * cols * cols) : nullptr;
+  L.UT = need_u ? c.take<float>((size_t)n_mats * cols * cols) : nullptr;
   L.dinv = c.take<double>((size_t)n_mats * cols * clha::kNb);
   L.dead = c.take<uint8_t>((size_t)n_mats * cols);
   L.lamd = c.take<double>((size_t)n_mats);
@@ -241,8 +243,9 @@ JobScan scan_jobs(int n_jobs, const clha_gptq_job* jobs, int cols) {
       id = it->second;
     }
     s.mat_of.push_back(id);
-    s.wf_elems += (int64_t)jobs[i].rows * cols;
-    s.total_slabs += (jobs[i].rows + clha::kGptqRows - 1) / clha::kGptqRows;
+    const int64_t slabs = (jobs[i].rows + clha::kGptqRows - 1) / clha::kGptqRows;
+    s.wf_elems += slabs * clha::kGptqRows * cols;   // whole 64-row slabs
+    s.total_slabs += slabs;
   }
   return s;
 }
@@ -437,8 +440,9 @@ static clha_status check_gptq_args(clha_ctx* ctx, int32_t n_jobs, const clha_gpt
   if (block != 64 && block != 128) return fail(ctx, CLHA_ERR_SHAPE, "gptq: block must be 64 or 128");
   if (cols < block || cols > 8192 || cols % block != 0)
     return fail(ctx, CLHA_ERR_SHAPE, "gptq: cols %d must be a multiple of block %d, <= 8192", cols, block);
-  if (group < 4 || group % 4 != 0 || block % group != 0)
-    return fail(ctx, CLHA_ERR_SHAPE, "gptq: group %d must be a multiple of 4 dividing block %d", group, block);
+  if (!clha::gptq_group_supported(group) || block % group != 0)
+    return fail(ctx, CLHA_ERR_SHAPE, "gptq: group %d must be one of 4, 8, 16, 32, 64, 128 and divide block %d",
+                group, block);
   if (!std::isfinite(damp) || damp < 0.0f) return fail(ctx, CLHA_ERR_INVALID_ARG, "gptq: bad damp");
   for (int i = 0; i < n_jobs; ++i) {
     const clha_gptq_job& j = jobs[i];
@@ -501,7 +505,7 @@ CLHA_API clha_status clha_gptq_quantize(clha_ctx* ctx, int32_t n_jobs, const clh
     g.slab_base = slab_base;
     g.n_slabs = (j.rows + clha::kGptqRows - 1) / clha::kGptqRows;
     hj[i] = g;
-    wf_off += (int64_t)j.rows * cols;
+    wf_off += (int64_t)g.n_slabs * clha::kGptqRows * cols;
     slab_base += g.n_slabs;
   }
   std::memcpy(host.data() + up256(sizeof(GJob) * n_jobs), js.mats.data(), sizeof(float*) * n_mats);
@@ -524,6 +528,7 @@ CLHA_API clha_status clha_gptq_quantize(clha_ctx* ctx, int32_t n_jobs, const clh
   p.A = L.A;
   p.X = L.X;
   p.U = L.U;
+  p.UT = L.UT;
   p.dinv = L.dinv;
   p.dead = L.dead;
   p.lamd = L.lamd;
@@ -576,6 +581,7 @@ CLHA_API clha_status clha_inverse_cholesky(clha_ctx* ctx, int32_t n, const float
   p.A = L.A;
   p.X = L.X;
   p.U = U_out;
+  p.UT = nullptr;
   p.dinv = L.dinv;
   p.dead = dead_out ? dead_out : L.dead;
   p.lamd = L.lamd;

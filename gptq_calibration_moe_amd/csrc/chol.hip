@@ -261,13 +261,15 @@ __global__ __launch_bounds__(256) void chol_update_kernel(double* __restrict__ A
 __global__ __launch_bounds__(256) void trtri_row_kernel(const double* __restrict__ Aall, int c, int i,
                                                         const double* __restrict__ dinv,
                                                         double* __restrict__ Xall,
-                                                        float* __restrict__ Uall) {
+                                                        float* __restrict__ Uall,
+                                                        float* __restrict__ UTall) {
   __shared__ double Ls[kNb][kNb + 1];
   __shared__ double Xs[kNb][kNb + 1];
   const int m = blockIdx.y, j = blockIdx.x;
   const double* A = Aall + (int64_t)m * c * c;
   double* X = Xall + (int64_t)m * c * c;
   float* U = Uall + (int64_t)m * c * c;
+  float* UT = UTall ? UTall + (int64_t)m * c * c : nullptr;
   const double* Di = dinv + ((int64_t)m * (c / kNb) + i) * kNb * kNb;
   const int64_t i0 = (int64_t)i * kNb, j0 = (int64_t)j * kNb;
   if (j == i) {
@@ -276,6 +278,9 @@ __global__ __launch_bounds__(256) void trtri_row_kernel(const double* __restrict
       const double v = cc <= r ? Di[idx] : 0.0;
       X[(i0 + r) * c + j0 + cc] = v;
       if (cc <= r) U[(c - 1 - (i0 + r)) * c + (c - 1 - (j0 + cc))] = (float)v;
+      // U^T: element (c-1-(j0+cc), c-1-(i0+r)); consecutive threads step r
+      const int rr = idx & 63, c2 = idx >> 6;
+      if (UT && c2 <= rr) UT[(c - 1 - (j0 + c2)) * c + (c - 1 - (i0 + rr))] = (float)Di[rr * kNb + c2];
     }
     return;
   }
@@ -304,6 +309,7 @@ __global__ __launch_bounds__(256) void trtri_row_kernel(const double* __restrict
   __syncthreads();
   t.zero();
   t.mac<false>(Ls, Xs, -1.0);
+  __syncthreads();
 #pragma unroll
   for (int x = 0; x < 2; ++x)
 #pragma unroll
@@ -314,7 +320,15 @@ __global__ __launch_bounds__(256) void trtri_row_kernel(const double* __restrict
         const double v = t.acc[x][y][r];
         X[(i0 + row) * c + j0 + col] = v;
         U[(c - 1 - (i0 + row)) * c + (c - 1 - (j0 + col))] = (float)v;
+        Xs[row][col] = v;
       }
+  if (UT) {
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < kNb * kNb; idx += 256) {
+      const int rr = idx & 63, cc = idx >> 6;   // consecutive threads step the U^T column
+      UT[(c - 1 - (j0 + cc)) * c + (c - 1 - (i0 + rr))] = (float)Xs[rr][cc];
+    }
+  }
 }
 
 void launch_inverse_cholesky(const GptqPlan& p, hipStream_t s) {
@@ -333,7 +347,7 @@ void launch_inverse_cholesky(const GptqPlan& p, hipStream_t s) {
   }
   for (int i = 0; i < nbk; ++i)
     hipLaunchKernelGGL(trtri_row_kernel, dim3(i + 1, p.n_mats), dim3(256), 0, s, p.A, c, i, p.dinv,
-                       p.X, p.U);
+                       p.X, p.U, p.UT);
 }
 
 }  // namespace clha

@@ -6,41 +6,31 @@
 // (the bit width is per job).  The GPTQ steps follow Frantar et al. (ICLR 2023):
 // for column j, with U the upper Cholesky factor of Hd^-1,
 //   err_j = (w_j - dequant(quant(w_j))) / U_jj,   w_k -= err_j U_jk  (k > j),
-// applied eagerly inside a block of B columns and lazily (one rank-B product)
+// applied eagerly inside a block of columns and lazily (one rank-64 product)
 // to the columns after the block.  The grid of each (row, group) is fitted at
 // the group's first column on the weights updated so far.
 //
-// Work decomposition: one workgroup per (job, slab of 64 rows); rows are
-// independent given U, so slabs never communicate.  Per block:
-//   * the slab's B columns are staged column-major in LDS (pitch 65), U's
-//     diagonal block in LDS;
-//   * column loop: 64 threads quantize the column (one row each; codes, scale
-//     and zero are decided in fp32 with IEEE division and rint), all 256
-//     threads apply the rank-1 update to the rest of the block;
-//   * the block's errors then update every later column of the slab's fp32
-//     working copy through U[block, later] on the fp32 matrix cores
-//     (v_mfma_f32_32x32x2f32), 64 columns at a time.
-// The loss is assembled from the OBS identity: sum_j err_j^2 equals
-// tr[(Wq - W) Hd (Wq - W)^T], so the undamped loss is
-// sum err^2 - lambda ||Wq - W||^2 (W after zeroing dead columns).
+// Work decomposition.  Rows are independent given U, so one wavefront owns a
+// slab of 64 rows (one workgroup = one wave) and one thread owns one row:
+//   * the row's current 64-column block lives in 64 registers; the column loop
+//     is fully unrolled, so quantization, the error and the rank-1 update of
+//     the rest of the block are register arithmetic with no barrier -- the
+//     U values of column j are the same for every row (uniform loads);
+//   * codes, scales and zero points are decided in fp32 with IEEE division and
+//     round-half-to-even, exactly as the definition states;
+//   * the block's 64x64 errors then update every later column of the slab's
+//     fp32 working copy through U[block, later] on the fp32 matrix cores
+//     (v_mfma_f32_32x32x2f32) in 64-row x 32-column tiles.
+// The loss uses the OBS identity: sum_j err_j^2 = tr[(Wq - W) Hd (Wq - W)^T],
+// so the undamped loss is sum err^2 - lambda ||Wq - W||^2 (W after zeroing
+// dead columns); ||Wq - W||^2 is a separate coalesced pass over the outputs.
 #include "kernels.h"
 
 namespace clha {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kP = kGptqRows + 1;    // LDS pitch of a staged column
-constexpr int kCodePitch = 68;       // bytes per staged code column
-
-struct GptqSmem {
-  static size_t bytes(int B, int group) {
-    return (size_t)B * kP * 4            // W1 / errors
-         + (size_t)B * B * 4             // U diagonal block, later a U tile [B][64]
-         + (size_t)B * kCodePitch        // codes
-         + 2 * 4 * kGptqRows * 4         // group min/max partials
-         + 2 * (size_t)(B / group) * kGptqRows * 4;  // grids of the block's groups
-  }
-};
+constexpr int kRB = 64;             // register block: columns held per thread
 
 __device__ __forceinline__ float load_w(const void* W, int dtype, int64_t i) {
   if (dtype == 1) {
@@ -50,18 +40,144 @@ __device__ __forceinline__ float load_w(const void* W, int dtype, int64_t i) {
   return reinterpret_cast<const float*>(W)[i];
 }
 
-__global__ __launch_bounds__(256) void gptq_kernel(GptqPlan p) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  const int B = p.block, c = p.cols, group = p.group;
-  float* W1 = reinterpret_cast<float*>(smem);
-  float* Ub = W1 + B * kP;
-  unsigned char* cs = reinterpret_cast<unsigned char*>(Ub + B * B);
-  float* redmn = reinterpret_cast<float*>(cs + B * kCodePitch);
-  float* redmx = redmn + 4 * kGptqRows;
-  float* gs = redmx + 4 * kGptqRows;
-  float* gz = gs + (B / group) * kGptqRows;
+__device__ __forceinline__ void fit_grid(float xmin, float xmax, float fmaxq, float& s, float& z) {
+  xmin = fminf(xmin, 0.0f);
+  xmax = fmaxf(xmax, 0.0f);
+  if (xmin == 0.0f && xmax == 0.0f) {
+    xmin = -1.0f;
+    xmax = 1.0f;
+  }
+  s = __fdiv_rn(__fsub_rn(xmax, xmin), fmaxq);
+  z = rintf(__fdiv_rn(-xmin, s));
+}
 
-  // job of this slab
+// U is read-only while the GPTQ kernel runs; reading it through the constant
+// address space lets the compiler fetch the per-column U values (identical for
+// every row of the wave) with scalar loads into SGPRs.
+typedef const __attribute__((address_space(4))) float* const_fptr;
+
+struct ColCtx {
+  const_fptr ublk;                  // U[i1][i1]: the block's diagonal U block, row stride c
+  int c;
+  float fmaxq;
+  float* scales;
+  uint8_t* zeros;
+  int64_t grid0;                    // index of the block's first group in scales/zeros
+  bool live;
+};
+
+// Column JJ of the register block (the recursion makes every register index a
+// compile-time constant, so the block stays in registers).
+template <int G, int JJ>
+__device__ __forceinline__ void column_steps(float (&w)[kRB], uint32_t (&packed)[kRB / 4], float& s,
+                                             float& z, double& obs, const ColCtx& cx) {
+  if constexpr (G <= kRB && (JJ % G) == 0) {
+    float mn = w[JJ], mx = w[JJ];
+#pragma unroll
+    for (int u = 1; u < G; ++u) {
+      mn = fminf(mn, w[JJ + u]);
+      mx = fmaxf(mx, w[JJ + u]);
+    }
+    fit_grid(mn, mx, cx.fmaxq, s, z);
+    if (cx.live) {
+      cx.scales[cx.grid0 + JJ / G] = s;
+      cx.zeros[cx.grid0 + JJ / G] = (uint8_t)z;
+    }
+  }
+  const_fptr urow = cx.ublk + (int64_t)JJ * cx.c;
+  const float x = w[JJ];
+  float q = rintf(__fdiv_rn(x, s)) + z;
+  q = fminf(fmaxf(q, 0.0f), cx.fmaxq);
+  const float what = __fmul_rn(s, __fsub_rn(q, z));
+  const float e = __fdiv_rn(__fsub_rn(x, what), urow[JJ]);
+  packed[JJ >> 2] |= (uint32_t)q << (8 * (JJ & 3));
+  obs += (double)e * (double)e;
+  w[JJ] = e;
+#pragma unroll
+  for (int kk = JJ + 1; kk < kRB; ++kk) w[kk] = fmaf(-e, urow[kk], w[kk]);
+  if constexpr (JJ + 1 < kRB) column_steps<G, JJ + 1>(w, packed, s, z, obs, cx);
+}
+
+// One 64-row x 32-column tile of the far update: the A operands (U) and the
+// current W values, loaded ahead of use.
+struct TileBuf {
+  float4 u[kRB / 8];          // A operands: U^T row jt+lc, columns i1+32kh .. +31
+  float4 wa[4], wb[4];        // W rows lc and 32+lc, columns jt+8q+4kh .. +3
+  __device__ __forceinline__ void load(const float* UT, const float* wr0, const float* wr1, int c,
+                                       int jt, int ucol) {
+    const float* ut = UT + (int64_t)jt * c + ucol;
+#pragma unroll
+    for (int m = 0; m < kRB / 8; ++m) u[m] = *reinterpret_cast<const float4*>(ut + 4 * m);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      wa[q] = *reinterpret_cast<const float4*>(wr0 + jt + 8 * q);
+      wb[q] = *reinterpret_cast<const float4*>(wr1 + jt + 8 * q);
+    }
+  }
+  __device__ __forceinline__ void apply(const float (&b0)[kRB / 2], const float (&b1)[kRB / 2],
+                                        float* wr0, float* wr1, int jt) {
+    f32x16 acc0, acc1;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      acc0[4 * q] = wa[q].x; acc0[4 * q + 1] = wa[q].y; acc0[4 * q + 2] = wa[q].z; acc0[4 * q + 3] = wa[q].w;
+      acc1[4 * q] = wb[q].x; acc1[4 * q + 1] = wb[q].y; acc1[4 * q + 2] = wb[q].z; acc1[4 * q + 3] = wb[q].w;
+    }
+#pragma unroll
+    for (int st = 0; st < kRB / 2; ++st) {
+      const float a = (&u[st >> 2].x)[st & 3];
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b0[st], acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b1[st], acc1, 0, 0, 0);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      *reinterpret_cast<float4*>(wr0 + jt + 8 * q) =
+          make_float4(acc0[4 * q], acc0[4 * q + 1], acc0[4 * q + 2], acc0[4 * q + 3]);
+      *reinterpret_cast<float4*>(wr1 + jt + 8 * q) =
+          make_float4(acc1[4 * q], acc1[4 * q + 1], acc1[4 * q + 2], acc1[4 * q + 3]);
+    }
+  }
+};
+
+// Wf[:, jt0:] -= E U[i1:i1+64, jt0:] for one 64-row slab, E = the block's
+// errors (thread-per-row in e[]).  Transposed product on the fp32 matrix cores:
+// C[i][j] = sum_k U[i1+k][jt+i] E[j][k] is the update of W[row j][column jt+i].
+// With U as the A operand (read from U^T, so a lane's operands are contiguous)
+// and -E as the B operand, each lane's 16 results are 4 runs of 4 consecutive
+// columns of one row.  MFMA step st contracts k = st (lanes 0..31) and
+// k = st+32 (lanes 32..63); the B operands come from the row-owner registers by
+// one cross-half shuffle per step.  Tiles are double-buffered: the next tile's
+// U and W load while the current tile's products run.
+__device__ __forceinline__ void far_update(const float (&e)[kRB], float* Wf, const float* UT, int c,
+                                           int i1, int jt0, int lane) {
+  const int kh = lane >> 5, lc = lane & 31;
+  float b0[kRB / 2], b1[kRB / 2];   // B operands for rows 0..31 and 32..63
+#pragma unroll
+  for (int st = 0; st < kRB / 2; ++st) {
+    const float lo = e[st], hi = e[st + kRB / 2];
+    const float lo_x = __shfl_xor(lo, 32), hi_x = __shfl_xor(hi, 32);
+    b0[st] = -(kh == 0 ? lo : hi_x);      // row lc:    k = st (lanes < 32), st+32 (lanes >= 32)
+    b1[st] = -(kh == 0 ? lo_x : hi);      // row 32+lc
+  }
+  const float* utl = UT + (int64_t)lc * c;            // U^T row jt+lc
+  const int ucol = i1 + (kRB / 2) * kh;
+  float* wr0 = Wf + (int64_t)lc * c + 4 * kh;          // rows lc and 32+lc, columns jt+8q+4kh
+  float* wr1 = wr0 + (int64_t)32 * c;
+  TileBuf x, y;
+  x.load(utl, wr0, wr1, c, jt0, ucol);
+#pragma unroll 1
+  for (int jt = jt0; jt < c; jt += 64) {
+    const bool second = jt + 32 < c;
+    if (second) y.load(utl, wr0, wr1, c, jt + 32, ucol);
+    x.apply(b0, b1, wr0, wr1, jt);
+    if (!second) break;
+    if (jt + 64 < c) x.load(utl, wr0, wr1, c, jt + 64, ucol);
+    y.apply(b0, b1, wr0, wr1, jt + 32);
+  }
+}
+
+template <int G>
+__global__ __launch_bounds__(64) void gptq_kernel(GptqPlan p) {
+  const int c = p.cols;
   int lo = 0, hi = p.n_jobs;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
@@ -71,163 +187,120 @@ __global__ __launch_bounds__(256) void gptq_kernel(GptqPlan p) {
   const int slab = blockIdx.x - job.slab_base;
   const int row0 = slab * kGptqRows;
   const int nrows = min(kGptqRows, job.rows - row0);
-  const float* U = p.U + (int64_t)job.mat * c * c;
-  const uint8_t* dead = p.dead + (int64_t)job.mat * c;
+  const float* __restrict__ U = p.U + (int64_t)job.mat * c * c;
+  const float* __restrict__ UT = p.UT + (int64_t)job.mat * c * c;
+  const uint8_t* __restrict__ dead = p.dead + (int64_t)job.mat * c;
   float* Wf = p.wf + job.wf_off + (int64_t)row0 * c;
-  const int maxq = (1 << job.bits) - 1;
-  const float fmaxq = (float)maxq;
-  const int ngroups_row = c / group;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const float fmaxq = (float)((1 << job.bits) - 1);
+  const int ngroups_row = c / G;
+  const int lane = threadIdx.x;
+  const bool live = lane < nrows;
 
-  // fp32 working copy of the slab, dead columns zeroed
-  for (int64_t idx = tid; idx < (int64_t)nrows * c; idx += 256) {
+  // fp32 working copy of the slab (64 rows; rows past the matrix are zero),
+  // dead columns zeroed (coalesced)
+  for (int64_t idx = lane; idx < (int64_t)kGptqRows * c; idx += 64) {
     const int col = (int)(idx % c);
-    const float v = load_w(job.W, job.dtype, (int64_t)row0 * c + idx);
+    const bool in = idx < (int64_t)nrows * c;
+    const float v = in ? load_w(job.W, job.dtype, (int64_t)row0 * c + idx) : 0.0f;
     Wf[idx] = dead[col] ? 0.0f : v;
   }
   __threadfence_block();
   __syncthreads();
 
-  double obs = 0.0, d2 = 0.0;
-  float s = 1.0f, z = 0.0f;   // grid of the current group (threads < 64, row = tid)
+  double obs = 0.0;
+  float s = 1.0f, z = 0.0f;
+  float* myrow = Wf + (int64_t)lane * c;
 
-  for (int i1 = 0; i1 < c; i1 += B) {
-    for (int idx = tid; idx < kGptqRows * B; idx += 256) {
-      const int r = idx / B, col = idx - r * B;
-      W1[col * kP + r] = r < nrows ? Wf[(int64_t)r * c + i1 + col] : 0.0f;
-    }
-    for (int idx = tid; idx < B * B; idx += 256) {
-      const int a = idx / B, b = idx - a * B;
-      Ub[idx] = b >= a ? U[(int64_t)(i1 + a) * c + i1 + b] : 0.0f;
-    }
-    __syncthreads();
-
-    for (int jj = 0; jj < B; ++jj) {
-      const int j = i1 + jj;
-      if (j % group == 0) {
-        const int r = lane, part = wave, q = group / 4;
-        float mn = INFINITY, mx = -INFINITY;
-        for (int u = 0; u < q; ++u) {
-          const float v = W1[(jj + part * q + u) * kP + r];
-          mn = fminf(mn, v);
-          mx = fmaxf(mx, v);
-        }
-        redmn[part * kGptqRows + r] = mn;
-        redmx[part * kGptqRows + r] = mx;
-        __syncthreads();
-        if (tid < kGptqRows) {
-          float xmin = fminf(fminf(redmn[r], redmn[kGptqRows + r]),
-                             fminf(redmn[2 * kGptqRows + r], redmn[3 * kGptqRows + r]));
-          float xmax = fmaxf(fmaxf(redmx[r], redmx[kGptqRows + r]),
-                             fmaxf(redmx[2 * kGptqRows + r], redmx[3 * kGptqRows + r]));
-          xmin = fminf(xmin, 0.0f);
-          xmax = fmaxf(xmax, 0.0f);
-          if (xmin == 0.0f && xmax == 0.0f) {
-            xmin = -1.0f;
-            xmax = 1.0f;
-          }
-          s = __fdiv_rn(__fsub_rn(xmax, xmin), fmaxq);
-          z = rintf(__fdiv_rn(-xmin, s));
-          const int gb = jj / group;
-          gs[gb * kGptqRows + r] = s;
-          gz[gb * kGptqRows + r] = z;
-          if (r < nrows) {
-            const int64_t o = (int64_t)(row0 + r) * ngroups_row + j / group;
-            job.scales[o] = s;
-            job.zeros[o] = (uint8_t)z;
-          }
-        }
-      }
-      if (tid < kGptqRows) {
-        const float w = W1[jj * kP + tid];
-        float q = rintf(__fdiv_rn(w, s)) + z;
-        q = fminf(fmaxf(q, 0.0f), fmaxq);
-        const float what = __fmul_rn(s, __fsub_rn(q, z));
-        const float e = __fdiv_rn(__fsub_rn(w, what), Ub[jj * B + jj]);
-        cs[jj * kCodePitch + tid] = (unsigned char)q;
-        W1[jj * kP + tid] = e;
-        obs += (double)e * (double)e;
-      }
-      __syncthreads();
-      {
-        const int r = lane;
-        const float e = W1[jj * kP + r];
-        const float* urow = Ub + jj * B;
-        for (int kk = jj + 1 + wave; kk < B; kk += 4) W1[kk * kP + r] -= e * urow[kk];
-      }
-      __syncthreads();
-    }
-
-    // codes of the block, and ||Wq - W||^2 over it
-    for (int idx = tid; idx < kGptqRows * (B / 4); idx += 256) {
-      const int r = idx / (B / 4), c4 = (idx - r * (B / 4)) * 4;
-      if (r < nrows) {
-        uint32_t packed = 0;
+  for (int i1 = 0; i1 < c; i1 += kRB) {
+    float w[kRB];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int col = c4 + u;
-          const unsigned q = cs[col * kCodePitch + r];
-          packed |= q << (8 * u);
-          const int gb = col / group;
-          const float what = __fmul_rn(gs[gb * kGptqRows + r], __fsub_rn((float)q, gz[gb * kGptqRows + r]));
-          const float w0 = dead[i1 + col] ? 0.0f : load_w(job.W, job.dtype, (int64_t)(row0 + r) * c + i1 + col);
-          const double dd = (double)what - (double)w0;
-          d2 += dd * dd;
-        }
-        *reinterpret_cast<uint32_t*>(job.codes + (int64_t)(row0 + r) * c + i1 + c4) = packed;
+    for (int q = 0; q < kRB / 4; ++q) {
+      const float4 v = *reinterpret_cast<const float4*>(myrow + i1 + 4 * q);
+      w[4 * q] = v.x;
+      w[4 * q + 1] = v.y;
+      w[4 * q + 2] = v.z;
+      w[4 * q + 3] = v.w;
+    }
+    if (G > kRB && (i1 % G) == 0) {
+      // group wider than the register block: its other columns are current in Wf
+      float mn = INFINITY, mx = -INFINITY;
+#pragma unroll
+      for (int u = 0; u < kRB; ++u) {
+        mn = fminf(mn, w[u]);
+        mx = fmaxf(mx, w[u]);
       }
+      for (int u = kRB; u < G; u += 4) {
+        const float4 v = *reinterpret_cast<const float4*>(myrow + i1 + u);
+        mn = fminf(fminf(mn, v.x), fminf(fminf(v.y, v.z), v.w));
+        mx = fmaxf(fmaxf(mx, v.x), fmaxf(fmaxf(v.y, v.z), v.w));
+      }
+      fit_grid(mn, mx, fmaxq, s, z);
+      if (live) {
+        const int64_t o = (int64_t)(row0 + lane) * ngroups_row + i1 / G;
+        job.scales[o] = s;
+        job.zeros[o] = (uint8_t)z;
+      }
+    }
+    uint32_t packed[kRB / 4];
+#pragma unroll
+    for (int q = 0; q < kRB / 4; ++q) packed[q] = 0u;
+    ColCtx cx{(const_fptr)(U + (int64_t)i1 * c + i1), c, fmaxq, job.scales, job.zeros,
+              (int64_t)(row0 + lane) * ngroups_row + i1 / G, live};
+    column_steps<G, 0>(w, packed, s, z, obs, cx);
+    if (live) {
+      uint8_t* cp = job.codes + (int64_t)(row0 + lane) * c + i1;
+#pragma unroll
+      for (int q = 0; q < kRB / 16; ++q)
+        *reinterpret_cast<uint4*>(cp + 16 * q) =
+            make_uint4(packed[4 * q], packed[4 * q + 1], packed[4 * q + 2], packed[4 * q + 3]);
     }
 
-    // lazy update of the later columns: Wf[:, i2:] -= E1 U[i1:i2, i2:]
-    const int i2 = i1 + B;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int arow = wm * 32 + (lane & 31), kh = lane >> 5;
-    for (int jt = i2; jt < c; jt += 64) {
+    // lazy update of the later columns: Wf[:, i2:] -= E U[i1:i2, i2:]
+    const int i2 = i1 + kRB;
+    if (i2 < c) {
+      far_update(w, Wf, UT, c, i1, i2, lane);
+      __threadfence_block();
       __syncthreads();
-      for (int idx = tid; idx < B * 64; idx += 256) {
-        const int k = idx >> 6, jc = idx & 63;
-        Ub[idx] = U[(int64_t)(i1 + k) * c + jt + jc];
-      }
-      __syncthreads();
-      const int col = jt + wn * 32 + (lane & 31);
-      f32x16 acc;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = wm * 32 + 8 * (r >> 2) + 4 * kh + (r & 3);
-        acc[r] = row < nrows ? Wf[(int64_t)row * c + col] : 0.0f;
-      }
-      for (int k = 0; k < B; k += 2) {
-        const float a = -W1[(k + kh) * kP + arow];
-        const float b = Ub[(k + kh) * 64 + wn * 32 + (lane & 31)];
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc, 0, 0, 0);
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = wm * 32 + 8 * (r >> 2) + 4 * kh + (r & 3);
-        if (row < nrows) Wf[(int64_t)row * c + col] = acc[r];
-      }
     }
-    __threadfence_block();
-    __syncthreads();
   }
+  double* part = reinterpret_cast<double*>(p.partials) + 2 * (int64_t)blockIdx.x;
+  // sum of err^2 over the slab's live rows, reduced in a fixed lane order
+  double v = live ? obs : 0.0;
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_down(v, off);
+  if (lane == 0) part[0] = v;
+}
 
-  // per-slab partial sums, reduced in a fixed order
-  __shared__ double red[2][256];
-  red[0][tid] = (tid < nrows) ? obs : 0.0;
-  red[1][tid] = d2;
+// ||Wq - W||^2 per slab (W with dead columns zeroed), coalesced over the outputs.
+__global__ __launch_bounds__(256) void gptq_dist_kernel(GptqPlan p) {
+  __shared__ double red[256];
+  const int c = p.cols, group = p.group;
+  int lo = 0, hi = p.n_jobs;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (p.jobs[mid].slab_base <= (int)blockIdx.x) lo = mid; else hi = mid;
+  }
+  const GJob job = p.jobs[lo];
+  const int row0 = (blockIdx.x - job.slab_base) * kGptqRows;
+  const int nrows = min(kGptqRows, job.rows - row0);
+  const uint8_t* dead = p.dead + (int64_t)job.mat * c;
+  const int ng = c / group;
+  double acc = 0.0;
+  for (int64_t idx = threadIdx.x; idx < (int64_t)nrows * c; idx += 256) {
+    const int r = (int)(idx / c), col = (int)(idx - (int64_t)r * c);
+    const int64_t e = (int64_t)(row0 + r) * c + col;
+    const int64_t gi = (int64_t)(row0 + r) * ng + col / group;
+    const float what = __fmul_rn(job.scales[gi], __fsub_rn((float)job.codes[e], (float)job.zeros[gi]));
+    const float w0 = dead[col] ? 0.0f : load_w(job.W, job.dtype, e);
+    const double dd = (double)what - (double)w0;
+    acc += dd * dd;
+  }
+  red[threadIdx.x] = acc;
   __syncthreads();
   for (int st = 128; st > 0; st >>= 1) {
-    if (tid < st) {
-      red[0][tid] += red[0][tid + st];
-      red[1][tid] += red[1][tid + st];
-    }
+    if (threadIdx.x < st) red[threadIdx.x] += red[threadIdx.x + st];
     __syncthreads();
   }
-  if (tid == 0) {
-    double* part = reinterpret_cast<double*>(p.partials) + 2 * (int64_t)blockIdx.x;
-    part[0] = red[0][0];
-    part[1] = red[1][0];
-  }
+  if (threadIdx.x == 0) reinterpret_cast<double*>(p.partials)[2 * (int64_t)blockIdx.x + 1] = red[0];
 }
 
 __global__ void gptq_finish_kernel(GptqPlan p) {
@@ -242,14 +315,22 @@ __global__ void gptq_finish_kernel(GptqPlan p) {
   job.loss[0] = (float)(obs - p.lamd[job.mat] * d2);
 }
 
-void launch_gptq(const GptqPlan& p, hipStream_t s) {
-  const size_t smem = GptqSmem::bytes(p.block, p.group);
-  hipFuncSetAttribute(reinterpret_cast<const void*>(gptq_kernel),
-                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-  hipLaunchKernelGGL(gptq_kernel, dim3(p.total_slabs), dim3(256), smem, s, p);
-  hipLaunchKernelGGL(gptq_finish_kernel, dim3(p.n_jobs), dim3(64), 0, s, p);
+bool gptq_group_supported(int group) {
+  return group == 4 || group == 8 || group == 16 || group == 32 || group == 64 || group == 128;
 }
 
-size_t gptq_smem_bytes(int block, int group) { return GptqSmem::bytes(block, group); }
+void launch_gptq(const GptqPlan& p, hipStream_t s) {
+  const dim3 grid(p.total_slabs), blk(64);
+  switch (p.group) {
+    case 4: hipLaunchKernelGGL(gptq_kernel<4>, grid, blk, 0, s, p); break;
+    case 8: hipLaunchKernelGGL(gptq_kernel<8>, grid, blk, 0, s, p); break;
+    case 16: hipLaunchKernelGGL(gptq_kernel<16>, grid, blk, 0, s, p); break;
+    case 32: hipLaunchKernelGGL(gptq_kernel<32>, grid, blk, 0, s, p); break;
+    case 64: hipLaunchKernelGGL(gptq_kernel<64>, grid, blk, 0, s, p); break;
+    default: hipLaunchKernelGGL(gptq_kernel<128>, grid, blk, 0, s, p); break;
+  }
+  hipLaunchKernelGGL(gptq_dist_kernel, dim3(p.total_slabs), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(gptq_finish_kernel, dim3(p.n_jobs), dim3(64), 0, s, p);
+}
 
 }  // namespace clha

@@ -82,6 +82,7 @@ struct GptqPlan {
   double* A;                 // device [n_mats][cols][cols]  reversed damped H, then its Cholesky factor
   double* X;                 // device [n_mats][cols][cols]  inverse of that factor
   float* U;                  // device [n_mats][cols][cols]  upper factor of Hd^-1 (fp32)
+  float* UT;                 // device [n_mats][cols][cols]  its transpose (may be null when only U is wanted)
   double* dinv;              // device [n_mats][cols/kNb][kNb][kNb] inverses of L's diagonal blocks
   uint8_t* dead;             // device [n_mats][cols]
   double* lamd;              // device [n_mats] damping lambda

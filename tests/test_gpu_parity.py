@@ -278,6 +278,9 @@ def _gptq_case(seed, rows, c, bits, group, dead=(), w_dtype="f32", spread=3.0):
     (52, 130, 256, 4, 32, 64, "f32", ()),            # block 64, small groups
     (53, 96, 512, 2, 128, 128, "bf16", (0, 300)),
     (54, 64, 128, 8, 128, 128, "f32", ()),           # 8 bits, a single block
+    (55, 96, 256, 2, 16, 128, "f32", ()),            # small groups
+    (56, 70, 128, 3, 4, 64, "bf16", (100,)),         # group 4, ragged rows, dead column
+    (57, 300, 1024, 2, 128, 128, "bf16", ()),        # 5 slabs, 16 register blocks
 ])
 def test_gptq_stage(seed, rows, c, bits, group, block, wdt, dead):
     import gptq_calibration_moe_amd as clha
