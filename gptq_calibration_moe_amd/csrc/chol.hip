@@ -22,10 +22,11 @@
 //   diag_stats      dead columns (H_ii == 0) and lambda = damp * mean(diag),
 //                   taking H_ii := 1 on dead columns first
 //   build_reversed  A = J (H + fixes + lambda I) J, lower triangle, fp64
-//   per 64-column block step k:
-//     potrf_panel   factor the diagonal block (kept only as its inverse) and
-//                   solve the panel below it
-//     chol_update   trailing lower update A[i][j] -= L[i][k] L[j][k]^T
+//   left-looking Cholesky, per 64-column block step k:
+//     chol_left     T_i = A[i][k] - sum_{m<k} L[i][m] L[k][m]^T for block rows i >= k
+//                   (a chunked fp64 MFMA product, next chunk prefetched)
+//     chol_diag     L_kk = chol(T_k) and its inverse Dinv_k (one workgroup per matrix)
+//     chol_panel    L[i][k] = T_i Dinv_k^T for i > k
 //   per block row i:
 //     trtri_row     X[i][j] = -Linv_ii sum_m L[i][m] X[m][j] (X = L^-1, fp64),
 //                   and U at the reversed position in fp32
@@ -140,17 +141,95 @@ __global__ __launch_bounds__(256) void build_reversed_kernel(const float* const*
   }
 }
 
-// ---------------------------------------------------------------- blocked Cholesky
+// ---------------------------------------------------------------- chunked 64x64 products
+// Sum over chunks m of P_m Q_m (64x64 fp64 blocks read from global memory):
+// each thread prefetches its 16+16 elements of the next chunk into registers
+// while the matrix cores work on the current chunk in LDS.
+struct ChunkPipe {
+  double ra[16], rb[16];
+  __device__ __forceinline__ void fetch(const double* P, int64_t ldp, const double* Q, int64_t ldq) {
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int idx = threadIdx.x + 256 * u, r = idx >> 6, cc = idx & 63;
+      ra[u] = P[r * ldp + cc];
+      rb[u] = Q[r * ldq + cc];
+    }
+  }
+  __device__ __forceinline__ void stage(double (*As)[kNb + 1], double (*Bs)[kNb + 1]) {
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int idx = threadIdx.x + 256 * u, r = idx >> 6, cc = idx & 63;
+      As[r][cc] = ra[u];
+      Bs[r][cc] = rb[u];
+    }
+  }
+};
 
-__device__ void factor_block(double (*L)[kNb + 1], int* status) {
+// ---------------------------------------------------------------- left-looking Cholesky
+// Step k, block row i >= k:  T_i = A[i][k] - sum_{m<k} L[i][m] L[k][m]^T, stored over A[i][k].
+__global__ __launch_bounds__(256) void chol_left_kernel(double* __restrict__ Aall, int c, int k) {
+  __shared__ double As[kNb][kNb + 1];
+  __shared__ double Bs[kNb][kNb + 1];
+  const int m = blockIdx.y, i = k + blockIdx.x;
+  const bool diag = i == k;
+  double* A = Aall + (int64_t)m * c * c;
+  const int64_t i0 = (int64_t)i * kNb, k0 = (int64_t)k * kNb;
+  Tile64 t;
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = Tile64::row(x, r), col = Tile64::col(y);
+        t.acc[x][y][r] = (!diag || col <= row) ? A[(i0 + row) * c + k0 + col] : 0.0;
+      }
+  if (k > 0) {
+    ChunkPipe pipe;
+    pipe.fetch(A + i0 * c, c, A + k0 * c, c);
+    for (int mm = 0; mm < k; ++mm) {
+      __syncthreads();
+      pipe.stage(As, Bs);
+      __syncthreads();
+      if (mm + 1 < k) pipe.fetch(A + i0 * c + (mm + 1) * kNb, c, A + k0 * c + (mm + 1) * kNb, c);
+      t.mac<true>(As, Bs, -1.0);
+    }
+  }
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = Tile64::row(x, r), col = Tile64::col(y);
+        if (!diag || col <= row) A[(i0 + row) * c + k0 + col] = t.acc[x][y][r];
+      }
+}
+
+// Step k: L_kk = chol(T_k) and Dinv_k = L_kk^-1 (one workgroup per matrix).
+__global__ __launch_bounds__(256) void chol_diag_kernel(const double* __restrict__ Aall, int c, int k,
+                                                        double* __restrict__ dinv,
+                                                        int* __restrict__ status) {
+  __shared__ double L[kNb][kNb + 1];
+  __shared__ double X[kNb][kNb + 1];
+  const int m = blockIdx.x;
+  const double* A = Aall + (int64_t)m * c * c;
+  const int64_t k0 = (int64_t)k * kNb;
+  for (int idx = threadIdx.x; idx < kNb * kNb; idx += 256) {
+    const int r = idx >> 6, cc = idx & 63;
+    L[r][cc] = cc <= r ? A[(k0 + r) * c + k0 + cc] : 0.0;
+    X[r][cc] = r == cc ? 1.0 : 0.0;
+  }
+  __syncthreads();
+  // right-looking factorisation of the 64x64 block
   for (int j = 0; j < kNb; ++j) {
     if (threadIdx.x == 0) {
-      double p = L[j][j];
-      if (!(p > 0.0)) {
+      double pv = L[j][j];
+      if (!(pv > 0.0)) {
         atomicOr(status, kStatusNotPd);
-        p = 1.0;
+        pv = 1.0;
       }
-      L[j][j] = sqrt(p);
+      L[j][j] = sqrt(pv);
     }
     __syncthreads();
     if (threadIdx.x > j && threadIdx.x < kNb) L[threadIdx.x][j] = L[threadIdx.x][j] / L[j][j];
@@ -161,103 +240,51 @@ __device__ void factor_block(double (*L)[kNb + 1], int* status) {
     }
     __syncthreads();
   }
-}
-
-__global__ __launch_bounds__(256) void potrf_panel_kernel(double* __restrict__ Aall, int c, int k,
-                                                          double* __restrict__ dinv,
-                                                          int* __restrict__ status) {
-  __shared__ double L[kNb][kNb + 1];
-  __shared__ double P[kNb][kNb + 1];
-  const int m = blockIdx.y;
-  const int i = k + blockIdx.x;
-  double* A = Aall + (int64_t)m * c * c;
-  const int64_t k0 = (int64_t)k * kNb;
-  for (int idx = threadIdx.x; idx < kNb * kNb; idx += 256) {
-    const int r = idx >> 6, cc = idx & 63;
-    L[r][cc] = cc <= r ? A[(k0 + r) * c + k0 + cc] : 0.0;
-  }
-  __syncthreads();
-  factor_block(L, status);
-  if (i == k) {
-    // The diagonal block of A stays unfactored (other workgroups of this launch
-    // read it); the factor is needed only as its inverse.
-    for (int idx = threadIdx.x; idx < kNb * kNb; idx += 256) P[idx >> 6][idx & 63] = 0.0;
+  // X = L^-1 by forward elimination on L X = I, one pivot row at a time
+  for (int j = 0; j < kNb; ++j) {
+    if (threadIdx.x <= j) X[j][threadIdx.x] = X[j][threadIdx.x] / L[j][j];
     __syncthreads();
-    if (threadIdx.x < kNb) {
-      const int j = threadIdx.x;       // column j of L_kk^-1 by forward substitution
-      P[j][j] = 1.0 / L[j][j];
-      for (int r = j + 1; r < kNb; ++r) {
-        double v = 0.0;
-        for (int mm = j; mm < r; ++mm) v += L[r][mm] * P[mm][j];
-        P[r][j] = -v / L[r][r];
-      }
+    for (int idx = threadIdx.x; idx < kNb * kNb; idx += 256) {
+      const int r = idx >> 6, cc = idx & 63;
+      if (r > j && cc <= j) X[r][cc] -= L[r][j] * X[j][cc];
     }
     __syncthreads();
-    double* D = dinv + ((int64_t)m * (c / kNb) + k) * kNb * kNb;
-    for (int idx = threadIdx.x; idx < kNb * kNb; idx += 256) D[idx] = P[idx >> 6][idx & 63];
-    return;
   }
-  const int64_t i0 = (int64_t)i * kNb;
-  for (int idx = threadIdx.x; idx < kNb * kNb; idx += 256) {
-    const int r = idx >> 6, cc = idx & 63;
-    P[r][cc] = A[(i0 + r) * c + k0 + cc];
-  }
-  __syncthreads();
-  if (threadIdx.x < kNb) {
-    const int r = threadIdx.x;         // row r of the panel: x L^T = p
-    for (int j = 0; j < kNb; ++j) {
-      double v = P[r][j];
-      for (int mm = 0; mm < j; ++mm) v -= P[r][mm] * L[j][mm];
-      P[r][j] = v / L[j][j];
-    }
-  }
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < kNb * kNb; idx += 256) {
-    const int r = idx >> 6, cc = idx & 63;
-    A[(i0 + r) * c + k0 + cc] = P[r][cc];
-  }
+  double* D = dinv + ((int64_t)m * (c / kNb) + k) * kNb * kNb;
+  for (int idx = threadIdx.x; idx < kNb * kNb; idx += 256) D[idx] = X[idx >> 6][idx & 63];
 }
 
-__global__ __launch_bounds__(256) void chol_update_kernel(double* __restrict__ Aall, int c, int k) {
-  __shared__ double Pi[kNb][kNb + 1];
-  __shared__ double Pj[kNb][kNb + 1];
-  const int m = blockIdx.y;
-  int bi, bj;
-  tri_of(blockIdx.x, bi, bj);
-  const int i = k + 1 + bi, j = k + 1 + bj;
-  const bool diag = i == j;
+// Step k, block row i > k:  L[i][k] = T_i Dinv_k^T.
+__global__ __launch_bounds__(256) void chol_panel_kernel(double* __restrict__ Aall, int c, int k,
+                                                         const double* __restrict__ dinv) {
+  __shared__ double Ts[kNb][kNb + 1];
+  __shared__ double Ds[kNb][kNb + 1];
+  const int m = blockIdx.y, i = k + 1 + blockIdx.x;
   double* A = Aall + (int64_t)m * c * c;
-  const int64_t k0 = (int64_t)k * kNb, i0 = (int64_t)i * kNb, j0 = (int64_t)j * kNb;
+  const double* D = dinv + ((int64_t)m * (c / kNb) + k) * kNb * kNb;
+  const int64_t i0 = (int64_t)i * kNb, k0 = (int64_t)k * kNb;
   for (int idx = threadIdx.x; idx < kNb * kNb; idx += 256) {
     const int r = idx >> 6, cc = idx & 63;
-    Pi[r][cc] = A[(i0 + r) * c + k0 + cc];
-    Pj[r][cc] = A[(j0 + r) * c + k0 + cc];
+    Ts[r][cc] = A[(i0 + r) * c + k0 + cc];
+    Ds[r][cc] = D[idx];
   }
   __syncthreads();
   Tile64 t;
+  t.zero();
+  t.mac<true>(Ts, Ds, 1.0);
 #pragma unroll
   for (int x = 0; x < 2; ++x)
 #pragma unroll
     for (int y = 0; y < 2; ++y)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = Tile64::row(x, r), col = Tile64::col(y);
-        t.acc[x][y][r] = (!diag || col <= row) ? A[(i0 + row) * c + j0 + col] : 0.0;
-      }
-  t.mac<true>(Pi, Pj, -1.0);
-#pragma unroll
-  for (int x = 0; x < 2; ++x)
-#pragma unroll
-    for (int y = 0; y < 2; ++y)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = Tile64::row(x, r), col = Tile64::col(y);
-        if (!diag || col <= row) A[(i0 + row) * c + j0 + col] = t.acc[x][y][r];
-      }
+      for (int r = 0; r < 4; ++r)
+        A[(i0 + Tile64::row(x, r)) * c + k0 + Tile64::col(y)] = t.acc[x][y][r];
 }
 
 // ---------------------------------------------------------------- triangular inverse
-
+// Block row i of X = L^-1:  X[i][j] = -Dinv_i sum_{m=j}^{i-1} L[i][m] X[m][j]  (j < i),
+// X[i][i] = Dinv_i.  X is kept in fp64; U (and U^T) receive the fp32 values at
+// the reversed position.
 __global__ __launch_bounds__(256) void trtri_row_kernel(const double* __restrict__ Aall, int c, int i,
                                                         const double* __restrict__ dinv,
                                                         double* __restrict__ Xall,
@@ -286,16 +313,16 @@ __global__ __launch_bounds__(256) void trtri_row_kernel(const double* __restrict
   }
   Tile64 t;
   t.zero();
-  for (int mm = j; mm < i; ++mm) {
-    const int64_t m0 = (int64_t)mm * kNb;
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < kNb * kNb; idx += 256) {
-      const int r = idx >> 6, cc = idx & 63;
-      Ls[r][cc] = A[(i0 + r) * c + m0 + cc];
-      Xs[r][cc] = X[(m0 + r) * c + j0 + cc];
+  {
+    ChunkPipe pipe;
+    pipe.fetch(A + i0 * c + j0, c, X + j0 * c + j0, c);
+    for (int mm = j; mm < i; ++mm) {
+      __syncthreads();
+      pipe.stage(Ls, Xs);
+      __syncthreads();
+      if (mm + 1 < i) pipe.fetch(A + i0 * c + (mm + 1) * kNb, c, X + (int64_t)(mm + 1) * kNb * c + j0, c);
+      t.mac<false>(Ls, Xs, 1.0);
     }
-    __syncthreads();
-    t.mac<false>(Ls, Xs, 1.0);
   }
   // Xs <- T (the sum), Ls <- Linv_ii; then X[i][j] = -Linv_ii T
   __syncthreads();
@@ -338,12 +365,11 @@ void launch_inverse_cholesky(const GptqPlan& p, hipStream_t s) {
   hipLaunchKernelGGL(build_reversed_kernel, dim3(nbk * (nbk + 1) / 2, p.n_mats), dim3(256), 0, s,
                      p.mats, c, p.dead, p.lamd, p.A);
   for (int k = 0; k < nbk; ++k) {
-    hipLaunchKernelGGL(potrf_panel_kernel, dim3(nbk - k, p.n_mats), dim3(256), 0, s, p.A, c, k,
-                       p.dinv, p.status);
-    const int rem = nbk - k - 1;
-    if (rem > 0)
-      hipLaunchKernelGGL(chol_update_kernel, dim3(rem * (rem + 1) / 2, p.n_mats), dim3(256), 0, s,
-                         p.A, c, k);
+    hipLaunchKernelGGL(chol_left_kernel, dim3(nbk - k, p.n_mats), dim3(256), 0, s, p.A, c, k);
+    hipLaunchKernelGGL(chol_diag_kernel, dim3(p.n_mats), dim3(256), 0, s, p.A, c, k, p.dinv, p.status);
+    if (k + 1 < nbk)
+      hipLaunchKernelGGL(chol_panel_kernel, dim3(nbk - k - 1, p.n_mats), dim3(256), 0, s, p.A, c, k,
+                         p.dinv);
   }
   for (int i = 0; i < nbk; ++i)
     hipLaunchKernelGGL(trtri_row_kernel, dim3(i + 1, p.n_mats), dim3(256), 0, s, p.A, c, i, p.dinv,
