@@ -6,21 +6,26 @@
 // Products of bf16 values are exact in fp32; they are accumulated in fp32 on
 // the matrix cores (v_mfma_f32_32x32x16_bf16).
 //
-// Work decomposition.  S is symmetric, so only the lower-triangular 128x128
-// tiles (ti >= tj) of each slot are computed: nt(nt+1)/2 tiles for nt = d/128.
+// Work decomposition.  S is symmetric, so only the lower-triangular 256x256
+// tiles (ti >= tj) of each slot are computed: nt(nt+1)/2 tiles for nt = d/256.
 // Workgroup b takes slot slot_order[b / tiles_per_slot] -- slots are ordered
 // longest token list first, so the long shared-expert and heavily loaded
 // experts start first -- and tile b % tiles_per_slot.  One workgroup owns one
 // (slot, tile) for the whole token range, so every element of S is summed in a
 // fixed order by a single workgroup: results are bit-identical run to run.
 // The running sum is added into S every kFlushSteps token steps (two-level
-// summation keeps fp32 error independent of the expert's size).
+// summation keeps the fp32 error independent of the expert's size).
 //
-// Tile pipeline: 256 threads (4 waves, 2x2), 64 output rows x 64 columns per
-// wave as 2x2 MFMA 32x32 blocks; tokens advance 64 at a time through LDS.  The
-// operand tiles are feature-major [128 features][64 tokens] so each lane's
-// MFMA fragment (8 consecutive tokens of one feature) is one 16-byte LDS read;
-// the LDS row pitch of 72 bf16 (144 B) keeps those reads bank-conflict free.
+// Tile pipeline: 512 threads = 8 waves in a 2x4 arrangement, each wave owns a
+// 128x64 part as 4x2 MFMA blocks of 32x32 (128 fp32 accumulators per lane).
+// Tokens advance 32 at a time through two LDS buffers: while the matrix cores
+// consume one buffer, the next token step is loaded into registers and then
+// written to the other buffer.  Operand tiles are feature-major
+// [256 features][32 tokens]; a lane's MFMA fragment (8 consecutive tokens of one
+// feature) is one 16-byte LDS read, and the row pitch of 40 bf16 (80 bytes)
+// keeps those reads bank-conflict free.  On diagonal tiles the two waves whose
+// parts lie entirely above the diagonal skip their products, and the B operand
+// is the A operand.
 #include "kernels.h"
 
 namespace clha {
@@ -28,9 +33,11 @@ namespace clha {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kSK = 64;              // tokens per step
-constexpr int kPitch = kSK + 8;      // LDS row pitch (bf16 elements)
-constexpr int kFlushSteps = 128;     // 8192 tokens between partial-sum flushes
+constexpr int kT = 256;              // output tile
+constexpr int kSK = 32;              // tokens per step
+constexpr int kPitch = kSK + 8;      // LDS row pitch (bf16 elements, 80 bytes)
+constexpr int kFlushSteps = 256;     // 8192 tokens between partial-sum flushes
+constexpr int kBuf = kT * kPitch;    // one operand buffer (bf16 elements)
 
 __device__ __forceinline__ void tile_of(int t, int& ti, int& tj) {
   int i = (int)((sqrtf(8.0f * (float)t + 1.0f) - 1.0f) * 0.5f);
@@ -40,28 +47,37 @@ __device__ __forceinline__ void tile_of(int t, int& ti, int& tj) {
   tj = t - i * (i + 1) / 2;
 }
 
-__device__ __forceinline__ void flush_acc(f32x16 (&acc)[2][2], float* __restrict__ Sslot, int d,
+// Adds the running sums into S and clears them.  One 32x32 block at a time
+// (scheduling barriers keep at most 16 loads of S in flight per lane).
+__device__ __forceinline__ void flush_acc(f32x16 (&acc)[4][2], float* __restrict__ Sslot, int d,
                                           int row0, int col0, bool diag, int lane) {
+  // An opaque zero keeps the 128 element addresses from being hoisted out of
+  // the token loop (where they would occupy registers for the whole kernel).
+  int opaque;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(opaque));
+  const int lc = (lane & 31) + opaque, kh = lane >> 5;
 #pragma unroll
-  for (int im = 0; im < 2; ++im)
+  for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
-    for (int jn = 0; jn < 2; ++jn) {
-      const int j = col0 + jn * 32 + (lane & 31);
+    for (int bj = 0; bj < 2; ++bj) {
+      const int j = col0 + bj * 32 + lc;
+      float* p = Sslot + (int64_t)(row0 + bi * 32 + 4 * kh) * d + j;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int i = row0 + im * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (!diag || i >= j) Sslot[(int64_t)i * d + j] += acc[im][jn][r];
-        acc[im][jn][r] = 0.0f;
+        const int i = row0 + bi * 32 + 8 * (r >> 2) + 4 * kh + (r & 3);
+        if ((!diag || i >= j) && i < d && j < d) p[(int64_t)(8 * (r >> 2) + (r & 3)) * d] += acc[bi][bj][r];
+        acc[bi][bj][r] = 0.0f;
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
 }
 
-__global__ __launch_bounds__(256) void syrk_kernel(const uint16_t* __restrict__ xgT,
-                                                   const int64_t* __restrict__ pad_off,
-                                                   const int32_t* __restrict__ slot_order, int d,
-                                                   int tiles_per_slot, float* __restrict__ S) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[kSyrkTile * kPitch];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[kSyrkTile * kPitch];
+__global__ __launch_bounds__(512) void syrk_kernel(const uint16_t* __restrict__ xgT,
+                                                      const int64_t* __restrict__ pad_off,
+                                                      const int32_t* __restrict__ slot_order,
+                                                      int d, int tiles_per_slot,
+                                                      float* __restrict__ S) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[4 * kBuf];   // A0 B0 A1 B1
 
   const int rank = blockIdx.x / tiles_per_slot;
   const int tile = blockIdx.x - rank * tiles_per_slot;
@@ -72,73 +88,90 @@ __global__ __launch_bounds__(256) void syrk_kernel(const uint16_t* __restrict__ 
   tile_of(tile, ti, tj);
   const bool diag = ti == tj;
   const uint16_t* base = xgT + pad_off[slot] * d;
-  const uint16_t* Ag = base + (int64_t)ti * kSyrkTile * npad;
-  const uint16_t* Bg = base + (int64_t)tj * kSyrkTile * npad;
-  const uint16_t* Bsrc = diag ? As : Bs;
+  const uint16_t* Ag = base + (int64_t)ti * kT * npad;
+  const uint16_t* Bg = base + (int64_t)tj * kT * npad;
+  const int arows = min(kT, d - ti * kT), brows = min(kT, d - tj * kT);   // d % 256 may be 128
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;
+  const bool idle = diag && wm * 128 + 127 < wn * 64;   // part strictly above the diagonal
 
-  f32x16 acc[2][2];
+  f32x16 acc[4][2];
 #pragma unroll
-  for (int im = 0; im < 2; ++im)
+  for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
-    for (int jn = 0; jn < 2; ++jn) acc[im][jn] = f32x16{};
+    for (int bj = 0; bj < 2; ++bj) acc[bi][bj] = f32x16{};
 
-  int steps = 0;
-  for (int64_t k0 = 0; k0 < npad; k0 += kSK) {
-    uint4 ra[4], rb[4];
+  // thread t moves 16-byte chunks q = t + 512u: row q/4, token chunk q%4
+  uint4 ra[2], rb[2];
+  auto fetch = [&](int64_t k0) {
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int c = tid + 256 * m;
-      const int row = c >> 3, ch = c & 7;
-      ra[m] = *reinterpret_cast<const uint4*>(Ag + (int64_t)row * npad + k0 + ch * 8);
-      if (!diag) rb[m] = *reinterpret_cast<const uint4*>(Bg + (int64_t)row * npad + k0 + ch * 8);
+    for (int u = 0; u < 2; ++u) {
+      const int q = tid + 512 * u, row = q >> 2, ch = q & 3;
+      ra[u] = row < arows ? *reinterpret_cast<const uint4*>(Ag + (int64_t)row * npad + k0 + ch * 8)
+                          : make_uint4(0, 0, 0, 0);
+      if (!diag)
+        rb[u] = row < brows ? *reinterpret_cast<const uint4*>(Bg + (int64_t)row * npad + k0 + ch * 8)
+                            : make_uint4(0, 0, 0, 0);
     }
+  };
+  auto stage = [&](int buf) {
+    uint16_t* As = lds + (2 * buf) * kBuf;
+    uint16_t* Bs = lds + (2 * buf + 1) * kBuf;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int c = tid + 256 * m;
-      const int row = c >> 3, ch = c & 7;
-      *reinterpret_cast<uint4*>(&As[row * kPitch + ch * 8]) = ra[m];
-      if (!diag) *reinterpret_cast<uint4*>(&Bs[row * kPitch + ch * 8]) = rb[m];
+    for (int u = 0; u < 2; ++u) {
+      const int q = tid + 512 * u, row = q >> 2, ch = q & 3;
+      *reinterpret_cast<uint4*>(&As[row * kPitch + ch * 8]) = ra[u];
+      if (!diag) *reinterpret_cast<uint4*>(&Bs[row * kPitch + ch * 8]) = rb[u];
     }
-    __syncthreads();
+  };
+
+  const int64_t nsteps = npad / kSK;
+  fetch(0);
+  stage(0);
+  __syncthreads();
+  float* Sslot = S + (int64_t)slot * d * d;
+  for (int64_t c0 = 0; c0 < nsteps; c0 += kFlushSteps) {
+    const int64_t c1 = c0 + kFlushSteps < nsteps ? c0 + kFlushSteps : nsteps;
+    for (int64_t st = c0; st < c1; ++st) {
+      const int buf = (int)(st & 1);
+      if (st + 1 < nsteps) fetch((st + 1) * kSK);
+      if (!idle) {
+        const uint16_t* As = lds + (2 * buf) * kBuf;
+        const uint16_t* Bs = diag ? As : lds + (2 * buf + 1) * kBuf;
 #pragma unroll
-    for (int kk = 0; kk < kSK / 16; ++kk) {
-      const int kcol = kk * 16 + (lane >> 5) * 8;
-      bf16x8 a[2], b[2];
+        for (int kk = 0; kk < kSK / 16; ++kk) {
+          const int kcol = kk * 16 + (lane >> 5) * 8;
+          bf16x8 a[4], b[2];
 #pragma unroll
-      for (int im = 0; im < 2; ++im) {
-        const int row = wm * 64 + im * 32 + (lane & 31);
-        a[im] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&As[row * kPitch + kcol]));
+          for (int bi = 0; bi < 4; ++bi) {
+            const int row = wm * 128 + bi * 32 + (lane & 31);
+            a[bi] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&As[row * kPitch + kcol]));
+          }
+#pragma unroll
+          for (int bj = 0; bj < 2; ++bj) {
+            const int row = wn * 64 + bj * 32 + (lane & 31);
+            b[bj] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&Bs[row * kPitch + kcol]));
+          }
+#pragma unroll
+          for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+            for (int bj = 0; bj < 2; ++bj)
+              acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[bi], b[bj], acc[bi][bj], 0, 0, 0);
+        }
       }
-#pragma unroll
-      for (int jn = 0; jn < 2; ++jn) {
-        const int row = wn * 64 + jn * 32 + (lane & 31);
-        b[jn] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&Bsrc[row * kPitch + kcol]));
-      }
-#pragma unroll
-      for (int im = 0; im < 2; ++im)
-#pragma unroll
-        for (int jn = 0; jn < 2; ++jn)
-          acc[im][jn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[im], b[jn], acc[im][jn], 0, 0, 0);
+      if (st + 1 < nsteps) stage(buf ^ 1);
+      __syncthreads();
     }
-    __syncthreads();
-    if (++steps == kFlushSteps) {
-      steps = 0;
-      flush_acc(acc, S + (int64_t)slot * d * d, d, ti * kSyrkTile + wm * 64,
-                tj * kSyrkTile + wn * 64, diag, lane);
-    }
+    if (!idle) flush_acc(acc, Sslot, d, ti * kT + wm * 128, tj * kT + wn * 64, diag, lane);
   }
-  if (steps) flush_acc(acc, S + (int64_t)slot * d * d, d, ti * kSyrkTile + wm * 64,
-                       tj * kSyrkTile + wn * 64, diag, lane);
 }
 
 void launch_syrk(const CollectPlan& p, float* S, hipStream_t s) {
-  const int nt = p.d / kSyrkTile;
+  const int nt = (p.d + kT - 1) / kT;
   const int tiles = nt * (nt + 1) / 2;
   const int slots = p.E + p.has_shared;
-  hipLaunchKernelGGL(syrk_kernel, dim3(tiles * slots), dim3(256), 0, s, p.xgT, p.pad_off,
+  hipLaunchKernelGGL(syrk_kernel, dim3(tiles * slots), dim3(512), 0, s, p.xgT, p.pad_off,
                      p.slot_order, p.d, tiles, S);
 }
 
