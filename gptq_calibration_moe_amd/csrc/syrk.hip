@@ -18,9 +18,10 @@
 //
 // Tile pipeline: 512 threads = 8 waves in a 2x4 arrangement, each wave owns a
 // 128x64 part as 4x2 MFMA blocks of 32x32 (128 fp32 accumulators per lane).
-// Tokens advance 32 at a time through two LDS buffers: while the matrix cores
-// consume one buffer, the next token step is loaded into registers and then
-// written to the other buffer.  Operand tiles are feature-major
+// Tokens advance 32 at a time through two LDS buffers and two register stages:
+// while the matrix cores consume one buffer, the other buffer is filled from
+// the register stage loaded a step earlier, and the register stage is refilled
+// with the step after that -- each global load has a full step to arrive.  Operand tiles are feature-major
 // [256 features][32 tokens]; a lane's MFMA fragment (8 consecutive tokens of one
 // feature) is one 16-byte LDS read, and the row pitch of 40 bf16 (80 bytes)
 // keeps those reads bank-conflict free.  On diagonal tiles the two waves whose
@@ -36,7 +37,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int kT = 256;              // output tile
 constexpr int kSK = 32;              // tokens per step
 constexpr int kPitch = kSK + 8;      // LDS row pitch (bf16 elements, 80 bytes)
-constexpr int kFlushSteps = 256;     // 8192 tokens between partial-sum flushes
+constexpr int kFlushSteps = 256;     // 8192 tokens between partial-sum flushes (even)
 constexpr int kBuf = kT * kPitch;    // one operand buffer (bf16 elements)
 
 __device__ __forceinline__ void tile_of(int t, int& ti, int& tj) {
@@ -102,65 +103,80 @@ __global__ __launch_bounds__(512) void syrk_kernel(const uint16_t* __restrict__ 
 #pragma unroll
     for (int bj = 0; bj < 2; ++bj) acc[bi][bj] = f32x16{};
 
-  // thread t moves 16-byte chunks q = t + 512u: row q/4, token chunk q%4
-  uint4 ra[2], rb[2];
-  auto fetch = [&](int64_t k0) {
+  // thread t moves 16-byte chunks q = t + 512u: row q/4, token chunk q%4.
+  // Two register stages: the loads for step st+2 are issued while step st is
+  // multiplied, so each load has a full step of products to arrive.
+  struct Stage {
+    uint4 a[2], b[2];
+  };
+  auto fetch = [&](Stage& r, int64_t k0) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int q = tid + 512 * u, row = q >> 2, ch = q & 3;
-      ra[u] = row < arows ? *reinterpret_cast<const uint4*>(Ag + (int64_t)row * npad + k0 + ch * 8)
-                          : make_uint4(0, 0, 0, 0);
+      r.a[u] = row < arows ? *reinterpret_cast<const uint4*>(Ag + (int64_t)row * npad + k0 + ch * 8)
+                           : make_uint4(0, 0, 0, 0);
       if (!diag)
-        rb[u] = row < brows ? *reinterpret_cast<const uint4*>(Bg + (int64_t)row * npad + k0 + ch * 8)
-                            : make_uint4(0, 0, 0, 0);
+        r.b[u] = row < brows ? *reinterpret_cast<const uint4*>(Bg + (int64_t)row * npad + k0 + ch * 8)
+                             : make_uint4(0, 0, 0, 0);
     }
   };
-  auto stage = [&](int buf) {
+  auto stage = [&](const Stage& r, int buf) {
     uint16_t* As = lds + (2 * buf) * kBuf;
     uint16_t* Bs = lds + (2 * buf + 1) * kBuf;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int q = tid + 512 * u, row = q >> 2, ch = q & 3;
-      *reinterpret_cast<uint4*>(&As[row * kPitch + ch * 8]) = ra[u];
-      if (!diag) *reinterpret_cast<uint4*>(&Bs[row * kPitch + ch * 8]) = rb[u];
+      *reinterpret_cast<uint4*>(&As[row * kPitch + ch * 8]) = r.a[u];
+      if (!diag) *reinterpret_cast<uint4*>(&Bs[row * kPitch + ch * 8]) = r.b[u];
+    }
+  };
+  auto multiply = [&](int buf) {
+    if (idle) return;
+    const uint16_t* As = lds + (2 * buf) * kBuf;
+    const uint16_t* Bs = diag ? As : lds + (2 * buf + 1) * kBuf;
+#pragma unroll
+    for (int kk = 0; kk < kSK / 16; ++kk) {
+      const int kcol = kk * 16 + (lane >> 5) * 8;
+      bf16x8 a[4], b[2];
+#pragma unroll
+      for (int bi = 0; bi < 4; ++bi) {
+        const int row = wm * 128 + bi * 32 + (lane & 31);
+        a[bi] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&As[row * kPitch + kcol]));
+      }
+#pragma unroll
+      for (int bj = 0; bj < 2; ++bj) {
+        const int row = wn * 64 + bj * 32 + (lane & 31);
+        b[bj] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&Bs[row * kPitch + kcol]));
+      }
+#pragma unroll
+      for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < 2; ++bj)
+          acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[bi], b[bj], acc[bi][bj], 0, 0, 0);
     }
   };
 
+  // nsteps is even (token lists are padded to 64); steps 2s and 2s+1 form a pair
   const int64_t nsteps = npad / kSK;
-  fetch(0);
-  stage(0);
+  Stage r0, r1;
+  fetch(r0, 0);
+  stage(r0, 0);
+  fetch(r1, kSK);
+  if (nsteps > 2) fetch(r0, 2 * kSK);
   __syncthreads();
   float* Sslot = S + (int64_t)slot * d * d;
   for (int64_t c0 = 0; c0 < nsteps; c0 += kFlushSteps) {
     const int64_t c1 = c0 + kFlushSteps < nsteps ? c0 + kFlushSteps : nsteps;
-    for (int64_t st = c0; st < c1; ++st) {
-      const int buf = (int)(st & 1);
-      if (st + 1 < nsteps) fetch((st + 1) * kSK);
-      if (!idle) {
-        const uint16_t* As = lds + (2 * buf) * kBuf;
-        const uint16_t* Bs = diag ? As : lds + (2 * buf + 1) * kBuf;
-#pragma unroll
-        for (int kk = 0; kk < kSK / 16; ++kk) {
-          const int kcol = kk * 16 + (lane >> 5) * 8;
-          bf16x8 a[4], b[2];
-#pragma unroll
-          for (int bi = 0; bi < 4; ++bi) {
-            const int row = wm * 128 + bi * 32 + (lane & 31);
-            a[bi] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&As[row * kPitch + kcol]));
-          }
-#pragma unroll
-          for (int bj = 0; bj < 2; ++bj) {
-            const int row = wn * 64 + bj * 32 + (lane & 31);
-            b[bj] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&Bs[row * kPitch + kcol]));
-          }
-#pragma unroll
-          for (int bi = 0; bi < 4; ++bi)
-#pragma unroll
-            for (int bj = 0; bj < 2; ++bj)
-              acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[bi], b[bj], acc[bi][bj], 0, 0, 0);
-        }
-      }
-      if (st + 1 < nsteps) stage(buf ^ 1);
+    for (int64_t st = c0; st < c1; st += 2) {
+      // step st: LDS buffer 0 holds it, r1 holds st+1, r0 holds st+2 (if any)
+      multiply(0);
+      stage(r1, 1);
+      if (st + 3 < nsteps) fetch(r1, (st + 3) * kSK);
+      __syncthreads();
+      // step st+1 from buffer 1; r0 (step st+2) goes to buffer 0
+      multiply(1);
+      if (st + 2 < nsteps) stage(r0, 0);
+      if (st + 4 < nsteps) fetch(r0, (st + 4) * kSK);
       __syncthreads();
     }
     if (!idle) flush_acc(acc, Sslot, d, ti * kT + wm * 128, tj * kT + wn * 64, diag, lane);
