@@ -22,6 +22,7 @@ using clha::GptqPlan;
 
 namespace clha {
 bool gptq_group_supported(int group);
+int syrk_tiles_per_slot(int d);
 }
 
 struct LayerBufs {
@@ -162,6 +163,9 @@ struct CollectLayout {
   int64_t* offsets;
   int64_t* pad_off;
   int32_t* slot_order;
+  int32_t* work;
+  int32_t* work_len;
+  int32_t* work_next;
   int32_t* token_ids;
   uint16_t* xgT;
   size_t bytes;
@@ -181,6 +185,9 @@ CollectLayout collect_layout(const clha_ctx* ctx, void* ws) {
   L.offsets = c.take<int64_t>((size_t)d.n_routed + 1);
   L.pad_off = c.take<int64_t>((size_t)ctx->slots + 1);
   L.slot_order = c.take<int32_t>((size_t)ctx->slots);
+  L.work = c.take<int32_t>((size_t)clha::kXcds * ctx->slots * clha::syrk_tiles_per_slot(d.d));
+  L.work_len = c.take<int32_t>(clha::kXcds);
+  L.work_next = c.take<int32_t>(clha::kXcds);
   L.token_ids = c.take<int32_t>((size_t)n * d.top_k);
   L.xgT = c.take<uint16_t>((size_t)xg_tokens * d.d);
   L.bytes = c.off;
@@ -365,6 +372,10 @@ CLHA_API clha_status clha_collect_hessians(clha_ctx* ctx, int32_t layer, int64_t
   p.offsets = offsets_out ? offsets_out : L.offsets;
   p.pad_off = L.pad_off;
   p.slot_order = L.slot_order;
+  p.work = L.work;
+  p.work_len = L.work_len;
+  p.work_next = L.work_next;
+  p.syrk_tiles = clha::syrk_tiles_per_slot(d.d);
   p.token_ids = token_ids_out ? token_ids_out : L.token_ids;
   p.xgT = L.xgT;
   p.xg_tiles = (n_tokens * d.top_k + clha::kTokPad - 1) / clha::kTokPad + d.n_routed +

@@ -15,7 +15,9 @@ constexpr int kTokPad = 64;           // expert token lists are padded to this m
 constexpr int kMaxExperts = 256;
 constexpr int kMaxTopK = 16;
 constexpr int kMaxLayers = 8;
-constexpr int kSyrkTile = 128;        // Gram-sum output tile
+constexpr int kSyrkTile = 256;        // Gram-sum output tile
+constexpr int kXcds = 8;              // accelerator complex dies; workgroup b runs on die b % 8
+constexpr int kSyrkWgPerXcd = 32;     // persistent Gram-sum workgroups per die (one per CU)
 constexpr int kNb = 64;               // Cholesky / triangular-inverse block
 constexpr int kGptqRows = 64;         // rows per GPTQ workgroup
 
@@ -35,6 +37,10 @@ struct CollectPlan {
   int64_t* offsets;      // [E+1]
   int64_t* pad_off;      // [slots+1] padded starts of each slot's token list
   int32_t* slot_order;   // [slots] slots sorted by padded length, longest first
+  int32_t* work;         // [kXcds][slots*tiles] Gram-sum work items (slot*1024 + tile) per XCD
+  int32_t* work_len;     // [kXcds] items per XCD
+  int32_t* work_next;    // [kXcds] queue heads (reset by the bucketing scan)
+  int syrk_tiles;        // lower-triangular 256x256 tiles per slot
   int32_t* token_ids;    // [n*K]
   uint16_t* xgT;         // feature-major gathered activations
   int64_t xg_tiles;      // upper bound of 64-token tiles over all slots

@@ -115,9 +115,13 @@ __global__ __launch_bounds__(256) void bucket_count_kernel(const int32_t* __rest
 __global__ __launch_bounds__(256) void bucket_scan_kernel(
     const int32_t* __restrict__ blockcounts, int nblk, int64_t n, int E, int has_shared,
     int32_t* __restrict__ blockbase, int64_t* __restrict__ offsets, int64_t* __restrict__ pad_off,
-    int32_t* __restrict__ slot_order, int64_t* __restrict__ layer_counts) {
+    int32_t* __restrict__ slot_order, int64_t* __restrict__ layer_counts, int tiles,
+    int32_t* __restrict__ work, int32_t* __restrict__ work_len, int32_t* __restrict__ work_next) {
   __shared__ int64_t cnt[kMaxExperts + 1];
   __shared__ int64_t padc[kMaxExperts + 1];
+  __shared__ int32_t order[kMaxExperts + 1];
+  __shared__ int32_t home[kMaxExperts + 1];           // XCD of a whole slot, -1 = split over all
+  __shared__ int32_t base[kMaxExperts + 1][kXcds];    // first list position of the slot's items
   const int slots = E + has_shared;
   for (int e = threadIdx.x; e < E; e += 256) {
     int64_t run = 0;
@@ -153,6 +157,59 @@ __global__ __launch_bounds__(256) void bucket_scan_kernel(
     int r = 0;
     for (int o = 0; o < slots; ++o) r += (padc[o] > padc[e]) || (padc[o] == padc[e] && o < e);
     slot_order[r] = e;
+    order[r] = e;
+  }
+  __syncthreads();
+  // Gram-sum work lists, one per XCD (each XCD has its own L2): a slot's tiles
+  // share its activations, so a slot stays on one XCD, longest slots first onto
+  // the least-loaded XCD; a slot longer than an eighth of the work is split
+  // over all XCDs (tile t on XCD t % 8).
+  if (threadIdx.x == 0) {
+    int64_t total = 0;
+    for (int r = 0; r < slots; ++r) total += padc[r];
+    int64_t load[kXcds];
+    int32_t len[kXcds];
+    for (int x = 0; x < kXcds; ++x) {
+      load[x] = 0;
+      len[x] = 0;
+    }
+    for (int r = 0; r < slots; ++r) {
+      const int e = order[r];
+      if (tiles >= kXcds && padc[e] * kXcds > total) {
+        home[e] = -1;
+        for (int x = 0; x < kXcds; ++x) {
+          const int cntx = tiles / kXcds + (x < tiles % kXcds ? 1 : 0);
+          base[e][x] = len[x];
+          len[x] += cntx;
+          load[x] += padc[e] * cntx;
+        }
+      } else {
+        int best = 0;
+        for (int x = 1; x < kXcds; ++x) best = load[x] < load[best] ? x : best;
+        home[e] = best;
+        base[e][best] = len[best];
+        len[best] += tiles;
+        load[best] += padc[e] * tiles;
+      }
+    }
+    for (int x = 0; x < kXcds; ++x) {
+      work_len[x] = len[x];
+      work_next[x] = 0;
+    }
+  }
+  __syncthreads();
+  const int cap = slots * tiles;
+  for (int it = threadIdx.x; it < slots * tiles; it += 256) {
+    const int e = it / tiles, t = it - e * tiles;
+    int x, pos;
+    if (home[e] >= 0) {
+      x = home[e];
+      pos = base[e][x] + t;
+    } else {
+      x = t % kXcds;
+      pos = base[e][x] + t / kXcds;
+    }
+    work[x * cap + pos] = e * 1024 + t;
   }
 }
 
@@ -191,7 +248,7 @@ void launch_bucket(const CollectPlan& p, int64_t* layer_counts, hipStream_t s) {
                      p.E, p.blockcounts);
   hipLaunchKernelGGL(bucket_scan_kernel, dim3(1), dim3(256), 0, s, p.blockcounts, p.nblk,
                      p.n_tokens, p.E, p.has_shared, p.blockbase, p.offsets, p.pad_off,
-                     p.slot_order, layer_counts);
+                     p.slot_order, layer_counts, p.syrk_tiles, p.work, p.work_len, p.work_next);
   hipLaunchKernelGGL(bucket_scatter_kernel, dim3(p.nblk), dim3(256), 0, s, p.topk, p.n_tokens,
                      p.K, p.E, p.blockbase, p.offsets, p.token_ids);
 }

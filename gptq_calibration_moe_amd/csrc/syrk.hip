@@ -8,11 +8,12 @@
 //
 // Work decomposition.  S is symmetric, so only the lower-triangular 256x256
 // tiles (ti >= tj) of each slot are computed: nt(nt+1)/2 tiles for nt = d/256.
-// Workgroup b takes slot slot_order[b / tiles_per_slot] -- slots are ordered
-// longest token list first, so the long shared-expert and heavily loaded
-// experts start first -- and tile b % tiles_per_slot.  One workgroup owns one
-// (slot, tile) for the whole token range, so every element of S is summed in a
-// fixed order by a single workgroup: results are bit-identical run to run.
+// The (slot, tile) items are dealt to per-XCD lists by the bucketing scan (a
+// slot's tiles stay on one die, so its activations stream through one L2;
+// longest slots first).  Persistent workgroups pull items from their die's
+// list.  One workgroup owns one item for the whole token range, so every
+// element of S is summed in a fixed order: results are bit-identical run to
+// run whichever workgroup takes the item.
 // The running sum is added into S every kFlushSteps token steps (two-level
 // summation keeps the fp32 error independent of the expert's size).
 //
@@ -73,16 +74,10 @@ __device__ __forceinline__ void flush_acc(f32x16 (&acc)[4][2], float* __restrict
     }
 }
 
-__global__ __launch_bounds__(512) void syrk_kernel(const uint16_t* __restrict__ xgT,
-                                                      const int64_t* __restrict__ pad_off,
-                                                      const int32_t* __restrict__ slot_order,
-                                                      int d, int tiles_per_slot,
-                                                      float* __restrict__ S) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[4 * kBuf];   // A0 B0 A1 B1
-
-  const int rank = blockIdx.x / tiles_per_slot;
-  const int tile = blockIdx.x - rank * tiles_per_slot;
-  const int slot = slot_order[rank];
+// One (slot, tile) item: S[slot] tile (ti, tj) += X_slot^T X_slot over the slot's tokens.
+__device__ __forceinline__ void syrk_tile(const uint16_t* __restrict__ xgT,
+                                          const int64_t* __restrict__ pad_off, int slot, int tile,
+                                          int d, float* __restrict__ S, uint16_t* lds) {
   const int64_t npad = pad_off[slot + 1] - pad_off[slot];
   if (npad == 0) return;
   int ti, tj;
@@ -183,12 +178,39 @@ __global__ __launch_bounds__(512) void syrk_kernel(const uint16_t* __restrict__ 
   }
 }
 
+// Persistent workgroups, kSyrkWgPerXcd per die: workgroup b runs on die b % 8
+// and takes items from that die's list until the list is exhausted, so all
+// tiles of a slot read the slot's activations through one L2.
+__global__ __launch_bounds__(512) void syrk_kernel(const uint16_t* __restrict__ xgT,
+                                                   const int64_t* __restrict__ pad_off,
+                                                   const int32_t* __restrict__ work,
+                                                   const int32_t* __restrict__ work_len,
+                                                   int32_t* __restrict__ work_next, int cap, int d,
+                                                   float* __restrict__ S) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[4 * kBuf];   // A0 B0 A1 B1
+  __shared__ int item;
+  const int x = blockIdx.x % kXcds;
+  const int len = work_len[x];
+  for (;;) {
+    if (threadIdx.x == 0) item = atomicAdd(&work_next[x], 1);
+    __syncthreads();
+    const int it = item;
+    __syncthreads();
+    if (it >= len) break;
+    const int code = work[x * cap + it];
+    syrk_tile(xgT, pad_off, code >> 10, code & 1023, d, S, lds);
+  }
+}
+
 void launch_syrk(const CollectPlan& p, float* S, hipStream_t s) {
-  const int nt = (p.d + kT - 1) / kT;
-  const int tiles = nt * (nt + 1) / 2;
   const int slots = p.E + p.has_shared;
-  hipLaunchKernelGGL(syrk_kernel, dim3(tiles * slots), dim3(512), 0, s, p.xgT, p.pad_off,
-                     p.slot_order, p.d, tiles, S);
+  hipLaunchKernelGGL(syrk_kernel, dim3(kXcds * kSyrkWgPerXcd), dim3(512), 0, s, p.xgT, p.pad_off,
+                     p.work, p.work_len, p.work_next, slots * p.syrk_tiles, p.d, S);
+}
+
+int syrk_tiles_per_slot(int d) {
+  const int nt = (d + kT - 1) / kT;
+  return nt * (nt + 1) / 2;
 }
 
 }  // namespace clha
