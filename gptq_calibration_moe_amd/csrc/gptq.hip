@@ -57,7 +57,7 @@ __device__ __forceinline__ void fit_grid(float xmin, float xmax, float fmaxq, fl
 typedef const __attribute__((address_space(4))) float* const_fptr;
 
 struct ColCtx {
-  const_fptr ublk;                  // U[i1][i1]: the block's diagonal U block, row stride c
+  const float* ublk;                // the block's diagonal 64x64 U block in LDS, row stride 64
   int c;
   float fmaxq;
   float* scales;
@@ -84,7 +84,7 @@ __device__ __forceinline__ void column_steps(float (&w)[kRB], uint32_t (&packed)
       cx.zeros[cx.grid0 + JJ / G] = (uint8_t)z;
     }
   }
-  const_fptr urow = cx.ublk + (int64_t)JJ * cx.c;
+  const float* urow = cx.ublk + JJ * kRB;
   const float x = w[JJ];
   float q = rintf(__fdiv_rn(x, s)) + z;
   q = fminf(fmaxf(q, 0.0f), cx.fmaxq);
@@ -114,19 +114,24 @@ struct TileBuf {
       wb[q] = *reinterpret_cast<const float4*>(wr1 + jt + 8 * q);
     }
   }
-  __device__ __forceinline__ void apply(const float (&b0)[kRB / 2], const float (&b1)[kRB / 2],
-                                        float* wr0, float* wr1, int jt) {
+  // eb: the block's negated errors in B-operand order in LDS, eb[st*128 + mb*64 + lane]
+  __device__ __forceinline__ void apply(const float* eb, float* wr0, float* wr1, int jt, int lane) {
     f32x16 acc0, acc1;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       acc0[4 * q] = wa[q].x; acc0[4 * q + 1] = wa[q].y; acc0[4 * q + 2] = wa[q].z; acc0[4 * q + 3] = wa[q].w;
       acc1[4 * q] = wb[q].x; acc1[4 * q + 1] = wb[q].y; acc1[4 * q + 2] = wb[q].z; acc1[4 * q + 3] = wb[q].w;
     }
+    // an opaque zero keeps the 64 LDS reads inside the tile loop instead of
+    // holding them in registers for the whole update
+    int opaque;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(opaque));
+    const float* e = eb + lane + opaque;
 #pragma unroll
     for (int st = 0; st < kRB / 2; ++st) {
       const float a = (&u[st >> 2].x)[st & 3];
-      acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b0[st], acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b1[st], acc1, 0, 0, 0);
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a, e[st * 128], acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a, e[st * 128 + 64], acc1, 0, 0, 0);
     }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -145,19 +150,21 @@ struct TileBuf {
 // and -E as the B operand, each lane's 16 results are 4 runs of 4 consecutive
 // columns of one row.  MFMA step st contracts k = st (lanes 0..31) and
 // k = st+32 (lanes 32..63); the B operands come from the row-owner registers by
-// one cross-half shuffle per step.  Tiles are double-buffered: the next tile's
-// U and W load while the current tile's products run.
+// one cross-half shuffle per step and are staged in LDS.  Tiles are
+// double-buffered: the next tile's U and W load while the current tile's
+// products run.
 __device__ __forceinline__ void far_update(const float (&e)[kRB], float* Wf, const float* UT, int c,
-                                           int i1, int jt0, int lane) {
+                                           int i1, int jt0, int lane, float* eb) {
   const int kh = lane >> 5, lc = lane & 31;
-  float b0[kRB / 2], b1[kRB / 2];   // B operands for rows 0..31 and 32..63
+  // B operands for rows 0..31 (mb 0) and 32..63 (mb 1), negated, into LDS
 #pragma unroll
   for (int st = 0; st < kRB / 2; ++st) {
     const float lo = e[st], hi = e[st + kRB / 2];
     const float lo_x = __shfl_xor(lo, 32), hi_x = __shfl_xor(hi, 32);
-    b0[st] = -(kh == 0 ? lo : hi_x);      // row lc:    k = st (lanes < 32), st+32 (lanes >= 32)
-    b1[st] = -(kh == 0 ? lo_x : hi);      // row 32+lc
+    eb[st * 128 + lane] = -(kh == 0 ? lo : hi_x);        // row lc:    k = st / st+32
+    eb[st * 128 + 64 + lane] = -(kh == 0 ? lo_x : hi);   // row 32+lc
   }
+  __syncthreads();
   const float* utl = UT + (int64_t)lc * c;            // U^T row jt+lc
   const int ucol = i1 + (kRB / 2) * kh;
   float* wr0 = Wf + (int64_t)lc * c + 4 * kh;          // rows lc and 32+lc, columns jt+8q+4kh
@@ -168,15 +175,16 @@ __device__ __forceinline__ void far_update(const float (&e)[kRB], float* Wf, con
   for (int jt = jt0; jt < c; jt += 64) {
     const bool second = jt + 32 < c;
     if (second) y.load(utl, wr0, wr1, c, jt + 32, ucol);
-    x.apply(b0, b1, wr0, wr1, jt);
+    x.apply(eb, wr0, wr1, jt, lane);
     if (!second) break;
     if (jt + 64 < c) x.load(utl, wr0, wr1, c, jt + 64, ucol);
-    y.apply(b0, b1, wr0, wr1, jt + 32);
+    y.apply(eb, wr0, wr1, jt + 32, lane);
   }
 }
 
 template <int G>
-__global__ __launch_bounds__(64) void gptq_kernel(GptqPlan p) {
+__global__ __launch_bounds__(64, 2) void gptq_kernel(GptqPlan p) {
+  __shared__ float eb[kRB * 64];   // the block's errors as MFMA B operands
   const int c = p.cols;
   int lo = 0, hi = p.n_jobs;
   while (hi - lo > 1) {
@@ -244,7 +252,16 @@ __global__ __launch_bounds__(64) void gptq_kernel(GptqPlan p) {
     uint32_t packed[kRB / 4];
 #pragma unroll
     for (int q = 0; q < kRB / 4; ++q) packed[q] = 0u;
-    ColCtx cx{(const_fptr)(U + (int64_t)i1 * c + i1), c, fmaxq, job.scales, job.zeros,
+    // the block's diagonal U block into LDS (coalesced); every lane then reads
+    // the same U values (LDS broadcast)
+    __syncthreads();
+    for (int idx = lane; idx < kRB * kRB / 4; idx += 64) {
+      const int r = idx >> 4, q = idx & 15;
+      *reinterpret_cast<float4*>(eb + r * kRB + 4 * q) =
+          *reinterpret_cast<const float4*>(U + (int64_t)(i1 + r) * c + i1 + 4 * q);
+    }
+    __syncthreads();
+    ColCtx cx{eb, c, fmaxq, job.scales, job.zeros,
               (int64_t)(row0 + lane) * ngroups_row + i1 / G, live};
     column_steps<G, 0>(w, packed, s, z, obs, cx);
     if (live) {
@@ -258,7 +275,7 @@ __global__ __launch_bounds__(64) void gptq_kernel(GptqPlan p) {
     // lazy update of the later columns: Wf[:, i2:] -= E U[i1:i2, i2:]
     const int i2 = i1 + kRB;
     if (i2 < c) {
-      far_update(w, Wf, UT, c, i1, i2, lane);
+      far_update(w, Wf, UT, c, i1, i2, lane, eb);
       __threadfence_block();
       __syncthreads();
     }
