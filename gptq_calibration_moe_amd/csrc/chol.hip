@@ -25,7 +25,8 @@
 //   left-looking Cholesky, per 64-column block step k:
 //     chol_left     T_i = A[i][k] - sum_{m<k} L[i][m] L[k][m]^T for block rows i >= k
 //                   (a chunked fp64 MFMA product, next chunk prefetched)
-//     chol_diag     L_kk = chol(T_k) and its inverse Dinv_k (one workgroup per matrix)
+//     chol_diag     L_kk = chol(T_k) and its inverse Dinv_k (one wavefront per matrix,
+//                   rows in registers)
 //     chol_panel    L[i][k] = T_i Dinv_k^T for i > k
 //   per block row i:
 //     trtri_row     X[i][j] = -Linv_ii sum_m L[i][m] X[m][j] (X = L^-1, fp64),
@@ -206,52 +207,74 @@ __global__ __launch_bounds__(256) void chol_left_kernel(double* __restrict__ Aal
       }
 }
 
-// Step k: L_kk = chol(T_k) and Dinv_k = L_kk^-1 (one workgroup per matrix).
-__global__ __launch_bounds__(256) void chol_diag_kernel(const double* __restrict__ Aall, int c, int k,
-                                                        double* __restrict__ dinv,
-                                                        int* __restrict__ status) {
-  __shared__ double L[kNb][kNb + 1];
-  __shared__ double X[kNb][kNb + 1];
-  const int m = blockIdx.x;
+// Step k: L_kk = chol(T_k) and Dinv_k = L_kk^-1, one wavefront per matrix.
+// Lane r holds row r of the 64x64 block in registers; a pivot or a column
+// value is broadcast with readlane, so no step needs a barrier.  The template
+// recursion keeps every register index a compile-time constant.
+__device__ __forceinline__ double lane_value(double v, int src) {
+  const uint64_t b = __double_as_longlong(v);
+  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)b, src);
+  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(b >> 32), src);
+  return __longlong_as_double(((uint64_t)hi << 32) | lo);
+}
+
+// Cholesky column J: a[] is this lane's row of the block being factored.
+template <int J>
+__device__ __forceinline__ void chol_cols(double (&a)[kNb], double (&piv)[kNb], int r, bool& bad) {
+  double d = lane_value(a[J], J);
+  if (!(d > 0.0)) {
+    bad = true;
+    d = 1.0;
+  }
+  const double ljj = sqrt(d);
+  piv[J] = ljj;
+  if (r == J) a[J] = ljj;
+  if (r > J) a[J] = a[J] / ljj;
+#pragma unroll
+  for (int cc = J + 1; cc < kNb; ++cc) a[cc] = fma(-a[J], lane_value(a[J], cc), a[cc]);
+  if constexpr (J + 1 < kNb) chol_cols<J + 1>(a, piv, r, bad);
+}
+
+// Forward elimination on L X = I, pivot row J: x[] is this lane's row of X.
+template <int J>
+__device__ __forceinline__ void inv_rows(const double (&a)[kNb], const double (&piv)[kNb],
+                                         double (&x)[kNb], int r) {
+  const double inv = 1.0 / piv[J];
+  if (r == J) {
+#pragma unroll
+    for (int cc = 0; cc <= J; ++cc) x[cc] *= inv;
+  }
+#pragma unroll
+  for (int cc = 0; cc <= J; ++cc) {
+    const double xj = lane_value(x[cc], J);
+    if (r > J) x[cc] = fma(-a[J], xj, x[cc]);
+  }
+  if constexpr (J + 1 < kNb) inv_rows<J + 1>(a, piv, x, r);
+}
+
+__global__ __launch_bounds__(64) void chol_diag_kernel(const double* __restrict__ Aall, int c, int k,
+                                                       double* __restrict__ dinv,
+                                                       int* __restrict__ status) {
+  const int m = blockIdx.x, r = threadIdx.x;
   const double* A = Aall + (int64_t)m * c * c;
   const int64_t k0 = (int64_t)k * kNb;
-  for (int idx = threadIdx.x; idx < kNb * kNb; idx += 256) {
-    const int r = idx >> 6, cc = idx & 63;
-    L[r][cc] = cc <= r ? A[(k0 + r) * c + k0 + cc] : 0.0;
-    X[r][cc] = r == cc ? 1.0 : 0.0;
+  double a[kNb], x[kNb], piv[kNb];
+  const double* row = A + (k0 + r) * c + k0;
+#pragma unroll
+  for (int cc = 0; cc < kNb; cc += 2) {
+    const double2 v = *reinterpret_cast<const double2*>(row + cc);
+    a[cc] = cc <= r ? v.x : 0.0;
+    a[cc + 1] = cc + 1 <= r ? v.y : 0.0;
   }
-  __syncthreads();
-  // right-looking factorisation of the 64x64 block
-  for (int j = 0; j < kNb; ++j) {
-    if (threadIdx.x == 0) {
-      double pv = L[j][j];
-      if (!(pv > 0.0)) {
-        atomicOr(status, kStatusNotPd);
-        pv = 1.0;
-      }
-      L[j][j] = sqrt(pv);
-    }
-    __syncthreads();
-    if (threadIdx.x > j && threadIdx.x < kNb) L[threadIdx.x][j] = L[threadIdx.x][j] / L[j][j];
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < kNb * kNb; idx += 256) {
-      const int r = idx >> 6, cc = idx & 63;
-      if (cc > j && cc <= r) L[r][cc] -= L[r][j] * L[cc][j];
-    }
-    __syncthreads();
-  }
-  // X = L^-1 by forward elimination on L X = I, one pivot row at a time
-  for (int j = 0; j < kNb; ++j) {
-    if (threadIdx.x <= j) X[j][threadIdx.x] = X[j][threadIdx.x] / L[j][j];
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < kNb * kNb; idx += 256) {
-      const int r = idx >> 6, cc = idx & 63;
-      if (r > j && cc <= j) X[r][cc] -= L[r][j] * X[j][cc];
-    }
-    __syncthreads();
-  }
-  double* D = dinv + ((int64_t)m * (c / kNb) + k) * kNb * kNb;
-  for (int idx = threadIdx.x; idx < kNb * kNb; idx += 256) D[idx] = X[idx >> 6][idx & 63];
+  bool bad = false;
+  chol_cols<0>(a, piv, r, bad);
+  if (bad && r == 0) atomicOr(status, kStatusNotPd);
+#pragma unroll
+  for (int cc = 0; cc < kNb; ++cc) x[cc] = cc == r ? 1.0 : 0.0;
+  inv_rows<0>(a, piv, x, r);
+  double* D = dinv + ((int64_t)m * (c / kNb) + k) * kNb * kNb + (int64_t)r * kNb;
+#pragma unroll
+  for (int cc = 0; cc < kNb; cc += 2) *reinterpret_cast<double2*>(D + cc) = make_double2(x[cc], x[cc + 1]);
 }
 
 // Step k, block row i > k:  L[i][k] = T_i Dinv_k^T.
@@ -366,7 +389,7 @@ void launch_inverse_cholesky(const GptqPlan& p, hipStream_t s) {
                      p.mats, c, p.dead, p.lamd, p.A);
   for (int k = 0; k < nbk; ++k) {
     hipLaunchKernelGGL(chol_left_kernel, dim3(nbk - k, p.n_mats), dim3(256), 0, s, p.A, c, k);
-    hipLaunchKernelGGL(chol_diag_kernel, dim3(p.n_mats), dim3(256), 0, s, p.A, c, k, p.dinv, p.status);
+    hipLaunchKernelGGL(chol_diag_kernel, dim3(p.n_mats), dim3(64), 0, s, p.A, c, k, p.dinv, p.status);
     if (k + 1 < nbk)
       hipLaunchKernelGGL(chol_panel_kernel, dim3(nbk - k - 1, p.n_mats), dim3(256), 0, s, p.A, c, k,
                          p.dinv);
