@@ -36,6 +36,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", type=int, default=2, help="workload id of gen.WORKLOADS (default 2)")
+    ap.add_argument("--copy-probe", type=int, metavar="BYTES", help="only copy BYTES on the device and exit")
+    ap.add_argument("--profile-commands", metavar="DIR", help="print the profiling command lines and exit")
+    ap.add_argument("--summarize-profiles", metavar="DIR", help="write profiles/ summaries from DIR and exit")
     return ap.parse_args()
 
 
@@ -47,11 +50,13 @@ def syrk_source_hash():
     return hashlib.sha256(open(SYRK_SRC, "rb").read()).hexdigest()[:16]
 
 
-def cpu_baseline(wl, inp, w_expert0):
+def cpu_baseline(wl, inp, w_host, budget_s=10.0):
     """The CPU oracle, as it stands, on a bounded sample of the same workload:
-    routing and bucketing of all tokens of both layers, then Gram sums of routed
-    expert 0 in both layers, aggregation, GPTQ of its gate|up job and its loss."""
+    routing and bucketing of all tokens of both layers, then, routed expert by
+    routed expert until about budget_s seconds have passed, the expert's Gram
+    sums in both layers, aggregation, GPTQ of its gate|up job and its loss."""
     import numpy as np
+    import gen
     import oracle
     threads = os.cpu_count()
     try:
@@ -62,28 +67,151 @@ def cpu_baseline(wl, inp, w_expert0):
     except Exception:
         pass
     t0 = time.perf_counter()
-    S, n = [], []
-    for l in range(2):
-        tk = oracle.route(inp["logits"][l], wl.top_k)
-        s_l, c_l = oracle.layer_hessians(inp["x"][l], tk, wl.n_routed, wl.n_shared, slots=[0])
-        S.append(s_l[0])
-        n.append(c_l[0])
-    H, _ = oracle.aggregate(S, n, wl.alpha)
-    import gen
-    wv = gen.weights_value(wl, w_expert0).astype(np.float64)
-    g = oracle.gptq(wv, H, wl.bits, wl.group, wl.damp, wl.block)
-    oracle.loss(wv, g["wq"], H)
+    topk = [oracle.route(inp["logits"][l], wl.top_k) for l in range(2)]
+    done = 0
+    for e in range(wl.n_routed):
+        S, n = [], []
+        for l in range(2):
+            s_l, c_l = oracle.layer_hessians(inp["x"][l], topk[l], wl.n_routed, wl.n_shared, slots=[e])
+            S.append(s_l[e])
+            n.append(c_l[e])
+        H, _ = oracle.aggregate(S, n, wl.alpha)
+        wv = gen.weights_value(wl, w_host[e]).astype(np.float64)
+        g = oracle.gptq(wv, H, wl.bits, wl.group, wl.damp, wl.block)
+        oracle.loss(wv, g["wq"], H)
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
     dt = time.perf_counter() - t0
-    mats = len(wl.mats)
+    mats = done * len(wl.mats)
     return {"value": round(mats / dt, 4), "unit": "matrices/s", "cores": int(threads), "kind": "oracle",
-            "sample": (f"oracle (fp64 NumPy) on routed expert 0 of the {wl.name} workload: routing and "
-                       f"bucketing of all {wl.n_tokens} tokens of both layers, that expert's Gram sums in "
-                       f"both layers, aggregation, GPTQ of its {wl.job_rows}x{wl.d} gate|up job and the "
-                       f"loss = {mats} matrices in {dt:.2f} s")}
+            "sample": (f"oracle (fp64 NumPy) on routed experts 0..{done - 1} of the {wl.name} workload: "
+                       f"routing and bucketing of all {wl.n_tokens} tokens of both layers, then per expert "
+                       f"its Gram sums in both layers, aggregation, GPTQ of its {wl.job_rows}x{wl.d} "
+                       f"gate|up job and the loss = {mats} matrices in {dt:.2f} s")}
+
+
+# Profiling runs behind the committed summaries.  The counter runs read
+# FETCH_SIZE and WRITE_SIZE (KiB per dispatch) in passes of their own; the
+# copy probe moves a known number of bytes so that each counter can be scaled
+# to bytes.  `--profile-commands DIR` prints these lines; `--summarize-profiles
+# DIR` turns their CSV output into the text summaries.
+COPY_BYTES = 1 << 30
+PROFILE_RUNS = [
+    ("trace", "timeout -k 10 600 rocprofv3 --kernel-trace --stats --output-format csv -d {dir}/trace -o run "
+              "-- python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline"),
+    ("fetch", "timeout -s KILL 300 rocprofv3 --pmc FETCH_SIZE --output-format csv -d {dir}/fetch -o run "
+              "-- python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline"),
+    ("write", "timeout -s KILL 300 rocprofv3 --pmc WRITE_SIZE --output-format csv -d {dir}/write -o run "
+              "-- python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline"),
+    ("copy_fetch", "timeout -s KILL 60 rocprofv3 --pmc FETCH_SIZE --output-format csv -d {dir}/copy_fetch -o run "
+                   f"-- python3 bench.py --copy-probe {COPY_BYTES}"),
+    ("copy_write", "timeout -s KILL 60 rocprofv3 --pmc WRITE_SIZE --output-format csv -d {dir}/copy_write -o run "
+                   f"-- python3 bench.py --copy-probe {COPY_BYTES}"),
+]
+
+
+def copy_probe(nbytes):
+    """One plain device-to-device copy of nbytes (the counter scale reference)."""
+    import torch
+    src = torch.ones(nbytes // 4, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes}), flush=True)
+
+
+def _csv(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def _find(d, suffix):
+    for root, _, files in os.walk(d):
+        for f in files:
+            if f.endswith(suffix):
+                return os.path.join(root, f)
+    raise FileNotFoundError(f"no *{suffix} under {d}")
+
+
+def _short(name):
+    name = name.replace("void ", "")
+    return name.split("(")[0] if name.startswith("clha::") else name[:70]
+
+
+def summarize_profiles(d, workload_name="mid_moe_block"):
+    """Writes the kernel-trace summary and the per-kernel HBM traffic summary
+    (counter values scaled by the copy probe) under profiles/."""
+    steps = 4      # the trace run does 1 warm-up and 3 timed steps
+    stats = _csv(_find(os.path.join(d, "trace"), "kernel_stats.csv"))
+    cmd = {k: c.format(dir=d) for k, c in PROFILE_RUNS}
+    lines = [f"# Kernel time per step, {workload_name} workload (MI355X, rocprofv3 kernel trace)", "",
+             "Command (repository root):", "", f"    {cmd['trace']}", "",
+             f"{steps} steps traced (1 warm-up + 3 timed); per-step figures are totals / {steps}.", "",
+             "| kernel | calls/step | ms/step | avg us/launch | % |", "|---|---:|---:|---:|---:|"]
+    total = sum(float(r["TotalDurationNs"]) for r in stats)
+    for r in stats:
+        t = float(r["TotalDurationNs"])
+        lines.append(f"| {_short(r['Name'])} | {int(r['Calls']) / steps:g} | {t / 1e6 / steps:.3f} | "
+                     f"{float(r['AverageNs']) / 1e3:.1f} | {100 * t / total:.1f} |")
+    lines += ["", f"Sum of kernel time per step: {total / 1e6 / steps:.3f} ms", ""]
+    open(os.path.join(ROOT, "profiles", f"clha_step_{workload_name}_kernel_trace.md"), "w").write("\n".join(lines))
+
+    def per_kernel(sub, counter):
+        acc = {}
+        for r in _csv(_find(os.path.join(d, sub), "counter_collection.csv")):
+            if r["Counter_Name"] != counter:
+                continue
+            k = _short(r["Kernel_Name"])
+            v = acc.setdefault(k, [0.0, 0])
+            v[0] += float(r["Counter_Value"])
+            v[1] += 1
+        return acc
+
+    def copy_kib(sub, counter):
+        vals = [float(v[0]) / v[1] for k, v in per_kernel(sub, counter).items() if "copyBuffer" in k]
+        return max(vals)
+    copy_kib_total = COPY_BYTES / 1024
+    f_scale = copy_kib_total / copy_kib("copy_fetch", "FETCH_SIZE")
+    w_scale = copy_kib_total / copy_kib("copy_write", "WRITE_SIZE")
+    fetch, write = per_kernel("fetch", "FETCH_SIZE"), per_kernel("write", "WRITE_SIZE")
+    lines = [f"# HBM traffic per launch, {workload_name} workload (MI355X, rocprofv3 counters)", "",
+             "Commands (repository root), one counter per run:", ""]
+    lines += [f"    {cmd[k]}" for k in ("fetch", "write", "copy_fetch", "copy_write")]
+    lines += ["", f"Scale: a {COPY_BYTES} B device copy reads FETCH_SIZE x {f_scale:.3f} and "
+              f"WRITE_SIZE x {w_scale:.3f} of its bytes; every figure below is scaled by these factors.", "",
+              "| kernel | launches | read GB/launch | written GB/launch |", "|---|---:|---:|---:|"]
+    for k in sorted(fetch, key=lambda k: -fetch[k][0]):
+        if k not in write:
+            continue
+        rd = fetch[k][0] / fetch[k][1] * 1024 * f_scale
+        wr = write[k][0] / write[k][1] * 1024 * w_scale
+        lines.append(f"| {k} | {fetch[k][1]} | {rd / 1e9:.4f} | {wr / 1e9:.4f} |")
+    open(os.path.join(ROOT, "profiles", f"clha_step_{workload_name}_hbm_traffic.md"), "w").write("\n".join(lines) + "\n")
+    sk = "clha::syrk_kernel"
+    rec = {"workload": workload_name, "kernel": "syrk_kernel", "syrk_source_sha256_16": syrk_source_hash(),
+           "fetch_kib_per_launch": fetch[sk][0] / fetch[sk][1], "write_kib_per_launch": write[sk][0] / write[sk][1],
+           "fetch_scale": f_scale, "write_scale": w_scale,
+           "hbm_bytes_per_launch": (fetch[sk][0] / fetch[sk][1] * f_scale + write[sk][0] / write[sk][1] * w_scale) * 1024,
+           "commands": [cmd[k] for k in ("fetch", "write", "copy_fetch", "copy_write")]}
+    json.dump(rec, open(TRAFFIC_FILE, "w"), indent=1)
+    print(json.dumps(rec))
 
 
 def main():
     args = parse()
+    if args.profile_commands:
+        for _, c in PROFILE_RUNS:
+            print(c.format(dir=args.profile_commands))
+        return 0
+    if args.summarize_profiles:
+        summarize_profiles(args.summarize_profiles)
+        return 0
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (every run here uses "
               "exactly one MI355X; the multi-GPU design is described, not built)", file=sys.stderr)
@@ -172,7 +300,7 @@ def main():
            "roofline": roofline, "stages_ms_per_step": stages_ms}
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
-        out["cpu_baseline"] = cpu_baseline(wl, inp, w_host[0])
+        out["cpu_baseline"] = cpu_baseline(wl, inp, w_host)
     print(json.dumps(out), flush=True)
     return 0
 
