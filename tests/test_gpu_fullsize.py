@@ -1,0 +1,215 @@
+"""Parity at full workload sizes, on outputs the oracle can compute one by one.
+
+* mid MoE block, exactly as the benchmark step runs it: d 2048, 64 routed + 2
+  shared experts, top-6, 65,536 tokens per layer, routing-frequency alpha, 66
+  stacked gate|up jobs of 2816x2048 bf16, 3-bit, group 128.  Checked: routing,
+  counts and token lists of every token (bit-exact); the combined Hessian of
+  sampled routed experts and of the shared slot; GPTQ codes, grids and loss of
+  those experts.
+* full-depth shapes (d 2048, Zipf(1.1) expert load, equal alpha, 2-bit) on one
+  pair at 16,384 tokens: the most and least loaded experts end to end.
+* drift stress (d 4096, 128 experts, top-8, router logits from the activations,
+  group 64, 2048x4096 matrices) at 65,536 tokens and t = 0.5: rt, eq and PLIC
+  Hessians, GPTQ under rt, and the per-layer losses under each layer's own
+  Hessian (the calibration-Hessian error of the CLHA summary, section 4).
+
+Tolerances: routing bit-exact; Hessians 1e-4 normalised by sqrt(H_ii H_jj);
+codes >= 99.9 % identical; loss within 1e-3 relative.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gen
+import oracle
+from gpu_util import (CODE_AGREE, HESS_TOL, LOSS_RTOL, agree, bits_to_dev, dev, hess_err, to_dev,
+                      weights_to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gptq_calibration_moe_amd  # noqa: F401  (fails loudly if the library is missing)
+
+
+def _expert_rows(x_bits, token_ids, offsets, e):
+    ids = token_ids[offsets[e]:offsets[e + 1]]
+    return oracle.bf16_to_f64(x_bits[ids])
+
+
+def _check_gptq(wl, w_bits, H_ref, out, bits, label):
+    wv = gen.weights_value(wl, w_bits).astype(np.float64)
+    ref = oracle.gptq(wv, H_ref, bits, wl.group, wl.damp, wl.block)
+    codes = out["codes"].cpu().numpy()
+    a = agree(codes, ref["codes"])
+    assert a >= CODE_AGREE, f"{label}: codes agree {a:.5f}"
+    assert codes.max() <= (1 << bits) - 1
+    ok = (codes == ref["codes"]).all(axis=1)               # rows decided identically throughout
+    assert ok.mean() >= 0.9, f"{label}: only {ok.mean():.3f} of the rows agree in every code"
+    np.testing.assert_allclose(out["scales"].cpu().numpy()[ok], ref["scales"][ok], rtol=1e-5)
+    assert (out["zeros"].cpu().numpy()[ok] == ref["zeros"][ok]).all(), label
+    ref_loss = oracle.loss(wv, ref["wq"], H_ref)
+    got = float(out["loss"].cpu().numpy()[0])
+    assert abs(got - ref_loss) <= LOSS_RTOL * abs(ref_loss), f"{label}: loss {got} vs {ref_loss}"
+    return ref
+
+
+def test_mid_moe_block_full_size_in_bench_configuration():
+    import gptq_calibration_moe_amd as clha
+    from gptq_calibration_moe_amd.calibrate import SharedGroupCalibration
+
+    wl = gen.WORKLOADS[2]
+    inp = gen.pair_inputs(wl)
+    experts = list(range(wl.n_experts_total))
+    w_host = {e: gen.expert_weights(wl, 0, e) for e in experts}
+    n, E, K = wl.n_tokens, wl.n_routed, wl.top_k
+
+    # the benchmark's step: reset, collect both layers, aggregate, one GPTQ batch of all jobs
+    ctx = clha.Context(wl.d, E, K, wl.n_shared, max_tokens=n, device=dev())
+    cal = SharedGroupCalibration(ctx, [0, 1])
+    W = {e: weights_to_dev(wl, w) for e, w in w_host.items()}
+    prep, outputs = cal.prepare_quantize(W, wl.bits, wl.shared_bits, wl.group)
+    routing = []
+    cal.reset()
+    for l in range(2):
+        r = {"topk_out": torch.empty(n, K, dtype=torch.int32, device=dev()),
+             "offsets_out": torch.empty(E + 1, dtype=torch.int64, device=dev()),
+             "token_ids_out": torch.empty(n * K, dtype=torch.int32, device=dev())}
+        cal.collect(l, bits_to_dev(inp["x"][l]), to_dev(inp["logits"][l]), **r)
+        routing.append(r)
+    cal.aggregate(wl.alpha)
+    ctx.run_gptq(prep, wl.group, wl.block, wl.damp)
+    ctx.sync()
+
+    # routing of every token, bit-exact
+    buckets = []
+    for l in range(2):
+        tk = oracle.route(inp["logits"][l], K)
+        counts, offsets, ids = oracle.bucket(tk, E)
+        assert np.array_equal(routing[l]["topk_out"].cpu().numpy(), tk)
+        assert np.array_equal(routing[l]["offsets_out"].cpu().numpy(), offsets)
+        assert np.array_equal(routing[l]["token_ids_out"].cpu().numpy(), ids)
+        got_counts = cal.counts[l].cpu().numpy()
+        assert np.array_equal(got_counts[:E], counts) and got_counts[E] == n
+        buckets.append((counts, offsets, ids))
+
+    # sampled routed experts and the shared slot: H_comb, then GPTQ end to end
+    rng = np.random.default_rng(7)
+    sample = sorted(rng.choice(E, 2, replace=False).tolist()) + [E]        # E = first shared expert
+    for e in sample:
+        S, cnt = [], []
+        for l in range(2):
+            if e < E:
+                counts, offsets, ids = buckets[l]
+                S.append(oracle.gram(_expert_rows(inp["x"][l], ids, offsets, e)))
+                cnt.append(int(counts[e]))
+            else:
+                S.append(oracle.gram(oracle.bf16_to_f64(inp["x"][l])))
+                cnt.append(n)
+        H_ref, _ = oracle.aggregate(S, cnt, wl.alpha)
+        slot = cal.slot_of(e)
+        err = hess_err(cal.H[slot].cpu().numpy(), H_ref)
+        assert err <= HESS_TOL, f"expert {e}: H_comb error {err:.3e}"
+        bits = wl.shared_bits if e >= E else wl.bits
+        _check_gptq(wl, w_host[e], H_ref, outputs[e], bits, f"expert {e}")
+
+
+def test_full_depth_shapes_zipf_load_one_pair():
+    import gptq_calibration_moe_amd as clha
+    from gptq_calibration_moe_amd.calibrate import SharedGroupCalibration
+
+    wl = gen.WORKLOADS[3].scaled(n_tokens=16384, n_pairs=1)
+    inp = gen.pair_inputs(wl)
+    n, E, K = wl.n_tokens, wl.n_routed, wl.top_k
+    ctx = clha.Context(wl.d, E, K, wl.n_shared, max_tokens=n, device=dev())
+    cal = SharedGroupCalibration(ctx, [0, 1])
+    cal.reset()
+    for l in range(2):
+        cal.collect(l, bits_to_dev(inp["x"][l]), to_dev(inp["logits"][l]))
+    cal.aggregate(wl.alpha)
+    ctx.sync()
+    buckets = []
+    for l in range(2):
+        counts, offsets, ids = oracle.bucket(oracle.route(inp["logits"][l], K), E)
+        assert np.array_equal(cal.counts[l].cpu().numpy()[:E], counts)
+        buckets.append((counts, offsets, ids))
+    load = buckets[0][0] + buckets[1][0]
+    sample = [int(np.argmax(load)), int(np.argmin(load))]
+    assert load[sample[0]] > 8 * load[sample[1]]          # the Zipf skew is really there
+    w_host = {e: gen.expert_weights(wl, 0, e) for e in sample}
+    outputs = cal.quantize({e: weights_to_dev(wl, w) for e, w in w_host.items()}, wl.bits,
+                           wl.shared_bits, wl.group, block=wl.block, damp=wl.damp)
+    ctx.sync()
+    for e in sample:
+        S = [oracle.gram(_expert_rows(inp["x"][l], buckets[l][2], buckets[l][1], e)) for l in range(2)]
+        H_ref, _ = oracle.aggregate(S, [int(buckets[l][0][e]) for l in range(2)], wl.alpha)
+        err = hess_err(cal.H[e].cpu().numpy(), H_ref)
+        assert err <= HESS_TOL, f"expert {e}: H_comb error {err:.3e}"
+        _check_gptq(wl, w_host[e], H_ref, outputs[e], wl.bits, f"expert {e} (load {load[e]})")
+
+
+def test_drift_stress_d4096_per_layer_losses():
+    import gptq_calibration_moe_amd as clha
+    from gptq_calibration_moe_amd.calibrate import SharedGroupCalibration
+
+    # 65,536 tokens give each expert about 8k rows over the pair, more than d, as the
+    # workload's 262,144 tokens do.  With fewer rows than d the damped Hessian is
+    # mostly lambda I and ill-conditioned (cond ~1e3 at 8,192 tokens); then storing
+    # H in fp32 alone moves ~0.05 % of the codes and the GPU's fp32 sums ~0.2 %.
+    wl = gen.WORKLOADS[5].scaled(n_tokens=65536)
+    t = 0.5
+    inp = gen.pair_inputs(wl, t=t)
+    n, E, K, d = wl.n_tokens, wl.n_routed, wl.top_k, wl.d
+    ctx = clha.Context(d, E, K, wl.n_shared, max_tokens=n, device=dev())
+    cal = SharedGroupCalibration(ctx, [0, 1])
+    cal.reset()
+    for l in range(2):
+        cal.collect(l, bits_to_dev(inp["x"][l]), to_dev(inp["logits"][l]))
+    ctx.sync()
+    buckets = [oracle.bucket(oracle.route(inp["logits"][l], K), E) for l in range(2)]
+    for l in range(2):
+        assert np.array_equal(cal.counts[l].cpu().numpy()[:E], buckets[l][0])
+    sample = [5, 77]
+    S = {e: [oracle.gram(_expert_rows(inp["x"][l], buckets[l][2], buckets[l][1], e)) for l in range(2)]
+         for e in sample}
+    cnt = {e: [int(buckets[l][0][e]) for l in range(2)] for e in sample}
+
+    # per-layer Hessians (PLIC on each layer) and the eq combination
+    H_layer = []
+    for l in range(2):
+        cal.aggregate("explicit", alpha=[1.0], layers=[l])
+        ctx.sync()
+        H_layer.append({e: cal.H[e].clone() for e in sample})
+        for e in sample:
+            ref, _ = oracle.aggregate([S[e][l]], [cnt[e][l]], "explicit", alpha=[1.0])
+            assert hess_err(H_layer[l][e].cpu().numpy(), ref) <= HESS_TOL
+    cal.aggregate("eq")
+    ctx.sync()
+    for e in sample:
+        ref, _ = oracle.aggregate(S[e], cnt[e], "eq")
+        assert hess_err(cal.H[e].cpu().numpy(), ref) <= HESS_TOL
+
+    # rt combination, GPTQ, and the loss under each layer's own Hessian
+    cal.aggregate("rt")
+    w_host = {e: gen.expert_weights(wl, 0, e) for e in sample}
+    outputs = cal.quantize({e: weights_to_dev(wl, w) for e, w in w_host.items()}, wl.bits,
+                           wl.shared_bits, wl.group, block=wl.block, damp=wl.damp)
+    ctx.sync()
+    for e in sample:
+        H_ref, _ = oracle.aggregate(S[e], cnt[e], "rt")
+        assert hess_err(cal.H[e].cpu().numpy(), H_ref) <= HESS_TOL
+        ref = _check_gptq(wl, w_host[e], H_ref, outputs[e], wl.bits, f"expert {e}")
+        wv = gen.weights_value(wl, w_host[e]).astype(np.float64)
+        Wd = weights_to_dev(wl, w_host[e])
+        for l in range(2):
+            H_l, _ = oracle.aggregate([S[e][l]], [cnt[e][l]], "explicit", alpha=[1.0])
+            want = oracle.loss(wv, ref["wq"], H_l)
+            got = torch.empty(1, dtype=torch.float32, device=dev())
+            o = outputs[e]
+            ctx.loss(Wd, o["codes"], o["scales"], o["zeros"], H_layer[l][e], wl.group, got)
+            ctx.sync()
+            g = float(got.cpu().numpy()[0])
+            assert abs(g - want) <= LOSS_RTOL * abs(want), f"expert {e} layer {l}: {g} vs {want}"
