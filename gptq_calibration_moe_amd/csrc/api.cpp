@@ -206,6 +206,7 @@ struct GptqLayout {
   uint8_t* dead;
   double* lamd;
   float* wf;
+  float* ebuf;
   double* partials;
   size_t bytes;
 };
@@ -224,6 +225,7 @@ GptqLayout gptq_layout(void* ws, int n_jobs, int n_mats, int cols, int64_t wf_el
   L.dead = c.take<uint8_t>((size_t)n_mats * cols);
   L.lamd = c.take<double>((size_t)n_mats);
   L.wf = need_wf ? c.take<float>((size_t)wf_elems) : nullptr;
+  L.ebuf = need_wf && cols > clha::kSuper ? c.take<float>((size_t)(wf_elems / cols) * clha::kSuper) : nullptr;
   L.partials = need_wf ? c.take<double>((size_t)2 * (total_slabs > 0 ? total_slabs : 1)) : nullptr;
   L.bytes = c.off;
   return L;
@@ -499,7 +501,7 @@ CLHA_API clha_status clha_gptq_quantize(clha_ctx* ctx, int32_t n_jobs, const clh
   std::vector<char> host(up256(sizeof(GJob) * n_jobs) + sizeof(float*) * n_mats);
   GJob* hj = reinterpret_cast<GJob*>(host.data());
   int64_t wf_off = 0;
-  int slab_base = 0;
+  int slab_base = 0, tile_base = 0;
   for (int i = 0; i < n_jobs; ++i) {
     const clha_gptq_job& j = jobs[i];
     GJob g;
@@ -515,9 +517,12 @@ CLHA_API clha_status clha_gptq_quantize(clha_ctx* ctx, int32_t n_jobs, const clh
     g.mat = js.mat_of[i];
     g.slab_base = slab_base;
     g.n_slabs = (j.rows + clha::kGptqRows - 1) / clha::kGptqRows;
+    g.tile_base = tile_base;
+    g.n_tiles = (g.n_slabs * clha::kGptqRows + clha::kGemmTile - 1) / clha::kGemmTile;
     hj[i] = g;
     wf_off += (int64_t)g.n_slabs * clha::kGptqRows * cols;
     slab_base += g.n_slabs;
+    tile_base += g.n_tiles;
   }
   std::memcpy(host.data() + up256(sizeof(GJob) * n_jobs), js.mats.data(), sizeof(float*) * n_mats);
   const hipStream_t s = as_stream(stream);
@@ -533,6 +538,7 @@ CLHA_API clha_status clha_gptq_quantize(clha_ctx* ctx, int32_t n_jobs, const clh
   p.group = group;
   p.block = block;
   p.total_slabs = (int)js.total_slabs;
+  p.total_tiles = tile_base;
   p.damp = damp;
   p.jobs = L.jobs;
   p.mats = L.mats;
@@ -545,6 +551,7 @@ CLHA_API clha_status clha_gptq_quantize(clha_ctx* ctx, int32_t n_jobs, const clh
   p.lamd = L.lamd;
   p.lam = nullptr;
   p.wf = L.wf;
+  p.ebuf = L.ebuf;
   p.partials = reinterpret_cast<float*>(L.partials);
   p.status = ctx->status_dev;
   {

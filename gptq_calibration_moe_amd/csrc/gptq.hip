@@ -10,17 +10,22 @@
 // to the columns after the block.  The grid of each (row, group) is fitted at
 // the group's first column on the weights updated so far.
 //
-// Work decomposition.  Rows are independent given U, so one wavefront owns a
-// slab of 64 rows (one workgroup = one wave) and one thread owns one row:
-//   * the row's current 64-column block lives in 64 registers; the column loop
-//     is fully unrolled, so quantization, the error and the rank-1 update of
-//     the rest of the block are register arithmetic with no barrier -- the
-//     U values of column j are the same for every row (uniform loads);
-//   * codes, scales and zero points are decided in fp32 with IEEE division and
-//     round-half-to-even, exactly as the definition states;
-//   * the block's 64x64 errors then update every later column of the slab's
-//     fp32 working copy through U[block, later] on the fp32 matrix cores
-//     (v_mfma_f32_32x32x2f32) in 64-row x 32-column tiles.
+// Work decomposition.  Rows are independent given U.  Columns are processed
+// in superblocks of kSuper (256) columns, each in two launches:
+//   * the panel kernel: one wavefront owns a slab of 64 rows, one thread one
+//     row.  The row's current 64-column block lives in 64 registers; the column
+//     loop is fully unrolled, so quantization, the error and the rank-1 update
+//     of the rest of the block are register arithmetic with no barrier (the U
+//     values of column j are the same for every row: LDS broadcasts).  Codes,
+//     scales and zero points are decided in fp32 with IEEE division and
+//     round-half-to-even.  After each 64-column block its errors update the
+//     later columns of the same superblock (fp32 matrix cores,
+//     v_mfma_f32_32x32x2f32, 64-row x 32-column tiles) and are stored for the
+//     next launch;
+//   * the trailing kernel: Wf[:, later] -= E U[superblock, later] for every row
+//     of every job at once, a batched fp32 GEMM with K = 256 in 128x128 tiles
+//     staged through LDS, so each later weight is read and written once per
+//     superblock instead of once per 64 columns.
 // The loss uses the OBS identity: sum_j err_j^2 = tr[(Wq - W) Hd (Wq - W)^T],
 // so the undamped loss is sum err^2 - lambda ||Wq - W||^2 (W after zeroing
 // dead columns); ||Wq - W||^2 is a separate coalesced pass over the outputs.
@@ -32,12 +37,14 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kRB = 64;             // register block: columns held per thread
 
-__device__ __forceinline__ float load_w(const void* W, int dtype, int64_t i) {
+// Four consecutive weights (16-byte aligned fp32 or 8-byte aligned bf16).
+__device__ __forceinline__ float4 load_w4(const void* W, int dtype, int64_t i) {
   if (dtype == 1) {
-    const uint32_t b = reinterpret_cast<const uint16_t*>(W)[i];
-    return __uint_as_float(b << 16);
+    const uint2 b = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(W) + i);
+    return make_float4(__uint_as_float(b.x << 16), __uint_as_float(b.x & 0xffff0000u),
+                       __uint_as_float(b.y << 16), __uint_as_float(b.y & 0xffff0000u));
   }
-  return reinterpret_cast<const float*>(W)[i];
+  return *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(W) + i);
 }
 
 __device__ __forceinline__ void fit_grid(float xmin, float xmax, float fmaxq, float& s, float& z) {
@@ -143,7 +150,7 @@ struct TileBuf {
   }
 };
 
-// Wf[:, jt0:] -= E U[i1:i1+64, jt0:] for one 64-row slab, E = the block's
+// Wf[:, jt0:cend] -= E U[i1:i1+64, jt0:cend] for one 64-row slab, E = the block's
 // errors (thread-per-row in e[]).  Transposed product on the fp32 matrix cores:
 // C[i][j] = sum_k U[i1+k][jt+i] E[j][k] is the update of W[row j][column jt+i].
 // With U as the A operand (read from U^T, so a lane's operands are contiguous)
@@ -154,7 +161,7 @@ struct TileBuf {
 // double-buffered: the next tile's U and W load while the current tile's
 // products run.
 __device__ __forceinline__ void far_update(const float (&e)[kRB], float* Wf, const float* UT, int c,
-                                           int i1, int jt0, int lane, float* eb) {
+                                           int i1, int jt0, int cend, int lane, float* eb) {
   const int kh = lane >> 5, lc = lane & 31;
   // B operands for rows 0..31 (mb 0) and 32..63 (mb 1), negated, into LDS
 #pragma unroll
@@ -172,20 +179,22 @@ __device__ __forceinline__ void far_update(const float (&e)[kRB], float* Wf, con
   TileBuf x, y;
   x.load(utl, wr0, wr1, c, jt0, ucol);
 #pragma unroll 1
-  for (int jt = jt0; jt < c; jt += 64) {
-    const bool second = jt + 32 < c;
+  for (int jt = jt0; jt < cend; jt += 64) {
+    const bool second = jt + 32 < cend;
     if (second) y.load(utl, wr0, wr1, c, jt + 32, ucol);
     x.apply(eb, wr0, wr1, jt, lane);
     if (!second) break;
-    if (jt + 64 < c) x.load(utl, wr0, wr1, c, jt + 64, ucol);
+    if (jt + 64 < cend) x.load(utl, wr0, wr1, c, jt + 64, ucol);
     y.apply(eb, wr0, wr1, jt + 32, lane);
   }
 }
 
+// Columns [c0, min(c, c0 + kSuper)) of every slab.
 template <int G>
-__global__ __launch_bounds__(64, 2) void gptq_kernel(GptqPlan p) {
+__global__ __launch_bounds__(64, 2) void gptq_panel_kernel(GptqPlan p, int c0) {
   __shared__ float eb[kRB * 64];   // the block's errors as MFMA B operands
   const int c = p.cols;
+  const int cend = min(c, c0 + kSuper);
   int lo = 0, hi = p.n_jobs;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
@@ -204,22 +213,30 @@ __global__ __launch_bounds__(64, 2) void gptq_kernel(GptqPlan p) {
   const int lane = threadIdx.x;
   const bool live = lane < nrows;
 
-  // fp32 working copy of the slab (64 rows; rows past the matrix are zero),
-  // dead columns zeroed (coalesced)
-  for (int64_t idx = lane; idx < (int64_t)kGptqRows * c; idx += 64) {
-    const int col = (int)(idx % c);
-    const bool in = idx < (int64_t)nrows * c;
-    const float v = in ? load_w(job.W, job.dtype, (int64_t)row0 * c + idx) : 0.0f;
-    Wf[idx] = dead[col] ? 0.0f : v;
+  // first superblock: its columns of the fp32 working copy (rows past the
+  // matrix are zero, dead columns zeroed); the first trailing update fills the
+  // later columns straight from W
+  if (c0 == 0) {
+    for (int r = 0; r < kGptqRows; ++r) {
+      for (int col = 4 * lane; col < cend; col += 256) {
+        const float4 v = r < nrows ? load_w4(job.W, job.dtype, (int64_t)(row0 + r) * c + col)
+                                   : make_float4(0.f, 0.f, 0.f, 0.f);
+        const uchar4 dd = *reinterpret_cast<const uchar4*>(dead + col);
+        *reinterpret_cast<float4*>(Wf + (int64_t)r * c + col) =
+            make_float4(dd.x ? 0.f : v.x, dd.y ? 0.f : v.y, dd.z ? 0.f : v.z, dd.w ? 0.f : v.w);
+      }
+    }
+    __threadfence_block();
+    __syncthreads();
   }
-  __threadfence_block();
-  __syncthreads();
+  // this row's errors of the superblock, for the trailing update
+  float* erow = cend < c ? p.ebuf + (job.wf_off / c + row0 + lane) * kSuper : nullptr;
 
   double obs = 0.0;
   float s = 1.0f, z = 0.0f;
   float* myrow = Wf + (int64_t)lane * c;
 
-  for (int i1 = 0; i1 < c; i1 += kRB) {
+  for (int i1 = c0; i1 < cend; i1 += kRB) {
     float w[kRB];
 #pragma unroll
     for (int q = 0; q < kRB / 4; ++q) {
@@ -272,19 +289,191 @@ __global__ __launch_bounds__(64, 2) void gptq_kernel(GptqPlan p) {
             make_uint4(packed[4 * q], packed[4 * q + 1], packed[4 * q + 2], packed[4 * q + 3]);
     }
 
-    // lazy update of the later columns: Wf[:, i2:] -= E U[i1:i2, i2:]
+    // rows past the matrix have zero weights and so zero errors
+    if (erow) {
+#pragma unroll
+      for (int q = 0; q < kRB / 4; ++q)
+        *reinterpret_cast<float4*>(erow + (i1 - c0) + 4 * q) =
+            make_float4(w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]);
+    }
+    // lazy update of the superblock's later columns: Wf[:, i2:cend] -= E U[i1:i2, i2:cend]
     const int i2 = i1 + kRB;
-    if (i2 < c) {
-      far_update(w, Wf, UT, c, i1, i2, lane, eb);
+    if (i2 < cend) {
+      far_update(w, Wf, UT, c, i1, i2, cend, lane, eb);
       __threadfence_block();
       __syncthreads();
     }
   }
   double* part = reinterpret_cast<double*>(p.partials) + 2 * (int64_t)blockIdx.x;
-  // sum of err^2 over the slab's live rows, reduced in a fixed lane order
+  // sum of err^2 over the slab's live rows, reduced in a fixed lane order and
+  // added to the earlier superblocks' sum (launches run in order)
   double v = live ? obs : 0.0;
   for (int off = 32; off > 0; off >>= 1) v += __shfl_down(v, off);
-  if (lane == 0) part[0] = v;
+  if (lane == 0) part[0] = c0 == 0 ? v : part[0] + v;
+}
+
+// Trailing update after the superblock at c0, for all jobs:
+//   Wf[:, n0:] -= E U[c0:c0+kSuper, n0:],   n0 = c0 + kSuper,
+// accumulated as -Wf + E U and stored negated.
+// Tile: 128 padded rows x 128 columns of one job, 256 threads = 4 waves of
+// 64x64 (2x2 blocks of v_mfma_f32_32x32x2f32).  As in the panel's update the
+// product is transposed, C[col][row] = sum_k U^T[col][k] E[row][k], so each
+// lane's 16 results are 4 runs of 4 consecutive columns of one row.  Both
+// operands are K-contiguous rows (U^T and the error buffer) staged through LDS
+// in chunks of 32, double-buffered with two register stages.  MFMA step s
+// contracts k = s in lanes 0..31 and k = 16 + s in lanes 32..63 (the same
+// permutation of k for both operands), so a lane's 16 operands of a chunk
+// are 4 contiguous 16-byte LDS reads.  Tiles of one job are mapped to one XCD
+// (workgroup b runs on XCD b % 8), so U and the errors are shared through
+// one L2.
+constexpr int kGK = 32;              // K chunk
+constexpr int kGP = kGK + 4;         // LDS row pitch (floats): conflict-free 16-byte reads
+constexpr int kGBuf = kGemmTile * kGP;
+
+__global__ __launch_bounds__(256, 2) void gptq_trail_kernel(GptqPlan p, int c0) {
+  __shared__ __attribute__((aligned(16))) float lds[4 * kGBuf];   // A0 B0 A1 B1
+  const int c = p.cols, n0 = c0 + kSuper;
+  const int ct = (c - n0 + kGemmTile - 1) / kGemmTile;
+  const int total = p.total_tiles * ct;
+  const int per = (total + kXcds - 1) / kXcds;
+  const int L = (int)(blockIdx.x % kXcds) * per + (int)(blockIdx.x / kXcds);
+  if (L >= total) return;
+  const int rtg = L / ct, cti = L - rtg * ct;
+  int lo = 0, hi = p.n_jobs;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (p.jobs[mid].tile_base <= rtg) lo = mid; else hi = mid;
+  }
+  const GJob job = p.jobs[lo];
+  const int prow0 = (rtg - job.tile_base) * kGemmTile;
+  const int prows = min(kGemmTile, job.n_slabs * kGptqRows - prow0);   // 64 or 128
+  const int col0 = n0 + cti * kGemmTile;
+  const int ncols = min(kGemmTile, c - col0);                         // 64 or 128
+  const int64_t grow = job.wf_off / c + prow0;     // first padded row of the tile (all jobs)
+  const float* __restrict__ UT = p.UT + (int64_t)job.mat * c * c + (int64_t)col0 * c + c0;
+  const float* __restrict__ E = p.ebuf + grow * kSuper;
+  float* W = p.wf + grow * c + col0;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wr = wave >> 1, wc = wave & 1, h = lane >> 5, li = lane & 31;
+  const bool active = wr * 64 < prows && wc * 64 < ncols;
+
+  struct Stage {
+    float4 a[4], b[4];
+  };
+  // thread t moves 16-byte chunks q = t + 256u: row q/8, chunk q%8
+  auto fetch = [&](Stage& r, int k0) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int q = tid + 256 * u, row = q >> 3, ch = q & 7;
+      r.a[u] = row < ncols ? *reinterpret_cast<const float4*>(UT + (int64_t)row * c + k0 + 4 * ch)
+                           : make_float4(0.f, 0.f, 0.f, 0.f);
+      r.b[u] = row < prows ? *reinterpret_cast<const float4*>(E + (int64_t)row * kSuper + k0 + 4 * ch)
+                           : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  auto stage = [&](const Stage& r, int buf) {
+    float* As = lds + (2 * buf) * kGBuf;
+    float* Bs = lds + (2 * buf + 1) * kGBuf;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int q = tid + 256 * u, row = q >> 3, ch = q & 7;
+      *reinterpret_cast<float4*>(As + row * kGP + 4 * ch) = r.a[u];
+      *reinterpret_cast<float4*>(Bs + row * kGP + 4 * ch) = r.b[u];
+    }
+  };
+
+  f32x16 acc[2][2];
+  float* wrow[2];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) wrow[b] = W + (int64_t)(wr * 64 + 32 * b + li) * c + wc * 64 + 4 * h;
+  if (active && c0 == 0) {
+    // first trailing update: the working copy of these columns does not exist
+    // yet; start from W (rows past the matrix zero, dead columns zeroed)
+    const uint8_t* dead = p.dead + (int64_t)job.mat * c + col0 + wc * 64 + 4 * h;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int r = prow0 + wr * 64 + 32 * b + li;
+      const int64_t wbase = (int64_t)r * c + col0 + wc * 64 + 4 * h;
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float4 v = r < job.rows ? load_w4(job.W, job.dtype, wbase + 32 * a + 8 * q)
+                                  : make_float4(0.f, 0.f, 0.f, 0.f);
+          const uchar4 dd = *reinterpret_cast<const uchar4*>(dead + 32 * a + 8 * q);
+          acc[a][b][4 * q] = dd.x ? 0.f : -v.x;
+          acc[a][b][4 * q + 1] = dd.y ? 0.f : -v.y;
+          acc[a][b][4 * q + 2] = dd.z ? 0.f : -v.z;
+          acc[a][b][4 * q + 3] = dd.w ? 0.f : -v.w;
+        }
+    }
+  } else if (active) {
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 v = *reinterpret_cast<const float4*>(wrow[b] + 32 * a + 8 * q);
+          acc[a][b][4 * q] = -v.x;
+          acc[a][b][4 * q + 1] = -v.y;
+          acc[a][b][4 * q + 2] = -v.z;
+          acc[a][b][4 * q + 3] = -v.w;
+        }
+  }
+  auto multiply = [&](int buf) {
+    if (!active) return;
+    const float* As = lds + (2 * buf) * kGBuf + (wc * 64 + li) * kGP + 16 * h;
+    const float* Bs = lds + (2 * buf + 1) * kGBuf + (wr * 64 + li) * kGP + 16 * h;
+    float4 av[2][4], bv[2][4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        av[x][m] = *reinterpret_cast<const float4*>(As + 32 * x * kGP + 4 * m);
+        bv[x][m] = *reinterpret_cast<const float4*>(Bs + 32 * x * kGP + 4 * m);
+      }
+    }
+#pragma unroll
+    for (int st = 0; st < 16; ++st)
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x2f32((&av[a][st >> 2].x)[st & 3],
+                                                           (&bv[b][st >> 2].x)[st & 3], acc[a][b], 0, 0, 0);
+  };
+
+  constexpr int nch = kSuper / kGK;   // 8, even
+  Stage r0, r1;
+  fetch(r0, 0);
+  stage(r0, 0);
+  fetch(r1, kGK);
+  fetch(r0, 2 * kGK);
+  __syncthreads();
+#pragma unroll 1
+  for (int st = 0; st < nch; st += 2) {
+    // chunk st in buffer 0, st+1 in r1, st+2 in r0
+    multiply(0);
+    stage(r1, 1);
+    if (st + 3 < nch) fetch(r1, (st + 3) * kGK);
+    __syncthreads();
+    multiply(1);
+    if (st + 2 < nch) stage(r0, 0);
+    if (st + 4 < nch) fetch(r0, (st + 4) * kGK);
+    __syncthreads();
+  }
+  if (active) {
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<float4*>(wrow[b] + 32 * a + 8 * q) = make_float4(
+              -acc[a][b][4 * q], -acc[a][b][4 * q + 1], -acc[a][b][4 * q + 2], -acc[a][b][4 * q + 3]);
+  }
 }
 
 // ||Wq - W||^2 per slab (W with dead columns zeroed), coalesced over the outputs.
@@ -301,15 +490,25 @@ __global__ __launch_bounds__(256) void gptq_dist_kernel(GptqPlan p) {
   const int nrows = min(kGptqRows, job.rows - row0);
   const uint8_t* dead = p.dead + (int64_t)job.mat * c;
   const int ng = c / group;
+  // four consecutive columns per step (group >= 4, so they share one grid)
   double acc = 0.0;
-  for (int64_t idx = threadIdx.x; idx < (int64_t)nrows * c; idx += 256) {
-    const int r = (int)(idx / c), col = (int)(idx - (int64_t)r * c);
-    const int64_t e = (int64_t)(row0 + r) * c + col;
-    const int64_t gi = (int64_t)(row0 + r) * ng + col / group;
-    const float what = __fmul_rn(job.scales[gi], __fsub_rn((float)job.codes[e], (float)job.zeros[gi]));
-    const float w0 = dead[col] ? 0.0f : load_w(job.W, job.dtype, e);
-    const double dd = (double)what - (double)w0;
-    acc += dd * dd;
+  for (int r = 0; r < nrows; ++r) {
+    const int64_t row = row0 + r;
+    for (int col = 4 * (int)threadIdx.x; col < c; col += 1024) {
+      const int64_t gi = row * ng + col / group;
+      const float sc = job.scales[gi], zp = (float)job.zeros[gi];
+      const uchar4 q = *reinterpret_cast<const uchar4*>(job.codes + row * c + col);
+      const uchar4 dd = *reinterpret_cast<const uchar4*>(dead + col);
+      const float4 w = load_w4(job.W, job.dtype, row * c + col);
+      const float qv[4] = {(float)q.x, (float)q.y, (float)q.z, (float)q.w};
+      const float wv[4] = {dd.x ? 0.f : w.x, dd.y ? 0.f : w.y, dd.z ? 0.f : w.z, dd.w ? 0.f : w.w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float what = __fmul_rn(sc, __fsub_rn(qv[u], zp));
+        const double dv = (double)what - (double)wv[u];
+        acc += dv * dv;
+      }
+    }
   }
   red[threadIdx.x] = acc;
   __syncthreads();
@@ -338,13 +537,21 @@ bool gptq_group_supported(int group) {
 
 void launch_gptq(const GptqPlan& p, hipStream_t s) {
   const dim3 grid(p.total_slabs), blk(64);
-  switch (p.group) {
-    case 4: hipLaunchKernelGGL(gptq_kernel<4>, grid, blk, 0, s, p); break;
-    case 8: hipLaunchKernelGGL(gptq_kernel<8>, grid, blk, 0, s, p); break;
-    case 16: hipLaunchKernelGGL(gptq_kernel<16>, grid, blk, 0, s, p); break;
-    case 32: hipLaunchKernelGGL(gptq_kernel<32>, grid, blk, 0, s, p); break;
-    case 64: hipLaunchKernelGGL(gptq_kernel<64>, grid, blk, 0, s, p); break;
-    default: hipLaunchKernelGGL(gptq_kernel<128>, grid, blk, 0, s, p); break;
+  for (int c0 = 0; c0 < p.cols; c0 += kSuper) {
+    switch (p.group) {
+      case 4: hipLaunchKernelGGL(gptq_panel_kernel<4>, grid, blk, 0, s, p, c0); break;
+      case 8: hipLaunchKernelGGL(gptq_panel_kernel<8>, grid, blk, 0, s, p, c0); break;
+      case 16: hipLaunchKernelGGL(gptq_panel_kernel<16>, grid, blk, 0, s, p, c0); break;
+      case 32: hipLaunchKernelGGL(gptq_panel_kernel<32>, grid, blk, 0, s, p, c0); break;
+      case 64: hipLaunchKernelGGL(gptq_panel_kernel<64>, grid, blk, 0, s, p, c0); break;
+      default: hipLaunchKernelGGL(gptq_panel_kernel<128>, grid, blk, 0, s, p, c0); break;
+    }
+    const int n0 = c0 + kSuper;
+    if (n0 < p.cols) {
+      const int tiles = p.total_tiles * ((p.cols - n0 + kGemmTile - 1) / kGemmTile);
+      const int per = (tiles + kXcds - 1) / kXcds;
+      hipLaunchKernelGGL(gptq_trail_kernel, dim3(per * kXcds), dim3(256), 0, s, p, c0);
+    }
   }
   hipLaunchKernelGGL(gptq_dist_kernel, dim3(p.total_slabs), dim3(256), 0, s, p);
   hipLaunchKernelGGL(gptq_finish_kernel, dim3(p.n_jobs), dim3(64), 0, s, p);

@@ -20,6 +20,8 @@ constexpr int kXcds = 8;              // accelerator complex dies; workgroup b r
 constexpr int kSyrkWgPerXcd = 32;     // persistent Gram-sum workgroups per die (one per CU)
 constexpr int kNb = 64;               // Cholesky / triangular-inverse block
 constexpr int kGptqRows = 64;         // rows per GPTQ workgroup
+constexpr int kSuper = 256;           // GPTQ columns between trailing GEMM updates
+constexpr int kGemmTile = 128;        // rows and columns of a trailing-update tile
 
 // status word bits (device, latched; see clha_sync)
 constexpr int kStatusNonfinite = 1;
@@ -78,10 +80,12 @@ struct GJob {
   int32_t mat;           // index of the job's distinct Hessian
   int32_t slab_base;     // first global slab of this job
   int32_t n_slabs;
+  int32_t tile_base;     // first global row tile (kGemmTile rows) of the trailing update
+  int32_t n_tiles;
 };
 
 struct GptqPlan {
-  int n_jobs, n_mats, cols, group, block, total_slabs;
+  int n_jobs, n_mats, cols, group, block, total_slabs, total_tiles;
   float damp;
   const GJob* jobs;          // device [n_jobs]
   const float* const* mats;  // device [n_mats] Hessian pointers
@@ -94,6 +98,7 @@ struct GptqPlan {
   double* lamd;              // device [n_mats] damping lambda
   float* lam;                // device [n_mats] lambda as float (optional output, may be null)
   float* wf;                 // device fp32 working copies of all jobs' weights
+  float* ebuf;               // device [padded rows][kSuper] a superblock's negated errors
   float* partials;           // device [total_slabs][2]
   int* status;
 };
