@@ -237,6 +237,25 @@ __global__ __launch_bounds__(64, 2) void gptq_panel_kernel(GptqPlan p, int c0) {
   float* myrow = Wf + (int64_t)lane * c;
 
   for (int i1 = c0; i1 < cend; i1 += kRB) {
+    // U's diagonal block of these 64 columns into LDS (coalesced, all loads in
+    // flight together); every lane then reads the same U values (broadcast)
+    __syncthreads();
+    {
+      // lane moves rows lane/16 + 4m, columns 4 (lane % 16) .. +3; an opaque
+      // zero keeps the addresses from being hoisted out of the block loop
+      int opaque;
+      asm volatile("v_mov_b32 %0, 0" : "=v"(opaque));
+      const int r0 = (lane >> 4) + opaque, q4 = 4 * (lane & 15);
+      const float* ug = U + (int64_t)(i1 + r0) * c + i1 + q4;
+      float* ul = eb + r0 * kRB + q4;
+      const int64_t step = 4 * (int64_t)c;
+      float4 ub[kRB * kRB / 4 / 64];
+#pragma unroll
+      for (int m = 0; m < kRB * kRB / 4 / 64; ++m) ub[m] = *reinterpret_cast<const float4*>(ug + m * step);
+#pragma unroll
+      for (int m = 0; m < kRB * kRB / 4 / 64; ++m) *reinterpret_cast<float4*>(ul + 4 * m * kRB) = ub[m];
+    }
+    __syncthreads();
     float w[kRB];
 #pragma unroll
     for (int q = 0; q < kRB / 4; ++q) {
@@ -269,15 +288,6 @@ __global__ __launch_bounds__(64, 2) void gptq_panel_kernel(GptqPlan p, int c0) {
     uint32_t packed[kRB / 4];
 #pragma unroll
     for (int q = 0; q < kRB / 4; ++q) packed[q] = 0u;
-    // the block's diagonal U block into LDS (coalesced); every lane then reads
-    // the same U values (LDS broadcast)
-    __syncthreads();
-    for (int idx = lane; idx < kRB * kRB / 4; idx += 64) {
-      const int r = idx >> 4, q = idx & 15;
-      *reinterpret_cast<float4*>(eb + r * kRB + 4 * q) =
-          *reinterpret_cast<const float4*>(U + (int64_t)(i1 + r) * c + i1 + 4 * q);
-    }
-    __syncthreads();
     ColCtx cx{eb, c, fmaxq, job.scales, job.zeros,
               (int64_t)(row0 + lane) * ngroups_row + i1 / G, live};
     column_steps<G, 0>(w, packed, s, z, obs, cx);
