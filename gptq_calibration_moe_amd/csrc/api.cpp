@@ -49,6 +49,11 @@ struct clha_ctx {
   };
   std::vector<Rec> recs;
   std::vector<hipEvent_t> free_events;
+  // extra streams of the factorisation (default priority) and their events
+  hipStream_t aux[clha::kFactorStreams - 1] = {};
+  hipEvent_t stagger[clha::kFactorStreams] = {};
+  hipEvent_t join[clha::kFactorStreams] = {};
+  bool aux_ready = false;
 };
 
 namespace {
@@ -299,6 +304,15 @@ CLHA_API clha_status clha_destroy(clha_ctx* ctx) {
     hipEventDestroy(r.b);
   }
   for (auto e : ctx->free_events) hipEventDestroy(e);
+  for (auto& a : ctx->aux)
+    if (a) {
+      hipStreamSynchronize(a);
+      hipStreamDestroy(a);
+    }
+  for (int g = 0; g < clha::kFactorStreams; ++g) {
+    if (ctx->stagger[g]) hipEventDestroy(ctx->stagger[g]);
+    if (ctx->join[g]) hipEventDestroy(ctx->join[g]);
+  }
   if (ctx->status_dev) hipFree(ctx->status_dev);
   delete ctx;
   return CLHA_OK;
@@ -447,6 +461,34 @@ CLHA_API clha_status clha_aggregate(clha_ctx* ctx, int32_t n_layers, const int32
   return hip_check(ctx, "aggregate");
 }
 
+// Factorisation of all distinct Hessians: groups of Hessians on up to
+// kFactorStreams streams forked from and joined back to the caller's stream;
+// group g starts once group g-1 has finished its first block step.
+static clha_status run_factor(clha_ctx* ctx, const GptqPlan& p, hipStream_t s) {
+  if (!ctx->aux_ready) {
+    for (auto& a : ctx->aux)
+      if (hipStreamCreateWithFlags(&a, hipStreamNonBlocking) != hipSuccess)
+        return fail(ctx, CLHA_ERR_HIP, "factor: stream creation failed");
+    for (int g = 0; g < clha::kFactorStreams; ++g)
+      if (hipEventCreateWithFlags(&ctx->stagger[g], hipEventDisableTiming) != hipSuccess ||
+          hipEventCreateWithFlags(&ctx->join[g], hipEventDisableTiming) != hipSuccess)
+        return fail(ctx, CLHA_ERR_HIP, "factor: event creation failed");
+    ctx->aux_ready = true;
+  }
+  const int groups = p.n_mats < clha::kFactorStreams ? p.n_mats : clha::kFactorStreams;
+  for (int g = 0; g < groups; ++g) {
+    const int m0 = (int)((int64_t)p.n_mats * g / groups), m1 = (int)((int64_t)p.n_mats * (g + 1) / groups);
+    hipStream_t gs = g == 0 ? s : ctx->aux[g - 1];
+    if (g > 0) hipStreamWaitEvent(gs, ctx->stagger[g - 1], 0);
+    clha::launch_factor_group(p, m0, m1, gs, g + 1 < groups ? ctx->stagger[g] : nullptr);
+  }
+  for (int g = 1; g < groups; ++g) {
+    hipEventRecord(ctx->join[g], ctx->aux[g - 1]);
+    hipStreamWaitEvent(s, ctx->join[g], 0);
+  }
+  return CLHA_OK;
+}
+
 static clha_status check_gptq_args(clha_ctx* ctx, int32_t n_jobs, const clha_gptq_job* jobs,
                                    int32_t cols, int32_t group, int32_t block, float damp) {
   if (n_jobs < 1 || !jobs) return fail(ctx, CLHA_ERR_INVALID_ARG, "gptq: no jobs");
@@ -556,8 +598,9 @@ CLHA_API clha_status clha_gptq_quantize(clha_ctx* ctx, int32_t n_jobs, const clh
   p.status = ctx->status_dev;
   {
     StageTimer t(ctx, CLHA_STAGE_FACTOR, s);
-    clha::launch_inverse_cholesky(p, s);
+    st = run_factor(ctx, p, s);
   }
+  if (st != CLHA_OK) return st;
   {
     StageTimer t(ctx, CLHA_STAGE_GPTQ, s);
     clha::launch_gptq(p, s);
@@ -607,8 +650,9 @@ CLHA_API clha_status clha_inverse_cholesky(clha_ctx* ctx, int32_t n, const float
   p.status = ctx->status_dev;
   {
     StageTimer t(ctx, CLHA_STAGE_FACTOR, s);
-    clha::launch_inverse_cholesky(p, s);
+    st = run_factor(ctx, p, s);
   }
+  if (st != CLHA_OK) return st;
   return hip_check(ctx, "inverse_cholesky");
 }
 

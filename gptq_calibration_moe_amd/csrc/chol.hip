@@ -28,9 +28,12 @@
 //     chol_diag     L_kk = chol(T_k) and its inverse Dinv_k (one wavefront per matrix,
 //                   rows in registers)
 //     chol_panel    L[i][k] = T_i Dinv_k^T for i > k
-//   per block row i:
-//     trtri_row     X[i][j] = -Linv_ii sum_m L[i][m] X[m][j] (X = L^-1, fp64),
-//                   and U at the reversed position in fp32
+//   triangular inverse X = L^-1 (fp64), merged bottom-up over block ranges:
+//     trtri_leaf    X[i][i] = Dinv_i
+//     trtri_merge   X21 = -X22 L21 X11 per merge (two batched GEMMs per level),
+//                   U = J X J and U^T written in fp32 as X becomes final
+// The Hessians of one call are split into groups, one stream each, started one
+// block step apart (see launch_factor_group).
 #include "kernels.h"
 
 namespace clha {
@@ -305,98 +308,248 @@ __global__ __launch_bounds__(256) void chol_panel_kernel(double* __restrict__ Aa
 }
 
 // ---------------------------------------------------------------- triangular inverse
-// Block row i of X = L^-1:  X[i][j] = -Dinv_i sum_{m=j}^{i-1} L[i][m] X[m][j]  (j < i),
-// X[i][i] = Dinv_i.  X is kept in fp64; U (and U^T) receive the fp32 values at
-// the reversed position.
-__global__ __launch_bounds__(256) void trtri_row_kernel(const double* __restrict__ Aall, int c, int i,
-                                                        const double* __restrict__ dinv,
-                                                        double* __restrict__ Xall,
-                                                        float* __restrict__ Uall,
-                                                        float* __restrict__ UTall) {
-  __shared__ double Ls[kNb][kNb + 1];
-  __shared__ double Xs[kNb][kNb + 1];
-  const int m = blockIdx.y, j = blockIdx.x;
-  const double* A = Aall + (int64_t)m * c * c;
+// X = L^-1, merged bottom-up over ranges of 64-column blocks.  For a range
+// [a, b) split at mid, with X11 the inverse over [a, mid) and X22 over [mid, b):
+//   X21 = -X22 L21 X11,   L21 = L[mid:b, a:mid]
+// (the inverse of a 2x2 block lower-triangular matrix).  Level s merges ranges
+// of 2s blocks (s = 1, 2, 4, ...); merges of one level are independent.  The
+// leaves are the diagonal blocks' inverses Dinv from the factorisation.  Each
+// merge is two batched fp64 GEMMs on the matrix cores:
+//   phase 0:  T = L21 X11     (X11 lower triangular: only k >= column counts)
+//   phase 1:  X21 = -X22 T    (X22 lower triangular: only k <= row counts)
+// T is kept transposed in the strictly upper triangle of A, which the
+// factorisation leaves unused: T[row][col] at A[col][row].  Every X element is
+// final when written, so U = J X J (and U^T) get their fp32 values at once.
+
+// Leaves: X[i][i] = Dinv_i (zeros above the diagonal), and U, U^T there.
+__global__ __launch_bounds__(256) void trtri_leaf_kernel(int c, const double* __restrict__ dinv,
+                                                         double* __restrict__ Xall,
+                                                         float* __restrict__ Uall,
+                                                         float* __restrict__ UTall) {
+  const int m = blockIdx.y, i = blockIdx.x;
   double* X = Xall + (int64_t)m * c * c;
   float* U = Uall + (int64_t)m * c * c;
   float* UT = UTall ? UTall + (int64_t)m * c * c : nullptr;
   const double* Di = dinv + ((int64_t)m * (c / kNb) + i) * kNb * kNb;
-  const int64_t i0 = (int64_t)i * kNb, j0 = (int64_t)j * kNb;
-  if (j == i) {
-    for (int idx = threadIdx.x; idx < kNb * kNb; idx += 256) {
-      const int r = idx >> 6, cc = idx & 63;
-      const double v = cc <= r ? Di[idx] : 0.0;
-      X[(i0 + r) * c + j0 + cc] = v;
-      if (cc <= r) U[(c - 1 - (i0 + r)) * c + (c - 1 - (j0 + cc))] = (float)v;
-      // U^T: element (c-1-(j0+cc), c-1-(i0+r)); consecutive threads step r
-      const int rr = idx & 63, c2 = idx >> 6;
-      if (UT && c2 <= rr) UT[(c - 1 - (j0 + c2)) * c + (c - 1 - (i0 + rr))] = (float)Di[rr * kNb + c2];
-    }
-    return;
-  }
-  Tile64 t;
-  t.zero();
-  {
-    ChunkPipe pipe;
-    pipe.fetch(A + i0 * c + j0, c, X + j0 * c + j0, c);
-    for (int mm = j; mm < i; ++mm) {
-      __syncthreads();
-      pipe.stage(Ls, Xs);
-      __syncthreads();
-      if (mm + 1 < i) pipe.fetch(A + i0 * c + (mm + 1) * kNb, c, X + (int64_t)(mm + 1) * kNb * c + j0, c);
-      t.mac<false>(Ls, Xs, 1.0);
-    }
-  }
-  // Xs <- T (the sum), Ls <- Linv_ii; then X[i][j] = -Linv_ii T
-  __syncthreads();
-#pragma unroll
-  for (int x = 0; x < 2; ++x)
-#pragma unroll
-    for (int y = 0; y < 2; ++y)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) Xs[Tile64::row(x, r)][Tile64::col(y)] = t.acc[x][y][r];
-  for (int idx = threadIdx.x; idx < kNb * kNb; idx += 256) Ls[idx >> 6][idx & 63] = Di[idx];
-  __syncthreads();
-  t.zero();
-  t.mac<false>(Ls, Xs, -1.0);
-  __syncthreads();
-#pragma unroll
-  for (int x = 0; x < 2; ++x)
-#pragma unroll
-    for (int y = 0; y < 2; ++y)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = Tile64::row(x, r), col = Tile64::col(y);
-        const double v = t.acc[x][y][r];
-        X[(i0 + row) * c + j0 + col] = v;
-        U[(c - 1 - (i0 + row)) * c + (c - 1 - (j0 + col))] = (float)v;
-        Xs[row][col] = v;
-      }
-  if (UT) {
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < kNb * kNb; idx += 256) {
-      const int rr = idx & 63, cc = idx >> 6;   // consecutive threads step the U^T column
-      UT[(c - 1 - (j0 + cc)) * c + (c - 1 - (i0 + rr))] = (float)Xs[rr][cc];
-    }
+  const int64_t i0 = (int64_t)i * kNb;
+  for (int idx = threadIdx.x; idx < kNb * kNb; idx += 256) {
+    const int r = idx >> 6, cc = idx & 63;
+    const double v = cc <= r ? Di[idx] : 0.0;
+    X[(i0 + r) * c + i0 + cc] = v;
+    if (cc <= r) U[(c - 1 - (i0 + r)) * c + (c - 1 - (i0 + cc))] = (float)v;
+    // U^T: element (c-1-(i0+cc), c-1-(i0+r)); consecutive threads step r
+    const int rr = idx & 63, c2 = idx >> 6;
+    if (UT && c2 <= rr) UT[(c - 1 - (i0 + c2)) * c + (c - 1 - (i0 + rr))] = (float)Di[rr * kNb + c2];
   }
 }
 
-void launch_inverse_cholesky(const GptqPlan& p, hipStream_t s) {
-  const int c = p.cols, nbk = c / kNb;
-  hipLaunchKernelGGL(diag_stats_kernel, dim3(p.n_mats), dim3(256), 0, s, p.mats, c, p.damp,
-                     p.dead, p.lamd, p.lam);
-  hipLaunchKernelGGL(build_reversed_kernel, dim3(nbk * (nbk + 1) / 2, p.n_mats), dim3(256), 0, s,
-                     p.mats, c, p.dead, p.lamd, p.A);
-  for (int k = 0; k < nbk; ++k) {
-    hipLaunchKernelGGL(chol_left_kernel, dim3(nbk - k, p.n_mats), dim3(256), 0, s, p.A, c, k);
-    hipLaunchKernelGGL(chol_diag_kernel, dim3(p.n_mats), dim3(64), 0, s, p.A, c, k, p.dinv, p.status);
-    if (k + 1 < nbk)
-      hipLaunchKernelGGL(chol_panel_kernel, dim3(nbk - k - 1, p.n_mats), dim3(256), 0, s, p.A, c, k,
-                         p.dinv);
+constexpr int kTT = 128;          // merge tile: rows and columns
+constexpr int kTK = 16;           // K chunk
+constexpr int kTPa = kTK + 2;     // pitch of [row][k] LDS tiles (doubles): conflict-free lane reads
+constexpr int kTPb = kTT + 16;    // pitch of the [k][col] LDS tile (doubles)
+constexpr int kTBuf = kTT * kTPa; // one operand buffer (== kTK * kTPb)
+static_assert(kTT * kTPa == kTK * kTPb, "operand buffers share one size");
+
+// One 128x128 tile of one merge.  256 threads = 4 waves of 64x64 (4x4 blocks
+// of v_mfma_f64_16x16x4f64; lane layout as in Tile64).  Operands are staged
+// through LDS in chunks of 16 along K, double-buffered with two register
+// stages.  Tiles of one merge are mapped to one XCD (workgroup b runs on XCD
+// b % 8) so its operands are shared through one L2.
+template <int PHASE>
+__global__ __launch_bounds__(256, 2) void trtri_merge_kernel(double* __restrict__ Aall,
+                                                             double* __restrict__ Xall,
+                                                             float* __restrict__ Uall,
+                                                             float* __restrict__ UTall, int c, int s,
+                                                             int n_merge, int tc, int n_mats) {
+  __shared__ __attribute__((aligned(16))) double lds[4 * kTBuf];   // A0 B0 A1 B1
+  const int nbk = c / kNb, tmax = tc * tc;
+  const int total = n_mats * n_merge * tmax;
+  const int per = (total + kXcds - 1) / kXcds;
+  const int L = (int)(blockIdx.x % kXcds) * per + (int)(blockIdx.x / kXcds);
+  if (L >= total) return;
+  const int t = L % tmax, rest = L / tmax;
+  const int pm = rest % n_merge, m = rest / n_merge;
+  const int ti = t / tc, tj = t - (t / tc) * tc;
+  const int a = 2 * s * pm, mid = a + s, b = min(a + 2 * s, nbk);
+  const int r0 = mid * kNb + ti * kTT, c0 = a * kNb + tj * kTT;
+  const int nr = min(kTT, b * kNb - r0), nc = min(kTT, mid * kNb - c0);
+  if (nr <= 0 || nc <= 0) return;
+  // K range of the tile (64-aligned; masked elements contribute zero)
+  const int k0 = PHASE == 0 ? c0 : mid * kNb;
+  const int k1 = PHASE == 0 ? mid * kNb : min(r0 + kTT, b * kNb);
+  const int nch = (k1 - k0) / kTK;
+  double* A = Aall + (int64_t)m * c * c;
+  double* X = Xall + (int64_t)m * c * c;
+  // A operand rows (K-contiguous): phase 0 L[r0 + i][k], phase 1 X[r0 + i][k]
+  const double* Ar = (PHASE == 0 ? A : X) + (int64_t)r0 * c;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const bool active = wm * 64 < nr && wn * 64 < nc;
+  const int li = lane & 15, lk = lane >> 4, ai = 4 * (li & 3) + (li >> 2);
+
+  struct Stage {
+    double2 a[4], b[4];
+  };
+  // Phase 0 walks K downwards from the merge's common end, phase 1 upwards from
+  // its common start: the tiles of one merge then read the same K chunks at
+  // about the same time, so one L2 serves them all.
+  auto fetch = [&](Stage& rg, int ch) {
+    const int kb = PHASE == 0 ? k1 - (ch + 1) * kTK : k0 + ch * kTK;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int q = tid + 256 * u;
+      {  // A operand: row q/8, k pair 2(q%8)
+        const int row = q >> 3, kc = 2 * (q & 7), kk = kb + kc;
+        double2 v = make_double2(0.0, 0.0);
+        if (row < nr) {
+          v = *reinterpret_cast<const double2*>(Ar + (int64_t)row * c + kk);
+          if (PHASE == 1) {   // X22 lower triangular
+            if (kk > r0 + row) v.x = 0.0;
+            if (kk + 1 > r0 + row) v.y = 0.0;
+          }
+        }
+        rg.a[u] = v;
+      }
+      if (PHASE == 0) {  // B = X11[k][c0 + j]: k row q/64, column pair 2(q%64)
+        const int krow = q >> 6, jc = 2 * (q & 63), kk = kb + krow;
+        double2 v = make_double2(0.0, 0.0);
+        if (jc < nc) {
+          v = *reinterpret_cast<const double2*>(X + (int64_t)kk * c + c0 + jc);
+          if (kk < c0 + jc) v.x = 0.0;
+          if (kk < c0 + jc + 1) v.y = 0.0;
+        }
+        rg.b[u] = v;
+      } else {           // B^T = T^T[c0 + j][k] stored at A[c0 + j][k]: row q/8, k pair 2(q%8)
+        const int row = q >> 3, kc = 2 * (q & 7);
+        rg.b[u] = row < nc ? *reinterpret_cast<const double2*>(A + (int64_t)(c0 + row) * c + kb + kc)
+                           : make_double2(0.0, 0.0);
+      }
+    }
+  };
+  auto stage = [&](const Stage& rg, int buf) {
+    double* As = lds + (2 * buf) * kTBuf;
+    double* Bs = lds + (2 * buf + 1) * kTBuf;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int q = tid + 256 * u;
+      *reinterpret_cast<double2*>(As + (q >> 3) * kTPa + 2 * (q & 7)) = rg.a[u];
+      if (PHASE == 0)
+        *reinterpret_cast<double2*>(Bs + (q >> 6) * kTPb + 2 * (q & 63)) = rg.b[u];
+      else
+        *reinterpret_cast<double2*>(Bs + (q >> 3) * kTPa + 2 * (q & 7)) = rg.b[u];
+    }
+  };
+  f64x4 acc[4][4];
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+#pragma unroll
+    for (int y = 0; y < 4; ++y) acc[x][y] = f64x4{0.0, 0.0, 0.0, 0.0};
+  auto multiply = [&](int buf) {
+    if (!active) return;
+    const double* As = lds + (2 * buf) * kTBuf + (wm * 64 + ai) * kTPa + lk;
+    const double* Bs = lds + (2 * buf + 1) * kTBuf;
+#pragma unroll
+    for (int kk = 0; kk < kTK; kk += 4) {
+      double av[4], bv[4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) av[x] = As[x * 16 * kTPa + kk];
+#pragma unroll
+      for (int y = 0; y < 4; ++y)
+        bv[y] = PHASE == 0 ? Bs[(kk + lk) * kTPb + wn * 64 + y * 16 + li]
+                           : Bs[(wn * 64 + y * 16 + li) * kTPa + kk + lk];
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int y = 0; y < 4; ++y)
+          acc[x][y] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[x], bv[y], acc[x][y], 0, 0, 0);
+    }
+  };
+
+  // nch is a multiple of 4
+  Stage g0, g1;
+  fetch(g0, 0);
+  stage(g0, 0);
+  fetch(g1, 1);
+  if (nch > 2) fetch(g0, 2);
+  __syncthreads();
+#pragma unroll 1
+  for (int st = 0; st < nch; st += 2) {
+    multiply(0);
+    stage(g1, 1);
+    if (st + 3 < nch) fetch(g1, st + 3);
+    __syncthreads();
+    multiply(1);
+    if (st + 2 < nch) stage(g0, 0);
+    if (st + 4 < nch) fetch(g0, st + 4);
+    __syncthreads();
   }
-  for (int i = 0; i < nbk; ++i)
-    hipLaunchKernelGGL(trtri_row_kernel, dim3(i + 1, p.n_mats), dim3(256), 0, s, p.A, c, i, p.dinv,
-                       p.X, p.U, p.UT);
+  if (!active) return;
+  // element (row, col) of the tile: row = wm*64 + 16x + 4(lane/16) + r, col = wn*64 + 16y + lane%16
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+#pragma unroll
+    for (int y = 0; y < 4; ++y) {
+      const int row = r0 + wm * 64 + 16 * x + 4 * lk, col = c0 + wn * 64 + 16 * y + li;
+      const f64x4 v = acc[x][y];
+      if (PHASE == 0) {
+        // T^T[col][row .. row+3], contiguous
+        double* tp = A + (int64_t)col * c + row;
+        *reinterpret_cast<double2*>(tp) = make_double2(v[0], v[1]);
+        *reinterpret_cast<double2*>(tp + 2) = make_double2(v[2], v[3]);
+      } else {
+        float* U = Uall + (int64_t)m * c * c;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          X[(int64_t)(row + r) * c + col] = -v[r];
+          U[(int64_t)(c - 1 - (row + r)) * c + (c - 1 - col)] = (float)(-v[r]);
+        }
+        if (UTall) {
+          // U^T row c-1-col, columns c-1-row-3 .. c-1-row (ascending)
+          float* ut = UTall + (int64_t)m * c * c + (int64_t)(c - 1 - col) * c + (c - 4 - row);
+          *reinterpret_cast<float4*>(ut) =
+              make_float4((float)(-v[3]), (float)(-v[2]), (float)(-v[1]), (float)(-v[0]));
+        }
+      }
+    }
+}
+
+// One group of Hessians [m0, m1) on one stream: the block-step chain of the
+// factorisation, then the merge levels of the inverse.  Groups on separate
+// streams interleave one group's latency-bound diagonal steps with the others'
+// wide products.  step0_done (optional) is recorded after block step 0.
+void launch_factor_group(const GptqPlan& p, int m0, int m1, hipStream_t s, hipEvent_t step0_done) {
+  const int c = p.cols, nbk = c / kNb, n = m1 - m0;
+  if (n <= 0) return;
+  const int64_t cc = (int64_t)c * c;
+  const float* const* mats = p.mats + m0;
+  uint8_t* dead = p.dead + (int64_t)m0 * c;
+  double* lamd = p.lamd + m0;
+  float* lam = p.lam ? p.lam + m0 : nullptr;
+  double* A = p.A + m0 * cc;
+  double* X = p.X + m0 * cc;
+  double* dinv = p.dinv + (int64_t)m0 * c * kNb;
+  float* U = p.U + m0 * cc;
+  float* UT = p.UT ? p.UT + m0 * cc : nullptr;
+  hipLaunchKernelGGL(diag_stats_kernel, dim3(n), dim3(256), 0, s, mats, c, p.damp, dead, lamd, lam);
+  hipLaunchKernelGGL(build_reversed_kernel, dim3(nbk * (nbk + 1) / 2, n), dim3(256), 0, s, mats, c, dead,
+                     lamd, A);
+  for (int k = 0; k < nbk; ++k) {
+    hipLaunchKernelGGL(chol_left_kernel, dim3(nbk - k, n), dim3(256), 0, s, A, c, k);
+    hipLaunchKernelGGL(chol_diag_kernel, dim3(n), dim3(64), 0, s, A, c, k, dinv, p.status);
+    if (k == 0 && step0_done) hipEventRecord(step0_done, s);
+    if (k + 1 < nbk)
+      hipLaunchKernelGGL(chol_panel_kernel, dim3(nbk - k - 1, n), dim3(256), 0, s, A, c, k, dinv);
+  }
+  hipLaunchKernelGGL(trtri_leaf_kernel, dim3(nbk, n), dim3(256), 0, s, c, dinv, X, U, UT);
+  for (int sz = 1; sz < nbk; sz *= 2) {
+    const int n_merge = (nbk - sz + 2 * sz - 1) / (2 * sz);
+    const int tc = (sz * kNb + kTT - 1) / kTT;
+    const int total = n * n_merge * tc * tc;
+    const dim3 grid(((total + kXcds - 1) / kXcds) * kXcds);
+    hipLaunchKernelGGL(trtri_merge_kernel<0>, grid, dim3(256), 0, s, A, X, U, UT, c, sz, n_merge, tc, n);
+    hipLaunchKernelGGL(trtri_merge_kernel<1>, grid, dim3(256), 0, s, A, X, U, UT, c, sz, n_merge, tc, n);
+  }
 }
 
 }  // namespace clha

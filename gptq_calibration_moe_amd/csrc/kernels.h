@@ -102,7 +102,8 @@ struct GptqPlan {
   float* partials;           // device [total_slabs][2]
   int* status;
 };
-void launch_inverse_cholesky(const GptqPlan& p, hipStream_t s);
+constexpr int kFactorStreams = 4;     // Hessian groups factored on separate streams
+void launch_factor_group(const GptqPlan& p, int m0, int m1, hipStream_t s, hipEvent_t step0_done);
 void launch_gptq(const GptqPlan& p, hipStream_t s);
 
 // ---------------------------------------------------------------- loss
