@@ -22,7 +22,7 @@ using clha::GptqPlan;
 
 namespace clha {
 bool gptq_group_supported(int group);
-int syrk_tiles_per_slot(int d);
+int syrk_items_per_slot(int d);
 }
 
 struct LayerBufs {
@@ -171,6 +171,9 @@ struct CollectLayout {
   int32_t* work;
   int32_t* work_len;
   int32_t* work_next;
+  int32_t* seg;
+  int32_t* split;
+  float* partials;
   int32_t* token_ids;
   uint16_t* xgT;
   size_t bytes;
@@ -190,9 +193,12 @@ CollectLayout collect_layout(const clha_ctx* ctx, void* ws) {
   L.offsets = c.take<int64_t>((size_t)d.n_routed + 1);
   L.pad_off = c.take<int64_t>((size_t)ctx->slots + 1);
   L.slot_order = c.take<int32_t>((size_t)ctx->slots);
-  L.work = c.take<int32_t>((size_t)clha::kXcds * ctx->slots * clha::syrk_tiles_per_slot(d.d));
+  L.work = c.take<int32_t>((size_t)clha::kXcds * clha::kMaxSegs * clha::syrk_items_per_slot(d.d));
   L.work_len = c.take<int32_t>(clha::kXcds);
   L.work_next = c.take<int32_t>(clha::kXcds);
+  L.seg = c.take<int32_t>((size_t)4 * clha::kMaxSegs);
+  L.split = c.take<int32_t>((size_t)1 + 3 * clha::kMaxPartials);
+  L.partials = c.take<float>((size_t)clha::kMaxPartials * d.d * d.d);
   L.token_ids = c.take<int32_t>((size_t)n * d.top_k);
   L.xgT = c.take<uint16_t>((size_t)xg_tokens * d.d);
   L.bytes = c.off;
@@ -391,7 +397,10 @@ CLHA_API clha_status clha_collect_hessians(clha_ctx* ctx, int32_t layer, int64_t
   p.work = L.work;
   p.work_len = L.work_len;
   p.work_next = L.work_next;
-  p.syrk_tiles = clha::syrk_tiles_per_slot(d.d);
+  p.seg = L.seg;
+  p.split = L.split;
+  p.partials = L.partials;
+  p.syrk_items = clha::syrk_items_per_slot(d.d);
   p.token_ids = token_ids_out ? token_ids_out : L.token_ids;
   p.xgT = L.xgT;
   p.xg_tiles = (n_tokens * d.top_k + clha::kTokPad - 1) / clha::kTokPad + d.n_routed +

@@ -16,6 +16,8 @@ constexpr int kMaxExperts = 256;
 constexpr int kMaxTopK = 16;
 constexpr int kMaxLayers = 8;
 constexpr int kSyrkTile = 256;        // Gram-sum output tile
+constexpr int kMaxPartials = 8;       // partial Gram-sum buffers of token-split slots
+constexpr int kMaxSegs = kMaxExperts + 1 + kMaxPartials;   // Gram-sum segments per call
 constexpr int kXcds = 8;              // accelerator complex dies; workgroup b runs on die b % 8
 constexpr int kSyrkWgPerXcd = 32;     // persistent Gram-sum workgroups per die (one per CU)
 constexpr int kNb = 64;               // Cholesky / triangular-inverse block
@@ -39,10 +41,14 @@ struct CollectPlan {
   int64_t* offsets;      // [E+1]
   int64_t* pad_off;      // [slots+1] padded starts of each slot's token list
   int32_t* slot_order;   // [slots] slots sorted by padded length, longest first
-  int32_t* work;         // [kXcds][slots*tiles] Gram-sum work items (slot*1024 + tile) per XCD
+  int32_t* work;         // [kXcds][kMaxSegs*items] Gram-sum items (segment*1024 + item) per XCD
   int32_t* work_len;     // [kXcds] items per XCD
   int32_t* work_next;    // [kXcds] queue heads (reset by the bucketing scan)
-  int syrk_tiles;        // lower-triangular 256x256 tiles per slot
+  int32_t* seg;          // [kMaxSegs][4] slot, destination (-1: S, else partial buffer),
+                         //   first token and token count within the slot's padded list
+  int32_t* split;        // [1 + 3*kMaxPartials] count, then (slot, first partial, partials)
+  float* partials;       // [kMaxPartials][d][d] partial sums of token-split slots
+  int syrk_items;        // Gram-sum items per segment
   int32_t* token_ids;    // [n*K]
   uint16_t* xgT;         // feature-major gathered activations
   int64_t xg_tiles;      // upper bound of 64-token tiles over all slots
@@ -53,6 +59,7 @@ void launch_route(const float* logits, const CollectPlan& p, hipStream_t s);
 void launch_bucket(const CollectPlan& p, int64_t* layer_counts, hipStream_t s);
 void launch_gather(const uint16_t* x, const CollectPlan& p, hipStream_t s);
 void launch_syrk(const CollectPlan& p, float* S, hipStream_t s);
+int syrk_items_per_slot(int d);
 
 // ---------------------------------------------------------------- aggregation
 struct AggArgs {

@@ -115,13 +115,15 @@ __global__ __launch_bounds__(256) void bucket_count_kernel(const int32_t* __rest
 __global__ __launch_bounds__(256) void bucket_scan_kernel(
     const int32_t* __restrict__ blockcounts, int nblk, int64_t n, int E, int has_shared,
     int32_t* __restrict__ blockbase, int64_t* __restrict__ offsets, int64_t* __restrict__ pad_off,
-    int32_t* __restrict__ slot_order, int64_t* __restrict__ layer_counts, int tiles,
-    int32_t* __restrict__ work, int32_t* __restrict__ work_len, int32_t* __restrict__ work_next) {
+    int32_t* __restrict__ slot_order, int64_t* __restrict__ layer_counts, int items,
+    int32_t* __restrict__ work, int32_t* __restrict__ work_len, int32_t* __restrict__ work_next,
+    int32_t* __restrict__ seg, int32_t* __restrict__ split) {
   __shared__ int64_t cnt[kMaxExperts + 1];
   __shared__ int64_t padc[kMaxExperts + 1];
   __shared__ int32_t order[kMaxExperts + 1];
-  __shared__ int32_t home[kMaxExperts + 1];           // XCD of a whole slot, -1 = split over all
-  __shared__ int32_t base[kMaxExperts + 1][kXcds];    // first list position of the slot's items
+  __shared__ int32_t seg_x[kMaxSegs];      // XCD of each segment
+  __shared__ int32_t seg_pos[kMaxSegs];    // first list position of its items
+  __shared__ int32_t nseg_s;
   const int slots = E + has_shared;
   for (int e = threadIdx.x; e < E; e += 256) {
     int64_t run = 0;
@@ -160,56 +162,68 @@ __global__ __launch_bounds__(256) void bucket_scan_kernel(
     order[r] = e;
   }
   __syncthreads();
-  // Gram-sum work lists, one per XCD (each XCD has its own L2): a slot's tiles
-  // share its activations, so a slot stays on one XCD, longest slots first onto
-  // the least-loaded XCD; a slot longer than an eighth of the work is split
-  // over all XCDs (tile t on XCD t % 8).
+  // Gram-sum work lists, one per XCD (each XCD has its own L2).  A segment is
+  // a token range of one slot; every item of a segment reads the same
+  // activations, so a segment stays on one XCD and its items are consecutive
+  // in the list, the diagonal-pair items first.  Slots far longer than the
+  // average XCD share are split into up to 8 token ranges (the parts after the
+  // first go to partial buffers, added back in part order afterwards).
+  // Longest slots first, each segment onto the least-loaded XCD.
   if (threadIdx.x == 0) {
     int64_t total = 0;
-    for (int r = 0; r < slots; ++r) total += padc[r];
+    for (int e = 0; e < slots; ++e) total += padc[e];
+    const int64_t target = ((total / (8 * kXcds)) / kTokPad + 1) * kTokPad;
     int64_t load[kXcds];
     int32_t len[kXcds];
     for (int x = 0; x < kXcds; ++x) {
       load[x] = 0;
       len[x] = 0;
     }
+    int nseg = 0, nsplit = 0, used = 0;
     for (int r = 0; r < slots; ++r) {
       const int e = order[r];
-      if (tiles >= kXcds && padc[e] * kXcds > total) {
-        home[e] = -1;
-        for (int x = 0; x < kXcds; ++x) {
-          const int cntx = tiles / kXcds + (x < tiles % kXcds ? 1 : 0);
-          base[e][x] = len[x];
-          len[x] += cntx;
-          load[x] += padc[e] * cntx;
-        }
-      } else {
+      const int64_t chunks = padc[e] / kTokPad;
+      if (chunks == 0) continue;
+      int64_t k = (padc[e] + target - 1) / target;
+      k = k < kXcds ? k : kXcds;
+      k = k < 1 + kMaxPartials - used ? k : 1 + kMaxPartials - used;
+      k = k < chunks ? k : chunks;
+      if (k > 1) {
+        split[1 + 3 * nsplit] = e;
+        split[2 + 3 * nsplit] = used;
+        split[3 + 3 * nsplit] = (int32_t)(k - 1);
+        ++nsplit;
+      }
+      int64_t b = 0;
+      for (int j = 0; j < (int)k; ++j) {
+        const int64_t nc = chunks / k + (j < chunks % k ? 1 : 0);
+        seg[4 * nseg] = e;
+        seg[4 * nseg + 1] = j == 0 ? -1 : used + j - 1;
+        seg[4 * nseg + 2] = (int32_t)(b * kTokPad);
+        seg[4 * nseg + 3] = (int32_t)(nc * kTokPad);
         int best = 0;
         for (int x = 1; x < kXcds; ++x) best = load[x] < load[best] ? x : best;
-        home[e] = best;
-        base[e][best] = len[best];
-        len[best] += tiles;
-        load[best] += padc[e] * tiles;
+        seg_x[nseg] = best;
+        seg_pos[nseg] = len[best];
+        len[best] += items;
+        load[best] += nc;
+        b += nc;
+        ++nseg;
       }
+      used += (int)k - 1;
     }
+    split[0] = nsplit;
+    nseg_s = nseg;
     for (int x = 0; x < kXcds; ++x) {
       work_len[x] = len[x];
       work_next[x] = 0;
     }
   }
   __syncthreads();
-  const int cap = slots * tiles;
-  for (int it = threadIdx.x; it < slots * tiles; it += 256) {
-    const int e = it / tiles, t = it - e * tiles;
-    int x, pos;
-    if (home[e] >= 0) {
-      x = home[e];
-      pos = base[e][x] + t;
-    } else {
-      x = t % kXcds;
-      pos = base[e][x] + t / kXcds;
-    }
-    work[x * cap + pos] = e * 1024 + t;
+  const int cap = kMaxSegs * items;
+  for (int it = threadIdx.x; it < nseg_s * items; it += 256) {
+    const int sg = it / items, t = it - sg * items;
+    work[seg_x[sg] * cap + seg_pos[sg] + t] = sg * 1024 + t;
   }
 }
 
@@ -248,7 +262,8 @@ void launch_bucket(const CollectPlan& p, int64_t* layer_counts, hipStream_t s) {
                      p.E, p.blockcounts);
   hipLaunchKernelGGL(bucket_scan_kernel, dim3(1), dim3(256), 0, s, p.blockcounts, p.nblk,
                      p.n_tokens, p.E, p.has_shared, p.blockbase, p.offsets, p.pad_off,
-                     p.slot_order, layer_counts, p.syrk_tiles, p.work, p.work_len, p.work_next);
+                     p.slot_order, layer_counts, p.syrk_items, p.work, p.work_len, p.work_next,
+                     p.seg, p.split);
   hipLaunchKernelGGL(bucket_scatter_kernel, dim3(p.nblk), dim3(256), 0, s, p.topk, p.n_tokens,
                      p.K, p.E, p.blockbase, p.offsets, p.token_ids);
 }
