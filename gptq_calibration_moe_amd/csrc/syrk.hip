@@ -24,13 +24,14 @@
 // slot it goes to a partial buffer, added into S in part order afterwards.
 //
 // Tile pipeline: 512 threads = 8 waves.  Tokens advance 32 at a time through
-// two LDS buffers and two register stages: while the matrix cores consume one
-// buffer, the other buffer is filled from the register stage loaded a step
-// earlier, and the register stage is refilled with the step after that -- each
-// global load has a full step to arrive.  Operand tiles are feature-major
-// [256 features][32 tokens]; a lane's MFMA fragment (8 consecutive tokens of
-// one feature) is one 16-byte LDS read, and the row pitch of 40 bf16 (80 bytes)
-// keeps those reads bank-conflict free.
+// four LDS stages filled by direct global-to-LDS loads (global_load_lds_dwordx4)
+// issued three steps ahead, so no registers stage the operands and each load
+// has three steps of products to arrive.  Each wave waits for its own loads of
+// the step (vmcnt) and one barrier per step publishes them.  Operand tiles are
+// feature-major [256 features][32 tokens] with 64-byte rows; a lane's MFMA
+// fragment (8 consecutive tokens of one feature) is one 16-byte chunk, and the
+// four chunks of row r sit at slots c ^ ((r >> 2) & 3), which makes the
+// fragment reads bank-conflict free.
 //   off-diagonal tile (ti, tj): waves in 2x4, each 128x64 as 4x2 32x32 blocks;
 //   diagonal pair (p, q): waves 0-3 take panel p, waves 4-7 panel q; wave k of a
 //     panel owns block rows 7-k and k (9 blocks), both operands from that panel.
@@ -43,64 +44,89 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kT = 256;              // output tile
 constexpr int kSK = 32;              // tokens per step
-constexpr int kPitch = kSK + 8;      // LDS row pitch (bf16 elements, 80 bytes)
-constexpr int kFlushSteps = 256;     // 8192 tokens between partial-sum flushes (even)
-constexpr int kBuf = kT * kPitch;    // one operand buffer (bf16 elements)
+constexpr int kFlushSteps = 256;     // 8192 tokens between partial-sum flushes (multiple of kStages)
+constexpr int kStages = 4;           // LDS stages; loads run kStages - 1 steps ahead
+constexpr int kPanel = kT * kSK;     // one operand stage: 256 rows x 32 tokens (bf16 elements)
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+typedef const __attribute__((address_space(1))) void* glb_ptr;
+
+// The LDS stages, one array each so that the compiler can tell a stage being
+// loaded from a stage being read.
+struct Stages {
+  uint16_t* a[kStages];
+  uint16_t* b[kStages];
+};
+
+// s_waitcnt with vmcnt <= N and lgkmcnt == 0: this wave's global loads up to
+// the N most recent have landed, and its LDS reads have all returned (so a
+// barrier after it also means the wave is done reading the stages it read).
+template <int N>
+__device__ __forceinline__ void wait_loads() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | (((N >> 4) & 3) << 14));
+}
+
+// Byte offset in a stage of 16-byte chunk c (0..3) of row r.
+__device__ __forceinline__ int chunk_off(int r, int c) { return r * 64 + ((c ^ ((r >> 2) & 3)) << 4); }
 
 // The token pipeline shared by both item kinds.  Ag / Bg: feature-major rows of
-// the two panels (row stride npad); Bg unused when !loadB.  multiply(buf) runs
-// one 32-token step from LDS buffer buf; flush(first) adds the running sums.
+// the two panels (row stride npad); when !loadB only Ag is used.
+// multiply(stage) runs one 32-token step from LDS stage `stage`; flush(first)
+// adds the running sums.  Steps past nsteps are padding: their loads re-read
+// the last step (clamped, always in range) and they run no products, so every
+// wave issues the same loads, waits and barriers.
 template <class Mul, class Flush>
 __device__ __forceinline__ void token_loop(const uint16_t* __restrict__ Ag, const uint16_t* __restrict__ Bg,
                                            int64_t npad, int64_t t0, int64_t nsteps, int arows, int brows,
-                                           bool loadB, uint16_t* lds, Mul&& multiply, Flush&& flush) {
-  const int tid = threadIdx.x;
-  // thread t moves 16-byte chunks q = t + 512u: row q/4, token chunk q%4
-  struct Stage {
-    uint4 a[2], b[2];
-  };
-  auto fetch = [&](Stage& r, int64_t k0) {
+                                           bool loadB, const Stages& sb, Mul&& multiply, Flush&& flush) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (!loadB) {
+    Bg = Ag;
+    brows = arows;
+  }
+  // wave w loads 1 KB blocks 2w and 2w+1 of each panel: 16 rows x 4 chunks,
+  // lane l -> row 16 blk + l/4, LDS slot l%4 (holding chunk slot ^ ((row>>2)&3))
+  const uint16_t* pa[2];
+  const uint16_t* pb[2];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int q = tid + 512 * u, row = q >> 2, ch = q & 3;
-      r.a[u] = row < arows ? *reinterpret_cast<const uint4*>(Ag + (int64_t)row * npad + t0 + k0 + ch * 8)
-                           : make_uint4(0, 0, 0, 0);
-      if (loadB)
-        r.b[u] = row < brows ? *reinterpret_cast<const uint4*>(Bg + (int64_t)row * npad + t0 + k0 + ch * 8)
-                             : make_uint4(0, 0, 0, 0);
+  for (int j = 0; j < 2; ++j) {
+    const int row = 16 * (2 * wave + j) + (lane >> 2);
+    const int c = (lane & 3) ^ ((row >> 2) & 3);
+    pa[j] = Ag + (int64_t)min(row, arows - 1) * npad + t0 + c * 8;
+    pb[j] = Bg + (int64_t)min(row, brows - 1) * npad + t0 + c * 8;
+  }
+  auto issue = [&](int stage, int64_t st) {
+    const int64_t k0 = (st < nsteps ? st : nsteps - 1) * kSK;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      __builtin_amdgcn_global_load_lds((glb_ptr)(pa[j] + k0), (lds_ptr)(sb.a[stage] + (2 * wave + j) * 512), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((glb_ptr)(pb[j] + k0), (lds_ptr)(sb.b[stage] + (2 * wave + j) * 512), 16, 0, 0);
     }
   };
-  auto stage = [&](const Stage& r, int buf) {
-    uint16_t* As = lds + (2 * buf) * kBuf;
-    uint16_t* Bs = lds + (2 * buf + 1) * kBuf;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int q = tid + 512 * u, row = q >> 2, ch = q & 3;
-      *reinterpret_cast<uint4*>(&As[row * kPitch + ch * 8]) = r.a[u];
-      if (loadB) *reinterpret_cast<uint4*>(&Bs[row * kPitch + ch * 8]) = r.b[u];
-    }
+  // one step: this wave's loads for stage `stage` are done once at most the
+  // loads of the (kStages - 2) later steps are outstanding
+  auto step = [&](auto stage_c, int64_t st) {
+    constexpr int stage = decltype(stage_c)::value;
+    wait_loads<4 * (kStages - 2)>();
+    __builtin_amdgcn_s_barrier();
+    issue((stage + kStages - 1) % kStages, st + kStages - 1);
+    if (st < nsteps) multiply(stage);
   };
-  // nsteps is even (token ranges are multiples of 64); steps 2s and 2s+1 form a pair
-  Stage r0, r1;
-  fetch(r0, 0);
-  stage(r0, 0);
-  fetch(r1, kSK);
-  if (nsteps > 2) fetch(r0, 2 * kSK);
-  __syncthreads();
   for (int64_t c0 = 0; c0 < nsteps; c0 += kFlushSteps) {
+    // restart the pipeline (all earlier loads and stores drained)
+    wait_loads<0>();
+    __builtin_amdgcn_s_barrier();
+#pragma unroll
+    for (int j = 0; j < kStages - 1; ++j) issue(j, c0 + j);
     const int64_t c1 = c0 + kFlushSteps < nsteps ? c0 + kFlushSteps : nsteps;
-    for (int64_t st = c0; st < c1; st += 2) {
-      // step st: LDS buffer 0 holds it, r1 holds st+1, r0 holds st+2 (if any)
-      multiply(0);
-      stage(r1, 1);
-      if (st + 3 < nsteps) fetch(r1, (st + 3) * kSK);
-      __syncthreads();
-      // step st+1 from buffer 1; r0 (step st+2) goes to buffer 0
-      multiply(1);
-      if (st + 2 < nsteps) stage(r0, 0);
-      if (st + 4 < nsteps) fetch(r0, (st + 4) * kSK);
-      __syncthreads();
+    for (int64_t st = c0; st < c1; st += kStages) {
+      step(std::integral_constant<int, 0>{}, st);
+      step(std::integral_constant<int, 1>{}, st + 1);
+      step(std::integral_constant<int, 2>{}, st + 2);
+      step(std::integral_constant<int, 3>{}, st + 3);
     }
+    wait_loads<0>();
+    __builtin_amdgcn_s_barrier();
     flush(c0 == 0);
   }
 }
@@ -128,7 +154,7 @@ __device__ __forceinline__ void flush_block(f32x16& acc, float* __restrict__ Sd,
 
 // Off-diagonal tile (ti, tj), ti > tj: waves 2x4, each 128x64.
 __device__ __forceinline__ void syrk_offdiag(const uint16_t* base, int64_t npad, int64_t t0, int64_t nsteps,
-                                             int d, int ti, int tj, float* Sd, bool partial, uint16_t* lds) {
+                                             int d, int ti, int tj, float* Sd, bool partial, const Stages& sb) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 2, wn = wave & 3;
   f32x16 acc[4][2];
@@ -136,23 +162,19 @@ __device__ __forceinline__ void syrk_offdiag(const uint16_t* base, int64_t npad,
   for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
     for (int bj = 0; bj < 2; ++bj) acc[bi][bj] = f32x16{};
-  auto multiply = [&](int buf) {
-    const uint16_t* As = lds + (2 * buf) * kBuf;
-    const uint16_t* Bs = lds + (2 * buf + 1) * kBuf;
+  auto multiply = [&](int stage) {
+    const char* As = reinterpret_cast<const char*>(sb.a[stage]);
+    const char* Bs = reinterpret_cast<const char*>(sb.b[stage]);
 #pragma unroll
     for (int kk = 0; kk < kSK / 16; ++kk) {
-      const int kcol = kk * 16 + (lane >> 5) * 8;
+      const int c = 2 * kk + (lane >> 5);
       bf16x8 a[4], b[2];
 #pragma unroll
-      for (int bi = 0; bi < 4; ++bi) {
-        const int row = wm * 128 + bi * 32 + (lane & 31);
-        a[bi] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&As[row * kPitch + kcol]));
-      }
+      for (int bi = 0; bi < 4; ++bi)
+        a[bi] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(As + chunk_off(wm * 128 + bi * 32 + (lane & 31), c)));
 #pragma unroll
-      for (int bj = 0; bj < 2; ++bj) {
-        const int row = wn * 64 + bj * 32 + (lane & 31);
-        b[bj] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&Bs[row * kPitch + kcol]));
-      }
+      for (int bj = 0; bj < 2; ++bj)
+        b[bj] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Bs + chunk_off(wn * 64 + bj * 32 + (lane & 31), c)));
 #pragma unroll
       for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
@@ -170,7 +192,7 @@ __device__ __forceinline__ void syrk_offdiag(const uint16_t* base, int64_t npad,
                     store, lane);
   };
   token_loop(base + (int64_t)ti * kT * npad, base + (int64_t)tj * kT * npad, npad, t0, nsteps,
-             min(kT, d - ti * kT), min(kT, d - tj * kT), true, lds, multiply, flush);
+             min(kT, d - ti * kT), min(kT, d - tj * kT), true, sb, multiply, flush);
 }
 
 // Diagonal pair: this wave's share of panel P's diagonal tile -- block rows
@@ -178,22 +200,22 @@ __device__ __forceinline__ void syrk_offdiag(const uint16_t* base, int64_t npad,
 template <int K>
 __device__ __forceinline__ void syrk_diag_wave(const uint16_t* Ag, const uint16_t* Bg, bool loadB, int64_t npad,
                                                int64_t t0, int64_t nsteps, int d, int P, int pb, bool active,
-                                               float* Sd, bool partial, int arows, int brows, uint16_t* lds) {
+                                               float* Sd, bool partial, int arows, int brows, const Stages& sb) {
   constexpr int R1 = 7 - K, R2 = K, NA = 8 - K;   // NA fragments: panel blocks 0..7-K
   const int lane = threadIdx.x & 63;
   f32x16 acc[9];
 #pragma unroll
   for (int x = 0; x < 9; ++x) acc[x] = f32x16{};
-  auto multiply = [&](int buf) {
+  auto multiply = [&](int stage) {
     if (!active) return;
-    const uint16_t* Ps = lds + (2 * buf + pb) * kBuf;
+    const char* Ps = reinterpret_cast<const char*>(pb ? sb.b[stage] : sb.a[stage]);
 #pragma unroll
     for (int kk = 0; kk < kSK / 16; ++kk) {
-      const int kcol = kk * 16 + (lane >> 5) * 8;
+      const int c = 2 * kk + (lane >> 5);
       bf16x8 f[NA];
 #pragma unroll
       for (int cb = 0; cb < NA; ++cb)
-        f[cb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&Ps[(cb * 32 + (lane & 31)) * kPitch + kcol]));
+        f[cb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Ps + chunk_off(cb * 32 + (lane & 31), c)));
 #pragma unroll
       for (int cb = 0; cb <= R1; ++cb)
         acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[R1], f[cb], acc[cb], 0, 0, 0);
@@ -212,7 +234,7 @@ __device__ __forceinline__ void syrk_diag_wave(const uint16_t* Ag, const uint16_
     for (int cb = 0; cb <= R2; ++cb)
       flush_block(acc[NA + cb], Sd, d, P * kT + R2 * 32, P * kT + cb * 32, cb == R2, store, lane);
   };
-  token_loop(Ag, Bg, npad, t0, nsteps, arows, brows, loadB, lds, multiply, flush);
+  token_loop(Ag, Bg, npad, t0, nsteps, arows, brows, loadB, sb, multiply, flush);
 }
 
 __device__ __forceinline__ void tile_of(int t, int& ti, int& tj) {
@@ -226,7 +248,7 @@ __device__ __forceinline__ void tile_of(int t, int& ti, int& tj) {
 // One item of one segment.
 __device__ __forceinline__ void syrk_item(const uint16_t* __restrict__ xgT, const int64_t* __restrict__ pad_off,
                                           const int32_t* __restrict__ seg, int sg, int item, int d,
-                                          float* __restrict__ S, float* __restrict__ partials, uint16_t* lds) {
+                                          float* __restrict__ S, float* __restrict__ partials, const Stages& sb) {
   const int slot = seg[4 * sg], dest = seg[4 * sg + 1];
   const int64_t t0 = seg[4 * sg + 2], ntok = seg[4 * sg + 3];
   const int64_t npad = pad_off[slot + 1] - pad_off[slot];
@@ -239,7 +261,7 @@ __device__ __forceinline__ void syrk_item(const uint16_t* __restrict__ xgT, cons
   if (item >= nd) {
     int a, b;
     tile_of(item - nd, a, b);
-    syrk_offdiag(base, npad, t0, nsteps, d, a + 1, b, Sd, partial, lds);
+    syrk_offdiag(base, npad, t0, nsteps, d, a + 1, b, Sd, partial, sb);
     return;
   }
   const int p = item, q = nt - 1 - item;
@@ -251,10 +273,10 @@ __device__ __forceinline__ void syrk_item(const uint16_t* __restrict__ xgT, cons
   const uint16_t* Bg = base + (int64_t)q * kT * npad;
   const int arows = min(kT, d - p * kT), brows = min(kT, d - q * kT);
   switch (k) {
-    case 0: syrk_diag_wave<0>(Ag, Bg, !single, npad, t0, nsteps, d, P, hp, active, Sd, partial, arows, brows, lds); break;
-    case 1: syrk_diag_wave<1>(Ag, Bg, !single, npad, t0, nsteps, d, P, hp, active, Sd, partial, arows, brows, lds); break;
-    case 2: syrk_diag_wave<2>(Ag, Bg, !single, npad, t0, nsteps, d, P, hp, active, Sd, partial, arows, brows, lds); break;
-    default: syrk_diag_wave<3>(Ag, Bg, !single, npad, t0, nsteps, d, P, hp, active, Sd, partial, arows, brows, lds); break;
+    case 0: syrk_diag_wave<0>(Ag, Bg, !single, npad, t0, nsteps, d, P, hp, active, Sd, partial, arows, brows, sb); break;
+    case 1: syrk_diag_wave<1>(Ag, Bg, !single, npad, t0, nsteps, d, P, hp, active, Sd, partial, arows, brows, sb); break;
+    case 2: syrk_diag_wave<2>(Ag, Bg, !single, npad, t0, nsteps, d, P, hp, active, Sd, partial, arows, brows, sb); break;
+    default: syrk_diag_wave<3>(Ag, Bg, !single, npad, t0, nsteps, d, P, hp, active, Sd, partial, arows, brows, sb); break;
   }
 }
 
@@ -267,8 +289,10 @@ __global__ __launch_bounds__(512) void syrk_kernel(const uint16_t* __restrict__ 
                                                    int32_t* __restrict__ work_next,
                                                    const int32_t* __restrict__ seg, int cap, int d,
                                                    float* __restrict__ S, float* __restrict__ partials) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[4 * kBuf];   // A0 B0 A1 B1
+  __shared__ __attribute__((aligned(16))) uint16_t a0[kPanel], a1[kPanel], a2[kPanel], a3[kPanel];
+  __shared__ __attribute__((aligned(16))) uint16_t b0[kPanel], b1[kPanel], b2[kPanel], b3[kPanel];
   __shared__ int item;
+  const Stages sb{{a0, a1, a2, a3}, {b0, b1, b2, b3}};
   const int x = blockIdx.x % kXcds;
   const int len = work_len[x];
   for (;;) {
@@ -278,7 +302,7 @@ __global__ __launch_bounds__(512) void syrk_kernel(const uint16_t* __restrict__ 
     __syncthreads();
     if (it >= len) break;
     const int code = work[x * cap + it];
-    syrk_item(xgT, pad_off, seg, code >> 10, code & 1023, d, S, partials, lds);
+    syrk_item(xgT, pad_off, seg, code >> 10, code & 1023, d, S, partials, sb);
   }
 }
 
