@@ -9,6 +9,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <algorithm>
 #include <map>
 #include <string>
 #include <vector>
@@ -470,10 +471,13 @@ CLHA_API clha_status clha_aggregate(clha_ctx* ctx, int32_t n_layers, const int32
   return hip_check(ctx, "aggregate");
 }
 
-// Factorisation of all distinct Hessians: groups of Hessians on up to
-// kFactorStreams streams forked from and joined back to the caller's stream;
-// group g starts once group g-1 has finished its first block step.
-static clha_status run_factor(clha_ctx* ctx, const GptqPlan& p, hipStream_t s) {
+// Factorisation of all distinct Hessians (and, when `jobs` is given, the GPTQ
+// of their jobs): groups of Hessians on up to kFactorStreams streams forked
+// from and joined back to the caller's stream; group g starts once group g-1
+// has finished its first block step.  A group's GPTQ jobs follow its own
+// factorisation on its stream, so they overlap the later groups' factors.
+// `jobs` (host copy of the device job table) must be sorted by Hessian.
+static clha_status run_factor(clha_ctx* ctx, const GptqPlan& p, hipStream_t s, const GJob* jobs) {
   if (!ctx->aux_ready) {
     for (auto& a : ctx->aux)
       if (hipStreamCreateWithFlags(&a, hipStreamNonBlocking) != hipSuccess)
@@ -485,11 +489,27 @@ static clha_status run_factor(clha_ctx* ctx, const GptqPlan& p, hipStream_t s) {
     ctx->aux_ready = true;
   }
   const int groups = p.n_mats < clha::kFactorStreams ? p.n_mats : clha::kFactorStreams;
+  int j = 0;
   for (int g = 0; g < groups; ++g) {
     const int m0 = (int)((int64_t)p.n_mats * g / groups), m1 = (int)((int64_t)p.n_mats * (g + 1) / groups);
     hipStream_t gs = g == 0 ? s : ctx->aux[g - 1];
     if (g > 0) hipStreamWaitEvent(gs, ctx->stagger[g - 1], 0);
     clha::launch_factor_group(p, m0, m1, gs, g + 1 < groups ? ctx->stagger[g] : nullptr);
+    if (jobs) {
+      clha::JobRange r{};
+      r.j0 = j;
+      while (j < p.n_jobs && jobs[j].mat < m1) ++j;
+      r.j1 = j;
+      if (r.j1 > r.j0) {
+        const GJob& first = jobs[r.j0];
+        const GJob& last = jobs[r.j1 - 1];
+        r.slab0 = first.slab_base;
+        r.n_slabs = last.slab_base + last.n_slabs - first.slab_base;
+        r.tile0 = first.tile_base;
+        r.n_tiles = last.tile_base + last.n_tiles - first.tile_base;
+        clha::launch_gptq(p, r, gs);
+      }
+    }
   }
   for (int g = 1; g < groups; ++g) {
     hipEventRecord(ctx->join[g], ctx->aux[g - 1]);
@@ -551,9 +571,15 @@ CLHA_API clha_status clha_gptq_quantize(clha_ctx* ctx, int32_t n_jobs, const clh
   // host tables: jobs, then the distinct Hessian pointers, staged in one copy
   std::vector<char> host(up256(sizeof(GJob) * n_jobs) + sizeof(float*) * n_mats);
   GJob* hj = reinterpret_cast<GJob*>(host.data());
+  // device job table ordered by Hessian (stable), so the jobs of each
+  // factorisation group are contiguous
+  std::vector<int> order(n_jobs);
+  for (int i = 0; i < n_jobs; ++i) order[i] = i;
+  std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return js.mat_of[a] < js.mat_of[b]; });
   int64_t wf_off = 0;
   int slab_base = 0, tile_base = 0;
-  for (int i = 0; i < n_jobs; ++i) {
+  for (int k = 0; k < n_jobs; ++k) {
+    const int i = order[k];
     const clha_gptq_job& j = jobs[i];
     GJob g;
     g.W = j.W;
@@ -570,7 +596,7 @@ CLHA_API clha_status clha_gptq_quantize(clha_ctx* ctx, int32_t n_jobs, const clh
     g.n_slabs = (j.rows + clha::kGptqRows - 1) / clha::kGptqRows;
     g.tile_base = tile_base;
     g.n_tiles = (g.n_slabs * clha::kGptqRows + clha::kGemmTile - 1) / clha::kGemmTile;
-    hj[i] = g;
+    hj[k] = g;
     wf_off += (int64_t)g.n_slabs * clha::kGptqRows * cols;
     slab_base += g.n_slabs;
     tile_base += g.n_tiles;
@@ -606,14 +632,11 @@ CLHA_API clha_status clha_gptq_quantize(clha_ctx* ctx, int32_t n_jobs, const clh
   p.partials = reinterpret_cast<float*>(L.partials);
   p.status = ctx->status_dev;
   {
-    StageTimer t(ctx, CLHA_STAGE_FACTOR, s);
-    st = run_factor(ctx, p, s);
+    // the factorisation and the quantization overlap: both are timed as GPTQ
+    StageTimer t(ctx, CLHA_STAGE_GPTQ, s);
+    st = run_factor(ctx, p, s, hj);
   }
   if (st != CLHA_OK) return st;
-  {
-    StageTimer t(ctx, CLHA_STAGE_GPTQ, s);
-    clha::launch_gptq(p, s);
-  }
   return hip_check(ctx, "gptq_quantize");
 }
 
@@ -659,7 +682,7 @@ CLHA_API clha_status clha_inverse_cholesky(clha_ctx* ctx, int32_t n, const float
   p.status = ctx->status_dev;
   {
     StageTimer t(ctx, CLHA_STAGE_FACTOR, s);
-    st = run_factor(ctx, p, s);
+    st = run_factor(ctx, p, s, nullptr);
   }
   if (st != CLHA_OK) return st;
   return hip_check(ctx, "inverse_cholesky");

@@ -191,17 +191,18 @@ __device__ __forceinline__ void far_update(const float (&e)[kRB], float* Wf, con
 
 // Columns [c0, min(c, c0 + kSuper)) of every slab.
 template <int G>
-__global__ __launch_bounds__(64, 2) void gptq_panel_kernel(GptqPlan p, int c0) {
+__global__ __launch_bounds__(64, 2) void gptq_panel_kernel(GptqPlan p, int c0, JobRange jr) {
   __shared__ float eb[kRB * 64];   // the block's errors as MFMA B operands
   const int c = p.cols;
   const int cend = min(c, c0 + kSuper);
-  int lo = 0, hi = p.n_jobs;
+  const int gslab = jr.slab0 + (int)blockIdx.x;
+  int lo = jr.j0, hi = jr.j1;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if (p.jobs[mid].slab_base <= (int)blockIdx.x) lo = mid; else hi = mid;
+    if (p.jobs[mid].slab_base <= gslab) lo = mid; else hi = mid;
   }
   const GJob job = p.jobs[lo];
-  const int slab = blockIdx.x - job.slab_base;
+  const int slab = gslab - job.slab_base;
   const int row0 = slab * kGptqRows;
   const int nrows = min(kGptqRows, job.rows - row0);
   const float* __restrict__ U = p.U + (int64_t)job.mat * c * c;
@@ -314,7 +315,7 @@ __global__ __launch_bounds__(64, 2) void gptq_panel_kernel(GptqPlan p, int c0) {
       __syncthreads();
     }
   }
-  double* part = reinterpret_cast<double*>(p.partials) + 2 * (int64_t)blockIdx.x;
+  double* part = reinterpret_cast<double*>(p.partials) + 2 * (int64_t)gslab;
   // sum of err^2 over the slab's live rows, reduced in a fixed lane order and
   // added to the earlier superblocks' sum (launches run in order)
   double v = live ? obs : 0.0;
@@ -340,16 +341,16 @@ constexpr int kGK = 32;              // K chunk
 constexpr int kGP = kGK + 4;         // LDS row pitch (floats): conflict-free 16-byte reads
 constexpr int kGBuf = kGemmTile * kGP;
 
-__global__ __launch_bounds__(256, 2) void gptq_trail_kernel(GptqPlan p, int c0) {
+__global__ __launch_bounds__(256, 2) void gptq_trail_kernel(GptqPlan p, int c0, JobRange jr) {
   __shared__ __attribute__((aligned(16))) float lds[4 * kGBuf];   // A0 B0 A1 B1
   const int c = p.cols, n0 = c0 + kSuper;
   const int ct = (c - n0 + kGemmTile - 1) / kGemmTile;
-  const int total = p.total_tiles * ct;
+  const int total = jr.n_tiles * ct;
   const int per = (total + kXcds - 1) / kXcds;
   const int L = (int)(blockIdx.x % kXcds) * per + (int)(blockIdx.x / kXcds);
   if (L >= total) return;
-  const int rtg = L / ct, cti = L - rtg * ct;
-  int lo = 0, hi = p.n_jobs;
+  const int rtg = jr.tile0 + L / ct, cti = L % ct;
+  int lo = jr.j0, hi = jr.j1;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
     if (p.jobs[mid].tile_base <= rtg) lo = mid; else hi = mid;
@@ -487,16 +488,17 @@ __global__ __launch_bounds__(256, 2) void gptq_trail_kernel(GptqPlan p, int c0) 
 }
 
 // ||Wq - W||^2 per slab (W with dead columns zeroed), coalesced over the outputs.
-__global__ __launch_bounds__(256) void gptq_dist_kernel(GptqPlan p) {
+__global__ __launch_bounds__(256) void gptq_dist_kernel(GptqPlan p, JobRange jr) {
   __shared__ double red[256];
   const int c = p.cols, group = p.group;
-  int lo = 0, hi = p.n_jobs;
+  const int gslab = jr.slab0 + (int)blockIdx.x;
+  int lo = jr.j0, hi = jr.j1;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if (p.jobs[mid].slab_base <= (int)blockIdx.x) lo = mid; else hi = mid;
+    if (p.jobs[mid].slab_base <= gslab) lo = mid; else hi = mid;
   }
   const GJob job = p.jobs[lo];
-  const int row0 = (blockIdx.x - job.slab_base) * kGptqRows;
+  const int row0 = (gslab - job.slab_base) * kGptqRows;
   const int nrows = min(kGptqRows, job.rows - row0);
   const uint8_t* dead = p.dead + (int64_t)job.mat * c;
   const int ng = c / group;
@@ -526,11 +528,11 @@ __global__ __launch_bounds__(256) void gptq_dist_kernel(GptqPlan p) {
     if (threadIdx.x < st) red[threadIdx.x] += red[threadIdx.x + st];
     __syncthreads();
   }
-  if (threadIdx.x == 0) reinterpret_cast<double*>(p.partials)[2 * (int64_t)blockIdx.x + 1] = red[0];
+  if (threadIdx.x == 0) reinterpret_cast<double*>(p.partials)[2 * (int64_t)gslab + 1] = red[0];
 }
 
-__global__ void gptq_finish_kernel(GptqPlan p) {
-  const GJob job = p.jobs[blockIdx.x];
+__global__ void gptq_finish_kernel(GptqPlan p, JobRange jr) {
+  const GJob job = p.jobs[jr.j0 + blockIdx.x];
   if (threadIdx.x != 0 || job.loss == nullptr) return;
   const double* part = reinterpret_cast<const double*>(p.partials);
   double obs = 0.0, d2 = 0.0;
@@ -545,26 +547,27 @@ bool gptq_group_supported(int group) {
   return group == 4 || group == 8 || group == 16 || group == 32 || group == 64 || group == 128;
 }
 
-void launch_gptq(const GptqPlan& p, hipStream_t s) {
-  const dim3 grid(p.total_slabs), blk(64);
+void launch_gptq(const GptqPlan& p, const JobRange& jr, hipStream_t s) {
+  if (jr.j1 <= jr.j0) return;
+  const dim3 grid(jr.n_slabs), blk(64);
   for (int c0 = 0; c0 < p.cols; c0 += kSuper) {
     switch (p.group) {
-      case 4: hipLaunchKernelGGL(gptq_panel_kernel<4>, grid, blk, 0, s, p, c0); break;
-      case 8: hipLaunchKernelGGL(gptq_panel_kernel<8>, grid, blk, 0, s, p, c0); break;
-      case 16: hipLaunchKernelGGL(gptq_panel_kernel<16>, grid, blk, 0, s, p, c0); break;
-      case 32: hipLaunchKernelGGL(gptq_panel_kernel<32>, grid, blk, 0, s, p, c0); break;
-      case 64: hipLaunchKernelGGL(gptq_panel_kernel<64>, grid, blk, 0, s, p, c0); break;
-      default: hipLaunchKernelGGL(gptq_panel_kernel<128>, grid, blk, 0, s, p, c0); break;
+      case 4: hipLaunchKernelGGL(gptq_panel_kernel<4>, grid, blk, 0, s, p, c0, jr); break;
+      case 8: hipLaunchKernelGGL(gptq_panel_kernel<8>, grid, blk, 0, s, p, c0, jr); break;
+      case 16: hipLaunchKernelGGL(gptq_panel_kernel<16>, grid, blk, 0, s, p, c0, jr); break;
+      case 32: hipLaunchKernelGGL(gptq_panel_kernel<32>, grid, blk, 0, s, p, c0, jr); break;
+      case 64: hipLaunchKernelGGL(gptq_panel_kernel<64>, grid, blk, 0, s, p, c0, jr); break;
+      default: hipLaunchKernelGGL(gptq_panel_kernel<128>, grid, blk, 0, s, p, c0, jr); break;
     }
     const int n0 = c0 + kSuper;
     if (n0 < p.cols) {
-      const int tiles = p.total_tiles * ((p.cols - n0 + kGemmTile - 1) / kGemmTile);
+      const int tiles = jr.n_tiles * ((p.cols - n0 + kGemmTile - 1) / kGemmTile);
       const int per = (tiles + kXcds - 1) / kXcds;
-      hipLaunchKernelGGL(gptq_trail_kernel, dim3(per * kXcds), dim3(256), 0, s, p, c0);
+      hipLaunchKernelGGL(gptq_trail_kernel, dim3(per * kXcds), dim3(256), 0, s, p, c0, jr);
     }
   }
-  hipLaunchKernelGGL(gptq_dist_kernel, dim3(p.total_slabs), dim3(256), 0, s, p);
-  hipLaunchKernelGGL(gptq_finish_kernel, dim3(p.n_jobs), dim3(64), 0, s, p);
+  hipLaunchKernelGGL(gptq_dist_kernel, dim3(jr.n_slabs), dim3(256), 0, s, p, jr);
+  hipLaunchKernelGGL(gptq_finish_kernel, dim3(jr.j1 - jr.j0), dim3(64), 0, s, p, jr);
 }
 
 }  // namespace clha

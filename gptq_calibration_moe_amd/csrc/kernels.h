@@ -111,7 +111,11 @@ struct GptqPlan {
 };
 constexpr int kFactorStreams = 4;     // Hessian groups factored on separate streams
 void launch_factor_group(const GptqPlan& p, int m0, int m1, hipStream_t s, hipEvent_t step0_done);
-void launch_gptq(const GptqPlan& p, hipStream_t s);
+// A contiguous range of jobs [j0, j1) with their global slabs and row tiles.
+struct JobRange {
+  int j0, j1, slab0, n_slabs, tile0, n_tiles;
+};
+void launch_gptq(const GptqPlan& p, const JobRange& r, hipStream_t s);
 
 // ---------------------------------------------------------------- loss
 void launch_loss(int rows, int cols, int group, const void* W, int dtype, const uint8_t* codes,

@@ -224,8 +224,8 @@ typedef enum clha_stage {
   CLHA_STAGE_GATHER = 2,     /* gather of each expert's rows */
   CLHA_STAGE_SYRK = 3,       /* Gram-sum kernel (one launch per collect call) */
   CLHA_STAGE_AGGREGATE = 4,  /* aggregation kernel */
-  CLHA_STAGE_FACTOR = 5,     /* damping, Cholesky and triangular inverse kernels */
-  CLHA_STAGE_GPTQ = 6,       /* GPTQ kernel and its loss reduction */
+  CLHA_STAGE_FACTOR = 5,     /* damping, Cholesky and triangular inverse (clha_inverse_cholesky) */
+  CLHA_STAGE_GPTQ = 6,       /* clha_gptq_quantize: factorisation and GPTQ, which overlap */
   CLHA_STAGE_LOSS = 7,       /* explicit loss kernels */
   CLHA_NUM_STAGES = 8
 } clha_stage;
