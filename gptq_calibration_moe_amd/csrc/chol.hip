@@ -11,12 +11,13 @@
 // R = J L J upper triangular, Hd^-1 = R^-T R^-1, and U = R^-1 = J L^-1 J.
 // Cost: c^3/3 flops for the factorisation and c^3/3 for the triangular inverse.
 //
-// Precision: the factorisation and the inverse run in fp64 (the fp64 matrix
-// cores, v_mfma_f64_16x16x4f64, run at half the fp32 rate on MI355X).  A
+// Precision: the factorisation runs in fp64 (v_mfma_f64_16x16x4f64).  A
 // right-looking fp32 factorisation rounds each diagonal entry once per block
 // step while it shrinks from H_jj to its Schur complement, which costs about a
 // decimal digit on ill-conditioned Hessians; GPTQ's code decisions inherit that
-// error.  U is rounded to fp32 once, at the end.
+// error.  The triangular inverse then runs in fp32 (v_mfma_f32_32x32x2f32,
+// about four times the sustained fp64 matrix rate): its error is governed by
+// cond(L) = sqrt(cond(Hd)), and it moves U by a few fp32 ulps.
 //
 // Every step is batched over all distinct Hessians of one call:
 //   diag_stats      dead columns (H_ii == 0) and lambda = damp * mean(diag),
@@ -28,10 +29,10 @@
 //     chol_diag     L_kk = chol(T_k) and its inverse Dinv_k (one wavefront per matrix,
 //                   rows in registers)
 //     chol_panel    L[i][k] = T_i Dinv_k^T for i > k
-//   triangular inverse X = L^-1 (fp64), merged bottom-up over block ranges:
+//   triangular inverse X = L^-1, merged bottom-up over block ranges in fp32:
 //     trtri_leaf    X[i][i] = Dinv_i
 //     trtri_merge   X21 = -X22 L21 X11 per merge (two batched GEMMs per level),
-//                   U = J X J and U^T written in fp32 as X becomes final
+//                   U = J X J and U^T written as X becomes final
 // The Hessians of one call are split into groups, one stream each, started one
 // block step apart (see launch_factor_group).
 #include "kernels.h"
@@ -313,55 +314,68 @@ __global__ __launch_bounds__(256) void chol_panel_kernel(double* __restrict__ Aa
 //   X21 = -X22 L21 X11,   L21 = L[mid:b, a:mid]
 // (the inverse of a 2x2 block lower-triangular matrix).  Level s merges ranges
 // of 2s blocks (s = 1, 2, 4, ...); merges of one level are independent.  The
-// leaves are the diagonal blocks' inverses Dinv from the factorisation.  Each
-// merge is two batched fp64 GEMMs on the matrix cores:
+// leaves are the fp64 diagonal-block inverses Dinv of the factorisation.
+// The factor L is fp64; the merges run in fp32 on the matrix cores
+// (v_mfma_f32_32x32x2f32): the inverse is well conditioned relative to the
+// factor (cond(L) = sqrt(cond(Hd))), and U is stored in fp32 in any case.
+// Each merge is two batched GEMMs:
 //   phase 0:  T = L21 X11     (X11 lower triangular: only k >= column counts)
 //   phase 1:  X21 = -X22 T    (X22 lower triangular: only k <= row counts)
-// T is kept transposed in the strictly upper triangle of A, which the
-// factorisation leaves unused: T[row][col] at A[col][row].  Every X element is
-// final when written, so U = J X J (and U^T) get their fp32 values at once.
+// fp32 storage, in the (fp64-sized) X buffer of each Hessian:
+//   X32  [c][c]  X row-major (lower triangle); its strictly upper triangle holds
+//                T^T during a level: T[row][col] at X32[col][row]
+//   XT32 [c][c]  X^T row-major (upper triangle)
+// so every GEMM operand is a K-contiguous row.  Every X element is final when
+// written, so U = J X J and U^T get their values at once.
 
-// Leaves: X[i][i] = Dinv_i (zeros above the diagonal), and U, U^T there.
+// Leaves: X[i][i] = Dinv_i (zeros above the diagonal), in X32, XT32, U and U^T.
 __global__ __launch_bounds__(256) void trtri_leaf_kernel(int c, const double* __restrict__ dinv,
                                                          double* __restrict__ Xall,
                                                          float* __restrict__ Uall,
                                                          float* __restrict__ UTall) {
   const int m = blockIdx.y, i = blockIdx.x;
-  double* X = Xall + (int64_t)m * c * c;
+  float* X32 = reinterpret_cast<float*>(Xall + (int64_t)m * c * c);
+  float* XT32 = X32 + (int64_t)c * c;
   float* U = Uall + (int64_t)m * c * c;
   float* UT = UTall ? UTall + (int64_t)m * c * c : nullptr;
   const double* Di = dinv + ((int64_t)m * (c / kNb) + i) * kNb * kNb;
   const int64_t i0 = (int64_t)i * kNb;
   for (int idx = threadIdx.x; idx < kNb * kNb; idx += 256) {
     const int r = idx >> 6, cc = idx & 63;
-    const double v = cc <= r ? Di[idx] : 0.0;
-    X[(i0 + r) * c + i0 + cc] = v;
-    if (cc <= r) U[(c - 1 - (i0 + r)) * c + (c - 1 - (i0 + cc))] = (float)v;
-    // U^T: element (c-1-(i0+cc), c-1-(i0+r)); consecutive threads step r
+    const float v = cc <= r ? (float)Di[idx] : 0.0f;
+    X32[(i0 + r) * c + i0 + cc] = v;
+    if (cc <= r) U[(c - 1 - (i0 + r)) * c + (c - 1 - (i0 + cc))] = v;
+    // transposed element (consecutive threads step its column)
     const int rr = idx & 63, c2 = idx >> 6;
-    if (UT && c2 <= rr) UT[(c - 1 - (i0 + c2)) * c + (c - 1 - (i0 + rr))] = (float)Di[rr * kNb + c2];
+    const float vt = c2 <= rr ? (float)Di[rr * kNb + c2] : 0.0f;
+    XT32[(i0 + c2) * c + i0 + rr] = vt;
+    if (UT && c2 <= rr) UT[(c - 1 - (i0 + c2)) * c + (c - 1 - (i0 + rr))] = vt;
   }
 }
 
-constexpr int kTT = 128;          // merge tile: rows and columns
-constexpr int kTK = 16;           // K chunk
-constexpr int kTPa = kTK + 2;     // pitch of [row][k] LDS tiles (doubles): conflict-free lane reads
-constexpr int kTPb = kTT + 16;    // pitch of the [k][col] LDS tile (doubles)
-constexpr int kTBuf = kTT * kTPa; // one operand buffer (== kTK * kTPb)
-static_assert(kTT * kTPa == kTK * kTPb, "operand buffers share one size");
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-// One 128x128 tile of one merge.  256 threads = 4 waves of 64x64 (4x4 blocks
-// of v_mfma_f64_16x16x4f64; lane layout as in Tile64).  Operands are staged
-// through LDS in chunks of 16 along K, double-buffered with two register
-// stages.  Tiles of one merge are mapped to one XCD (workgroup b runs on XCD
-// b % 8) so its operands are shared through one L2.
+constexpr int kTT = 128;          // merge tile: rows and columns
+constexpr int kTK = 32;           // K chunk
+constexpr int kTP = kTK + 4;      // LDS row pitch (floats): conflict-free 16-byte lane reads
+constexpr int kTBuf = kTT * kTP;  // one operand buffer (floats)
+
+// One 128x128 tile of one merge.  256 threads = 4 waves of 64x64 (2x2 blocks of
+// v_mfma_f32_32x32x2f32).  Both operands are K-contiguous rows staged through
+// LDS in chunks of 32, double-buffered with two register stages; MFMA step s
+// contracts k = s in lanes 0..31 and k = 16 + s in lanes 32..63 (one
+// permutation of k for both operands), so a lane's operands of a chunk are 4
+// contiguous 16-byte LDS reads.  Phase 0 walks K downwards from the merge's
+// common end, phase 1 upwards from its common start, so the tiles of a merge
+// read the same chunks at about the same time; tiles of one merge are mapped
+// to one XCD (workgroup b runs on XCD b % 8).
 template <int PHASE>
-__global__ __launch_bounds__(256, 2) void trtri_merge_kernel(double* __restrict__ Aall,
+__global__ __launch_bounds__(256, 2) void trtri_merge_kernel(const double* __restrict__ Aall,
                                                              double* __restrict__ Xall,
                                                              float* __restrict__ Uall,
                                                              float* __restrict__ UTall, int c, int s,
                                                              int n_merge, int tc, int n_mats) {
-  __shared__ __attribute__((aligned(16))) double lds[4 * kTBuf];   // A0 B0 A1 B1
+  __shared__ __attribute__((aligned(16))) float lds[4 * kTBuf];   // A0 B0 A1 B1
   const int nbk = c / kNb, tmax = tc * tc;
   const int total = n_mats * n_merge * tmax;
   const int per = (total + kXcds - 1) / kXcds;
@@ -374,99 +388,97 @@ __global__ __launch_bounds__(256, 2) void trtri_merge_kernel(double* __restrict_
   const int r0 = mid * kNb + ti * kTT, c0 = a * kNb + tj * kTT;
   const int nr = min(kTT, b * kNb - r0), nc = min(kTT, mid * kNb - c0);
   if (nr <= 0 || nc <= 0) return;
-  // K range of the tile (64-aligned; masked elements contribute zero)
   const int k0 = PHASE == 0 ? c0 : mid * kNb;
   const int k1 = PHASE == 0 ? mid * kNb : min(r0 + kTT, b * kNb);
-  const int nch = (k1 - k0) / kTK;
-  double* A = Aall + (int64_t)m * c * c;
-  double* X = Xall + (int64_t)m * c * c;
-  // A operand rows (K-contiguous): phase 0 L[r0 + i][k], phase 1 X[r0 + i][k]
-  const double* Ar = (PHASE == 0 ? A : X) + (int64_t)r0 * c;
+  const int nch = (k1 - k0) / kTK;   // even: K ranges are multiples of 64
+  const double* A = Aall + (int64_t)m * c * c;
+  float* X32 = reinterpret_cast<float*>(Xall + (int64_t)m * c * c);
+  float* XT32 = X32 + (int64_t)c * c;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 1, wn = wave & 1, h = lane >> 5, li = lane & 31;
   const bool active = wm * 64 < nr && wn * 64 < nc;
-  const int li = lane & 15, lk = lane >> 4, ai = 4 * (li & 3) + (li >> 2);
 
+  // MFMA A operand rows (tile row i):  phase 0 L21[r0+i][k] (fp64), phase 1 X22[r0+i][k]
+  // MFMA B operand rows (tile column j): phase 0 X11^T[c0+j][k] = XT32, phase 1 T^T[c0+j][k] = X32
   struct Stage {
-    double2 a[4], b[4];
+    float4 a[4], b[4];
   };
-  // Phase 0 walks K downwards from the merge's common end, phase 1 upwards from
-  // its common start: the tiles of one merge then read the same K chunks at
-  // about the same time, so one L2 serves them all.
+  // thread t moves 16-byte chunks q = t + 256u: row q/8, k = 4(q%8) .. +3
   auto fetch = [&](Stage& rg, int ch) {
     const int kb = PHASE == 0 ? k1 - (ch + 1) * kTK : k0 + ch * kTK;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int q = tid + 256 * u;
-      {  // A operand: row q/8, k pair 2(q%8)
-        const int row = q >> 3, kc = 2 * (q & 7), kk = kb + kc;
-        double2 v = make_double2(0.0, 0.0);
-        if (row < nr) {
-          v = *reinterpret_cast<const double2*>(Ar + (int64_t)row * c + kk);
-          if (PHASE == 1) {   // X22 lower triangular
-            if (kk > r0 + row) v.x = 0.0;
-            if (kk + 1 > r0 + row) v.y = 0.0;
-          }
+      const int q = tid + 256 * u, row = q >> 3, kk = kb + 4 * (q & 7);
+      float4 va = make_float4(0.f, 0.f, 0.f, 0.f), vb = va;
+      if (row < nr) {
+        if (PHASE == 0) {
+          const double* src = A + (int64_t)(r0 + row) * c + kk;
+          const double2 lo = *reinterpret_cast<const double2*>(src);
+          const double2 hi = *reinterpret_cast<const double2*>(src + 2);
+          va = make_float4((float)lo.x, (float)lo.y, (float)hi.x, (float)hi.y);
+        } else {   // X22 lower triangular: k <= row
+          va = *reinterpret_cast<const float4*>(X32 + (int64_t)(r0 + row) * c + kk);
+          const int rr = r0 + row;
+          if (kk > rr) va.x = 0.f;
+          if (kk + 1 > rr) va.y = 0.f;
+          if (kk + 2 > rr) va.z = 0.f;
+          if (kk + 3 > rr) va.w = 0.f;
         }
-        rg.a[u] = v;
       }
-      if (PHASE == 0) {  // B = X11[k][c0 + j]: k row q/64, column pair 2(q%64)
-        const int krow = q >> 6, jc = 2 * (q & 63), kk = kb + krow;
-        double2 v = make_double2(0.0, 0.0);
-        if (jc < nc) {
-          v = *reinterpret_cast<const double2*>(X + (int64_t)kk * c + c0 + jc);
-          if (kk < c0 + jc) v.x = 0.0;
-          if (kk < c0 + jc + 1) v.y = 0.0;
+      if (row < nc) {
+        const int cc = c0 + row;
+        if (PHASE == 0) {   // X11^T row cc: X11[k][cc] is nonzero for k >= cc
+          vb = *reinterpret_cast<const float4*>(XT32 + (int64_t)cc * c + kk);
+          if (kk < cc) vb.x = 0.f;
+          if (kk + 1 < cc) vb.y = 0.f;
+          if (kk + 2 < cc) vb.z = 0.f;
+          if (kk + 3 < cc) vb.w = 0.f;
+        } else {
+          vb = *reinterpret_cast<const float4*>(X32 + (int64_t)cc * c + kk);
         }
-        rg.b[u] = v;
-      } else {           // B^T = T^T[c0 + j][k] stored at A[c0 + j][k]: row q/8, k pair 2(q%8)
-        const int row = q >> 3, kc = 2 * (q & 7);
-        rg.b[u] = row < nc ? *reinterpret_cast<const double2*>(A + (int64_t)(c0 + row) * c + kb + kc)
-                           : make_double2(0.0, 0.0);
       }
+      rg.a[u] = va;
+      rg.b[u] = vb;
     }
   };
   auto stage = [&](const Stage& rg, int buf) {
-    double* As = lds + (2 * buf) * kTBuf;
-    double* Bs = lds + (2 * buf + 1) * kTBuf;
+    float* As = lds + (2 * buf) * kTBuf;
+    float* Bs = lds + (2 * buf + 1) * kTBuf;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int q = tid + 256 * u;
-      *reinterpret_cast<double2*>(As + (q >> 3) * kTPa + 2 * (q & 7)) = rg.a[u];
-      if (PHASE == 0)
-        *reinterpret_cast<double2*>(Bs + (q >> 6) * kTPb + 2 * (q & 63)) = rg.b[u];
-      else
-        *reinterpret_cast<double2*>(Bs + (q >> 3) * kTPa + 2 * (q & 7)) = rg.b[u];
+      const int q = tid + 256 * u, row = q >> 3, kc = 4 * (q & 7);
+      *reinterpret_cast<float4*>(As + row * kTP + kc) = rg.a[u];
+      *reinterpret_cast<float4*>(Bs + row * kTP + kc) = rg.b[u];
     }
   };
-  f64x4 acc[4][4];
+  f32x16 acc[2][2];
 #pragma unroll
-  for (int x = 0; x < 4; ++x)
+  for (int x = 0; x < 2; ++x)
 #pragma unroll
-    for (int y = 0; y < 4; ++y) acc[x][y] = f64x4{0.0, 0.0, 0.0, 0.0};
+    for (int y = 0; y < 2; ++y) acc[x][y] = f32x16{};
   auto multiply = [&](int buf) {
     if (!active) return;
-    const double* As = lds + (2 * buf) * kTBuf + (wm * 64 + ai) * kTPa + lk;
-    const double* Bs = lds + (2 * buf + 1) * kTBuf;
+    const float* As = lds + (2 * buf) * kTBuf + (wm * 64 + li) * kTP + 16 * h;
+    const float* Bs = lds + (2 * buf + 1) * kTBuf + (wn * 64 + li) * kTP + 16 * h;
+    float4 av[2][4], bv[2][4];
 #pragma unroll
-    for (int kk = 0; kk < kTK; kk += 4) {
-      double av[4], bv[4];
+    for (int mm = 0; mm < 4; ++mm)
 #pragma unroll
-      for (int x = 0; x < 4; ++x) av[x] = As[x * 16 * kTPa + kk];
+      for (int x = 0; x < 2; ++x) {
+        av[x][mm] = *reinterpret_cast<const float4*>(As + 32 * x * kTP + 4 * mm);
+        bv[x][mm] = *reinterpret_cast<const float4*>(Bs + 32 * x * kTP + 4 * mm);
+      }
 #pragma unroll
-      for (int y = 0; y < 4; ++y)
-        bv[y] = PHASE == 0 ? Bs[(kk + lk) * kTPb + wn * 64 + y * 16 + li]
-                           : Bs[(wn * 64 + y * 16 + li) * kTPa + kk + lk];
+    for (int st = 0; st < 16; ++st)
 #pragma unroll
-      for (int x = 0; x < 4; ++x)
+      for (int x = 0; x < 2; ++x)
 #pragma unroll
-        for (int y = 0; y < 4; ++y)
-          acc[x][y] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[x], bv[y], acc[x][y], 0, 0, 0);
-    }
+        for (int y = 0; y < 2; ++y)
+          acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x2f32((&av[x][st >> 2].x)[st & 3],
+                                                           (&bv[y][st >> 2].x)[st & 3], acc[x][y], 0, 0, 0);
   };
 
-  // nch is a multiple of 4
   Stage g0, g1;
   fetch(g0, 0);
   stage(g0, 0);
@@ -485,30 +497,35 @@ __global__ __launch_bounds__(256, 2) void trtri_merge_kernel(double* __restrict_
     __syncthreads();
   }
   if (!active) return;
-  // element (row, col) of the tile: row = wm*64 + 16x + 4(lane/16) + r, col = wn*64 + 16y + lane%16
+  // element (i, j) of the tile: i = wm*64 + 32x + 8(r/4) + 4h + r%4, j = wn*64 + 32y + li
+  float* U = Uall + (int64_t)m * c * c;
+  float* UT = UTall ? UTall + (int64_t)m * c * c : nullptr;
 #pragma unroll
-  for (int x = 0; x < 4; ++x)
+  for (int x = 0; x < 2; ++x)
 #pragma unroll
-    for (int y = 0; y < 4; ++y) {
-      const int row = r0 + wm * 64 + 16 * x + 4 * lk, col = c0 + wn * 64 + 16 * y + li;
-      const f64x4 v = acc[x][y];
-      if (PHASE == 0) {
-        // T^T[col][row .. row+3], contiguous
-        double* tp = A + (int64_t)col * c + row;
-        *reinterpret_cast<double2*>(tp) = make_double2(v[0], v[1]);
-        *reinterpret_cast<double2*>(tp + 2) = make_double2(v[2], v[3]);
-      } else {
-        float* U = Uall + (int64_t)m * c * c;
+    for (int y = 0; y < 2; ++y) {
+      const int col = c0 + wn * 64 + 32 * y + li;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          X[(int64_t)(row + r) * c + col] = -v[r];
-          U[(int64_t)(c - 1 - (row + r)) * c + (c - 1 - col)] = (float)(-v[r]);
-        }
-        if (UTall) {
+      for (int q = 0; q < 4; ++q) {
+        const int row = r0 + wm * 64 + 32 * x + 8 * q + 4 * h;   // rows row .. row+3
+        const f32x16& v = acc[x][y];
+        if (PHASE == 0) {
+          // T^T[col][row .. row+3] in X32's strictly upper triangle
+          *reinterpret_cast<float4*>(X32 + (int64_t)col * c + row) =
+              make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+        } else {
+          const float e0 = -v[4 * q], e1 = -v[4 * q + 1], e2 = -v[4 * q + 2], e3 = -v[4 * q + 3];
+          *reinterpret_cast<float4*>(XT32 + (int64_t)col * c + row) = make_float4(e0, e1, e2, e3);
+          const float ev[4] = {e0, e1, e2, e3};
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            X32[(int64_t)(row + r) * c + col] = ev[r];
+            U[(int64_t)(c - 1 - (row + r)) * c + (c - 1 - col)] = ev[r];
+          }
           // U^T row c-1-col, columns c-1-row-3 .. c-1-row (ascending)
-          float* ut = UTall + (int64_t)m * c * c + (int64_t)(c - 1 - col) * c + (c - 4 - row);
-          *reinterpret_cast<float4*>(ut) =
-              make_float4((float)(-v[3]), (float)(-v[2]), (float)(-v[1]), (float)(-v[0]));
+          if (UT)
+            *reinterpret_cast<float4*>(UT + (int64_t)(c - 1 - col) * c + (c - 4 - row)) =
+                make_float4(e3, e2, e1, e0);
         }
       }
     }

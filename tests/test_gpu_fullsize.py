@@ -22,7 +22,7 @@ import torch
 
 import gen
 import oracle
-from gpu_util import (CODE_AGREE, HESS_TOL, LOSS_RTOL, agree, bits_to_dev, dev, hess_err, to_dev,
+from gpu_util import (CODE_AGREE, HESS_TOL, LOSS_RTOL, SCALE_RTOL, agree, bits_to_dev, dev, hess_err, to_dev,
                       weights_to_dev)
 
 pytestmark = pytest.mark.gpu
@@ -49,7 +49,7 @@ def _check_gptq(wl, w_bits, H_ref, out, bits, label):
     assert codes.max() <= (1 << bits) - 1
     ok = (codes == ref["codes"]).all(axis=1)               # rows decided identically throughout
     assert ok.mean() >= 0.9, f"{label}: only {ok.mean():.3f} of the rows agree in every code"
-    np.testing.assert_allclose(out["scales"].cpu().numpy()[ok], ref["scales"][ok], rtol=1e-5)
+    np.testing.assert_allclose(out["scales"].cpu().numpy()[ok], ref["scales"][ok], rtol=SCALE_RTOL)
     assert (out["zeros"].cpu().numpy()[ok] == ref["zeros"][ok]).all(), label
     ref_loss = oracle.loss(wv, ref["wq"], H_ref)
     got = float(out["loss"].cpu().numpy()[0])

@@ -10,7 +10,7 @@ import torch
 
 import gen
 import oracle
-from gpu_util import (CODE_AGREE, HESS_TOL, LOSS_RTOL, agree, bits_to_dev, dev, hess_err,
+from gpu_util import (CODE_AGREE, HESS_TOL, LOSS_RTOL, SCALE_RTOL, agree, bits_to_dev, dev, hess_err,
                       run_group, to_dev, weights_to_dev)
 
 pytestmark = pytest.mark.gpu
@@ -300,7 +300,7 @@ def test_gptq_stage(seed, rows, c, bits, group, block, wdt, dead):
     assert codes.max() <= (1 << bits) - 1
     ok = (codes == ref["codes"]).all(axis=1)
     if ok.any():
-        np.testing.assert_allclose(job["scales"].cpu().numpy()[ok], ref["scales"][ok], rtol=1e-5)
+        np.testing.assert_allclose(job["scales"].cpu().numpy()[ok], ref["scales"][ok], rtol=SCALE_RTOL)
         assert (job["zeros"].cpu().numpy()[ok] == ref["zeros"][ok]).all()
     want = oracle.loss(Wv, ref["wq"], H.astype(np.float64))
     got = float(job["loss"].cpu().numpy()[0])
