@@ -149,7 +149,10 @@ def summarize_profiles(d, workload_name="mid_moe_block"):
     cmd = {k: c.format(dir=d) for k, c in PROFILE_RUNS}
     lines = [f"# Kernel time per step, {workload_name} workload (MI355X, rocprofv3 kernel trace)", "",
              "Command (repository root):", "", f"    {cmd['trace']}", "",
-             f"{steps} steps traced (1 warm-up + 3 timed); per-step figures are totals / {steps}.", "",
+             f"{steps} steps traced (1 warm-up + 3 timed); per-step figures are totals / {steps}.",
+             "The factorisation runs as four Hessian groups on concurrent streams, overlapped with the",
+             "GPTQ kernels, so per-kernel times overlap in wall time; wall-clock stage times are",
+             "`stages_ms_per_step` in the bench line.", "",
              "| kernel | calls/step | ms/step | avg us/launch | % |", "|---|---:|---:|---:|---:|"]
     total = sum(float(r["TotalDurationNs"]) for r in stats)
     for r in stats:
