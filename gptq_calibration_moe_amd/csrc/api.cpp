@@ -369,6 +369,7 @@ CLHA_API clha_status clha_collect_hessians(clha_ctx* ctx, int32_t layer, int64_t
   if (n_tokens < 0 || n_tokens > ctx->desc.max_tokens)
     return fail(ctx, CLHA_ERR_SHAPE, "collect_hessians: n_tokens %lld outside 0..%lld",
                 (long long)n_tokens, (long long)ctx->desc.max_tokens);
+  if (n_tokens == 0) return CLHA_OK;   // an empty batch adds nothing; its pointers are not read
   if (!x || !logits || !workspace)
     return fail(ctx, CLHA_ERR_INVALID_ARG, "collect_hessians: null x, logits or workspace");
   if (!aligned16(x) || !aligned4(logits) || !aligned16(workspace) ||
@@ -379,7 +380,6 @@ CLHA_API clha_status clha_collect_hessians(clha_ctx* ctx, int32_t layer, int64_t
   if (workspace_bytes < need.bytes)
     return fail(ctx, CLHA_ERR_WORKSPACE, "collect_hessians: workspace %zu < %zu bytes",
                 workspace_bytes, need.bytes);
-  if (n_tokens == 0) return CLHA_OK;
   const CollectLayout L = collect_layout(ctx, workspace);
   const clha_moe_desc& d = ctx->desc;
   CollectPlan p;

@@ -324,8 +324,7 @@ __global__ __launch_bounds__(64, 2) void gptq_panel_kernel(GptqPlan p, int c0, J
 }
 
 // Trailing update after the superblock at c0, for all jobs:
-//   Wf[:, n0:] -= E U[c0:c0+kSuper, n0:],   n0 = c0 + kSuper,
-// accumulated as -Wf + E U and stored negated.
+//   Wf[:, n0:] -= E U[c0:c0+kSuper, n0:],   n0 = c0 + kSuper.
 // Tile: 128 padded rows x 128 columns of one job, 256 threads = 4 waves of
 // 64x64 (2x2 blocks of v_mfma_f32_32x32x2f32).  As in the panel's update the
 // product is transposed, C[col][row] = sum_k U^T[col][k] E[row][k], so each
@@ -394,7 +393,16 @@ __global__ __launch_bounds__(256, 2) void gptq_trail_kernel(GptqPlan p, int c0, 
     }
   };
 
-  f32x16 acc[2][2];
+  // The tile's current weights are loaded first, into registers, and only
+  // used at the end (W - E U), so their latency overlaps the products.
+  f32x16 acc[2][2], wv[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      acc[a][b] = f32x16{};
+      wv[a][b] = f32x16{};
+    }
   float* wrow[2];
 #pragma unroll
   for (int b = 0; b < 2; ++b) wrow[b] = W + (int64_t)(wr * 64 + 32 * b + li) * c + wc * 64 + 4 * h;
@@ -413,10 +421,10 @@ __global__ __launch_bounds__(256, 2) void gptq_trail_kernel(GptqPlan p, int c0, 
           float4 v = r < job.rows ? load_w4(job.W, job.dtype, wbase + 32 * a + 8 * q)
                                   : make_float4(0.f, 0.f, 0.f, 0.f);
           const uchar4 dd = *reinterpret_cast<const uchar4*>(dead + 32 * a + 8 * q);
-          acc[a][b][4 * q] = dd.x ? 0.f : -v.x;
-          acc[a][b][4 * q + 1] = dd.y ? 0.f : -v.y;
-          acc[a][b][4 * q + 2] = dd.z ? 0.f : -v.z;
-          acc[a][b][4 * q + 3] = dd.w ? 0.f : -v.w;
+          wv[a][b][4 * q] = dd.x ? 0.f : v.x;
+          wv[a][b][4 * q + 1] = dd.y ? 0.f : v.y;
+          wv[a][b][4 * q + 2] = dd.z ? 0.f : v.z;
+          wv[a][b][4 * q + 3] = dd.w ? 0.f : v.w;
         }
     }
   } else if (active) {
@@ -427,10 +435,10 @@ __global__ __launch_bounds__(256, 2) void gptq_trail_kernel(GptqPlan p, int c0, 
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const float4 v = *reinterpret_cast<const float4*>(wrow[b] + 32 * a + 8 * q);
-          acc[a][b][4 * q] = -v.x;
-          acc[a][b][4 * q + 1] = -v.y;
-          acc[a][b][4 * q + 2] = -v.z;
-          acc[a][b][4 * q + 3] = -v.w;
+          wv[a][b][4 * q] = v.x;
+          wv[a][b][4 * q + 1] = v.y;
+          wv[a][b][4 * q + 2] = v.z;
+          wv[a][b][4 * q + 3] = v.w;
         }
   }
   auto multiply = [&](int buf) {
@@ -456,14 +464,15 @@ __global__ __launch_bounds__(256, 2) void gptq_trail_kernel(GptqPlan p, int c0, 
                                                            (&bv[b][st >> 2].x)[st & 3], acc[a][b], 0, 0, 0);
   };
 
-  constexpr int nch = kSuper / kGK;   // 8, even
+  constexpr int nch = kSuper / kGK;   // 8, even; the loop is unrolled, so every
+                                      // fetch is unconditional and waits count exactly
   Stage r0, r1;
   fetch(r0, 0);
   stage(r0, 0);
   fetch(r1, kGK);
   fetch(r0, 2 * kGK);
   __syncthreads();
-#pragma unroll 1
+#pragma unroll
   for (int st = 0; st < nch; st += 2) {
     // chunk st in buffer 0, st+1 in r1, st+2 in r0
     multiply(0);
@@ -482,8 +491,9 @@ __global__ __launch_bounds__(256, 2) void gptq_trail_kernel(GptqPlan p, int c0, 
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          *reinterpret_cast<float4*>(wrow[b] + 32 * a + 8 * q) = make_float4(
-              -acc[a][b][4 * q], -acc[a][b][4 * q + 1], -acc[a][b][4 * q + 2], -acc[a][b][4 * q + 3]);
+          *reinterpret_cast<float4*>(wrow[b] + 32 * a + 8 * q) =
+              make_float4(wv[a][b][4 * q] - acc[a][b][4 * q], wv[a][b][4 * q + 1] - acc[a][b][4 * q + 1],
+                          wv[a][b][4 * q + 2] - acc[a][b][4 * q + 2], wv[a][b][4 * q + 3] - acc[a][b][4 * q + 3]);
   }
 }
 

@@ -118,7 +118,8 @@ CLHA_API size_t clha_collect_workspace_bytes(const clha_ctx* ctx);
  *   workspace device, >= clha_collect_workspace_bytes(ctx) bytes.
  * Non-finite logits latch CLHA_ERR_NONFINITE (routing of that token is then undefined).
  * Errors: INVALID_ARG (unregistered layer, null x/logits), SHAPE (n_tokens outside
- * 0..max_tokens), ALIGN, WORKSPACE.  n_tokens == 0 enqueues nothing. */
+ * 0..max_tokens), ALIGN, WORKSPACE.  n_tokens == 0 enqueues nothing and reads none of
+ * the pointers (they may be NULL). */
 CLHA_API clha_status clha_collect_hessians(clha_ctx* ctx, int32_t layer, int64_t n_tokens,
                                            const uint16_t* x, const float* logits,
                                            int32_t* topk_out, int64_t* offsets_out,

@@ -46,6 +46,8 @@ ROUTE_CASES = [
     dict(wid=1, n_tokens=3001, n_routed=64, top_k=6, n_shared=2),       # ragged, E=64, K=6
     dict(wid=1, n_tokens=2500, n_routed=128, top_k=8),                  # E=128, K=8
     dict(wid=1, n_tokens=777, n_routed=5, top_k=5),                     # K = E
+    dict(wid=1, n_tokens=1500, n_routed=256, top_k=16),                 # largest E and K
+    dict(wid=1, n_tokens=300, n_routed=1, top_k=1),                     # one expert
 ]
 
 
