@@ -88,36 +88,64 @@ __global__ __launch_bounds__(256) void aggregate_kernel(AggArgs g, float* __rest
   const float ftotal = (float)total;
   float* Hs = H + (int64_t)slot * d * d;
   const int64_t soff = (int64_t)slot * d * d;
-  for (int idx = threadIdx.x; idx < 64 * 64; idx += 256) {
-    const int r = idx >> 6, c = idx & 63;
+  // four consecutive columns per thread (16-byte loads and stores)
+  for (int idx = threadIdx.x; idx < 64 * 16; idx += 256) {
+    const int r = idx >> 4, c = 4 * (idx & 15);
     if (diag && c > r) continue;
     const int i = ti * 64 + r, j = tj * 64 + c;
     const int64_t e = (int64_t)i * d + j;
-    float v;
+    float v[4];
     if (w.identity) {
-      v = (i == j) ? 1.0f : 0.0f;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = (i == j + u) ? 1.0f : 0.0f;
     } else if (w.rt) {
-      float sum = 0.0f;
-      for (int l = 0; l < g.n_layers; ++l) sum = __fadd_rn(sum, g.S[l][soff + e]);
-      v = __fdiv_rn(sum, ftotal);
+      float sum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      for (int l = 0; l < g.n_layers; ++l) {
+        const float4 x = *reinterpret_cast<const float4*>(g.S[l] + soff + e);
+        sum[0] = __fadd_rn(sum[0], x.x);
+        sum[1] = __fadd_rn(sum[1], x.y);
+        sum[2] = __fadd_rn(sum[2], x.z);
+        sum[3] = __fadd_rn(sum[3], x.w);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = __fdiv_rn(sum[u], ftotal);
     } else {
-      float acc = 0.0f;
+      float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
       for (int l = 0; l < g.n_layers; ++l) {
         if (w.a[l] != 0.0f && n[l] > 0) {
-          const float h = __fdiv_rn(g.S[l][soff + e], (float)n[l]);
-          acc = __fadd_rn(acc, __fmul_rn(w.a[l], h));
+          const float4 x = *reinterpret_cast<const float4*>(g.S[l] + soff + e);
+          const float xs[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+          for (int u = 0; u < 4; ++u) acc[u] = __fadd_rn(acc[u], __fmul_rn(w.a[l], __fdiv_rn(xs[u], (float)n[l])));
         }
       }
-      v = acc;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = acc[u];
     }
-    T[r][c] = v;
-    Hs[e] = v;
+    // on a diagonal tile, columns past the row are above the diagonal: S is not
+    // written there, so those values come from the mirror write below instead
+#pragma unroll
+    for (int u = 0; u < 4; ++u) T[r][c + u] = v[u];
+    if (!diag || c + 3 <= r) {
+      *reinterpret_cast<float4*>(Hs + e) = make_float4(v[0], v[1], v[2], v[3]);
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (c + u <= r) Hs[e + u] = v[u];
+    }
   }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < 64 * 64; idx += 256) {
-    const int r = idx >> 6, c = idx & 63;   // writes row tj*64 + r, column ti*64 + c
-    if (diag && c <= r) continue;
-    Hs[(int64_t)(tj * 64 + r) * d + ti * 64 + c] = T[c][r];
+  for (int idx = threadIdx.x; idx < 64 * 16; idx += 256) {
+    const int r = idx >> 4, c = 4 * (idx & 15);   // writes row tj*64 + r, columns ti*64 + c ..
+    if (diag && c + 3 <= r) continue;
+    float* o = Hs + (int64_t)(tj * 64 + r) * d + ti * 64 + c;
+    if (!diag) {
+      *reinterpret_cast<float4*>(o) = make_float4(T[c][r], T[c + 1][r], T[c + 2][r], T[c + 3][r]);
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (c + u > r) o[u] = T[c + u][r];
+    }
   }
 }
 
