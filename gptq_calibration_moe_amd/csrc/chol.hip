@@ -401,55 +401,65 @@ __global__ __launch_bounds__(256, 2) void trtri_merge_kernel(const double* __res
 
   // MFMA A operand rows (tile row i):  phase 0 L21[r0+i][k] (fp64), phase 1 X22[r0+i][k]
   // MFMA B operand rows (tile column j): phase 0 X11^T[c0+j][k] = XT32, phase 1 T^T[c0+j][k] = X32
+  // A fetch only issues loads (raw values in registers); conversion and the
+  // triangular masks happen when the stage is written to LDS, so a prefetch
+  // is never waited for before its turn.
   struct Stage {
+    double2 alo[4], ahi[4];   // phase 0: fp64 A operand
     float4 a[4], b[4];
   };
-  // thread t moves 16-byte chunks q = t + 256u: row q/8, k = 4(q%8) .. +3
+  // thread t moves 16-byte chunks q = t + 256u: row q/8, k = 4(q%8) .. +3.
+  // Every fetch is unconditional (chunk and row indices are clamped into
+  // range), so the compiler counts outstanding loads exactly; clamped rows
+  // (past nr or nc) only feed waves that are inactive for this tile.
+  auto chunk_base = [&](int ch) {
+    ch = ch < nch ? ch : nch - 1;
+    return PHASE == 0 ? k1 - (ch + 1) * kTK : k0 + ch * kTK;
+  };
   auto fetch = [&](Stage& rg, int ch) {
-    const int kb = PHASE == 0 ? k1 - (ch + 1) * kTK : k0 + ch * kTK;
+    const int kb = chunk_base(ch);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int q = tid + 256 * u, row = q >> 3, kk = kb + 4 * (q & 7);
-      float4 va = make_float4(0.f, 0.f, 0.f, 0.f), vb = va;
-      if (row < nr) {
-        if (PHASE == 0) {
-          const double* src = A + (int64_t)(r0 + row) * c + kk;
-          const double2 lo = *reinterpret_cast<const double2*>(src);
-          const double2 hi = *reinterpret_cast<const double2*>(src + 2);
-          va = make_float4((float)lo.x, (float)lo.y, (float)hi.x, (float)hi.y);
-        } else {   // X22 lower triangular: k <= row
-          va = *reinterpret_cast<const float4*>(X32 + (int64_t)(r0 + row) * c + kk);
-          const int rr = r0 + row;
-          if (kk > rr) va.x = 0.f;
-          if (kk + 1 > rr) va.y = 0.f;
-          if (kk + 2 > rr) va.z = 0.f;
-          if (kk + 3 > rr) va.w = 0.f;
-        }
+      const int ra = min(row, nr - 1), rb = min(row, nc - 1);
+      if (PHASE == 0) {
+        const double* src = A + (int64_t)(r0 + ra) * c + kk;
+        rg.alo[u] = *reinterpret_cast<const double2*>(src);
+        rg.ahi[u] = *reinterpret_cast<const double2*>(src + 2);
+        rg.b[u] = *reinterpret_cast<const float4*>(XT32 + (int64_t)(c0 + rb) * c + kk);
+      } else {
+        rg.a[u] = *reinterpret_cast<const float4*>(X32 + (int64_t)(r0 + ra) * c + kk);
+        rg.b[u] = *reinterpret_cast<const float4*>(X32 + (int64_t)(c0 + rb) * c + kk);
       }
-      if (row < nc) {
-        const int cc = c0 + row;
-        if (PHASE == 0) {   // X11^T row cc: X11[k][cc] is nonzero for k >= cc
-          vb = *reinterpret_cast<const float4*>(XT32 + (int64_t)cc * c + kk);
-          if (kk < cc) vb.x = 0.f;
-          if (kk + 1 < cc) vb.y = 0.f;
-          if (kk + 2 < cc) vb.z = 0.f;
-          if (kk + 3 < cc) vb.w = 0.f;
-        } else {
-          vb = *reinterpret_cast<const float4*>(X32 + (int64_t)cc * c + kk);
-        }
-      }
-      rg.a[u] = va;
-      rg.b[u] = vb;
     }
   };
-  auto stage = [&](const Stage& rg, int buf) {
+  auto stage = [&](const Stage& rg, int buf, int ch) {
+    const int kb = chunk_base(ch);
     float* As = lds + (2 * buf) * kTBuf;
     float* Bs = lds + (2 * buf + 1) * kTBuf;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int q = tid + 256 * u, row = q >> 3, kc = 4 * (q & 7);
-      *reinterpret_cast<float4*>(As + row * kTP + kc) = rg.a[u];
-      *reinterpret_cast<float4*>(Bs + row * kTP + kc) = rg.b[u];
+      const int q = tid + 256 * u, row = q >> 3, kc = 4 * (q & 7), kk = kb + kc;
+      float4 va, vb = rg.b[u];
+      if (PHASE == 0) {
+        va = make_float4((float)rg.alo[u].x, (float)rg.alo[u].y, (float)rg.ahi[u].x, (float)rg.ahi[u].y);
+        // X11^T row cc: X11[k][cc] is nonzero for k >= cc
+        const int cc = c0 + min(row, nc - 1);
+        vb.x = kk < cc ? 0.f : vb.x;
+        vb.y = kk + 1 < cc ? 0.f : vb.y;
+        vb.z = kk + 2 < cc ? 0.f : vb.z;
+        vb.w = kk + 3 < cc ? 0.f : vb.w;
+      } else {
+        // X22 lower triangular: k <= row
+        va = rg.a[u];
+        const int rr = r0 + min(row, nr - 1);
+        va.x = kk > rr ? 0.f : va.x;
+        va.y = kk + 1 > rr ? 0.f : va.y;
+        va.z = kk + 2 > rr ? 0.f : va.z;
+        va.w = kk + 3 > rr ? 0.f : va.w;
+      }
+      *reinterpret_cast<float4*>(As + row * kTP + kc) = va;
+      *reinterpret_cast<float4*>(Bs + row * kTP + kc) = vb;
     }
   };
   f32x16 acc[2][2];
@@ -481,19 +491,19 @@ __global__ __launch_bounds__(256, 2) void trtri_merge_kernel(const double* __res
 
   Stage g0, g1;
   fetch(g0, 0);
-  stage(g0, 0);
+  stage(g0, 0, 0);
   fetch(g1, 1);
-  if (nch > 2) fetch(g0, 2);
+  fetch(g0, 2);
   __syncthreads();
 #pragma unroll 1
   for (int st = 0; st < nch; st += 2) {
     multiply(0);
-    stage(g1, 1);
-    if (st + 3 < nch) fetch(g1, st + 3);
+    stage(g1, 1, st + 1);
+    fetch(g1, st + 3);
     __syncthreads();
     multiply(1);
-    if (st + 2 < nch) stage(g0, 0);
-    if (st + 4 < nch) fetch(g0, st + 4);
+    stage(g0, 0, st + 2);
+    fetch(g0, st + 4);
     __syncthreads();
   }
   if (!active) return;
