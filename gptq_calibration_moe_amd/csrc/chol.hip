@@ -26,8 +26,8 @@
 //   left-looking Cholesky, per 64-column block step k:
 //     chol_left     T_i = A[i][k] - sum_{m<k} L[i][m] L[k][m]^T for block rows i >= k
 //                   (a chunked fp64 MFMA product, next chunk prefetched)
-//     chol_diag     L_kk = chol(T_k) and its inverse Dinv_k (one wavefront per matrix,
-//                   rows in registers)
+//     chol_diag     L_kk = chol(T_k) and its inverse Dinv_k (two wavefronts per matrix:
+//                   one factors, one inverts, sharing each column through LDS)
 //     chol_panel    L[i][k] = T_i Dinv_k^T for i > k
 //   triangular inverse X = L^-1, merged bottom-up over block ranges in fp32:
 //     trtri_leaf    X[i][i] = Dinv_i
@@ -211,10 +211,15 @@ __global__ __launch_bounds__(256) void chol_left_kernel(double* __restrict__ Aal
       }
 }
 
-// Step k: L_kk = chol(T_k) and Dinv_k = L_kk^-1, one wavefront per matrix.
-// Lane r holds row r of the 64x64 block in registers; a pivot or a column
-// value is broadcast with readlane, so no step needs a barrier.  The template
-// recursion keeps every register index a compile-time constant.
+// Step k: L_kk = chol(T_k) and Dinv_k = L_kk^-1, one workgroup of two
+// wavefronts per matrix.  Wave 0 factors (lane r holds row r of T_k); wave 1
+// inverts (lane r holds column r of X = L_kk^-1, eliminated forward on
+// L X = I, starting from the identity).  At step J wave 0 finishes column J of
+// L and puts it in LDS with 1 / L_JJ; then both waves apply the same rank-one
+// update with that column, read as broadcasts: wave 0 to the later columns of
+// its row, wave 1 to the rows of its column below J once X_Jr is final.  The
+// column is double-buffered, so one barrier per step orders everything.  The
+// template recursion keeps every register index a compile-time constant.
 __device__ __forceinline__ double lane_value(double v, int src) {
   const uint64_t b = __double_as_longlong(v);
   const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)b, src);
@@ -222,63 +227,62 @@ __device__ __forceinline__ double lane_value(double v, int src) {
   return __longlong_as_double(((uint64_t)hi << 32) | lo);
 }
 
-// Cholesky column J: a[] is this lane's row of the block being factored.
 template <int J>
-__device__ __forceinline__ void chol_cols(double (&a)[kNb], double (&piv)[kNb], int r, bool& bad) {
-  double d = lane_value(a[J], J);
-  if (!(d > 0.0)) {
-    bad = true;
-    d = 1.0;
+__device__ __forceinline__ void diag_step(double (&v)[kNb], int r, bool factor, bool& bad,
+                                          double (*col)[kNb + 2]) {
+  double* cj = col[J & 1];
+  if (factor) {
+    double d = lane_value(v[J], J);
+    if (!(d > 0.0)) {
+      bad = true;
+      d = 1.0;
+    }
+    const double ljj = sqrt(d);
+    if (r == J) v[J] = ljj;
+    if (r > J) v[J] = v[J] / ljj;
+    cj[r] = v[J];
+    if (r == 0) cj[kNb] = 1.0 / ljj;
   }
-  const double ljj = sqrt(d);
-  piv[J] = ljj;
-  if (r == J) a[J] = ljj;
-  if (r > J) a[J] = a[J] / ljj;
+  __syncthreads();
+  if (!factor) v[J] *= cj[kNb];   // X_Jr is final (zero for r > J)
+  // rows above J of the factoring wave hold nothing of L: leave them alone
+  const double mult = (factor && r <= J) ? 0.0 : v[J];
 #pragma unroll
-  for (int cc = J + 1; cc < kNb; ++cc) a[cc] = fma(-a[J], lane_value(a[J], cc), a[cc]);
-  if constexpr (J + 1 < kNb) chol_cols<J + 1>(a, piv, r, bad);
+  for (int cc = J + 1; cc < kNb; ++cc) v[cc] = fma(-mult, cj[cc], v[cc]);
+  if constexpr (J + 1 < kNb) diag_step<J + 1>(v, r, factor, bad, col);
 }
 
-// Forward elimination on L X = I, pivot row J: x[] is this lane's row of X.
-template <int J>
-__device__ __forceinline__ void inv_rows(const double (&a)[kNb], const double (&piv)[kNb],
-                                         double (&x)[kNb], int r) {
-  const double inv = 1.0 / piv[J];
-  if (r == J) {
-#pragma unroll
-    for (int cc = 0; cc <= J; ++cc) x[cc] *= inv;
-  }
-#pragma unroll
-  for (int cc = 0; cc <= J; ++cc) {
-    const double xj = lane_value(x[cc], J);
-    if (r > J) x[cc] = fma(-a[J], xj, x[cc]);
-  }
-  if constexpr (J + 1 < kNb) inv_rows<J + 1>(a, piv, x, r);
-}
-
-__global__ __launch_bounds__(64) void chol_diag_kernel(const double* __restrict__ Aall, int c, int k,
-                                                       double* __restrict__ dinv,
-                                                       int* __restrict__ status) {
-  const int m = blockIdx.x, r = threadIdx.x;
+__global__ __launch_bounds__(128) void chol_diag_kernel(const double* __restrict__ Aall, int c, int k,
+                                                        double* __restrict__ dinv,
+                                                        int* __restrict__ status) {
+  __shared__ __align__(16) double col[2][kNb + 2];
+  const int m = blockIdx.x, r = threadIdx.x & 63;
+  const bool factor = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) == 0;
   const double* A = Aall + (int64_t)m * c * c;
   const int64_t k0 = (int64_t)k * kNb;
-  double a[kNb], x[kNb], piv[kNb];
-  const double* row = A + (k0 + r) * c + k0;
+  double v[kNb];
+  if (factor) {
+    const double* row = A + (k0 + r) * c + k0;
 #pragma unroll
-  for (int cc = 0; cc < kNb; cc += 2) {
-    const double2 v = *reinterpret_cast<const double2*>(row + cc);
-    a[cc] = cc <= r ? v.x : 0.0;
-    a[cc + 1] = cc + 1 <= r ? v.y : 0.0;
+    for (int cc = 0; cc < kNb; cc += 2) {
+      const double2 t = *reinterpret_cast<const double2*>(row + cc);
+      v[cc] = cc <= r ? t.x : 0.0;
+      v[cc + 1] = cc + 1 <= r ? t.y : 0.0;
+    }
+  } else {
+#pragma unroll
+    for (int cc = 0; cc < kNb; ++cc) v[cc] = cc == r ? 1.0 : 0.0;
   }
   bool bad = false;
-  chol_cols<0>(a, piv, r, bad);
-  if (bad && r == 0) atomicOr(status, kStatusNotPd);
+  diag_step<0>(v, r, factor, bad, col);
+  if (factor) {
+    if (bad && r == 0) atomicOr(status, kStatusNotPd);
+  } else {
+    // Dinv_k row-major: lane r writes column r, each store one coalesced row
+    double* D = dinv + ((int64_t)m * (c / kNb) + k) * kNb * kNb + r;
 #pragma unroll
-  for (int cc = 0; cc < kNb; ++cc) x[cc] = cc == r ? 1.0 : 0.0;
-  inv_rows<0>(a, piv, x, r);
-  double* D = dinv + ((int64_t)m * (c / kNb) + k) * kNb * kNb + (int64_t)r * kNb;
-#pragma unroll
-  for (int cc = 0; cc < kNb; cc += 2) *reinterpret_cast<double2*>(D + cc) = make_double2(x[cc], x[cc + 1]);
+    for (int kk = 0; kk < kNb; ++kk) D[kk * kNb] = v[kk];
+  }
 }
 
 // Step k, block row i > k:  L[i][k] = T_i Dinv_k^T.
@@ -563,7 +567,7 @@ void launch_factor_group(const GptqPlan& p, int m0, int m1, hipStream_t s, hipEv
                      lamd, A);
   for (int k = 0; k < nbk; ++k) {
     hipLaunchKernelGGL(chol_left_kernel, dim3(nbk - k, n), dim3(256), 0, s, A, c, k);
-    hipLaunchKernelGGL(chol_diag_kernel, dim3(n), dim3(64), 0, s, A, c, k, dinv, p.status);
+    hipLaunchKernelGGL(chol_diag_kernel, dim3(n), dim3(128), 0, s, A, c, k, dinv, p.status);
     if (k == 0 && step0_done) hipEventRecord(step0_done, s);
     if (k + 1 < nbk)
       hipLaunchKernelGGL(chol_panel_kernel, dim3(nbk - k - 1, n), dim3(256), 0, s, A, c, k, dinv);
