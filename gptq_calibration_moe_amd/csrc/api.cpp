@@ -217,6 +217,7 @@ struct GptqLayout {
   double* dinv;
   uint8_t* dead;
   double* lamd;
+  int* lexp;
   float* wf;
   float* ebuf;
   double* partials;
@@ -236,6 +237,7 @@ GptqLayout gptq_layout(void* ws, int n_jobs, int n_mats, int cols, int64_t wf_el
   L.dinv = c.take<double>((size_t)n_mats * cols * clha::kNb);
   L.dead = c.take<uint8_t>((size_t)n_mats * cols);
   L.lamd = c.take<double>((size_t)n_mats);
+  L.lexp = c.take<int>((size_t)n_mats * cols);
   L.wf = need_wf ? c.take<float>((size_t)wf_elems) : nullptr;
   L.ebuf = need_wf && cols > clha::kSuper ? c.take<float>((size_t)(wf_elems / cols) * clha::kSuper) : nullptr;
   L.partials = need_wf ? c.take<double>((size_t)2 * (total_slabs > 0 ? total_slabs : 1)) : nullptr;
@@ -626,6 +628,7 @@ CLHA_API clha_status clha_gptq_quantize(clha_ctx* ctx, int32_t n_jobs, const clh
   p.dinv = L.dinv;
   p.dead = L.dead;
   p.lamd = L.lamd;
+  p.lexp = L.lexp;
   p.lam = nullptr;
   p.wf = L.wf;
   p.ebuf = L.ebuf;
@@ -678,6 +681,7 @@ CLHA_API clha_status clha_inverse_cholesky(clha_ctx* ctx, int32_t n, const float
   p.dinv = L.dinv;
   p.dead = dead_out ? dead_out : L.dead;
   p.lamd = L.lamd;
+  p.lexp = L.lexp;
   p.lam = lambda_out;
   p.status = ctx->status_dev;
   {

@@ -11,11 +11,13 @@
 // R = J L J upper triangular, Hd^-1 = R^-T R^-1, and U = R^-1 = J L^-1 J.
 // Cost: c^3/3 flops for the factorisation and c^3/3 for the triangular inverse.
 //
-// Precision: the factorisation runs in fp64 (v_mfma_f64_16x16x4f64).  A
-// right-looking fp32 factorisation rounds each diagonal entry once per block
-// step while it shrinks from H_jj to its Schur complement, which costs about a
-// decimal digit on ill-conditioned Hessians; GPTQ's code decisions inherit that
-// error.  The triangular inverse then runs in fp32 (v_mfma_f32_32x32x2f32,
+// Precision: the factorisation keeps fp64 values.  A right-looking fp32
+// factorisation rounds each diagonal entry once per block step while it
+// shrinks from H_jj to its Schur complement, which costs about a decimal digit
+// on ill-conditioned Hessians; GPTQ's code decisions inherit that error.  Its
+// long products (the left-looking updates) run exactly on the int8 matrix
+// cores over 42-bit digit expansions of L (see "sliced factor" below): about
+// five times the sustained fp64 matrix rate, within 2^-36 of the fp64 product.  The triangular inverse then runs in fp32 (v_mfma_f32_32x32x2f32,
 // about four times the sustained fp64 matrix rate): its error is governed by
 // cond(L) = sqrt(cond(Hd)), and it moves U by a few fp32 ulps.
 //
@@ -25,10 +27,10 @@
 //   build_reversed  A = J (H + fixes + lambda I) J, lower triangle, fp64
 //   left-looking Cholesky, per 64-column block step k:
 //     chol_left     T_i = A[i][k] - sum_{m<k} L[i][m] L[k][m]^T for block rows i >= k
-//                   (a chunked fp64 MFMA product, next chunk prefetched)
+//                   (int8 digit-pair products accumulated exactly, next chunk prefetched)
 //     chol_diag     L_kk = chol(T_k) and its inverse Dinv_k (two wavefronts per matrix:
 //                   one factors, one inverts, sharing each column through LDS)
-//     chol_panel    L[i][k] = T_i Dinv_k^T for i > k
+//     chol_panel    L[i][k] = T_i Dinv_k^T for i > k, and its digit planes
 //   triangular inverse X = L^-1, merged bottom-up over block ranges in fp32:
 //     trtri_leaf    X[i][i] = Dinv_i
 //     trtri_merge   X21 = -X22 L21 X11 per merge (two batched GEMMs per level),
@@ -128,7 +130,8 @@ __global__ __launch_bounds__(256) void diag_stats_kernel(const float* const* __r
 __global__ __launch_bounds__(256) void build_reversed_kernel(const float* const* __restrict__ mats,
                                                              int c, const uint8_t* __restrict__ dead,
                                                              const double* __restrict__ lamd,
-                                                             double* __restrict__ Aall) {
+                                                             double* __restrict__ Aall,
+                                                             int* __restrict__ lexp) {
   const int m = blockIdx.y;
   int bi, bj;
   tri_of(blockIdx.x, bi, bj);
@@ -141,74 +144,126 @@ __global__ __launch_bounds__(256) void build_reversed_kernel(const float* const*
     if (j > i) continue;
     const int hi = c - 1 - i, hj = c - 1 - j;
     double v = (double)H[(int64_t)hi * c + hj];
-    if (i == j) v = (dead[(int64_t)m * c + hi] ? 1.0 : v) + l;
+    if (i == j) {
+      v = (dead[(int64_t)m * c + hi] ? 1.0 : v) + l;
+      // every entry of row i of the factor is at most sqrt(A_ii) in magnitude:
+      // 2^e >= sqrt(A_ii) (1 + 1/64) scales the row's digits, so that a scaled
+      // entry times 128 stays within 126.1 and its first digit fits int8
+      int e = 0;
+      if (v > 0.0) frexp(sqrt(v) * (1.0 + 1.0 / 64.0), &e);
+      lexp[(int64_t)m * c + i] = e;
+    }
     A[(int64_t)i * c + j] = v;
   }
 }
 
-// ---------------------------------------------------------------- chunked 64x64 products
-// Sum over chunks m of P_m Q_m (64x64 fp64 blocks read from global memory):
-// each thread prefetches its 16+16 elements of the next chunk into registers
-// while the matrix cores work on the current chunk in LDS.
-struct ChunkPipe {
-  double ra[16], rb[16];
-  __device__ __forceinline__ void fetch(const double* P, int64_t ldp, const double* Q, int64_t ldq) {
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int idx = threadIdx.x + 256 * u, r = idx >> 6, cc = idx & 63;
-      ra[u] = P[r * ldp + cc];
-      rb[u] = Q[r * ldq + cc];
-    }
-  }
-  __device__ __forceinline__ void stage(double (*As)[kNb + 1], double (*Bs)[kNb + 1]) {
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int idx = threadIdx.x + 256 * u, r = idx >> 6, cc = idx & 63;
-      As[r][cc] = ra[u];
-      Bs[r][cc] = rb[u];
-    }
-  }
-};
+// ---------------------------------------------------------------- sliced factor
+// The off-diagonal blocks of L are also kept as kSlices signed 7-bit digit
+// planes, so that the left-looking products run exactly on the int8 matrix
+// cores (the splitting scheme of Ozaki, Ogita, Oishi and Rump, Numerical
+// Algorithms 2012, with integer slices): row i has a power-of-two scale 2^e_i
+// bounding its entries, and
+//   L_im ~ 2^e_i * sum_p d_p(i,m) 2^-7(p+1),   |d_0| <= 126, |d_p| <= 64 after,
+// a base-128 expansion of L_im 2^-e_i whose digits are each rounded to the
+// nearest integer (so the dropped remainder is at most half the last digit's
+// weight and carries no bias across a long sum).  A product sum_m L_im L_jm is
+// then a sum over digit pairs (p, q) of integer dot products, exact in int32,
+// weighted by 2^(e_i + e_j - 7(p + q + 2)).  Pairs with p + q >= kSlices are
+// dropped: their weight is below the expansion's own remainder.  With
+// kSlices = 6 each entry carries 42 bits relative to its row bound; products
+// over 2048 terms come out within about 2^-35 sqrt(A_ii A_jj), against 2^-24
+// for an fp32 product and far below the fp32 precision of everything
+// downstream of the factor.
+//
+// Storage: per Hessian, tile (I, K) of 64x64 is kSlices contiguous 4 KB
+// planes, row-major, at ((I * nbk + K) * kSlices) * 4096 bytes; the planes
+// occupy the inverse's buffer (8 c^2 bytes per Hessian), which is free until
+// the factorisation has finished.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+constexpr int kLqTile = kSlices * kNb * kNb;   // bytes of one sliced 64x64 tile
+constexpr int kLqPitch = 80;                    // LDS row pitch (bytes): conflict-free 16-byte reads
+
+__device__ __forceinline__ int64_t lq_offset(int c, int m, int I, int K) {
+  return (int64_t)m * c * c * 8 + ((int64_t)I * (c / kNb) + K) * kLqTile;
+}
 
 // ---------------------------------------------------------------- left-looking Cholesky
 // Step k, block row i >= k:  T_i = A[i][k] - sum_{m<k} L[i][m] L[k][m]^T, stored over A[i][k].
-__global__ __launch_bounds__(256) void chol_left_kernel(double* __restrict__ Aall, int c, int k) {
-  __shared__ double As[kNb][kNb + 1];
-  __shared__ double Bs[kNb][kNb + 1];
+// Four waves each own a 32x32 quarter (v_mfma_i32_32x32x32_i8: lane l holds
+// row l%32, bytes 16(l/32)..+15 of each 32-byte K step; result row
+// 8(r/4) + 4(l/32) + r%4, column l%32).  The digit planes of chunk m+1 are
+// fetched into registers while the matrix cores work on chunk m in LDS.
+__global__ __launch_bounds__(256, 2) void chol_left_kernel(double* __restrict__ Aall,
+                                                           const int8_t* __restrict__ Lq,
+                                                           const int* __restrict__ lexp, int c, int k) {
+  __shared__ __align__(16) int8_t As[kSlices][kNb][kLqPitch];
+  __shared__ __align__(16) int8_t Bs[kSlices][kNb][kLqPitch];
   const int m = blockIdx.y, i = k + blockIdx.x;
   const bool diag = i == k;
   double* A = Aall + (int64_t)m * c * c;
   const int64_t i0 = (int64_t)i * kNb, k0 = (int64_t)k * kNb;
-  Tile64 t;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  i32x16 acc[kSlices];
 #pragma unroll
-  for (int x = 0; x < 2; ++x)
-#pragma unroll
-    for (int y = 0; y < 2; ++y)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = Tile64::row(x, r), col = Tile64::col(y);
-        t.acc[x][y][r] = (!diag || col <= row) ? A[(i0 + row) * c + k0 + col] : 0.0;
-      }
+  for (int w = 0; w < kSlices; ++w) acc[w] = i32x16{};
   if (k > 0) {
-    ChunkPipe pipe;
-    pipe.fetch(A + i0 * c, c, A + k0 * c, c);
+    const int8_t* Pa = Lq + lq_offset(c, m, i, 0) + 16 * threadIdx.x;
+    const int8_t* Pb = Lq + lq_offset(c, m, k, 0) + 16 * threadIdx.x;
+    const int pr = threadIdx.x >> 2, pc = 16 * (threadIdx.x & 3);   // this thread's piece of a plane
+    const int fa = 32 * wm + (lane & 31), fb = 32 * wn + (lane & 31), fk = 16 * (lane >> 5);
+    i32x4 ra[kSlices], rb[kSlices];
+#pragma unroll
+    for (int p = 0; p < kSlices; ++p) {
+      ra[p] = *reinterpret_cast<const i32x4*>(Pa + p * kNb * kNb);
+      rb[p] = *reinterpret_cast<const i32x4*>(Pb + p * kNb * kNb);
+    }
     for (int mm = 0; mm < k; ++mm) {
       __syncthreads();
-      pipe.stage(As, Bs);
+#pragma unroll
+      for (int p = 0; p < kSlices; ++p) {
+        *reinterpret_cast<i32x4*>(&As[p][pr][pc]) = ra[p];
+        *reinterpret_cast<i32x4*>(&Bs[p][pr][pc]) = rb[p];
+      }
       __syncthreads();
-      if (mm + 1 < k) pipe.fetch(A + i0 * c + (mm + 1) * kNb, c, A + k0 * c + (mm + 1) * kNb, c);
-      t.mac<true>(As, Bs, -1.0);
+      // next chunk (the last one again at the end: no conditional load)
+      const int64_t nx = (int64_t)min(mm + 1, k - 1) * kLqTile;
+#pragma unroll
+      for (int p = 0; p < kSlices; ++p) {
+        ra[p] = *reinterpret_cast<const i32x4*>(Pa + nx + p * kNb * kNb);
+        rb[p] = *reinterpret_cast<const i32x4*>(Pb + nx + p * kNb * kNb);
+      }
+      i32x4 a[kSlices][2], b[kSlices][2];
+#pragma unroll
+      for (int p = 0; p < kSlices; ++p)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          a[p][h] = *reinterpret_cast<const i32x4*>(&As[p][fa][fk + 32 * h]);
+          b[p][h] = *reinterpret_cast<const i32x4*>(&Bs[p][fb][fk + 32 * h]);
+        }
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int p = 0; p < kSlices; ++p)
+#pragma unroll
+          for (int q = 0; q + p < kSlices; ++q)
+            acc[p + q] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[p][h], b[q][h], acc[p + q], 0, 0, 0);
     }
   }
+  const int* ex = lexp + (int64_t)m * c;
+  const int col = 32 * wn + (lane & 31);
+  const int ecol = ex[k0 + col];
 #pragma unroll
-  for (int x = 0; x < 2; ++x)
+  for (int r = 0; r < 16; ++r) {
+    const int row = 32 * wm + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+    if (diag && col > row) continue;
+    double sum = 0.0;
 #pragma unroll
-    for (int y = 0; y < 2; ++y)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = Tile64::row(x, r), col = Tile64::col(y);
-        if (!diag || col <= row) A[(i0 + row) * c + k0 + col] = t.acc[x][y][r];
-      }
+    for (int w = kSlices - 1; w >= 0; --w) sum += ldexp((double)acc[w][r], -7 * (w + 2));
+    double* t = A + (i0 + row) * c + k0 + col;
+    *t = *t - ldexp(sum, ex[i0 + row] + ecol);
+  }
 }
 
 // Step k: L_kk = chol(T_k) and Dinv_k = L_kk^-1, one workgroup of two
@@ -287,7 +342,9 @@ __global__ __launch_bounds__(128) void chol_diag_kernel(const double* __restrict
 
 // Step k, block row i > k:  L[i][k] = T_i Dinv_k^T.
 __global__ __launch_bounds__(256) void chol_panel_kernel(double* __restrict__ Aall, int c, int k,
-                                                         const double* __restrict__ dinv) {
+                                                         const double* __restrict__ dinv,
+                                                         int8_t* __restrict__ Lq,
+                                                         const int* __restrict__ lexp) {
   __shared__ double Ts[kNb][kNb + 1];
   __shared__ double Ds[kNb][kNb + 1];
   const int m = blockIdx.y, i = k + 1 + blockIdx.x;
@@ -310,6 +367,40 @@ __global__ __launch_bounds__(256) void chol_panel_kernel(double* __restrict__ Aa
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         A[(i0 + Tile64::row(x, r)) * c + k0 + Tile64::col(y)] = t.acc[x][y][r];
+  // digit planes of the tile: thread t writes 16 consecutive entries of row t/4
+  __syncthreads();
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Ts[Tile64::row(x, r)][Tile64::col(y)] = t.acc[x][y][r];
+  __syncthreads();
+  const int pr = threadIdx.x >> 2, pc = 16 * (threadIdx.x & 3);
+  const int e = lexp[(int64_t)m * c + i0 + pr];
+  uint32_t packed[kSlices][4];
+#pragma unroll
+  for (int p = 0; p < kSlices; ++p)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) packed[p][u] = 0;
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    // |x| <= 0.985, so the first digit is at most 126 and each later one, a
+    // rounded remainder times 128, at most 64; the clamp only guards a factor
+    // that has already failed (status not positive definite)
+    double x = fmin(fmax(ldexp(Ts[pr][pc + u], -e), -0.984375), 0.984375);
+#pragma unroll
+    for (int p = 0; p < kSlices; ++p) {
+      x *= 128.0;
+      const double d = rint(x);
+      x -= d;
+      packed[p][u >> 2] |= ((uint32_t)(int)d & 0xffu) << (8 * (u & 3));
+    }
+  }
+  int8_t* out = Lq + lq_offset(c, m, i, k) + 16 * threadIdx.x;
+#pragma unroll
+  for (int p = 0; p < kSlices; ++p)
+    *reinterpret_cast<uint4*>(out + p * kNb * kNb) = make_uint4(packed[p][0], packed[p][1], packed[p][2], packed[p][3]);
 }
 
 // ---------------------------------------------------------------- triangular inverse
@@ -563,14 +654,16 @@ void launch_factor_group(const GptqPlan& p, int m0, int m1, hipStream_t s, hipEv
   float* U = p.U + m0 * cc;
   float* UT = p.UT ? p.UT + m0 * cc : nullptr;
   hipLaunchKernelGGL(diag_stats_kernel, dim3(n), dim3(256), 0, s, mats, c, p.damp, dead, lamd, lam);
+  int* lexp = p.lexp + (int64_t)m0 * c;
+  int8_t* Lq = reinterpret_cast<int8_t*>(X);   // free until the inverse starts
   hipLaunchKernelGGL(build_reversed_kernel, dim3(nbk * (nbk + 1) / 2, n), dim3(256), 0, s, mats, c, dead,
-                     lamd, A);
+                     lamd, A, lexp);
   for (int k = 0; k < nbk; ++k) {
-    hipLaunchKernelGGL(chol_left_kernel, dim3(nbk - k, n), dim3(256), 0, s, A, c, k);
+    hipLaunchKernelGGL(chol_left_kernel, dim3(nbk - k, n), dim3(256), 0, s, A, Lq, lexp, c, k);
     hipLaunchKernelGGL(chol_diag_kernel, dim3(n), dim3(128), 0, s, A, c, k, dinv, p.status);
     if (k == 0 && step0_done) hipEventRecord(step0_done, s);
     if (k + 1 < nbk)
-      hipLaunchKernelGGL(chol_panel_kernel, dim3(nbk - k - 1, n), dim3(256), 0, s, A, c, k, dinv);
+      hipLaunchKernelGGL(chol_panel_kernel, dim3(nbk - k - 1, n), dim3(256), 0, s, A, c, k, dinv, Lq, lexp);
   }
   hipLaunchKernelGGL(trtri_leaf_kernel, dim3(nbk, n), dim3(256), 0, s, c, dinv, X, U, UT);
   for (int sz = 1; sz < nbk; sz *= 2) {

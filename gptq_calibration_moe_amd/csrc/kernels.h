@@ -28,6 +28,7 @@ constexpr int kGemmTile = 128;        // rows and columns of a trailing-update t
 // status word bits (device, latched; see clha_sync)
 constexpr int kStatusNonfinite = 1;
 constexpr int kStatusNotPd = 2;
+constexpr int kSlices = 6;            // signed 7-bit digits per sliced fp64 factor entry
 
 // ---------------------------------------------------------------- collection
 struct CollectPlan {
@@ -103,6 +104,7 @@ struct GptqPlan {
   double* dinv;              // device [n_mats][cols/kNb][kNb][kNb] inverses of L's diagonal blocks
   uint8_t* dead;             // device [n_mats][cols]
   double* lamd;              // device [n_mats] damping lambda
+  int* lexp;                 // device [n_mats][cols] row exponents of the sliced factor
   float* lam;                // device [n_mats] lambda as float (optional output, may be null)
   float* wf;                 // device fp32 working copies of all jobs' weights
   float* ebuf;               // device [padded rows][kSuper] a superblock's negated errors
