@@ -298,8 +298,10 @@ def main():
                       "routed_experts": wl.n_routed, "top_k": wl.top_k, "shared_experts": wl.n_shared,
                       "matrices": n_mats, "matrix_shape": [wl.rows, wl.d], "bits": wl.bits,
                       "shared_bits": wl.shared_bits, "group": wl.group, "alpha": wl.alpha,
-                      "precision": "Gram sums bf16 in / fp32 accumulate; factor of the inverse fp64; "
-                                   "GPTQ propagation fp32"},
+                      "precision": "Gram sums bf16 in / fp32 accumulate; Cholesky fp64 values, its "
+                                   "long products exact int8 digit products of 42-bit expansions; "
+                                   "triangular inverse fp32; GPTQ fp32, trailing products exact int8 "
+                                   "digit products of 28-bit expansions"},
            "roofline": roofline, "stages_ms_per_step": stages_ms}
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")

@@ -500,6 +500,8 @@ static clha_status run_factor(clha_ctx* ctx, const GptqPlan& p, hipStream_t s, c
     if (jobs) {
       clha::JobRange r{};
       r.j0 = j;
+      r.m0 = m0;
+      r.m1 = m1;
       while (j < p.n_jobs && jobs[j].mat < m1) ++j;
       r.j1 = j;
       if (r.j1 > r.j0) {

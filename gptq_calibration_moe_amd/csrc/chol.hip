@@ -192,8 +192,9 @@ __device__ __forceinline__ int64_t lq_offset(int c, int m, int I, int K) {
 // Step k, block row i >= k:  T_i = A[i][k] - sum_{m<k} L[i][m] L[k][m]^T, stored over A[i][k].
 // Four waves each own a 32x32 quarter (v_mfma_i32_32x32x32_i8: lane l holds
 // row l%32, bytes 16(l/32)..+15 of each 32-byte K step; result row
-// 8(r/4) + 4(l/32) + r%4, column l%32).  The digit planes of chunk m+1 are
-// fetched into registers while the matrix cores work on chunk m in LDS.
+// 8(r/4) + 4(l/32) + r%4, column l%32).  The digit planes of chunks m+1 and
+// m+2 are in flight in two register sets while the matrix cores work on chunk
+// m in LDS.
 __global__ __launch_bounds__(256, 2) void chol_left_kernel(double* __restrict__ Aall,
                                                            const int8_t* __restrict__ Lq,
                                                            const int* __restrict__ lexp, int c, int k) {
@@ -213,13 +214,18 @@ __global__ __launch_bounds__(256, 2) void chol_left_kernel(double* __restrict__ 
     const int8_t* Pb = Lq + lq_offset(c, m, k, 0) + 16 * threadIdx.x;
     const int pr = threadIdx.x >> 2, pc = 16 * (threadIdx.x & 3);   // this thread's piece of a plane
     const int fa = 32 * wm + (lane & 31), fb = 32 * wn + (lane & 31), fk = 16 * (lane >> 5);
-    i32x4 ra[kSlices], rb[kSlices];
+    i32x4 ra0[kSlices], rb0[kSlices], ra1[kSlices], rb1[kSlices];
+    auto load = [&](i32x4 (&ra)[kSlices], i32x4 (&rb)[kSlices], int ch) {
+      const int64_t nx = (int64_t)min(ch, k - 1) * kLqTile;
 #pragma unroll
-    for (int p = 0; p < kSlices; ++p) {
-      ra[p] = *reinterpret_cast<const i32x4*>(Pa + p * kNb * kNb);
-      rb[p] = *reinterpret_cast<const i32x4*>(Pb + p * kNb * kNb);
-    }
-    for (int mm = 0; mm < k; ++mm) {
+      for (int p = 0; p < kSlices; ++p) {
+        ra[p] = *reinterpret_cast<const i32x4*>(Pa + nx + p * kNb * kNb);
+        rb[p] = *reinterpret_cast<const i32x4*>(Pb + nx + p * kNb * kNb);
+      }
+    };
+    load(ra0, rb0, 0);
+    load(ra1, rb1, 1);
+    auto step = [&](i32x4 (&ra)[kSlices], i32x4 (&rb)[kSlices], int mm) {
       __syncthreads();
 #pragma unroll
       for (int p = 0; p < kSlices; ++p) {
@@ -227,13 +233,7 @@ __global__ __launch_bounds__(256, 2) void chol_left_kernel(double* __restrict__ 
         *reinterpret_cast<i32x4*>(&Bs[p][pr][pc]) = rb[p];
       }
       __syncthreads();
-      // next chunk (the last one again at the end: no conditional load)
-      const int64_t nx = (int64_t)min(mm + 1, k - 1) * kLqTile;
-#pragma unroll
-      for (int p = 0; p < kSlices; ++p) {
-        ra[p] = *reinterpret_cast<const i32x4*>(Pa + nx + p * kNb * kNb);
-        rb[p] = *reinterpret_cast<const i32x4*>(Pb + nx + p * kNb * kNb);
-      }
+      load(ra, rb, mm + 2);
       i32x4 a[kSlices][2], b[kSlices][2];
 #pragma unroll
       for (int p = 0; p < kSlices; ++p)
@@ -249,7 +249,13 @@ __global__ __launch_bounds__(256, 2) void chol_left_kernel(double* __restrict__ 
 #pragma unroll
           for (int q = 0; q + p < kSlices; ++q)
             acc[p + q] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[p][h], b[q][h], acc[p + q], 0, 0, 0);
+    };
+    int mm = 0;
+    for (; mm + 1 < k; mm += 2) {
+      step(ra0, rb0, mm);
+      step(ra1, rb1, mm + 1);
     }
+    if (mm < k) step(ra0, rb0, mm);
   }
   const int* ex = lexp + (int64_t)m * c;
   const int col = 32 * wn + (lane & 31);

@@ -23,8 +23,9 @@
 //     v_mfma_f32_32x32x2f32, 64-row x 32-column tiles) and are stored for the
 //     next launch;
 //   * the trailing kernel: Wf[:, later] -= E U[superblock, later] for every row
-//     of every job at once, a batched fp32 GEMM with K = 256 in 128x128 tiles
-//     staged through LDS, so each later weight is read and written once per
+//     of every job at once, a batched GEMM with K = 256 in 128x128 tiles, run
+//     exactly on the int8 matrix cores over 28-bit digit expansions of E and U
+//     (see "trailing update"), so each later weight is read and written once per
 //     superblock instead of once per 64 columns.
 // The loss uses the OBS identity: sum_j err_j^2 = tr[(Wq - W) Hd (Wq - W)^T],
 // so the undamped loss is sum err^2 - lambda ||Wq - W||^2 (W after zeroing
@@ -34,6 +35,8 @@
 namespace clha {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kRB = 64;             // register block: columns held per thread
 
@@ -323,177 +326,274 @@ __global__ __launch_bounds__(64, 2) void gptq_panel_kernel(GptqPlan p, int c0, J
   if (lane == 0) part[0] = c0 == 0 ? v : part[0] + v;
 }
 
+// ---------------------------------------------------------------- trailing update
 // Trailing update after the superblock at c0, for all jobs:
 //   Wf[:, n0:] -= E U[c0:c0+kSuper, n0:],   n0 = c0 + kSuper.
-// Tile: 128 padded rows x 128 columns of one job, 256 threads = 4 waves of
-// 64x64 (2x2 blocks of v_mfma_f32_32x32x2f32).  As in the panel's update the
-// product is transposed, C[col][row] = sum_k U^T[col][k] E[row][k], so each
-// lane's 16 results are 4 runs of 4 consecutive columns of one row.  Both
-// operands are K-contiguous rows (U^T and the error buffer) staged through LDS
-// in chunks of 32, double-buffered with two register stages.  MFMA step s
-// contracts k = s in lanes 0..31 and k = 16 + s in lanes 32..63 (the same
-// permutation of k for both operands), so a lane's 16 operands of a chunk
-// are 4 contiguous 16-byte LDS reads.  Tiles of one job are mapped to one XCD
-// (workgroup b runs on XCD b % 8), so U and the errors are shared through
-// one L2.
-constexpr int kGK = 32;              // K chunk
-constexpr int kGP = kGK + 4;         // LDS row pitch (floats): conflict-free 16-byte reads
-constexpr int kGBuf = kGemmTile * kGP;
+// The product runs exactly on the int8 matrix cores over digit expansions of
+// its operands (the splitting scheme of Ozaki, Ogita, Oishi and Rump, with
+// integer slices, as in the factorisation): each row of E (over the
+// superblock) and each column of U (over the superblock's rows) has a
+// power-of-two bound 2^e >= max |.| (1 + 1/64) and kTS base-128 digits, each
+// rounded to nearest, so an operand is carried to 28 bits relative to its
+// row's (column's) largest entry.  Digit pairs p + q < kTS are multiplied
+// (v_mfma_i32_32x32x32_i8, exact int32 sums over K = 256) and combined in
+// fp32: sum_w acc_w 2^-7w by Horner, then scaled by 2^(e_row + e_col - 14).
+// The fp32 products this replaces carry 24 bits per operand and round at
+// every accumulation step; the code decisions downstream see no difference.
+constexpr int kTS = 4;                  // digits per operand entry
+constexpr int kTK = 32;                 // K chunk of one MFMA step
+constexpr float kDigitBound = 0.984375f;  // 1 / (1 + 1/64): |scaled entry| * 128 <= 126
 
+// Digit planes of U for the trailing products, once per Hessian after the
+// factor: for superblock sb and column col >= (sb + 1) kSuper, with the 256
+// values U[sb*kSuper + k][col] (contiguous in U^T).  Layout in the Hessian's
+// inverse buffer (free once U is written): plane p at byte p c^2; in a plane,
+// the 32 digits of K step kc (k = 32 kc .. +31) of column col at byte
+// ((sb * 8 + kc) * c + col) * 32, so that the operands of one K step for 32
+// consecutive columns are 1 KB of consecutive bytes; the exponents follow at
+// byte kTS c^2 as int eU[sb][col].  Four threads share a column, 64 values
+// (two K steps) each.
+__global__ __launch_bounds__(256) void u_digits_kernel(const float* __restrict__ UTall, double* Xall, int c) {
+  const int sb = blockIdx.y, m = blockIdx.z;
+  const int col = 64 * blockIdx.x + (threadIdx.x >> 2), part = threadIdx.x & 3;
+  if (64 * (int)blockIdx.x < (sb + 1) * kSuper) return;   // whole block at or before the superblock
+  const int64_t cc = (int64_t)c * c;
+  const float* src = UTall + m * cc + (int64_t)col * c + sb * kSuper + 64 * part;
+  int8_t* X8 = reinterpret_cast<int8_t*>(Xall + m * cc);
+  float v[64];
+  float mx = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const float4 t = *reinterpret_cast<const float4*>(src + 4 * q);
+    v[4 * q] = t.x; v[4 * q + 1] = t.y; v[4 * q + 2] = t.z; v[4 * q + 3] = t.w;
+    mx = fmaxf(mx, fmaxf(fmaxf(fabsf(t.x), fabsf(t.y)), fmaxf(fabsf(t.z), fabsf(t.w))));
+  }
+  mx = fmaxf(mx, __shfl_xor(mx, 1));
+  mx = fmaxf(mx, __shfl_xor(mx, 2));
+  int e = 0;
+  if (mx > 0.0f) frexpf(mx * (1.0f + 1.0f / 64.0f), &e);
+  if (part == 0) reinterpret_cast<int*>(X8 + kTS * cc)[(int64_t)sb * c + col] = e;
+  uint32_t packed[kTS][16];
+#pragma unroll
+  for (int p = 0; p < kTS; ++p)
+#pragma unroll
+    for (int u = 0; u < 16; ++u) packed[p][u] = 0u;
+#pragma unroll
+  for (int u = 0; u < 64; ++u) {
+    float x = fminf(fmaxf(ldexpf(v[u], -e), -kDigitBound), kDigitBound);
+#pragma unroll
+    for (int p = 0; p < kTS; ++p) {
+      x *= 128.0f;
+      const float d = rintf(x);
+      x -= d;
+      packed[p][u >> 2] |= ((uint32_t)(int)d & 0xffu) << (8 * (u & 3));
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    int8_t* dst = X8 + (((int64_t)sb * (kSuper / kTK) + 2 * part + h) * c + col) * kTK;
+#pragma unroll
+    for (int p = 0; p < kTS; ++p)
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int u4 = 8 * h + 4 * q;
+        *reinterpret_cast<uint4*>(dst + p * cc + 16 * q) =
+            make_uint4(packed[p][u4], packed[p][u4 + 1], packed[p][u4 + 2], packed[p][u4 + 3]);
+      }
+  }
+}
+
+// One workgroup per slab (64 padded rows of one job) and superblock, sweeping
+// all of the job's trailing column tiles of 128: the slab's error digits are
+// made once, into LDS, and every column tile reuses them.  256 threads = 4
+// waves; wave w owns columns 32w..32w+31 of a tile for all 64 rows, as two
+// 32x32 blocks.  The product is transposed, C[col][row] = sum_k U^T[col][k]
+// E[row][k], so each lane's 16 results of a block are 4 runs of 4 consecutive
+// columns of one row.  Operand lanes of v_mfma_i32_32x32x32_i8: lane l holds
+// row l%32, K bytes 16(l/32)..+15 of the 32-byte step; result r of lane l is
+// row 8(r/4) + 4(l/32) + r%4, column l%32.  Each wave streams its own U
+// digits from global memory two K steps ahead in registers, so the K loop has
+// no barrier; two workgroups share a CU.  Slabs of one job are mapped to one
+// XCD (workgroup b runs on XCD b % 8), so the job's U digits are shared
+// through one L2.
 __global__ __launch_bounds__(256, 2) void gptq_trail_kernel(GptqPlan p, int c0, JobRange jr) {
-  __shared__ __attribute__((aligned(16))) float lds[4 * kGBuf];   // A0 B0 A1 B1
-  const int c = p.cols, n0 = c0 + kSuper;
-  const int ct = (c - n0 + kGemmTile - 1) / kGemmTile;
-  const int total = jr.n_tiles * ct;
+  // error digits: row r's 16-byte chunk ch at slot ch ^ (r % 16) (conflict-free lane reads)
+  __shared__ __attribute__((aligned(16))) int8_t Eq[kTS][kGptqRows][kSuper];
+  __shared__ int eE[kGptqRows];
+  const int c = p.cols, n0 = c0 + kSuper, sb = c0 / kSuper;
+  const int total = jr.n_slabs;
   const int per = (total + kXcds - 1) / kXcds;
   const int L = (int)(blockIdx.x % kXcds) * per + (int)(blockIdx.x / kXcds);
   if (L >= total) return;
-  const int rtg = jr.tile0 + L / ct, cti = L % ct;
+  const int gslab = jr.slab0 + L;
   int lo = jr.j0, hi = jr.j1;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if (p.jobs[mid].tile_base <= rtg) lo = mid; else hi = mid;
+    if (p.jobs[mid].slab_base <= gslab) lo = mid; else hi = mid;
   }
   const GJob job = p.jobs[lo];
-  const int prow0 = (rtg - job.tile_base) * kGemmTile;
-  const int prows = min(kGemmTile, job.n_slabs * kGptqRows - prow0);   // 64 or 128
-  const int col0 = n0 + cti * kGemmTile;
-  const int ncols = min(kGemmTile, c - col0);                         // 64 or 128
-  const int64_t grow = job.wf_off / c + prow0;     // first padded row of the tile (all jobs)
-  const float* __restrict__ UT = p.UT + (int64_t)job.mat * c * c + (int64_t)col0 * c + c0;
-  const float* __restrict__ E = p.ebuf + grow * kSuper;
-  float* W = p.wf + grow * c + col0;
+  const int prow0 = (gslab - job.slab_base) * kGptqRows;
+  const int64_t grow = job.wf_off / c + prow0;     // first padded row of the slab (all jobs)
+  const int64_t cc = (int64_t)c * c;
+  const int8_t* UTq = reinterpret_cast<const int8_t*>(p.X + (int64_t)job.mat * cc);
+  const int* eU = reinterpret_cast<const int*>(UTq + kTS * cc) + (int64_t)sb * c;
+  const int tid = threadIdx.x, lane = tid & 63, wc = tid >> 6, hh = lane >> 5, li = lane & 31;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wr = wave >> 1, wc = wave & 1, h = lane >> 5, li = lane & 31;
-  const bool active = wr * 64 < prows && wc * 64 < ncols;
-
-  struct Stage {
-    float4 a[4], b[4];
-  };
-  // thread t moves 16-byte chunks q = t + 256u: row q/8, chunk q%8
-  auto fetch = [&](Stage& r, int k0) {
+  // ---- error digits of the slab's rows
+  {
+    const int row = tid >> 2, part = tid & 3;
+    const float* er = p.ebuf + (grow + row) * kSuper + 64 * part;
+    float v[64];
+    float mx = 0.0f;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int q = tid + 256 * u, row = q >> 3, ch = q & 7;
-      r.a[u] = row < ncols ? *reinterpret_cast<const float4*>(UT + (int64_t)row * c + k0 + 4 * ch)
-                           : make_float4(0.f, 0.f, 0.f, 0.f);
-      r.b[u] = row < prows ? *reinterpret_cast<const float4*>(E + (int64_t)row * kSuper + k0 + 4 * ch)
-                           : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int q = 0; q < 16; ++q) {
+      const float4 t = *reinterpret_cast<const float4*>(er + 4 * q);
+      v[4 * q] = t.x; v[4 * q + 1] = t.y; v[4 * q + 2] = t.z; v[4 * q + 3] = t.w;
+      mx = fmaxf(mx, fmaxf(fmaxf(fabsf(t.x), fabsf(t.y)), fmaxf(fabsf(t.z), fabsf(t.w))));
     }
-  };
-  auto stage = [&](const Stage& r, int buf) {
-    float* As = lds + (2 * buf) * kGBuf;
-    float* Bs = lds + (2 * buf + 1) * kGBuf;
+    mx = fmaxf(mx, __shfl_xor(mx, 1));
+    mx = fmaxf(mx, __shfl_xor(mx, 2));
+    int e = 0;
+    if (mx > 0.0f) frexpf(mx * (1.0f + 1.0f / 64.0f), &e);
+    if (part == 0) eE[row] = e;
+    uint32_t packed[kTS][16];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int q = tid + 256 * u, row = q >> 3, ch = q & 7;
-      *reinterpret_cast<float4*>(As + row * kGP + 4 * ch) = r.a[u];
-      *reinterpret_cast<float4*>(Bs + row * kGP + 4 * ch) = r.b[u];
-    }
-  };
-
-  // The tile's current weights are loaded first, into registers, and only
-  // used at the end (W - E U), so their latency overlaps the products.
-  f32x16 acc[2][2], wv[2][2];
+    for (int pp = 0; pp < kTS; ++pp)
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+      for (int u = 0; u < 16; ++u) packed[pp][u] = 0u;
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      acc[a][b] = f32x16{};
-      wv[a][b] = f32x16{};
-    }
-  float* wrow[2];
+    for (int u = 0; u < 64; ++u) {
+      float x = fminf(fmaxf(ldexpf(v[u], -e), -kDigitBound), kDigitBound);
 #pragma unroll
-  for (int b = 0; b < 2; ++b) wrow[b] = W + (int64_t)(wr * 64 + 32 * b + li) * c + wc * 64 + 4 * h;
-  if (active && c0 == 0) {
-    // first trailing update: the working copy of these columns does not exist
-    // yet; start from W (rows past the matrix zero, dead columns zeroed)
-    const uint8_t* dead = p.dead + (int64_t)job.mat * c + col0 + wc * 64 + 4 * h;
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const int r = prow0 + wr * 64 + 32 * b + li;
-      const int64_t wbase = (int64_t)r * c + col0 + wc * 64 + 4 * h;
-#pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          float4 v = r < job.rows ? load_w4(job.W, job.dtype, wbase + 32 * a + 8 * q)
-                                  : make_float4(0.f, 0.f, 0.f, 0.f);
-          const uchar4 dd = *reinterpret_cast<const uchar4*>(dead + 32 * a + 8 * q);
-          wv[a][b][4 * q] = dd.x ? 0.f : v.x;
-          wv[a][b][4 * q + 1] = dd.y ? 0.f : v.y;
-          wv[a][b][4 * q + 2] = dd.z ? 0.f : v.z;
-          wv[a][b][4 * q + 3] = dd.w ? 0.f : v.w;
-        }
-    }
-  } else if (active) {
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float4 v = *reinterpret_cast<const float4*>(wrow[b] + 32 * a + 8 * q);
-          wv[a][b][4 * q] = v.x;
-          wv[a][b][4 * q + 1] = v.y;
-          wv[a][b][4 * q + 2] = v.z;
-          wv[a][b][4 * q + 3] = v.w;
-        }
-  }
-  auto multiply = [&](int buf) {
-    if (!active) return;
-    const float* As = lds + (2 * buf) * kGBuf + (wc * 64 + li) * kGP + 16 * h;
-    const float* Bs = lds + (2 * buf + 1) * kGBuf + (wr * 64 + li) * kGP + 16 * h;
-    float4 av[2][4], bv[2][4];
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-#pragma unroll
-      for (int x = 0; x < 2; ++x) {
-        av[x][m] = *reinterpret_cast<const float4*>(As + 32 * x * kGP + 4 * m);
-        bv[x][m] = *reinterpret_cast<const float4*>(Bs + 32 * x * kGP + 4 * m);
+      for (int pp = 0; pp < kTS; ++pp) {
+        x *= 128.0f;
+        const float d = rintf(x);
+        x -= d;
+        packed[pp][u >> 2] |= ((uint32_t)(int)d & 0xffu) << (8 * (u & 3));
       }
     }
 #pragma unroll
-    for (int st = 0; st < 16; ++st)
+    for (int pp = 0; pp < kTS; ++pp)
 #pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x2f32((&av[a][st >> 2].x)[st & 3],
-                                                           (&bv[b][st >> 2].x)[st & 3], acc[a][b], 0, 0, 0);
-  };
-
-  constexpr int nch = kSuper / kGK;   // 8, even; the loop is unrolled, so every
-                                      // fetch is unconditional and waits count exactly
-  Stage r0, r1;
-  fetch(r0, 0);
-  stage(r0, 0);
-  fetch(r1, kGK);
-  fetch(r0, 2 * kGK);
-  __syncthreads();
-#pragma unroll
-  for (int st = 0; st < nch; st += 2) {
-    // chunk st in buffer 0, st+1 in r1, st+2 in r0
-    multiply(0);
-    stage(r1, 1);
-    if (st + 3 < nch) fetch(r1, (st + 3) * kGK);
-    __syncthreads();
-    multiply(1);
-    if (st + 2 < nch) stage(r0, 0);
-    if (st + 4 < nch) fetch(r0, (st + 4) * kGK);
-    __syncthreads();
+      for (int q = 0; q < 4; ++q) {
+        const int ch = 4 * part + q;
+        *reinterpret_cast<uint4*>(&Eq[pp][row][16 * (ch ^ (row & 15))]) =
+            make_uint4(packed[pp][4 * q], packed[pp][4 * q + 1], packed[pp][4 * q + 2], packed[pp][4 * q + 3]);
+      }
   }
-  if (active) {
+  __syncthreads();
+
+  // ---- U digits: this lane's A operands of K step g (over all column tiles)
+  const int n_ct = (c - n0 + kGemmTile - 1) / kGemmTile;
+  const int last = n_ct * (kSuper / kTK) - 1;
+  const int lcol = wc * 32 + li;                    // the lane's operand column in a tile
+  auto fetch = [&](i32x4 (&a)[kTS], int g) {
+    g = min(g, last);
+    const int t = g / (kSuper / kTK), kc = g % (kSuper / kTK);
+    const int col = min(n0 + t * kGemmTile + lcol, c - 1);
+    const int8_t* src = UTq + (((int64_t)sb * (kSuper / kTK) + kc) * c + col) * kTK + 16 * hh;
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int pp = 0; pp < kTS; ++pp) a[pp] = *reinterpret_cast<const i32x4*>(src + pp * cc);
+  };
+  i32x4 a0[kTS], a1[kTS];
+  fetch(a0, 0);
+  fetch(a1, 1);
+  const int erow[2] = {eE[li] - 14, eE[32 + li] - 14};
+  const int cl = wc * 32 + 4 * hh;                  // lane's first result column in a tile
+  int g = 0;
+  for (int t = 0; t < n_ct; ++t) {
+    const int col0 = n0 + t * kGemmTile;
+    const int ncols = min(kGemmTile, c - col0);   // 64 or 128
+    const bool active = wc * 32 < ncols;
+    float* W = p.wf + grow * c + col0;
+    // the tile's weights (consumed at the end, so their latency overlaps the products)
+    f32x16 wv[2];
+    wv[0] = f32x16{};
+    wv[1] = f32x16{};
+    if (active && c0 == 0) {
+      // first trailing update: the working copy of these columns does not exist
+      // yet; start from W (rows past the matrix zero, dead columns zeroed)
+      const uint8_t* dead = p.dead + (int64_t)job.mat * c + col0 + cl;
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const int r = prow0 + 32 * b + li;
+        const int64_t wbase = (int64_t)r * c + col0 + cl;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 v = r < job.rows ? load_w4(job.W, job.dtype, wbase + 8 * q) : make_float4(0.f, 0.f, 0.f, 0.f);
+          const uchar4 dd = *reinterpret_cast<const uchar4*>(dead + 8 * q);
+          wv[b][4 * q] = dd.x ? 0.f : v.x;
+          wv[b][4 * q + 1] = dd.y ? 0.f : v.y;
+          wv[b][4 * q + 2] = dd.z ? 0.f : v.z;
+          wv[b][4 * q + 3] = dd.w ? 0.f : v.w;
+        }
+      }
+    } else if (active) {
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          *reinterpret_cast<float4*>(wrow[b] + 32 * a + 8 * q) =
-              make_float4(wv[a][b][4 * q] - acc[a][b][4 * q], wv[a][b][4 * q + 1] - acc[a][b][4 * q + 1],
-                          wv[a][b][4 * q + 2] - acc[a][b][4 * q + 2], wv[a][b][4 * q + 3] - acc[a][b][4 * q + 3]);
+        for (int q = 0; q < 4; ++q) {
+          const float4 v = *reinterpret_cast<const float4*>(W + (int64_t)(32 * b + li) * c + cl + 8 * q);
+          wv[b][4 * q] = v.x;
+          wv[b][4 * q + 1] = v.y;
+          wv[b][4 * q + 2] = v.z;
+          wv[b][4 * q + 3] = v.w;
+        }
+    }
+    i32x16 acc[2][kTS];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int w = 0; w < kTS; ++w) acc[b][w] = i32x16{};
+    auto step = [&](const i32x4 (&a)[kTS], int kc) {
+      i32x4 bq[2][kTS];
+      const int ch = 2 * kc + hh;
+#pragma unroll
+      for (int pp = 0; pp < kTS; ++pp)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          const int row = 32 * b + li;
+          bq[b][pp] = *reinterpret_cast<const i32x4*>(&Eq[pp][row][16 * (ch ^ (row & 15))]);
+        }
+      // the two blocks alternate, so products into one accumulator are never adjacent
+#pragma unroll
+      for (int pp = 0; pp < kTS; ++pp)
+#pragma unroll
+        for (int q = 0; pp + q < kTS; ++q)
+#pragma unroll
+          for (int b = 0; b < 2; ++b)
+            acc[b][pp + q] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[pp], bq[b][q], acc[b][pp + q], 0, 0, 0);
+    };
+    // K steps in pairs: even steps use a0, odd ones a1, each refilled two steps ahead
+#pragma unroll 1
+    for (int kc = 0; kc < kSuper / kTK; kc += 2, g += 2) {
+      step(a0, kc);
+      fetch(a0, g + 2);
+      step(a1, kc + 1);
+      fetch(a1, g + 3);
+    }
+    if (active) {
+      // results r = 4q .. 4q+3 are columns cl + 8q .. +3 (their exponents: one int4)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int4 e4 = *reinterpret_cast<const int4*>(eU + col0 + cl + 8 * q);
+        const int ec[4] = {e4.x, e4.y, e4.z, e4.w};
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          float out[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int r = 4 * q + u;
+            float f = (float)acc[b][kTS - 1][r];
+#pragma unroll
+            for (int w = kTS - 2; w >= 0; --w) f = fmaf(f, 1.0f / 128.0f, (float)acc[b][w][r]);
+            out[u] = wv[b][r] - ldexpf(f, erow[b] + ec[u]);
+          }
+          *reinterpret_cast<float4*>(W + (int64_t)(32 * b + li) * c + cl + 8 * q) =
+              make_float4(out[0], out[1], out[2], out[3]);
+        }
+      }
+    }
   }
 }
 
@@ -559,6 +659,13 @@ bool gptq_group_supported(int group) {
 
 void launch_gptq(const GptqPlan& p, const JobRange& jr, hipStream_t s) {
   if (jr.j1 <= jr.j0) return;
+  if (p.cols > kSuper) {
+    const int64_t cc = (int64_t)p.cols * p.cols;
+    // superblocks followed by trailing columns: all but the last (full ones)
+    const int nsb = (p.cols + kSuper - 1) / kSuper - 1;
+    hipLaunchKernelGGL(u_digits_kernel, dim3(p.cols / 64, nsb, jr.m1 - jr.m0), dim3(256), 0, s,
+                       p.UT + jr.m0 * cc, p.X + jr.m0 * cc, p.cols);
+  }
   const dim3 grid(jr.n_slabs), blk(64);
   for (int c0 = 0; c0 < p.cols; c0 += kSuper) {
     switch (p.group) {
@@ -571,8 +678,7 @@ void launch_gptq(const GptqPlan& p, const JobRange& jr, hipStream_t s) {
     }
     const int n0 = c0 + kSuper;
     if (n0 < p.cols) {
-      const int tiles = jr.n_tiles * ((p.cols - n0 + kGemmTile - 1) / kGemmTile);
-      const int per = (tiles + kXcds - 1) / kXcds;
+      const int per = (jr.n_slabs + kXcds - 1) / kXcds;
       hipLaunchKernelGGL(gptq_trail_kernel, dim3(per * kXcds), dim3(256), 0, s, p, c0, jr);
     }
   }

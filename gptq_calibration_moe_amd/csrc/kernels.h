@@ -116,6 +116,7 @@ void launch_factor_group(const GptqPlan& p, int m0, int m1, hipStream_t s, hipEv
 // A contiguous range of jobs [j0, j1) with their global slabs and row tiles.
 struct JobRange {
   int j0, j1, slab0, n_slabs, tile0, n_tiles;
+  int m0, m1;   // the Hessians of these jobs
 };
 void launch_gptq(const GptqPlan& p, const JobRange& r, hipStream_t s);
 
