@@ -23,8 +23,11 @@
 //
 // Every step is batched over all distinct Hessians of one call:
 //   diag_stats      dead columns (H_ii == 0) and lambda = damp * mean(diag),
-//                   taking H_ii := 1 on dead columns first
-//   build_reversed  A = J (H + fixes + lambda I) J, lower triangle, fp64
+//                   taking H_ii := 1 on dead columns first; row exponents of the
+//                   sliced factor (below)
+//   The reversed damped matrix A = J (H + fixes + lambda I) J is never formed:
+//   each entry is read from H (fp32, exact in fp64) once, by the block step
+//   that first needs it.
 //   left-looking Cholesky, per 64-column block step k:
 //     chol_left     T_i = A[i][k] - sum_{m<k} L[i][m] L[k][m]^T for block rows i >= k
 //                   (int8 digit-pair products accumulated exactly, next chunk prefetched)
@@ -103,7 +106,8 @@ __global__ __launch_bounds__(256) void diag_stats_kernel(const float* const* __r
                                                          int c, float damp,
                                                          uint8_t* __restrict__ dead,
                                                          double* __restrict__ lamd,
-                                                         float* __restrict__ lam_out) {
+                                                         float* __restrict__ lam_out,
+                                                         int* __restrict__ lexp) {
   __shared__ double red[256];
   const int m = blockIdx.x;
   const float* H = mats[m];
@@ -120,40 +124,21 @@ __global__ __launch_bounds__(256) void diag_stats_kernel(const float* const* __r
     if (threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
     __syncthreads();
   }
+  const double l = (double)damp * (red[0] / (double)c);
   if (threadIdx.x == 0) {
-    const double l = (double)damp * (red[0] / (double)c);
     lamd[m] = l;
     if (lam_out) lam_out[m] = (float)l;
   }
-}
-
-__global__ __launch_bounds__(256) void build_reversed_kernel(const float* const* __restrict__ mats,
-                                                             int c, const uint8_t* __restrict__ dead,
-                                                             const double* __restrict__ lamd,
-                                                             double* __restrict__ Aall,
-                                                             int* __restrict__ lexp) {
-  const int m = blockIdx.y;
-  int bi, bj;
-  tri_of(blockIdx.x, bi, bj);
-  const float* H = mats[m];
-  double* A = Aall + (int64_t)m * c * c;
-  const double l = lamd[m];
-  for (int idx = threadIdx.x; idx < kNb * kNb; idx += 256) {
-    const int r = idx >> 6, cc = idx & 63;
-    const int i = bi * kNb + r, j = bj * kNb + cc;
-    if (j > i) continue;
-    const int hi = c - 1 - i, hj = c - 1 - j;
-    double v = (double)H[(int64_t)hi * c + hj];
-    if (i == j) {
-      v = (dead[(int64_t)m * c + hi] ? 1.0 : v) + l;
-      // every entry of row i of the factor is at most sqrt(A_ii) in magnitude:
-      // 2^e >= sqrt(A_ii) (1 + 1/64) scales the row's digits, so that a scaled
-      // entry times 128 stays within 126.1 and its first digit fits int8
-      int e = 0;
-      if (v > 0.0) frexp(sqrt(v) * (1.0 + 1.0 / 64.0), &e);
-      lexp[(int64_t)m * c + i] = e;
-    }
-    A[(int64_t)i * c + j] = v;
+  // Row exponents of the factor of the reversed matrix A = J Hd J: every entry
+  // of row i of the factor is at most sqrt(A_ii) in magnitude, and 2^e >=
+  // sqrt(A_ii) (1 + 1/64) scales the row's digits so that a scaled entry
+  // times 128 stays within 126.1 and its first digit fits int8.
+  for (int hi = threadIdx.x; hi < c; hi += 256) {
+    const float h = H[(int64_t)hi * c + hi];
+    const double v = (h == 0.0f ? 1.0 : (double)h) + l;
+    int e = 0;
+    if (v > 0.0) frexp(sqrt(v) * (1.0 + 1.0 / 64.0), &e);
+    lexp[(int64_t)m * c + (c - 1 - hi)] = e;
   }
 }
 
@@ -197,7 +182,10 @@ __device__ __forceinline__ int64_t lq_offset(int c, int m, int I, int K) {
 // m in LDS.
 __global__ __launch_bounds__(256, 2) void chol_left_kernel(double* __restrict__ Aall,
                                                            const int8_t* __restrict__ Lq,
-                                                           const int* __restrict__ lexp, int c, int k) {
+                                                           const int* __restrict__ lexp,
+                                                           const float* const* __restrict__ mats,
+                                                           const uint8_t* __restrict__ dead,
+                                                           const double* __restrict__ lamd, int c, int k) {
   __shared__ __align__(16) int8_t As[kSlices][kNb][kLqPitch];
   __shared__ __align__(16) int8_t Bs[kSlices][kNb][kLqPitch];
   const int m = blockIdx.y, i = k + blockIdx.x;
@@ -257,9 +245,13 @@ __global__ __launch_bounds__(256, 2) void chol_left_kernel(double* __restrict__ 
     }
     if (mm < k) step(ra0, rb0, mm);
   }
+  // A[i][j] = Hd[c-1-i][c-1-j], read from H: its diagonal takes the dead-column
+  // fix (H_jj := 1) and lambda
   const int* ex = lexp + (int64_t)m * c;
+  const float* H = mats[m];
   const int col = 32 * wn + (lane & 31);
   const int ecol = ex[k0 + col];
+  const int64_t hj = c - 1 - (k0 + col);
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int row = 32 * wm + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
@@ -267,8 +259,10 @@ __global__ __launch_bounds__(256, 2) void chol_left_kernel(double* __restrict__ 
     double sum = 0.0;
 #pragma unroll
     for (int w = kSlices - 1; w >= 0; --w) sum += ldexp((double)acc[w][r], -7 * (w + 2));
-    double* t = A + (i0 + row) * c + k0 + col;
-    *t = *t - ldexp(sum, ex[i0 + row] + ecol);
+    const int64_t hi = c - 1 - (i0 + row);
+    double a = (double)H[hi * c + hj];
+    if (hi == hj) a = (dead[(int64_t)m * c + hi] ? 1.0 : a) + lamd[m];
+    A[(i0 + row) * c + k0 + col] = a - ldexp(sum, ex[i0 + row] + ecol);
   }
 }
 
@@ -659,13 +653,11 @@ void launch_factor_group(const GptqPlan& p, int m0, int m1, hipStream_t s, hipEv
   double* dinv = p.dinv + (int64_t)m0 * c * kNb;
   float* U = p.U + m0 * cc;
   float* UT = p.UT ? p.UT + m0 * cc : nullptr;
-  hipLaunchKernelGGL(diag_stats_kernel, dim3(n), dim3(256), 0, s, mats, c, p.damp, dead, lamd, lam);
   int* lexp = p.lexp + (int64_t)m0 * c;
   int8_t* Lq = reinterpret_cast<int8_t*>(X);   // free until the inverse starts
-  hipLaunchKernelGGL(build_reversed_kernel, dim3(nbk * (nbk + 1) / 2, n), dim3(256), 0, s, mats, c, dead,
-                     lamd, A, lexp);
+  hipLaunchKernelGGL(diag_stats_kernel, dim3(n), dim3(256), 0, s, mats, c, p.damp, dead, lamd, lam, lexp);
   for (int k = 0; k < nbk; ++k) {
-    hipLaunchKernelGGL(chol_left_kernel, dim3(nbk - k, n), dim3(256), 0, s, A, Lq, lexp, c, k);
+    hipLaunchKernelGGL(chol_left_kernel, dim3(nbk - k, n), dim3(256), 0, s, A, Lq, lexp, mats, dead, lamd, c, k);
     hipLaunchKernelGGL(chol_diag_kernel, dim3(n), dim3(128), 0, s, A, c, k, dinv, p.status);
     if (k == 0 && step0_done) hipEventRecord(step0_done, s);
     if (k + 1 < nbk)
