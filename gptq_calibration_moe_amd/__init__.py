@@ -28,6 +28,7 @@ F32, BF16 = 0, 1
 
 EXPORTS = (
     "clha_create", "clha_destroy", "clha_last_error", "clha_num_slots", "clha_register_layer",
+    "clha_reset_layer",
     "clha_collect_workspace_bytes", "clha_collect_hessians", "clha_aggregate",
     "clha_gptq_workspace_bytes", "clha_gptq_quantize", "clha_inverse_cholesky_workspace_bytes",
     "clha_inverse_cholesky", "clha_loss_workspace_bytes", "clha_loss", "clha_set_timing",
@@ -65,6 +66,7 @@ def _load() -> C.CDLL:
         "clha_last_error": ([vp], C.c_char_p),
         "clha_num_slots": ([vp], i32),
         "clha_register_layer": ([vp, i32, vp, vp], i32),
+        "clha_reset_layer": ([vp, i32, vp], i32),
         "clha_collect_workspace_bytes": ([vp], sz),
         "clha_collect_hessians": ([vp, i32, i64, vp, vp, vp, vp, vp, vp, sz, vp], i32),
         "clha_aggregate": ([vp, i32, C.POINTER(i32), i32, C.POINTER(f32), vp, vp, vp], i32),
@@ -178,6 +180,11 @@ class Context:
         _check_dev("counts", counts, torch.int64, (self.slots,), self.device)
         self._raise(lib.clha_register_layer(self._h, layer, _ptr(S), _ptr(counts)))
         self._layers[layer] = (S, counts)
+
+    def reset_layer(self, layer: int, stream=None):
+        """New accumulation for a registered layer: counts zeroed now, and the next
+        collection with tokens overwrites S instead of adding (no clearing of S)."""
+        self._raise(lib.clha_reset_layer(self._h, layer, _stream(stream)))
 
     def collect_workspace_bytes(self) -> int:
         return lib.clha_collect_workspace_bytes(self._h)

@@ -31,9 +31,10 @@ class SharedGroupCalibration:
         self.alpha = torch.empty(ctx.slots, len(self.layer_ids), dtype=torch.float32, device=ctx.device)
 
     def reset(self):
+        """Starts a new accumulation: the next collection of each layer overwrites
+        its sums (the library zeroes the counts now and S only where no token lands)."""
         for l in self.layer_ids:
-            self.S[l].zero_()
-            self.counts[l].zero_()
+            self.ctx.reset_layer(l)
 
     def collect(self, layer: int, x: torch.Tensor, logits: torch.Tensor, **kw):
         self.ctx.collect_hessians(layer, x, logits, **kw)

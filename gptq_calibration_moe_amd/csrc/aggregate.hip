@@ -101,6 +101,7 @@ __global__ __launch_bounds__(256) void aggregate_kernel(AggArgs g, float* __rest
     } else if (w.rt) {
       float sum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
       for (int l = 0; l < g.n_layers; ++l) {
+        if (n[l] == 0) continue;   // a layer without tokens for this slot drops out
         const float4 x = *reinterpret_cast<const float4*>(g.S[l] + soff + e);
         sum[0] = __fadd_rn(sum[0], x.x);
         sum[1] = __fadd_rn(sum[1], x.y);

@@ -29,6 +29,7 @@ int syrk_items_per_slot(int d);
 struct LayerBufs {
   float* S;
   int64_t* counts;
+  bool fresh;   // reset since the last collection with tokens: the next one overwrites
 };
 
 struct clha_ctx {
@@ -350,8 +351,18 @@ CLHA_API clha_status clha_register_layer(clha_ctx* ctx, int32_t layer, float* S,
   }
   if (overlaps(S, sb, counts, cb))
     return fail(ctx, CLHA_ERR_INVALID_ARG, "register_layer: S and counts overlap");
-  ctx->layers[layer] = LayerBufs{S, counts};
+  ctx->layers[layer] = LayerBufs{S, counts, false};
   return CLHA_OK;
+}
+
+CLHA_API clha_status clha_reset_layer(clha_ctx* ctx, int32_t layer, void* stream) {
+  if (!ctx) return CLHA_ERR_INVALID_ARG;
+  auto it = ctx->layers.find(layer);
+  if (it == ctx->layers.end())
+    return fail(ctx, CLHA_ERR_INVALID_ARG, "reset_layer: layer %d is not registered", layer);
+  clha::launch_zero_counts(it->second.counts, ctx->slots, as_stream(stream));
+  it->second.fresh = true;
+  return hip_check(ctx, "reset_layer");
 }
 
 CLHA_API size_t clha_collect_workspace_bytes(const clha_ctx* ctx) {
@@ -404,6 +415,7 @@ CLHA_API clha_status clha_collect_hessians(clha_ctx* ctx, int32_t layer, int64_t
   p.split = L.split;
   p.partials = L.partials;
   p.syrk_items = clha::syrk_items_per_slot(d.d);
+  p.overwrite = it->second.fresh ? 1 : 0;
   p.token_ids = token_ids_out ? token_ids_out : L.token_ids;
   p.xgT = L.xgT;
   p.xg_tiles = (n_tokens * d.top_k + clha::kTokPad - 1) / clha::kTokPad + d.n_routed +
@@ -424,8 +436,9 @@ CLHA_API clha_status clha_collect_hessians(clha_ctx* ctx, int32_t layer, int64_t
   }
   {
     StageTimer t(ctx, CLHA_STAGE_SYRK, s);
-    clha::launch_syrk(p, it->second.S, s);
+    clha::launch_syrk(p, it->second.S, it->second.counts, s);
   }
+  it->second.fresh = false;
   return hip_check(ctx, "collect_hessians");
 }
 

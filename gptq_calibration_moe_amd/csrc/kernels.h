@@ -50,6 +50,7 @@ struct CollectPlan {
   int32_t* split;        // [1 + 3*kMaxPartials] count, then (slot, first partial, partials)
   float* partials;       // [kMaxPartials][d][d] partial sums of token-split slots
   int syrk_items;        // Gram-sum items per segment
+  int overwrite;         // first collection after a reset: S and counts are stored, not added
   int32_t* token_ids;    // [n*K]
   uint16_t* xgT;         // feature-major gathered activations
   int64_t xg_tiles;      // upper bound of 64-token tiles over all slots
@@ -59,7 +60,8 @@ struct CollectPlan {
 void launch_route(const float* logits, const CollectPlan& p, hipStream_t s);
 void launch_bucket(const CollectPlan& p, int64_t* layer_counts, hipStream_t s);
 void launch_gather(const uint16_t* x, const CollectPlan& p, hipStream_t s);
-void launch_syrk(const CollectPlan& p, float* S, hipStream_t s);
+void launch_syrk(const CollectPlan& p, float* S, const int64_t* layer_counts, hipStream_t s);
+void launch_zero_counts(int64_t* counts, int n, hipStream_t s);
 int syrk_items_per_slot(int d);
 
 // ---------------------------------------------------------------- aggregation

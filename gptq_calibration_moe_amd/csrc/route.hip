@@ -115,7 +115,7 @@ __global__ __launch_bounds__(256) void bucket_count_kernel(const int32_t* __rest
 __global__ __launch_bounds__(256) void bucket_scan_kernel(
     const int32_t* __restrict__ blockcounts, int nblk, int64_t n, int E, int has_shared,
     int32_t* __restrict__ blockbase, int64_t* __restrict__ offsets, int64_t* __restrict__ pad_off,
-    int32_t* __restrict__ slot_order, int64_t* __restrict__ layer_counts, int items,
+    int32_t* __restrict__ slot_order, int64_t* __restrict__ layer_counts, int overwrite, int items,
     int32_t* __restrict__ work, int32_t* __restrict__ work_len, int32_t* __restrict__ work_next,
     int32_t* __restrict__ seg, int32_t* __restrict__ split) {
   __shared__ int64_t cnt[kMaxExperts + 1];
@@ -138,7 +138,7 @@ __global__ __launch_bounds__(256) void bucket_scan_kernel(
   __syncthreads();
   for (int e = threadIdx.x; e < slots; e += 256) {
     padc[e] = (cnt[e] + kTokPad - 1) / kTokPad * kTokPad;
-    if (layer_counts) layer_counts[e] += cnt[e];
+    if (layer_counts) layer_counts[e] = overwrite ? cnt[e] : layer_counts[e] + cnt[e];
   }
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -257,12 +257,21 @@ __global__ __launch_bounds__(256) void bucket_scatter_kernel(
   }
 }
 
+__global__ void zero_counts_kernel(int64_t* __restrict__ counts, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) counts[i] = 0;
+}
+
+// A fill kernel rather than a memset, so that the reset can be captured in a graph.
+void launch_zero_counts(int64_t* counts, int n, hipStream_t s) {
+  hipLaunchKernelGGL(zero_counts_kernel, dim3(1), dim3(256), 0, s, counts, n);
+}
+
 void launch_bucket(const CollectPlan& p, int64_t* layer_counts, hipStream_t s) {
   hipLaunchKernelGGL(bucket_count_kernel, dim3(p.nblk), dim3(256), 0, s, p.topk, p.n_tokens, p.K,
                      p.E, p.blockcounts);
   hipLaunchKernelGGL(bucket_scan_kernel, dim3(1), dim3(256), 0, s, p.blockcounts, p.nblk,
                      p.n_tokens, p.E, p.has_shared, p.blockbase, p.offsets, p.pad_off,
-                     p.slot_order, layer_counts, p.syrk_items, p.work, p.work_len, p.work_next,
+                     p.slot_order, layer_counts, p.overwrite, p.syrk_items, p.work, p.work_len, p.work_next,
                      p.seg, p.split);
   hipLaunchKernelGGL(bucket_scatter_kernel, dim3(p.nblk), dim3(256), 0, s, p.topk, p.n_tokens,
                      p.K, p.E, p.blockbase, p.offsets, p.token_ids);

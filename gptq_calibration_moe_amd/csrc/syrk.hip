@@ -248,14 +248,17 @@ __device__ __forceinline__ void tile_of(int t, int& ti, int& tj) {
 // One item of one segment.
 __device__ __forceinline__ void syrk_item(const uint16_t* __restrict__ xgT, const int64_t* __restrict__ pad_off,
                                           const int32_t* __restrict__ seg, int sg, int item, int d,
-                                          float* __restrict__ S, float* __restrict__ partials, const Stages& sb) {
+                                          float* __restrict__ S, float* __restrict__ partials, bool overwrite,
+                                          const Stages& sb) {
   const int slot = seg[4 * sg], dest = seg[4 * sg + 1];
   const int64_t t0 = seg[4 * sg + 2], ntok = seg[4 * sg + 3];
   const int64_t npad = pad_off[slot + 1] - pad_off[slot];
   const uint16_t* base = xgT + pad_off[slot] * d;
   const int64_t dd = (int64_t)d * d;
   float* Sd = dest < 0 ? S + (int64_t)slot * dd : partials + (int64_t)dest * dd;
-  const bool partial = dest >= 0;
+  // the first flush of a partial buffer stores; so does the first flush into S
+  // when this collection overwrites the layer's sums
+  const bool partial = dest >= 0 || overwrite;
   const int64_t nsteps = ntok / kSK;
   const int nt = (d + kT - 1) / kT, nd = (nt + 1) / 2;
   if (item >= nd) {
@@ -288,7 +291,8 @@ __global__ __launch_bounds__(512) void syrk_kernel(const uint16_t* __restrict__ 
                                                    const int32_t* __restrict__ work_len,
                                                    int32_t* __restrict__ work_next,
                                                    const int32_t* __restrict__ seg, int cap, int d,
-                                                   float* __restrict__ S, float* __restrict__ partials) {
+                                                   float* __restrict__ S, float* __restrict__ partials,
+                                                   int overwrite) {
   __shared__ __attribute__((aligned(16))) uint16_t a0[kPanel], a1[kPanel], a2[kPanel], a3[kPanel];
   __shared__ __attribute__((aligned(16))) uint16_t b0[kPanel], b1[kPanel], b2[kPanel], b3[kPanel];
   __shared__ int item;
@@ -302,7 +306,7 @@ __global__ __launch_bounds__(512) void syrk_kernel(const uint16_t* __restrict__ 
     __syncthreads();
     if (it >= len) break;
     const int code = work[x * cap + it];
-    syrk_item(xgT, pad_off, seg, code >> 10, code & 1023, d, S, partials, sb);
+    syrk_item(xgT, pad_off, seg, code >> 10, code & 1023, d, S, partials, overwrite != 0, sb);
   }
 }
 
@@ -334,9 +338,32 @@ __global__ __launch_bounds__(256) void syrk_reduce_kernel(const int32_t* __restr
   }
 }
 
-void launch_syrk(const CollectPlan& p, float* S, hipStream_t s) {
+// When a collection overwrites the layer's sums, a slot that received no
+// token has no Gram-sum item: its lower triangle is zeroed here instead.
+// One workgroup per slot; slots with tokens return at once.
+__global__ __launch_bounds__(256) void zero_empty_slots_kernel(const int64_t* __restrict__ counts,
+                                                               float* __restrict__ S, int d) {
+  const int slot = blockIdx.x;
+  if (counts[slot] != 0) return;
+  float* Ss = S + (int64_t)slot * d * d;
+  for (int i = 0; i < d; ++i)
+    for (int j = 4 * (int)threadIdx.x; j <= i; j += 1024) {
+      float* o = Ss + (int64_t)i * d + j;
+      if (j + 3 <= i) {
+        *reinterpret_cast<float4*>(o) = make_float4(0.f, 0.f, 0.f, 0.f);
+      } else {
+        for (int u = 0; j + u <= i; ++u) o[u] = 0.0f;
+      }
+    }
+}
+
+void launch_syrk(const CollectPlan& p, float* S, const int64_t* layer_counts, hipStream_t s) {
+  if (p.overwrite)
+    hipLaunchKernelGGL(zero_empty_slots_kernel, dim3(p.E + p.has_shared), dim3(256), 0, s, layer_counts, S,
+                       p.d);
   hipLaunchKernelGGL(syrk_kernel, dim3(kXcds * kSyrkWgPerXcd), dim3(512), 0, s, p.xgT, p.pad_off, p.work,
-                     p.work_len, p.work_next, p.seg, kMaxSegs * p.syrk_items, p.d, S, p.partials);
+                     p.work_len, p.work_next, p.seg, kMaxSegs * p.syrk_items, p.d, S, p.partials,
+                     p.overwrite);
   hipLaunchKernelGGL(syrk_reduce_kernel, dim3((p.d + 1023) / 1024, p.d), dim3(256), 0, s, p.split,
                      p.partials, S, p.d);
 }

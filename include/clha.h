@@ -94,12 +94,25 @@ CLHA_API int32_t clha_num_slots(const clha_ctx* ctx);
 /* Binds the accumulators of one layer (the layer-aware collection of section 2.4).
  *   S      device, float [slots][d][d]: Gram sums S[e] = sum_t x_t x_t^T over the tokens
  *          routed to slot e (slot E: all tokens).  Only the lower triangle (i >= j) is
- *          ever written; the caller zeroes the buffer before the first collection.
- *   counts device, int64 [slots]: token counts n[e]; zeroed by the caller.
+ *          ever written; before the first collection the caller either zeroes the
+ *          buffer or calls clha_reset_layer.
+ *   counts device, int64 [slots]: token counts n[e]; zeroed by the caller (or by
+ *          clha_reset_layer).
  * A layer may be registered again (rebinding it).  Registering a buffer range that
  * overlaps another layer's S or counts returns INVALID_ARG: two layers never share
  * one accumulator. */
 CLHA_API clha_status clha_register_layer(clha_ctx* ctx, int32_t layer, float* S, int64_t* counts);
+
+/* Starts a new accumulation for a registered layer (section 2.4: per-layer
+ * accumulators, emptied between calibration runs) without clearing S:
+ *   counts are zeroed on `stream` now; the next clha_collect_hessians of this
+ *   layer that has tokens stores instead of adding: S[e] = X_e^T X_e (lower
+ *   triangle; slots that receive no token are zeroed) and counts[e] = n_e.
+ *   Later collections add as usual.
+ * Until that collection S holds stale sums, but with zero counts every
+ * aggregation treats the layer as empty and reads none of them.
+ * Errors: INVALID_ARG (null ctx, unregistered layer), HIP. */
+CLHA_API clha_status clha_reset_layer(clha_ctx* ctx, int32_t layer, void* stream);
 
 /* Device workspace bytes that clha_collect_hessians needs for max_tokens tokens. */
 CLHA_API size_t clha_collect_workspace_bytes(const clha_ctx* ctx);
@@ -110,7 +123,8 @@ CLHA_API size_t clha_collect_workspace_bytes(const clha_ctx* ctx);
  *   3. gathers each expert's rows of X;
  *   4. S[e] += X_e^T X_e (fp32 accumulation of bf16 products) for every routed expert,
  *      and S[E] += X^T X over all tokens when the block has shared experts;
- *      counts[e] += n_e, counts[E] += n_tokens.
+ *      counts[e] += n_e, counts[E] += n_tokens (stored instead of added by the first
+ *      collection with tokens after clha_reset_layer).
  *   x        device, bf16 bits [n_tokens][d]
  *   logits   device, float [n_tokens][E]
  *   topk_out, offsets_out, token_ids_out: optional device outputs of this batch's

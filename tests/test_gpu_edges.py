@@ -6,7 +6,10 @@
   round-to-nearest on the same grid;
 * all-zero weight rows: every group takes the (-1, 1) grid, every code is z;
 * the largest hidden size, d = 8192: routing, Gram sums (sampled columns) and
-  GPTQ of a 32-row matrix on a well-conditioned Hessian.
+  GPTQ of a 32-row matrix on a well-conditioned Hessian;
+* a reset accumulator (stale sums left in S, counts zeroed) collects exactly
+  what a zeroed one does, an unrouted slot included, and a layer reset but
+  never collected drops out of the aggregation.
 """
 import numpy as np
 import pytest
@@ -141,3 +144,39 @@ def test_largest_hidden_size():
     want = oracle.loss(W.astype(np.float64), refq["wq"], Hm.astype(np.float64))
     got_loss = float(job["loss"].cpu().numpy()[0])
     assert abs(got_loss - want) <= LOSS_RTOL * want
+
+
+def test_reset_layer_matches_a_zeroed_accumulator():
+    import gptq_calibration_moe_amd as clha
+    wl = gen.WORKLOADS[1].scaled(n_tokens=4096)
+    inp = gen.pair_inputs(wl)
+    lg = [l.copy() for l in inp["logits"]]
+    for l in lg:
+        l[:, 5] = -100.0                     # expert 5 is never chosen: an empty slot
+    ctx = clha.Context(wl.d, wl.n_routed, wl.top_k, wl.n_shared, wl.n_tokens, device=dev())
+    Sz, nz = ctx.new_layer_buffers()         # zeroed: the plain accumulation
+    Sr, nr = ctx.new_layer_buffers()
+    Sr.fill_(3.0)                            # stale sums and counts of an earlier run
+    nr.fill_(7)
+    ctx.register_layer(0, Sz, nz)
+    ctx.register_layer(1, Sr, nr)
+    ctx.reset_layer(1)
+    half = wl.n_tokens // 2
+    for lo, hi in ((0, half), (half, wl.n_tokens)):   # two batches: overwrite, then add
+        for layer in (0, 1):
+            ctx.collect_hessians(layer, bits_to_dev(inp["x"][0][lo:hi]), to_dev(lg[0][lo:hi]))
+    ctx.sync()
+    assert torch.equal(nr, nz) and int(nr[5]) == 0
+    low = torch.tril(torch.ones(wl.d, wl.d, dtype=torch.bool, device=dev()))
+    for slot in range(ctx.slots):
+        assert torch.equal(Sr[slot][low], Sz[slot][low]), f"slot {slot}"
+    assert not bool(Sr[5][low].any())        # the empty slot was zeroed
+
+    # a layer reset and never collected has zero counts: rt drops it
+    ctx.reset_layer(0)
+    H2 = torch.empty(ctx.slots, wl.d, wl.d, dtype=torch.float32, device=dev())
+    H1 = torch.empty_like(H2)
+    ctx.aggregate([0, 1], "rt", H2)
+    ctx.aggregate([1], "rt", H1)
+    ctx.sync()
+    assert torch.equal(H2, H1)
