@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libclha.so"
 OK, ERR_INVALID_ARG, ERR_SHAPE, ERR_ALIGN, ERR_HIP, ERR_NOT_PD, ERR_NONFINITE, ERR_WORKSPACE = range(8)
 STATUS_NAMES = {0: "OK", 1: "INVALID_ARG", 2: "SHAPE", 3: "ALIGN", 4: "HIP", 5: "NOT_PD",
                 6: "NONFINITE", 7: "WORKSPACE"}
-ALPHA_MODES = {"rt": 0, "eq": 1, "explicit": 2}
+ALPHA_MODES = {"rt": 0, "eq": 1, "explicit": 2, "explicit_slot": 3}
 F32, BF16 = 0, 1
 
 EXPORTS = (
@@ -210,13 +210,18 @@ class Context:
             _ptr(token_ids_out), _ptr(ws), ws.numel(), _stream(stream)))
 
     def aggregate(self, layers: Sequence[int], mode: str, H_out: torch.Tensor,
-                  alpha: Optional[Sequence[float]] = None,
-                  alpha_out: Optional[torch.Tensor] = None, stream=None):
+                  alpha=None, alpha_out: Optional[torch.Tensor] = None, stream=None):
+        """alpha: host sequence of n_layers weights ('explicit'), or a device
+        float32 tensor [slots, n_layers] of per-slot weights ('explicit_slot')."""
         _check_dev("H_out", H_out, torch.float32, (self.slots, self.d, self.d), self.device)
         if alpha_out is not None:
             _check_dev("alpha_out", alpha_out, torch.float32, (self.slots, len(layers)), self.device)
         arr = (C.c_int32 * len(layers))(*layers)
-        al = None if alpha is None else (C.c_float * len(alpha))(*alpha)
+        if mode == "explicit_slot":
+            _check_dev("alpha", alpha, torch.float32, (self.slots, len(layers)), self.device)
+            al = C.cast(C.c_void_p(alpha.data_ptr()), C.POINTER(C.c_float))
+        else:
+            al = None if alpha is None else (C.c_float * len(alpha))(*alpha)
         self._raise(lib.clha_aggregate(self._h, len(layers), arr, ALPHA_MODES[mode], al,
                                        _ptr(H_out), _ptr(alpha_out), _stream(stream)))
 

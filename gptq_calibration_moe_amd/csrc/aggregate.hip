@@ -10,6 +10,8 @@
 // that form is used here.  Equal and explicit weights form sum_i a_i (S_i / n_i)
 // with separately rounded products and sums, in layer order, so that a = (1, 0)
 // returns S_a/n_a bit for bit and two identical layers return S/n bit for bit.
+// Any number of layers up to kMaxLayers combine the same way (Proposition 1 is
+// stated for n layers); explicit weights may also differ per expert slot.
 //
 // Each workgroup reads one 64x64 lower-triangular tile of every layer's S and
 // writes the tile and its mirror image, so H comes out full and symmetric.
@@ -45,11 +47,13 @@ __device__ SlotWeights slot_weights(const AggArgs& g, int slot) {
     const float a = 1.0f / (float)nonempty;
     for (int l = 0; l < g.n_layers; ++l) w.a[l] = n[l] > 0 ? a : 0.0f;
   } else {
+    // explicit weights: one set for every slot (mode 2) or one per slot (mode 3)
+    const float* al = g.mode == 3 ? g.alpha_slot + (int64_t)slot * g.n_layers : g.alpha;
     bool lost = false;
     float sum = 0.0f;
     for (int l = 0; l < g.n_layers; ++l) {
-      lost |= (g.alpha[l] != 0.0f) && n[l] == 0;
-      w.a[l] = n[l] > 0 ? g.alpha[l] : 0.0f;
+      lost |= (al[l] != 0.0f) && n[l] == 0;
+      w.a[l] = n[l] > 0 ? al[l] : 0.0f;
       sum += w.a[l];
     }
     if (lost) {

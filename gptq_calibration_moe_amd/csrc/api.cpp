@@ -448,8 +448,11 @@ CLHA_API clha_status clha_aggregate(clha_ctx* ctx, int32_t n_layers, const int32
   if (!ctx) return CLHA_ERR_INVALID_ARG;
   if (n_layers < 1 || n_layers > clha::kMaxLayers || !layers)
     return fail(ctx, CLHA_ERR_SHAPE, "aggregate: n_layers must be 1..%d", clha::kMaxLayers);
-  if (mode != CLHA_ALPHA_ROUTING_FREQ && mode != CLHA_ALPHA_EQUAL && mode != CLHA_ALPHA_EXPLICIT)
+  if (mode != CLHA_ALPHA_ROUTING_FREQ && mode != CLHA_ALPHA_EQUAL && mode != CLHA_ALPHA_EXPLICIT &&
+      mode != CLHA_ALPHA_EXPLICIT_PER_SLOT)
     return fail(ctx, CLHA_ERR_INVALID_ARG, "aggregate: unknown alpha mode %d", (int)mode);
+  if (mode == CLHA_ALPHA_EXPLICIT_PER_SLOT && (!alpha || !aligned4(alpha)))
+    return fail(ctx, CLHA_ERR_INVALID_ARG, "aggregate: per-slot mode needs a device alpha table");
   if (!H_out) return fail(ctx, CLHA_ERR_INVALID_ARG, "aggregate: null H_out");
   if (!aligned16(H_out) || (alpha_out && !aligned4(alpha_out)))
     return fail(ctx, CLHA_ERR_ALIGN, "aggregate: misaligned output");
@@ -475,6 +478,7 @@ CLHA_API clha_status clha_aggregate(clha_ctx* ctx, int32_t n_layers, const int32
   for (const auto& kv : ctx->layers)
     if (overlaps(H_out, hb, kv.second.S, hb))
       return fail(ctx, CLHA_ERR_INVALID_ARG, "aggregate: H_out overlaps layer %d's S", kv.first);
+  a.alpha_slot = mode == CLHA_ALPHA_EXPLICIT_PER_SLOT ? alpha : nullptr;
   a.n_layers = n_layers;
   a.mode = (int)mode;
   a.d = ctx->desc.d;

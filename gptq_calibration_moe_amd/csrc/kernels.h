@@ -69,6 +69,7 @@ struct AggArgs {
   const float* S[kMaxLayers];
   const int64_t* counts[kMaxLayers];
   float alpha[kMaxLayers];
+  const float* alpha_slot;   // per-slot explicit weights, device [slots][n_layers] (mode 3)
   int n_layers;
   int mode;              // clha_alpha_mode
   int d;

@@ -61,7 +61,9 @@ typedef enum clha_status {
 typedef enum clha_alpha_mode {
   CLHA_ALPHA_ROUTING_FREQ = 0, /* alpha_i = n_i / sum_j n_j ("CLHA-rt", section 2.2)      */
   CLHA_ALPHA_EQUAL = 1,        /* alpha_i = 1/m over the m non-empty layers ("CLHA-eq")    */
-  CLHA_ALPHA_EXPLICIT = 2      /* caller-given alpha_i; alpha = (1, 0) is PLIC (section 2.1) */
+  CLHA_ALPHA_EXPLICIT = 2,     /* caller-given alpha_i; alpha = (1, 0) is PLIC (section 2.1) */
+  CLHA_ALPHA_EXPLICIT_PER_SLOT = 3  /* caller-given alpha_i per expert slot (Proposition 1 holds
+                                       for each shared weight separately, section 2.1) */
 } clha_alpha_mode;
 
 typedef enum clha_dtype { CLHA_F32 = 0, CLHA_BF16 = 1 } clha_dtype;
@@ -146,9 +148,13 @@ CLHA_API clha_status clha_collect_hessians(clha_ctx* ctx, int32_t layer, int64_t
  *   EQUAL:        H[e] = sum_i (1/m) (S_i[e] / n_i[e]) over the m layers with n_i[e] > 0
  *   EXPLICIT:     H[e] = sum_i alpha_i (S_i[e] / n_i[e]); layers with n_i[e] == 0 drop out
  *                 and, if a dropped layer had alpha_i != 0, the rest are renormalised.
+ *   EXPLICIT_PER_SLOT: the same with weights alpha_i[e] of each slot.
  * A slot with no tokens in any layer gets H[e] = I and alpha 0.
  *   layers    host, int32 [n_layers]; registered layers; n_layers 1..8
- *   alpha     host, float [n_layers]; EXPLICIT only, else ignored (may be NULL)
+ *   alpha     EXPLICIT: host, float [n_layers], finite and >= 0.
+ *             EXPLICIT_PER_SLOT: device, float [slots][n_layers], finite and >= 0 (not
+ *             checked: it is read on the device; other values give undefined H).
+ *             Other modes: ignored (may be NULL).
  *   H_out     device, float [slots][d][d]; full symmetric matrices
  *   alpha_out device, float [slots][n_layers] (the weights used); may be NULL
  * Errors: INVALID_ARG, SHAPE, ALIGN. */

@@ -179,6 +179,24 @@ def test_proposition1_identity(mode):
         assert abs(lhs - rhs) <= 1e-12 * abs(lhs)
 
 
+@pytest.mark.parametrize("mode", ["rt", "eq", "explicit"])
+def test_proposition1_identity_three_layers(mode):
+    """Proposition 1 is stated for n layers: with three layers of different
+    sizes, sum_i alpha_i tr[D H_i D^T] = tr[D H_comb D^T] and the weights are
+    the token shares (rt), 1/3 (eq) or the given ones (explicit)."""
+    rng = _rng(15)
+    ns = [40, 130, 75]
+    S = [oracle.gram(rng.standard_normal((n, 10)) * (1 + i)) for i, n in enumerate(ns)]
+    given = [0.2, 0.5, 0.3]
+    H, a = oracle.aggregate(S, ns, mode, alpha=given if mode == "explicit" else None)
+    want = {"rt": [n / sum(ns) for n in ns], "eq": [1 / 3] * 3, "explicit": given}[mode]
+    np.testing.assert_allclose(a, want, rtol=1e-15)
+    for _ in range(5):
+        D = rng.standard_normal((6, 10))
+        lhs = sum(w * np.trace(D @ (Si / n) @ D.T) for w, Si, n in zip(want, S, ns))
+        assert abs(lhs - np.trace(D @ H @ D.T)) <= 1e-12 * abs(lhs)
+
+
 def test_plic_is_alpha_one():
     """alpha = 1 on the primary layer reduces exactly to PLIC = H_a (section 2.1)."""
     Sa, na, Sb, nb = _layers(11)
