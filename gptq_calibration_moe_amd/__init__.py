@@ -32,7 +32,7 @@ EXPORTS = (
     "clha_collect_workspace_bytes", "clha_collect_hessians", "clha_aggregate",
     "clha_gptq_workspace_bytes", "clha_gptq_quantize", "clha_inverse_cholesky_workspace_bytes",
     "clha_inverse_cholesky", "clha_loss_workspace_bytes", "clha_loss", "clha_set_timing",
-    "clha_read_timing", "clha_sync",
+    "clha_read_timing", "clha_sync", "clha_pack_codes", "clha_unpack_codes",
 )
 STAGES = ("route", "bucket", "gather", "syrk", "aggregate", "factor", "gptq", "loss")
 
@@ -67,6 +67,8 @@ def _load() -> C.CDLL:
         "clha_num_slots": ([vp], i32),
         "clha_register_layer": ([vp, i32, vp, vp], i32),
         "clha_reset_layer": ([vp, i32, vp], i32),
+        "clha_pack_codes": ([vp, i64, i32, vp, vp, vp], i32),
+        "clha_unpack_codes": ([vp, i64, i32, vp, vp, vp], i32),
         "clha_collect_workspace_bytes": ([vp], sz),
         "clha_collect_hessians": ([vp, i32, i64, vp, vp, vp, vp, vp, vp, sz, vp], i32),
         "clha_aggregate": ([vp, i32, C.POINTER(i32), i32, C.POINTER(f32), vp, vp, vp], i32),
@@ -185,6 +187,31 @@ class Context:
         """New accumulation for a registered layer: counts zeroed now, and the next
         collection with tokens overwrites S instead of adding (no clearing of S)."""
         self._raise(lib.clha_reset_layer(self._h, layer, _stream(stream)))
+
+    def pack_codes(self, codes: torch.Tensor, bits: int, out: Optional[torch.Tensor] = None,
+                   stream=None) -> torch.Tensor:
+        """b-bit packing of a uint8 code tensor (last dimension a multiple of 8):
+        returns uint8 [..., cols * bits / 8]."""
+        if codes.dtype != torch.uint8 or codes.device != self.device or not codes.is_contiguous():
+            raise ValueError("codes must be a contiguous uint8 tensor on the context's device")
+        if codes.shape[-1] % 8:
+            raise ValueError("the last dimension of codes must be a multiple of 8")
+        shape = (*codes.shape[:-1], codes.shape[-1] * bits // 8)
+        if out is None:
+            out = torch.empty(shape, dtype=torch.uint8, device=self.device)
+        _check_dev("packed", out, torch.uint8, shape, self.device)
+        self._raise(lib.clha_pack_codes(self._h, codes.numel(), bits, _ptr(codes), _ptr(out), _stream(stream)))
+        return out
+
+    def unpack_codes(self, packed: torch.Tensor, bits: int, cols: int, stream=None) -> torch.Tensor:
+        """Inverse of pack_codes: uint8 [..., cols] codes from [..., cols * bits / 8] bytes."""
+        if packed.dtype != torch.uint8 or packed.device != self.device or not packed.is_contiguous():
+            raise ValueError("packed must be a contiguous uint8 tensor on the context's device")
+        if cols % 8 or packed.shape[-1] != cols * bits // 8:
+            raise ValueError("cols must be a multiple of 8 and match the packed width")
+        out = torch.empty((*packed.shape[:-1], cols), dtype=torch.uint8, device=self.device)
+        self._raise(lib.clha_unpack_codes(self._h, out.numel(), bits, _ptr(packed), _ptr(out), _stream(stream)))
+        return out
 
     def collect_workspace_bytes(self) -> int:
         return lib.clha_collect_workspace_bytes(self._h)

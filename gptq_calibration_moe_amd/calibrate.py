@@ -90,3 +90,20 @@ class SharedGroupCalibration:
                          "bits": shared_bits if e >= self.ctx.n_routed else bits, **o})
         self.ctx.gptq_quantize(jobs, self.ctx.d, group, block, damp)
         return outputs
+
+
+def storage_bits(rows: int, cols: int, bits: int, group: int, scale_bits: int = 32, zero_bits: int = 8) -> int:
+    """Bits of one quantized matrix in packed storage: rows*cols codes of `bits`
+    bits plus one scale and one zero point per (row, group)."""
+    return rows * cols * bits + rows * (cols // group) * (scale_bits + zero_bits)
+
+
+def mixed_precision_overhead(jobs, group: int, scale_bits: int = 32, zero_bits: int = 8) -> dict:
+    """CLHA-MP accounting (section 2.3): `jobs` is a sequence of (rows, cols,
+    bits, base_bits); returns the packed bits per parameter with each job at its
+    own width, the same at every job's base width, and the relative overhead."""
+    params = sum(r * c for r, c, _, _ in jobs)
+    mixed = sum(storage_bits(r, c, b, group, scale_bits, zero_bits) for r, c, b, _ in jobs)
+    base = sum(storage_bits(r, c, b0, group, scale_bits, zero_bits) for r, c, _, b0 in jobs)
+    return {"bits_per_param": mixed / params, "base_bits_per_param": base / params,
+            "overhead": mixed / base - 1.0}

@@ -783,4 +783,34 @@ CLHA_API clha_status clha_sync(clha_ctx* ctx, void* stream) {
   return fail(ctx, CLHA_ERR_NOT_PD, "a damped Hessian is not positive definite");
 }
 
+static clha_status check_pack(clha_ctx* ctx, const char* what, int64_t n_codes, int32_t bits, const void* a,
+                              const void* b) {
+  if (n_codes < 0 || n_codes % 8 != 0)
+    return fail(ctx, CLHA_ERR_SHAPE, "%s: n_codes %lld must be a multiple of 8", what, (long long)n_codes);
+  if (bits < 2 || bits > 8) return fail(ctx, CLHA_ERR_SHAPE, "%s: bits %d outside 2..8", what, bits);
+  if (n_codes == 0) return CLHA_OK;
+  if (!a || !b) return fail(ctx, CLHA_ERR_INVALID_ARG, "%s: null pointer", what);
+  return CLHA_OK;
+}
+
+CLHA_API clha_status clha_pack_codes(clha_ctx* ctx, int64_t n_codes, int32_t bits, const uint8_t* codes,
+                                     uint8_t* packed, void* stream) {
+  if (!ctx) return CLHA_ERR_INVALID_ARG;
+  const clha_status st = check_pack(ctx, "pack_codes", n_codes, bits, codes, packed);
+  if (st != CLHA_OK || n_codes == 0) return st;
+  if (!aligned16(codes)) return fail(ctx, CLHA_ERR_ALIGN, "pack_codes: codes not 16-byte aligned");
+  clha::launch_pack_codes(codes, packed, n_codes, bits, as_stream(stream));
+  return hip_check(ctx, "pack_codes");
+}
+
+CLHA_API clha_status clha_unpack_codes(clha_ctx* ctx, int64_t n_codes, int32_t bits, const uint8_t* packed,
+                                       uint8_t* codes, void* stream) {
+  if (!ctx) return CLHA_ERR_INVALID_ARG;
+  const clha_status st = check_pack(ctx, "unpack_codes", n_codes, bits, packed, codes);
+  if (st != CLHA_OK || n_codes == 0) return st;
+  if (!aligned16(codes)) return fail(ctx, CLHA_ERR_ALIGN, "unpack_codes: codes not 16-byte aligned");
+  clha::launch_unpack_codes(packed, codes, n_codes, bits, as_stream(stream));
+  return hip_check(ctx, "unpack_codes");
+}
+
 }  // extern "C"

@@ -129,4 +129,8 @@ void launch_loss(int rows, int cols, int group, const void* W, int dtype, const 
                  float* loss_out, hipStream_t s);
 int64_t loss_partial_count(int rows, int cols);
 
+// ---------------------------------------------------------------- packed codes
+void launch_pack_codes(const uint8_t* codes, uint8_t* packed, int64_t n_codes, int bits, hipStream_t s);
+void launch_unpack_codes(const uint8_t* packed, uint8_t* codes, int64_t n_codes, int bits, hipStream_t s);
+
 }  // namespace clha

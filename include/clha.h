@@ -238,6 +238,24 @@ CLHA_API clha_status clha_loss(clha_ctx* ctx, int32_t rows, int32_t cols, int32_
                                float* loss_out, void* workspace, size_t workspace_bytes,
                                void* stream);
 
+/* Packed storage of codes at b bits (section 2.3, CLHA-MP: routed experts at b bits,
+ * shared ones at b+1).  Code j of the stream occupies bits j*b .. j*b+b-1 of a
+ * little-endian bit stream (bit 0 = least significant bit of byte 0); n_codes codes
+ * take n_codes*b/8 bytes.  A [rows][cols] code matrix with cols a multiple of 8 packs
+ * row by row into [rows][cols*b/8].
+ *   n_codes  multiple of 8, >= 0 (0 enqueues nothing and reads no pointer)
+ *   bits     2..8; codes must lie in 0 .. 2^bits - 1 (GPTQ's codes do); higher bits
+ *            of a code are dropped
+ *   codes    device uint8 [n_codes], 16-byte aligned
+ *   packed   device uint8 [n_codes*bits/8]
+ * Errors: INVALID_ARG (null pointer), SHAPE (n_codes or bits), ALIGN, HIP. */
+CLHA_API clha_status clha_pack_codes(clha_ctx* ctx, int64_t n_codes, int32_t bits, const uint8_t* codes,
+                                     uint8_t* packed, void* stream);
+
+/* The inverse of clha_pack_codes: codes[j] = bits j*b .. j*b+b-1 of the stream. */
+CLHA_API clha_status clha_unpack_codes(clha_ctx* ctx, int64_t n_codes, int32_t bits, const uint8_t* packed,
+                                       uint8_t* codes, void* stream);
+
 /* Stages timed by the optional per-stage timers. */
 typedef enum clha_stage {
   CLHA_STAGE_ROUTE = 0,      /* top-K routing kernel */

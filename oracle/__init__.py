@@ -276,6 +276,23 @@ def gptq(w, H, bits: int, group: int, damp: float = 0.01, block: int = 128) -> d
             "wq": wq, "dead": dead, "lam": lam, "U": U}
 
 
+def pack_codes(codes, bits: int) -> np.ndarray:
+    """b-bit packed storage of a flat code stream (CLHA section 2.3 stores
+    shared experts at b+1 bits, routed ones at b): code j contributes its bits,
+    least significant first, at positions j*b .. j*b+b-1 of a bit stream whose
+    bit 0 is the least significant bit of byte 0."""
+    c = np.asarray(codes, dtype=np.int64).ravel()
+    stream = ((c[:, None] >> np.arange(bits)[None, :]) & 1).ravel().astype(np.uint8)
+    return np.packbits(stream, bitorder="little")
+
+
+def unpack_codes(packed, bits: int, n: int) -> np.ndarray:
+    """Inverse of pack_codes: the first n codes of the stream."""
+    stream = np.unpackbits(np.asarray(packed, dtype=np.uint8), bitorder="little")[: n * bits]
+    w = (1 << np.arange(bits)).astype(np.int64)
+    return (stream.reshape(n, bits).astype(np.int64) @ w).astype(np.uint8)
+
+
 def loss(w, wq, H) -> float:
     """tr[(W_q - W) H (W_q - W)^T] = sum over rows of delta_r H delta_r^T
     (CLHA section 2.1 objective for one layer term)."""

@@ -529,3 +529,36 @@ def test_planted_route_mistake_is_caught():
                   "np.lexsort((-key_idx, -lg.astype(np.float64)), axis=-1)")     # ties to the higher index
     g = json.load(open(os.path.join(GOLDEN, "route_small.json")))
     assert bad(np.array(g["logits"], np.float32), g["k"]).tolist() != g["topk"]
+
+
+# =========================================================================== packed storage
+
+def test_pack_codes_hand_example():
+    """Section 2.3 stores codes at b (or b+1) bits.  Worked by hand, bits least
+    significant first: 3-bit codes 1,2,3,4,5,6,7,0 are the stream
+    100 010 110 001 101 011 111 000, i.e. bytes 10001011 00011010 11111000
+    read from bit 0 up: 1+16+64+128 = 209, 8+16+64 = 88, 1+2+4+8+16 = 31.
+    2-bit codes 0,1,2,3: stream 00 10 01 11 -> 4+32+64+128 = 228."""
+    assert oracle.pack_codes([1, 2, 3, 4, 5, 6, 7, 0], 3).tolist() == [209, 88, 31]
+    assert oracle.pack_codes([0, 1, 2, 3], 2).tolist() == [228]
+    assert oracle.pack_codes([255] * 8, 8).tolist() == [255] * 8
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 7, 8])
+def test_pack_codes_round_trip_and_size(bits):
+    codes = _rng(40 + bits).integers(0, 1 << bits, 8 * 37)
+    packed = oracle.pack_codes(codes, bits)
+    assert packed.size == codes.size * bits // 8
+    assert np.array_equal(oracle.unpack_codes(packed, bits, codes.size), codes)
+
+
+def test_mixed_precision_accounting():
+    """Packed bits per parameter: b + (32 + 8)/g; shared experts at b+1 raise the
+    total by their share of the parameters (section 2.3)."""
+    from gptq_calibration_moe_amd.calibrate import mixed_precision_overhead, storage_bits
+    assert storage_bits(2, 256, 3, 128) == 2 * 256 * 3 + 2 * 2 * 40
+    jobs = [(1408, 2048, 3, 3)] * 64 + [(1408, 2048, 4, 3)] * 2
+    r = mixed_precision_overhead(jobs, 128)
+    assert abs(r["base_bits_per_param"] - (3 + 40 / 128)) < 1e-12
+    assert abs(r["bits_per_param"] - (3 + 40 / 128 + 2 / 66)) < 1e-12
+    assert abs(r["overhead"] - (2 / 66) / (3 + 40 / 128)) < 1e-12
