@@ -247,6 +247,13 @@ def pair_inputs(wl: Workload, pair: int = 0, t: Optional[float] = None,
     return {"x": [xa, xb], "logits": [la, lb]}
 
 
+def swiglu_weights(seed: int, slots: int, f: int, d: int, scale: float = 0.02) -> list:
+    """Gate and up weights of `slots` experts, each [2f, d] bf16 bits: rows 0..f-1
+    gate, rows f..2f-1 up, N(0, scale^2) (the configs' N(0, 0.02))."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed)))
+    return [bf16_bits(_normal_f32(rng, (2 * f, d), scale)) for _ in range(slots)]
+
+
 def structured_activations(seed: int, n: int, d: int, log_spread: float = 3.0,
                            dead_cols=()) -> np.ndarray:
     """Correlated activations X = Z diag(s) Q (s log-uniform over 10^[-spread/2, spread/2]),

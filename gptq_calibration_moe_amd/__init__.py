@@ -33,6 +33,7 @@ EXPORTS = (
     "clha_gptq_workspace_bytes", "clha_gptq_quantize", "clha_inverse_cholesky_workspace_bytes",
     "clha_inverse_cholesky", "clha_loss_workspace_bytes", "clha_loss", "clha_set_timing",
     "clha_read_timing", "clha_sync", "clha_pack_codes", "clha_unpack_codes",
+    "clha_down_workspace_bytes", "clha_collect_down_hessians",
 )
 STAGES = ("route", "bucket", "gather", "syrk", "aggregate", "factor", "gptq", "loss")
 
@@ -68,6 +69,8 @@ def _load() -> C.CDLL:
         "clha_register_layer": ([vp, i32, vp, vp], i32),
         "clha_reset_layer": ([vp, i32, vp], i32),
         "clha_pack_codes": ([vp, i64, i32, vp, vp, vp], i32),
+        "clha_down_workspace_bytes": ([vp, i32], sz),
+        "clha_collect_down_hessians": ([vp, i32, i64, i32, i32, vp, vp, vp, vp, vp, sz, vp], i32),
         "clha_unpack_codes": ([vp, i64, i32, vp, vp, vp], i32),
         "clha_collect_workspace_bytes": ([vp], sz),
         "clha_collect_hessians": ([vp, i32, i64, vp, vp, vp, vp, vp, vp, sz, vp], i32),
@@ -187,6 +190,28 @@ class Context:
         """New accumulation for a registered layer: counts zeroed now, and the next
         collection with tokens overwrites S instead of adding (no clearing of S)."""
         self._raise(lib.clha_reset_layer(self._h, layer, _stream(stream)))
+
+    def collect_down_hessians(self, layer: int, x: torch.Tensor, token_ids: torch.Tensor,
+                              offsets: torch.Tensor, wgu: Sequence[torch.Tensor], n_routed: int,
+                              workspace: Optional[torch.Tensor] = None, stream=None):
+        """down_proj inputs of one layer on a down_proj context (d = f, one slot per
+        routed and per shared expert, no shared slot): h = bf16(silu(x Wg^T) * (x Wu^T))
+        per slot, over the routing (token_ids, offsets) of the same batch on the block's
+        main context for routed slots and all tokens for the shared ones; S[slot] += h^T h."""
+        n, dm = x.shape
+        _check_dev("x", x, (torch.bfloat16, torch.int16, torch.uint16), (n, dm), self.device)
+        if len(wgu) != self.slots:
+            raise ValueError(f"wgu needs one [2f, d_model] weight per slot ({self.slots})")
+        for w in wgu:
+            _check_dev("wgu", w, (torch.bfloat16, torch.int16, torch.uint16), (2 * self.d, dm), self.device)
+        _check_dev("token_ids", token_ids, torch.int32, (token_ids.numel(),), self.device)
+        _check_dev("offsets", offsets, torch.int64, (n_routed + 1,), self.device)
+        need = lib.clha_down_workspace_bytes(self._h, n_routed)
+        ws = workspace if workspace is not None else self.workspace("down", need)
+        table = (C.c_void_p * len(wgu))(*[w.data_ptr() for w in wgu])
+        self._raise(lib.clha_collect_down_hessians(
+            self._h, layer, n, dm, n_routed, _ptr(x), _ptr(token_ids), _ptr(offsets), table,
+            _ptr(ws), ws.numel(), _stream(stream)))
 
     def pack_codes(self, codes: torch.Tensor, bits: int, out: Optional[torch.Tensor] = None,
                    stream=None) -> torch.Tensor:

@@ -207,6 +207,47 @@ CollectLayout collect_layout(const clha_ctx* ctx, void* ws) {
   return L;
 }
 
+// ---------------------------------------------------------------- down_proj layout
+// The down_proj context has d = f (the intermediate size) and one slot per
+// routed expert and per shared expert; its collection reads the model-width
+// activations through the routing of the block's main context.
+struct DownLayout {
+  const uint16_t** wgu;
+  int64_t* pad_off;
+  int32_t* slot_order;
+  int32_t* tile_off;
+  int32_t* work;
+  int32_t* work_len;
+  int32_t* work_next;
+  int32_t* seg;
+  int32_t* split;
+  float* partials;
+  uint16_t* hT;
+  size_t bytes;
+};
+
+DownLayout down_layout(const clha_ctx* ctx, int n_routed, void* ws) {
+  const clha_moe_desc& d = ctx->desc;
+  const int64_t n = d.max_tokens;
+  const int slots = ctx->slots;
+  const int64_t h_tokens = n * d.top_k + (int64_t)(slots - n_routed) * n + (int64_t)clha::kTokPad * slots;
+  Carver c(ws);
+  DownLayout L;
+  L.wgu = c.take<const uint16_t*>((size_t)slots);
+  L.pad_off = c.take<int64_t>((size_t)slots + 1);
+  L.slot_order = c.take<int32_t>((size_t)slots);
+  L.tile_off = c.take<int32_t>((size_t)slots + 1);
+  L.work = c.take<int32_t>((size_t)clha::kXcds * clha::kMaxSegs * clha::syrk_items_per_slot(d.d));
+  L.work_len = c.take<int32_t>(clha::kXcds);
+  L.work_next = c.take<int32_t>(clha::kXcds);
+  L.seg = c.take<int32_t>((size_t)4 * clha::kMaxSegs);
+  L.split = c.take<int32_t>((size_t)1 + 3 * clha::kMaxPartials);
+  L.partials = c.take<float>((size_t)clha::kMaxPartials * d.d * d.d);
+  L.hT = c.take<uint16_t>((size_t)h_tokens * d.d);
+  L.bytes = c.off;
+  return L;
+}
+
 // ---------------------------------------------------------------- GPTQ layout
 struct GptqLayout {
   GJob* jobs;
@@ -811,6 +852,84 @@ CLHA_API clha_status clha_unpack_codes(clha_ctx* ctx, int64_t n_codes, int32_t b
   if (!aligned16(codes)) return fail(ctx, CLHA_ERR_ALIGN, "unpack_codes: codes not 16-byte aligned");
   clha::launch_unpack_codes(packed, codes, n_codes, bits, as_stream(stream));
   return hip_check(ctx, "unpack_codes");
+}
+
+CLHA_API size_t clha_down_workspace_bytes(const clha_ctx* ctx, int32_t n_routed) {
+  if (!ctx || n_routed < 1 || n_routed > ctx->slots) return 0;
+  return down_layout(ctx, n_routed, nullptr).bytes;
+}
+
+CLHA_API clha_status clha_collect_down_hessians(clha_ctx* ctx, int32_t layer, int64_t n_tokens, int32_t d_model,
+                                                int32_t n_routed, const uint16_t* x, const int32_t* token_ids,
+                                                const int64_t* offsets, const uint16_t* const* wgu,
+                                                void* workspace, size_t workspace_bytes, void* stream) {
+  if (!ctx) return CLHA_ERR_INVALID_ARG;
+  auto it = ctx->layers.find(layer);
+  if (it == ctx->layers.end())
+    return fail(ctx, CLHA_ERR_INVALID_ARG, "collect_down_hessians: layer %d is not registered", layer);
+  const clha_moe_desc& d = ctx->desc;
+  if (d.n_shared != 0)
+    return fail(ctx, CLHA_ERR_INVALID_ARG, "collect_down_hessians: a down_proj context has no shared slot "
+                "(one slot per routed and per shared expert)");
+  if (n_routed < 1 || n_routed > ctx->slots)
+    return fail(ctx, CLHA_ERR_SHAPE, "collect_down_hessians: n_routed %d outside 1..%d", n_routed, ctx->slots);
+  if (d_model < 64 || d_model > 8192 || d_model % 64 != 0)
+    return fail(ctx, CLHA_ERR_SHAPE, "collect_down_hessians: d_model %d must be a multiple of 64, <= 8192", d_model);
+  if (n_tokens < 0 || n_tokens > d.max_tokens)
+    return fail(ctx, CLHA_ERR_SHAPE, "collect_down_hessians: n_tokens %lld outside 0..%lld",
+                (long long)n_tokens, (long long)d.max_tokens);
+  if (n_tokens == 0) return CLHA_OK;   // an empty batch adds nothing; its pointers are not read
+  if (!x || !token_ids || !offsets || !wgu || !workspace)
+    return fail(ctx, CLHA_ERR_INVALID_ARG, "collect_down_hessians: null pointer");
+  if (!aligned16(x) || !aligned4(token_ids) || !aligned16(offsets) || !aligned16(workspace))
+    return fail(ctx, CLHA_ERR_ALIGN, "collect_down_hessians: misaligned pointer");
+  for (int e = 0; e < ctx->slots; ++e)
+    if (!wgu[e] || !aligned16(wgu[e]))
+      return fail(ctx, CLHA_ERR_ALIGN, "collect_down_hessians: weights of slot %d null or misaligned", e);
+  const DownLayout need = down_layout(ctx, n_routed, nullptr);
+  if (workspace_bytes < need.bytes)
+    return fail(ctx, CLHA_ERR_WORKSPACE, "collect_down_hessians: workspace %zu < %zu bytes", workspace_bytes,
+                need.bytes);
+  const DownLayout L = down_layout(ctx, n_routed, workspace);
+  const hipStream_t s = as_stream(stream);
+  clha_status st = stage_to_device(ctx, L.wgu, wgu, sizeof(const uint16_t*) * ctx->slots, s);
+  if (st != CLHA_OK) return st;
+  CollectPlan p;
+  std::memset(&p, 0, sizeof p);
+  p.n_tokens = n_tokens;
+  p.d = d.d;
+  p.E = ctx->slots;
+  p.K = d.top_k;
+  p.has_shared = 0;
+  p.pad_off = L.pad_off;
+  p.slot_order = L.slot_order;
+  p.work = L.work;
+  p.work_len = L.work_len;
+  p.work_next = L.work_next;
+  p.seg = L.seg;
+  p.split = L.split;
+  p.partials = L.partials;
+  p.syrk_items = clha::syrk_items_per_slot(d.d);
+  p.overwrite = it->second.fresh ? 1 : 0;
+  p.xgT = L.hT;
+  p.status = ctx->status_dev;
+  // token tiles of 128 over all slots, at most one partial tile per slot
+  const int64_t max_tiles = (n_tokens * d.top_k + (int64_t)(ctx->slots - n_routed) * n_tokens +
+                             (int64_t)clha::kTokPad * ctx->slots) / 128 + ctx->slots + 1;
+  {
+    StageTimer t(ctx, CLHA_STAGE_BUCKET, s);
+    clha::launch_down_scan(offsets, n_tokens, n_routed, p, it->second.counts, L.tile_off, s);
+  }
+  {
+    StageTimer t(ctx, CLHA_STAGE_GATHER, s);
+    clha::launch_down_gemm(x, d_model, token_ids, offsets, n_routed, n_tokens, L.wgu, p, L.tile_off, max_tiles, s);
+  }
+  {
+    StageTimer t(ctx, CLHA_STAGE_SYRK, s);
+    clha::launch_syrk(p, it->second.S, it->second.counts, s);
+  }
+  it->second.fresh = false;
+  return hip_check(ctx, "collect_down_hessians");
 }
 
 }  // extern "C"

@@ -17,6 +17,7 @@ constexpr int kMaxTopK = 16;
 constexpr int kMaxLayers = 8;
 constexpr int kSyrkTile = 256;        // Gram-sum output tile
 constexpr int kMaxPartials = 8;       // partial Gram-sum buffers of token-split slots
+constexpr int kMaxSlots = kMaxExperts + 1;                // Hessian slots of one layer
 constexpr int kMaxSegs = kMaxExperts + 1 + kMaxPartials;   // Gram-sum segments per call
 constexpr int kXcds = 8;              // accelerator complex dies; workgroup b runs on die b % 8
 constexpr int kSyrkWgPerXcd = 32;     // persistent Gram-sum workgroups per die (one per CU)
@@ -61,6 +62,13 @@ void launch_route(const float* logits, const CollectPlan& p, hipStream_t s);
 void launch_bucket(const CollectPlan& p, int64_t* layer_counts, hipStream_t s);
 void launch_gather(const uint16_t* x, const CollectPlan& p, hipStream_t s);
 void launch_syrk(const CollectPlan& p, float* S, const int64_t* layer_counts, hipStream_t s);
+// down_proj inputs: plan from a layer's routing, and the grouped SwiGLU GEMM
+// writing each slot's h^T (feature-major, like the gathered activations)
+void launch_down_scan(const int64_t* routed_offsets, int64_t n, int E, const CollectPlan& p,
+                      int64_t* layer_counts, int32_t* tile_off, hipStream_t s);
+void launch_down_gemm(const uint16_t* x, int d_model, const int32_t* token_ids, const int64_t* routed_offsets,
+                      int E, int64_t n, const uint16_t* const* wgu, const CollectPlan& p, const int32_t* tile_off,
+                      int64_t max_tiles, hipStream_t s);
 void launch_zero_counts(int64_t* counts, int n, hipStream_t s);
 int syrk_items_per_slot(int d);
 

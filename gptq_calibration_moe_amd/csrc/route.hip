@@ -109,69 +109,51 @@ __global__ __launch_bounds__(256) void bucket_count_kernel(const int32_t* __rest
   }
 }
 
-// One workgroup: per-expert exclusive scan over bucketing workgroups, expert
-// offsets, padded slot offsets, the longest-first slot order used by the Gram
-// kernel, and the layer's running token counts.
-__global__ __launch_bounds__(256) void bucket_scan_kernel(
-    const int32_t* __restrict__ blockcounts, int nblk, int64_t n, int E, int has_shared,
-    int32_t* __restrict__ blockbase, int64_t* __restrict__ offsets, int64_t* __restrict__ pad_off,
-    int32_t* __restrict__ slot_order, int64_t* __restrict__ layer_counts, int overwrite, int items,
-    int32_t* __restrict__ work, int32_t* __restrict__ work_len, int32_t* __restrict__ work_next,
-    int32_t* __restrict__ seg, int32_t* __restrict__ split) {
-  __shared__ int64_t cnt[kMaxExperts + 1];
-  __shared__ int64_t padc[kMaxExperts + 1];
-  __shared__ int32_t order[kMaxExperts + 1];
-  __shared__ int32_t seg_x[kMaxSegs];      // XCD of each segment
-  __shared__ int32_t seg_pos[kMaxSegs];    // first list position of its items
-  __shared__ int32_t nseg_s;
-  const int slots = E + has_shared;
-  for (int e = threadIdx.x; e < E; e += 256) {
-    int64_t run = 0;
-    for (int b = 0; b < nblk; ++b) {
-      const int c = blockcounts[(int64_t)b * E + e];
-      blockbase[(int64_t)b * E + e] = (int32_t)run;
-      run += c;
-    }
-    cnt[e] = run;
-  }
-  if (threadIdx.x == 0 && has_shared) cnt[E] = n;
-  __syncthreads();
-  for (int e = threadIdx.x; e < slots; e += 256) {
-    padc[e] = (cnt[e] + kTokPad - 1) / kTokPad * kTokPad;
+// Gram-sum plan of `slots` slots whose token counts are in cnt[] (LDS, complete
+// before the call; every thread of the workgroup calls this): padded counts,
+// padded slot offsets, the longest-first slot order, the layer's running token
+// counts, and the per-XCD Gram-sum work lists.  A segment is a token range of
+// one slot; every item of a segment reads the same activations, so a segment
+// stays on one XCD and its items are consecutive in the list.  Slots far
+// longer than the average XCD share are split into up to 8 token ranges (the
+// parts after the first go to partial buffers, added back in part order
+// afterwards).  Longest slots first, each segment onto the least-loaded XCD.
+struct PlanLds {
+  int64_t padc[kMaxSlots];
+  int32_t order[kMaxSlots];
+  int32_t seg_x[kMaxSegs];      // XCD of each segment
+  int32_t seg_pos[kMaxSegs];    // first list position of its items
+  int32_t nseg;
+};
+
+__device__ void plan_gram(const int64_t* cnt, PlanLds& L, int slots, int64_t* __restrict__ pad_off,
+                          int32_t* __restrict__ slot_order, int64_t* __restrict__ layer_counts, int overwrite,
+                          int items, int32_t* __restrict__ work, int32_t* __restrict__ work_len,
+                          int32_t* __restrict__ work_next, int32_t* __restrict__ seg, int32_t* __restrict__ split) {
+  for (int e = threadIdx.x; e < slots; e += blockDim.x) {
+    L.padc[e] = (cnt[e] + kTokPad - 1) / kTokPad * kTokPad;
     if (layer_counts) layer_counts[e] = overwrite ? cnt[e] : layer_counts[e] + cnt[e];
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    int64_t o = 0, po = 0;
-    for (int e = 0; e < E; ++e) {
-      offsets[e] = o;
-      o += cnt[e];
-    }
-    offsets[E] = o;
+    int64_t po = 0;
     for (int e = 0; e < slots; ++e) {
       pad_off[e] = po;
-      po += padc[e];
+      po += L.padc[e];
     }
     pad_off[slots] = po;
   }
   // rank of each slot by (padded length descending, slot ascending)
-  for (int e = threadIdx.x; e < slots; e += 256) {
+  for (int e = threadIdx.x; e < slots; e += blockDim.x) {
     int r = 0;
-    for (int o = 0; o < slots; ++o) r += (padc[o] > padc[e]) || (padc[o] == padc[e] && o < e);
+    for (int o = 0; o < slots; ++o) r += (L.padc[o] > L.padc[e]) || (L.padc[o] == L.padc[e] && o < e);
     slot_order[r] = e;
-    order[r] = e;
+    L.order[r] = e;
   }
   __syncthreads();
-  // Gram-sum work lists, one per XCD (each XCD has its own L2).  A segment is
-  // a token range of one slot; every item of a segment reads the same
-  // activations, so a segment stays on one XCD and its items are consecutive
-  // in the list, the diagonal-pair items first.  Slots far longer than the
-  // average XCD share are split into up to 8 token ranges (the parts after the
-  // first go to partial buffers, added back in part order afterwards).
-  // Longest slots first, each segment onto the least-loaded XCD.
   if (threadIdx.x == 0) {
     int64_t total = 0;
-    for (int e = 0; e < slots; ++e) total += padc[e];
+    for (int e = 0; e < slots; ++e) total += L.padc[e];
     const int64_t target = ((total / (8 * kXcds)) / kTokPad + 1) * kTokPad;
     int64_t load[kXcds];
     int32_t len[kXcds];
@@ -181,10 +163,10 @@ __global__ __launch_bounds__(256) void bucket_scan_kernel(
     }
     int nseg = 0, nsplit = 0, used = 0;
     for (int r = 0; r < slots; ++r) {
-      const int e = order[r];
-      const int64_t chunks = padc[e] / kTokPad;
+      const int e = L.order[r];
+      const int64_t chunks = L.padc[e] / kTokPad;
       if (chunks == 0) continue;
-      int64_t k = (padc[e] + target - 1) / target;
+      int64_t k = (L.padc[e] + target - 1) / target;
       k = k < kXcds ? k : kXcds;
       k = k < 1 + kMaxPartials - used ? k : 1 + kMaxPartials - used;
       k = k < chunks ? k : chunks;
@@ -203,8 +185,8 @@ __global__ __launch_bounds__(256) void bucket_scan_kernel(
         seg[4 * nseg + 3] = (int32_t)(nc * kTokPad);
         int best = 0;
         for (int x = 1; x < kXcds; ++x) best = load[x] < load[best] ? x : best;
-        seg_x[nseg] = best;
-        seg_pos[nseg] = len[best];
+        L.seg_x[nseg] = best;
+        L.seg_pos[nseg] = len[best];
         len[best] += items;
         load[best] += nc;
         b += nc;
@@ -213,7 +195,7 @@ __global__ __launch_bounds__(256) void bucket_scan_kernel(
       used += (int)k - 1;
     }
     split[0] = nsplit;
-    nseg_s = nseg;
+    L.nseg = nseg;
     for (int x = 0; x < kXcds; ++x) {
       work_len[x] = len[x];
       work_next[x] = 0;
@@ -221,10 +203,78 @@ __global__ __launch_bounds__(256) void bucket_scan_kernel(
   }
   __syncthreads();
   const int cap = kMaxSegs * items;
-  for (int it = threadIdx.x; it < nseg_s * items; it += 256) {
+  for (int it = threadIdx.x; it < L.nseg * items; it += blockDim.x) {
     const int sg = it / items, t = it - sg * items;
-    work[seg_x[sg] * cap + seg_pos[sg] + t] = sg * 1024 + t;
+    work[L.seg_x[sg] * cap + L.seg_pos[sg] + t] = sg * 1024 + t;
   }
+}
+
+// One workgroup: per-expert exclusive scan over bucketing workgroups, expert
+// offsets, then the Gram-sum plan of the layer's slots (routed experts, and the
+// shared-expert slot with all tokens).
+__global__ __launch_bounds__(256) void bucket_scan_kernel(
+    const int32_t* __restrict__ blockcounts, int nblk, int64_t n, int E, int has_shared,
+    int32_t* __restrict__ blockbase, int64_t* __restrict__ offsets, int64_t* __restrict__ pad_off,
+    int32_t* __restrict__ slot_order, int64_t* __restrict__ layer_counts, int overwrite, int items,
+    int32_t* __restrict__ work, int32_t* __restrict__ work_len, int32_t* __restrict__ work_next,
+    int32_t* __restrict__ seg, int32_t* __restrict__ split) {
+  __shared__ int64_t cnt[kMaxSlots];
+  __shared__ PlanLds L;
+  const int slots = E + has_shared;
+  for (int e = threadIdx.x; e < E; e += 256) {
+    int64_t run = 0;
+    for (int b = 0; b < nblk; ++b) {
+      const int c = blockcounts[(int64_t)b * E + e];
+      blockbase[(int64_t)b * E + e] = (int32_t)run;
+      run += c;
+    }
+    cnt[e] = run;
+  }
+  if (threadIdx.x == 0 && has_shared) cnt[E] = n;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int64_t o = 0;
+    for (int e = 0; e < E; ++e) {
+      offsets[e] = o;
+      o += cnt[e];
+    }
+    offsets[E] = o;
+  }
+  plan_gram(cnt, L, slots, pad_off, slot_order, layer_counts, overwrite, items, work, work_len, work_next, seg,
+            split);
+}
+
+// Plan of the down_proj inputs of one layer: slot e < E takes expert e's routed
+// tokens (offsets of the layer's routing), every slot from E on (one per shared
+// expert) all n tokens; then the Gram-sum plan, and the grouped GEMM's tile
+// offsets: ceil(padded count / 128) token tiles per slot.
+__global__ __launch_bounds__(256) void down_scan_kernel(
+    const int64_t* __restrict__ routed_offsets, int64_t n, int E, int slots, int64_t* __restrict__ pad_off,
+    int32_t* __restrict__ slot_order, int64_t* __restrict__ layer_counts, int overwrite, int items,
+    int32_t* __restrict__ work, int32_t* __restrict__ work_len, int32_t* __restrict__ work_next,
+    int32_t* __restrict__ seg, int32_t* __restrict__ split, int32_t* __restrict__ tile_off) {
+  __shared__ int64_t cnt[kMaxSlots];
+  __shared__ PlanLds L;
+  for (int e = threadIdx.x; e < slots; e += 256)
+    cnt[e] = e < E ? routed_offsets[e + 1] - routed_offsets[e] : n;
+  __syncthreads();
+  plan_gram(cnt, L, slots, pad_off, slot_order, layer_counts, overwrite, items, work, work_len, work_next, seg,
+            split);
+  if (threadIdx.x == 0) {
+    int32_t t = 0;
+    for (int e = 0; e < slots; ++e) {
+      tile_off[e] = t;
+      t += (int32_t)((L.padc[e] + 127) / 128);
+    }
+    tile_off[slots] = t;
+  }
+}
+
+void launch_down_scan(const int64_t* routed_offsets, int64_t n, int E, const CollectPlan& p,
+                      int64_t* layer_counts, int32_t* tile_off, hipStream_t s) {
+  hipLaunchKernelGGL(down_scan_kernel, dim3(1), dim3(256), 0, s, routed_offsets, n, E, p.E, p.pad_off,
+                     p.slot_order, layer_counts, p.overwrite, p.syrk_items, p.work, p.work_len, p.work_next,
+                     p.seg, p.split, tile_off);
 }
 
 __global__ __launch_bounds__(256) void bucket_scatter_kernel(

@@ -238,6 +238,36 @@ CLHA_API clha_status clha_loss(clha_ctx* ctx, int32_t rows, int32_t cols, int32_
                                float* loss_out, void* workspace, size_t workspace_bytes,
                                void* stream);
 
+/* Inputs of the experts' second matrix (down_proj).  Section 2.2 collects the Hessian
+ * of every shared weight over that weight's own input; the input of an expert's
+ * down_proj is its SwiGLU intermediate
+ *   h = bf16( silu(x Wg^T) * (x Wu^T) ),  silu(g) = g / (1 + e^-g)
+ * from the full-precision gate and up weights.  Each routed expert (over its routed
+ * tokens) and each shared expert (over all tokens, with its own weights) has its own
+ * down_proj Hessian, so these run on a separate "down_proj context":
+ *   desc.d = f (intermediate size, multiple of 128), desc.n_routed = routed + shared
+ *   experts (one slot each), desc.n_shared = 0, desc.top_k and max_tokens as the block's.
+ * Its layers are registered, reset, aggregated and quantized like any other
+ * (clha_register_layer, clha_aggregate, clha_gptq_quantize with cols = f).
+ *   n_routed  the block's routed experts E: slots 0..E-1 are routed, E.. shared
+ *   x         device bf16 bits [n_tokens][d_model], the layer's model-width activations
+ *   token_ids, offsets  device, the routing of this batch on the block's main context
+ *             (the token_ids_out / offsets_out of clha_collect_hessians: int32 [n*K],
+ *             int64 [E+1])
+ *   wgu       host array [slots] of device pointers, bf16 bits [2f][d_model] each:
+ *             gate rows 0..f-1, up rows f..2f-1
+ *   S[e] += h_e^T h_e (lower triangle) and counts[e] += n_e for the registered layer,
+ *   stored instead of added by the first collection after clha_reset_layer.
+ * Errors: INVALID_ARG (not a down_proj context, unregistered layer, null pointer),
+ * SHAPE (d_model not a multiple of 64 or > 8192, n_routed, n_tokens), ALIGN, WORKSPACE.
+ * n_tokens == 0 enqueues nothing and reads no pointer. */
+CLHA_API size_t clha_down_workspace_bytes(const clha_ctx* ctx, int32_t n_routed);
+CLHA_API clha_status clha_collect_down_hessians(clha_ctx* ctx, int32_t layer, int64_t n_tokens,
+                                                int32_t d_model, int32_t n_routed, const uint16_t* x,
+                                                const int32_t* token_ids, const int64_t* offsets,
+                                                const uint16_t* const* wgu, void* workspace,
+                                                size_t workspace_bytes, void* stream);
+
 /* Packed storage of codes at b bits (section 2.3, CLHA-MP: routed experts at b bits,
  * shared ones at b+1).  Code j of the stream occupies bits j*b .. j*b+b-1 of a
  * little-endian bit stream (bit 0 = least significant bit of byte 0); n_codes codes

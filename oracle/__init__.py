@@ -132,6 +132,57 @@ def layer_hessians(x_bits, topk, n_routed: int, n_shared: int, slots=None):
     return out, all_counts
 
 
+def round_bf16(v) -> np.ndarray:
+    """Nearest bf16 value (8 significant bits), ties to even, from fp64; returns
+    fp64 values.  Zero stays zero; the bf16 subnormal range is not needed here."""
+    v = np.asarray(v, dtype=np.float64)
+    m, e = np.frexp(v)                       # v = m 2^e, 0.5 <= |m| < 1
+    return np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)
+
+
+def silu(g) -> np.ndarray:
+    """silu(g) = g * sigmoid(g) = g / (1 + e^-g), in the precision of g."""
+    g = np.asarray(g)
+    one = g.dtype.type(1) if np.issubdtype(g.dtype, np.floating) else 1.0
+    return g / (one + np.exp(-g))
+
+
+def swiglu_intermediate(x_bits, wgu_bits, f: int, with_fp32: bool = False):
+    """The input of an expert's down_proj (CLHA section 2.2 collects every shared
+    weight's Hessian over its own input): h = bf16(silu(x Wg^T) * (x Wu^T)) with
+    Wg = rows 0..f-1 and Wu = rows f..2f-1 of the stacked [2f, d] weight.
+
+    Rounding h to bf16 is a discrete decision taken by floating point, so it is
+    taken in the kernel's precision: g and u are fp32 sums of the (exact) bf16
+    products, silu and the product are fp32, and that fp32 h is rounded to the
+    nearest bf16 (ties to even).  Returns fp64 values of the bf16 h (and, with
+    with_fp32, the fp32 h before rounding)."""
+    x = bf16_to_f64(x_bits).astype(np.float32)
+    w = bf16_to_f64(wgu_bits).astype(np.float32)
+    g = x @ w[:f].T
+    u = x @ w[f:].T
+    h = (silu(g) * u).astype(np.float32)
+    hb = round_bf16(h.astype(np.float64))
+    return (hb, h.astype(np.float64)) if with_fp32 else hb
+
+
+def down_layer_hessians(x_bits, topk, wgu_list, n_routed: int, f: int, slots=None):
+    """Per-layer Gram sums of the down_proj inputs: slot e < n_routed over expert
+    e's routed tokens with its weights, slot n_routed + s over all tokens with
+    shared expert s's weights.  Returns ({slot: S}, counts)."""
+    n = np.asarray(x_bits).shape[0]
+    counts, offsets, ids = bucket(topk, n_routed)
+    n_slots = len(wgu_list)
+    all_counts = np.zeros(n_slots, np.int64)
+    all_counts[:n_routed] = counts
+    all_counts[n_routed:] = n
+    out = {}
+    for s in (range(n_slots) if slots is None else slots):
+        rows = np.asarray(x_bits)[ids[offsets[s]:offsets[s + 1]]] if s < n_routed else np.asarray(x_bits)
+        out[s] = gram(swiglu_intermediate(rows, wgu_list[s], f)) if len(rows) else np.zeros((f, f))
+    return out, all_counts
+
+
 def aggregate(S_list, n_list, mode: str, alpha=None):
     """Combined Hessian of one shared weight (CLHA section 2.1 Proposition 1;
     section 2.2 aggregation).

@@ -94,3 +94,37 @@ def run_group(wl, inputs, jobs, *, mode=None, alpha=None, chunks=1, layers=(0, 1
 
 def agree(a, b) -> float:
     return float(np.mean(np.asarray(a) == np.asarray(b)))
+
+
+# A rounding of h to bf16 is decided in fp32 on both sides, but the two fp32
+# sums (matrix-core order against BLAS order) can differ by a few fp32 ulps, so
+# an h within that distance of a bf16 midpoint may round either way.  Every
+# value whose fp32 h lies within a relative 2^-16 of a midpoint (16 times the
+# fp32 error of a 2048-term sum) is taken as ambiguous: the GPU may hold its
+# other neighbour, one bf16 step away.
+BF16_TIE_MARGIN = 2.0 ** -16
+
+
+def down_gram_flip_bound(hb, h32):
+    """Largest change of sum_t h_t h_t^T that admissible bf16 flips of the
+    ambiguous values can cause, per element (all from the oracle)."""
+    hb = np.asarray(hb, np.float64)
+    h32 = np.asarray(h32, np.float64)
+    m, e = np.frexp(np.where(h32 == 0.0, 1.0, h32))
+    step = np.ldexp(1.0, e - 8)                           # bf16 spacing around h
+    frac = np.ldexp(np.abs(m), 8)                          # in [128, 256)
+    dist = np.abs(frac - np.floor(frac) - 0.5) * step      # distance to the nearest midpoint
+    amb = (dist <= BF16_TIE_MARGIN * np.abs(h32)) & (h32 != 0.0)
+    A = np.where(amb, step, 0.0)
+    H = np.abs(hb)
+    return A.T @ H + H.T @ A + A.T @ A
+
+
+def assert_down_gram(S_gpu, S_ref, bound, label):
+    """|S_gpu - S_ref| <= flip bound + HESS_TOL sqrt(S_ii S_jj), elementwise."""
+    S_gpu = np.asarray(S_gpu, np.float64)
+    d = np.sqrt(np.clip(np.diag(S_ref), 1e-300, None))
+    low = np.tril(np.ones_like(S_ref, dtype=bool))
+    excess = np.abs(S_gpu - S_ref) - bound - HESS_TOL * np.outer(d, d)
+    worst = float(np.max(np.where(low, excess, -np.inf)))
+    assert worst <= 0.0, f"{label}: exceeds the bound by {worst:.3e}"

@@ -16,6 +16,7 @@ import types
 import numpy as np
 import pytest
 
+import gen
 import oracle
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -562,3 +563,42 @@ def test_mixed_precision_accounting():
     assert abs(r["base_bits_per_param"] - (3 + 40 / 128)) < 1e-12
     assert abs(r["bits_per_param"] - (3 + 40 / 128 + 2 / 66)) < 1e-12
     assert abs(r["overhead"] - (2 / 66) / (3 + 40 / 128)) < 1e-12
+
+
+# =========================================================================== down_proj inputs
+
+def test_round_bf16_hand_values():
+    """bf16 keeps 8 significant bits: on [1, 2) the spacing is 2^-7, on [256, 512) it is 2.
+    1 + 2^-8 is a tie and goes to the even neighbour 1; 1 + 0.75 * 2^-7 rounds up;
+    -257.5 lies between -256 and -258 and rounds to -258."""
+    got = oracle.round_bf16([1.0, 1.0 + 2.0 ** -8, 1.0 + 0.75 * 2.0 ** -7, 1.0 + 2.0 ** -9, -257.5, 0.0])
+    assert got.tolist() == [1.0, 1.0, 1.0078125, 1.0, -258.0, 0.0]
+
+
+def test_silu_closed_forms():
+    assert oracle.silu(0.0) == 0.0
+    assert abs(oracle.silu(1.0) - 1.0 / (1.0 + np.exp(-1.0))) < 1e-16
+    assert abs(oracle.silu(40.0) - 40.0) < 1e-12 and abs(oracle.silu(-40.0)) < 1e-15
+
+
+def test_swiglu_intermediate_hand_example():
+    """x = (1, 0) picks column 0 of the weights: g = (1, 0), u = (3, 0), so
+    h = (bf16(3 sigmoid(1)), 0) = (bf16(2.19318), 0) = (2.1875, 0) (spacing 2^-6 on [2, 4))."""
+    x = gen.bf16_bits(np.array([[1.0, 0.0]], np.float32))
+    w = gen.bf16_bits(np.array([[1.0, 0.0], [0.0, 2.0], [3.0, 0.0], [0.0, 0.5]], np.float32))
+    h = oracle.swiglu_intermediate(x, w, 2)
+    assert h.tolist() == [[2.1875, 0.0]]
+
+
+def test_down_layer_hessians_one_token_per_expert():
+    """Two routed experts with one token each and one shared expert over both:
+    each routed Gram sum is h h^T of its token, the shared one the sum of both."""
+    x = gen.bf16_bits(np.array([[1.0, 0.0], [0.0, 1.0]], np.float32))
+    topk = np.array([[0], [1]])
+    ws = [gen.bf16_bits(np.array([[1.0, 1.0], [0.5, 0.0], [2.0, 2.0], [1.0, 4.0]], np.float32))] * 3
+    S, n = oracle.down_layer_hessians(x, topk, ws, 2, 2)
+    assert n.tolist() == [1, 1, 2]
+    h0 = oracle.swiglu_intermediate(x[:1], ws[0], 2)[0]
+    h1 = oracle.swiglu_intermediate(x[1:], ws[1], 2)[0]
+    assert (S[0] == np.outer(h0, h0)).all() and (S[1] == np.outer(h1, h1)).all()
+    assert np.allclose(S[2], np.outer(h0, h0) + np.outer(h1, h1), rtol=1e-15)
