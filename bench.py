@@ -7,11 +7,17 @@ d = 2048; 65,536 tokens per layer; gate and up 1408x2048 bf16 per expert;
 3-bit, group 128, routing-frequency alpha):
   reset accumulators -> collect layer a -> collect layer b (route, bucket,
   gather, Gram sums) -> aggregate H_comb -> GPTQ of 66 stacked gate|up jobs
-  (damping, fp64 factor of the inverse, column loop, lazy block updates, loss)
+  (damping, factor of the inverse, column loop, lazy block updates, loss)
 = 132 expert matrices.  Inputs are seeded synthetic arrays resident in HBM
 before the timed region.  Prints one JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+--down-proj measures the experts' second matrices instead (the same block and
+batch): one step resets the down_proj accumulators, collects both layers'
+SwiGLU inputs h = bf16(silu(x Wg^T) * (x Wu^T)) and their Gram sums (routing
+taken from the main context's collection of the same batch, done once before
+timing), aggregates, and runs GPTQ on the 66 down_proj matrices (2048x1408).
 """
 import argparse
 import hashlib
@@ -37,8 +43,11 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", type=int, default=2, help="workload id of gen.WORKLOADS (default 2)")
     ap.add_argument("--copy-probe", type=int, metavar="BYTES", help="only copy BYTES on the device and exit")
+    ap.add_argument("--down-proj", action="store_true", help="measure the down_proj calibration step instead")
     ap.add_argument("--profile-commands", metavar="DIR", help="print the profiling command lines and exit")
     ap.add_argument("--summarize-profiles", metavar="DIR", help="write profiles/ summaries from DIR and exit")
+    ap.add_argument("--summarize-down-profile", nargs=2, metavar=("DIR", "BENCH_JSON"),
+                    help="write the down_proj profile summaries from DIR and the bench output file, and exit")
     return ap.parse_args()
 
 
@@ -141,15 +150,13 @@ def _short(name):
     return name.split("(")[0] if name.startswith("clha::") else name[:70]
 
 
-def summarize_profiles(d, workload_name="mid_moe_block"):
-    """Writes the kernel-trace summary and the per-kernel HBM traffic summary
-    (counter values scaled by the copy probe) under profiles/."""
-    steps = 4      # the trace run does 1 warm-up and 3 timed steps
-    timed = 3
-    # per-dispatch trace: each kernel's first launches (1/steps of them) belong to
-    # the warm-up step, whose first touch of fresh device memory is slow; they are
-    # left out, so the figures are those of the timed steps
-    trace = _csv(_find(os.path.join(d, "trace"), "kernel_trace.csv"))
+def _trace_lines(trace_dir, title, cmd, notes, steps=4, timed=3, setup_free=False):
+    """Kernel-time table of a traced bench run (1 warm-up + `timed` steps).  Each
+    kernel's first launches (1/steps of them) belong to the warm-up step, whose
+    first touch of fresh device memory is slow; they are left out.  With
+    setup_free, kernels launched fewer than `steps` times ran only in the set-up
+    before the steps and are left out too."""
+    trace = _csv(_find(trace_dir, "kernel_trace.csv"))
     by_name = {}
     for r in trace:
         by_name.setdefault(r["Kernel_Name"], []).append(
@@ -157,19 +164,18 @@ def summarize_profiles(d, workload_name="mid_moe_block"):
     stats = []
     for name, ds in by_name.items():
         ds.sort()
+        if setup_free and len(ds) < steps:
+            continue
+        if setup_free:
+            ds = ds[len(ds) % steps:]          # launches before the steps
         keep = [t for _, t in ds[len(ds) // steps:]] if len(ds) >= steps else [t for _, t in ds]
         if keep:
             stats.append({"Name": name, "Calls": len(keep), "TotalDurationNs": sum(keep),
                           "AverageNs": sum(keep) / len(keep)})
     stats.sort(key=lambda r: -r["TotalDurationNs"])
-    cmd = {k: c.format(dir=d) for k, c in PROFILE_RUNS}
-    lines = [f"# Kernel time per step, {workload_name} workload (MI355X, rocprofv3 kernel trace)", "",
-             "Command (repository root):", "", f"    {cmd['trace']}", "",
+    lines = [title, "", "Command (repository root):", "", f"    {cmd}", "",
              f"{steps} steps traced (1 warm-up + {timed} timed); the warm-up step's launches are left out "
-             f"and per-step figures are totals / {timed}.",
-             "The factorisation runs as four Hessian groups on concurrent streams, overlapped with the",
-             "GPTQ kernels, so per-kernel times overlap in wall time; wall-clock stage times are",
-             "`stages_ms_per_step` in the bench line.", "",
+             f"and per-step figures are totals / {timed}.", *notes, "",
              "| kernel | calls/step | ms/step | avg us/launch | % |", "|---|---:|---:|---:|---:|"]
     total = sum(float(r["TotalDurationNs"]) for r in stats)
     for r in stats:
@@ -177,6 +183,41 @@ def summarize_profiles(d, workload_name="mid_moe_block"):
         lines.append(f"| {_short(r['Name'])} | {int(r['Calls']) / timed:g} | {t / 1e6 / timed:.3f} | "
                      f"{float(r['AverageNs']) / 1e3:.1f} | {100 * t / total:.1f} |")
     lines += ["", f"Sum of kernel time per step: {total / 1e6 / timed:.3f} ms", ""]
+    return lines
+
+
+DOWN_TRACE = ("timeout -k 10 400 rocprofv3 --kernel-trace --stats --output-format csv -d {dir}/trace -o run "
+              "-- python3 bench.py --down-proj --steps 3 --warmup 1")
+
+
+def summarize_down_profile(d, bench_json):
+    """Writes the down_proj step's kernel-trace summary and bench line under profiles/."""
+    lines = _trace_lines(os.path.join(d, "trace"),
+                         "# Kernel time per step, down_proj calibration of the mid MoE block "
+                         "(MI355X, rocprofv3 kernel trace)", DOWN_TRACE.format(dir=d),
+                         ["The routing of the block's main context (and its Gram sums) runs once before the",
+                          "steps; those launches are left out.  The factorisation and GPTQ overlap on",
+                          "concurrent streams; wall-clock stage times are `stages_ms_per_step` in the bench line."],
+                         setup_free=True)
+    open(os.path.join(ROOT, "profiles", "down_proj_mid_moe_block_kernel_trace.md"), "w").write("\n".join(lines))
+    line = open(bench_json).read().strip().splitlines()[-1]
+    json.loads(line)
+    out = ["# Bench line, down_proj calibration of the mid MoE block (MI355X)", "",
+           "Command (repository root):", "", "    timeout -k 10 400 python3 -u bench.py --down-proj", "",
+           "Output:", "", "```json", line, "```", ""]
+    open(os.path.join(ROOT, "profiles", "bench_down_proj_mid_moe_block.md"), "w").write("\n".join(out))
+
+
+def summarize_profiles(d, workload_name="mid_moe_block"):
+    """Writes the kernel-trace summary and the per-kernel HBM traffic summary
+    (counter values scaled by the copy probe) under profiles/."""
+    cmd = {k: c.format(dir=d) for k, c in PROFILE_RUNS}
+    lines = _trace_lines(os.path.join(d, "trace"),
+                         f"# Kernel time per step, {workload_name} workload (MI355X, rocprofv3 kernel trace)",
+                         cmd["trace"],
+                         ["The factorisation runs as four Hessian groups on concurrent streams, overlapped with the",
+                          "GPTQ kernels, so per-kernel times overlap in wall time; wall-clock stage times are",
+                          "`stages_ms_per_step` in the bench line."])
     open(os.path.join(ROOT, "profiles", f"clha_step_{workload_name}_kernel_trace.md"), "w").write("\n".join(lines))
 
     def per_kernel(sub, counter):
@@ -220,6 +261,76 @@ def summarize_profiles(d, workload_name="mid_moe_block"):
     print(json.dumps(rec))
 
 
+def down_proj_bench(args):
+    """The down_proj calibration step of the mid-MoE block (see the module docstring)."""
+    import numpy as np
+    import torch
+    import gen
+    import gptq_calibration_moe_amd as clha
+    from gptq_calibration_moe_amd.calibrate import SharedGroupCalibration
+
+    wl = gen.WORKLOADS[2]
+    n, E, K, nsh, f, dm = wl.n_tokens, wl.n_routed, wl.top_k, wl.n_shared, wl.rows, wl.d
+    dev = torch.device("cuda", 0)
+    inp = gen.pair_inputs(wl)
+    x = [torch.from_numpy(inp["x"][l].view(np.int16)).to(dev) for l in range(2)]
+    lg = [torch.from_numpy(inp["logits"][l]).to(dev) for l in range(2)]
+    main_ctx = clha.Context(dm, E, K, 0, n, device=dev)
+    down = clha.Context(f, E + nsh, K, 0, n, device=dev)
+    wgu = [torch.from_numpy(gen.expert_weights(wl, 0, e).view(np.int16)).to(dev) for e in range(E + nsh)]
+    w_down = [torch.from_numpy(gen.swiglu_weights(2000 + e, 1, dm // 2, f)[0].view(np.int16)).to(dev)
+              .view(torch.bfloat16) for e in range(E + nsh)]
+    routing = []
+    for l in range(2):
+        main_ctx.register_layer(l, *main_ctx.new_layer_buffers())
+        ids = torch.empty(n * K, dtype=torch.int32, device=dev)
+        off = torch.empty(E + 1, dtype=torch.int64, device=dev)
+        main_ctx.collect_hessians(l, x[l], lg[l], offsets_out=off, token_ids_out=ids)
+        routing.append((ids, off))
+    cal = SharedGroupCalibration(down, [0, 1])
+    outputs = cal.make_outputs(range(E + nsh), dm, wl.group)
+    jobs = [{"H": cal.H[e], "W": w_down[e], "bits": wl.bits, **outputs[e]} for e in range(E + nsh)]
+    prep = down.prepare_gptq(jobs, f)
+
+    def step():
+        cal.reset()
+        for l in range(2):
+            down.collect_down_hessians(l, x[l], routing[l][0], routing[l][1], wgu, E)
+        cal.aggregate("rt")
+        down.run_gptq(prep, wl.group, 128, wl.damp)
+
+    for _ in range(args.warmup):
+        step()
+    down.sync()
+    down.set_timing(True)
+    down.read_timing()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / args.steps * 1e3
+    stages = {k: v[0] / args.steps for k, v in down.read_timing().items() if v[1]}
+    rows = 2 * (n * K + nsh * n)
+    gemm_flops = rows * 2 * dm * 2 * f / 2          # per collection (one layer)
+    gemm_ms = stages.get("gather", 0.0) / 2
+    achieved = gemm_flops / (gemm_ms * 1e-3) / 1e12 if gemm_ms else None
+    line = {"metric": "down_proj matrices calibrated/sec (SwiGLU inputs + Hessians + CLHA-GPTQ)",
+            "value": round((E + nsh) / (ms * 1e-3), 2), "unit": "matrices/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": "mid_moe_block_down_proj", "layers": 2, "tokens_per_layer": n, "d_model": dm,
+                       "f": f, "routed_experts": E, "top_k": K, "shared_experts": nsh, "matrices": E + nsh,
+                       "matrix_shape": [dm, f], "bits": wl.bits, "group": wl.group, "alpha": "rt"},
+            "roofline": {"kernel": "down_gemm_kernel", "bound": "mfma",
+                         "achieved": round(achieved, 2) if achieved else None, "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4) if achieved else None,
+                         "traffic": None, "avg_launch_ms": round(gemm_ms, 4), "flops_per_launch": gemm_flops},
+            "stages_ms_per_step": {k: round(v, 4) for k, v in stages.items()}}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main():
     args = parse()
     if args.profile_commands:
@@ -229,6 +340,9 @@ def main():
     if args.summarize_profiles:
         summarize_profiles(args.summarize_profiles)
         return 0
+    if args.summarize_down_profile:
+        summarize_down_profile(*args.summarize_down_profile)
+        return 0
     if args.copy_probe:
         copy_probe(args.copy_probe)
         return 0
@@ -236,6 +350,8 @@ def main():
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (every run here uses "
               "exactly one MI355X; the multi-GPU design is described, not built)", file=sys.stderr)
         return 2
+    if args.down_proj:
+        return down_proj_bench(args)
     import numpy as np
     import torch
     import gen
