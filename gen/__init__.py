@@ -218,6 +218,17 @@ def router_logits(wl: Workload, pair: int, layer: int, x_bits: Optional[np.ndarr
     raise ValueError(wl.logit_kind)
 
 
+def sharpness_logits(wl: Workload, pair: int, layer: int, x_bits: np.ndarray, tau: float) -> np.ndarray:
+    """Router logits of the routing-sharpness sweep: x R / tau + Gumbel(0, 1), with
+    R ~ N(0, 1/d) [d, E] shared by the pair and the Gumbel noise drawn per layer.
+    Top-K of these logits is a sample without replacement from softmax(x R / tau),
+    so tau sets how sharp routing is: small tau follows x R in both layers, large
+    tau makes the two layers' choices independent.  fp32 [N, E]."""
+    base = router_logits(wl.scaled(logit_kind="router"), pair, layer, x_bits)
+    u = _rng(wl, pair, _S_LA if layer == 0 else _S_LB).random(base.shape)
+    return (base.astype(np.float64) / tau - np.log(-np.log(u))).astype(np.float32)
+
+
 # --------------------------------------------------------------------------- weights
 
 def expert_weights(wl: Workload, pair: int, expert: int) -> np.ndarray:

@@ -1,0 +1,77 @@
+"""Routing-sharpness sweep of one CLWS pair (the CLHA summary's divergence
+experiment, section 4): how far the two layers' routing diverges, and how the
+quantization loss of PLIC, CLHA-rt and CLHA-eq behaves under each layer's own
+Hessian as it does.
+
+Host-side orchestration; every arithmetic step of the calibration runs in the
+library's kernels.  The two divergence measures are small host computations on
+the routing the library returns:
+  load_divergence   Jensen-Shannon divergence (natural log) of the layers'
+                    expert-load distributions n_e / sum n
+  topk_overlap      mean over tokens of the fraction of experts chosen in both layers
+"""
+from __future__ import annotations
+
+from typing import Callable, Sequence
+
+import numpy as np
+import torch
+
+from .calibrate import SharedGroupCalibration
+
+
+def load_divergence(counts_a, counts_b) -> float:
+    p = np.asarray(counts_a, np.float64)
+    q = np.asarray(counts_b, np.float64)
+    p, q = p / p.sum(), q / q.sum()
+    m = 0.5 * (p + q)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        kp = np.where(p > 0, p * np.log(p / m), 0.0).sum()
+        kq = np.where(q > 0, q * np.log(q / m), 0.0).sum()
+    return float(0.5 * (kp + kq))
+
+
+def topk_overlap(topk_a, topk_b) -> float:
+    a = np.sort(np.asarray(topk_a), axis=1)
+    b = np.sort(np.asarray(topk_b), axis=1)
+    k = a.shape[1]
+    hits = (a[:, :, None] == b[:, None, :]).any(axis=2).sum(axis=1)
+    return float(hits.mean() / k)
+
+
+def sharpness_sweep(ctx, x: Sequence[torch.Tensor], logits_for: Callable[[float], Sequence[torch.Tensor]],
+                    taus: Sequence[float], weights: dict, bits: int, group: int, block: int = 128,
+                    damp: float = 0.01) -> list:
+    """For each tau: route and collect both layers with logits_for(tau), combine
+    under PLIC (alpha = (1, 0)), CLHA-rt and CLHA-eq, quantize `weights`
+    ({routed expert: W}) under each, and measure every result's loss under the
+    layer-a and layer-b Hessians.  Returns one dict per tau."""
+    cal = SharedGroupCalibration(ctx, [0, 1])
+    E, K, d, dev = ctx.n_routed, ctx.top_k, ctx.d, ctx.device
+    H_layer = [torch.empty(ctx.slots, d, d, dtype=torch.float32, device=dev) for _ in range(2)]
+    rows = []
+    for tau in taus:
+        lg = logits_for(tau)
+        topk = [torch.empty(x[l].shape[0], K, dtype=torch.int32, device=dev) for l in range(2)]
+        cal.reset()
+        for l in range(2):
+            cal.collect(l, x[l], lg[l], topk_out=topk[l])
+        for l in range(2):
+            cal.aggregate("explicit", alpha=[1.0], layers=[l])
+            H_layer[l].copy_(cal.H)
+        counts = [cal.counts[l].cpu().numpy()[:E] for l in range(2)]
+        row = {"tau": float(tau), "load_divergence": load_divergence(*counts),
+               "topk_overlap": topk_overlap(topk[0].cpu().numpy(), topk[1].cpu().numpy())}
+        for name, mode, alpha in (("plic", "explicit", [1.0, 0.0]), ("rt", "rt", None), ("eq", "eq", None)):
+            cal.aggregate(mode, alpha=alpha)
+            out = cal.quantize(weights, bits, bits, group, block=block, damp=damp)
+            for l, tag in ((0, "a"), (1, "b")):
+                total = 0.0
+                for e, w in weights.items():
+                    o = out[e]
+                    got = torch.empty(1, dtype=torch.float32, device=dev)
+                    ctx.loss(w, o["codes"], o["scales"], o["zeros"], H_layer[l][e], group, got)
+                    total += float(got.cpu()[0])
+                row[f"loss_{name}_{tag}"] = total
+        rows.append(row)
+    return rows

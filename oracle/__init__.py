@@ -344,6 +344,27 @@ def unpack_codes(packed, bits: int, n: int) -> np.ndarray:
     return (stream.reshape(n, bits).astype(np.int64) @ w).astype(np.uint8)
 
 
+def load_divergence(counts_a, counts_b) -> float:
+    """Jensen-Shannon divergence (natural log) between two layers' expert-load
+    distributions p = n / sum n: JSD = (KL(p||m) + KL(q||m)) / 2, m = (p + q)/2,
+    with 0 log 0 = 0 (a divergence between the layers' routing, section 4)."""
+    p = np.asarray(counts_a, np.float64)
+    q = np.asarray(counts_b, np.float64)
+    p, q = p / p.sum(), q / q.sum()
+    m = (p + q) / 2
+    def kl(a):
+        return sum(ai * np.log(ai / mi) for ai, mi in zip(a, m) if ai > 0)
+    return 0.5 * (kl(p) + kl(q))
+
+
+def topk_overlap(topk_a, topk_b) -> float:
+    """Mean over tokens of |choices in layer a and in layer b| / K."""
+    a = np.asarray(topk_a)
+    b = np.asarray(topk_b)
+    k = a.shape[1]
+    return float(np.mean([len(set(ra.tolist()) & set(rb.tolist())) / k for ra, rb in zip(a, b)]))
+
+
 def loss(w, wq, H) -> float:
     """tr[(W_q - W) H (W_q - W)^T] = sum over rows of delta_r H delta_r^T
     (CLHA section 2.1 objective for one layer term)."""

@@ -602,3 +602,47 @@ def test_down_layer_hessians_one_token_per_expert():
     h1 = oracle.swiglu_intermediate(x[1:], ws[1], 2)[0]
     assert (S[0] == np.outer(h0, h0)).all() and (S[1] == np.outer(h1, h1)).all()
     assert np.allclose(S[2], np.outer(h0, h0) + np.outer(h1, h1), rtol=1e-15)
+
+
+# =========================================================================== routing divergence
+
+def test_load_divergence_closed_forms():
+    """JSD = 0 for equal loads, ln 2 for disjoint ones, and for p = (1, 0),
+    q = (1/2, 1/2): m = (3/4, 1/4), KL(p||m) = ln(4/3), KL(q||m) = ln(4/3)/2,
+    so JSD = (3/4) ln(4/3)."""
+    assert oracle.load_divergence([3, 5, 2], [6, 10, 4]) == 0.0
+    assert abs(oracle.load_divergence([4, 0], [0, 9]) - np.log(2.0)) < 1e-15
+    assert abs(oracle.load_divergence([8, 0], [5, 5]) - 0.75 * np.log(4.0 / 3.0)) < 1e-15
+
+
+def test_topk_overlap_hand_example():
+    a = np.array([[0, 1], [2, 3], [4, 5]])
+    b = np.array([[1, 0], [3, 6], [7, 8]])
+    assert oracle.topk_overlap(a, b) == (1.0 + 0.5 + 0.0) / 3
+    assert oracle.topk_overlap(a, a) == 1.0
+
+
+def test_sweep_metrics_match_oracle():
+    """The package's vectorised host metrics against the oracle's definitions."""
+    from gptq_calibration_moe_amd.sweep import load_divergence, topk_overlap
+    rng = _rng(60)
+    for _ in range(5):
+        ca, cb = rng.integers(0, 50, 16), rng.integers(0, 50, 16)
+        ca[3] = 0
+        assert abs(load_divergence(ca, cb) - oracle.load_divergence(ca, cb)) < 1e-14
+        ta = np.stack([rng.permutation(16)[:4] for _ in range(200)])
+        tb = np.stack([rng.permutation(16)[:4] for _ in range(200)])
+        assert topk_overlap(ta, tb) == oracle.topk_overlap(ta, tb)
+
+
+def test_sharpness_logits_limits():
+    """Sampled routing: with the same activations in both layers, a small tau
+    follows x R in both (overlap 1), a large tau is close to independent sampling
+    (overlap near K/E)."""
+    wl = gen.WORKLOADS[1].scaled(n_tokens=2048, x_kind="drift", drift=(0.0,))
+    xa, xb = gen.activations(wl, 0, t=0.0)
+    assert np.array_equal(xa, xb)
+    sharp = [oracle.route(gen.sharpness_logits(wl, 0, l, xa, 1e-5), wl.top_k) for l in range(2)]
+    assert oracle.topk_overlap(*sharp) == 1.0
+    flat = [oracle.route(gen.sharpness_logits(wl, 0, l, xa, 1e3), wl.top_k) for l in range(2)]
+    assert abs(oracle.topk_overlap(*flat) - wl.top_k / wl.n_routed) < 0.05
