@@ -39,6 +39,10 @@ Readings of silent points (each is a stated choice, not a page fact):
   * damping: lambda = damp * mean(diag H) after the dead fix.
   * group statistics computed at each group's first column from the updated
     weights; natural column order; the group size divides the block size.
+    Two common GPTQ options are also offered: activation order (columns by
+    decreasing H_ii, dead columns counted as 1, ties by index; groups are
+    runs of processed columns) and static groups (every natural group's grid
+    fitted once on the weights after the dead fix, before any update).
   * quantizer grid: range widened to contain 0, an all-zero group uses
     (-1, 1); s = (max - min)/maxq, z = rint(-min/s); rint ties to even.
   * an empty layer (n = 0) drops out of the combination; if every layer is
@@ -51,6 +55,7 @@ import numpy as np
 __all__ = [
     "bf16_to_f64", "route", "bucket", "gram", "layer_hessians", "aggregate",
     "inverse_cholesky_upper", "quant_params", "quantize", "gptq", "dequantize",
+    "dequantize_idx", "act_order_perm",
     "loss", "calibrate_pair",
 ]
 
@@ -267,22 +272,44 @@ def dequantize(codes, scales, zeros, group: int) -> np.ndarray:
     return s * (c - z)
 
 
-def gptq(w, H, bits: int, group: int, damp: float = 0.01, block: int = 128) -> dict:
+def act_order_perm(H) -> np.ndarray:
+    """Processing order of GPTQ's activation-order option: columns by
+    decreasing H_ii, with a dead column (H_ii == 0) counted as 1 (its value
+    after the dead fix) and ties in increasing column index.  Returns perm with
+    perm[j] = the column processed j-th.  H_ii are compared as the float32
+    values they are stored as."""
+    d = np.diag(np.asarray(H, np.float32)).astype(np.float64)
+    key = np.where(d == 0, 1.0, d)
+    idx = np.arange(d.size)
+    return np.array(sorted(idx, key=lambda i: (-key[i], i)), dtype=np.int64)
+
+
+def gptq(w, H, bits: int, group: int, damp: float = 0.01, block: int = 128,
+         act_order: bool = False, static_groups: bool = False) -> dict:
     """GPTQ on one weight matrix with Hessian H (CLHA section 2.2 step 3,
     "standard GPTQ column-sequential updates" with H = H_comb).
 
     w: [r, c] weights, H: [c, c] symmetric PSD (undamped).  Steps:
       1. dead columns (H_ii == 0): H_ii := 1, W[:, i] := 0;
-      2. lambda = damp * mean(diag H); H += lambda I;
-      3. U = upper Cholesky factor of H^-1;
-      4. blocks of `block` columns; inside a block, column by column:
-         at a group's first column fit (s, z) per row on the group's current
-         weights; quantize the column; err = (w - what)/U_jj; propagate
-         err * U[j, j+1:] into the rest of the block;
-         after the block, propagate the block's errors into all later columns
-         through U[block, later].
-    Returns codes [r,c] uint8, scales [r,c/g] float32, zeros [r,c/g] uint8,
-    obs [r] (sum of err^2 per row), wq [r,c] float64, dead [c] bool, lam.
+      2. static_groups: fit (s, z) of every row and natural group
+         (columns g*group .. +group-1) once, on these weights;
+      3. act_order: process the columns in act_order_perm(H) order, i.e.
+         run the rest on W[:, perm] and H[perm][:, perm];
+      4. lambda = damp * mean(diag H); H += lambda I;
+      5. U = upper Cholesky factor of H^-1;
+      6. blocks of `block` columns; inside a block, column by column:
+         the column's grid is its static one (step 2), or else, at every
+         group-th processed column, (s, z) fitted per row on the next `group`
+         processed columns' current weights; quantize the column;
+         err = (w - what)/U_jj; propagate err * U[j, j+1:] into the rest of
+         the block; after the block, propagate the block's errors into all
+         later columns through U[block, later].
+    Returns, in natural column order, codes [r,c] uint8, and the grids
+    scales [r,c/g] float32 and zeros [r,c/g] uint8 with g_idx [c] (column i
+    uses grid g_idx[i]: i // group, except for act_order without static
+    groups, where it is the column's processing position // group); also obs
+    [r] (sum of err^2 per row), wq [r,c] float64, dead [c] bool, lam, perm,
+    and U in processing order.
     """
     W = np.array(w, dtype=np.float64)
     Hd = np.array(H, dtype=np.float64)
@@ -290,17 +317,26 @@ def gptq(w, H, bits: int, group: int, damp: float = 0.01, block: int = 128) -> d
     if c % group or block % group:
         raise ValueError("group must divide the column count and the block size")
     maxq = (1 << bits) - 1
+    ng = c // group
     diag = np.diag(Hd).copy()
     dead = diag == 0
     Hd[dead, dead] = 1.0
     W[:, dead] = 0.0
+    scales = np.zeros((r, ng), np.float32)
+    zeros = np.zeros((r, ng), np.uint8)
+    if static_groups:
+        zs = np.zeros((r, ng), np.float32)
+        for g in range(ng):
+            scales[:, g], zs[:, g] = quant_params(W[:, g * group:(g + 1) * group], maxq)
+        zeros = zs.astype(np.uint8)
+    perm = act_order_perm(H) if act_order else np.arange(c)
+    W = W[:, perm]
+    Hd = Hd[np.ix_(perm, perm)]
     lam = damp * float(np.mean(np.diag(Hd)))
     Hd[np.diag_indices(c)] += lam
     U = inverse_cholesky_upper(Hd)
 
-    codes = np.zeros((r, c), np.uint8)
-    scales = np.zeros((r, c // group), np.float32)
-    zeros = np.zeros((r, c // group), np.uint8)
+    codes_p = np.zeros((r, c), np.uint8)   # processing order
     obs = np.zeros(r)
     s = z = None
     for i1 in range(0, c, block):
@@ -309,22 +345,38 @@ def gptq(w, H, bits: int, group: int, damp: float = 0.01, block: int = 128) -> d
         E1 = np.zeros_like(W1)
         for j in range(i1, i2):
             jj = j - i1
-            if j % group == 0:
+            if static_groups:
+                g = perm[j] // group
+                s, z = scales[:, g], zeros[:, g].astype(np.float32)
+            elif j % group == 0:
                 s, z = quant_params(W1[:, jj:jj + group], maxq)
                 scales[:, j // group] = s
                 zeros[:, j // group] = z.astype(np.uint8)
             wcol = W1[:, jj]
             q = quantize(wcol, s, z, maxq)
-            codes[:, j] = q.astype(np.uint8)
+            codes_p[:, j] = q.astype(np.uint8)
             what = s.astype(np.float64) * (q.astype(np.float64) - z.astype(np.float64))
             err = (wcol - what) / U[j, j]
             obs += err * err
             W1[:, jj + 1:] -= np.outer(err, U[j, j + 1:i2])
             E1[:, jj] = err
         W[:, i2:] -= E1 @ U[i1:i2, i2:]
-    wq = dequantize(codes, scales, zeros, group)
+    codes = np.zeros_like(codes_p)
+    codes[:, perm] = codes_p
+    g_idx = np.arange(c) // group
+    if act_order and not static_groups:
+        g_idx[perm] = np.arange(c) // group
+    wq = dequantize_idx(codes, scales, zeros, g_idx)
     return {"codes": codes, "scales": scales, "zeros": zeros, "obs": obs,
-            "wq": wq, "dead": dead, "lam": lam, "U": U}
+            "wq": wq, "dead": dead, "lam": lam, "U": U, "perm": perm, "g_idx": g_idx}
+
+
+def dequantize_idx(codes, scales, zeros, g_idx) -> np.ndarray:
+    """W_q[:, i] = s[:, g_idx[i]] (q[:, i] - z[:, g_idx[i]]), float64."""
+    gi = np.asarray(g_idx, np.int64)
+    s = np.asarray(scales, np.float64)[:, gi]
+    z = np.asarray(zeros, np.float64)[:, gi]
+    return s * (np.asarray(codes, np.float64) - z)
 
 
 def pack_codes(codes, bits: int) -> np.ndarray:

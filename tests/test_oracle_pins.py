@@ -448,6 +448,173 @@ def test_gptq_not_better_than_brute_force(seed, c, group):
         assert abs(vals[idx] - g) <= 1e-12 * max(g, 1e-30)
 
 
+# ---- activation order and static groups (two GPTQ options the CLHA pages leave
+# open; their readings: columns by decreasing H_ii with dead columns counted as
+# 1 and ties by index, groups as runs of processed columns; static grids fitted
+# once per natural group on the weights after the dead fix)
+
+def test_act_order_perm_hand_example():
+    # H_ii = 2, 0 (dead: counts as 1), 5, 2, 1 -> 5 (col 2), the tie 2, 2 in
+    # column order (0, 3), then the tie 1, 1 (1, 4)
+    H = np.diag([2.0, 0.0, 5.0, 2.0, 1.0]).astype(np.float32)
+    assert oracle.act_order_perm(H).tolist() == [2, 0, 3, 1, 4]
+
+
+@pytest.mark.parametrize("bits,group,block", [(2, 8, 32), (3, 16, 32), (4, 32, 64)])
+def test_act_order_diagonal_hessian_is_rtn_on_sorted_groups(bits, group, block):
+    """A diagonal H propagates nothing, so GPTQ is round-to-nearest; with
+    activation order the groups are runs of columns by decreasing H_ii."""
+    rng = _rng(40)
+    c = 64
+    w = rng.normal(0, 0.02, (12, c))
+    d = rng.permutation(np.linspace(0.5, 2.0, c))     # distinct diagonal
+    H = np.diag(d)
+    out = oracle.gptq(w, H, bits, group, 0.01, block, act_order=True)
+    order = np.argsort(-d)
+    maxq = (1 << bits) - 1
+    want = np.zeros((12, c), np.uint8)
+    for g0 in range(0, c, group):
+        cols = order[g0:g0 + group]
+        s, z = oracle.quant_params(w[:, cols], maxq)
+        for j in cols:
+            want[:, j] = oracle.quantize(w[:, j], s, z, maxq)
+        assert (out["g_idx"][cols] == g0 // group).all()
+    assert (out["codes"] == want).all()
+    # static groups: the natural groups' grids, so round-to-nearest as without
+    # activation order
+    st = oracle.gptq(w, H, bits, group, 0.01, block, act_order=True, static_groups=True)
+    assert (st["codes"] == _rtn(w, bits, group)).all()
+    assert (st["g_idx"] == np.arange(c) // group).all()
+
+
+def _conditional_optimum_ordered(w, H, bits, group, damp, perm, static):
+    """The conditional-optimum form of GPTQ (no U) over columns in the order
+    perm: before processed column j is quantized, the unprocessed columns take
+    their best values given the processed ones.  Grids: the natural group's,
+    fitted on the dead-fixed weights (static), or fitted on the next `group`
+    processed columns' current values.  Returns codes and W_q in natural
+    column order."""
+    r, c = w.shape
+    maxq = (1 << bits) - 1
+    Hn = np.array(H, np.float64)
+    dead = np.diag(Hn) == 0
+    Hn[dead, dead] = 1.0
+    wn = np.array(w, np.float64)
+    wn[:, dead] = 0.0
+    Hn = Hn + damp * np.mean(np.diag(Hn)) * np.eye(c)
+    sgrid = [oracle.quant_params(wn[:, g:g + group], maxq) for g in range(0, c, group)]
+    codes = np.zeros((r, c), np.uint8)
+    what = np.zeros((r, c))
+    s = z = None
+    for j in range(c):
+        done, rest = list(perm[:j]), list(perm[j:])
+        if j == 0:
+            v = wn.copy()
+        else:
+            delta = what[:, done] - wn[:, done]
+            corr = np.linalg.solve(Hn[np.ix_(rest, rest)], Hn[np.ix_(rest, done)] @ delta.T).T
+            v = wn.copy()
+            v[:, done] = what[:, done]
+            v[:, rest] = wn[:, rest] - corr
+        col = perm[j]
+        if static:
+            s, z = sgrid[col // group]
+        elif j % group == 0:
+            s, z = oracle.quant_params(v[:, list(perm[j:j + group])], maxq)
+        q = oracle.quantize(v[:, col], s, z, maxq)
+        codes[:, col] = q
+        what[:, col] = s.astype(np.float64) * (q - z)
+    return codes, what
+
+
+@pytest.mark.parametrize("seed,c,group,block,bits,act,static", [
+    (41, 32, 8, 16, 2, True, False), (42, 24, 8, 24, 3, True, True),
+    (43, 32, 16, 32, 2, False, True), (44, 32, 4, 16, 4, True, False)])
+def test_gptq_options_match_conditional_optimum(seed, c, group, block, bits, act, static):
+    rng = _rng(seed)
+    w = rng.normal(0, 0.05, (6, c))
+    H = _spd(rng, c, spread=3.0)
+    H[3, :] = 0.0
+    H[:, 3] = 0.0          # a dead column, counted as H_ii = 1 in the order
+    out = oracle.gptq(w, H, bits, group, 0.01, block, act_order=act, static_groups=static)
+    perm = oracle.act_order_perm(H) if act else np.arange(c)
+    codes, what = _conditional_optimum_ordered(w, H, bits, group, 0.01, perm, static)
+    assert (out["codes"] == codes).all()
+    np.testing.assert_allclose(out["wq"], what, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("act,static", [(True, False), (False, True), (True, True)])
+def test_gptq_options_obs_identity(act, static):
+    """sum_j err_j^2 = tr[(Wq - W) Hd (Wq - W)^T] in natural column order: the
+    codes, grids and g_idx come back in the columns they belong to."""
+    rng = _rng(45)
+    c = 64
+    w = rng.normal(0, 0.02, (10, c))
+    H = _spd(rng, c, spread=3.0)
+    out = oracle.gptq(w, H, 3, 16, 0.01, 32, act_order=act, static_groups=static)
+    Hd = H + out["lam"] * np.eye(c)
+    D = out["wq"] - w
+    tr = np.sum((D @ Hd) * D)
+    assert abs(out["obs"].sum() - tr) <= 1e-10 * tr
+
+
+def test_act_order_ignores_input_column_order():
+    """With distinct H_ii, activation order processes the same columns in the
+    same order whatever order they arrive in; codes follow their columns."""
+    rng = _rng(46)
+    c = 48
+    w = rng.normal(0, 0.02, (7, c))
+    H = _spd(rng, c, spread=3.0)
+    P = rng.permutation(c)
+    a = oracle.gptq(w, H, 3, 8, 0.01, 16, act_order=True)
+    b = oracle.gptq(w[:, P], H[np.ix_(P, P)], 3, 8, 0.01, 16, act_order=True)
+    assert (b["codes"] == a["codes"][:, P]).all()
+    assert (b["g_idx"] == a["g_idx"][P]).all()
+    assert (b["scales"] == a["scales"]).all() and (b["zeros"] == a["zeros"]).all()
+
+
+def test_static_grids_do_not_depend_on_h():
+    rng = _rng(47)
+    w = rng.normal(0, 0.02, (5, 32))
+    a = oracle.gptq(w, _spd(rng, 32, spread=3.0), 2, 8, 0.01, 16, static_groups=True)
+    b = oracle.gptq(w, _spd(rng, 32, spread=1.0), 2, 8, 0.01, 16, static_groups=True, act_order=True)
+    assert (a["scales"] == b["scales"]).all() and (a["zeros"] == b["zeros"]).all()
+    for g in range(4):
+        s, z = oracle.quant_params(w[:, 8 * g:8 * g + 8], 3)
+        assert (a["scales"][:, g] == s).all() and (a["zeros"][:, g] == z).all()
+
+
+def _options_pins_hold(gptq_fn):
+    rng = _rng(48)
+    c = 24
+    w = rng.normal(0, 0.05, (5, c))
+    H = _spd(rng, c, spread=3.0)
+    ok = True
+    for act, static in ((True, False), (True, True)):
+        try:
+            out = gptq_fn(w, H, 2, 8, 0.01, 8, act_order=act, static_groups=static)
+        except np.linalg.LinAlgError:
+            return False          # a mutant that breaks the factorisation is caught too
+        perm = oracle.act_order_perm(H)
+        codes, _ = _conditional_optimum_ordered(w, H, 2, 8, 0.01, perm, static)
+        Hd = H + out["lam"] * np.eye(c)
+        D = out["wq"] - w
+        ok &= bool((out["codes"] == codes).all())
+        ok &= bool(abs(out["obs"].sum() - np.sum((D @ Hd) * D)) <= 1e-10 * np.sum((D @ Hd) * D))
+    return ok
+
+
+@pytest.mark.parametrize("old,new", [
+    ("codes[:, perm] = codes_p", "codes[:] = codes_p"),                           # order not undone
+    ("Hd = Hd[np.ix_(perm, perm)]", "Hd = Hd[perm]"),                             # rows only
+    ("g = perm[j] // group", "g = j // group"),                                   # static grid by position
+    ("g_idx[perm] = np.arange(c) // group", "g_idx[:] = np.arange(c) // group"),  # natural g_idx
+])
+def test_planted_gptq_option_mistakes_are_caught(old, new):
+    assert _options_pins_hold(oracle.gptq)
+    assert not _options_pins_hold(_mutant(oracle.gptq, old, new))
+
+
 def test_loss_equals_projected_residual():
     """tr[D (X^T X / n) D^T] = ||D X^T||_F^2 / n."""
     rng = _rng(29)
