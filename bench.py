@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--workload", type=int, default=2, help="workload id of gen.WORKLOADS (default 2)")
     ap.add_argument("--copy-probe", type=int, metavar="BYTES", help="only copy BYTES on the device and exit")
     ap.add_argument("--down-proj", action="store_true", help="measure the down_proj calibration step instead")
+    ap.add_argument("--act-order", action="store_true", help="GPTQ with activation order")
+    ap.add_argument("--static-groups", action="store_true", help="GPTQ with static groups")
     ap.add_argument("--profile-commands", metavar="DIR", help="print the profiling command lines and exit")
     ap.add_argument("--summarize-profiles", metavar="DIR", help="write profiles/ summaries from DIR and exit")
     ap.add_argument("--summarize-down-profile", nargs=2, metavar=("DIR", "BENCH_JSON"),
@@ -376,7 +378,8 @@ def main():
     W = {e: (bits_dev(w) if wl.w_dtype == "bf16" else torch.from_numpy(w).to(dev)) for e, w in w_host.items()}
     ctx = clha.Context(wl.d, wl.n_routed, wl.top_k, wl.n_shared, max_tokens=wl.n_tokens, device=dev)
     cal = SharedGroupCalibration(ctx, [0, 1])
-    prep, outputs = cal.prepare_quantize(W, wl.bits, wl.shared_bits, wl.group)
+    prep, outputs = cal.prepare_quantize(W, wl.bits, wl.shared_bits, wl.group,
+                                         act_order=args.act_order, static_groups=args.static_groups)
     ctx.workspace("collect", ctx.collect_workspace_bytes())
     n_mats = len(experts) * len(wl.mats)
 
@@ -431,6 +434,9 @@ def main():
                       "routed_experts": wl.n_routed, "top_k": wl.top_k, "shared_experts": wl.n_shared,
                       "matrices": n_mats, "matrix_shape": [wl.rows, wl.d], "bits": wl.bits,
                       "shared_bits": wl.shared_bits, "group": wl.group, "alpha": wl.alpha,
+                      **({"gptq_options": [o for o, on in (("act_order", args.act_order),
+                                                            ("static_groups", args.static_groups)) if on]}
+                         if args.act_order or args.static_groups else {}),
                       "precision": "Gram sums bf16 in / fp32 accumulate; Cholesky fp64 values, its "
                                    "long products exact int8 digit products of 42-bit expansions; "
                                    "triangular inverse fp32; GPTQ fp32, trailing products exact int8 "

@@ -25,12 +25,14 @@ STATUS_NAMES = {0: "OK", 1: "INVALID_ARG", 2: "SHAPE", 3: "ALIGN", 4: "HIP", 5: 
                 6: "NONFINITE", 7: "WORKSPACE"}
 ALPHA_MODES = {"rt": 0, "eq": 1, "explicit": 2, "explicit_slot": 3}
 F32, BF16 = 0, 1
+GPTQ_ACT_ORDER, GPTQ_STATIC_GROUPS = 1, 2   # clha_gptq_flag
 
 EXPORTS = (
     "clha_create", "clha_destroy", "clha_last_error", "clha_num_slots", "clha_register_layer",
     "clha_reset_layer",
     "clha_collect_workspace_bytes", "clha_collect_hessians", "clha_aggregate",
-    "clha_gptq_workspace_bytes", "clha_gptq_quantize", "clha_inverse_cholesky_workspace_bytes",
+    "clha_gptq_workspace_bytes", "clha_gptq_quantize", "clha_gptq_workspace_bytes_ex",
+    "clha_gptq_quantize_ex", "clha_inverse_cholesky_workspace_bytes",
     "clha_inverse_cholesky", "clha_loss_workspace_bytes", "clha_loss", "clha_set_timing",
     "clha_read_timing", "clha_sync", "clha_pack_codes", "clha_unpack_codes",
     "clha_down_workspace_bytes", "clha_collect_down_hessians",
@@ -77,6 +79,9 @@ def _load() -> C.CDLL:
         "clha_aggregate": ([vp, i32, C.POINTER(i32), i32, C.POINTER(f32), vp, vp, vp], i32),
         "clha_gptq_workspace_bytes": ([vp, i32, C.POINTER(GptqJob), i32], sz),
         "clha_gptq_quantize": ([vp, i32, C.POINTER(GptqJob), i32, i32, i32, f32, vp, sz, vp], i32),
+        "clha_gptq_workspace_bytes_ex": ([vp, i32, C.POINTER(GptqJob), i32, C.c_uint32], sz),
+        "clha_gptq_quantize_ex": ([vp, i32, C.POINTER(GptqJob), i32, i32, i32, f32, C.c_uint32,
+                                   C.POINTER(vp), vp, sz, vp], i32),
         "clha_inverse_cholesky_workspace_bytes": ([vp, i32, i32], sz),
         "clha_inverse_cholesky": ([vp, i32, C.POINTER(vp), i32, f32, vp, vp, vp, vp, sz, vp], i32),
         "clha_loss_workspace_bytes": ([vp, i32, i32], sz),
@@ -298,19 +303,26 @@ class Context:
     class PreparedGptq:
         """A checked, marshalled job batch for repeated clha_gptq_quantize calls."""
 
-        def __init__(self, arr, n, cols, ws):
-            self.arr, self.n, self.cols, self.ws = arr, n, cols, ws
+        def __init__(self, arr, n, cols, ws, flags=0):
+            self.arr, self.n, self.cols, self.ws, self.flags = arr, n, cols, ws, flags
 
-    def prepare_gptq(self, jobs, cols: int) -> "Context.PreparedGptq":
+    def prepare_gptq(self, jobs, cols: int, act_order: bool = False,
+                     static_groups: bool = False) -> "Context.PreparedGptq":
         arr = self._jobs(jobs, cols)
-        need = lib.clha_gptq_workspace_bytes(self._h, len(jobs), arr, cols)
+        flags = (GPTQ_ACT_ORDER if act_order else 0) | (GPTQ_STATIC_GROUPS if static_groups else 0)
+        need = lib.clha_gptq_workspace_bytes_ex(self._h, len(jobs), arr, cols, flags)
         ws = torch.empty(max(int(need), 256), dtype=torch.uint8, device=self.device)
-        prep = Context.PreparedGptq(arr, len(jobs), cols, ws)
+        prep = Context.PreparedGptq(arr, len(jobs), cols, ws, flags)
         prep.tensors = jobs          # keep the job tensors alive with the pointers
         return prep
 
     def run_gptq(self, prep: "Context.PreparedGptq", group: int, block: int = 128,
                  damp: float = 0.01, stream=None):
+        if prep.flags:
+            self._raise(lib.clha_gptq_quantize_ex(self._h, prep.n, prep.arr, prep.cols, group, block,
+                                                  damp, prep.flags, None, _ptr(prep.ws), prep.ws.numel(),
+                                                  _stream(stream)))
+            return
         self._raise(lib.clha_gptq_quantize(self._h, prep.n, prep.arr, prep.cols, group, block,
                                            damp, _ptr(prep.ws), prep.ws.numel(), _stream(stream)))
 
@@ -319,13 +331,28 @@ class Context:
         return lib.clha_gptq_workspace_bytes(self._h, len(jobs), arr, cols)
 
     def gptq_quantize(self, jobs, cols: int, group: int, block: int = 128, damp: float = 0.01,
-                      workspace: Optional[torch.Tensor] = None, stream=None):
-        """jobs: list of dicts with H, W, bits, codes, scales, zeros and optional loss."""
+                      workspace: Optional[torch.Tensor] = None, stream=None,
+                      act_order: bool = False, static_groups: bool = False):
+        """jobs: list of dicts with H, W, bits, codes, scales, zeros and optional loss and
+        g_idx (device int32 [cols], receives each column's grid index).  act_order and
+        static_groups select clha_gptq_quantize_ex's options."""
         arr = self._jobs(jobs, cols)
-        need = lib.clha_gptq_workspace_bytes(self._h, len(jobs), arr, cols)
+        flags = (GPTQ_ACT_ORDER if act_order else 0) | (GPTQ_STATIC_GROUPS if static_groups else 0)
+        gi = [j.get("g_idx") for j in jobs]
+        if not flags and all(g is None for g in gi):
+            need = lib.clha_gptq_workspace_bytes(self._h, len(jobs), arr, cols)
+            ws = workspace if workspace is not None else self.workspace("gptq", need)
+            self._raise(lib.clha_gptq_quantize(self._h, len(jobs), arr, cols, group, block, damp,
+                                               _ptr(ws), ws.numel(), _stream(stream)))
+            return
+        for g in gi:
+            if g is not None:
+                _check_dev("g_idx", g, torch.int32, (cols,), self.device)
+        garr = (C.c_void_p * len(jobs))(*[g.data_ptr() if g is not None else None for g in gi])
+        need = lib.clha_gptq_workspace_bytes_ex(self._h, len(jobs), arr, cols, flags)
         ws = workspace if workspace is not None else self.workspace("gptq", need)
-        self._raise(lib.clha_gptq_quantize(self._h, len(jobs), arr, cols, group, block, damp,
-                                           _ptr(ws), ws.numel(), _stream(stream)))
+        self._raise(lib.clha_gptq_quantize_ex(self._h, len(jobs), arr, cols, group, block, damp, flags,
+                                              garr, _ptr(ws), ws.numel(), _stream(stream)))
 
     def inverse_cholesky(self, H: Sequence[torch.Tensor], U_out: torch.Tensor, damp: float = 0.01,
                          lambda_out: Optional[torch.Tensor] = None,

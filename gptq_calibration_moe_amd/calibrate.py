@@ -62,8 +62,10 @@ class SharedGroupCalibration:
         return out
 
     def prepare_quantize(self, weights: dict, bits: int, shared_bits: int, group: int,
-                         outputs: Optional[dict] = None, H: Optional[torch.Tensor] = None):
-        """Marshals the GPTQ job batch once; run it with ctx.run_gptq(prep, group, ...)."""
+                         outputs: Optional[dict] = None, H: Optional[torch.Tensor] = None,
+                         act_order: bool = False, static_groups: bool = False):
+        """Marshals the GPTQ job batch once; run it with ctx.run_gptq(prep, group, ...).
+        act_order / static_groups select GPTQ's activation-order and static-group options."""
         H = self.H if H is None else H
         experts = sorted(weights)
         rows = weights[experts[0]].shape[0]
@@ -72,10 +74,11 @@ class SharedGroupCalibration:
         jobs = [{"H": H[self.slot_of(e)], "W": weights[e],
                  "bits": shared_bits if e >= self.ctx.n_routed else bits, **outputs[e]}
                 for e in experts]
-        return self.ctx.prepare_gptq(jobs, self.ctx.d), outputs
+        return self.ctx.prepare_gptq(jobs, self.ctx.d, act_order, static_groups), outputs
 
     def quantize(self, weights: dict, bits: int, shared_bits: int, group: int, block: int = 128,
-                 damp: float = 0.01, outputs: Optional[dict] = None, H: Optional[torch.Tensor] = None):
+                 damp: float = 0.01, outputs: Optional[dict] = None, H: Optional[torch.Tensor] = None,
+                 act_order: bool = False, static_groups: bool = False):
         """weights: {expert: W [rows, d] float32 or bfloat16}.  Routed expert e uses
         H[e]; shared experts (e >= E) use H[E] and shared_bits."""
         H = self.H if H is None else H
@@ -88,7 +91,8 @@ class SharedGroupCalibration:
             o = outputs[e]
             jobs.append({"H": H[self.slot_of(e)], "W": weights[e],
                          "bits": shared_bits if e >= self.ctx.n_routed else bits, **o})
-        self.ctx.gptq_quantize(jobs, self.ctx.d, group, block, damp)
+        self.ctx.gptq_quantize(jobs, self.ctx.d, group, block, damp, act_order=act_order,
+                               static_groups=static_groups)
         return outputs
 
 

@@ -60,6 +60,8 @@ struct clha_ctx {
 
 namespace {
 
+constexpr uint32_t kGptqFlags = CLHA_GPTQ_ACT_ORDER | CLHA_GPTQ_STATIC_GROUPS;
+
 clha_status fail(clha_ctx* ctx, clha_status st, const char* fmt, ...) {
   char buf[512];
   va_list ap;
@@ -263,15 +265,23 @@ struct GptqLayout {
   float* wf;
   float* ebuf;
   double* partials;
+  const float** src_mats;
+  float* hperm;
+  int* perm;
+  int* ipos;
+  int* gidx;
   size_t bytes;
 };
 
 GptqLayout gptq_layout(void* ws, int n_jobs, int n_mats, int cols, int64_t wf_elems,
-                       int64_t total_slabs, bool need_u, bool need_wf) {
+                       int64_t total_slabs, bool need_u, bool need_wf, uint32_t flags = 0) {
   Carver c(ws);
   GptqLayout L;
+  const bool act = flags & CLHA_GPTQ_ACT_ORDER;
   L.jobs = c.take<GJob>((size_t)(n_jobs > 0 ? n_jobs : 1));
   L.mats = c.take<const float*>((size_t)n_mats);
+  // the callers' Hessians, staged with the job and Hessian tables in one copy
+  L.src_mats = flags ? c.take<const float*>((size_t)n_mats) : nullptr;
   L.A = c.take<double>((size_t)n_mats * cols * cols);
   L.X = c.take<double>((size_t)n_mats * cols * cols);
   L.U = need_u ? c.take<float>((size_t)n_mats * cols * cols) : nullptr;
@@ -283,6 +293,10 @@ GptqLayout gptq_layout(void* ws, int n_jobs, int n_mats, int cols, int64_t wf_el
   L.wf = need_wf ? c.take<float>((size_t)wf_elems) : nullptr;
   L.ebuf = need_wf && cols > clha::kSuper ? c.take<float>((size_t)(wf_elems / cols) * clha::kSuper) : nullptr;
   L.partials = need_wf ? c.take<double>((size_t)2 * (total_slabs > 0 ? total_slabs : 1)) : nullptr;
+  L.hperm = act ? c.take<float>((size_t)n_mats * cols * cols) : nullptr;
+  L.perm = act ? c.take<int>((size_t)n_mats * cols) : nullptr;
+  L.ipos = flags ? c.take<int>((size_t)n_mats * cols) : nullptr;
+  L.gidx = flags ? c.take<int>((size_t)n_mats * cols) : nullptr;
   L.bytes = c.off;
   return L;
 }
@@ -554,12 +568,11 @@ static clha_status run_factor(clha_ctx* ctx, const GptqPlan& p, hipStream_t s, c
     const int m0 = (int)((int64_t)p.n_mats * g / groups), m1 = (int)((int64_t)p.n_mats * (g + 1) / groups);
     hipStream_t gs = g == 0 ? s : ctx->aux[g - 1];
     if (g > 0) hipStreamWaitEvent(gs, ctx->stagger[g - 1], 0);
-    clha::launch_factor_group(p, m0, m1, gs, g + 1 < groups ? ctx->stagger[g] : nullptr);
+    clha::JobRange r{};
+    r.j0 = j;
+    r.m0 = m0;
+    r.m1 = m1;
     if (jobs) {
-      clha::JobRange r{};
-      r.j0 = j;
-      r.m0 = m0;
-      r.m1 = m1;
       while (j < p.n_jobs && jobs[j].mat < m1) ++j;
       r.j1 = j;
       if (r.j1 > r.j0) {
@@ -569,9 +582,11 @@ static clha_status run_factor(clha_ctx* ctx, const GptqPlan& p, hipStream_t s, c
         r.n_slabs = last.slab_base + last.n_slabs - first.slab_base;
         r.tile0 = first.tile_base;
         r.n_tiles = last.tile_base + last.n_tiles - first.tile_base;
-        clha::launch_gptq(p, r, gs);
       }
+      clha::launch_gptq_prep(p, r, gs);
     }
+    clha::launch_factor_group(p, m0, m1, gs, g + 1 < groups ? ctx->stagger[g] : nullptr);
+    if (jobs && r.j1 > r.j0) clha::launch_gptq(p, r, gs);
   }
   for (int g = 1; g < groups; ++g) {
     hipEventRecord(ctx->join[g], ctx->aux[g - 1]);
@@ -605,33 +620,47 @@ static clha_status check_gptq_args(clha_ctx* ctx, int32_t n_jobs, const clha_gpt
   return CLHA_OK;
 }
 
-CLHA_API size_t clha_gptq_workspace_bytes(const clha_ctx* ctx, int32_t n_jobs,
-                                          const clha_gptq_job* jobs, int32_t cols) {
+CLHA_API size_t clha_gptq_workspace_bytes_ex(const clha_ctx* ctx, int32_t n_jobs,
+                                             const clha_gptq_job* jobs, int32_t cols, uint32_t flags) {
   if (!ctx || n_jobs < 1 || !jobs || cols < 1) return 0;
   const JobScan js = scan_jobs(n_jobs, jobs, cols);
   return gptq_layout(nullptr, n_jobs, (int)js.mats.size(), cols, js.wf_elems, js.total_slabs, true,
-                     true).bytes;
+                     true, flags & kGptqFlags).bytes;
 }
 
-CLHA_API clha_status clha_gptq_quantize(clha_ctx* ctx, int32_t n_jobs, const clha_gptq_job* jobs,
-                                        int32_t cols, int32_t group, int32_t block, float damp,
-                                        void* workspace, size_t workspace_bytes, void* stream) {
+CLHA_API size_t clha_gptq_workspace_bytes(const clha_ctx* ctx, int32_t n_jobs,
+                                          const clha_gptq_job* jobs, int32_t cols) {
+  return clha_gptq_workspace_bytes_ex(ctx, n_jobs, jobs, cols, 0);
+}
+
+CLHA_API clha_status clha_gptq_quantize_ex(clha_ctx* ctx, int32_t n_jobs, const clha_gptq_job* jobs,
+                                           int32_t cols, int32_t group, int32_t block, float damp,
+                                           uint32_t flags, int32_t* const* g_idx, void* workspace,
+                                           size_t workspace_bytes, void* stream) {
   if (!ctx) return CLHA_ERR_INVALID_ARG;
   clha_status st = check_gptq_args(ctx, n_jobs, jobs, cols, group, block, damp);
   if (st != CLHA_OK) return st;
+  if (flags & ~kGptqFlags) return fail(ctx, CLHA_ERR_INVALID_ARG, "gptq: unknown flags 0x%x", flags);
+  if (g_idx)
+    for (int i = 0; i < n_jobs; ++i)
+      if (g_idx[i] && !aligned4(g_idx[i]))
+        return fail(ctx, CLHA_ERR_ALIGN, "gptq: g_idx[%d] is misaligned", i);
   if (!workspace || !aligned16(workspace))
     return fail(ctx, CLHA_ERR_ALIGN, "gptq: workspace null or misaligned");
   const JobScan js = scan_jobs(n_jobs, jobs, cols);
   const int n_mats = (int)js.mats.size();
   const GptqLayout need = gptq_layout(nullptr, n_jobs, n_mats, cols, js.wf_elems, js.total_slabs,
-                                      true, true);
+                                      true, true, flags);
   if (workspace_bytes < need.bytes)
     return fail(ctx, CLHA_ERR_WORKSPACE, "gptq: workspace %zu < %zu bytes", workspace_bytes, need.bytes);
   if (js.total_slabs > INT32_MAX) return fail(ctx, CLHA_ERR_SHAPE, "gptq: too many rows");
   const GptqLayout L = gptq_layout(workspace, n_jobs, n_mats, cols, js.wf_elems, js.total_slabs,
-                                   true, true);
-  // host tables: jobs, then the distinct Hessian pointers, staged in one copy
-  std::vector<char> host(up256(sizeof(GJob) * n_jobs) + sizeof(float*) * n_mats);
+                                   true, true, flags);
+  const bool act = flags & CLHA_GPTQ_ACT_ORDER;
+  // host tables: jobs, the Hessian pointers the factorisation reads, and (with
+  // an option) the callers' Hessians, staged in one copy
+  const size_t mats_bytes = sizeof(float*) * n_mats;
+  std::vector<char> host(up256(sizeof(GJob) * n_jobs) + (flags ? up256(mats_bytes) : 0) + mats_bytes);
   GJob* hj = reinterpret_cast<GJob*>(host.data());
   // device job table ordered by Hessian (stable), so the jobs of each
   // factorisation group are contiguous
@@ -663,14 +692,30 @@ CLHA_API clha_status clha_gptq_quantize(clha_ctx* ctx, int32_t n_jobs, const clh
     slab_base += g.n_slabs;
     tile_base += g.n_tiles;
   }
-  std::memcpy(host.data() + up256(sizeof(GJob) * n_jobs), js.mats.data(), sizeof(float*) * n_mats);
+  {
+    char* hm = host.data() + up256(sizeof(GJob) * n_jobs);
+    std::vector<const float*> fmats(js.mats);
+    if (act)   // the factorisation reads the permuted copies
+      for (int m = 0; m < n_mats; ++m) fmats[m] = L.hperm + (size_t)m * cols * cols;
+    std::memcpy(hm, fmats.data(), mats_bytes);
+    if (flags) std::memcpy(hm + up256(mats_bytes), js.mats.data(), mats_bytes);
+  }
   const hipStream_t s = as_stream(stream);
-  // jobs and mats are adjacent in the layout (both carved first)
+  // jobs, mats and src_mats are adjacent in the layout (carved first)
+  if (reinterpret_cast<char*>(L.mats) != reinterpret_cast<char*>(L.jobs) + up256(sizeof(GJob) * n_jobs) ||
+      (flags && reinterpret_cast<char*>(L.src_mats) != reinterpret_cast<char*>(L.mats) + up256(mats_bytes)))
+    return fail(ctx, CLHA_ERR_WORKSPACE, "gptq: internal layout mismatch");
   st = stage_to_device(ctx, L.jobs, host.data(), host.size(), s);
   if (st != CLHA_OK) return st;
-  if (reinterpret_cast<char*>(L.mats) != reinterpret_cast<char*>(L.jobs) + up256(sizeof(GJob) * n_jobs))
-    return fail(ctx, CLHA_ERR_WORKSPACE, "gptq: internal layout mismatch");
   GptqPlan p;
+  std::memset(&p, 0, sizeof p);
+  p.act_order = act;
+  p.static_groups = (flags & CLHA_GPTQ_STATIC_GROUPS) != 0;
+  p.src_mats = flags ? L.src_mats : L.mats;
+  p.hperm = L.hperm;
+  p.perm = L.perm;
+  p.ipos = L.ipos;
+  p.gidx = L.gidx;
   p.n_jobs = n_jobs;
   p.n_mats = n_mats;
   p.cols = cols;
@@ -700,7 +745,25 @@ CLHA_API clha_status clha_gptq_quantize(clha_ctx* ctx, int32_t n_jobs, const clh
     st = run_factor(ctx, p, s, hj);
   }
   if (st != CLHA_OK) return st;
+  if (g_idx) {
+    for (int i = 0; i < n_jobs; ++i) {
+      if (!g_idx[i]) continue;
+      if (p.gidx) {
+        hipMemcpyAsync(g_idx[i], p.gidx + (size_t)js.mat_of[i] * cols, sizeof(int32_t) * cols,
+                       hipMemcpyDeviceToDevice, s);
+      } else {
+        clha::launch_natural_gidx(g_idx[i], cols, group, s);
+      }
+    }
+  }
   return hip_check(ctx, "gptq_quantize");
+}
+
+CLHA_API clha_status clha_gptq_quantize(clha_ctx* ctx, int32_t n_jobs, const clha_gptq_job* jobs,
+                                        int32_t cols, int32_t group, int32_t block, float damp,
+                                        void* workspace, size_t workspace_bytes, void* stream) {
+  return clha_gptq_quantize_ex(ctx, n_jobs, jobs, cols, group, block, damp, 0, nullptr, workspace,
+                               workspace_bytes, stream);
 }
 
 CLHA_API size_t clha_inverse_cholesky_workspace_bytes(const clha_ctx* ctx, int32_t n, int32_t cols) {

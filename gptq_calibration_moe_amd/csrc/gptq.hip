@@ -27,6 +27,15 @@
 //     exactly on the int8 matrix cores over 28-bit digit expansions of E and U
 //     (see "trailing update"), so each later weight is read and written once per
 //     superblock instead of once per 64 columns.
+// Options (GPTQ's activation order and static groups).  Activation order
+// processes the columns by decreasing H_ii (a dead column counts as 1, ties by
+// column index): the Hessian is permuted once (H[perm][:, perm]) and factored
+// as usual, the working copy holds the permuted columns, and after the last
+// superblock each row's codes are moved back to their natural columns; a grid
+// then belongs to a run of `group` processed columns, and g_idx gives each
+// column's grid.  Static groups fit every natural group's grid once, before
+// any update, on the weights with dead columns zeroed; the column loop loads
+// a column's grid instead of fitting it.
 // The loss uses the OBS identity: sum_j err_j^2 = tr[(Wq - W) Hd (Wq - W)^T],
 // so the undamped loss is sum err^2 - lambda ||Wq - W||^2 (W after zeroing
 // dead columns); ||Wq - W||^2 is a separate coalesced pass over the outputs.
@@ -48,6 +57,11 @@ __device__ __forceinline__ float4 load_w4(const void* W, int dtype, int64_t i) {
                        __uint_as_float(b.y << 16), __uint_as_float(b.y & 0xffff0000u));
   }
   return *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(W) + i);
+}
+
+__device__ __forceinline__ float load_w1(const void* W, int dtype, int64_t i) {
+  if (dtype == 1) return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(W)[i] << 16);
+  return reinterpret_cast<const float*>(W)[i];
 }
 
 __device__ __forceinline__ void fit_grid(float xmin, float xmax, float fmaxq, float& s, float& z) {
@@ -74,24 +88,48 @@ struct ColCtx {
   uint8_t* zeros;
   int64_t grid0;                    // index of the block's first group in scales/zeros
   bool live;
+  // static grids: this row's grids, the block's first natural group, and the
+  // natural column of each of the block's processed columns (activation order)
+  const float* srow;
+  const uint8_t* zrow;
+  int gfirst;
+  const int* gperm;
 };
 
 // Column JJ of the register block (the recursion makes every register index a
 // compile-time constant, so the block stays in registers).
-template <int G, int JJ>
+template <int G, bool ST, int JJ>
 __device__ __forceinline__ void column_steps(float (&w)[kRB], uint32_t (&packed)[kRB / 4], float& s,
                                              float& z, double& obs, const ColCtx& cx) {
-  if constexpr (G <= kRB && (JJ % G) == 0) {
-    float mn = w[JJ], mx = w[JJ];
-#pragma unroll
-    for (int u = 1; u < G; ++u) {
-      mn = fminf(mn, w[JJ + u]);
-      mx = fmaxf(mx, w[JJ + u]);
+  if constexpr (ST) {
+    if (cx.gperm) {
+      // activation order: each processed column keeps its natural group's grid
+      if (cx.live) {
+        const int gi = cx.gperm[JJ] / G;
+        s = cx.srow[gi];
+        z = (float)cx.zrow[gi];
+      }
+    } else {
+      if constexpr (G <= kRB && (JJ % G) == 0) {
+        if (cx.live) {
+          s = cx.srow[cx.gfirst + JJ / G];
+          z = (float)cx.zrow[cx.gfirst + JJ / G];
+        }
+      }
     }
-    fit_grid(mn, mx, cx.fmaxq, s, z);
-    if (cx.live) {
-      cx.scales[cx.grid0 + JJ / G] = s;
-      cx.zeros[cx.grid0 + JJ / G] = (uint8_t)z;
+  } else {
+    if constexpr (G <= kRB && (JJ % G) == 0) {
+      float mn = w[JJ], mx = w[JJ];
+#pragma unroll
+      for (int u = 1; u < G; ++u) {
+        mn = fminf(mn, w[JJ + u]);
+        mx = fmaxf(mx, w[JJ + u]);
+      }
+      fit_grid(mn, mx, cx.fmaxq, s, z);
+      if (cx.live) {
+        cx.scales[cx.grid0 + JJ / G] = s;
+        cx.zeros[cx.grid0 + JJ / G] = (uint8_t)z;
+      }
     }
   }
   const float* urow = cx.ublk + JJ * kRB;
@@ -105,7 +143,7 @@ __device__ __forceinline__ void column_steps(float (&w)[kRB], uint32_t (&packed)
   w[JJ] = e;
 #pragma unroll
   for (int kk = JJ + 1; kk < kRB; ++kk) w[kk] = fmaf(-e, urow[kk], w[kk]);
-  if constexpr (JJ + 1 < kRB) column_steps<G, JJ + 1>(w, packed, s, z, obs, cx);
+  if constexpr (JJ + 1 < kRB) column_steps<G, ST, JJ + 1>(w, packed, s, z, obs, cx);
 }
 
 // One 64-row x 32-column tile of the far update: the A operands (U) and the
@@ -193,7 +231,7 @@ __device__ __forceinline__ void far_update(const float (&e)[kRB], float* Wf, con
 }
 
 // Columns [c0, min(c, c0 + kSuper)) of every slab.
-template <int G>
+template <int G, bool ST>
 __global__ __launch_bounds__(64, 2) void gptq_panel_kernel(GptqPlan p, int c0, JobRange jr) {
   __shared__ float eb[kRB * 64];   // the block's errors as MFMA B operands
   const int c = p.cols;
@@ -219,8 +257,9 @@ __global__ __launch_bounds__(64, 2) void gptq_panel_kernel(GptqPlan p, int c0, J
 
   // first superblock: its columns of the fp32 working copy (rows past the
   // matrix are zero, dead columns zeroed); the first trailing update fills the
-  // later columns straight from W
-  if (c0 == 0) {
+  // later columns straight from W.  With an option on, the preparation pass
+  // has written the whole working copy.
+  if (c0 == 0 && !(p.act_order | p.static_groups)) {
     for (int r = 0; r < kGptqRows; ++r) {
       for (int col = 4 * lane; col < cend; col += 256) {
         const float4 v = r < nrows ? load_w4(job.W, job.dtype, (int64_t)(row0 + r) * c + col)
@@ -239,6 +278,8 @@ __global__ __launch_bounds__(64, 2) void gptq_panel_kernel(GptqPlan p, int c0, J
   double obs = 0.0;
   float s = 1.0f, z = 0.0f;
   float* myrow = Wf + (int64_t)lane * c;
+  const int64_t rowg = (int64_t)(row0 + lane) * ngroups_row;   // this row's first grid
+  const int* perm = p.perm ? p.perm + (int64_t)job.mat * c : nullptr;
 
   for (int i1 = c0; i1 < cend; i1 += kRB) {
     // U's diagonal block of these 64 columns into LDS (coalesced, all loads in
@@ -269,7 +310,12 @@ __global__ __launch_bounds__(64, 2) void gptq_panel_kernel(GptqPlan p, int c0, J
       w[4 * q + 2] = v.z;
       w[4 * q + 3] = v.w;
     }
-    if (G > kRB && (i1 % G) == 0) {
+    if (ST && G > kRB && (i1 % G) == 0) {
+      if (live && !perm) {
+        s = job.scales[rowg + i1 / G];
+        z = (float)job.zeros[rowg + i1 / G];
+      }
+    } else if (G > kRB && (i1 % G) == 0) {
       // group wider than the register block: its other columns are current in Wf
       float mn = INFINITY, mx = -INFINITY;
 #pragma unroll
@@ -292,9 +338,9 @@ __global__ __launch_bounds__(64, 2) void gptq_panel_kernel(GptqPlan p, int c0, J
     uint32_t packed[kRB / 4];
 #pragma unroll
     for (int q = 0; q < kRB / 4; ++q) packed[q] = 0u;
-    ColCtx cx{eb, c, fmaxq, job.scales, job.zeros,
-              (int64_t)(row0 + lane) * ngroups_row + i1 / G, live};
-    column_steps<G, 0>(w, packed, s, z, obs, cx);
+    ColCtx cx{eb, c, fmaxq, job.scales, job.zeros, rowg + i1 / G, live,
+              job.scales + rowg, job.zeros + rowg, i1 / G, perm ? perm + i1 : nullptr};
+    column_steps<G, ST, 0>(w, packed, s, z, obs, cx);
     if (live) {
       uint8_t* cp = job.codes + (int64_t)(row0 + lane) * c + i1;
 #pragma unroll
@@ -510,7 +556,7 @@ __global__ __launch_bounds__(256, 2) void gptq_trail_kernel(GptqPlan p, int c0, 
     f32x16 wv[2];
     wv[0] = f32x16{};
     wv[1] = f32x16{};
-    if (active && c0 == 0) {
+    if (active && c0 == 0 && !(p.act_order | p.static_groups)) {
       // first trailing update: the working copy of these columns does not exist
       // yet; start from W (rows past the matrix zero, dead columns zeroed)
       const uint8_t* dead = p.dead + (int64_t)job.mat * c + col0 + cl;
@@ -612,20 +658,32 @@ __global__ __launch_bounds__(256) void gptq_dist_kernel(GptqPlan p, JobRange jr)
   const int nrows = min(kGptqRows, job.rows - row0);
   const uint8_t* dead = p.dead + (int64_t)job.mat * c;
   const int ng = c / group;
-  // four consecutive columns per step (group >= 4, so they share one grid)
+  // with activation order the dead flags are in processing order: use the
+  // natural ones (H_ii == 0 of the caller's Hessian) instead
+  const float* Hsrc = p.act_order ? p.src_mats[job.mat] : nullptr;
+  const int* gidx = p.gidx ? p.gidx + (int64_t)job.mat * c : nullptr;
+  // four consecutive columns per step (without g_idx they share one grid: group >= 4)
   double acc = 0.0;
   for (int r = 0; r < nrows; ++r) {
     const int64_t row = row0 + r;
     for (int col = 4 * (int)threadIdx.x; col < c; col += 1024) {
-      const int64_t gi = row * ng + col / group;
-      const float sc = job.scales[gi], zp = (float)job.zeros[gi];
+      const int4 g4 = gidx ? *reinterpret_cast<const int4*>(gidx + col) : make_int4(0, 0, 0, 0);
+      const int gq[4] = {g4.x, g4.y, g4.z, g4.w};
       const uchar4 q = *reinterpret_cast<const uchar4*>(job.codes + row * c + col);
-      const uchar4 dd = *reinterpret_cast<const uchar4*>(dead + col);
+      uchar4 dd;
+      if (Hsrc) {
+        dd = make_uchar4(Hsrc[(int64_t)col * c + col] == 0.0f, Hsrc[(int64_t)(col + 1) * c + col + 1] == 0.0f,
+                         Hsrc[(int64_t)(col + 2) * c + col + 2] == 0.0f, Hsrc[(int64_t)(col + 3) * c + col + 3] == 0.0f);
+      } else {
+        dd = *reinterpret_cast<const uchar4*>(dead + col);
+      }
       const float4 w = load_w4(job.W, job.dtype, row * c + col);
       const float qv[4] = {(float)q.x, (float)q.y, (float)q.z, (float)q.w};
       const float wv[4] = {dd.x ? 0.f : w.x, dd.y ? 0.f : w.y, dd.z ? 0.f : w.z, dd.w ? 0.f : w.w};
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
+        const int64_t gi = row * ng + (gidx ? gq[u] : col / group);
+        const float sc = job.scales[gi], zp = (float)job.zeros[gi];
         const float what = __fmul_rn(sc, __fsub_rn(qv[u], zp));
         const double dv = (double)what - (double)wv[u];
         acc += dv * dv;
@@ -639,6 +697,163 @@ __global__ __launch_bounds__(256) void gptq_dist_kernel(GptqPlan p, JobRange jr)
     __syncthreads();
   }
   if (threadIdx.x == 0) reinterpret_cast<double*>(p.partials)[2 * (int64_t)gslab + 1] = red[0];
+}
+
+// ---------------------------------------------------------------- options
+// Processing position and grid of every column of Hessian m0 + blockIdx.x.
+// Activation order ranks the keys k_i = H_ii (1 for a dead column) by
+// decreasing value, ties by index: position(i) = #{j : k_j > k_i, or k_j = k_i
+// and j < i}.  The keys are compared as integers that order like the floats
+// (sign-magnitude to offset binary), a strict total order with the index tie
+// break, so the positions are a permutation for any input.
+__global__ __launch_bounds__(1024) void order_kernel(GptqPlan p, int m0) {
+  __shared__ uint32_t key[8192];
+  const int m = m0 + (int)blockIdx.x, c = p.cols;
+  const float* H = p.src_mats[m];
+  for (int i = threadIdx.x; i < c; i += blockDim.x) {
+    float d = H[(int64_t)i * c + i];
+    if (d == 0.0f) d = 1.0f;
+    const uint32_t u = __float_as_uint(d);
+    key[i] = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  }
+  __syncthreads();
+  int* ipos = p.ipos + (int64_t)m * c;
+  int* gidx = p.gidx + (int64_t)m * c;
+  int* perm = p.perm ? p.perm + (int64_t)m * c : nullptr;
+  for (int i = threadIdx.x; i < c; i += blockDim.x) {
+    int pos = i;
+    if (p.act_order) {
+      const uint32_t ki = key[i];
+      pos = 0;
+      for (int j = 0; j < c; ++j) {
+        const uint32_t kj = key[j];
+        pos += (kj > ki) | ((kj == ki) & (j < i));
+      }
+    }
+    ipos[i] = pos;
+    if (perm) perm[pos] = i;
+    gidx[i] = (p.act_order && !p.static_groups ? pos : i) / p.group;
+  }
+}
+
+// Hp[i][j] = H[perm[i]][perm[j]]: row i of Hessian m0 + blockIdx.y per workgroup.
+__global__ __launch_bounds__(256) void permute_h_kernel(GptqPlan p, int m0) {
+  const int c = p.cols, i = blockIdx.x, m = m0 + (int)blockIdx.y;
+  const int* perm = p.perm + (int64_t)m * c;
+  const float* Hr = p.src_mats[m] + (int64_t)perm[i] * c;
+  float* out = p.hperm + (int64_t)m * c * c + (int64_t)i * c;
+  for (int j = 4 * (int)threadIdx.x; j < c; j += 1024) {
+    const int4 pj = *reinterpret_cast<const int4*>(perm + j);
+    *reinterpret_cast<float4*>(out + j) = make_float4(Hr[pj.x], Hr[pj.y], Hr[pj.z], Hr[pj.w]);
+  }
+}
+
+// One slab per workgroup: the whole fp32 working copy in processing order
+// (rows past the matrix zero, dead columns zeroed) and, with static groups,
+// the grid of every (row, natural group) fitted on the same weights.
+__global__ __launch_bounds__(256) void gptq_prep_kernel(GptqPlan p, JobRange jr) {
+  __shared__ uint8_t deadn[8192];
+  const int c = p.cols;
+  const int gslab = jr.slab0 + (int)blockIdx.x;
+  int lo = jr.j0, hi = jr.j1;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (p.jobs[mid].slab_base <= gslab) lo = mid; else hi = mid;
+  }
+  const GJob job = p.jobs[lo];
+  const int row0 = (gslab - job.slab_base) * kGptqRows;
+  const int nrows = min(kGptqRows, job.rows - row0);
+  const float* H = p.src_mats[job.mat];
+  for (int i = threadIdx.x; i < c; i += 256) deadn[i] = H[(int64_t)i * c + i] == 0.0f;
+  __syncthreads();
+  const int* perm = p.perm ? p.perm + (int64_t)job.mat * c : nullptr;
+  float* Wf = p.wf + job.wf_off + (int64_t)row0 * c;
+  for (int r = 0; r < kGptqRows; ++r) {
+    const int64_t wrow = (int64_t)(row0 + r) * c;
+    for (int j = 4 * (int)threadIdx.x; j < c; j += 1024) {
+      float v[4] = {0.f, 0.f, 0.f, 0.f};
+      if (r < nrows) {
+        if (perm) {
+          const int4 pj = *reinterpret_cast<const int4*>(perm + j);
+          const int src[4] = {pj.x, pj.y, pj.z, pj.w};
+#pragma unroll
+          for (int u = 0; u < 4; ++u) v[u] = deadn[src[u]] ? 0.f : load_w1(job.W, job.dtype, wrow + src[u]);
+        } else {
+          const float4 t = load_w4(job.W, job.dtype, wrow + j);
+          v[0] = deadn[j] ? 0.f : t.x;
+          v[1] = deadn[j + 1] ? 0.f : t.y;
+          v[2] = deadn[j + 2] ? 0.f : t.z;
+          v[3] = deadn[j + 3] ? 0.f : t.w;
+        }
+      }
+      *reinterpret_cast<float4*>(Wf + (int64_t)r * c + j) = make_float4(v[0], v[1], v[2], v[3]);
+    }
+  }
+  if (!p.static_groups) return;
+  const int G = p.group, ng = c / G;
+  const float fmaxq = (float)((1 << job.bits) - 1);
+  for (int idx = threadIdx.x; idx < nrows * ng; idx += 256) {
+    const int r = idx / ng, g = idx - r * ng;
+    const int64_t wrow = (int64_t)(row0 + r) * c;
+    float mn = INFINITY, mx = -INFINITY;
+    for (int u = 0; u < G; ++u) {
+      const int col = g * G + u;
+      const float x = deadn[col] ? 0.f : load_w1(job.W, job.dtype, wrow + col);
+      mn = fminf(mn, x);
+      mx = fmaxf(mx, x);
+    }
+    float s, z;
+    fit_grid(mn, mx, fmaxq, s, z);
+    job.scales[(int64_t)(row0 + r) * ng + g] = s;
+    job.zeros[(int64_t)(row0 + r) * ng + g] = (uint8_t)z;
+  }
+}
+
+// Activation order: each row's codes, written in processing order, back to
+// their natural columns (code of column i = the one at position ipos[i]).
+__global__ __launch_bounds__(256) void unpermute_codes_kernel(GptqPlan p, JobRange jr) {
+  __shared__ __attribute__((aligned(16))) uint8_t rowc[8192];
+  const int c = p.cols;
+  const int gslab = jr.slab0 + (int)blockIdx.x;
+  int lo = jr.j0, hi = jr.j1;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (p.jobs[mid].slab_base <= gslab) lo = mid; else hi = mid;
+  }
+  const GJob job = p.jobs[lo];
+  const int row0 = (gslab - job.slab_base) * kGptqRows;
+  const int nrows = min(kGptqRows, job.rows - row0);
+  const int* ipos = p.ipos + (int64_t)job.mat * c;
+  for (int r = 0; r < nrows; ++r) {
+    uint8_t* cr = job.codes + (int64_t)(row0 + r) * c;
+    for (int j = 16 * (int)threadIdx.x; j < c; j += 4096)
+      *reinterpret_cast<uint4*>(rowc + j) = *reinterpret_cast<const uint4*>(cr + j);
+    __syncthreads();
+    for (int j = 4 * (int)threadIdx.x; j < c; j += 1024) {
+      const int4 q = *reinterpret_cast<const int4*>(ipos + j);
+      *reinterpret_cast<uchar4*>(cr + j) = make_uchar4(rowc[q.x], rowc[q.y], rowc[q.z], rowc[q.w]);
+    }
+    __syncthreads();
+  }
+}
+
+void launch_gptq_prep(const GptqPlan& p, const JobRange& jr, hipStream_t s) {
+  if (!(p.act_order | p.static_groups)) return;
+  const int nm = jr.m1 - jr.m0;
+  if (nm > 0) {
+    hipLaunchKernelGGL(order_kernel, dim3(nm), dim3(1024), 0, s, p, jr.m0);
+    if (p.act_order) hipLaunchKernelGGL(permute_h_kernel, dim3(p.cols, nm), dim3(256), 0, s, p, jr.m0);
+  }
+  if (jr.j1 > jr.j0) hipLaunchKernelGGL(gptq_prep_kernel, dim3(jr.n_slabs), dim3(256), 0, s, p, jr);
+}
+
+__global__ void natural_gidx_kernel(int32_t* g, int cols, int group) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < cols) g[i] = i / group;
+}
+
+void launch_natural_gidx(int32_t* g, int cols, int group, hipStream_t s) {
+  hipLaunchKernelGGL(natural_gidx_kernel, dim3((cols + 255) / 256), dim3(256), 0, s, g, cols, group);
 }
 
 __global__ void gptq_finish_kernel(GptqPlan p, JobRange jr) {
@@ -668,13 +883,24 @@ void launch_gptq(const GptqPlan& p, const JobRange& jr, hipStream_t s) {
   }
   const dim3 grid(jr.n_slabs), blk(64);
   for (int c0 = 0; c0 < p.cols; c0 += kSuper) {
-    switch (p.group) {
-      case 4: hipLaunchKernelGGL(gptq_panel_kernel<4>, grid, blk, 0, s, p, c0, jr); break;
-      case 8: hipLaunchKernelGGL(gptq_panel_kernel<8>, grid, blk, 0, s, p, c0, jr); break;
-      case 16: hipLaunchKernelGGL(gptq_panel_kernel<16>, grid, blk, 0, s, p, c0, jr); break;
-      case 32: hipLaunchKernelGGL(gptq_panel_kernel<32>, grid, blk, 0, s, p, c0, jr); break;
-      case 64: hipLaunchKernelGGL(gptq_panel_kernel<64>, grid, blk, 0, s, p, c0, jr); break;
-      default: hipLaunchKernelGGL(gptq_panel_kernel<128>, grid, blk, 0, s, p, c0, jr); break;
+    if (p.static_groups) {
+      switch (p.group) {
+        case 4: hipLaunchKernelGGL((gptq_panel_kernel<4, true>), grid, blk, 0, s, p, c0, jr); break;
+        case 8: hipLaunchKernelGGL((gptq_panel_kernel<8, true>), grid, blk, 0, s, p, c0, jr); break;
+        case 16: hipLaunchKernelGGL((gptq_panel_kernel<16, true>), grid, blk, 0, s, p, c0, jr); break;
+        case 32: hipLaunchKernelGGL((gptq_panel_kernel<32, true>), grid, blk, 0, s, p, c0, jr); break;
+        case 64: hipLaunchKernelGGL((gptq_panel_kernel<64, true>), grid, blk, 0, s, p, c0, jr); break;
+        default: hipLaunchKernelGGL((gptq_panel_kernel<128, true>), grid, blk, 0, s, p, c0, jr); break;
+      }
+    } else {
+      switch (p.group) {
+        case 4: hipLaunchKernelGGL((gptq_panel_kernel<4, false>), grid, blk, 0, s, p, c0, jr); break;
+        case 8: hipLaunchKernelGGL((gptq_panel_kernel<8, false>), grid, blk, 0, s, p, c0, jr); break;
+        case 16: hipLaunchKernelGGL((gptq_panel_kernel<16, false>), grid, blk, 0, s, p, c0, jr); break;
+        case 32: hipLaunchKernelGGL((gptq_panel_kernel<32, false>), grid, blk, 0, s, p, c0, jr); break;
+        case 64: hipLaunchKernelGGL((gptq_panel_kernel<64, false>), grid, blk, 0, s, p, c0, jr); break;
+        default: hipLaunchKernelGGL((gptq_panel_kernel<128, false>), grid, blk, 0, s, p, c0, jr); break;
+      }
     }
     const int n0 = c0 + kSuper;
     if (n0 < p.cols) {
@@ -682,6 +908,7 @@ void launch_gptq(const GptqPlan& p, const JobRange& jr, hipStream_t s) {
       hipLaunchKernelGGL(gptq_trail_kernel, dim3(per * kXcds), dim3(256), 0, s, p, c0, jr);
     }
   }
+  if (p.perm) hipLaunchKernelGGL(unpermute_codes_kernel, dim3(jr.n_slabs), dim3(256), 0, s, p, jr);
   hipLaunchKernelGGL(gptq_dist_kernel, dim3(jr.n_slabs), dim3(256), 0, s, p, jr);
   hipLaunchKernelGGL(gptq_finish_kernel, dim3(jr.j1 - jr.j0), dim3(64), 0, s, p, jr);
 }

@@ -121,6 +121,14 @@ struct GptqPlan {
   float* ebuf;               // device [padded rows][kSuper] a superblock's negated errors
   float* partials;           // device [total_slabs][2]
   int* status;
+  // GPTQ options (zero / null when off)
+  int act_order;             // columns processed by decreasing H_ii
+  int static_groups;         // grids fitted once per natural group before any update
+  const float* const* src_mats;  // device [n_mats] the callers' Hessians (mats may point at hperm)
+  float* hperm;              // device [n_mats][cols][cols] H[perm][:, perm] (activation order)
+  int* perm;                 // device [n_mats][cols] column processed j-th (activation order, else null)
+  int* ipos;                 // device [n_mats][cols] processing position of each column
+  int* gidx;                 // device [n_mats][cols] grid of each column (any option)
 };
 constexpr int kFactorStreams = 4;     // Hessian groups factored on separate streams
 void launch_factor_group(const GptqPlan& p, int m0, int m1, hipStream_t s, hipEvent_t step0_done);
@@ -130,6 +138,12 @@ struct JobRange {
   int m0, m1;   // the Hessians of these jobs
 };
 void launch_gptq(const GptqPlan& p, const JobRange& r, hipStream_t s);
+// Before the factorisation of Hessians [m0, m1) and the GPTQ of their jobs,
+// when an option is on: processing order and grid index per column, the
+// permuted Hessians, the jobs' working copies and their static grids.
+void launch_gptq_prep(const GptqPlan& p, const JobRange& r, hipStream_t s);
+// g_idx of the natural order: g[i] = i / group
+void launch_natural_gidx(int32_t* g, int cols, int group, hipStream_t s);
 
 // ---------------------------------------------------------------- loss
 void launch_loss(int rows, int cols, int group, const void* W, int dtype, const uint8_t* codes,

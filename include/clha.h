@@ -204,6 +204,41 @@ CLHA_API clha_status clha_gptq_quantize(clha_ctx* ctx, int32_t n_jobs, const clh
                                         int32_t cols, int32_t group, int32_t block, float damp,
                                         void* workspace, size_t workspace_bytes, void* stream);
 
+/* Options of clha_gptq_quantize_ex (bit flags).  Neither is on the CLHA pages, which
+ * name only "standard GPTQ"; both are common GPTQ settings.
+ *   CLHA_GPTQ_ACT_ORDER      process the columns by decreasing H_ii (a dead column counts
+ *                            as 1; ties by column index); a grid is fitted at every
+ *                            group-th processed column over the next `group` processed
+ *                            columns, so a column's grid is given by g_idx.
+ *   CLHA_GPTQ_STATIC_GROUPS  fit the grid of every row and natural group (columns
+ *                            k*group .. k*group+group-1) once, before any update, on the
+ *                            weights with dead columns zeroed; every column is then
+ *                            quantized on its natural group's grid (g_idx[i] = i/group),
+ *                            also under CLHA_GPTQ_ACT_ORDER. */
+typedef enum clha_gptq_flag {
+  CLHA_GPTQ_ACT_ORDER = 1,
+  CLHA_GPTQ_STATIC_GROUPS = 2
+} clha_gptq_flag;
+
+/* Device workspace bytes clha_gptq_quantize_ex needs for these jobs and flags.  Activation
+ * order adds a permuted copy of every distinct H (4 cols^2 bytes each). */
+CLHA_API size_t clha_gptq_workspace_bytes_ex(const clha_ctx* ctx, int32_t n_jobs,
+                                             const clha_gptq_job* jobs, int32_t cols, uint32_t flags);
+
+/* clha_gptq_quantize with options.  Codes are always returned in natural column order
+ * (codes[r][i] is column i's code); column i dequantizes as
+ *   scales[r][g_idx[i]] * (codes[r][i] - zeros[r][g_idx[i]]).
+ * The loss is that of the returned Wq (the same identity as clha_gptq_quantize).
+ *   flags      0 or an OR of clha_gptq_flag values; 0 gives clha_gptq_quantize exactly
+ *   g_idx      NULL, or a host array of n_jobs pointers, each NULL or device int32 [cols]
+ *              (4-byte aligned) that receives the job's g_idx
+ * Errors: as clha_gptq_quantize; INVALID_ARG for unknown flags, ALIGN for a misaligned
+ * g_idx pointer. */
+CLHA_API clha_status clha_gptq_quantize_ex(clha_ctx* ctx, int32_t n_jobs, const clha_gptq_job* jobs,
+                                           int32_t cols, int32_t group, int32_t block, float damp,
+                                           uint32_t flags, int32_t* const* g_idx, void* workspace,
+                                           size_t workspace_bytes, void* stream);
+
 /* Device workspace bytes clha_inverse_cholesky needs for n Hessians of size cols. */
 CLHA_API size_t clha_inverse_cholesky_workspace_bytes(const clha_ctx* ctx, int32_t n, int32_t cols);
 
