@@ -86,36 +86,51 @@ struct ColCtx {
   float fmaxq;
   float* scales;
   uint8_t* zeros;
-  int64_t grid0;                    // index of the block's first group in scales/zeros
   bool live;
-  // static grids: this row's grids, the block's first natural group, and the
-  // natural column of each of the block's processed columns (activation order)
-  const float* srow;
-  const uint8_t* zrow;
+  // static grids: the block's first natural group, the natural column of each
+  // of the block's processed columns (activation order), and the index of this
+  // row's first grid in scales/zeros.  Rows past the matrix use row 0's grids
+  // (their weights are zero, so their errors stay zero and no code is stored).
   int gfirst;
   const int* gperm;
+  uint32_t rowg;
 };
+
+// Grid modes of the column loop: fitted at each group's first column (dynamic),
+// loaded at each group's first column (static, natural order), or loaded for
+// every column, kLook columns ahead (static under activation order, where
+// consecutive processed columns belong to unrelated natural groups).
+enum { kGridFit = 0, kGridStatic = 1, kGridStaticPerm = 2 };
+constexpr int kLook = 4;
 
 // Column JJ of the register block (the recursion makes every register index a
 // compile-time constant, so the block stays in registers).
-template <int G, bool ST, int JJ>
+// Grids fitted inside a register block, stored after it (a store inside the
+// column chain would be a branch on the row's liveness, and the compiler would
+// then hoist and spill the U block).
+constexpr int grids_per_block(int G) { return G <= kRB ? kRB / G : 1; }
+
+template <int G, int MODE, int JJ>
 __device__ __forceinline__ void column_steps(float (&w)[kRB], uint32_t (&packed)[kRB / 4], float& s,
-                                             float& z, double& obs, const ColCtx& cx) {
-  if constexpr (ST) {
-    if (cx.gperm) {
-      // activation order: each processed column keeps its natural group's grid
-      if (cx.live) {
-        const int gi = cx.gperm[JJ] / G;
-        s = cx.srow[gi];
-        z = (float)cx.zrow[gi];
-      }
-    } else {
-      if constexpr (G <= kRB && (JJ % G) == 0) {
-        if (cx.live) {
-          s = cx.srow[cx.gfirst + JJ / G];
-          z = (float)cx.zrow[cx.gfirst + JJ / G];
-        }
-      }
+                                             float& z, float (&sq)[kLook], float (&zq)[kLook],
+                                             float (&sb)[grids_per_block(G)], float (&zb)[grids_per_block(G)],
+                                             double& obs, const ColCtx& cx) {
+  if constexpr (MODE == kGridStaticPerm) {
+    s = sq[JJ % kLook];
+    z = zq[JJ % kLook];
+    if constexpr (JJ + kLook < kRB) {
+      // unconditional (rows past the matrix read row 0's grids, see ColCtx):
+      // a branch here would split the column and let the compiler hoist and
+      // spill the whole U block
+      const uint32_t gi = cx.rowg + (uint32_t)(cx.gperm[JJ + kLook] / G);
+      sq[JJ % kLook] = cx.scales[gi];
+      zq[JJ % kLook] = (float)cx.zeros[gi];
+    }
+  } else if constexpr (MODE == kGridStatic) {
+    if constexpr (G <= kRB && (JJ % G) == 0) {
+      const uint32_t gi = cx.rowg + (uint32_t)(cx.gfirst + JJ / G);
+      s = cx.scales[gi];
+      z = (float)cx.zeros[gi];
     }
   } else {
     if constexpr (G <= kRB && (JJ % G) == 0) {
@@ -126,10 +141,8 @@ __device__ __forceinline__ void column_steps(float (&w)[kRB], uint32_t (&packed)
         mx = fmaxf(mx, w[JJ + u]);
       }
       fit_grid(mn, mx, cx.fmaxq, s, z);
-      if (cx.live) {
-        cx.scales[cx.grid0 + JJ / G] = s;
-        cx.zeros[cx.grid0 + JJ / G] = (uint8_t)z;
-      }
+      sb[JJ / G] = s;
+      zb[JJ / G] = z;
     }
   }
   const float* urow = cx.ublk + JJ * kRB;
@@ -143,7 +156,9 @@ __device__ __forceinline__ void column_steps(float (&w)[kRB], uint32_t (&packed)
   w[JJ] = e;
 #pragma unroll
   for (int kk = JJ + 1; kk < kRB; ++kk) w[kk] = fmaf(-e, urow[kk], w[kk]);
-  if constexpr (JJ + 1 < kRB) column_steps<G, ST, JJ + 1>(w, packed, s, z, obs, cx);
+  // keep each look-ahead load in its own column instead of all at the top
+  if constexpr (MODE == kGridStaticPerm) __builtin_amdgcn_sched_barrier(0);
+  if constexpr (JJ + 1 < kRB) column_steps<G, MODE, JJ + 1>(w, packed, s, z, sq, zq, sb, zb, obs, cx);
 }
 
 // One 64-row x 32-column tile of the far update: the A operands (U) and the
@@ -231,7 +246,7 @@ __device__ __forceinline__ void far_update(const float (&e)[kRB], float* Wf, con
 }
 
 // Columns [c0, min(c, c0 + kSuper)) of every slab.
-template <int G, bool ST>
+template <int G, int MODE>
 __global__ __launch_bounds__(64, 2) void gptq_panel_kernel(GptqPlan p, int c0, JobRange jr) {
   __shared__ float eb[kRB * 64];   // the block's errors as MFMA B operands
   const int c = p.cols;
@@ -310,12 +325,10 @@ __global__ __launch_bounds__(64, 2) void gptq_panel_kernel(GptqPlan p, int c0, J
       w[4 * q + 2] = v.z;
       w[4 * q + 3] = v.w;
     }
-    if (ST && G > kRB && (i1 % G) == 0) {
-      if (live && !perm) {
-        s = job.scales[rowg + i1 / G];
-        z = (float)job.zeros[rowg + i1 / G];
-      }
-    } else if (G > kRB && (i1 % G) == 0) {
+    if (MODE == kGridStatic && G > kRB && (i1 % G) == 0) {
+      s = job.scales[(live ? rowg : 0) + i1 / G];
+      z = (float)job.zeros[(live ? rowg : 0) + i1 / G];
+    } else if (MODE == kGridFit && G > kRB && (i1 % G) == 0) {
       // group wider than the register block: its other columns are current in Wf
       float mn = INFINITY, mx = -INFINITY;
 #pragma unroll
@@ -338,9 +351,28 @@ __global__ __launch_bounds__(64, 2) void gptq_panel_kernel(GptqPlan p, int c0, J
     uint32_t packed[kRB / 4];
 #pragma unroll
     for (int q = 0; q < kRB / 4; ++q) packed[q] = 0u;
-    ColCtx cx{eb, c, fmaxq, job.scales, job.zeros, rowg + i1 / G, live,
-              job.scales + rowg, job.zeros + rowg, i1 / G, perm ? perm + i1 : nullptr};
-    column_steps<G, ST, 0>(w, packed, s, z, obs, cx);
+    const uint32_t grow = live ? (uint32_t)rowg : 0u;
+    ColCtx cx{eb, c, fmaxq, job.scales, job.zeros, live, i1 / G, perm ? perm + i1 : nullptr, grow};
+    float sq[kLook], zq[kLook];
+#pragma unroll
+    for (int k = 0; k < kLook; ++k) {
+      sq[k] = 1.0f;
+      zq[k] = 0.0f;
+      if (MODE == kGridStaticPerm) {
+        const uint32_t gi = grow + (uint32_t)(perm[i1 + k] / G);
+        sq[k] = job.scales[gi];
+        zq[k] = (float)job.zeros[gi];
+      }
+    }
+    float sb[grids_per_block(G)], zb[grids_per_block(G)];
+    column_steps<G, MODE, 0>(w, packed, s, z, sq, zq, sb, zb, obs, cx);
+    if (MODE == kGridFit && G <= kRB && live) {
+#pragma unroll
+      for (int k = 0; k < grids_per_block(G); ++k) {
+        job.scales[rowg + i1 / G + k] = sb[k];
+        job.zeros[rowg + i1 / G + k] = (uint8_t)zb[k];
+      }
+    }
     if (live) {
       uint8_t* cp = job.codes + (int64_t)(row0 + lane) * c + i1;
 #pragma unroll
@@ -872,6 +904,18 @@ bool gptq_group_supported(int group) {
   return group == 4 || group == 8 || group == 16 || group == 32 || group == 64 || group == 128;
 }
 
+template <int MODE>
+void launch_panel(const GptqPlan& p, int c0, const JobRange& jr, dim3 grid, dim3 blk, hipStream_t s) {
+  switch (p.group) {
+    case 4: hipLaunchKernelGGL((gptq_panel_kernel<4, MODE>), grid, blk, 0, s, p, c0, jr); break;
+    case 8: hipLaunchKernelGGL((gptq_panel_kernel<8, MODE>), grid, blk, 0, s, p, c0, jr); break;
+    case 16: hipLaunchKernelGGL((gptq_panel_kernel<16, MODE>), grid, blk, 0, s, p, c0, jr); break;
+    case 32: hipLaunchKernelGGL((gptq_panel_kernel<32, MODE>), grid, blk, 0, s, p, c0, jr); break;
+    case 64: hipLaunchKernelGGL((gptq_panel_kernel<64, MODE>), grid, blk, 0, s, p, c0, jr); break;
+    default: hipLaunchKernelGGL((gptq_panel_kernel<128, MODE>), grid, blk, 0, s, p, c0, jr); break;
+  }
+}
+
 void launch_gptq(const GptqPlan& p, const JobRange& jr, hipStream_t s) {
   if (jr.j1 <= jr.j0) return;
   if (p.cols > kSuper) {
@@ -883,25 +927,9 @@ void launch_gptq(const GptqPlan& p, const JobRange& jr, hipStream_t s) {
   }
   const dim3 grid(jr.n_slabs), blk(64);
   for (int c0 = 0; c0 < p.cols; c0 += kSuper) {
-    if (p.static_groups) {
-      switch (p.group) {
-        case 4: hipLaunchKernelGGL((gptq_panel_kernel<4, true>), grid, blk, 0, s, p, c0, jr); break;
-        case 8: hipLaunchKernelGGL((gptq_panel_kernel<8, true>), grid, blk, 0, s, p, c0, jr); break;
-        case 16: hipLaunchKernelGGL((gptq_panel_kernel<16, true>), grid, blk, 0, s, p, c0, jr); break;
-        case 32: hipLaunchKernelGGL((gptq_panel_kernel<32, true>), grid, blk, 0, s, p, c0, jr); break;
-        case 64: hipLaunchKernelGGL((gptq_panel_kernel<64, true>), grid, blk, 0, s, p, c0, jr); break;
-        default: hipLaunchKernelGGL((gptq_panel_kernel<128, true>), grid, blk, 0, s, p, c0, jr); break;
-      }
-    } else {
-      switch (p.group) {
-        case 4: hipLaunchKernelGGL((gptq_panel_kernel<4, false>), grid, blk, 0, s, p, c0, jr); break;
-        case 8: hipLaunchKernelGGL((gptq_panel_kernel<8, false>), grid, blk, 0, s, p, c0, jr); break;
-        case 16: hipLaunchKernelGGL((gptq_panel_kernel<16, false>), grid, blk, 0, s, p, c0, jr); break;
-        case 32: hipLaunchKernelGGL((gptq_panel_kernel<32, false>), grid, blk, 0, s, p, c0, jr); break;
-        case 64: hipLaunchKernelGGL((gptq_panel_kernel<64, false>), grid, blk, 0, s, p, c0, jr); break;
-        default: hipLaunchKernelGGL((gptq_panel_kernel<128, false>), grid, blk, 0, s, p, c0, jr); break;
-      }
-    }
+    if (p.static_groups && p.perm) launch_panel<kGridStaticPerm>(p, c0, jr, grid, blk, s);
+    else if (p.static_groups) launch_panel<kGridStatic>(p, c0, jr, grid, blk, s);
+    else launch_panel<kGridFit>(p, c0, jr, grid, blk, s);
     const int n0 = c0 + kSuper;
     if (n0 < p.cols) {
       const int per = (jr.n_slabs + kXcds - 1) / kXcds;
