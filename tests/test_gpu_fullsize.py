@@ -117,6 +117,62 @@ def test_mid_moe_block_full_size_in_bench_configuration():
         _check_gptq(wl, w_host[e], H_ref, outputs[e], bits, f"expert {e}")
 
 
+@pytest.mark.parametrize("act,static", [(True, True), (True, False)])
+def test_mid_moe_block_full_size_gptq_options(act, static):
+    """The benchmark's step with GPTQ's options (bench.py --act-order
+    --static-groups): all 66 gate|up jobs in one batch; sampled experts against
+    the oracle, g_idx bit-exact, static grids bit-exact."""
+    import gptq_calibration_moe_amd as clha
+    from gptq_calibration_moe_amd.calibrate import SharedGroupCalibration
+
+    print(f"mid MoE block, GPTQ options act={act} static={static}", flush=True)
+    wl = gen.WORKLOADS[2]
+    inp = gen.pair_inputs(wl)
+    experts = list(range(wl.n_experts_total))
+    w_host = {e: gen.expert_weights(wl, 0, e) for e in experts}
+    n, E, K = wl.n_tokens, wl.n_routed, wl.top_k
+    ctx = clha.Context(wl.d, E, K, wl.n_shared, max_tokens=n, device=dev())
+    cal = SharedGroupCalibration(ctx, [0, 1])
+    W = {e: weights_to_dev(wl, w) for e, w in w_host.items()}
+    outputs = cal.make_outputs(experts, wl.rows, wl.group)
+    for e in experts:
+        outputs[e]["g_idx"] = torch.empty(wl.d, dtype=torch.int32, device=dev())
+    cal.reset()
+    for l in range(2):
+        cal.collect(l, bits_to_dev(inp["x"][l]), to_dev(inp["logits"][l]))
+    cal.aggregate(wl.alpha)
+    cal.quantize(W, wl.bits, wl.shared_bits, wl.group, block=wl.block, damp=wl.damp, outputs=outputs,
+                 act_order=act, static_groups=static)
+    ctx.sync()
+    rng = np.random.default_rng(11)
+    for e in sorted(rng.choice(E, 2, replace=False).tolist()):
+        S, cnt = [], []
+        for l in range(2):
+            counts, offsets, ids = oracle.bucket(oracle.route(inp["logits"][l], K), E)
+            S.append(oracle.gram(_expert_rows(inp["x"][l], ids, offsets, e)))
+            cnt.append(int(counts[e]))
+        H_ref, _ = oracle.aggregate(S, cnt, wl.alpha)
+        wv = gen.weights_value(wl, w_host[e]).astype(np.float64)
+        ref = oracle.gptq(wv, H_ref.astype(np.float32).astype(np.float64), wl.bits, wl.group, wl.damp,
+                          wl.block, act_order=act, static_groups=static)
+        out = outputs[e]
+        gi = out["g_idx"].cpu().numpy()
+        # the order is decided from H_ii: the GPU's own H_comb (within 1e-4 of
+        # H_ref) orders the same way unless two H_ii are that close
+        if not (gi == ref["g_idx"]).all():
+            d = np.sort(np.diag(H_ref))
+            assert np.min(np.diff(d) / d[1:]) < 1e-4, f"expert {e}: g_idx differs"
+        codes = out["codes"].cpu().numpy()
+        a = agree(codes, ref["codes"])
+        assert a >= CODE_AGREE, f"expert {e}: codes agree {a:.5f}"
+        sc, zp = out["scales"].cpu().numpy(), out["zeros"].cpu().numpy()
+        if static:
+            assert (sc == ref["scales"]).all() and (zp == ref["zeros"]).all(), f"expert {e}"
+        ref_loss = oracle.loss(wv, ref["wq"], H_ref)
+        got = float(out["loss"].cpu().numpy()[0])
+        assert abs(got - ref_loss) <= LOSS_RTOL * abs(ref_loss), f"expert {e}: loss {got} vs {ref_loss}"
+
+
 def test_full_depth_shapes_zipf_load_one_pair():
     import gptq_calibration_moe_amd as clha
     from gptq_calibration_moe_amd.calibrate import SharedGroupCalibration
