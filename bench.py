@@ -48,6 +48,8 @@ def parse():
     ap.add_argument("--static-groups", action="store_true", help="GPTQ with static groups")
     ap.add_argument("--profile-commands", metavar="DIR", help="print the profiling command lines and exit")
     ap.add_argument("--summarize-profiles", metavar="DIR", help="write profiles/ summaries from DIR and exit")
+    ap.add_argument("--summarize-options-profile", nargs=2, metavar=("DIR", "BENCH_JSON"),
+                    help="write the options step's trace summary and bench line under profiles/ and exit")
     ap.add_argument("--summarize-down-profile", nargs=2, metavar=("DIR", "BENCH_JSON"),
                     help="write the down_proj profile summaries from DIR and the bench output file, and exit")
     return ap.parse_args()
@@ -210,6 +212,29 @@ def summarize_down_profile(d, bench_json):
     open(os.path.join(ROOT, "profiles", "bench_down_proj_mid_moe_block.md"), "w").write("\n".join(out))
 
 
+OPTIONS_TRACE = ("timeout -k 10 400 rocprofv3 --kernel-trace --stats --output-format csv -d {dir}/trace -o run "
+                 "-- python3 bench.py --act-order --static-groups --steps 3 --warmup 1 --no-cpu-baseline")
+
+
+def summarize_options_profile(d, bench_json):
+    """Writes the kernel-trace summary and bench line of the step with GPTQ's
+    activation-order and static-group options under profiles/."""
+    lines = _trace_lines(os.path.join(d, "trace"),
+                         "# Kernel time per step, mid_moe_block workload with GPTQ activation order and "
+                         "static groups (MI355X, rocprofv3 kernel trace)", OPTIONS_TRACE.format(dir=d),
+                         ["The factorisation runs as four Hessian groups on concurrent streams, overlapped with the",
+                          "GPTQ kernels, so per-kernel times overlap in wall time; wall-clock stage times are",
+                          "`stages_ms_per_step` in the bench line."])
+    open(os.path.join(ROOT, "profiles", "gptq_options_mid_moe_block_kernel_trace.md"), "w").write("\n".join(lines))
+    line = open(bench_json).read().strip().splitlines()[-1]
+    json.loads(line)
+    out = ["# Bench line, mid MoE block with GPTQ activation order and static groups (MI355X)", "",
+           "Command (repository root):", "",
+           "    timeout -k 10 400 python3 -u bench.py --act-order --static-groups --no-cpu-baseline", "",
+           "Output:", "", "```json", line, "```", ""]
+    open(os.path.join(ROOT, "profiles", "bench_gptq_options_mid_moe_block.md"), "w").write("\n".join(out))
+
+
 def summarize_profiles(d, workload_name="mid_moe_block"):
     """Writes the kernel-trace summary and the per-kernel HBM traffic summary
     (counter values scaled by the copy probe) under profiles/."""
@@ -341,6 +366,9 @@ def main():
         return 0
     if args.summarize_profiles:
         summarize_profiles(args.summarize_profiles)
+        return 0
+    if args.summarize_options_profile:
+        summarize_options_profile(*args.summarize_options_profile)
         return 0
     if args.summarize_down_profile:
         summarize_down_profile(*args.summarize_down_profile)

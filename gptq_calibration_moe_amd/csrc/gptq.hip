@@ -678,6 +678,7 @@ __global__ __launch_bounds__(256, 2) void gptq_trail_kernel(GptqPlan p, int c0, 
 // ||Wq - W||^2 per slab (W with dead columns zeroed), coalesced over the outputs.
 __global__ __launch_bounds__(256) void gptq_dist_kernel(GptqPlan p, JobRange jr) {
   __shared__ double red[256];
+  __shared__ __attribute__((aligned(4))) uint8_t deadn[8192];
   const int c = p.cols, group = p.group;
   const int gslab = jr.slab0 + (int)blockIdx.x;
   int lo = jr.j0, hi = jr.j1;
@@ -692,7 +693,12 @@ __global__ __launch_bounds__(256) void gptq_dist_kernel(GptqPlan p, JobRange jr)
   const int ng = c / group;
   // with activation order the dead flags are in processing order: use the
   // natural ones (H_ii == 0 of the caller's Hessian) instead
-  const float* Hsrc = p.act_order ? p.src_mats[job.mat] : nullptr;
+  if (p.act_order) {
+    const float* Hsrc = p.src_mats[job.mat];
+    for (int i = threadIdx.x; i < c; i += 256) deadn[i] = Hsrc[(int64_t)i * c + i] == 0.0f;
+    __syncthreads();
+    dead = deadn;
+  }
   const int* gidx = p.gidx ? p.gidx + (int64_t)job.mat * c : nullptr;
   // four consecutive columns per step (without g_idx they share one grid: group >= 4)
   double acc = 0.0;
@@ -702,13 +708,7 @@ __global__ __launch_bounds__(256) void gptq_dist_kernel(GptqPlan p, JobRange jr)
       const int4 g4 = gidx ? *reinterpret_cast<const int4*>(gidx + col) : make_int4(0, 0, 0, 0);
       const int gq[4] = {g4.x, g4.y, g4.z, g4.w};
       const uchar4 q = *reinterpret_cast<const uchar4*>(job.codes + row * c + col);
-      uchar4 dd;
-      if (Hsrc) {
-        dd = make_uchar4(Hsrc[(int64_t)col * c + col] == 0.0f, Hsrc[(int64_t)(col + 1) * c + col + 1] == 0.0f,
-                         Hsrc[(int64_t)(col + 2) * c + col + 2] == 0.0f, Hsrc[(int64_t)(col + 3) * c + col + 3] == 0.0f);
-      } else {
-        dd = *reinterpret_cast<const uchar4*>(dead + col);
-      }
+      const uchar4 dd = *reinterpret_cast<const uchar4*>(dead + col);
       const float4 w = load_w4(job.W, job.dtype, row * c + col);
       const float qv[4] = {(float)q.x, (float)q.y, (float)q.z, (float)q.w};
       const float wv[4] = {dd.x ? 0.f : w.x, dd.y ? 0.f : w.y, dd.z ? 0.f : w.z, dd.w ? 0.f : w.w};
@@ -732,40 +732,39 @@ __global__ __launch_bounds__(256) void gptq_dist_kernel(GptqPlan p, JobRange jr)
 }
 
 // ---------------------------------------------------------------- options
-// Processing position and grid of every column of Hessian m0 + blockIdx.x.
-// Activation order ranks the keys k_i = H_ii (1 for a dead column) by
-// decreasing value, ties by index: position(i) = #{j : k_j > k_i, or k_j = k_i
-// and j < i}.  The keys are compared as integers that order like the floats
-// (sign-magnitude to offset binary), a strict total order with the index tie
-// break, so the positions are a permutation for any input.
-__global__ __launch_bounds__(1024) void order_kernel(GptqPlan p, int m0) {
+// Processing position and grid of every column of Hessian m0 + blockIdx.y,
+// 256 columns per workgroup.  Activation order ranks the keys k_i = H_ii (1 for
+// a dead column) by decreasing value, ties by index: position(i) = #{j : k_j >
+// k_i, or k_j = k_i and j < i}.  The keys are compared as integers that order
+// like the floats (sign-magnitude to offset binary), a strict total order with
+// the index tie break, so the positions are a permutation for any input.
+__global__ __launch_bounds__(256) void order_kernel(GptqPlan p, int m0) {
   __shared__ uint32_t key[8192];
-  const int m = m0 + (int)blockIdx.x, c = p.cols;
-  const float* H = p.src_mats[m];
-  for (int i = threadIdx.x; i < c; i += blockDim.x) {
-    float d = H[(int64_t)i * c + i];
-    if (d == 0.0f) d = 1.0f;
-    const uint32_t u = __float_as_uint(d);
-    key[i] = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  }
-  __syncthreads();
-  int* ipos = p.ipos + (int64_t)m * c;
-  int* gidx = p.gidx + (int64_t)m * c;
-  int* perm = p.perm ? p.perm + (int64_t)m * c : nullptr;
-  for (int i = threadIdx.x; i < c; i += blockDim.x) {
-    int pos = i;
-    if (p.act_order) {
-      const uint32_t ki = key[i];
-      pos = 0;
-      for (int j = 0; j < c; ++j) {
-        const uint32_t kj = key[j];
-        pos += (kj > ki) | ((kj == ki) & (j < i));
-      }
+  const int m = m0 + (int)blockIdx.y, c = p.cols;
+  const int i = (int)blockIdx.x * 256 + (int)threadIdx.x;
+  if (p.act_order) {
+    const float* H = p.src_mats[m];
+    for (int t = threadIdx.x; t < c; t += 256) {
+      float d = H[(int64_t)t * c + t];
+      if (d == 0.0f) d = 1.0f;
+      const uint32_t u = __float_as_uint(d);
+      key[t] = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
     }
-    ipos[i] = pos;
-    if (perm) perm[pos] = i;
-    gidx[i] = (p.act_order && !p.static_groups ? pos : i) / p.group;
+    __syncthreads();
   }
+  if (i >= c) return;
+  int pos = i;
+  if (p.act_order) {
+    const uint32_t ki = key[i];
+    pos = 0;
+    for (int j = 0; j < c; ++j) {
+      const uint32_t kj = key[j];
+      pos += (kj > ki) | ((kj == ki) & (j < i));
+    }
+    p.perm[(int64_t)m * c + pos] = i;
+  }
+  p.ipos[(int64_t)m * c + i] = pos;
+  p.gidx[(int64_t)m * c + i] = (p.act_order && !p.static_groups ? pos : i) / p.group;
 }
 
 // Hp[i][j] = H[perm[i]][perm[j]]: row i of Hessian m0 + blockIdx.y per workgroup.
@@ -782,9 +781,13 @@ __global__ __launch_bounds__(256) void permute_h_kernel(GptqPlan p, int m0) {
 
 // One slab per workgroup: the whole fp32 working copy in processing order
 // (rows past the matrix zero, dead columns zeroed) and, with static groups,
-// the grid of every (row, natural group) fitted on the same weights.
+// the grid of every (row, natural group) fitted on the same weights.  A row is
+// read once, coalesced (thread t holds natural columns 4t .. 4t+3); its static
+// grids are reduced from those registers across the group's lanes; the row
+// then goes through LDS to be written in processing order.
 __global__ __launch_bounds__(256) void gptq_prep_kernel(GptqPlan p, JobRange jr) {
   __shared__ uint8_t deadn[8192];
+  __shared__ __attribute__((aligned(16))) float rowbuf[8192];
   const int c = p.cols;
   const int gslab = jr.slab0 + (int)blockIdx.x;
   int lo = jr.j0, hi = jr.j1;
@@ -800,44 +803,53 @@ __global__ __launch_bounds__(256) void gptq_prep_kernel(GptqPlan p, JobRange jr)
   __syncthreads();
   const int* perm = p.perm ? p.perm + (int64_t)job.mat * c : nullptr;
   float* Wf = p.wf + job.wf_off + (int64_t)row0 * c;
-  for (int r = 0; r < kGptqRows; ++r) {
-    const int64_t wrow = (int64_t)(row0 + r) * c;
-    for (int j = 4 * (int)threadIdx.x; j < c; j += 1024) {
-      float v[4] = {0.f, 0.f, 0.f, 0.f};
-      if (r < nrows) {
-        if (perm) {
-          const int4 pj = *reinterpret_cast<const int4*>(perm + j);
-          const int src[4] = {pj.x, pj.y, pj.z, pj.w};
-#pragma unroll
-          for (int u = 0; u < 4; ++u) v[u] = deadn[src[u]] ? 0.f : load_w1(job.W, job.dtype, wrow + src[u]);
-        } else {
-          const float4 t = load_w4(job.W, job.dtype, wrow + j);
-          v[0] = deadn[j] ? 0.f : t.x;
-          v[1] = deadn[j + 1] ? 0.f : t.y;
-          v[2] = deadn[j + 2] ? 0.f : t.z;
-          v[3] = deadn[j + 3] ? 0.f : t.w;
-        }
-      }
-      *reinterpret_cast<float4*>(Wf + (int64_t)r * c + j) = make_float4(v[0], v[1], v[2], v[3]);
-    }
-  }
-  if (!p.static_groups) return;
   const int G = p.group, ng = c / G;
   const float fmaxq = (float)((1 << job.bits) - 1);
-  for (int idx = threadIdx.x; idx < nrows * ng; idx += 256) {
-    const int r = idx / ng, g = idx - r * ng;
+  for (int r = 0; r < kGptqRows; ++r) {
+    const bool live = r < nrows;
     const int64_t wrow = (int64_t)(row0 + r) * c;
-    float mn = INFINITY, mx = -INFINITY;
-    for (int u = 0; u < G; ++u) {
-      const int col = g * G + u;
-      const float x = deadn[col] ? 0.f : load_w1(job.W, job.dtype, wrow + col);
-      mn = fminf(mn, x);
-      mx = fmaxf(mx, x);
+    // the lanes with columns in a pass are a multiple of 16 (32 when g = 128,
+    // since then c is a multiple of 128), so a group's g/4 lanes are all active
+    for (int j = 4 * (int)threadIdx.x; j < c; j += 1024) {
+      float v[4] = {0.f, 0.f, 0.f, 0.f};
+      if (live) {
+        const float4 t = load_w4(job.W, job.dtype, wrow + j);
+        v[0] = deadn[j] ? 0.f : t.x;
+        v[1] = deadn[j + 1] ? 0.f : t.y;
+        v[2] = deadn[j + 2] ? 0.f : t.z;
+        v[3] = deadn[j + 3] ? 0.f : t.w;
+      }
+      if (perm) {
+        *reinterpret_cast<float4*>(rowbuf + j) = make_float4(v[0], v[1], v[2], v[3]);
+      } else {
+        *reinterpret_cast<float4*>(Wf + (int64_t)r * c + j) = make_float4(v[0], v[1], v[2], v[3]);
+      }
+      if (p.static_groups && live) {
+        // the G/4 lanes of a group are consecutive and aligned (G <= 128, so at
+        // most 32 lanes, within one wave)
+        float mn = fminf(fminf(v[0], v[1]), fminf(v[2], v[3]));
+        float mx = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
+        for (int off = 1; off < G / 4; off <<= 1) {
+          mn = fminf(mn, __shfl_xor(mn, off));
+          mx = fmaxf(mx, __shfl_xor(mx, off));
+        }
+        if ((j % G) == 0) {
+          float sc, zp;
+          fit_grid(mn, mx, fmaxq, sc, zp);
+          job.scales[(int64_t)(row0 + r) * ng + j / G] = sc;
+          job.zeros[(int64_t)(row0 + r) * ng + j / G] = (uint8_t)zp;
+        }
+      }
     }
-    float s, z;
-    fit_grid(mn, mx, fmaxq, s, z);
-    job.scales[(int64_t)(row0 + r) * ng + g] = s;
-    job.zeros[(int64_t)(row0 + r) * ng + g] = (uint8_t)z;
+    if (perm) {
+      __syncthreads();
+      for (int j = 4 * (int)threadIdx.x; j < c; j += 1024) {
+        const int4 pj = *reinterpret_cast<const int4*>(perm + j);
+        *reinterpret_cast<float4*>(Wf + (int64_t)r * c + j) =
+            make_float4(rowbuf[pj.x], rowbuf[pj.y], rowbuf[pj.z], rowbuf[pj.w]);
+      }
+      __syncthreads();
+    }
   }
 }
 
@@ -873,7 +885,7 @@ void launch_gptq_prep(const GptqPlan& p, const JobRange& jr, hipStream_t s) {
   if (!(p.act_order | p.static_groups)) return;
   const int nm = jr.m1 - jr.m0;
   if (nm > 0) {
-    hipLaunchKernelGGL(order_kernel, dim3(nm), dim3(1024), 0, s, p, jr.m0);
+    hipLaunchKernelGGL(order_kernel, dim3((p.cols + 255) / 256, nm), dim3(256), 0, s, p, jr.m0);
     if (p.act_order) hipLaunchKernelGGL(permute_h_kernel, dim3(p.cols, nm), dim3(256), 0, s, p, jr.m0);
   }
   if (jr.j1 > jr.j0) hipLaunchKernelGGL(gptq_prep_kernel, dim3(jr.n_slabs), dim3(256), 0, s, p, jr);

@@ -134,7 +134,7 @@ def test_mid_moe_block_full_size_gptq_options(act, static):
     ctx = clha.Context(wl.d, E, K, wl.n_shared, max_tokens=n, device=dev())
     cal = SharedGroupCalibration(ctx, [0, 1])
     W = {e: weights_to_dev(wl, w) for e, w in w_host.items()}
-    outputs = cal.make_outputs(experts, wl.rows, wl.group)
+    outputs = cal.make_outputs(experts, W[experts[0]].shape[0], wl.group)   # gate|up stacked
     for e in experts:
         outputs[e]["g_idx"] = torch.empty(wl.d, dtype=torch.int32, device=dev())
     cal.reset()
