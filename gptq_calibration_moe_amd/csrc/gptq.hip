@@ -483,21 +483,53 @@ __global__ __launch_bounds__(256) void u_digits_kernel(const float* __restrict__
 
 // One workgroup per slab (64 padded rows of one job) and superblock, sweeping
 // all of the job's trailing column tiles of 128: the slab's error digits are
-// made once, into LDS, and every column tile reuses them.  256 threads = 4
-// waves; wave w owns columns 32w..32w+31 of a tile for all 64 rows, as two
-// 32x32 blocks.  The product is transposed, C[col][row] = sum_k U^T[col][k]
-// E[row][k], so each lane's 16 results of a block are 4 runs of 4 consecutive
-// columns of one row.  Operand lanes of v_mfma_i32_32x32x32_i8: lane l holds
-// row l%32, K bytes 16(l/32)..+15 of the 32-byte step; result r of lane l is
-// row 8(r/4) + 4(l/32) + r%4, column l%32.  Each wave streams its own U
-// digits from global memory two K steps ahead in registers, so the K loop has
-// no barrier; two workgroups share a CU.  Slabs of one job are mapped to one
-// XCD (workgroup b runs on XCD b % 8), so the job's U digits are shared
-// through one L2.
-__global__ __launch_bounds__(256, 2) void gptq_trail_kernel(GptqPlan p, int c0, JobRange jr) {
+// made once, into LDS, and every column tile reuses them.  512 threads = 8
+// waves in two roles, so that the matrix-core work and the Wf traffic overlap
+// (a wave's memory counter retires in issue order, so one wave doing both
+// would wait for its Wf loads and stores at every U-digit wait):
+//   * waves 0-3 (products): wave w owns columns 32w..32w+31 of a tile for all
+//     64 rows, as two 32x32 blocks.  The product is transposed, C[col][row] =
+//     sum_k U^T[col][k] E[row][k], so each lane's 16 results of a block are 4
+//     runs of 4 consecutive columns of one row.  Operand lanes of
+//     v_mfma_i32_32x32x32_i8: lane l holds row l%32, K bytes 16(l/32)..+15 of
+//     the 32-byte step; result r of lane l is row 8(r/4) + 4(l/32) + r%4,
+//     column l%32.  Each wave streams its own U digits from global memory two
+//     K steps ahead in registers, so the K loop has no barrier.  A tile's
+//     digit sums, combined in fp32 (Horner), go to one of two LDS buffers;
+//   * waves 4-7 (weights): load the next tile's weights and column exponents
+//     while the products run, then apply Wf -= f 2^(e_row + e_col - 14) and
+//     store, coalesced by rows.
+// One barrier per tile hands a buffer from the first role to the second; the
+// buffers alternate, so a buffer is rewritten only after the second role has
+// read it (it reads before it reaches the next barrier).  Slabs of one job are
+// mapped to one XCD (workgroup b runs on XCD b % 8), so the job's U digits are
+// shared through one L2.
+constexpr int kRPitch = kGemmTile + 4;   // result buffer row pitch (floats): rows 4 banks apart
+
+// global-address-space views of the weights (the job table holds generic pointers)
+typedef const __attribute__((address_space(1))) uint16_t g_u16;
+typedef const __attribute__((address_space(1))) float g_f32;
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef const __attribute__((address_space(1))) u32x2 g_u32x2;
+typedef const __attribute__((address_space(1))) f32x4 g_f32x4;
+
+// Barrier over the workgroup's LDS only: s_waitcnt lgkmcnt(0) (vmcnt and expcnt
+// at their maxima), so this wave's LDS accesses have completed while its global
+// loads and stores stay in flight, then s_barrier.  The empty asm statements
+// keep the compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xF | (7 << 4) | (0 << 8) | (3 << 14));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__global__ __launch_bounds__(512, 1) void gptq_trail_kernel(GptqPlan p, int c0, JobRange jr) {
   // error digits: row r's 16-byte chunk ch at slot ch ^ (r % 16) (conflict-free lane reads)
   __shared__ __attribute__((aligned(16))) int8_t Eq[kTS][kGptqRows][kSuper];
   __shared__ int eE[kGptqRows];
+  __shared__ __attribute__((aligned(16))) float R[2][kGptqRows * kRPitch];
   const int c = p.cols, n0 = c0 + kSuper, sb = c0 / kSuper;
   const int total = jr.n_slabs;
   const int per = (total + kXcds - 1) / kXcds;
@@ -515,10 +547,11 @@ __global__ __launch_bounds__(256, 2) void gptq_trail_kernel(GptqPlan p, int c0, 
   const int64_t cc = (int64_t)c * c;
   const int8_t* UTq = reinterpret_cast<const int8_t*>(p.X + (int64_t)job.mat * cc);
   const int* eU = reinterpret_cast<const int*>(UTq + kTS * cc) + (int64_t)sb * c;
-  const int tid = threadIdx.x, lane = tid & 63, wc = tid >> 6, hh = lane >> 5, li = lane & 31;
+  const int tid = threadIdx.x;
+  const int n_ct = (c - n0 + kGemmTile - 1) / kGemmTile;
 
-  // ---- error digits of the slab's rows
-  {
+  // ---- error digits of the slab's rows (first role)
+  if (tid < 256) {
     const int row = tid >> 2, part = tid & 3;
     const float* er = p.ebuf + (grow + row) * kSuper + 64 * part;
     float v[64];
@@ -561,116 +594,155 @@ __global__ __launch_bounds__(256, 2) void gptq_trail_kernel(GptqPlan p, int c0, 
   }
   __syncthreads();
 
-  // ---- U digits: this lane's A operands of K step g (over all column tiles)
-  const int n_ct = (c - n0 + kGemmTile - 1) / kGemmTile;
-  const int last = n_ct * (kSuper / kTK) - 1;
-  const int lcol = wc * 32 + li;                    // the lane's operand column in a tile
-  auto fetch = [&](i32x4 (&a)[kTS], int g) {
-    g = min(g, last);
-    const int t = g / (kSuper / kTK), kc = g % (kSuper / kTK);
-    const int col = min(n0 + t * kGemmTile + lcol, c - 1);
-    const int8_t* src = UTq + (((int64_t)sb * (kSuper / kTK) + kc) * c + col) * kTK + 16 * hh;
+  if (tid < 256) {
+    // ---------------------------------------------------------- products
+    const int lane = tid & 63, wc = tid >> 6, hh = lane >> 5, li = lane & 31;
+    const int last = n_ct * (kSuper / kTK) - 1;
+    const int lcol = wc * 32 + li;                    // the lane's operand column in a tile
+    auto fetch = [&](i32x4 (&a)[kTS], int g) {
+      g = min(g, last);
+      const int t = g / (kSuper / kTK), kc = g % (kSuper / kTK);
+      const int col = min(n0 + t * kGemmTile + lcol, c - 1);
+      const int8_t* src = UTq + (((int64_t)sb * (kSuper / kTK) + kc) * c + col) * kTK + 16 * hh;
 #pragma unroll
-    for (int pp = 0; pp < kTS; ++pp) a[pp] = *reinterpret_cast<const i32x4*>(src + pp * cc);
-  };
-  i32x4 a0[kTS], a1[kTS];
-  fetch(a0, 0);
-  fetch(a1, 1);
-  const int erow[2] = {eE[li] - 14, eE[32 + li] - 14};
-  const int cl = wc * 32 + 4 * hh;                  // lane's first result column in a tile
-  int g = 0;
-  for (int t = 0; t < n_ct; ++t) {
-    const int col0 = n0 + t * kGemmTile;
-    const int ncols = min(kGemmTile, c - col0);   // 64 or 128
-    const bool active = wc * 32 < ncols;
-    float* W = p.wf + grow * c + col0;
-    // the tile's weights (consumed at the end, so their latency overlaps the products)
-    f32x16 wv[2];
-    wv[0] = f32x16{};
-    wv[1] = f32x16{};
-    if (active && c0 == 0 && !(p.act_order | p.static_groups)) {
-      // first trailing update: the working copy of these columns does not exist
-      // yet; start from W (rows past the matrix zero, dead columns zeroed)
-      const uint8_t* dead = p.dead + (int64_t)job.mat * c + col0 + cl;
-#pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        const int r = prow0 + 32 * b + li;
-        const int64_t wbase = (int64_t)r * c + col0 + cl;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float4 v = r < job.rows ? load_w4(job.W, job.dtype, wbase + 8 * q) : make_float4(0.f, 0.f, 0.f, 0.f);
-          const uchar4 dd = *reinterpret_cast<const uchar4*>(dead + 8 * q);
-          wv[b][4 * q] = dd.x ? 0.f : v.x;
-          wv[b][4 * q + 1] = dd.y ? 0.f : v.y;
-          wv[b][4 * q + 2] = dd.z ? 0.f : v.z;
-          wv[b][4 * q + 3] = dd.w ? 0.f : v.w;
-        }
-      }
-    } else if (active) {
+      for (int pp = 0; pp < kTS; ++pp) a[pp] = *reinterpret_cast<const i32x4*>(src + pp * cc);
+    };
+    i32x4 a0[kTS], a1[kTS];
+    fetch(a0, 0);
+    fetch(a1, 1);
+    const int cl = wc * 32 + 4 * hh;                  // lane's first result column in a tile
+    int g = 0;
+    for (int t = 0; t < n_ct; ++t) {
+      const int ncols = min(kGemmTile, c - (n0 + t * kGemmTile));   // 64 or 128
+      i32x16 acc[2][kTS];
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float4 v = *reinterpret_cast<const float4*>(W + (int64_t)(32 * b + li) * c + cl + 8 * q);
-          wv[b][4 * q] = v.x;
-          wv[b][4 * q + 1] = v.y;
-          wv[b][4 * q + 2] = v.z;
-          wv[b][4 * q + 3] = v.w;
-        }
-    }
-    i32x16 acc[2][kTS];
+        for (int w = 0; w < kTS; ++w) acc[b][w] = i32x16{};
+      auto step = [&](const i32x4 (&a)[kTS], int kc) {
+        i32x4 bq[2][kTS];
+        const int ch = 2 * kc + hh;
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+        for (int pp = 0; pp < kTS; ++pp)
 #pragma unroll
-      for (int w = 0; w < kTS; ++w) acc[b][w] = i32x16{};
-    auto step = [&](const i32x4 (&a)[kTS], int kc) {
-      i32x4 bq[2][kTS];
-      const int ch = 2 * kc + hh;
+          for (int b = 0; b < 2; ++b) {
+            const int row = 32 * b + li;
+            bq[b][pp] = *reinterpret_cast<const i32x4*>(&Eq[pp][row][16 * (ch ^ (row & 15))]);
+          }
+        // the two blocks alternate, so products into one accumulator are never adjacent
 #pragma unroll
-      for (int pp = 0; pp < kTS; ++pp)
+        for (int pp = 0; pp < kTS; ++pp)
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
-          const int row = 32 * b + li;
-          bq[b][pp] = *reinterpret_cast<const i32x4*>(&Eq[pp][row][16 * (ch ^ (row & 15))]);
-        }
-      // the two blocks alternate, so products into one accumulator are never adjacent
+          for (int q = 0; pp + q < kTS; ++q)
 #pragma unroll
-      for (int pp = 0; pp < kTS; ++pp)
-#pragma unroll
-        for (int q = 0; pp + q < kTS; ++q)
-#pragma unroll
-          for (int b = 0; b < 2; ++b)
-            acc[b][pp + q] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[pp], bq[b][q], acc[b][pp + q], 0, 0, 0);
-    };
-    // K steps in pairs: even steps use a0, odd ones a1, each refilled two steps ahead
+            for (int b = 0; b < 2; ++b)
+              acc[b][pp + q] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[pp], bq[b][q], acc[b][pp + q], 0, 0, 0);
+      };
+      // K steps in pairs: even steps use a0, odd ones a1, each refilled two steps ahead
 #pragma unroll 1
-    for (int kc = 0; kc < kSuper / kTK; kc += 2, g += 2) {
-      step(a0, kc);
-      fetch(a0, g + 2);
-      step(a1, kc + 1);
-      fetch(a1, g + 3);
-    }
-    if (active) {
-      // results r = 4q .. 4q+3 are columns cl + 8q .. +3 (their exponents: one int4)
+      for (int kc = 0; kc < kSuper / kTK; kc += 2, g += 2) {
+        step(a0, kc);
+        fetch(a0, g + 2);
+        step(a1, kc + 1);
+        fetch(a1, g + 3);
+      }
+      if (wc * 32 < ncols) {
+        // results r = 4q .. 4q+3 are columns cl + 8q .. +3 of row 32b + li
+        float* Rt = R[t & 1];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int4 e4 = *reinterpret_cast<const int4*>(eU + col0 + cl + 8 * q);
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            float f4[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const int r = 4 * q + u;
+              float f = (float)acc[b][kTS - 1][r];
+#pragma unroll
+              for (int w = kTS - 2; w >= 0; --w) f = fmaf(f, 1.0f / 128.0f, (float)acc[b][w][r]);
+              f4[u] = f;
+            }
+            *reinterpret_cast<float4*>(Rt + (32 * b + li) * kRPitch + cl + 8 * q) =
+                make_float4(f4[0], f4[1], f4[2], f4[3]);
+          }
+      }
+      lds_barrier();
+    }
+  } else {
+    // ---------------------------------------------------------- weights
+    // thread m: columns 4 (m % 32) .. +3 of rows m / 32 + 8 i, i = 0..7
+    const int m = tid - 256, col4 = 4 * (m & 31), rsub = m >> 5;
+    const bool fill = c0 == 0 && !(p.act_order | p.static_groups);
+    const uint8_t* dead = p.dead + (int64_t)job.mat * c;
+    float4 wv[kGptqRows / 8];
+    int4 e4;
+    auto load = [&](int t) {
+      const int col0 = n0 + t * kGemmTile;
+      const int ncols = min(kGemmTile, c - col0);
+      if (col4 >= ncols) return;
+      e4 = *reinterpret_cast<const int4*>(eU + col0 + col4);
+      if (fill) {
+        // first trailing update: the working copy of these columns does not exist
+        // yet; start from W (rows past the matrix zero, dead columns zeroed).  The
+        // loads are unconditional (row index clamped) and through global-space
+        // pointers: a flat load would also count against the LDS counter, which
+        // the barrier waits for.
+        const uchar4 dd = *reinterpret_cast<const uchar4*>(dead + col0 + col4);
+        if (job.dtype == 1) {
+          g_u16* Wb = (g_u16*)job.W;   // a C cast: reinterpret_cast cannot change address spaces
+#pragma unroll
+          for (int i = 0; i < kGptqRows / 8; ++i) {
+            const int64_t r = min(prow0 + rsub + 8 * i, job.rows - 1);
+            const u32x2 b = *(g_u32x2*)(Wb + r * c + col0 + col4);
+            wv[i] = make_float4(__uint_as_float(b.x << 16), __uint_as_float(b.x & 0xffff0000u),
+                                __uint_as_float(b.y << 16), __uint_as_float(b.y & 0xffff0000u));
+          }
+        } else {
+          g_f32* Wq = (g_f32*)job.W;
+#pragma unroll
+          for (int i = 0; i < kGptqRows / 8; ++i) {
+            const int64_t r = min(prow0 + rsub + 8 * i, job.rows - 1);
+            const f32x4 v = *(g_f32x4*)(Wq + r * c + col0 + col4);
+            wv[i] = make_float4(v.x, v.y, v.z, v.w);
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < kGptqRows / 8; ++i) {
+          const bool live = prow0 + rsub + 8 * i < job.rows;
+          wv[i] = make_float4(dd.x || !live ? 0.f : wv[i].x, dd.y || !live ? 0.f : wv[i].y,
+                              dd.z || !live ? 0.f : wv[i].z, dd.w || !live ? 0.f : wv[i].w);
+        }
+      } else {
+        const float* W = p.wf + grow * c + col0 + col4;
+#pragma unroll
+        for (int i = 0; i < kGptqRows / 8; ++i)
+          wv[i] = *reinterpret_cast<const float4*>(W + (int64_t)(rsub + 8 * i) * c);
+      }
+    };
+    load(0);
+    for (int t = 0; t < n_ct; ++t) {
+      // the barrier also retires this wave's reads of the buffer of tile t - 1
+      lds_barrier();
+      const int col0 = n0 + t * kGemmTile;
+      const int ncols = min(kGemmTile, c - col0);
+      if (col4 < ncols) {
+        const float* Rt = R[t & 1];
+        float* W = p.wf + grow * c + col0 + col4;
         const int ec[4] = {e4.x, e4.y, e4.z, e4.w};
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
+        for (int i = 0; i < kGptqRows / 8; ++i) {
+          const int row = rsub + 8 * i;
+          const float4 f = *reinterpret_cast<const float4*>(Rt + row * kRPitch + col4);
+          const int er = eE[row] - 14;
+          const float fv[4] = {f.x, f.y, f.z, f.w};
+          const float w4[4] = {wv[i].x, wv[i].y, wv[i].z, wv[i].w};
           float out[4];
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int r = 4 * q + u;
-            float f = (float)acc[b][kTS - 1][r];
-#pragma unroll
-            for (int w = kTS - 2; w >= 0; --w) f = fmaf(f, 1.0f / 128.0f, (float)acc[b][w][r]);
-            out[u] = wv[b][r] - ldexpf(f, erow[b] + ec[u]);
-          }
-          *reinterpret_cast<float4*>(W + (int64_t)(32 * b + li) * c + cl + 8 * q) =
-              make_float4(out[0], out[1], out[2], out[3]);
+          for (int u = 0; u < 4; ++u) out[u] = w4[u] - ldexpf(fv[u], er + ec[u]);
+          *reinterpret_cast<float4*>(W + (int64_t)row * c) = make_float4(out[0], out[1], out[2], out[3]);
         }
       }
+      if (t + 1 < n_ct) load(t + 1);
     }
   }
 }
@@ -945,7 +1017,7 @@ void launch_gptq(const GptqPlan& p, const JobRange& jr, hipStream_t s) {
     const int n0 = c0 + kSuper;
     if (n0 < p.cols) {
       const int per = (jr.n_slabs + kXcds - 1) / kXcds;
-      hipLaunchKernelGGL(gptq_trail_kernel, dim3(per * kXcds), dim3(256), 0, s, p, c0, jr);
+      hipLaunchKernelGGL(gptq_trail_kernel, dim3(per * kXcds), dim3(512), 0, s, p, c0, jr);
     }
   }
   if (p.perm) hipLaunchKernelGGL(unpermute_codes_kernel, dim3(jr.n_slabs), dim3(256), 0, s, p, jr);
