@@ -784,13 +784,24 @@ __global__ __launch_bounds__(256) void gptq_dist_kernel(GptqPlan p, JobRange jr)
       const float4 w = load_w4(job.W, job.dtype, row * c + col);
       const float qv[4] = {(float)q.x, (float)q.y, (float)q.z, (float)q.w};
       const float wv[4] = {dd.x ? 0.f : w.x, dd.y ? 0.f : w.y, dd.z ? 0.f : w.z, dd.w ? 0.f : w.w};
+      if (gidx) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int64_t gi = row * ng + (gidx ? gq[u] : col / group);
+        for (int u = 0; u < 4; ++u) {
+          const int64_t gi = row * ng + gq[u];
+          const float sc = job.scales[gi], zp = (float)job.zeros[gi];
+          const float what = __fmul_rn(sc, __fsub_rn(qv[u], zp));
+          const double dv = (double)what - (double)wv[u];
+          acc += dv * dv;
+        }
+      } else {
+        const int64_t gi = row * ng + col / group;     // one grid for the four columns
         const float sc = job.scales[gi], zp = (float)job.zeros[gi];
-        const float what = __fmul_rn(sc, __fsub_rn(qv[u], zp));
-        const double dv = (double)what - (double)wv[u];
-        acc += dv * dv;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float what = __fmul_rn(sc, __fsub_rn(qv[u], zp));
+          const double dv = (double)what - (double)wv[u];
+          acc += dv * dv;
+        }
       }
     }
   }
