@@ -31,6 +31,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "expert matrices calibrated/sec (Hessian+CLHA-GPTQ); SYRK % of MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0          # MI355X dense bf16 matrix peak
+PEAK_FP32_TFLOPS = 157.3           # MI355X fp32 matrix peak
+PEAK_HBM_GBS = 8000.0              # MI355X HBM3E bandwidth
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "syrk_mid_moe_block_traffic.json")
 SYRK_SRC = os.path.join(ROOT, "gptq_calibration_moe_amd", "csrc", "syrk.hip")
 
@@ -454,6 +456,24 @@ def main():
                 "flops_per_launch": flops_per_launch}
     stages_ms = {k: round(v[0] / args.steps, 4) for k, v in stages.items() if v[1]}
 
+    # gather rate on algorithmic bytes (each token read once, each routed row written once)
+    routed = [float(c[:wl.n_routed].sum()) for c in counts]
+    gather_bytes = sum(wl.n_tokens * wl.d * 2 + p * wl.d * 2 for p in routed)
+    gather_gbs = gather_bytes / (stages_ms["gather"] / 1e3) / 1e9 if stages_ms.get("gather") else None
+    # end-to-end roofline: each step's algorithmic work at the published peak of its bound
+    # (Gram sums on bf16 MFMA; inverse Cholesky (2/3)d^3 per distinct Hessian and GPTQ
+    # r c (c-1) per matrix on fp32 MFMA; the gather on HBM)
+    n_hess = wl.n_routed + (1 if wl.n_shared else 0)
+    rows_total = sum(int(W[e].shape[0]) for e in experts)
+    terms = {"gram_sums": 2 * flops_per_launch / (PEAK_BF16_TFLOPS * 1e12),
+             "inverse_cholesky": n_hess * (2.0 / 3.0) * wl.d ** 3 / (PEAK_FP32_TFLOPS * 1e12),
+             "gptq": rows_total * wl.d * (wl.d - 1) / (PEAK_FP32_TFLOPS * 1e12),
+             "gather": gather_bytes / (PEAK_HBM_GBS * 1e9)}
+    t_roof_ms = sum(terms.values()) * 1e3
+    end_to_end = {"t_roof_ms": round(t_roof_ms, 3), "frac": round(t_roof_ms / ms_per_step, 4),
+                  "terms_ms": {k: round(v * 1e3, 3) for k, v in terms.items()},
+                  "peaks": "bf16 MFMA 2500 TFLOP/s, fp32 MFMA 157.3 TFLOP/s, HBM 8000 GB/s"}
+
     out = {"metric": METRIC, "value": round(value, 2), "unit": "matrices/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
@@ -469,7 +489,8 @@ def main():
                                    "long products exact int8 digit products of 42-bit expansions; "
                                    "triangular inverse fp32; GPTQ fp32, trailing products exact int8 "
                                    "digit products of 28-bit expansions"},
-           "roofline": roofline, "stages_ms_per_step": stages_ms}
+           "roofline": roofline, "stages_ms_per_step": stages_ms,
+           "gather_gbs": round(gather_gbs, 1) if gather_gbs else None, "end_to_end_roofline": end_to_end}
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(wl, inp, w_host)
