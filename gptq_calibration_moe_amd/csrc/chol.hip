@@ -173,6 +173,83 @@ __device__ __forceinline__ int64_t lq_offset(int c, int m, int I, int K) {
   return (int64_t)m * c * c * 8 + ((int64_t)I * (c / kNb) + K) * kLqTile;
 }
 
+// Step k: L_kk = chol(T_k) and Dinv_k = L_kk^-1, by the workgroup of the
+// left-looking step that has just written T_k (its diagonal tile), so the
+// factorisation overlaps the off-diagonal tiles still in progress.  Wave 0
+// factors (lane r holds row r of T_k); wave 1 inverts (lane r holds column r
+// of X = L_kk^-1, eliminated forward on L X = I, starting from the identity);
+// waves 2 and 3 repeat wave 1's arithmetic on private registers and write
+// nothing, so that every wave of the workgroup takes the same barriers.  At
+// step J wave 0 finishes column J of L and puts it in LDS with 1 / L_JJ; then
+// the waves apply the same rank-one update with that column, read as
+// broadcasts: wave 0 to the later columns of its row, wave 1 to the rows of
+// its column below J once X_Jr is final.  The column is double-buffered, so
+// one barrier per step orders everything.  The template recursion keeps every
+// register index a compile-time constant.
+__device__ __forceinline__ double lane_value(double v, int src) {
+  const uint64_t b = __double_as_longlong(v);
+  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)b, src);
+  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(b >> 32), src);
+  return __longlong_as_double(((uint64_t)hi << 32) | lo);
+}
+
+template <int J>
+__device__ __forceinline__ void diag_step(double (&v)[kNb], int r, bool factor, bool& bad,
+                                          double (*col)[kNb + 2]) {
+  double* cj = col[J & 1];
+  if (factor) {
+    double d = lane_value(v[J], J);
+    if (!(d > 0.0)) {
+      bad = true;
+      d = 1.0;
+    }
+    const double ljj = sqrt(d);
+    if (r == J) v[J] = ljj;
+    if (r > J) v[J] = v[J] / ljj;
+    cj[r] = v[J];
+    if (r == 0) cj[kNb] = 1.0 / ljj;
+  }
+  __syncthreads();
+  if (!factor) v[J] *= cj[kNb];   // X_Jr is final (zero for r > J)
+  // rows above J of the factoring wave hold nothing of L: leave them alone
+  const double mult = (factor && r <= J) ? 0.0 : v[J];
+#pragma unroll
+  for (int cc = J + 1; cc < kNb; ++cc) v[cc] = fma(-mult, cj[cc], v[cc]);
+  if constexpr (J + 1 < kNb) diag_step<J + 1>(v, r, factor, bad, col);
+}
+
+__device__ __forceinline__ void diag_block(const double* __restrict__ A, int c, int k, int m,
+                                           double* __restrict__ dinv, int* __restrict__ status,
+                                           double (*col)[kNb + 2]) {
+  const int r = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bool factor = wave == 0;
+  const int64_t k0 = (int64_t)k * kNb;
+  double v[kNb];
+  if (factor) {
+    const double* row = A + (k0 + r) * c + k0;
+#pragma unroll
+    for (int cc = 0; cc < kNb; cc += 2) {
+      const double2 t = *reinterpret_cast<const double2*>(row + cc);
+      v[cc] = cc <= r ? t.x : 0.0;
+      v[cc + 1] = cc + 1 <= r ? t.y : 0.0;
+    }
+  } else {
+#pragma unroll
+    for (int cc = 0; cc < kNb; ++cc) v[cc] = cc == r ? 1.0 : 0.0;
+  }
+  bool bad = false;
+  diag_step<0>(v, r, factor, bad, col);
+  if (factor) {
+    if (bad && r == 0) atomicOr(status, kStatusNotPd);
+  } else if (wave == 1) {
+    // Dinv_k row-major: lane r writes column r, each store one coalesced row
+    double* D = dinv + ((int64_t)m * (c / kNb) + k) * kNb * kNb + r;
+#pragma unroll
+    for (int kk = 0; kk < kNb; ++kk) D[kk * kNb] = v[kk];
+  }
+}
+
 // ---------------------------------------------------------------- left-looking Cholesky
 // Step k, block row i >= k:  T_i = A[i][k] - sum_{m<k} L[i][m] L[k][m]^T, stored over A[i][k].
 // Four waves each own a 32x32 quarter (v_mfma_i32_32x32x32_i8: lane l holds
@@ -185,9 +262,12 @@ __global__ __launch_bounds__(256, 2) void chol_left_kernel(double* __restrict__ 
                                                            const int* __restrict__ lexp,
                                                            const float* const* __restrict__ mats,
                                                            const uint8_t* __restrict__ dead,
-                                                           const double* __restrict__ lamd, int c, int k) {
+                                                           const double* __restrict__ lamd, int c, int k,
+                                                           double* __restrict__ dinv,
+                                                           int* __restrict__ status) {
   __shared__ __align__(16) int8_t As[kSlices][kNb][kLqPitch];
   __shared__ __align__(16) int8_t Bs[kSlices][kNb][kLqPitch];
+  __shared__ __align__(16) double dcol[2][kNb + 2];
   const int m = blockIdx.y, i = k + blockIdx.x;
   const bool diag = i == k;
   double* A = Aall + (int64_t)m * c * c;
@@ -264,79 +344,11 @@ __global__ __launch_bounds__(256, 2) void chol_left_kernel(double* __restrict__ 
     if (hi == hj) a = (dead[(int64_t)m * c + hi] ? 1.0 : a) + lamd[m];
     A[(i0 + row) * c + k0 + col] = a - ldexp(sum, ex[i0 + row] + ecol);
   }
-}
-
-// Step k: L_kk = chol(T_k) and Dinv_k = L_kk^-1, one workgroup of two
-// wavefronts per matrix.  Wave 0 factors (lane r holds row r of T_k); wave 1
-// inverts (lane r holds column r of X = L_kk^-1, eliminated forward on
-// L X = I, starting from the identity).  At step J wave 0 finishes column J of
-// L and puts it in LDS with 1 / L_JJ; then both waves apply the same rank-one
-// update with that column, read as broadcasts: wave 0 to the later columns of
-// its row, wave 1 to the rows of its column below J once X_Jr is final.  The
-// column is double-buffered, so one barrier per step orders everything.  The
-// template recursion keeps every register index a compile-time constant.
-__device__ __forceinline__ double lane_value(double v, int src) {
-  const uint64_t b = __double_as_longlong(v);
-  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)b, src);
-  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(b >> 32), src);
-  return __longlong_as_double(((uint64_t)hi << 32) | lo);
-}
-
-template <int J>
-__device__ __forceinline__ void diag_step(double (&v)[kNb], int r, bool factor, bool& bad,
-                                          double (*col)[kNb + 2]) {
-  double* cj = col[J & 1];
-  if (factor) {
-    double d = lane_value(v[J], J);
-    if (!(d > 0.0)) {
-      bad = true;
-      d = 1.0;
-    }
-    const double ljj = sqrt(d);
-    if (r == J) v[J] = ljj;
-    if (r > J) v[J] = v[J] / ljj;
-    cj[r] = v[J];
-    if (r == 0) cj[kNb] = 1.0 / ljj;
-  }
-  __syncthreads();
-  if (!factor) v[J] *= cj[kNb];   // X_Jr is final (zero for r > J)
-  // rows above J of the factoring wave hold nothing of L: leave them alone
-  const double mult = (factor && r <= J) ? 0.0 : v[J];
-#pragma unroll
-  for (int cc = J + 1; cc < kNb; ++cc) v[cc] = fma(-mult, cj[cc], v[cc]);
-  if constexpr (J + 1 < kNb) diag_step<J + 1>(v, r, factor, bad, col);
-}
-
-__global__ __launch_bounds__(128) void chol_diag_kernel(const double* __restrict__ Aall, int c, int k,
-                                                        double* __restrict__ dinv,
-                                                        int* __restrict__ status) {
-  __shared__ __align__(16) double col[2][kNb + 2];
-  const int m = blockIdx.x, r = threadIdx.x & 63;
-  const bool factor = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) == 0;
-  const double* A = Aall + (int64_t)m * c * c;
-  const int64_t k0 = (int64_t)k * kNb;
-  double v[kNb];
-  if (factor) {
-    const double* row = A + (k0 + r) * c + k0;
-#pragma unroll
-    for (int cc = 0; cc < kNb; cc += 2) {
-      const double2 t = *reinterpret_cast<const double2*>(row + cc);
-      v[cc] = cc <= r ? t.x : 0.0;
-      v[cc + 1] = cc + 1 <= r ? t.y : 0.0;
-    }
-  } else {
-#pragma unroll
-    for (int cc = 0; cc < kNb; ++cc) v[cc] = cc == r ? 1.0 : 0.0;
-  }
-  bool bad = false;
-  diag_step<0>(v, r, factor, bad, col);
-  if (factor) {
-    if (bad && r == 0) atomicOr(status, kStatusNotPd);
-  } else {
-    // Dinv_k row-major: lane r writes column r, each store one coalesced row
-    double* D = dinv + ((int64_t)m * (c / kNb) + k) * kNb * kNb + r;
-#pragma unroll
-    for (int kk = 0; kk < kNb; ++kk) D[kk * kNb] = v[kk];
+  if (diag) {
+    // the whole workgroup: T_k is written, then factored and inverted
+    __threadfence_block();
+    __syncthreads();
+    diag_block(A, c, k, m, dinv, status, dcol);
   }
 }
 
@@ -657,8 +669,8 @@ void launch_factor_group(const GptqPlan& p, int m0, int m1, hipStream_t s, hipEv
   int8_t* Lq = reinterpret_cast<int8_t*>(X);   // free until the inverse starts
   hipLaunchKernelGGL(diag_stats_kernel, dim3(n), dim3(256), 0, s, mats, c, p.damp, dead, lamd, lam, lexp);
   for (int k = 0; k < nbk; ++k) {
-    hipLaunchKernelGGL(chol_left_kernel, dim3(nbk - k, n), dim3(256), 0, s, A, Lq, lexp, mats, dead, lamd, c, k);
-    hipLaunchKernelGGL(chol_diag_kernel, dim3(n), dim3(128), 0, s, A, c, k, dinv, p.status);
+    hipLaunchKernelGGL(chol_left_kernel, dim3(nbk - k, n), dim3(256), 0, s, A, Lq, lexp, mats, dead, lamd, c, k,
+                       dinv, p.status);
     if (k == 0 && step0_done) hipEventRecord(step0_done, s);
     if (k + 1 < nbk)
       hipLaunchKernelGGL(chol_panel_kernel, dim3(nbk - k - 1, n), dim3(256), 0, s, A, c, k, dinv, Lq, lexp);
