@@ -17,8 +17,9 @@
 // on ill-conditioned Hessians; GPTQ's code decisions inherit that error.  Its
 // long products (the left-looking updates) run exactly on the int8 matrix
 // cores over 42-bit digit expansions of L (see "sliced factor" below): about
-// five times the sustained fp64 matrix rate, within 2^-36 of the fp64 product.  The triangular inverse then runs in fp32 (v_mfma_f32_32x32x2f32,
-// about four times the sustained fp64 matrix rate): its error is governed by
+// five times the sustained fp64 matrix rate, within 2^-36 of the fp64 product.
+// The triangular inverse then runs in fp32 (v_mfma_f32_32x32x2f32, about four
+// times the sustained fp64 matrix rate): its error is governed by
 // cond(L) = sqrt(cond(Hd)), and it moves U by a few fp32 ulps.
 //
 // Every step is batched over all distinct Hessians of one call:
@@ -30,9 +31,10 @@
 //   that first needs it.
 //   left-looking Cholesky, per 64-column block step k:
 //     chol_left     T_i = A[i][k] - sum_{m<k} L[i][m] L[k][m]^T for block rows i >= k
-//                   (int8 digit-pair products accumulated exactly, next chunk prefetched)
-//     chol_diag     L_kk = chol(T_k) and its inverse Dinv_k (two wavefronts per matrix:
-//                   one factors, one inverts, sharing each column through LDS)
+//                   (int8 digit-pair products accumulated exactly, next chunk prefetched);
+//                   the diagonal tile's workgroup then forms L_kk = chol(T_k) and its
+//                   inverse Dinv_k (one wave factors, one inverts, sharing each column
+//                   through LDS)
 //     chol_panel    L[i][k] = T_i Dinv_k^T for i > k, and its digit planes
 //   triangular inverse X = L^-1, merged bottom-up over block ranges in fp32:
 //     trtri_leaf    X[i][i] = Dinv_i
