@@ -283,12 +283,15 @@ def _gptq_case(seed, rows, c, bits, group, dead=(), w_dtype="f32", spread=3.0):
     (55, 96, 256, 2, 16, 128, "f32", ()),            # small groups
     (56, 70, 128, 3, 4, 64, "bf16", (100,)),         # group 4, ragged rows, dead column
     (57, 300, 1024, 2, 128, 128, "bf16", ()),        # 5 slabs, 16 register blocks
+    (58, 130, 448, 3, 32, 64, "bf16", (300,)),       # trailing tiles of 128 and 64 columns, dead
+                                                     # column in the first trailing fill
+    (59, 65, 320, 2, 64, 64, "f32", ()),             # one trailing tile of 64 columns, 2 slabs
 ])
 def test_gptq_stage(seed, rows, c, bits, group, block, wdt, dead):
     import gptq_calibration_moe_amd as clha
     H, Wst, Wv = _gptq_case(seed, rows, c, bits, group, dead, wdt)
     ref = oracle.gptq(Wv, H.astype(np.float64), bits, group, 0.01, 128)
-    ctx = clha.Context(c, 4, 2, 0, 16, device=dev())
+    ctx = clha.Context(c if c % 128 == 0 else 128, 4, 2, 0, 16, device=dev())
     Wd = to_dev(Wst.view(np.int16)).view(torch.bfloat16) if wdt == "bf16" else to_dev(Wst)
     job = {"H": to_dev(H), "W": Wd, "bits": bits,
            "codes": torch.empty(rows, c, dtype=torch.uint8, device=dev()),
