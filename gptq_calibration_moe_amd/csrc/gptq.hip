@@ -82,6 +82,7 @@ typedef const __attribute__((address_space(4))) float* const_fptr;
 
 struct ColCtx {
   const float* ublk;                // the block's diagonal 64x64 U block in LDS, row stride 64
+  const float* urcp;                // 1 / U_jj of the block's columns, in LDS
   int c;
   float fmaxq;
   float* scales;
@@ -150,7 +151,9 @@ __device__ __forceinline__ void column_steps(float (&w)[kRB], uint32_t (&packed)
   float q = rintf(__fdiv_rn(x, s)) + z;
   q = fminf(fmaxf(q, 0.0f), cx.fmaxq);
   const float what = __fmul_rn(s, __fsub_rn(q, z));
-  const float e = __fdiv_rn(__fsub_rn(x, what), urow[JJ]);
+  // the error is propagation arithmetic, not a decision: multiplied by 1/U_jj,
+  // rounded once per block (within an ulp of the quotient)
+  const float e = __fmul_rn(__fsub_rn(x, what), cx.urcp[JJ]);
   packed[JJ >> 2] |= (uint32_t)q << (8 * (JJ & 3));
   obs += (double)e * (double)e;
   w[JJ] = e;
@@ -249,6 +252,7 @@ __device__ __forceinline__ void far_update(const float (&e)[kRB], float* Wf, con
 template <int G, int MODE>
 __global__ __launch_bounds__(64, 2) void gptq_panel_kernel(GptqPlan p, int c0, JobRange jr) {
   __shared__ float eb[kRB * 64];   // the block's errors as MFMA B operands
+  __shared__ float urcp[kRB];      // 1 / U_jj of the current block
   const int c = p.cols;
   const int cend = min(c, c0 + kSuper);
   const int gslab = jr.slab0 + (int)blockIdx.x;
@@ -316,6 +320,8 @@ __global__ __launch_bounds__(64, 2) void gptq_panel_kernel(GptqPlan p, int c0, J
       for (int m = 0; m < kRB * kRB / 4 / 64; ++m) *reinterpret_cast<float4*>(ul + 4 * m * kRB) = ub[m];
     }
     __syncthreads();
+    urcp[lane] = __fdiv_rn(1.0f, eb[lane * kRB + lane]);
+    __syncthreads();
     float w[kRB];
 #pragma unroll
     for (int q = 0; q < kRB / 4; ++q) {
@@ -352,7 +358,7 @@ __global__ __launch_bounds__(64, 2) void gptq_panel_kernel(GptqPlan p, int c0, J
 #pragma unroll
     for (int q = 0; q < kRB / 4; ++q) packed[q] = 0u;
     const uint32_t grow = live ? (uint32_t)rowg : 0u;
-    ColCtx cx{eb, c, fmaxq, job.scales, job.zeros, live, i1 / G, perm ? perm + i1 : nullptr, grow};
+    ColCtx cx{eb, urcp, c, fmaxq, job.scales, job.zeros, live, i1 / G, perm ? perm + i1 : nullptr, grow};
     float sq[kLook], zq[kLook];
 #pragma unroll
     for (int k = 0; k < kLook; ++k) {
