@@ -177,3 +177,39 @@ def test_option_argument_errors():
     assert st == clha.ERR_ALIGN                         # misaligned g_idx
     st = lib.clha_gptq_quantize_ex(ctx._h, 1, arr, c, 128, 128, 0.01, 1, None, ws.data_ptr(), 256, None)
     assert st == clha.ERR_WORKSPACE                     # the permuted Hessian does not fit
+
+
+def test_act_order_with_equal_diagonal_is_plain_gptq_bitwise():
+    """All H_ii equal: every key ties, the order is the natural one, and the
+    permuted Hessian is H itself, so activation order returns exactly the plain
+    result (and g_idx = column // group)."""
+    import gptq_calibration_moe_amd as clha
+    c, rows, group = 256, 130, 32
+    H = _hessian(92, c)
+    np.fill_diagonal(H, np.max(np.diag(H)))       # raising the diagonal keeps H positive definite
+    Wd, _ = _weights(92, rows, c, "bf16")
+    ctx = clha.Context(c, 4, 2, 0, 16, device=dev())
+    a = _job(to_dev(H), Wd, rows, c, 3, group)
+    b = _job(to_dev(H), Wd, rows, c, 3, group)
+    ctx.gptq_quantize([a], c, group, 128, 0.01)
+    ctx.gptq_quantize([b], c, group, 128, 0.01, act_order=True)
+    ctx.sync()
+    for k in ("codes", "scales", "zeros", "loss"):
+        assert torch.equal(a[k], b[k]), k
+    assert (b["g_idx"].cpu().numpy() == np.arange(c) // group).all()
+
+
+def test_options_runs_are_bit_identical():
+    import gptq_calibration_moe_amd as clha
+    c, rows, group = 512, 200, 64
+    H = _hessian(93, c, (11,), 5)
+    Wd, _ = _weights(93, rows, c, "bf16")
+    ctx = clha.Context(c, 4, 2, 0, 16, device=dev())
+    runs = []
+    for _ in range(2):
+        j = _job(to_dev(H), Wd, rows, c, 3, group)
+        ctx.gptq_quantize([j], c, group, 128, 0.01, act_order=True, static_groups=True)
+        runs.append(j)
+    ctx.sync()
+    for k in ("codes", "scales", "zeros", "loss", "g_idx"):
+        assert torch.equal(runs[0][k], runs[1][k]), k
