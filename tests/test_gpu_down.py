@@ -142,3 +142,59 @@ def test_down_proj_mid_moe_shapes_sampled():
     assert_down_gram(H[E].cpu().numpy(), H_ref, B[E] / int(ref_n[E]), "H shared slot")
     w_down = gen.swiglu_weights(74, 1, 128, f)[0]                  # [256, f]
     _gptq_check(down, H[E], H_ref, w_down, 3, 128, "shared slot, c = 1408")
+
+
+def test_down_proj_full_size_in_bench_configuration():
+    """The down_proj step as the benchmark runs it (bench.py --down-proj): mid
+    MoE block at 65,536 tokens per layer, both layers collected through their
+    routing, routing-frequency aggregation, GPTQ of all 66 down_proj jobs in one
+    batch; counts of both layers bit-exact, and one sampled routed expert's
+    H_comb and GPTQ against the oracle."""
+    import gptq_calibration_moe_amd as clha
+    from gptq_calibration_moe_amd.calibrate import SharedGroupCalibration
+    print("down_proj full size, bench configuration", flush=True)
+    wl = gen.WORKLOADS[2]
+    n, E, K, nsh, f, dm = wl.n_tokens, wl.n_routed, wl.top_k, wl.n_shared, wl.rows, wl.d
+    inp = gen.pair_inputs(wl)
+    main = clha.Context(dm, E, K, 0, n, device=dev())
+    down = clha.Context(f, E + nsh, K, 0, n, device=dev())
+    wgu_bits = [gen.expert_weights(wl, 0, e) for e in range(E + nsh)]
+    wgu = [bits_to_dev(w) for w in wgu_bits]
+    wd_bits = [gen.swiglu_weights(2000 + e, 1, dm // 2, f)[0] for e in range(E + nsh)]
+    routing = []
+    for l in range(2):
+        main.register_layer(l, *main.new_layer_buffers())
+        ids = torch.empty(n * K, dtype=torch.int32, device=dev())
+        off = torch.empty(E + 1, dtype=torch.int64, device=dev())
+        main.collect_hessians(l, bits_to_dev(inp["x"][l]), to_dev(inp["logits"][l]), offsets_out=off,
+                              token_ids_out=ids)
+        routing.append((ids, off))
+    cal = SharedGroupCalibration(down, [0, 1])
+    outputs = cal.make_outputs(range(E + nsh), dm, wl.group)
+    jobs = [{"H": cal.H[e], "W": bits_to_dev(wd_bits[e]), "bits": wl.bits, **outputs[e]}
+            for e in range(E + nsh)]
+    prep = down.prepare_gptq(jobs, f)
+    cal.reset()
+    for l in range(2):
+        down.collect_down_hessians(l, bits_to_dev(inp["x"][l]), routing[l][0], routing[l][1], wgu, E)
+    cal.aggregate("rt")
+    down.run_gptq(prep, wl.group, 128, wl.damp)
+    down.sync()
+    e = int(np.random.default_rng(12).integers(E))
+    S, cnt, B = [], [], []
+    for l in range(2):
+        ref_S, ref_n, ref_B = _down_ref(inp["x"][l], inp["logits"][l], wgu_bits, E, K, f, [e])
+        assert np.array_equal(cal.counts[l].cpu().numpy(), ref_n), f"layer {l} counts"
+        S.append(ref_S[e])
+        cnt.append(int(ref_n[e]))
+        B.append(ref_B[e])
+    H_ref, _ = oracle.aggregate(S, cnt, "rt")
+    assert_down_gram(cal.H[e].cpu().numpy(), H_ref, (B[0] + B[1]) / (cnt[0] + cnt[1]), f"H_comb expert {e}")
+    wv = oracle.bf16_to_f64(wd_bits[e])
+    ref = oracle.gptq(wv, H_ref, wl.bits, wl.group, wl.damp, 128)
+    codes = outputs[e]["codes"].cpu().numpy()
+    a = agree(codes, ref["codes"])
+    assert a >= CODE_AGREE, f"expert {e}: codes agree {a:.5f}"
+    want = oracle.loss(wv, ref["wq"], H_ref)
+    got = float(outputs[e]["loss"].cpu().numpy()[0])
+    assert abs(got - want) <= LOSS_RTOL * abs(want), f"expert {e}: loss {got} vs {want}"
