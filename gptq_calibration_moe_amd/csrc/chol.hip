@@ -424,9 +424,14 @@ __global__ __launch_bounds__(256) void chol_panel_kernel(double* __restrict__ Aa
 // (the inverse of a 2x2 block lower-triangular matrix).  Level s merges ranges
 // of 2s blocks (s = 1, 2, 4, ...); merges of one level are independent.  The
 // leaves are the fp64 diagonal-block inverses Dinv of the factorisation.
-// The factor L is fp64; the merges run in fp32 on the matrix cores
-// (v_mfma_f32_32x32x2f32): the inverse is well conditioned relative to the
-// factor (cond(L) = sqrt(cond(Hd))), and U is stored in fp32 in any case.
+// The factor L is fp64; the merges run at fp32 precision on the bf16 matrix
+// cores: every operand x is split into three bf16 parts, x = x1 + x2 + x3 to
+// within 2^-25 |x| (x1 = bf16(x), x2 = bf16(x - x1), x3 = bf16(x - x1 - x2)), and
+// a product is the sum of the six part products above 2^-24 of it (x1y1, x1y2,
+// x2y1, x1y3, x3y1, x2y2), each exact in fp32 and accumulated in fp32
+// (v_mfma_f32_32x32x16_bf16, about 2.7 times the fp32 matrix rate).  The
+// inverse is well conditioned relative to the factor (cond(L) = sqrt(cond(Hd))),
+// and U is stored in fp32 in any case.
 // Each merge is two batched GEMMs:
 //   phase 0:  T = L21 X11     (X11 lower triangular: only k >= column counts)
 //   phase 1:  X21 = -X22 T    (X22 lower triangular: only k <= row counts)
@@ -463,28 +468,36 @@ __global__ __launch_bounds__(256) void trtri_leaf_kernel(int c, const double* __
 }
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kTT = 128;          // merge tile: rows and columns
-constexpr int kTK = 32;           // K chunk
-constexpr int kTP = kTK + 4;      // LDS row pitch (floats): conflict-free 16-byte lane reads
-constexpr int kTBuf = kTT * kTP;  // one operand buffer (floats)
+constexpr int kTK = 16;           // K chunk (one MFMA step)
+constexpr int kTRow = 48;         // LDS row pitch (bytes) of one bf16 part: 16 k + padding,
+                                  // so the 16-byte fragment reads of 16 lanes hit distinct banks
+constexpr int kTPart = kTT * kTRow;     // one part of one operand (bytes)
+constexpr int kTBuf = 6 * kTPart;       // one stage: three parts of A, three of B
+
+// bf16 round to nearest even of an fp32 value (finite inputs), as raw bits
+__device__ __forceinline__ uint32_t bf16_bits_rne(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
 
 // One 128x128 tile of one merge.  256 threads = 4 waves of 64x64 (2x2 blocks of
-// v_mfma_f32_32x32x2f32).  Both operands are K-contiguous rows staged through
-// LDS in chunks of 32, double-buffered with two register stages; MFMA step s
-// contracts k = s in lanes 0..31 and k = 16 + s in lanes 32..63 (one
-// permutation of k for both operands), so a lane's operands of a chunk are 4
-// contiguous 16-byte LDS reads.  Phase 0 walks K downwards from the merge's
-// common end, phase 1 upwards from its common start, so the tiles of a merge
-// read the same chunks at about the same time; tiles of one merge are mapped
-// to one XCD (workgroup b runs on XCD b % 8).
+// v_mfma_f32_32x32x16_bf16, six part products each).  Both operands are
+// K-contiguous rows staged through LDS in chunks of 16 as three bf16 parts,
+// double-buffered with two register stages; a lane's operand fragment of a
+// block is one 16-byte LDS read per part (row l%32, k 8(l/32) .. +7).  Phase 0
+// walks K downwards from the merge's common end, phase 1 upwards from its
+// common start, so the tiles of a merge read the same chunks at about the same
+// time; tiles of one merge are mapped to one XCD (workgroup b runs on XCD b % 8).
 template <int PHASE>
 __global__ __launch_bounds__(256, 2) void trtri_merge_kernel(const double* __restrict__ Aall,
                                                              double* __restrict__ Xall,
                                                              float* __restrict__ Uall,
                                                              float* __restrict__ UTall, int c, int s,
                                                              int n_merge, int tc, int n_mats) {
-  __shared__ __attribute__((aligned(16))) float lds[4 * kTBuf];   // A0 B0 A1 B1
+  __shared__ __attribute__((aligned(16))) char lds[2 * kTBuf];   // stage 0, stage 1
   const int nbk = c / kNb, tmax = tc * tc;
   const int total = n_mats * n_merge * tmax;
   const int per = (total + kXcds - 1) / kXcds;
@@ -499,7 +512,7 @@ __global__ __launch_bounds__(256, 2) void trtri_merge_kernel(const double* __res
   if (nr <= 0 || nc <= 0) return;
   const int k0 = PHASE == 0 ? c0 : mid * kNb;
   const int k1 = PHASE == 0 ? mid * kNb : min(r0 + kTT, b * kNb);
-  const int nch = (k1 - k0) / kTK;   // even: K ranges are multiples of 64
+  const int nch = (k1 - k0) / kTK;   // a multiple of 4: K ranges are multiples of 64
   const double* A = Aall + (int64_t)m * c * c;
   float* X32 = reinterpret_cast<float*>(Xall + (int64_t)m * c * c);
   float* XT32 = X32 + (int64_t)c * c;
@@ -514,10 +527,10 @@ __global__ __launch_bounds__(256, 2) void trtri_merge_kernel(const double* __res
   // triangular masks happen when the stage is written to LDS, so a prefetch
   // is never waited for before its turn.
   struct Stage {
-    double2 alo[4], ahi[4];   // phase 0: fp64 A operand
-    float4 a[4], b[4];
+    double2 alo[2], ahi[2];   // phase 0: fp64 A operand
+    float4 a[2], b[2];
   };
-  // thread t moves 16-byte chunks q = t + 256u: row q/8, k = 4(q%8) .. +3.
+  // thread t moves 16-byte chunks q = t + 256u: row q/4, k = 4(q%4) .. +3.
   // Every fetch is unconditional (chunk and row indices are clamped into
   // range), so the compiler counts outstanding loads exactly; clamped rows
   // (past nr or nc) only feed waves that are inactive for this tile.
@@ -528,8 +541,8 @@ __global__ __launch_bounds__(256, 2) void trtri_merge_kernel(const double* __res
   auto fetch = [&](Stage& rg, int ch) {
     const int kb = chunk_base(ch);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int q = tid + 256 * u, row = q >> 3, kk = kb + 4 * (q & 7);
+    for (int u = 0; u < 2; ++u) {
+      const int q = tid + 256 * u, row = q >> 2, kk = kb + 4 * (q & 3);
       const int ra = min(row, nr - 1), rb = min(row, nc - 1);
       if (PHASE == 0) {
         const double* src = A + (int64_t)(r0 + ra) * c + kk;
@@ -542,13 +555,32 @@ __global__ __launch_bounds__(256, 2) void trtri_merge_kernel(const double* __res
       }
     }
   };
+  // four values -> three bf16 parts, each four consecutive k (8 bytes) of one row
+  auto put_parts = [&](char* base, int row, int kc, const float (&v)[4]) {
+    uint32_t w[3][2];
+    float r[4] = {v[0], v[1], v[2], v[3]};
+#pragma unroll
+    for (int p = 0; p < 3; ++p) {
+      uint32_t hb[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        hb[e] = bf16_bits_rne(r[e]);
+        r[e] = r[e] - __uint_as_float(hb[e] << 16);   // exact: the remainder of a rounding
+      }
+      w[p][0] = hb[0] | (hb[1] << 16);
+      w[p][1] = hb[2] | (hb[3] << 16);
+    }
+#pragma unroll
+    for (int p = 0; p < 3; ++p)
+      *reinterpret_cast<uint2*>(base + p * kTPart + row * kTRow + 2 * kc) = make_uint2(w[p][0], w[p][1]);
+  };
   auto stage = [&](const Stage& rg, int buf, int ch) {
     const int kb = chunk_base(ch);
-    float* As = lds + (2 * buf) * kTBuf;
-    float* Bs = lds + (2 * buf + 1) * kTBuf;
+    char* As = lds + buf * kTBuf;
+    char* Bs = As + 3 * kTPart;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int q = tid + 256 * u, row = q >> 3, kc = 4 * (q & 7), kk = kb + kc;
+    for (int u = 0; u < 2; ++u) {
+      const int q = tid + 256 * u, row = q >> 2, kc = 4 * (q & 3), kk = kb + kc;
       float4 va, vb = rg.b[u];
       if (PHASE == 0) {
         va = make_float4((float)rg.alo[u].x, (float)rg.alo[u].y, (float)rg.ahi[u].x, (float)rg.ahi[u].y);
@@ -567,8 +599,9 @@ __global__ __launch_bounds__(256, 2) void trtri_merge_kernel(const double* __res
         va.z = kk + 2 > rr ? 0.f : va.z;
         va.w = kk + 3 > rr ? 0.f : va.w;
       }
-      *reinterpret_cast<float4*>(As + row * kTP + kc) = va;
-      *reinterpret_cast<float4*>(Bs + row * kTP + kc) = vb;
+      const float fa[4] = {va.x, va.y, va.z, va.w}, fb[4] = {vb.x, vb.y, vb.z, vb.w};
+      put_parts(As, row, kc, fa);
+      put_parts(Bs, row, kc, fb);
     }
   };
   f32x16 acc[2][2];
@@ -578,24 +611,28 @@ __global__ __launch_bounds__(256, 2) void trtri_merge_kernel(const double* __res
     for (int y = 0; y < 2; ++y) acc[x][y] = f32x16{};
   auto multiply = [&](int buf) {
     if (!active) return;
-    const float* As = lds + (2 * buf) * kTBuf + (wm * 64 + li) * kTP + 16 * h;
-    const float* Bs = lds + (2 * buf + 1) * kTBuf + (wn * 64 + li) * kTP + 16 * h;
-    float4 av[2][4], bv[2][4];
+    const char* As = lds + buf * kTBuf + (wm * 64 + li) * kTRow + 16 * h;
+    const char* Bs = lds + buf * kTBuf + 3 * kTPart + (wn * 64 + li) * kTRow + 16 * h;
+    bf16x8 av[2][3], bv[2][3];
 #pragma unroll
-    for (int mm = 0; mm < 4; ++mm)
+    for (int x = 0; x < 2; ++x)
 #pragma unroll
-      for (int x = 0; x < 2; ++x) {
-        av[x][mm] = *reinterpret_cast<const float4*>(As + 32 * x * kTP + 4 * mm);
-        bv[x][mm] = *reinterpret_cast<const float4*>(Bs + 32 * x * kTP + 4 * mm);
+      for (int p = 0; p < 3; ++p) {
+        av[x][p] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(As + p * kTPart + 32 * x * kTRow));
+        bv[x][p] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Bs + p * kTPart + 32 * x * kTRow));
       }
+    // smallest part products first; x1 y1 last
 #pragma unroll
-    for (int st = 0; st < 16; ++st)
+    for (int x = 0; x < 2; ++x)
 #pragma unroll
-      for (int x = 0; x < 2; ++x)
-#pragma unroll
-        for (int y = 0; y < 2; ++y)
-          acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x2f32((&av[x][st >> 2].x)[st & 3],
-                                                           (&bv[y][st >> 2].x)[st & 3], acc[x][y], 0, 0, 0);
+      for (int y = 0; y < 2; ++y) {
+        acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[x][1], bv[y][1], acc[x][y], 0, 0, 0);
+        acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[x][0], bv[y][2], acc[x][y], 0, 0, 0);
+        acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[x][2], bv[y][0], acc[x][y], 0, 0, 0);
+        acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[x][0], bv[y][1], acc[x][y], 0, 0, 0);
+        acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[x][1], bv[y][0], acc[x][y], 0, 0, 0);
+        acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[x][0], bv[y][0], acc[x][y], 0, 0, 0);
+      }
   };
 
   Stage g0, g1;
