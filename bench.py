@@ -487,8 +487,9 @@ def main():
                          if args.act_order or args.static_groups else {}),
                       "precision": "Gram sums bf16 in / fp32 accumulate; Cholesky fp64 values, its "
                                    "long products exact int8 digit products of 42-bit expansions; "
-                                   "triangular inverse fp32-precision (three bf16 parts per operand); GPTQ fp32, trailing products exact int8 "
-                                   "digit products of 28-bit expansions"},
+                                   "triangular inverse at fp32 precision (three bf16 parts per operand); "
+                                   "GPTQ fp32, trailing products exact int8 digit products of 28-bit "
+                                   "expansions"},
            "roofline": roofline, "stages_ms_per_step": stages_ms,
            "gather_gbs": round(gather_gbs, 1) if gather_gbs else None, "end_to_end_roofline": end_to_end}
     if not args.no_cpu_baseline:
