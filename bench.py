@@ -379,8 +379,8 @@ def main():
         copy_probe(args.copy_probe)
         return 0
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (every run here uses "
-              "exactly one MI355X; the multi-GPU design is described, not built)", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the multi-GPU "
+              "exchange is designed, not built)", file=sys.stderr)
         return 2
     if args.down_proj:
         return down_proj_bench(args)
