@@ -266,11 +266,17 @@ __global__ __launch_bounds__(256, 2) void chol_left_kernel(double* __restrict__ 
                                                            const uint8_t* __restrict__ dead,
                                                            const double* __restrict__ lamd, int c, int k,
                                                            double* __restrict__ dinv,
-                                                           int* __restrict__ status) {
+                                                           int* __restrict__ status, int n_mats) {
   __shared__ __align__(16) int8_t As[kSlices][kNb][kLqPitch];
   __shared__ __align__(16) int8_t Bs[kSlices][kNb][kLqPitch];
   __shared__ __align__(16) double dcol[2][kNb + 2];
-  const int m = blockIdx.y, i = k + blockIdx.x;
+  // the tiles of one Hessian run on one XCD (workgroup b runs on XCD b % 8), so
+  // its B panel, read by all of them, is fetched into one L2
+  const int nt = c / kNb - k, total = nt * n_mats;
+  const int per = (total + kXcds - 1) / kXcds;
+  const int L = (int)(blockIdx.x % kXcds) * per + (int)(blockIdx.x / kXcds);
+  if (L >= total) return;   // the whole workgroup, before any barrier
+  const int m = L / nt, i = k + L % nt;
   const bool diag = i == k;
   double* A = Aall + (int64_t)m * c * c;
   const int64_t i0 = (int64_t)i * kNb, k0 = (int64_t)k * kNb;
@@ -358,10 +364,15 @@ __global__ __launch_bounds__(256, 2) void chol_left_kernel(double* __restrict__ 
 __global__ __launch_bounds__(256) void chol_panel_kernel(double* __restrict__ Aall, int c, int k,
                                                          const double* __restrict__ dinv,
                                                          int8_t* __restrict__ Lq,
-                                                         const int* __restrict__ lexp) {
+                                                         const int* __restrict__ lexp, int n_mats) {
   __shared__ double Ts[kNb][kNb + 1];
   __shared__ double Ds[kNb][kNb + 1];
-  const int m = blockIdx.y, i = k + 1 + blockIdx.x;
+  // the tiles of one Hessian run on one XCD, so its Dinv_k is fetched into one L2
+  const int nt = c / kNb - k - 1, total = nt * n_mats;
+  const int per = (total + kXcds - 1) / kXcds;
+  const int L = (int)(blockIdx.x % kXcds) * per + (int)(blockIdx.x / kXcds);
+  if (L >= total) return;   // the whole workgroup, before any barrier
+  const int m = L / nt, i = k + 1 + L % nt;
   double* A = Aall + (int64_t)m * c * c;
   const double* D = dinv + ((int64_t)m * (c / kNb) + k) * kNb * kNb;
   const int64_t i0 = (int64_t)i * kNb, k0 = (int64_t)k * kNb;
@@ -708,11 +719,14 @@ void launch_factor_group(const GptqPlan& p, int m0, int m1, hipStream_t s, hipEv
   int8_t* Lq = reinterpret_cast<int8_t*>(X);   // free until the inverse starts
   hipLaunchKernelGGL(diag_stats_kernel, dim3(n), dim3(256), 0, s, mats, c, p.damp, dead, lamd, lam, lexp);
   for (int k = 0; k < nbk; ++k) {
-    hipLaunchKernelGGL(chol_left_kernel, dim3(nbk - k, n), dim3(256), 0, s, A, Lq, lexp, mats, dead, lamd, c, k,
-                       dinv, p.status);
+    const int per = ((nbk - k) * n + kXcds - 1) / kXcds;
+    hipLaunchKernelGGL(chol_left_kernel, dim3(per * kXcds), dim3(256), 0, s, A, Lq, lexp, mats, dead, lamd, c, k,
+                       dinv, p.status, n);
     if (k == 0 && step0_done) hipEventRecord(step0_done, s);
-    if (k + 1 < nbk)
-      hipLaunchKernelGGL(chol_panel_kernel, dim3(nbk - k - 1, n), dim3(256), 0, s, A, c, k, dinv, Lq, lexp);
+    if (k + 1 < nbk) {
+      const int pper = ((nbk - k - 1) * n + kXcds - 1) / kXcds;
+      hipLaunchKernelGGL(chol_panel_kernel, dim3(pper * kXcds), dim3(256), 0, s, A, c, k, dinv, Lq, lexp, n);
+    }
   }
   hipLaunchKernelGGL(trtri_leaf_kernel, dim3(nbk, n), dim3(256), 0, s, c, dinv, X, U, UT);
   for (int sz = 1; sz < nbk; sz *= 2) {
