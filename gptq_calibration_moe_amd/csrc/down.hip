@@ -19,8 +19,9 @@
 // staged through two LDS buffers in chunks of 32 from two register stages;
 // rows are 64 bytes with the four 16-byte chunks of row r at slots
 // c ^ ((r >> 2) & 3); each chunk is fetched two products ahead of its
-// staging.  The output is written feature-major per slot, [f][n_pad]
-// bf16 with zeros for the padding tokens: the layout the Gram-sum kernel reads.
+// staging.  The output is bf16 with zeros for the padding tokens, in the
+// layout the Gram-sum kernel reads: per slot, blocks of 32 tokens, each block
+// [f][32] (element (feature, t) at ((t/32)*f + feature)*32 + t%32).
 #include "kernels.h"
 
 namespace clha {
@@ -168,7 +169,7 @@ __global__ __launch_bounds__(256, 2) void down_gemm_kernel(const uint16_t* __res
         const int feat = f0 + 64 * wf + 32 * a + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
         const float g = acc[0][a][b][r], u = acc[1][a][b][r];
         const float h = tok < cnt ? g / (1.0f + expf(-g)) * u : 0.0f;
-        out[(int64_t)feat * npad + tok] = bf16_rne(h);
+        out[((tok >> 5) * f + feat) * 32 + (tok & 31)] = bf16_rne(h);
       }
     }
 }

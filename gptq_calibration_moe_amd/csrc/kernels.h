@@ -53,7 +53,7 @@ struct CollectPlan {
   int syrk_items;        // Gram-sum items per segment
   int overwrite;         // first collection after a reset: S and counts are stored, not added
   int32_t* token_ids;    // [n*K]
-  uint16_t* xgT;         // feature-major gathered activations
+  uint16_t* xgT;         // gathered activations: per slot, 32-token blocks of [d][32]
   int64_t xg_tiles;      // upper bound of 64-token tiles over all slots
   int* status;
 };
@@ -63,7 +63,7 @@ void launch_bucket(const CollectPlan& p, int64_t* layer_counts, hipStream_t s);
 void launch_gather(const uint16_t* x, const CollectPlan& p, hipStream_t s);
 void launch_syrk(const CollectPlan& p, float* S, const int64_t* layer_counts, hipStream_t s);
 // down_proj inputs: plan from a layer's routing, and the grouped SwiGLU GEMM
-// writing each slot's h^T (feature-major, like the gathered activations)
+// writing each slot's h^T (in the gathered activations' 32-token blocks)
 void launch_down_scan(const int64_t* routed_offsets, int64_t n, int E, const CollectPlan& p,
                       int64_t* layer_counts, int32_t* tile_off, hipStream_t s);
 void launch_down_gemm(const uint16_t* x, int d_model, const int32_t* token_ids, const int64_t* routed_offsets,

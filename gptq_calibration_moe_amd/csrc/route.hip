@@ -1,5 +1,5 @@
 // Collection phase, first half: top-K routing, per-expert bucketing and the
-// gather of each expert's rows into a feature-major layout.
+// gather of each expert's rows into a token-blocked, feature-major layout.
 //
 // CLHA summary, section 2.2 (collection): per calibration batch, every layer
 // accumulates a Hessian and a token count for each expert that is active for
@@ -14,10 +14,14 @@
 //                                   each slot padded to a multiple of 64 tokens;
 //                                   slot E (if the block has shared experts) holds
 //                                   all N tokens in order
-//   xgT         bf16  per slot e a [d][npad_e] feature-major matrix at
-//                     xgT + pad_off[e]*d; padding columns are zero
-// Feature-major storage puts the Gram sum's contraction index (tokens) in
-// contiguous memory, which is the operand layout the matrix cores read.
+//   xgT         bf16  per slot e, at xgT + pad_off[e]*d: npad_e/32 blocks of
+//                     32 tokens, each block [d][32] (feature-major inside the
+//                     block); element (f, t) at ((t/32)*d + f)*32 + t%32;
+//                     padding tokens are zero
+// Inside a block the Gram sum's contraction index (tokens) is contiguous, which
+// is the operand layout the matrix cores read, and the 32-token step of 256
+// features that one Gram-sum workgroup reads is one contiguous 16 KB run, so
+// every 128-byte line it fetches is used whole in one step.
 #include "kernels.h"
 
 namespace clha {
@@ -328,11 +332,16 @@ void launch_bucket(const CollectPlan& p, int64_t* layer_counts, hipStream_t s) {
 }
 
 // ------------------------------------------------------------------ gather
-// One workgroup of 128 threads moves a 64-token x 128-feature tile.  Thread
-// (q, fc) reads 8 token rows x 8 features (16 B per row, 256 B contiguous per
-// row across the 16 threads of a token group), transposes the 8x8 bf16 block in
-// registers and writes 8 feature rows x 8 tokens (128 B contiguous per feature
-// across the 8 threads q = 0..7).  Tiles past the last slot exit at once.
+// One workgroup of 128 threads moves a 64-token x 128-feature tile, i.e. two
+// 32-token blocks of 128 features, each 8 KB contiguous in xgT.  Thread
+// (q, fc) = (tid / 16, tid % 16) reads 8 token rows x 8 features (16 B per row,
+// 256 B contiguous per row across the 16 threads of a token group), transposes
+// the 8x8 bf16 block in registers and puts each feature's 8 tokens (16 B) into
+// an LDS copy of the two blocks; the workgroup then writes the blocks out in
+// order, 16 B per thread, so each wave stores 1 KB contiguous.  In LDS a
+// feature row is 64 B with 16 B of padding after every 8 features, which keeps
+// both the transposed writes and the in-order reads free of bank conflicts.
+// Tiles past the last slot exit at once.
 
 __device__ __forceinline__ uint32_t lo_pair(uint32_t a, uint32_t b) {
   return (a & 0xffffu) | (b << 16);
@@ -341,10 +350,18 @@ __device__ __forceinline__ uint32_t hi_pair(uint32_t a, uint32_t b) {
   return (a >> 16) | (b & 0xffff0000u);
 }
 
+constexpr int kGatherBlk = 128 * 64 + 16 * 16;   // LDS bytes of one 32-token block of 128 features
+
+// LDS byte offset of the 16 B holding tokens 8*qq .. 8*qq+7 of feature f in block b.
+__device__ __forceinline__ int gather_lds_off(int b, int f, int qq) {
+  return b * kGatherBlk + f * 64 + (f >> 3) * 16 + qq * 16;
+}
+
 __global__ __launch_bounds__(128) void gather_kernel(
     const uint16_t* __restrict__ x, int64_t n, int d, int E, int has_shared,
     const int64_t* __restrict__ offsets, const int64_t* __restrict__ pad_off,
     const int32_t* __restrict__ token_ids, uint16_t* __restrict__ xgT) {
+  __shared__ __attribute__((aligned(16))) char tile[2 * kGatherBlk];
   const int slots = E + has_shared;
   const int64_t p0 = (int64_t)blockIdx.x * kTokPad;
   const int64_t total = pad_off[slots];
@@ -355,14 +372,13 @@ __global__ __launch_bounds__(128) void gather_kernel(
     if (pad_off[mid] <= p0) lo = mid; else hi = mid;
   }
   const int s = lo;
-  const int64_t npad = pad_off[s + 1] - pad_off[s];
-  const int64_t i0 = p0 - pad_off[s];
+  const int64_t i0 = p0 - pad_off[s];    // a multiple of 64
   const bool routed = s < E;
   const int64_t cnt = routed ? offsets[s + 1] - offsets[s] : n;
   const int32_t* ids = token_ids + (routed ? offsets[s] : 0);
-  const int q = threadIdx.x & 7;         // token group of 8
-  const int fc = threadIdx.x >> 3;       // feature group of 8 (0..15)
-  const int f0 = blockIdx.y * 128 + fc * 8;
+  const int q = threadIdx.x >> 4;        // token group of 8 (0..7)
+  const int fc = threadIdx.x & 15;       // feature group of 8 (0..15)
+  const int fbase = blockIdx.y * 128;
 
   uint4 in[8];
 #pragma unroll
@@ -371,10 +387,9 @@ __global__ __launch_bounds__(128) void gather_kernel(
     in[u] = make_uint4(0, 0, 0, 0);
     if (i < cnt) {
       const int64_t tok = routed ? (int64_t)ids[i] : i;
-      in[u] = *reinterpret_cast<const uint4*>(x + tok * d + f0);
+      in[u] = *reinterpret_cast<const uint4*>(x + tok * d + fbase + fc * 8);
     }
   }
-  uint16_t* out = xgT + pad_off[s] * d + i0 + q * 8;
 #pragma unroll
   for (int fp = 0; fp < 4; ++fp) {       // feature pair (2fp, 2fp+1) inside the 8
     uint32_t a[8];
@@ -385,8 +400,18 @@ __global__ __launch_bounds__(128) void gather_kernel(
     e.z = lo_pair(a[4], a[5]); e.w = lo_pair(a[6], a[7]);
     o.x = hi_pair(a[0], a[1]); o.y = hi_pair(a[2], a[3]);
     o.z = hi_pair(a[4], a[5]); o.w = hi_pair(a[6], a[7]);
-    *reinterpret_cast<uint4*>(out + (int64_t)(f0 + 2 * fp) * npad) = e;
-    *reinterpret_cast<uint4*>(out + (int64_t)(f0 + 2 * fp + 1) * npad) = o;
+    *reinterpret_cast<uint4*>(tile + gather_lds_off(q >> 2, fc * 8 + 2 * fp, q & 3)) = e;
+    *reinterpret_cast<uint4*>(tile + gather_lds_off(q >> 2, fc * 8 + 2 * fp + 1, q & 3)) = o;
+  }
+  __syncthreads();
+  // block b of the tile is 32-token block i0/32 + b of the slot: 128 features x 64 B
+  uint16_t* out = xgT + pad_off[s] * d + (i0 >> 5) * ((int64_t)d * 32) + (int64_t)fbase * 32;
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    const int c = r * 128 + threadIdx.x;   // 16-byte chunk of the tile in output order
+    const int b = c >> 9, w = c & 511;
+    const uint4 v = *reinterpret_cast<const uint4*>(tile + gather_lds_off(b, w >> 2, w & 3));
+    *reinterpret_cast<uint4*>(out + (int64_t)b * d * 32 + w * 8) = v;
   }
 }
 

@@ -27,8 +27,11 @@
 // four LDS stages filled by direct global-to-LDS loads (global_load_lds_dwordx4)
 // issued three steps ahead, so no registers stage the operands and each load
 // has three steps of products to arrive.  Each wave waits for its own loads of
-// the step (vmcnt) and one barrier per step publishes them.  Operand tiles are
-// feature-major [256 features][32 tokens] with 64-byte rows; a lane's MFMA
+// the step (vmcnt) and one barrier per step publishes them.  The activations
+// are stored in blocks of 32 tokens, each block [d features][32 tokens], so a
+// step's operand panel (256 features x 32 tokens) is one contiguous 16 KB run
+// and every 128-byte line fetched is used whole in the step that fetches it.
+// Operand tiles are [256 features][32 tokens] with 64-byte rows; a lane's MFMA
 // fragment (8 consecutive tokens of one feature) is one 16-byte chunk, and the
 // four chunks of row r sit at slots c ^ ((r >> 2) & 3), which makes the
 // fragment reads bank-conflict free.
@@ -69,15 +72,16 @@ __device__ __forceinline__ void wait_loads() {
 // Byte offset in a stage of 16-byte chunk c (0..3) of row r.
 __device__ __forceinline__ int chunk_off(int r, int c) { return r * 64 + ((c ^ ((r >> 2) & 3)) << 4); }
 
-// The token pipeline shared by both item kinds.  Ag / Bg: feature-major rows of
-// the two panels (row stride npad); when !loadB only Ag is used.
+// The token pipeline shared by both item kinds.  Ag / Bg: the two panels' first
+// rows in a 32-token block (row stride kSK, block stride bstride = d * kSK);
+// t0, a multiple of kSK, is the first token; when !loadB only Ag is used.
 // multiply(stage) runs one 32-token step from LDS stage `stage`; flush(first)
 // adds the running sums.  Steps past nsteps are padding: their loads re-read
 // the last step (clamped, always in range) and they run no products, so every
 // wave issues the same loads, waits and barriers.
 template <class Mul, class Flush>
 __device__ __forceinline__ void token_loop(const uint16_t* __restrict__ Ag, const uint16_t* __restrict__ Bg,
-                                           int64_t npad, int64_t t0, int64_t nsteps, int arows, int brows,
+                                           int64_t bstride, int64_t t0, int64_t nsteps, int arows, int brows,
                                            bool loadB, const Stages& sb, Mul&& multiply, Flush&& flush) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (!loadB) {
@@ -92,11 +96,11 @@ __device__ __forceinline__ void token_loop(const uint16_t* __restrict__ Ag, cons
   for (int j = 0; j < 2; ++j) {
     const int row = 16 * (2 * wave + j) + (lane >> 2);
     const int c = (lane & 3) ^ ((row >> 2) & 3);
-    pa[j] = Ag + (int64_t)min(row, arows - 1) * npad + t0 + c * 8;
-    pb[j] = Bg + (int64_t)min(row, brows - 1) * npad + t0 + c * 8;
+    pa[j] = Ag + (int64_t)min(row, arows - 1) * kSK + (t0 / kSK) * bstride + c * 8;
+    pb[j] = Bg + (int64_t)min(row, brows - 1) * kSK + (t0 / kSK) * bstride + c * 8;
   }
   auto issue = [&](int stage, int64_t st) {
-    const int64_t k0 = (st < nsteps ? st : nsteps - 1) * kSK;
+    const int64_t k0 = (st < nsteps ? st : nsteps - 1) * bstride;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       __builtin_amdgcn_global_load_lds((glb_ptr)(pa[j] + k0), (lds_ptr)(sb.a[stage] + (2 * wave + j) * 512), 16, 0, 0);
@@ -153,7 +157,7 @@ __device__ __forceinline__ void flush_block(f32x16& acc, float* __restrict__ Sd,
 }
 
 // Off-diagonal tile (ti, tj), ti > tj: waves 2x4, each 128x64.
-__device__ __forceinline__ void syrk_offdiag(const uint16_t* base, int64_t npad, int64_t t0, int64_t nsteps,
+__device__ __forceinline__ void syrk_offdiag(const uint16_t* base, int64_t t0, int64_t nsteps,
                                              int d, int ti, int tj, float* Sd, bool partial, const Stages& sb) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 2, wn = wave & 3;
@@ -191,14 +195,14 @@ __device__ __forceinline__ void syrk_offdiag(const uint16_t* base, int64_t npad,
         flush_block(acc[bi][bj], Sd, d, ti * kT + wm * 128 + bi * 32, tj * kT + wn * 64 + bj * 32, false,
                     store, lane);
   };
-  token_loop(base + (int64_t)ti * kT * npad, base + (int64_t)tj * kT * npad, npad, t0, nsteps,
+  token_loop(base + (int64_t)ti * kT * kSK, base + (int64_t)tj * kT * kSK, (int64_t)d * kSK, t0, nsteps,
              min(kT, d - ti * kT), min(kT, d - tj * kT), true, sb, multiply, flush);
 }
 
 // Diagonal pair: this wave's share of panel P's diagonal tile -- block rows
 // 7-K (columns 0..7-K) and K (columns 0..K) -- read from LDS buffer half `pb`.
 template <int K>
-__device__ __forceinline__ void syrk_diag_wave(const uint16_t* Ag, const uint16_t* Bg, bool loadB, int64_t npad,
+__device__ __forceinline__ void syrk_diag_wave(const uint16_t* Ag, const uint16_t* Bg, bool loadB, int64_t bstride,
                                                int64_t t0, int64_t nsteps, int d, int P, int pb, bool active,
                                                float* Sd, bool partial, int arows, int brows, const Stages& sb) {
   constexpr int R1 = 7 - K, R2 = K, NA = 8 - K;   // NA fragments: panel blocks 0..7-K
@@ -234,7 +238,7 @@ __device__ __forceinline__ void syrk_diag_wave(const uint16_t* Ag, const uint16_
     for (int cb = 0; cb <= R2; ++cb)
       flush_block(acc[NA + cb], Sd, d, P * kT + R2 * 32, P * kT + cb * 32, cb == R2, store, lane);
   };
-  token_loop(Ag, Bg, npad, t0, nsteps, arows, brows, loadB, sb, multiply, flush);
+  token_loop(Ag, Bg, bstride, t0, nsteps, arows, brows, loadB, sb, multiply, flush);
 }
 
 __device__ __forceinline__ void tile_of(int t, int& ti, int& tj) {
@@ -252,7 +256,6 @@ __device__ __forceinline__ void syrk_item(const uint16_t* __restrict__ xgT, cons
                                           const Stages& sb) {
   const int slot = seg[4 * sg], dest = seg[4 * sg + 1];
   const int64_t t0 = seg[4 * sg + 2], ntok = seg[4 * sg + 3];
-  const int64_t npad = pad_off[slot + 1] - pad_off[slot];
   const uint16_t* base = xgT + pad_off[slot] * d;
   const int64_t dd = (int64_t)d * d;
   float* Sd = dest < 0 ? S + (int64_t)slot * dd : partials + (int64_t)dest * dd;
@@ -264,7 +267,7 @@ __device__ __forceinline__ void syrk_item(const uint16_t* __restrict__ xgT, cons
   if (item >= nd) {
     int a, b;
     tile_of(item - nd, a, b);
-    syrk_offdiag(base, npad, t0, nsteps, d, a + 1, b, Sd, partial, sb);
+    syrk_offdiag(base, t0, nsteps, d, a + 1, b, Sd, partial, sb);
     return;
   }
   const int p = item, q = nt - 1 - item;
@@ -272,14 +275,15 @@ __device__ __forceinline__ void syrk_item(const uint16_t* __restrict__ xgT, cons
   const int wave = threadIdx.x >> 6, hp = wave >> 2, k = wave & 3;
   const int P = hp ? q : p;
   const bool active = !(hp && single);
-  const uint16_t* Ag = base + (int64_t)p * kT * npad;
-  const uint16_t* Bg = base + (int64_t)q * kT * npad;
+  const uint16_t* Ag = base + (int64_t)p * kT * kSK;
+  const uint16_t* Bg = base + (int64_t)q * kT * kSK;
+  const int64_t bstride = (int64_t)d * kSK;
   const int arows = min(kT, d - p * kT), brows = min(kT, d - q * kT);
   switch (k) {
-    case 0: syrk_diag_wave<0>(Ag, Bg, !single, npad, t0, nsteps, d, P, hp, active, Sd, partial, arows, brows, sb); break;
-    case 1: syrk_diag_wave<1>(Ag, Bg, !single, npad, t0, nsteps, d, P, hp, active, Sd, partial, arows, brows, sb); break;
-    case 2: syrk_diag_wave<2>(Ag, Bg, !single, npad, t0, nsteps, d, P, hp, active, Sd, partial, arows, brows, sb); break;
-    default: syrk_diag_wave<3>(Ag, Bg, !single, npad, t0, nsteps, d, P, hp, active, Sd, partial, arows, brows, sb); break;
+    case 0: syrk_diag_wave<0>(Ag, Bg, !single, bstride, t0, nsteps, d, P, hp, active, Sd, partial, arows, brows, sb); break;
+    case 1: syrk_diag_wave<1>(Ag, Bg, !single, bstride, t0, nsteps, d, P, hp, active, Sd, partial, arows, brows, sb); break;
+    case 2: syrk_diag_wave<2>(Ag, Bg, !single, bstride, t0, nsteps, d, P, hp, active, Sd, partial, arows, brows, sb); break;
+    default: syrk_diag_wave<3>(Ag, Bg, !single, bstride, t0, nsteps, d, P, hp, active, Sd, partial, arows, brows, sb); break;
   }
 }
 
