@@ -137,6 +137,9 @@ __device__ __forceinline__ void token_loop(const uint16_t* __restrict__ Ag, cons
 
 // Adds (or, for the first flush into a partial buffer, stores) one 32x32
 // accumulator block at (row0, col0) of Sd; lower triangle and i, j < d only.
+// S is touched once per flush, so its loads and stores are non-temporal: they
+// stream past the L2, which keeps the activation panels other workgroups of
+// the die are still reading.
 __device__ __forceinline__ void flush_block(f32x16& acc, float* __restrict__ Sd, int d, int row0, int col0,
                                             bool diag, bool store, int lane) {
   // An opaque zero keeps the element addresses from being hoisted out of the
@@ -150,7 +153,8 @@ __device__ __forceinline__ void flush_block(f32x16& acc, float* __restrict__ Sd,
   for (int r = 0; r < 16; ++r) {
     const int i = row0 + 8 * (r >> 2) + 4 * kh + (r & 3);
     float* e = p + (int64_t)(8 * (r >> 2) + (r & 3)) * d;
-    if ((!diag || i >= j) && i < d && j < d) *e = store ? acc[r] : *e + acc[r];
+    if ((!diag || i >= j) && i < d && j < d)
+      __builtin_nontemporal_store(store ? acc[r] : __builtin_nontemporal_load(e) + acc[r], e);
     acc[r] = 0.0f;
   }
   __builtin_amdgcn_sched_barrier(0);
