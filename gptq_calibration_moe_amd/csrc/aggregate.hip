@@ -14,7 +14,9 @@
 // stated for n layers); explicit weights may also differ per expert slot.
 //
 // Each workgroup reads one 64x64 lower-triangular tile of every layer's S and
-// writes the tile and its mirror image, so H comes out full and symmetric.
+// writes the tile and its mirror image, so H comes out full and symmetric.  A
+// thread's four 16-byte positions of a layer are loaded together before they
+// are summed, which keeps four loads in flight per thread.
 #include "kernels.h"
 
 namespace clha {
@@ -92,51 +94,63 @@ __global__ __launch_bounds__(256) void aggregate_kernel(AggArgs g, float* __rest
   const float ftotal = (float)total;
   float* Hs = H + (int64_t)slot * d * d;
   const int64_t soff = (int64_t)slot * d * d;
-  // four consecutive columns per thread (16-byte loads and stores)
-  for (int idx = threadIdx.x; idx < 64 * 16; idx += 256) {
-    const int r = idx >> 4, c = 4 * (idx & 15);
-    if (diag && c > r) continue;
-    const int i = ti * 64 + r, j = tj * 64 + c;
-    const int64_t e = (int64_t)i * d + j;
-    float v[4];
-    if (w.identity) {
+  // four 16-byte positions per thread (row r = idx / 16, columns c .. c+3, idx =
+  // tid + 256k); every layer's loads of the four are issued before their sums.
+  // On a diagonal tile the positions above the diagonal are loaded and summed
+  // as well (in range, never stored), so all threads issue the same loads.
+  float v[4][4];
+  if (w.identity) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] = (i == j + u) ? 1.0f : 0.0f;
-    } else if (w.rt) {
-      float sum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-      for (int l = 0; l < g.n_layers; ++l) {
-        if (n[l] == 0) continue;   // a layer without tokens for this slot drops out
-        const float4 x = *reinterpret_cast<const float4*>(g.S[l] + soff + e);
-        sum[0] = __fadd_rn(sum[0], x.x);
-        sum[1] = __fadd_rn(sum[1], x.y);
-        sum[2] = __fadd_rn(sum[2], x.z);
-        sum[3] = __fadd_rn(sum[3], x.w);
-      }
+    for (int k = 0; k < 4; ++k) {
+      const int idx = threadIdx.x + 256 * k, r = idx >> 4, c = 4 * (idx & 15);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] = __fdiv_rn(sum[u], ftotal);
-    } else {
-      float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-      for (int l = 0; l < g.n_layers; ++l) {
-        if (w.a[l] != 0.0f && n[l] > 0) {
-          const float4 x = *reinterpret_cast<const float4*>(g.S[l] + soff + e);
-          const float xs[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-          for (int u = 0; u < 4; ++u) acc[u] = __fadd_rn(acc[u], __fmul_rn(w.a[l], __fdiv_rn(xs[u], (float)n[l])));
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] = acc[u];
+      for (int u = 0; u < 4; ++u) v[k][u] = (ti * 64 + r == tj * 64 + c + u) ? 1.0f : 0.0f;
     }
+  } else {
+    float acc[4][4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) acc[k][u] = 0.0f;
+    for (int l = 0; l < g.n_layers; ++l) {
+      // a layer without tokens for this slot drops out (and, with explicit or
+      // equal weights, so does a layer of weight zero)
+      if (n[l] == 0 || (!w.rt && w.a[l] == 0.0f)) continue;
+      float4 x[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int idx = threadIdx.x + 256 * k, r = idx >> 4, c = 4 * (idx & 15);
+        x[k] = *reinterpret_cast<const float4*>(g.S[l] + soff + (int64_t)(ti * 64 + r) * d + tj * 64 + c);
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float xs[4] = {x[k].x, x[k].y, x[k].z, x[k].w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          acc[k][u] = w.rt ? __fadd_rn(acc[k][u], xs[u])
+                           : __fadd_rn(acc[k][u], __fmul_rn(w.a[l], __fdiv_rn(xs[u], (float)n[l])));
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[k][u] = w.rt ? __fdiv_rn(acc[k][u], ftotal) : acc[k][u];
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int idx = threadIdx.x + 256 * k, r = idx >> 4, c = 4 * (idx & 15);
+    if (diag && c > r) continue;
+    const int64_t e = (int64_t)(ti * 64 + r) * d + tj * 64 + c;
     // on a diagonal tile, columns past the row are above the diagonal: S is not
     // written there, so those values come from the mirror write below instead
 #pragma unroll
-    for (int u = 0; u < 4; ++u) T[r][c + u] = v[u];
+    for (int u = 0; u < 4; ++u) T[r][c + u] = v[k][u];
     if (!diag || c + 3 <= r) {
-      *reinterpret_cast<float4*>(Hs + e) = make_float4(v[0], v[1], v[2], v[3]);
+      *reinterpret_cast<float4*>(Hs + e) = make_float4(v[k][0], v[k][1], v[k][2], v[k][3]);
     } else {
 #pragma unroll
       for (int u = 0; u < 4; ++u)
-        if (c + u <= r) Hs[e + u] = v[u];
+        if (c + u <= r) Hs[e + u] = v[k][u];
     }
   }
   __syncthreads();
