@@ -158,7 +158,9 @@ __device__ void plan_gram(const int64_t* cnt, PlanLds& L, int slots, int64_t* __
   if (threadIdx.x == 0) {
     int64_t total = 0;
     for (int e = 0; e < slots; ++e) total += L.padc[e];
-    const int64_t target = ((total / (8 * kXcds)) / kTokPad + 1) * kTokPad;
+    // segment target length in 64-token chunks; the splitting below runs in
+    // 32-bit chunk counts (64-bit division is a long instruction sequence)
+    const int target = (int)((total / (8 * kXcds)) / kTokPad + 1);
     int64_t load[kXcds];
     int32_t len[kXcds];
     for (int x = 0; x < kXcds; ++x) {
@@ -168,9 +170,9 @@ __device__ void plan_gram(const int64_t* cnt, PlanLds& L, int slots, int64_t* __
     int nseg = 0, nsplit = 0, used = 0;
     for (int r = 0; r < slots; ++r) {
       const int e = L.order[r];
-      const int64_t chunks = L.padc[e] / kTokPad;
+      const int chunks = (int)(L.padc[e] / kTokPad);
       if (chunks == 0) continue;
-      int64_t k = (L.padc[e] + target - 1) / target;
+      int k = (chunks + target - 1) / target;
       k = k < kXcds ? k : kXcds;
       k = k < 1 + kMaxPartials - used ? k : 1 + kMaxPartials - used;
       k = k < chunks ? k : chunks;
@@ -180,9 +182,10 @@ __device__ void plan_gram(const int64_t* cnt, PlanLds& L, int slots, int64_t* __
         split[3 + 3 * nsplit] = (int32_t)(k - 1);
         ++nsplit;
       }
-      int64_t b = 0;
-      for (int j = 0; j < (int)k; ++j) {
-        const int64_t nc = chunks / k + (j < chunks % k ? 1 : 0);
+      const int per = chunks / k, rem = chunks - per * k;
+      int b = 0;
+      for (int j = 0; j < k; ++j) {
+        const int nc = per + (j < rem ? 1 : 0);
         seg[4 * nseg] = e;
         seg[4 * nseg + 1] = j == 0 ? -1 : used + j - 1;
         seg[4 * nseg + 2] = (int32_t)(b * kTokPad);
@@ -225,12 +228,21 @@ __global__ __launch_bounds__(256) void bucket_scan_kernel(
   __shared__ int64_t cnt[kMaxSlots];
   __shared__ PlanLds L;
   const int slots = E + has_shared;
+  // 16 blocks' counts are loaded together, so a thread waits for memory once
+  // per 16 blocks rather than once per block
+  constexpr int kScanBatch = 16;
   for (int e = threadIdx.x; e < E; e += 256) {
     int64_t run = 0;
-    for (int b = 0; b < nblk; ++b) {
-      const int c = blockcounts[(int64_t)b * E + e];
-      blockbase[(int64_t)b * E + e] = (int32_t)run;
-      run += c;
+    for (int b0 = 0; b0 < nblk; b0 += kScanBatch) {
+      int c[kScanBatch];
+#pragma unroll
+      for (int j = 0; j < kScanBatch; ++j)
+        c[j] = b0 + j < nblk ? blockcounts[(int64_t)(b0 + j) * E + e] : 0;
+#pragma unroll
+      for (int j = 0; j < kScanBatch; ++j) {
+        if (b0 + j < nblk) blockbase[(int64_t)(b0 + j) * E + e] = (int32_t)run;
+        run += c[j];
+      }
     }
     cnt[e] = run;
   }
