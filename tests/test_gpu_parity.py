@@ -364,7 +364,10 @@ def test_end_to_end_clha_mp_small():
     """CLHA-MP: shared experts at b+1 bits against the all-token Hessian."""
     wl = gen.WORKLOADS[4].scaled(d=256, n_tokens=4096, n_routed=8, top_k=2, rows=96, n_pairs=1)
     r, ref = _e2e(wl, gen.pair_inputs(wl), [0, 3, 8, 9])
-    assert r["gptq"][8]["codes"].max() <= 7 and r["gptq"][0]["codes"].max() <= 3
+    for e in (8, 9):                      # shared experts: the 3-bit range is used
+        assert 4 <= r["gptq"][e]["codes"].max() <= 7, e
+    for e in (0, 3):                      # routed experts stay at 2 bits
+        assert r["gptq"][e]["codes"].max() <= 3, e
 
 
 def test_drift_zero_clha_equals_plic_bitwise():

@@ -813,3 +813,110 @@ def test_sharpness_logits_limits():
     assert oracle.topk_overlap(*sharp) == 1.0
     flat = [oracle.route(gen.sharpness_logits(wl, 0, l, xa, 1e3), wl.top_k) for l in range(2)]
     assert abs(oracle.topk_overlap(*flat) - wl.top_k / wl.n_routed) < 0.05
+
+
+# =========================================================================== whole pair
+
+def _pair_case():
+    """Two layers of 12 tokens over d = 8, two routed experts at top-1 and one
+    shared expert (CLHA section 2.3: it sees every token).  The winning expert
+    of each token is planted in the logits, so the routed token sets are known
+    without the oracle's routing."""
+    rng = _rng(70)
+    d, n = 8, 12
+    x = [gen.bf16_bits(rng.standard_normal((n, d)).astype(np.float32)) for _ in range(2)]
+    win = [np.array([0, 1, 1, 0, 0, 1, 0, 1, 1, 1, 0, 1]), np.array([1, 1, 0, 0, 1, 1, 1, 1, 0, 1, 1, 1])]
+    logits = []
+    for wv in win:
+        lg = rng.uniform(-1.0, 0.0, (n, 2)).astype(np.float32)
+        lg[np.arange(n), wv] += 2.0
+        logits.append(lg)
+    jobs = {e: rng.normal(0, 0.02, (4, d)) for e in range(3)}    # 2 = the shared expert
+    return x, logits, win, jobs
+
+
+def _brute_hessians(x, win, mode):
+    """Sums of outer products over each job's tokens, per layer and combined:
+    routed expert e over the tokens whose planted winner is e, the shared
+    expert over all tokens."""
+    xs = [gen.bf16_value(b).astype(np.float64) for b in x]
+    per_layer = {}
+    for e in range(3):
+        S, n = [], []
+        for l in range(2):
+            rows = [t for t in range(xs[l].shape[0]) if e == 2 or win[l][t] == e]
+            S.append(sum(np.outer(xs[l][t], xs[l][t]) for t in rows))
+            n.append(len(rows))
+        per_layer[e] = (S, n)
+    H = {}
+    for e, (S, n) in per_layer.items():
+        if mode == "rt":
+            H[e] = (S[0] + S[1]) / (n[0] + n[1])
+        else:
+            H[e] = 0.5 * S[0] / n[0] + 0.5 * S[1] / n[1]
+    return per_layer, H
+
+
+def _calibrate_pair_pins_hold(fn, mode="rt"):
+    """The CLHA phases wired together: each job's Hessian is the brute-force
+    combination of its own tokens (the shared job's over all tokens), GPTQ ran
+    on that Hessian (its lambda and U), the shared job at b+1 bits and the
+    routed ones at b (CLHA-MP), and the losses are tr[D H D^T] under H_comb and
+    under each layer's S_l / n_l."""
+    x, logits, win, jobs = _pair_case()
+    damp, bits, shared_bits = 0.01, 2, 3
+    try:
+        out = fn(x, logits, jobs, n_routed=2, top_k=1, n_shared=1, mode=mode, bits=bits,
+                 shared_bits=shared_bits, group=8, damp=damp, block=8, layer_losses=True)
+        per_layer, H = _brute_hessians(x, win, mode)
+        slot = {0: 0, 1: 1, 2: 2}
+        for e, w in jobs.items():
+            He = H[e]
+            if not np.allclose(out["H"][slot[e]], He, rtol=1e-12, atol=0):
+                return False
+            g = out["gptq"][e]
+            if abs(g["lam"] - damp * np.mean(np.diag(He))) > 1e-15 * abs(g["lam"]):
+                return False
+            Hd = He + g["lam"] * np.eye(He.shape[0])
+            if np.max(np.abs(g["U"].T @ g["U"] @ Hd - np.eye(He.shape[0]))) > 1e-9:
+                return False
+            b = shared_bits if e == 2 else bits
+            maxq = (1 << b) - 1
+            codes = g["codes"]
+            if codes.max() > maxq or (e == 2 and codes.max() <= (1 << bits) - 1):
+                return False
+            # group 0's grid is fitted on the untouched first group: s = range / maxq
+            w32 = w.astype(np.float32)
+            rng_ = np.maximum(w32.max(axis=1), 0) - np.minimum(w32.min(axis=1), 0)
+            if not np.array_equal(g["scales"][:, 0], (rng_ / np.float32(maxq)).astype(np.float32)):
+                return False
+            D = g["wq"] - w
+            want = float(np.sum((D @ He) * D))
+            if abs(out["loss"][e] - want) > 1e-12 * want:
+                return False
+            S, n = per_layer[e]
+            for l in range(2):
+                want_l = float(np.sum((D @ (S[l] / n[l])) * D))
+                if abs(out["layer_loss"][e][l] - want_l) > 1e-12 * want_l:
+                    return False
+        return True
+    except (KeyError, IndexError, ValueError, np.linalg.LinAlgError):
+        return False
+
+
+@pytest.mark.parametrize("mode", ["rt", "eq"])
+def test_calibrate_pair_wiring(mode):
+    assert _calibrate_pair_pins_hold(oracle.calibrate_pair, mode)
+
+
+@pytest.mark.parametrize("old,new", [
+    ("b = shared_bits if e >= n_routed else bits", "b = bits"),                  # CLHA-MP width dropped
+    ("return e if e < n_routed else n_routed", "return e if e < n_routed else 0"),  # shared job on a routed slot
+    ("loss(w, g[\"wq\"], S[s] / n[s])", "loss(w, g[\"wq\"], S[s])"),              # layer loss under S, not S/n
+    ("out[\"loss\"][e] = loss(w, g[\"wq\"], out[\"H\"][s])",
+     "out[\"loss\"][e] = loss(w, g[\"wq\"], out[\"S\"][0][s] / out[\"n\"][0][s])"),   # loss under layer a only
+])
+def test_planted_calibrate_pair_mistakes_are_caught(old, new):
+    assert _calibrate_pair_pins_hold(oracle.calibrate_pair)
+    bad = _mutant(oracle.calibrate_pair, old, new)
+    assert not _calibrate_pair_pins_hold(bad)
