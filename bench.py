@@ -1,22 +1,28 @@
 #!/usr/bin/env python3
 """Throughput of the CLHA calibration hot path on one MI355X (gfx950).
 
-One step is one full calibration pass of the mid-MoE-block workload (two
-layers sharing 64 routed experts, top-6, plus 2 always-active shared experts;
-d = 2048; 65,536 tokens per layer; gate and up 1408x2048 bf16 per expert;
-3-bit, group 128, routing-frequency alpha):
-  reset accumulators -> collect layer a -> collect layer b (route, bucket,
-  gather, Gram sums) -> aggregate H_comb -> GPTQ of 66 stacked gate|up jobs
-  (damping, factor of the inverse, column loop, lazy block updates, loss)
-= 132 expert matrices.  Inputs are seeded synthetic arrays resident in HBM
-before the timed region.  Prints one JSON line.
+One step calibrates one CLWS pair (two layers that share their routed experts):
+  reset the pair's accumulators -> collect layer a -> collect layer b (route,
+  bucket, gather, Gram sums) -> aggregate H_comb -> GPTQ of the pair's expert
+  jobs (damping, factor of the inverse, column loop, lazy block updates, loss).
+Inputs are seeded synthetic arrays, every pair's resident in HBM before the
+timed region; steps cycle over the pairs.  Prints one JSON line.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+Default workload: full depth (24 layers as 12 CLWS pairs; 64 routed experts
+top-6 with a Zipf(1.1) router load plus 2 shared experts; d = 2048; 262,144
+tokens per layer; gate and up 1408x2048 bf16 per expert, stacked into 66 jobs
+of 2816x2048 = 132 matrices per pair; 2-bit, group 128, equal weighting).  The
+default 12 timed steps are one pass over all 24 layers.  --workload selects
+another shape sheet of gen.WORKLOADS (2 mid MoE block, 4 CLHA-MP, 5 drift
+stress, whose steps cycle over the drift values t of one pair).
 
---down-proj measures the experts' second matrices instead (the same block and
-batch): one step resets the down_proj accumulators, collects both layers'
-SwiGLU inputs h = bf16(silu(x Wg^T) * (x Wu^T)) and their Gram sums (routing
-taken from the main context's collection of the same batch, done once before
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload ID] [--pairs N]
+                  [--no-cpu-baseline]
+
+--down-proj measures the experts' second matrices of the mid MoE block instead:
+one step resets the down_proj accumulators, collects both layers' SwiGLU
+inputs h = bf16(silu(x Wg^T) * (x Wu^T)) and their Gram sums (routing taken
+from the main context's collection of the same batch, done once before
 timing), aggregates, and runs GPTQ on the 66 down_proj matrices (2048x1408).
 """
 import argparse
@@ -33,17 +39,18 @@ METRIC = "expert matrices calibrated/sec (Hessian+CLHA-GPTQ); SYRK % of MFMA pea
 PEAK_BF16_TFLOPS = 2500.0          # MI355X dense bf16 matrix peak
 PEAK_FP32_TFLOPS = 157.3           # MI355X fp32 matrix peak
 PEAK_HBM_GBS = 8000.0              # MI355X HBM3E bandwidth
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "syrk_mid_moe_block_traffic.json")
 SYRK_SRC = os.path.join(ROOT, "gptq_calibration_moe_amd", "csrc", "syrk.hip")
 
 
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=12)
     ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--pairs", type=int, default=0,
+                    help="keep only the first N pairs (drift values) resident; 0 = all of the workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", type=int, default=2, help="workload id of gen.WORKLOADS (default 2)")
+    ap.add_argument("--workload", type=int, default=3, help="workload id of gen.WORKLOADS (default 3, full depth)")
     ap.add_argument("--copy-probe", type=int, metavar="BYTES", help="only copy BYTES on the device and exit")
     ap.add_argument("--down-proj", action="store_true", help="measure the down_proj calibration step instead")
     ap.add_argument("--act-order", action="store_true", help="GPTQ with activation order")
@@ -106,19 +113,31 @@ def cpu_baseline(wl, inp, w_host, budget_s=10.0):
                        f"gate|up job and the loss = {mats} matrices in {dt:.2f} s")}
 
 
-# Profiling runs behind the committed summaries.  The counter runs read
+# Profiling runs behind the committed summaries, on two resident pairs (the
+# kernels and their shapes are those of every pair).  The counter runs read
 # FETCH_SIZE and WRITE_SIZE (KiB per dispatch) in passes of their own; the
 # copy probe moves a known number of bytes so that each counter can be scaled
-# to bytes.  `--profile-commands DIR` prints these lines; `--summarize-profiles
-# DIR` turns their CSV output into the text summaries.
+# to bytes.  Two more passes read the matrix-core counters (MFMA busy cycles,
+# MFMA operations by type) and the LDS counters (bank conflicts against LDS
+# activity), each within one pass's counter limits.  `--profile-commands DIR`
+# prints these lines; `--summarize-profiles DIR` turns their CSV output into
+# the text summaries.
 COPY_BYTES = 1 << 30
+MFMA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_I8 "
+                 "SQ_INSTS_VALU_MFMA_MOPS_F32 SQ_INSTS_VALU_MFMA_MOPS_F64 GRBM_GUI_ACTIVE")
+LDS_COUNTERS = "SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_BUSY_CYCLES SQ_WAVE_CYCLES GRBM_GUI_ACTIVE"
+_BENCH = "-- python3 bench.py --workload {wid} --pairs 2 --no-cpu-baseline"
 PROFILE_RUNS = [
     ("trace", "timeout -k 10 600 rocprofv3 --kernel-trace --stats --output-format csv -d {dir}/trace -o run "
-              "-- python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline"),
+              + _BENCH + " --steps 3 --warmup 1"),
     ("fetch", "timeout -s KILL 300 rocprofv3 --pmc FETCH_SIZE --output-format csv -d {dir}/fetch -o run "
-              "-- python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline"),
+              + _BENCH + " --steps 1 --warmup 1"),
     ("write", "timeout -s KILL 300 rocprofv3 --pmc WRITE_SIZE --output-format csv -d {dir}/write -o run "
-              "-- python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline"),
+              + _BENCH + " --steps 1 --warmup 1"),
+    ("mfma", "timeout -s KILL 300 rocprofv3 --pmc " + MFMA_COUNTERS + " --output-format csv -d {dir}/mfma -o run "
+             + _BENCH + " --steps 1 --warmup 1"),
+    ("lds", "timeout -s KILL 300 rocprofv3 --pmc " + LDS_COUNTERS + " --output-format csv -d {dir}/lds -o run "
+            + _BENCH + " --steps 1 --warmup 1"),
     ("copy_fetch", "timeout -s KILL 60 rocprofv3 --pmc FETCH_SIZE --output-format csv -d {dir}/copy_fetch -o run "
                    f"-- python3 bench.py --copy-probe {COPY_BYTES}"),
     ("copy_write", "timeout -s KILL 60 rocprofv3 --pmc WRITE_SIZE --output-format csv -d {dir}/copy_write -o run "
@@ -237,17 +256,21 @@ def summarize_options_profile(d, bench_json):
     open(os.path.join(ROOT, "profiles", "bench_gptq_options_mid_moe_block.md"), "w").write("\n".join(out))
 
 
-def summarize_profiles(d, workload_name="mid_moe_block"):
-    """Writes the kernel-trace summary and the per-kernel HBM traffic summary
-    (counter values scaled by the copy probe) under profiles/."""
-    cmd = {k: c.format(dir=d) for k, c in PROFILE_RUNS}
+def summarize_profiles(d, wid):
+    """Writes, for workload `wid`, the kernel-trace summary, the per-kernel HBM
+    traffic (counter values scaled by the copy probe), the matrix-core and LDS
+    counter summaries under profiles/, and the Gram-sum traffic record that
+    bench.py reports while syrk.hip is unchanged."""
+    import gen
+    name = gen.WORKLOADS[wid].name
+    cmd = {k: c.format(dir=d, wid=wid) for k, c in PROFILE_RUNS}
     lines = _trace_lines(os.path.join(d, "trace"),
-                         f"# Kernel time per step, {workload_name} workload (MI355X, rocprofv3 kernel trace)",
+                         f"# Kernel time per step, {name} workload (MI355X, rocprofv3 kernel trace)",
                          cmd["trace"],
-                         ["The factorisation runs as four Hessian groups on concurrent streams, overlapped with the",
-                          "GPTQ kernels, so per-kernel times overlap in wall time; wall-clock stage times are",
-                          "`stages_ms_per_step` in the bench line."])
-    open(os.path.join(ROOT, "profiles", f"clha_step_{workload_name}_kernel_trace.md"), "w").write("\n".join(lines))
+                         ["One step is one CLWS pair.  The factorisation runs as four Hessian groups on",
+                          "concurrent streams, overlapped with the GPTQ kernels, so per-kernel times overlap in",
+                          "wall time; wall-clock stage times are `stages_ms_per_step` in the bench line."])
+    open(os.path.join(ROOT, "profiles", f"clha_step_{name}_kernel_trace.md"), "w").write("\n".join(lines))
 
     def per_kernel(sub, counter):
         acc = {}
@@ -267,7 +290,7 @@ def summarize_profiles(d, workload_name="mid_moe_block"):
     f_scale = copy_kib_total / copy_kib("copy_fetch", "FETCH_SIZE")
     w_scale = copy_kib_total / copy_kib("copy_write", "WRITE_SIZE")
     fetch, write = per_kernel("fetch", "FETCH_SIZE"), per_kernel("write", "WRITE_SIZE")
-    lines = [f"# HBM traffic per launch, {workload_name} workload (MI355X, rocprofv3 counters)", "",
+    lines = [f"# HBM traffic per launch, {name} workload (MI355X, rocprofv3 counters)", "",
              "Commands (repository root), one counter per run:", ""]
     lines += [f"    {cmd[k]}" for k in ("fetch", "write", "copy_fetch", "copy_write")]
     lines += ["", f"Scale: a {COPY_BYTES} B device copy reads FETCH_SIZE x {f_scale:.3f} and "
@@ -279,14 +302,53 @@ def summarize_profiles(d, workload_name="mid_moe_block"):
         rd = fetch[k][0] / fetch[k][1] * 1024 * f_scale
         wr = write[k][0] / write[k][1] * 1024 * w_scale
         lines.append(f"| {k} | {fetch[k][1]} | {rd / 1e9:.4f} | {wr / 1e9:.4f} |")
-    open(os.path.join(ROOT, "profiles", f"clha_step_{workload_name}_hbm_traffic.md"), "w").write("\n".join(lines) + "\n")
+    open(os.path.join(ROOT, "profiles", f"clha_step_{name}_hbm_traffic.md"), "w").write("\n".join(lines) + "\n")
+
+    # matrix-core and LDS counters per kernel (sums over all units, per launch)
+    trace = _csv(_find(os.path.join(d, "trace"), "kernel_trace.csv"))
+    dur = {}
+    for r in trace:
+        v = dur.setdefault(_short(r["Kernel_Name"]), [])
+        v.append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    avg_ns = {k: sorted(v)[len(v) // 2] for k, v in dur.items()}
+    m = {c: per_kernel("mfma", c) for c in MFMA_COUNTERS.split()}
+    ld = {c: per_kernel("lds", c) for c in LDS_COUNTERS.split()}
+    per = lambda tab, c, k: tab[c][k][0] / tab[c][k][1] if k in tab[c] else 0.0
+    lines = [f"# Matrix-core and LDS counters per launch, {name} workload (MI355X, rocprofv3)", "",
+             "Commands (repository root), one pass each:", "", f"    {cmd['mfma']}", f"    {cmd['lds']}", "",
+             "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x 256 CUs), the share of CU cycles with",
+             "the matrix pipe busy while the kernel ran (counters serialise kernels, so each launch has the",
+             "GPU alone).  Executed TFLOP/s = 512 x SQ_INSTS_VALU_MFMA_MOPS_<type> over the launch's median",
+             "duration in the kernel trace (tile overcompute included, so it is at least the algorithmic",
+             "rate).  LDS bank conflicts are SQ_LDS_BANK_CONFLICT over SQ_LDS_IDX_ACTIVE (cycles).", "",
+             "| kernel | launches | MFMA busy | bf16 TFLOP/s | int8 TOP/s | fp32 TFLOP/s | fp64 TFLOP/s | "
+             "LDS conflict / active |", "|---|---:|---:|---:|---:|---:|---:|---:|"]
+    ks = sorted(m["GRBM_GUI_ACTIVE"], key=lambda k: -per(m, "SQ_VALU_MFMA_BUSY_CYCLES", k))
+    rec_counters = {}
+    for k in ks:
+        busy = per(m, "SQ_VALU_MFMA_BUSY_CYCLES", k)
+        gui = per(m, "GRBM_GUI_ACTIVE", k)
+        if busy == 0 and per(ld, "SQ_LDS_IDX_ACTIVE", k) == 0:
+            continue
+        t = avg_ns.get(k)
+        rate = {ty: (512 * per(m, f"SQ_INSTS_VALU_MFMA_MOPS_{ty}", k) / (t * 1e-9) / 1e12 if t else 0.0)
+                for ty in ("BF16", "I8", "F32", "F64")}
+        act, conf = per(ld, "SQ_LDS_IDX_ACTIVE", k), per(ld, "SQ_LDS_BANK_CONFLICT", k)
+        u = busy / (gui * 256) if gui else 0.0
+        rec_counters[k] = {"mfma_busy": u, "lds_conflict_per_active": conf / act if act else 0.0,
+                           **{f"{ty.lower()}_rate": v for ty, v in rate.items()}}
+        lines.append(f"| {k} | {m['GRBM_GUI_ACTIVE'][k][1]} | {u:.3f} | {rate['BF16']:.1f} | {rate['I8']:.1f} | "
+                     f"{rate['F32']:.1f} | {rate['F64']:.2f} | {conf / act if act else 0.0:.4f} |")
+    open(os.path.join(ROOT, "profiles", f"clha_step_{name}_mfma_lds_counters.md"), "w").write("\n".join(lines) + "\n")
+
     sk = "clha::syrk_kernel"
-    rec = {"workload": workload_name, "kernel": "syrk_kernel", "syrk_source_sha256_16": syrk_source_hash(),
+    rec = {"workload": name, "kernel": "syrk_kernel", "syrk_source_sha256_16": syrk_source_hash(),
            "fetch_kib_per_launch": fetch[sk][0] / fetch[sk][1], "write_kib_per_launch": write[sk][0] / write[sk][1],
            "fetch_scale": f_scale, "write_scale": w_scale,
            "hbm_bytes_per_launch": (fetch[sk][0] / fetch[sk][1] * f_scale + write[sk][0] / write[sk][1] * w_scale) * 1024,
-           "commands": [cmd[k] for k in ("fetch", "write", "copy_fetch", "copy_write")]}
-    json.dump(rec, open(TRAFFIC_FILE, "w"), indent=1)
+           "counters": rec_counters.get(sk),
+           "commands": [cmd[k] for k in ("fetch", "write", "copy_fetch", "copy_write", "mfma", "lds")]}
+    json.dump(rec, open(traffic_file(name), "w"), indent=1)
     print(json.dumps(rec))
 
 
@@ -364,10 +426,10 @@ def main():
     args = parse()
     if args.profile_commands:
         for _, c in PROFILE_RUNS:
-            print(c.format(dir=args.profile_commands))
+            print(c.format(dir=args.profile_commands, wid=args.workload))
         return 0
     if args.summarize_profiles:
-        summarize_profiles(args.summarize_profiles)
+        summarize_profiles(args.summarize_profiles, args.workload)
         return 0
     if args.summarize_options_profile:
         summarize_options_profile(*args.summarize_options_profile)
@@ -384,6 +446,15 @@ def main():
         return 2
     if args.down_proj:
         return down_proj_bench(args)
+    return calibration_bench(args)
+
+
+def traffic_file(wl_name):
+    return os.path.join(ROOT, "profiles", f"syrk_{wl_name}_traffic.json")
+
+
+def calibration_bench(args):
+    """The CLHA calibration step over one CLWS pair; see the module docstring."""
     import numpy as np
     import torch
     import gen
@@ -391,37 +462,60 @@ def main():
     from gptq_calibration_moe_amd.calibrate import SharedGroupCalibration
 
     wl = gen.WORKLOADS[args.workload]
-    if wl.n_pairs != 1 and args.workload != 2:
-        wl = wl.scaled(n_pairs=1)
     dev = torch.device("cuda", 0)
-    t0 = time.perf_counter()
-    inp = gen.pair_inputs(wl, t=wl.drift[-1] if wl.drift else None)
+    # the step's units: CLWS pairs, or for the drift workload one pair at each drift t
+    units = list(wl.drift) if wl.drift else list(range(wl.n_pairs))
+    if args.pairs:
+        units = units[:args.pairs]
     experts = list(range(wl.n_experts_total))
-    w_host = {e: gen.expert_weights(wl, 0, e) for e in experts}
-    log(f"generated {wl.name} inputs in {time.perf_counter() - t0:.1f} s")
 
     def bits_dev(b):
         return torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).to(dev).view(torch.bfloat16)
 
-    x = [bits_dev(b) for b in inp["x"]]
-    lg = [torch.from_numpy(a).to(dev) for a in inp["logits"]]
-    W = {e: (bits_dev(w) if wl.w_dtype == "bf16" else torch.from_numpy(w).to(dev)) for e, w in w_host.items()}
     ctx = clha.Context(wl.d, wl.n_routed, wl.top_k, wl.n_shared, max_tokens=wl.n_tokens, device=dev)
-    cal = SharedGroupCalibration(ctx, [0, 1])
-    prep, outputs = cal.prepare_quantize(W, wl.bits, wl.shared_bits, wl.group,
-                                         act_order=args.act_order, static_groups=args.static_groups)
+    H = torch.empty(ctx.slots, wl.d, wl.d, dtype=torch.float32, device=dev)
+    x, lg, W, cals, host0 = [], [], [], [], None
+    t0 = time.perf_counter()
+    for u, unit in enumerate(units):
+        if wl.drift:
+            inp = gen.pair_inputs(wl, 0, t=unit)
+            w_host = gen.all_expert_weights(wl, 0, experts) if u == 0 else host0[1]
+        else:
+            inp = gen.pair_inputs(wl, unit)
+            w_host = gen.all_expert_weights(wl, unit, experts)
+        if u == 0 or (wl.drift and u == len(units) - 1):
+            host0 = (inp, w_host)
+        x += [bits_dev(b) for b in inp["x"]]
+        lg += [torch.from_numpy(a).to(dev) for a in inp["logits"]]
+        if not wl.drift or u == 0:
+            W.append({e: (bits_dev(w) if wl.w_dtype == "bf16" else torch.from_numpy(w).to(dev))
+                      for e, w in w_host.items()})
+        cals.append(SharedGroupCalibration(ctx, [2 * u, 2 * u + 1], H=H))
+        del inp
+        log(f"unit {u + 1}/{len(units)} ({'t=' + str(unit) if wl.drift else 'pair ' + str(unit)}) "
+            f"resident after {time.perf_counter() - t0:.1f} s")
+    # one GPTQ workspace for every pair's batch: the batches run one after another
+    outputs = [cals[0].make_outputs(experts, W[i][0].shape[0], wl.group) for i in range(len(W))]
+    jobs0 = cals[0].quantize_jobs(W[0], wl.bits, wl.shared_bits, outputs[0])
+    ws = torch.empty(ctx.gptq_workspace_bytes(jobs0, wl.d, args.act_order, args.static_groups),
+                     dtype=torch.uint8, device=dev)
+    preps = [cals[0].prepare_quantize(W[i], wl.bits, wl.shared_bits, wl.group, outputs=outputs[i],
+                                      act_order=args.act_order, static_groups=args.static_groups,
+                                      workspace=ws)[0] for i in range(len(W))]
     ctx.workspace("collect", ctx.collect_workspace_bytes())
     n_mats = len(experts) * len(wl.mats)
 
-    def step():
+    def step(i):
+        u = i % len(units)
+        cal = cals[u]
         cal.reset()
-        cal.collect(0, x[0], lg[0])
-        cal.collect(1, x[1], lg[1])
+        cal.collect(2 * u, x[2 * u], lg[2 * u])
+        cal.collect(2 * u + 1, x[2 * u + 1], lg[2 * u + 1])
         cal.aggregate(wl.alpha)
-        ctx.run_gptq(prep, wl.group, wl.block, wl.damp)
+        ctx.run_gptq(preps[0 if wl.drift else u], wl.group, wl.block, wl.damp)
 
     for i in range(args.warmup):
-        step()
+        step(i)
     ctx.sync()
     log(f"warmup done ({args.warmup} steps)")
     ctx.set_timing(True)
@@ -429,7 +523,7 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step()
+        step(i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ctx.sync()
@@ -439,16 +533,19 @@ def main():
     value = n_mats / (ms_per_step / 1e3)
     log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step")
 
-    # Gram-sum roofline: algorithmic flops = sum over slots of n_e d (d+1), per launch
-    counts = [cal.counts[l].cpu().numpy() for l in (0, 1)]
-    flops_per_launch = sum(float(c.sum()) for c in counts) * wl.d * (wl.d + 1) / 2.0
+    # Gram-sum roofline: algorithmic flops = sum over slots of n_e d (d+1), averaged per launch
+    launched = [i % len(units) for i in range(args.steps)]
+    counts = {u: [cals[u].counts[l].cpu().numpy() for l in cals[u].layer_ids] for u in set(launched)}
+    rows_per_launch = sum(float(c.sum()) for u in launched for c in counts[u]) / (2 * args.steps)
+    flops_per_launch = rows_per_launch * wl.d * (wl.d + 1)
     syrk_ms, syrk_calls = stages["syrk"]
     syrk_avg_ms = syrk_ms / max(syrk_calls, 1)
     achieved = flops_per_launch / (syrk_avg_ms / 1e3) / 1e12
     traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        rec = json.load(open(TRAFFIC_FILE))
-        if rec.get("syrk_source_sha256_16") == syrk_source_hash() and rec.get("workload") == wl.name:
+    tf = traffic_file(wl.name)
+    if os.path.exists(tf):
+        rec = json.load(open(tf))
+        if rec.get("syrk_source_sha256_16") == syrk_source_hash():
             traffic = rec.get("hbm_bytes_per_launch")
     roofline = {"kernel": "syrk_kernel", "bound": "mfma", "achieved": round(achieved, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
@@ -457,14 +554,14 @@ def main():
     stages_ms = {k: round(v[0] / args.steps, 4) for k, v in stages.items() if v[1]}
 
     # gather rate on algorithmic bytes (each token read once, each routed row written once)
-    routed = [float(c[:wl.n_routed].sum()) for c in counts]
-    gather_bytes = sum(wl.n_tokens * wl.d * 2 + p * wl.d * 2 for p in routed)
+    routed_per_step = wl.n_tokens * wl.top_k * 2
+    gather_bytes = 2 * wl.n_tokens * wl.d * 2 + routed_per_step * wl.d * 2
     gather_gbs = gather_bytes / (stages_ms["gather"] / 1e3) / 1e9 if stages_ms.get("gather") else None
     # end-to-end roofline: each step's algorithmic work at the published peak of its bound
     # (Gram sums on bf16 MFMA; inverse Cholesky (2/3)d^3 per distinct Hessian and GPTQ
     # r c (c-1) per matrix on fp32 MFMA; the gather on HBM)
     n_hess = wl.n_routed + (1 if wl.n_shared else 0)
-    rows_total = sum(int(W[e].shape[0]) for e in experts)
+    rows_total = sum(int(W[0][e].shape[0]) for e in experts)
     terms = {"gram_sums": 2 * flops_per_launch / (PEAK_BF16_TFLOPS * 1e12),
              "inverse_cholesky": n_hess * (2.0 / 3.0) * wl.d ** 3 / (PEAK_FP32_TFLOPS * 1e12),
              "gptq": rows_total * wl.d * (wl.d - 1) / (PEAK_FP32_TFLOPS * 1e12),
@@ -474,27 +571,33 @@ def main():
                   "terms_ms": {k: round(v * 1e3, 3) for k, v in terms.items()},
                   "peaks": "bf16 MFMA 2500 TFLOP/s, fp32 MFMA 157.3 TFLOP/s, HBM 8000 GB/s"}
 
+    n_layers = 2 * (wl.n_pairs if not wl.drift else 1)
+    config = {"workload": wl.name, "layers": n_layers, "clws_pairs": wl.n_pairs,
+              "pairs_resident": len(units) if not wl.drift else 1,
+              "step": ("one CLWS pair at one drift t (cycling t over " + str(list(units)) + ")") if wl.drift
+              else "one CLWS pair (cycling over the resident pairs)",
+              "tokens_per_layer": wl.n_tokens, "d": wl.d,
+              "routed_experts": wl.n_routed, "top_k": wl.top_k, "shared_experts": wl.n_shared,
+              "router_load": {"normal": "N(0,1) logits", "zipf": "Zipf(1.1)",
+                              "router": "logits = x R"}[wl.logit_kind],
+              "matrices_per_step": n_mats, "matrix_shape": [wl.rows, wl.d], "bits": wl.bits,
+              "shared_bits": wl.shared_bits, "group": wl.group, "alpha": wl.alpha}
+    if args.act_order or args.static_groups:
+        config["gptq_options"] = [o for o, on in (("act_order", args.act_order),
+                                                   ("static_groups", args.static_groups)) if on]
+    config["precision"] = ("Gram sums bf16 in / fp32 accumulate; Cholesky fp64 values, its long products "
+                           "exact int8 digit products of 42-bit expansions; triangular inverse at fp32 "
+                           "precision (three bf16 parts per operand); GPTQ fp32, trailing products exact "
+                           "int8 digit products of 28-bit expansions")
     out = {"metric": METRIC, "value": round(value, 2), "unit": "matrices/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-           "data": "synthetic",
-           "config": {"workload": wl.name, "layers": 2, "tokens_per_layer": wl.n_tokens, "d": wl.d,
-                      "routed_experts": wl.n_routed, "top_k": wl.top_k, "shared_experts": wl.n_shared,
-                      "matrices": n_mats, "matrix_shape": [wl.rows, wl.d], "bits": wl.bits,
-                      "shared_bits": wl.shared_bits, "group": wl.group, "alpha": wl.alpha,
-                      **({"gptq_options": [o for o, on in (("act_order", args.act_order),
-                                                            ("static_groups", args.static_groups)) if on]}
-                         if args.act_order or args.static_groups else {}),
-                      "precision": "Gram sums bf16 in / fp32 accumulate; Cholesky fp64 values, its "
-                                   "long products exact int8 digit products of 42-bit expansions; "
-                                   "triangular inverse at fp32 precision (three bf16 parts per operand); "
-                                   "GPTQ fp32, trailing products exact int8 digit products of 28-bit "
-                                   "expansions"},
+           "data": "synthetic", "config": config,
            "roofline": roofline, "stages_ms_per_step": stages_ms,
            "gather_gbs": round(gather_gbs, 1) if gather_gbs else None, "end_to_end_roofline": end_to_end}
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
-        out["cpu_baseline"] = cpu_baseline(wl, inp, w_host)
+        out["cpu_baseline"] = cpu_baseline(wl, host0[0], host0[1])
     print(json.dumps(out), flush=True)
     return 0
 

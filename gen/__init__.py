@@ -22,12 +22,17 @@ workloads stand in for it (their shapes are listed in ``WORKLOADS``):
 Random streams are addressed, not spawned in order:
 ``SeedSequence(seed_base + workload_id, spawn_key=(pair, stream, index))``,
 so a subset of experts or pairs can be generated without drawing the rest.
+Activations and router logits are drawn in chunks of 16,384 rows, chunk i
+from index i of its stream, on a pool of host threads; an array of at most
+16,384 rows is one chunk.
 
 bf16 values are made from fp32 by round-to-nearest-even and stored as the
 upper 16 bits of the fp32 pattern (uint16).
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, replace
 from typing import Optional
 
@@ -107,6 +112,25 @@ WORKLOADS = {
 assert WORKLOADS[4].seed_base + 4 == WORKLOADS[3].seed_base + 3
 
 
+CHUNK_ROWS = 16384      # rows per independently seeded chunk of a row-major stream
+_POOL = None
+
+
+def _pool() -> ThreadPoolExecutor:
+    global _POOL
+    if _POOL is None:
+        _POOL = ThreadPoolExecutor(max_workers=max(1, min(16, os.cpu_count() or 1)))
+    return _POOL
+
+
+def _by_chunks(n: int, fill) -> None:
+    """Runs fill(lo, hi, i) for the row chunks [i*CHUNK_ROWS, ...) of an n-row
+    array on the thread pool (numpy's generators and ufuncs release the GIL)."""
+    bounds = [(lo, min(lo + CHUNK_ROWS, n), i) for i, lo in enumerate(range(0, n, CHUNK_ROWS))]
+    for f in [_pool().submit(fill, *b) for b in bounds]:
+        f.result()
+
+
 # --------------------------------------------------------------------------- formats
 
 def bf16_bits(a) -> np.ndarray:
@@ -162,23 +186,38 @@ def activations(wl: Workload, pair: int = 0, t: Optional[float] = None,
     """
     n = wl.n_tokens if n_tokens is None else n_tokens
     d = wl.d
+    xa = np.empty((n, d), np.uint16)
+    xb = np.empty((n, d), np.uint16)
     if wl.x_kind == "rotated":
-        xa = bf16_bits(_normal_f32(_rng(wl, pair, _S_XA), (n, d)))
+        def fa(lo, hi, i):
+            xa[lo:hi] = bf16_bits(_normal_f32(_rng(wl, pair, _S_XA, i), (hi - lo, d)))
+        _by_chunks(n, fa)
         q = _haar_orthogonal(_rng(wl, pair, _S_ROT), d).astype(np.float32)
-        noise = _normal_f32(_rng(wl, pair, _S_XB), (n, d), 0.3)
-        xb = bf16_bits(bf16_value(xa) @ q + noise)
+        m = bf16_value(xa) @ q
+
+        def fb(lo, hi, i):
+            xb[lo:hi] = bf16_bits(m[lo:hi] + _normal_f32(_rng(wl, pair, _S_XB, i), (hi - lo, d), 0.3))
+        _by_chunks(n, fb)
+        del m
     elif wl.x_kind == "student_t":
-        xa = bf16_bits(_student_t_f32(_rng(wl, pair, _S_XA), (n, d), 4.0))
-        xb = bf16_bits(_student_t_f32(_rng(wl, pair, _S_XB), (n, d), 4.0))
+        def fs(lo, hi, i):
+            xa[lo:hi] = bf16_bits(_student_t_f32(_rng(wl, pair, _S_XA, i), (hi - lo, d), 4.0))
+            xb[lo:hi] = bf16_bits(_student_t_f32(_rng(wl, pair, _S_XB, i), (hi - lo, d), 4.0))
+        _by_chunks(n, fs)
     elif wl.x_kind == "drift":
         if t is None:
             raise ValueError("drift workload needs t")
-        xa = bf16_bits(_normal_f32(_rng(wl, pair, _S_XA), (n, d)))
-        z = _normal_f32(_rng(wl, pair, _S_Z), (n, d))
-        xb = bf16_bits(np.float32(1.0 - t) * bf16_value(xa) + np.float32(t) * z)
+
+        def fd(lo, hi, i):
+            xa[lo:hi] = bf16_bits(_normal_f32(_rng(wl, pair, _S_XA, i), (hi - lo, d)))
+            z = _normal_f32(_rng(wl, pair, _S_Z, i), (hi - lo, d))
+            xb[lo:hi] = bf16_bits(np.float32(1.0 - t) * bf16_value(xa[lo:hi]) + np.float32(t) * z)
+        _by_chunks(n, fd)
     elif wl.x_kind == "normal":
-        xa = bf16_bits(_normal_f32(_rng(wl, pair, _S_XA), (n, d)))
-        xb = bf16_bits(_normal_f32(_rng(wl, pair, _S_XB), (n, d)))
+        def fn(lo, hi, i):
+            xa[lo:hi] = bf16_bits(_normal_f32(_rng(wl, pair, _S_XA, i), (hi - lo, d)))
+            xb[lo:hi] = bf16_bits(_normal_f32(_rng(wl, pair, _S_XB, i), (hi - lo, d)))
+        _by_chunks(n, fn)
     else:
         raise ValueError(wl.x_kind)
     return xa, xb
@@ -198,14 +237,23 @@ def router_logits(wl: Workload, pair: int, layer: int, x_bits: Optional[np.ndarr
     e = wl.n_routed
     stream = _S_LA if layer == 0 else _S_LB
     if wl.logit_kind == "normal":
-        return _normal_f32(_rng(wl, pair, stream), (n, e))
+        out = np.empty((n, e), np.float32)
+
+        def fn(lo, hi, i):
+            out[lo:hi] = _normal_f32(_rng(wl, pair, stream, i), (hi - lo, e))
+        _by_chunks(n, fn)
+        return out
     if wl.logit_kind == "zipf":
         perm = _rng(wl, pair, _S_PERM_A if layer == 0 else _S_PERM_B).permutation(e)
         logp = -1.1 * np.log(np.arange(1, e + 1, dtype=np.float64))
         logp -= np.log(np.exp(logp).sum())
-        u = _rng(wl, pair, stream).random((n, e))
-        gumbel = -np.log(-np.log(u))
-        return (logp[perm][None, :] + gumbel).astype(np.float32)
+        out = np.empty((n, e), np.float32)
+
+        def fz(lo, hi, i):
+            u = _rng(wl, pair, stream, i).random((hi - lo, e))
+            out[lo:hi] = (logp[perm][None, :] - np.log(-np.log(u))).astype(np.float32)
+        _by_chunks(n, fz)
+        return out
     if wl.logit_kind == "router":
         if x_bits is None:
             raise ValueError("router logits need the layer's activations")
@@ -239,6 +287,13 @@ def expert_weights(wl: Workload, pair: int, expert: int) -> np.ndarray:
     """
     w = _normal_f32(_rng(wl, pair, _S_W, expert), (wl.job_rows, wl.d), 0.02)
     return w if wl.w_dtype == "f32" else bf16_bits(w)
+
+
+def all_expert_weights(wl: Workload, pair: int, experts) -> dict:
+    """expert_weights of several experts, drawn on the thread pool: {expert: W}."""
+    experts = list(experts)
+    futs = [_pool().submit(expert_weights, wl, pair, e) for e in experts]
+    return {e: f.result() for e, f in zip(experts, futs)}
 
 
 def weights_value(wl: Workload, w: np.ndarray) -> np.ndarray:

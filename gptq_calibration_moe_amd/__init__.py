@@ -54,7 +54,9 @@ class MoeDesc(C.Structure):
 class GptqJob(C.Structure):
     _fields_ = [("H", C.c_void_p), ("W", C.c_void_p), ("w_dtype", C.c_int32), ("rows", C.c_int32),
                 ("bits", C.c_int32), ("pad_", C.c_int32), ("codes", C.c_void_p),
-                ("scales", C.c_void_p), ("zeros", C.c_void_p), ("loss", C.c_void_p)]
+                ("scales", C.c_void_p), ("zeros", C.c_void_p), ("loss", C.c_void_p),
+                ("H_eval", C.c_void_p), ("loss_eval", C.c_void_p), ("dead", C.c_void_p),
+                ("status", C.c_void_p)]
 
 
 def _load() -> C.CDLL:
@@ -294,10 +296,21 @@ class Context:
             _check_dev("zeros", j["zeros"], torch.uint8, (rows, j["scales"].shape[1]), self.device)
             if j.get("loss") is not None:
                 _check_dev("loss", j["loss"], torch.float32, None, self.device)
+            if j.get("H_eval") is not None:
+                _check_dev("H_eval", j["H_eval"], torch.float32, (cols, cols), self.device)
+            if j.get("loss_eval") is not None:
+                _check_dev("loss_eval", j["loss_eval"], torch.float32, None, self.device)
+            if j.get("dead") is not None:
+                _check_dev("dead", j["dead"], torch.uint8, (cols,), self.device)
+            if j.get("status") is not None:
+                _check_dev("status", j["status"], torch.int32, None, self.device)
+
+            def opt(k):
+                return j[k].data_ptr() if j.get(k) is not None else None
             arr[i] = GptqJob(j["H"].data_ptr(), W.data_ptr(), BF16 if W.dtype == torch.bfloat16 else F32,
                              rows, int(j["bits"]), 0, j["codes"].data_ptr(), j["scales"].data_ptr(),
-                             j["zeros"].data_ptr(),
-                             j["loss"].data_ptr() if j.get("loss") is not None else None)
+                             j["zeros"].data_ptr(), opt("loss"), opt("H_eval"), opt("loss_eval"),
+                             opt("dead"), opt("status"))
         return arr
 
     class PreparedGptq:
@@ -307,11 +320,21 @@ class Context:
             self.arr, self.n, self.cols, self.ws, self.flags = arr, n, cols, ws, flags
 
     def prepare_gptq(self, jobs, cols: int, act_order: bool = False,
-                     static_groups: bool = False) -> "Context.PreparedGptq":
+                     static_groups: bool = False,
+                     workspace: Optional[torch.Tensor] = None) -> "Context.PreparedGptq":
+        """Checks and marshals a job batch.  `workspace` (uint8 device tensor) may be
+        shared by batches that run one after another on one stream and must hold
+        clha_gptq_workspace_bytes_ex bytes."""
         arr = self._jobs(jobs, cols)
         flags = (GPTQ_ACT_ORDER if act_order else 0) | (GPTQ_STATIC_GROUPS if static_groups else 0)
         need = lib.clha_gptq_workspace_bytes_ex(self._h, len(jobs), arr, cols, flags)
-        ws = torch.empty(max(int(need), 256), dtype=torch.uint8, device=self.device)
+        if workspace is not None:
+            _check_dev("workspace", workspace, torch.uint8, None, self.device)
+            if workspace.numel() < need:
+                raise ValueError(f"GPTQ workspace of {workspace.numel()} bytes < {need} needed")
+            ws = workspace
+        else:
+            ws = torch.empty(max(int(need), 256), dtype=torch.uint8, device=self.device)
         prep = Context.PreparedGptq(arr, len(jobs), cols, ws, flags)
         prep.tensors = jobs          # keep the job tensors alive with the pointers
         return prep
@@ -326,16 +349,20 @@ class Context:
         self._raise(lib.clha_gptq_quantize(self._h, prep.n, prep.arr, prep.cols, group, block,
                                            damp, _ptr(prep.ws), prep.ws.numel(), _stream(stream)))
 
-    def gptq_workspace_bytes(self, jobs, cols: int) -> int:
+    def gptq_workspace_bytes(self, jobs, cols: int, act_order: bool = False,
+                             static_groups: bool = False) -> int:
         arr = self._jobs(jobs, cols)
-        return lib.clha_gptq_workspace_bytes(self._h, len(jobs), arr, cols)
+        flags = (GPTQ_ACT_ORDER if act_order else 0) | (GPTQ_STATIC_GROUPS if static_groups else 0)
+        return lib.clha_gptq_workspace_bytes_ex(self._h, len(jobs), arr, cols, flags)
 
     def gptq_quantize(self, jobs, cols: int, group: int, block: int = 128, damp: float = 0.01,
                       workspace: Optional[torch.Tensor] = None, stream=None,
                       act_order: bool = False, static_groups: bool = False):
-        """jobs: list of dicts with H, W, bits, codes, scales, zeros and optional loss and
-        g_idx (device int32 [cols], receives each column's grid index).  act_order and
-        static_groups select clha_gptq_quantize_ex's options."""
+        """jobs: list of dicts with H, W, bits, codes, scales, zeros and optional loss,
+        H_eval with loss_eval (the result's loss under a second Hessian), dead (uint8
+        [cols]), status (int32 [1]: the job's clha_status code) and g_idx (device int32
+        [cols], receives each column's grid index).  act_order and static_groups select
+        clha_gptq_quantize_ex's options."""
         arr = self._jobs(jobs, cols)
         flags = (GPTQ_ACT_ORDER if act_order else 0) | (GPTQ_STATIC_GROUPS if static_groups else 0)
         gi = [j.get("g_idx") for j in jobs]

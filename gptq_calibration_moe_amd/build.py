@@ -15,7 +15,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libclha.so")
 BUILD = os.path.join(ROOT, "_build")
-SOURCES = ["route.hip", "syrk.hip", "aggregate.hip", "chol.hip", "gptq.hip", "loss.hip", "pack.hip", "down.hip", "api.cpp"]
+SOURCES = ["route.hip", "syrk.hip", "aggregate.hip", "chol.hip", "gptq.hip", "loss.hip", "pack.hip", "down.hip",
+           "status.hip", "api.cpp"]
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", f"--offload-arch={ARCH}",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -19,7 +19,9 @@ from . import Context
 class SharedGroupCalibration:
     """Accumulators of n_layers layers sharing one MoE block's experts."""
 
-    def __init__(self, ctx: Context, layer_ids: Sequence[int]):
+    def __init__(self, ctx: Context, layer_ids: Sequence[int], H: Optional[torch.Tensor] = None):
+        """H: optional [slots, d, d] float32 buffer for H_comb, e.g. one shared by
+        groups that are aggregated and quantized one after another."""
         self.ctx = ctx
         self.layer_ids = list(layer_ids)
         self.S, self.counts = {}, {}
@@ -27,7 +29,8 @@ class SharedGroupCalibration:
             S, n = ctx.new_layer_buffers()
             ctx.register_layer(l, S, n)
             self.S[l], self.counts[l] = S, n
-        self.H = torch.empty(ctx.slots, ctx.d, ctx.d, dtype=torch.float32, device=ctx.device)
+        self.H = (torch.empty(ctx.slots, ctx.d, ctx.d, dtype=torch.float32, device=ctx.device)
+                  if H is None else H)
         self.alpha = torch.empty(ctx.slots, len(self.layer_ids), dtype=torch.float32, device=ctx.device)
 
     def reset(self):
@@ -63,9 +66,11 @@ class SharedGroupCalibration:
 
     def prepare_quantize(self, weights: dict, bits: int, shared_bits: int, group: int,
                          outputs: Optional[dict] = None, H: Optional[torch.Tensor] = None,
-                         act_order: bool = False, static_groups: bool = False):
+                         act_order: bool = False, static_groups: bool = False,
+                         workspace: Optional[torch.Tensor] = None):
         """Marshals the GPTQ job batch once; run it with ctx.run_gptq(prep, group, ...).
-        act_order / static_groups select GPTQ's activation-order and static-group options."""
+        act_order / static_groups select GPTQ's activation-order and static-group options;
+        workspace may be shared with other batches run on the same stream."""
         H = self.H if H is None else H
         experts = sorted(weights)
         rows = weights[experts[0]].shape[0]
@@ -74,7 +79,16 @@ class SharedGroupCalibration:
         jobs = [{"H": H[self.slot_of(e)], "W": weights[e],
                  "bits": shared_bits if e >= self.ctx.n_routed else bits, **outputs[e]}
                 for e in experts]
-        return self.ctx.prepare_gptq(jobs, self.ctx.d, act_order, static_groups), outputs
+        return self.ctx.prepare_gptq(jobs, self.ctx.d, act_order, static_groups, workspace), outputs
+
+    def quantize_jobs(self, weights: dict, bits: int, shared_bits: int, outputs: dict,
+                      H: Optional[torch.Tensor] = None) -> list:
+        """The job dicts of a GPTQ batch (each expert on its slot's H_comb, shared
+        experts at shared_bits), e.g. to size a workspace shared by several batches."""
+        H = self.H if H is None else H
+        return [{"H": H[self.slot_of(e)], "W": weights[e],
+                 "bits": shared_bits if e >= self.ctx.n_routed else bits, **outputs[e]}
+                for e in sorted(weights)]
 
     def quantize(self, weights: dict, bits: int, shared_bits: int, group: int, block: int = 128,
                  damp: float = 0.01, outputs: Optional[dict] = None, H: Optional[torch.Tensor] = None,

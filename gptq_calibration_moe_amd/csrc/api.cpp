@@ -1,5 +1,5 @@
 // Host side of the CLHA C ABI: argument validation, the layer registry that keeps
-// per-layer accumulators apart, workspace carving and the device status latch.
+// per-layer accumulators apart, workspace carving and the device status record.
 // All compute is enqueued through the launchers in kernels.h.
 #include "clha.h"
 
@@ -36,7 +36,8 @@ struct clha_ctx {
   clha_moe_desc desc;
   int slots;
   int device;
-  int* status_dev;
+  int* status_dev;               // this context's status record (kernels.h), from the pool
+  int status_slot = -1;
   std::map<int32_t, LayerBufs> layers;
   std::string err;
   void* pinned = nullptr;        // staging for job tables (host, page-locked)
@@ -270,11 +271,14 @@ struct GptqLayout {
   int* perm;
   int* ipos;
   int* gidx;
+  int* mstat;
+  double* eval_part;
   size_t bytes;
 };
 
 GptqLayout gptq_layout(void* ws, int n_jobs, int n_mats, int cols, int64_t wf_elems,
-                       int64_t total_slabs, bool need_u, bool need_wf, uint32_t flags = 0) {
+                       int64_t total_slabs, bool need_u, bool need_wf, uint32_t flags = 0,
+                       int64_t eval_parts = 0) {
   Carver c(ws);
   GptqLayout L;
   const bool act = flags & CLHA_GPTQ_ACT_ORDER;
@@ -297,6 +301,8 @@ GptqLayout gptq_layout(void* ws, int n_jobs, int n_mats, int cols, int64_t wf_el
   L.perm = act ? c.take<int>((size_t)n_mats * cols) : nullptr;
   L.ipos = flags ? c.take<int>((size_t)n_mats * cols) : nullptr;
   L.gidx = flags ? c.take<int>((size_t)n_mats * cols) : nullptr;
+  L.mstat = c.take<int>((size_t)n_mats);
+  L.eval_part = eval_parts > 0 ? c.take<double>((size_t)eval_parts) : nullptr;
   L.bytes = c.off;
   return L;
 }
@@ -304,8 +310,10 @@ GptqLayout gptq_layout(void* ws, int n_jobs, int n_mats, int cols, int64_t wf_el
 struct JobScan {
   std::vector<const float*> mats;
   std::vector<int> mat_of;
+  std::vector<int64_t> eval_off;   // each job's loss partials under H_eval (-1: none)
   int64_t wf_elems = 0;
   int64_t total_slabs = 0;
+  int64_t eval_parts = 0;
 };
 
 JobScan scan_jobs(int n_jobs, const clha_gptq_job* jobs, int cols) {
@@ -322,6 +330,8 @@ JobScan scan_jobs(int n_jobs, const clha_gptq_job* jobs, int cols) {
       id = it->second;
     }
     s.mat_of.push_back(id);
+    s.eval_off.push_back(jobs[i].H_eval ? s.eval_parts : -1);
+    if (jobs[i].H_eval) s.eval_parts += clha::loss_partial_count(jobs[i].rows, cols);
     const int64_t slabs = (jobs[i].rows + clha::kGptqRows - 1) / clha::kGptqRows;
     s.wf_elems += slabs * clha::kGptqRows * cols;   // whole 64-row slabs
     s.total_slabs += slabs;
@@ -347,10 +357,9 @@ CLHA_API clha_status clha_create(const clha_moe_desc* desc, clha_ctx** out) {
   ctx->desc = d;
   ctx->slots = d.n_routed + (d.n_shared > 0 ? 1 : 0);
   if (hipGetDevice(&ctx->device) != hipSuccess ||
-      hipMalloc(&ctx->status_dev, 64) != hipSuccess ||
-      hipMemset(ctx->status_dev, 0, 64) != hipSuccess ||
+      !(ctx->status_dev = clha::status_acquire(ctx->device, &ctx->status_slot)) ||
       hipEventCreateWithFlags(&ctx->pinned_done, hipEventDisableTiming) != hipSuccess) {
-    if (ctx->status_dev) hipFree(ctx->status_dev);
+    if (ctx->status_dev) clha::status_release(ctx->device, ctx->status_slot);
     delete ctx;
     return CLHA_ERR_HIP;
   }
@@ -378,7 +387,15 @@ CLHA_API clha_status clha_destroy(clha_ctx* ctx) {
     if (ctx->stagger[g]) hipEventDestroy(ctx->stagger[g]);
     if (ctx->join[g]) hipEventDestroy(ctx->join[g]);
   }
-  if (ctx->status_dev) hipFree(ctx->status_dev);
+  if (ctx->status_dev) {
+    // kernels of this context may still write its record: wait for its device first
+    int cur = -1;
+    hipGetDevice(&cur);
+    if (cur != ctx->device) hipSetDevice(ctx->device);
+    hipDeviceSynchronize();
+    if (cur >= 0 && cur != ctx->device) hipSetDevice(cur);
+    clha::status_release(ctx->device, ctx->status_slot);
+  }
   delete ctx;
   return CLHA_OK;
 }
@@ -476,6 +493,7 @@ CLHA_API clha_status clha_collect_hessians(clha_ctx* ctx, int32_t layer, int64_t
   p.xg_tiles = (n_tokens * d.top_k + clha::kTokPad - 1) / clha::kTokPad + d.n_routed +
                (p.has_shared ? (n_tokens + clha::kTokPad - 1) / clha::kTokPad : 0);
   p.status = ctx->status_dev;
+  p.layer = layer;
   const hipStream_t s = as_stream(stream);
   {
     StageTimer t(ctx, CLHA_STAGE_ROUTE, s);
@@ -550,8 +568,17 @@ CLHA_API clha_status clha_aggregate(clha_ctx* ctx, int32_t n_layers, const int32
 // from and joined back to the caller's stream; group g starts once group g-1
 // has finished its first block step.  A group's GPTQ jobs follow its own
 // factorisation on its stream, so they overlap the later groups' factors.
-// `jobs` (host copy of the device job table) must be sorted by Hessian.
-static clha_status run_factor(clha_ctx* ctx, const GptqPlan& p, hipStream_t s, const GJob* jobs) {
+// `jobs` (host copy of the device job table) must be sorted by Hessian; `evals`
+// (same order, may be null) holds each job's optional second-Hessian loss,
+// computed on the job's stream once its GPTQ is done.
+struct EvalJob {
+  const float* H = nullptr;
+  float* out = nullptr;
+  float* partials = nullptr;
+};
+
+static clha_status run_factor(clha_ctx* ctx, const GptqPlan& p, hipStream_t s, const GJob* jobs,
+                              const EvalJob* evals = nullptr) {
   if (!ctx->aux_ready) {
     for (auto& a : ctx->aux)
       if (hipStreamCreateWithFlags(&a, hipStreamNonBlocking) != hipSuccess)
@@ -587,6 +614,12 @@ static clha_status run_factor(clha_ctx* ctx, const GptqPlan& p, hipStream_t s, c
     }
     clha::launch_factor_group(p, m0, m1, gs, g + 1 < groups ? ctx->stagger[g] : nullptr);
     if (jobs && r.j1 > r.j0) clha::launch_gptq(p, r, gs);
+    for (int k = r.j0; evals && k < r.j1; ++k) {
+      const GJob& jb = jobs[k];
+      if (!evals[k].H) continue;
+      clha::launch_loss(jb.rows, p.cols, p.group, jb.W, jb.dtype, jb.codes, jb.scales, jb.zeros, evals[k].H,
+                        p.gidx ? p.gidx + (size_t)jb.mat * p.cols : nullptr, evals[k].partials, evals[k].out, gs);
+    }
   }
   for (int g = 1; g < groups; ++g) {
     hipEventRecord(ctx->join[g], ctx->aux[g - 1]);
@@ -613,8 +646,11 @@ static clha_status check_gptq_args(clha_ctx* ctx, int32_t n_jobs, const clha_gpt
       return fail(ctx, CLHA_ERR_INVALID_ARG, "gptq: job %d has an unknown dtype", i);
     if (j.rows < 1 || j.bits < 2 || j.bits > 8)
       return fail(ctx, CLHA_ERR_SHAPE, "gptq: job %d needs rows >= 1 and bits in 2..8", i);
+    if (!j.H_eval != !j.loss_eval)
+      return fail(ctx, CLHA_ERR_INVALID_ARG, "gptq: job %d needs loss_eval exactly when H_eval is given", i);
     if (!aligned16(j.H) || !aligned16(j.W) || !aligned16(j.codes) || !aligned4(j.scales) ||
-        (j.loss && !aligned4(j.loss)))
+        (j.loss && !aligned4(j.loss)) || (j.H_eval && !aligned16(j.H_eval)) ||
+        (j.loss_eval && !aligned4(j.loss_eval)) || (j.status && !aligned4(j.status)))
       return fail(ctx, CLHA_ERR_ALIGN, "gptq: job %d has a misaligned pointer", i);
   }
   return CLHA_OK;
@@ -625,7 +661,7 @@ CLHA_API size_t clha_gptq_workspace_bytes_ex(const clha_ctx* ctx, int32_t n_jobs
   if (!ctx || n_jobs < 1 || !jobs || cols < 1) return 0;
   const JobScan js = scan_jobs(n_jobs, jobs, cols);
   return gptq_layout(nullptr, n_jobs, (int)js.mats.size(), cols, js.wf_elems, js.total_slabs, true,
-                     true, flags & kGptqFlags).bytes;
+                     true, flags & kGptqFlags, js.eval_parts).bytes;
 }
 
 CLHA_API size_t clha_gptq_workspace_bytes(const clha_ctx* ctx, int32_t n_jobs,
@@ -650,12 +686,12 @@ CLHA_API clha_status clha_gptq_quantize_ex(clha_ctx* ctx, int32_t n_jobs, const 
   const JobScan js = scan_jobs(n_jobs, jobs, cols);
   const int n_mats = (int)js.mats.size();
   const GptqLayout need = gptq_layout(nullptr, n_jobs, n_mats, cols, js.wf_elems, js.total_slabs,
-                                      true, true, flags);
+                                      true, true, flags, js.eval_parts);
   if (workspace_bytes < need.bytes)
     return fail(ctx, CLHA_ERR_WORKSPACE, "gptq: workspace %zu < %zu bytes", workspace_bytes, need.bytes);
   if (js.total_slabs > INT32_MAX) return fail(ctx, CLHA_ERR_SHAPE, "gptq: too many rows");
   const GptqLayout L = gptq_layout(workspace, n_jobs, n_mats, cols, js.wf_elems, js.total_slabs,
-                                   true, true, flags);
+                                   true, true, flags, js.eval_parts);
   const bool act = flags & CLHA_GPTQ_ACT_ORDER;
   // host tables: jobs, the Hessian pointers the factorisation reads, and (with
   // an option) the callers' Hessians, staged in one copy
@@ -669,9 +705,15 @@ CLHA_API clha_status clha_gptq_quantize_ex(clha_ctx* ctx, int32_t n_jobs, const 
   std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return js.mat_of[a] < js.mat_of[b]; });
   int64_t wf_off = 0;
   int slab_base = 0, tile_base = 0;
+  std::vector<EvalJob> evals(n_jobs);
   for (int k = 0; k < n_jobs; ++k) {
     const int i = order[k];
     const clha_gptq_job& j = jobs[i];
+    if (j.H_eval) {
+      evals[k].H = j.H_eval;
+      evals[k].out = j.loss_eval;
+      evals[k].partials = reinterpret_cast<float*>(L.eval_part + js.eval_off[i]);
+    }
     GJob g;
     g.W = j.W;
     g.codes = j.codes;
@@ -687,6 +729,9 @@ CLHA_API clha_status clha_gptq_quantize_ex(clha_ctx* ctx, int32_t n_jobs, const 
     g.n_slabs = (j.rows + clha::kGptqRows - 1) / clha::kGptqRows;
     g.tile_base = tile_base;
     g.n_tiles = (g.n_slabs * clha::kGptqRows + clha::kGemmTile - 1) / clha::kGemmTile;
+    g.user_index = i;
+    g.status = j.status;
+    g.dead_out = j.dead;
     hj[k] = g;
     wf_off += (int64_t)g.n_slabs * clha::kGptqRows * cols;
     slab_base += g.n_slabs;
@@ -739,10 +784,11 @@ CLHA_API clha_status clha_gptq_quantize_ex(clha_ctx* ctx, int32_t n_jobs, const 
   p.ebuf = L.ebuf;
   p.partials = reinterpret_cast<float*>(L.partials);
   p.status = ctx->status_dev;
+  p.mstat = L.mstat;
   {
     // the factorisation and the quantization overlap: both are timed as GPTQ
     StageTimer t(ctx, CLHA_STAGE_GPTQ, s);
-    st = run_factor(ctx, p, s, hj);
+    st = run_factor(ctx, p, s, hj, evals.data());
   }
   if (st != CLHA_OK) return st;
   if (g_idx) {
@@ -807,6 +853,7 @@ CLHA_API clha_status clha_inverse_cholesky(clha_ctx* ctx, int32_t n, const float
   p.lexp = L.lexp;
   p.lam = lambda_out;
   p.status = ctx->status_dev;
+  p.mstat = L.mstat;
   {
     StageTimer t(ctx, CLHA_STAGE_FACTOR, s);
     st = run_factor(ctx, p, s, nullptr);
@@ -837,7 +884,7 @@ CLHA_API clha_status clha_loss(clha_ctx* ctx, int32_t rows, int32_t cols, int32_
     return fail(ctx, CLHA_ERR_WORKSPACE, "loss: workspace too small");
   {
     StageTimer t(ctx, CLHA_STAGE_LOSS, as_stream(stream));
-    clha::launch_loss(rows, cols, group, W, w_dtype, codes, scales, zeros, H,
+    clha::launch_loss(rows, cols, group, W, w_dtype, codes, scales, zeros, H, nullptr,
                       static_cast<float*>(workspace), loss_out, as_stream(stream));
   }
   return hip_check(ctx, "loss");
@@ -871,20 +918,35 @@ CLHA_API clha_status clha_read_timing(clha_ctx* ctx, double* ms_out, int64_t* ca
 CLHA_API clha_status clha_sync(clha_ctx* ctx, void* stream) {
   if (!ctx) return CLHA_ERR_INVALID_ARG;
   const hipStream_t s = as_stream(stream);
-  int st = 0;
-  if (hipMemcpyAsync(&st, ctx->status_dev, sizeof(int), hipMemcpyDeviceToHost, s) != hipSuccess ||
+  uint32_t rec[clha::kStatusWords] = {};
+  if (hipMemcpyAsync(rec, ctx->status_dev, sizeof rec, hipMemcpyDeviceToHost, s) != hipSuccess ||
       hipStreamSynchronize(s) != hipSuccess)
     return fail(ctx, CLHA_ERR_HIP, "sync: %s", hipGetErrorString(hipGetLastError()));
   if (ctx->pinned_pending) {
     hipEventSynchronize(ctx->pinned_done);
     ctx->pinned_pending = false;
   }
-  if (st == 0) return CLHA_OK;
-  if (hipMemsetAsync(ctx->status_dev, 0, sizeof(int), s) != hipSuccess || hipStreamSynchronize(s) != hipSuccess)
-    return fail(ctx, CLHA_ERR_HIP, "sync: could not clear the status word");
-  if (st & clha::kStatusNonfinite)
-    return fail(ctx, CLHA_ERR_NONFINITE, "a router logit was NaN or infinite");
-  return fail(ctx, CLHA_ERR_NOT_PD, "a damped Hessian is not positive definite");
+  if (rec[0] == 0) return CLHA_OK;
+  if (hipMemsetAsync(ctx->status_dev, 0, sizeof rec, s) != hipSuccess || hipStreamSynchronize(s) != hipSuccess)
+    return fail(ctx, CLHA_ERR_HIP, "sync: could not clear the status record");
+  std::string where;
+  char buf[96];
+  if (rec[clha::kStatusJob]) {
+    snprintf(buf, sizeof buf, "GPTQ job %u", 0xffffffffu - rec[clha::kStatusJob]);
+    where += buf;
+  }
+  if (rec[clha::kStatusMat]) {
+    snprintf(buf, sizeof buf, "%sHessian %u", where.empty() ? "" : ", ", 0xffffffffu - rec[clha::kStatusMat]);
+    where += buf;
+  }
+  const uint64_t lay = (uint64_t)rec[clha::kStatusLayer] | ((uint64_t)rec[clha::kStatusLayer + 1] << 32);
+  if (rec[0] & clha::kStatusNonfinite) {
+    if (lay >> 32)
+      return fail(ctx, CLHA_ERR_NONFINITE, "layer %d: a router logit was NaN or infinite%s%s",
+                  (int32_t)(uint32_t)lay, where.empty() ? "" : "; also ", where.c_str());
+    return fail(ctx, CLHA_ERR_NONFINITE, "%s: a Hessian diagonal entry was NaN or infinite", where.c_str());
+  }
+  return fail(ctx, CLHA_ERR_NOT_PD, "%s: the damped Hessian is not positive definite", where.c_str());
 }
 
 static clha_status check_pack(clha_ctx* ctx, const char* what, int64_t n_codes, int32_t bits, const void* a,
@@ -976,6 +1038,7 @@ CLHA_API clha_status clha_collect_down_hessians(clha_ctx* ctx, int32_t layer, in
   p.overwrite = it->second.fresh ? 1 : 0;
   p.xgT = L.hT;
   p.status = ctx->status_dev;
+  p.layer = layer;
   // token tiles of 128 over all slots, at most one partial tile per slot
   const int64_t max_tiles = (n_tokens * d.top_k + (int64_t)(ctx->slots - n_routed) * n_tokens +
                              (int64_t)clha::kTokPad * ctx->slots) / 128 + ctx->slots + 1;

@@ -18,9 +18,13 @@
 // long products (the left-looking updates) run exactly on the int8 matrix
 // cores over 42-bit digit expansions of L (see "sliced factor" below): about
 // five times the sustained fp64 matrix rate, within 2^-36 of the fp64 product.
-// The triangular inverse then runs in fp32 (v_mfma_f32_32x32x2f32, about four
-// times the sustained fp64 matrix rate): its error is governed by
-// cond(L) = sqrt(cond(Hd)), and it moves U by a few fp32 ulps.
+// The triangular inverse then runs at fp32 precision on the bf16 matrix cores:
+// each fp32 operand is split into three bf16 parts and a product is the sum of
+// the six part products above 2^-24 of it, each exact, accumulated in fp32
+// (v_mfma_f32_32x32x16_bf16; see "triangular inverse" below).  Its error is
+// governed by cond(L) = sqrt(cond(Hd)): against the fp64 oracle U moves by
+// 1.7e-7 to 2.6e-7 relative at c = 256..2048 and cond(Hd) up to 2.4e3, about
+// what fp32 matrix-core products gave (1.8e-7 to 3.2e-7).
 //
 // Every step is batched over all distinct Hessians of one call:
 //   diag_stats      dead columns (H_ii == 0) and lambda = damp * mean(diag),
@@ -104,22 +108,34 @@ struct Tile64 {
 
 // ---------------------------------------------------------------- damping
 
+// Also starts the Hessian's status bits (mstat[m]): kStatusNonfinite when a
+// diagonal entry is NaN or infinite; the factor adds kStatusNotPd on a pivot
+// that is not positive.  A failing Hessian is recorded in the context's status
+// record by its index m_base + m.
 __global__ __launch_bounds__(256) void diag_stats_kernel(const float* const* __restrict__ mats,
                                                          int c, float damp,
                                                          uint8_t* __restrict__ dead,
                                                          double* __restrict__ lamd,
                                                          float* __restrict__ lam_out,
-                                                         int* __restrict__ lexp) {
+                                                         int* __restrict__ lexp,
+                                                         int* __restrict__ mstat,
+                                                         int* __restrict__ status, int m_base) {
   __shared__ double red[256];
+  __shared__ int nonfinite;
   const int m = blockIdx.x;
   const float* H = mats[m];
+  if (threadIdx.x == 0) nonfinite = 0;
+  __syncthreads();
   double sum = 0.0;
+  bool bad = false;
   for (int i = threadIdx.x; i < c; i += 256) {
     const float h = H[(int64_t)i * c + i];
     const bool z = h == 0.0f;
     dead[(int64_t)m * c + i] = z;
     sum += z ? 1.0 : (double)h;
+    bad |= !isfinite(h);
   }
+  if (bad) nonfinite = 1;   // any writer, the same value
   red[threadIdx.x] = sum;
   __syncthreads();
   for (int s = 128; s > 0; s >>= 1) {
@@ -130,6 +146,11 @@ __global__ __launch_bounds__(256) void diag_stats_kernel(const float* const* __r
   if (threadIdx.x == 0) {
     lamd[m] = l;
     if (lam_out) lam_out[m] = (float)l;
+    mstat[m] = nonfinite ? kStatusNonfinite : 0;
+    if (nonfinite) {
+      atomicOr(status, kStatusNonfinite);
+      atomicMax(reinterpret_cast<unsigned*>(status) + kStatusMat, 0xffffffffu - (unsigned)(m_base + m));
+    }
   }
   // Row exponents of the factor of the reversed matrix A = J Hd J: every entry
   // of row i of the factor is at most sqrt(A_ii) in magnitude, and 2^e >=
@@ -222,6 +243,7 @@ __device__ __forceinline__ void diag_step(double (&v)[kNb], int r, bool factor, 
 
 __device__ __forceinline__ void diag_block(const double* __restrict__ A, int c, int k, int m,
                                            double* __restrict__ dinv, int* __restrict__ status,
+                                           int* __restrict__ mstat, int m_base,
                                            double (*col)[kNb + 2]) {
   const int r = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -243,7 +265,11 @@ __device__ __forceinline__ void diag_block(const double* __restrict__ A, int c, 
   bool bad = false;
   diag_step<0>(v, r, factor, bad, col);
   if (factor) {
-    if (bad && r == 0) atomicOr(status, kStatusNotPd);
+    if (bad && r == 0) {
+      atomicOr(status, kStatusNotPd);
+      atomicOr(&mstat[m], kStatusNotPd);
+      atomicMax(reinterpret_cast<unsigned*>(status) + kStatusMat, 0xffffffffu - (unsigned)(m_base + m));
+    }
   } else if (wave == 1) {
     // Dinv_k row-major: lane r writes column r, each store one coalesced row
     double* D = dinv + ((int64_t)m * (c / kNb) + k) * kNb * kNb + r;
@@ -266,7 +292,9 @@ __global__ __launch_bounds__(256, 2) void chol_left_kernel(double* __restrict__ 
                                                            const uint8_t* __restrict__ dead,
                                                            const double* __restrict__ lamd, int c, int k,
                                                            double* __restrict__ dinv,
-                                                           int* __restrict__ status, int n_mats) {
+                                                           int* __restrict__ status,
+                                                           int* __restrict__ mstat, int m_base,
+                                                           int n_mats) {
   __shared__ __align__(16) int8_t As[kSlices][kNb][kLqPitch];
   __shared__ __align__(16) int8_t Bs[kSlices][kNb][kLqPitch];
   __shared__ __align__(16) double dcol[2][kNb + 2];
@@ -356,7 +384,7 @@ __global__ __launch_bounds__(256, 2) void chol_left_kernel(double* __restrict__ 
     // the whole workgroup: T_k is written, then factored and inverted
     __threadfence_block();
     __syncthreads();
-    diag_block(A, c, k, m, dinv, status, dcol);
+    diag_block(A, c, k, m, dinv, status, mstat, m_base, dcol);
   }
 }
 
@@ -717,11 +745,13 @@ void launch_factor_group(const GptqPlan& p, int m0, int m1, hipStream_t s, hipEv
   float* UT = p.UT ? p.UT + m0 * cc : nullptr;
   int* lexp = p.lexp + (int64_t)m0 * c;
   int8_t* Lq = reinterpret_cast<int8_t*>(X);   // free until the inverse starts
-  hipLaunchKernelGGL(diag_stats_kernel, dim3(n), dim3(256), 0, s, mats, c, p.damp, dead, lamd, lam, lexp);
+  int* mstat = p.mstat + m0;
+  hipLaunchKernelGGL(diag_stats_kernel, dim3(n), dim3(256), 0, s, mats, c, p.damp, dead, lamd, lam, lexp,
+                     mstat, p.status, m0);
   for (int k = 0; k < nbk; ++k) {
     const int per = ((nbk - k) * n + kXcds - 1) / kXcds;
     hipLaunchKernelGGL(chol_left_kernel, dim3(per * kXcds), dim3(256), 0, s, A, Lq, lexp, mats, dead, lamd, c, k,
-                       dinv, p.status, n);
+                       dinv, p.status, mstat, m0, n);
     if (k == 0 && step0_done) hipEventRecord(step0_done, s);
     if (k + 1 < nbk) {
       const int pper = ((nbk - k - 1) * n + kXcds - 1) / kXcds;

@@ -989,9 +989,22 @@ void launch_natural_gidx(int32_t* g, int cols, int group, hipStream_t s) {
   hipLaunchKernelGGL(natural_gidx_kernel, dim3((cols + 255) / 256), dim3(256), 0, s, g, cols, group);
 }
 
+// Per job: the loss by the OBS identity, the job's numerical status from its
+// Hessian's factor (NONFINITE before NOT_PD; a failing job is also recorded in
+// the context's status record by its caller index), and its Hessian's dead
+// columns in natural order (H_ii == 0 of the caller's Hessian).
 __global__ void gptq_finish_kernel(GptqPlan p, JobRange jr) {
   const GJob job = p.jobs[jr.j0 + blockIdx.x];
-  if (threadIdx.x != 0 || job.loss == nullptr) return;
+  const int c = p.cols;
+  if (job.dead_out) {
+    const float* H = p.src_mats ? p.src_mats[job.mat] : p.mats[job.mat];
+    for (int i = threadIdx.x; i < c; i += blockDim.x) job.dead_out[i] = H[(int64_t)i * c + i] == 0.0f;
+  }
+  if (threadIdx.x != 0) return;
+  const int ms = p.mstat[job.mat];
+  if (job.status) job.status[0] = (ms & kStatusNonfinite) ? 6 : (ms & kStatusNotPd) ? 5 : 0;   // clha_status
+  if (ms) atomicMax(reinterpret_cast<unsigned*>(p.status) + kStatusJob, 0xffffffffu - (unsigned)job.user_index);
+  if (job.loss == nullptr) return;
   const double* part = reinterpret_cast<const double*>(p.partials);
   double obs = 0.0, d2 = 0.0;
   for (int s = 0; s < job.n_slabs; ++s) {

@@ -26,9 +26,25 @@ constexpr int kGptqRows = 64;         // rows per GPTQ workgroup
 constexpr int kSuper = 256;           // GPTQ columns between trailing GEMM updates
 constexpr int kGemmTile = 128;        // rows and columns of a trailing-update tile
 
-// status word bits (device, latched; see clha_sync)
+// Status record of a context: 16 32-bit words of device memory (latched; see
+// clha_sync), held in a file-scope device array so that no context allocates.
+//   word 0       flag bits (kStatusNonfinite | kStatusNotPd)
+//   word 1       0, or 0xffffffff - i for the lowest caller index i of a GPTQ job
+//                whose Hessian failed (atomicMax keeps the lowest index)
+//   word 2       the same for the lowest failing Hessian of the call
+//   words 4, 5   0, or (1 << 32 | layer) of the first collection with a
+//                non-finite router logit (the first writer wins)
 constexpr int kStatusNonfinite = 1;
 constexpr int kStatusNotPd = 2;
+constexpr int kStatusWords = 16;
+constexpr int kStatusJob = 1;
+constexpr int kStatusMat = 2;
+constexpr int kStatusLayer = 4;
+constexpr int kMaxContexts = 1024;    // live contexts per device (status records)
+// A free status record of `device` (the current device), cleared, and its slot;
+// nullptr when all kMaxContexts records are taken or the lookup fails.
+int* status_acquire(int device, int* slot);
+void status_release(int device, int slot);
 constexpr int kSlices = 6;            // signed 7-bit digits per sliced fp64 factor entry
 
 // ---------------------------------------------------------------- collection
@@ -55,7 +71,8 @@ struct CollectPlan {
   int32_t* token_ids;    // [n*K]
   uint16_t* xgT;         // gathered activations: per slot, 32-token blocks of [d][32]
   int64_t xg_tiles;      // upper bound of 64-token tiles over all slots
-  int* status;
+  int* status;           // the context's status record
+  int layer;             // the collected layer (named by a non-finite logit)
 };
 
 void launch_route(const float* logits, const CollectPlan& p, hipStream_t s);
@@ -101,6 +118,9 @@ struct GJob {
   int32_t n_slabs;
   int32_t tile_base;     // first global row tile (kGemmTile rows) of the trailing update
   int32_t n_tiles;
+  int32_t user_index;    // the job's index in the caller's array
+  int32_t* status;       // optional: the job's numerical status (clha_status code)
+  uint8_t* dead_out;     // optional: dead-column flags of the job's Hessian, natural order
 };
 
 struct GptqPlan {
@@ -120,7 +140,8 @@ struct GptqPlan {
   float* wf;                 // device fp32 working copies of all jobs' weights
   float* ebuf;               // device [padded rows][kSuper] a superblock's negated errors
   float* partials;           // device [total_slabs][2]
-  int* status;
+  int* status;               // the context's status record
+  int* mstat;                // device [n_mats] status bits of each distinct Hessian's factor
   // GPTQ options (zero / null when off)
   int act_order;             // columns processed by decreasing H_ii
   int static_groups;         // grids fitted once per natural group before any update
@@ -146,9 +167,10 @@ void launch_gptq_prep(const GptqPlan& p, const JobRange& r, hipStream_t s);
 void launch_natural_gidx(int32_t* g, int cols, int group, hipStream_t s);
 
 // ---------------------------------------------------------------- loss
+// gidx (optional, device int32 [cols]) names each column's grid; null means column k / group
 void launch_loss(int rows, int cols, int group, const void* W, int dtype, const uint8_t* codes,
-                 const float* scales, const uint8_t* zeros, const float* H, float* partials,
-                 float* loss_out, hipStream_t s);
+                 const float* scales, const uint8_t* zeros, const float* H, const int* gidx,
+                 float* partials, float* loss_out, hipStream_t s);
 int64_t loss_partial_count(int rows, int cols);
 
 // ---------------------------------------------------------------- packed codes

@@ -1,5 +1,6 @@
 // Reconstruction loss of a quantized matrix under an arbitrary Hessian,
 //   loss = sum_r (Wq_r - W_r) H (Wq_r - W_r)^T ,
+// with column k of Wq on grid gidx[k] (or k / group when no g_idx is given),
 // the per-layer term of the objective in the CLHA summary, section 2.1 (with
 // H = H_comb it is the combined objective; with H = H_a or H_b it is the error
 // a shared weight leaves on one layer's calibration data).
@@ -15,9 +16,9 @@ namespace clha {
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 __device__ __forceinline__ float delta_at(const void* W, int dtype, const uint8_t* codes,
-                                          const float* scales, const uint8_t* zeros, int cols,
-                                          int group, int r, int k) {
-  const int64_t gi = (int64_t)r * (cols / group) + k / group;
+                                          const float* scales, const uint8_t* zeros, const int* gidx,
+                                          int cols, int group, int r, int k) {
+  const int64_t gi = (int64_t)r * (cols / group) + (gidx ? gidx[k] : k / group);
   const float wq = scales[gi] * ((float)codes[(int64_t)r * cols + k] - (float)zeros[gi]);
   float w;
   if (dtype == 1) w = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(W)[(int64_t)r * cols + k] << 16);
@@ -30,6 +31,7 @@ __global__ __launch_bounds__(256) void loss_tile_kernel(int rows, int cols, int 
                                                         const float* __restrict__ scales,
                                                         const uint8_t* __restrict__ zeros,
                                                         const float* __restrict__ H,
+                                                        const int* __restrict__ gidx,
                                                         double* __restrict__ partials) {
   __shared__ float Ds[64][65];   // Delta chunk, [k][row]
   __shared__ float Hs[64][65];   // H chunk, [k][col]
@@ -43,7 +45,7 @@ __global__ __launch_bounds__(256) void loss_tile_kernel(int rows, int cols, int 
     __syncthreads();
     for (int idx = tid; idx < 64 * 64; idx += 256) {
       const int a = idx >> 6, b = idx & 63;     // a: row (Delta) / k (H), b: k (Delta) / col (H)
-      Ds[b][a] = (r0 + a < rows) ? delta_at(W, dtype, codes, scales, zeros, cols, group, r0 + a, k0 + b) : 0.0f;
+      Ds[b][a] = (r0 + a < rows) ? delta_at(W, dtype, codes, scales, zeros, gidx, cols, group, r0 + a, k0 + b) : 0.0f;
       Hs[a][b] = H[(int64_t)(k0 + a) * cols + j0 + b];
     }
     __syncthreads();
@@ -58,7 +60,7 @@ __global__ __launch_bounds__(256) void loss_tile_kernel(int rows, int cols, int 
     const int row = r0 + wm * 32 + 8 * (r >> 2) + 4 * kh + (r & 3);
     if (row < rows)
       part += (double)acc[r] *
-              (double)delta_at(W, dtype, codes, scales, zeros, cols, group, row, j0 + bcol);
+              (double)delta_at(W, dtype, codes, scales, zeros, gidx, cols, group, row, j0 + bcol);
   }
   red[tid] = part;
   __syncthreads();
@@ -81,11 +83,11 @@ int64_t loss_partial_count(int rows, int cols) {
 }
 
 void launch_loss(int rows, int cols, int group, const void* W, int dtype, const uint8_t* codes,
-                 const float* scales, const uint8_t* zeros, const float* H, float* partials,
-                 float* loss_out, hipStream_t s) {
+                 const float* scales, const uint8_t* zeros, const float* H, const int* gidx,
+                 float* partials, float* loss_out, hipStream_t s) {
   double* part = reinterpret_cast<double*>(partials);
   hipLaunchKernelGGL(loss_tile_kernel, dim3(cols / 64, (rows + 63) / 64), dim3(256), 0, s, rows,
-                     cols, group, W, dtype, codes, scales, zeros, H, part);
+                     cols, group, W, dtype, codes, scales, zeros, H, gidx, part);
   hipLaunchKernelGGL(loss_finish_kernel, dim3(1), dim3(64), 0, s, part,
                      loss_partial_count(rows, cols), loss_out);
 }

@@ -30,7 +30,7 @@ namespace clha {
 
 __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits, int64_t n,
                                                     int E, int K, int32_t* __restrict__ topk,
-                                                    int* __restrict__ status) {
+                                                    int* __restrict__ status, int layer) {
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (t >= n) return;
   const float* row = logits + t * E;
@@ -65,13 +65,18 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
 #pragma unroll
   for (int p = 0; p < kMaxTopK; ++p)
     if (p < K) topk[t * K + p] = idx[p];
-  if (bad) atomicOr(status, kStatusNonfinite);
+  if (bad) {
+    atomicOr(status, kStatusNonfinite);
+    // the first collection with a non-finite logit names its layer
+    atomicCAS(reinterpret_cast<unsigned long long*>(status + kStatusLayer), 0ull,
+              (1ull << 32) | (unsigned long long)(uint32_t)layer);
+  }
 }
 
 void launch_route(const float* logits, const CollectPlan& p, hipStream_t s) {
   const unsigned grid = (unsigned)((p.n_tokens + 255) / 256);
   hipLaunchKernelGGL(route_kernel, dim3(grid), dim3(256), 0, s, logits, p.n_tokens, p.E, p.K,
-                     p.topk, p.status);
+                     p.topk, p.status, p.layer);
 }
 
 // ------------------------------------------------------------------ bucketing

@@ -19,17 +19,20 @@
  *
  * Conventions
  *   - Every array argument marked "device" is a pointer into GPU memory that the
- *     caller allocated and owns.  The library never frees caller memory.  The
- *     only memory the library allocates itself is a 64-byte device status word
- *     per context (clha_create) and host-side bookkeeping.
+ *     caller allocated and owns.  The library never allocates or frees device
+ *     memory: each context's status record (64 bytes) is one of 1024 records in
+ *     a device array of the library's code object, and the library's only
+ *     allocations are host-side (bookkeeping, page-locked staging of job tables).
  *   - `stream` is a hipStream_t passed as void*; NULL means the default stream.
  *     Every compute call only enqueues work on `stream` and returns; outputs are
  *     valid once the stream has been synchronised (clha_sync does that).
  *   - Argument, shape and alignment errors are detected on the host before
  *     anything is enqueued; the call then returns the error and enqueues
  *     nothing.  Numerical failures found on the device (non-finite router
- *     logits, a damped Hessian that is not positive definite) are latched in
- *     the context's status word and returned by the next clha_sync.
+ *     logits, a damped Hessian that is not positive definite or has a
+ *     non-finite diagonal) are written to the failing GPTQ job's status, when
+ *     it has one, and latched in the context's status record; the next
+ *     clha_sync returns the first of them and names the layer, job or Hessian.
  *   - Matrices are row-major.  bf16 values are passed as their uint16 bit
  *     patterns.  Device pointers must be 16-byte aligned.
  *   - A context is used by one host thread at a time.  No C++ exception crosses
@@ -81,10 +84,12 @@ typedef struct clha_moe_desc {
 typedef struct clha_ctx clha_ctx;
 
 /* Creates a context for one MoE block shape on the current HIP device.
- * Errors: INVALID_ARG (null), SHAPE (desc outside the ranges above), HIP. */
+ * Errors: INVALID_ARG (null), SHAPE (desc outside the ranges above), HIP (also when
+ * 1024 contexts are already alive on the device). */
 CLHA_API clha_status clha_create(const clha_moe_desc* desc, clha_ctx** out);
 
-/* Frees the context (host bookkeeping and its status word).  Accepts NULL. */
+/* Frees the context (host bookkeeping; its status record returns to the pool).
+ * Accepts NULL. */
 CLHA_API clha_status clha_destroy(clha_ctx* ctx);
 
 /* Text of the last error on this context (static storage owned by ctx). */
@@ -175,6 +180,18 @@ typedef struct clha_gptq_job {
   float* scales;       /* device out, float [rows][cols/group] */
   uint8_t* zeros;      /* device out, uint8 [rows][cols/group] */
   float* loss;         /* device out, float [1]: tr[(Wq - W) H (Wq - W)^T]; may be NULL */
+  const float* H_eval; /* device, float [cols][cols], may be NULL: a second Hessian to evaluate
+                          the result under (e.g. one layer's H_l, the calibration-Hessian
+                          error of section 4); H_eval may equal H */
+  float* loss_eval;    /* device out, float [1]: tr[(Wq - W) H_eval (Wq - W)^T], computed
+                          directly (2 rows cols^2 flops); needed iff H_eval is given */
+  uint8_t* dead;       /* device out, uint8 [cols], may be NULL: 1 where H_ii == 0 (the column
+                          was treated as dead), in natural column order */
+  int32_t* status;     /* device out, int32 [1], may be NULL: CLHA_OK, CLHA_ERR_NOT_PD (the
+                          damped H is not positive definite) or CLHA_ERR_NONFINITE (a diagonal
+                          entry of H is NaN or infinite); the job's outputs are undefined
+                          unless CLHA_OK.  Off-diagonal entries of H and the weights must be
+                          finite; they are not checked. */
 } clha_gptq_job;
 
 /* Device workspace bytes clha_gptq_quantize needs for these jobs. */
@@ -199,7 +216,9 @@ CLHA_API size_t clha_gptq_workspace_bytes(const clha_ctx* ctx, int32_t n_jobs,
  *   block     64 or 128
  *   damp      relative damping, >= 0 (0.01 is customary)
  * Errors: INVALID_ARG, SHAPE, ALIGN, WORKSPACE.  A Hessian that is not positive definite
- * after damping latches CLHA_ERR_NOT_PD (that job's outputs are then undefined). */
+ * after damping, or one with a non-finite diagonal entry, sets CLHA_ERR_NOT_PD or
+ * CLHA_ERR_NONFINITE in the status of every job on it (the other jobs are unaffected) and
+ * latches it for clha_sync, which names the lowest failing job index of the call. */
 CLHA_API clha_status clha_gptq_quantize(clha_ctx* ctx, int32_t n_jobs, const clha_gptq_job* jobs,
                                         int32_t cols, int32_t group, int32_t block, float damp,
                                         void* workspace, size_t workspace_bytes, void* stream);
@@ -343,8 +362,10 @@ CLHA_API clha_status clha_set_timing(clha_ctx* ctx, int32_t enable);
  * n <= CLHA_NUM_STAGES; either may be NULL), then forgets the records. */
 CLHA_API clha_status clha_read_timing(clha_ctx* ctx, double* ms_out, int64_t* calls_out, int32_t n);
 
-/* Waits for `stream`, then returns and clears the first latched device error
- * (NONFINITE or NOT_PD), or CLHA_OK. */
+/* Waits for `stream`, then returns and clears the latched device errors: NONFINITE (a router
+ * logit, naming the first layer that had one; or a Hessian's diagonal) before NOT_PD, or
+ * CLHA_OK.  clha_last_error names the lowest failing GPTQ job index and Hessian index of the
+ * calls since the last clha_sync (Hessians numbered in order of first use within a call). */
 CLHA_API clha_status clha_sync(clha_ctx* ctx, void* stream);
 
 #ifdef __cplusplus

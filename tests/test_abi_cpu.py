@@ -46,3 +46,21 @@ def test_create_rejects_bad_shapes_without_a_device():
 def test_build_entry_compiles_for_gfx950():
     src = open(os.path.join(ROOT, "gptq_calibration_moe_amd", "build.py")).read()
     assert "gfx950" in src and "-packed-fp32-ops" in src
+
+
+def test_job_struct_layout_matches_the_header(tmp_path):
+    """The binding's ctypes clha_gptq_job has the C struct's size and field offsets
+    (a host C program built against include/clha.h prints them)."""
+    import subprocess
+    import gptq_calibration_moe_amd as g
+    fields = [f for f, _ in g.GptqJob._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "clha.h"\nint main(void) {\n'
+                   '  printf("%zu\\n", sizeof(clha_gptq_job));\n'
+                   + "".join(f'  printf("%zu\\n", offsetof(clha_gptq_job, {f}));\n' for f in fields)
+                   + "  return 0;\n}\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    out = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    assert out[0] == ctypes.sizeof(g.GptqJob)
+    assert out[1:] == [getattr(g.GptqJob, f).offset for f in fields]
