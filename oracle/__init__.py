@@ -53,7 +53,7 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = [
-    "bf16_to_f64", "route", "bucket", "gram", "layer_hessians", "aggregate",
+    "bf16_to_f64", "route", "bucket", "gram", "gram_rows", "layer_hessians", "aggregate",
     "inverse_cholesky_upper", "quant_params", "quantize", "gptq", "dequantize",
     "dequantize_idx", "act_order_perm",
     "loss", "calibrate_pair",
@@ -109,6 +109,20 @@ def gram(x) -> np.ndarray:
     """S = X^T X in float64 (raw activation Gram sum of one expert's tokens)."""
     x64 = np.asarray(x, dtype=np.float64)
     return x64.T @ x64
+
+
+def gram_rows(x_bits, rows, chunk: int = 16384) -> np.ndarray:
+    """Rows `rows` of the Gram sum S = X^T X of bf16 activations, in float64:
+    S[i, j] = sum_t x_ti x_tj for i in rows and every j.  Tokens are taken in
+    chunks of `chunk` rows only to bound memory; every product of two bf16
+    values is exact in float64."""
+    xb = np.asarray(x_bits, dtype=np.uint16)
+    rows = np.asarray(rows, dtype=np.int64)
+    out = np.zeros((rows.size, xb.shape[1]))
+    for t0 in range(0, xb.shape[0], chunk):
+        x = bf16_to_f64(xb[t0:t0 + chunk])
+        out += x[:, rows].T @ x
+    return out
 
 
 def layer_hessians(x_bits, topk, n_routed: int, n_shared: int, slots=None):

@@ -131,6 +131,22 @@ def test_gram_equals_sum_of_outer_products():
     assert np.linalg.eigvalsh(g).min() >= -1e-12 * np.trace(g)
 
 
+def test_gram_rows_brute_force():
+    """Rows of S = X^T X, element by element as sums of products over tokens,
+    across the chunk boundary (chunk 7 over 23 tokens)."""
+    rng = _rng(8)
+    xb = gen.bf16_bits(rng.standard_normal((23, 6)).astype(np.float32))
+    x = gen.bf16_value(xb).astype(np.float64)
+    rows = [4, 0, 4]
+    got = oracle.gram_rows(xb, rows, chunk=7)
+    for a, i in enumerate(rows):
+        for j in range(6):
+            want = 0.0
+            for t in range(23):
+                want += x[t, i] * x[t, j]
+            assert abs(got[a, j] - want) <= 1e-14 * max(1.0, abs(want))
+
+
 def test_bf16_widening():
     bits = np.array([0x3F80, 0xBF80, 0x0000, 0x8000, 0x4049, 0x7F7F], np.uint16)
     v = oracle.bf16_to_f64(bits)
