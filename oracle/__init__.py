@@ -211,6 +211,8 @@ def aggregate(S_list, n_list, mode: str, alpha=None):
     mode 'explicit': H = sum_i alpha_i S_i/n_i (alpha renormalised over the
                      non-empty layers if some weighted layer is empty).
     A single layer (PLIC) is any mode with one entry: H = S/n.
+    The S_i may also be matching slices of the Gram sums (rows, or a diagonal):
+    every step is elementwise.
     Returns (H, alpha_used).  All layers empty -> (I, zeros).
     """
     n = np.asarray(n_list, dtype=np.int64)
@@ -237,7 +239,7 @@ def aggregate(S_list, n_list, mode: str, alpha=None):
             a = a / a.sum()
     else:
         raise ValueError(mode)
-    H = np.zeros((d, d))
+    H = np.zeros(np.shape(S_list[0]))
     for ai, S, ni in zip(a, S_list, n):
         if ni > 0 and ai != 0.0:
             H += ai * (np.asarray(S, np.float64) / float(ni))

@@ -4,6 +4,7 @@ import numpy as np
 import torch
 
 import gen
+import oracle
 
 HESS_TOL = 1e-4        # max |H_gpu - H_ref| / sqrt(H_ref_ii H_ref_jj)
 CODE_AGREE = 0.999     # fraction of identical codes
@@ -128,3 +129,79 @@ def assert_down_gram(S_gpu, S_ref, bound, label):
     excess = np.abs(S_gpu - S_ref) - bound - HESS_TOL * np.outer(d, d)
     worst = float(np.max(np.where(low, excess, -np.inf)))
     assert worst <= 0.0, f"{label}: exceeds the bound by {worst:.3e}"
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def slot_rows(x_bits, bucket, slot, n_routed):
+    """Token rows (bf16 bits) of one Hessian slot: a routed expert's tokens, or
+    every token for the shared slot."""
+    counts, offsets, ids = bucket
+    if slot < n_routed:
+        return x_bits[ids[offsets[slot]:offsets[slot + 1]]]
+    return x_bits
+
+
+def col_sq_sums(x_bits, chunk=16384):
+    """sum_t x_tj^2 per column, float64 (the tolerance's normaliser)."""
+    out = np.zeros(x_bits.shape[1])
+    for t0 in range(0, x_bits.shape[0], chunk):
+        x = oracle.bf16_to_f64(x_bits[t0:t0 + chunk])
+        out += np.einsum("ti,ti->i", x, x)
+    return out
+
+
+def check_all_slots(H_dev, x_list, buckets, n_routed, slots, mode, seed, n_rows=24, label=""):
+    """Every slot's combined Hessian on n_rows sampled rows against the oracle's
+    aggregation of the per-layer Gram-sum rows."""
+    rng = np.random.default_rng(seed)
+    d = H_dev.shape[-1]
+    worst = 0.0
+    for s in range(slots):
+        rows = np.sort(rng.choice(d, n_rows, replace=False))
+        S, D, n = [], [], []
+        for l, x in enumerate(x_list):
+            xs = slot_rows(x, buckets[l], s, n_routed)
+            S.append(oracle.gram_rows(xs, rows))
+            D.append(col_sq_sums(xs))
+            n.append(xs.shape[0])
+        R, _ = oracle.aggregate(S, n, mode)
+        Rd, _ = oracle.aggregate(D, n, mode)
+        G = H_dev[s][torch.from_numpy(rows).to(H_dev.device)].cpu().numpy().astype(np.float64)
+        den = np.sqrt(np.outer(Rd[rows], Rd))
+        err = float(np.max(np.abs(G - R) / den))
+        worst = max(worst, err)
+        assert err <= HESS_TOL, f"{label} slot {s}: H_comb error {err:.3e}"
+    say(f"{label}: all {slots} slots within {worst:.2e}")
+
+
+def full_hessian(x_list, buckets, slot, n_routed):
+    """Per-layer full Gram sums (float64) and token counts of one slot."""
+    S, n = [], []
+    for l, x in enumerate(x_list):
+        xs = slot_rows(x, buckets[l], slot, n_routed)
+        S.append(np.zeros((x.shape[1], x.shape[1])))
+        for t0 in range(0, xs.shape[0], 32768):
+            S[-1] += oracle.gram(oracle.bf16_to_f64(xs[t0:t0 + 32768]))
+        n.append(xs.shape[0])
+    return S, n
+
+
+def check_gptq(wl, w_bits, H_ref, out, bits, label):
+    wv = gen.weights_value(wl, w_bits).astype(np.float64)
+    ref = oracle.gptq(wv, H_ref, bits, wl.group, wl.damp, wl.block)
+    codes = out["codes"].cpu().numpy()
+    a = agree(codes, ref["codes"])
+    assert a >= CODE_AGREE, f"{label}: codes agree {a:.5f}"
+    assert codes.max() <= (1 << bits) - 1
+    ok = (codes == ref["codes"]).all(axis=1)
+    assert ok.mean() >= 0.9, f"{label}: only {ok.mean():.3f} of the rows agree in every code"
+    np.testing.assert_allclose(out["scales"].cpu().numpy()[ok], ref["scales"][ok], rtol=SCALE_RTOL)
+    assert (out["zeros"].cpu().numpy()[ok] == ref["zeros"][ok]).all(), label
+    want = oracle.loss(wv, ref["wq"], H_ref)
+    got = float(out["loss"].cpu().numpy()[0])
+    assert abs(got - want) <= LOSS_RTOL * abs(want), f"{label}: loss {got} vs {want}"
+    say(f"{label}: codes agree {a:.5f}, loss {got:.6g} vs {want:.6g}")
+    return ref, codes

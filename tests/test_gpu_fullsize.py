@@ -3,9 +3,9 @@
 * mid MoE block, exactly as the benchmark step runs it: d 2048, 64 routed + 2
   shared experts, top-6, 65,536 tokens per layer, routing-frequency alpha, 66
   stacked gate|up jobs of 2816x2048 bf16, 3-bit, group 128.  Checked: routing,
-  counts and token lists of every token (bit-exact); the combined Hessian of
-  sampled routed experts and of the shared slot; GPTQ codes, grids and loss of
-  those experts.
+  counts and token lists of every token (bit-exact); all 65 combined Hessians
+  on sampled rows; GPTQ codes, grids and loss of 14 routed experts and both
+  shared experts.
 * full-depth shapes (d 2048, Zipf(1.1) expert load, equal alpha, 2-bit) on one
   pair at 16,384 tokens: the most and least loaded experts end to end.
 * drift stress (d 4096, 128 experts, top-8, router logits from the activations,
@@ -22,8 +22,8 @@ import torch
 
 import gen
 import oracle
-from gpu_util import (CODE_AGREE, HESS_TOL, LOSS_RTOL, SCALE_RTOL, agree, bits_to_dev, dev, hess_err, to_dev,
-                      weights_to_dev)
+from gpu_util import (CODE_AGREE, HESS_TOL, LOSS_RTOL, SCALE_RTOL, agree, bits_to_dev, check_all_slots, dev,
+                      full_hessian, hess_err, to_dev, weights_to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -96,23 +96,13 @@ def test_mid_moe_block_full_size_in_bench_configuration():
         assert np.array_equal(got_counts[:E], counts) and got_counts[E] == n
         buckets.append((counts, offsets, ids))
 
-    # sampled routed experts and the shared slot: H_comb, then GPTQ end to end
+    # every slot's H_comb on sampled rows, then GPTQ of 16 jobs from the batch
+    check_all_slots(cal.H, inp["x"], buckets, E, ctx.slots, wl.alpha, seed=7, label="mid MoE block rt")
     rng = np.random.default_rng(7)
-    sample = sorted(rng.choice(E, 2, replace=False).tolist()) + [E]        # E = first shared expert
+    sample = sorted(rng.choice(E, 14, replace=False).tolist()) + [E, E + 1]   # two shared experts
     for e in sample:
-        S, cnt = [], []
-        for l in range(2):
-            if e < E:
-                counts, offsets, ids = buckets[l]
-                S.append(oracle.gram(_expert_rows(inp["x"][l], ids, offsets, e)))
-                cnt.append(int(counts[e]))
-            else:
-                S.append(oracle.gram(oracle.bf16_to_f64(inp["x"][l])))
-                cnt.append(n)
+        S, cnt = full_hessian(inp["x"], buckets, cal.slot_of(e), E)
         H_ref, _ = oracle.aggregate(S, cnt, wl.alpha)
-        slot = cal.slot_of(e)
-        err = hess_err(cal.H[slot].cpu().numpy(), H_ref)
-        assert err <= HESS_TOL, f"expert {e}: H_comb error {err:.3e}"
         bits = wl.shared_bits if e >= E else wl.bits
         _check_gptq(wl, w_host[e], H_ref, outputs[e], bits, f"expert {e}")
 

@@ -936,3 +936,15 @@ def test_planted_calibrate_pair_mistakes_are_caught(old, new):
     assert _calibrate_pair_pins_hold(oracle.calibrate_pair)
     bad = _mutant(oracle.calibrate_pair, old, new)
     assert not _calibrate_pair_pins_hold(bad)
+
+
+@pytest.mark.parametrize("mode", ["rt", "eq"])
+def test_aggregate_of_slices_is_the_slice_of_aggregate(mode):
+    """Aggregation is elementwise: the full-size parity tests combine sampled
+    rows (and diagonals) of the per-layer Gram sums."""
+    Sa, na, Sb, nb = _layers(34)
+    H, _ = oracle.aggregate([Sa, Sb], [na, nb], mode)
+    rows = [1, 7, 3]
+    Hr, _ = oracle.aggregate([Sa[rows], Sb[rows]], [na, nb], mode)
+    Hd, _ = oracle.aggregate([np.diag(Sa), np.diag(Sb)], [na, nb], mode)
+    assert np.array_equal(H[rows], Hr) and np.array_equal(np.diag(H), Hd)
