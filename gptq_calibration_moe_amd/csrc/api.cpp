@@ -179,6 +179,7 @@ struct CollectLayout {
   int32_t* seg;
   int32_t* split;
   float* partials;
+  int max_partials;
   int32_t* token_ids;
   uint16_t* xgT;
   size_t bytes;
@@ -198,12 +199,14 @@ CollectLayout collect_layout(const clha_ctx* ctx, void* ws) {
   L.offsets = c.take<int64_t>((size_t)d.n_routed + 1);
   L.pad_off = c.take<int64_t>((size_t)ctx->slots + 1);
   L.slot_order = c.take<int32_t>((size_t)ctx->slots);
-  L.work = c.take<int32_t>((size_t)clha::kXcds * clha::kMaxSegs * clha::syrk_items_per_slot(d.d));
+  L.max_partials = clha::max_partials(d.d, n, d.top_k, ctx->slots);
+  const int max_segs = ctx->slots + L.max_partials;
+  L.work = c.take<int32_t>((size_t)clha::kXcds * max_segs * clha::syrk_items_per_slot(d.d));
   L.work_len = c.take<int32_t>(clha::kXcds);
   L.work_next = c.take<int32_t>(clha::kXcds);
-  L.seg = c.take<int32_t>((size_t)4 * clha::kMaxSegs);
-  L.split = c.take<int32_t>((size_t)1 + 3 * clha::kMaxPartials);
-  L.partials = c.take<float>((size_t)clha::kMaxPartials * d.d * d.d);
+  L.seg = c.take<int32_t>((size_t)4 * max_segs);
+  L.split = c.take<int32_t>((size_t)1 + 3 * L.max_partials);
+  L.partials = c.take<float>((size_t)L.max_partials * d.d * d.d);
   L.token_ids = c.take<int32_t>((size_t)n * d.top_k);
   L.xgT = c.take<uint16_t>((size_t)xg_tokens * d.d);
   L.bytes = c.off;
@@ -225,6 +228,7 @@ struct DownLayout {
   int32_t* seg;
   int32_t* split;
   float* partials;
+  int max_partials;
   uint16_t* hT;
   size_t bytes;
 };
@@ -240,12 +244,14 @@ DownLayout down_layout(const clha_ctx* ctx, int n_routed, void* ws) {
   L.pad_off = c.take<int64_t>((size_t)slots + 1);
   L.slot_order = c.take<int32_t>((size_t)slots);
   L.tile_off = c.take<int32_t>((size_t)slots + 1);
-  L.work = c.take<int32_t>((size_t)clha::kXcds * clha::kMaxSegs * clha::syrk_items_per_slot(d.d));
+  L.max_partials = clha::max_partials(d.d, n, d.top_k, slots);
+  const int max_segs = slots + L.max_partials;
+  L.work = c.take<int32_t>((size_t)clha::kXcds * max_segs * clha::syrk_items_per_slot(d.d));
   L.work_len = c.take<int32_t>(clha::kXcds);
   L.work_next = c.take<int32_t>(clha::kXcds);
-  L.seg = c.take<int32_t>((size_t)4 * clha::kMaxSegs);
-  L.split = c.take<int32_t>((size_t)1 + 3 * clha::kMaxPartials);
-  L.partials = c.take<float>((size_t)clha::kMaxPartials * d.d * d.d);
+  L.seg = c.take<int32_t>((size_t)4 * max_segs);
+  L.split = c.take<int32_t>((size_t)1 + 3 * L.max_partials);
+  L.partials = c.take<float>((size_t)L.max_partials * d.d * d.d);
   L.hT = c.take<uint16_t>((size_t)h_tokens * d.d);
   L.bytes = c.off;
   return L;
@@ -486,6 +492,8 @@ CLHA_API clha_status clha_collect_hessians(clha_ctx* ctx, int32_t layer, int64_t
   p.seg = L.seg;
   p.split = L.split;
   p.partials = L.partials;
+  p.max_partials = L.max_partials;
+  p.max_segs = ctx->slots + L.max_partials;
   p.syrk_items = clha::syrk_items_per_slot(d.d);
   p.overwrite = it->second.fresh ? 1 : 0;
   p.token_ids = token_ids_out ? token_ids_out : L.token_ids;
@@ -1034,6 +1042,8 @@ CLHA_API clha_status clha_collect_down_hessians(clha_ctx* ctx, int32_t layer, in
   p.seg = L.seg;
   p.split = L.split;
   p.partials = L.partials;
+  p.max_partials = L.max_partials;
+  p.max_segs = ctx->slots + L.max_partials;
   p.syrk_items = clha::syrk_items_per_slot(d.d);
   p.overwrite = it->second.fresh ? 1 : 0;
   p.xgT = L.hT;

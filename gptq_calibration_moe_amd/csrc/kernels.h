@@ -16,9 +16,13 @@ constexpr int kMaxExperts = 256;
 constexpr int kMaxTopK = 16;
 constexpr int kMaxLayers = 8;
 constexpr int kSyrkTile = 256;        // Gram-sum output tile
-constexpr int kMaxPartials = 8;       // partial Gram-sum buffers of token-split slots
+constexpr int kMaxPartialsCap = 512;  // most partial Gram-sum buffers of token-split slots
+constexpr int kSegTokens = 8192;      // longest Gram-sum segment (one flush interval)
 constexpr int kMaxSlots = kMaxExperts + 1;                // Hessian slots of one layer
-constexpr int kMaxSegs = kMaxExperts + 1 + kMaxPartials;   // Gram-sum segments per call
+constexpr int kMaxSegsCap = kMaxSlots + kMaxPartialsCap;  // most Gram-sum segments per call
+// Partial buffers of a context: enough for every segment past each slot's first
+// at max_tokens, at most 4 GiB of them (and at least 8).
+int max_partials(int d, int64_t max_tokens, int top_k, int slots);
 constexpr int kXcds = 8;              // accelerator complex dies; workgroup b runs on die b % 8
 constexpr int kSyrkWgPerXcd = 32;     // persistent Gram-sum workgroups per die (one per CU)
 constexpr int kNb = 64;               // Cholesky / triangular-inverse block
@@ -59,13 +63,15 @@ struct CollectPlan {
   int64_t* offsets;      // [E+1]
   int64_t* pad_off;      // [slots+1] padded starts of each slot's token list
   int32_t* slot_order;   // [slots] slots sorted by padded length, longest first
-  int32_t* work;         // [kXcds][kMaxSegs*items] Gram-sum items (segment*1024 + item) per XCD
+  int32_t* work;         // [kXcds][max_segs*items] Gram-sum items (segment*1024 + item) per XCD
   int32_t* work_len;     // [kXcds] items per XCD
   int32_t* work_next;    // [kXcds] queue heads (reset by the bucketing scan)
-  int32_t* seg;          // [kMaxSegs][4] slot, destination (-1: S, else partial buffer),
+  int32_t* seg;          // [max_segs][4] slot, destination (-1: S, else partial buffer),
                          //   first token and token count within the slot's padded list
-  int32_t* split;        // [1 + 3*kMaxPartials] count, then (slot, first partial, partials)
-  float* partials;       // [kMaxPartials][d][d] partial sums of token-split slots
+  int32_t* split;        // [1 + 3*max_partials] count, then (slot, first partial, partials)
+  float* partials;       // [max_partials][d][d] partial sums of token-split slots
+  int max_partials;      // partial buffers in the workspace
+  int max_segs;          // slots + max_partials
   int syrk_items;        // Gram-sum items per segment
   int overwrite;         // first collection after a reset: S and counts are stored, not added
   int32_t* token_ids;    // [n*K]

@@ -123,22 +123,27 @@ __global__ __launch_bounds__(256) void bucket_count_kernel(const int32_t* __rest
 // padded slot offsets, the longest-first slot order, the layer's running token
 // counts, and the per-XCD Gram-sum work lists.  A segment is a token range of
 // one slot; every item of a segment reads the same activations, so a segment
-// stays on one XCD and its items are consecutive in the list.  Slots far
-// longer than the average XCD share are split into up to 8 token ranges (the
-// parts after the first go to partial buffers, added back in part order
-// afterwards).  Longest slots first, each segment onto the least-loaded XCD.
+// stays on one XCD and its items are consecutive in the list, the diagonal
+// pairs (the longest items) first.  Segments are at most kSegTokens long: the
+// workgroups of a die then start each segment's items together and run them
+// side by side, so the activation panels they all read stay in the die's L2
+// (over a long token range the items would drift apart and each fetch its
+// panels again).  The parts of a slot after its first go to partial buffers,
+// added into S in part order afterwards; when the buffers run short the
+// segments grow.  Longest slots first, each segment onto the least-loaded XCD.
 struct PlanLds {
   int64_t padc[kMaxSlots];
   int32_t order[kMaxSlots];
-  int32_t seg_x[kMaxSegs];      // XCD of each segment
-  int32_t seg_pos[kMaxSegs];    // first list position of its items
+  int32_t seg_x[kMaxSegsCap];   // XCD of each segment
+  int32_t seg_pos[kMaxSegsCap]; // first list position of its items
   int32_t nseg;
 };
 
 __device__ void plan_gram(const int64_t* cnt, PlanLds& L, int slots, int64_t* __restrict__ pad_off,
                           int32_t* __restrict__ slot_order, int64_t* __restrict__ layer_counts, int overwrite,
                           int items, int32_t* __restrict__ work, int32_t* __restrict__ work_len,
-                          int32_t* __restrict__ work_next, int32_t* __restrict__ seg, int32_t* __restrict__ split) {
+                          int32_t* __restrict__ work_next, int32_t* __restrict__ seg, int32_t* __restrict__ split,
+                          int max_partials) {
   for (int e = threadIdx.x; e < slots; e += blockDim.x) {
     L.padc[e] = (cnt[e] + kTokPad - 1) / kTokPad * kTokPad;
     if (layer_counts) layer_counts[e] = overwrite ? cnt[e] : layer_counts[e] + cnt[e];
@@ -163,48 +168,59 @@ __device__ void plan_gram(const int64_t* cnt, PlanLds& L, int slots, int64_t* __
   if (threadIdx.x == 0) {
     int64_t total = 0;
     for (int e = 0; e < slots; ++e) total += L.padc[e];
-    // segment target length in 64-token chunks; the splitting below runs in
-    // 32-bit chunk counts (64-bit division is a long instruction sequence)
-    const int target = (int)((total / (8 * kXcds)) / kTokPad + 1);
-    int64_t load[kXcds];
+    // In 64-token chunks (32-bit counts: 64-bit division is a long instruction
+    // sequence).  The slots, longest first, are laid end to end and cut into
+    // kXcds runs of per_x chunks, one run per die, so every die gets the same
+    // work whatever the load shape; each run is cut further into segments of at
+    // most seg_max chunks (kSegTokens, longer only when the partial buffers
+    // would run short: every segment of a slot after its first takes one).
+    const int total_chunks = (int)(total / kTokPad);
+    const int per_x = (total_chunks + kXcds - 1) / kXcds;
+    const int spare = max_partials > kXcds ? max_partials - (kXcds - 1) : 1;
+    int seg_max = kSegTokens / kTokPad;
+    const int need = (total_chunks + spare - 1) / spare;
+    seg_max = seg_max > need ? seg_max : need;
     int32_t len[kXcds];
-    for (int x = 0; x < kXcds; ++x) {
-      load[x] = 0;
-      len[x] = 0;
-    }
-    int nseg = 0, nsplit = 0, used = 0;
+    for (int x = 0; x < kXcds; ++x) len[x] = 0;
+    int x = 0, xload = 0, nseg = 0, nsplit = 0, used = 0;
     for (int r = 0; r < slots; ++r) {
       const int e = L.order[r];
       const int chunks = (int)(L.padc[e] / kTokPad);
       if (chunks == 0) continue;
-      int k = (chunks + target - 1) / target;
-      k = k < kXcds ? k : kXcds;
-      k = k < 1 + kMaxPartials - used ? k : 1 + kMaxPartials - used;
-      k = k < chunks ? k : chunks;
-      if (k > 1) {
-        split[1 + 3 * nsplit] = e;
-        split[2 + 3 * nsplit] = used;
-        split[3 + 3 * nsplit] = (int32_t)(k - 1);
-        ++nsplit;
-      }
-      const int per = chunks / k, rem = chunks - per * k;
-      int b = 0;
-      for (int j = 0; j < k; ++j) {
-        const int nc = per + (j < rem ? 1 : 0);
+      const int first_part = used;
+      int pos = 0, parts = 0;
+      while (pos < chunks) {
+        if (parts > 0 && used >= max_partials) {
+          // no partial buffer left: the slot's last segment takes the rest
+          seg[4 * (nseg - 1) + 3] += (int32_t)((chunks - pos) * kTokPad);
+          xload += chunks - pos;
+          break;
+        }
+        if (xload >= per_x && x < kXcds - 1) {
+          ++x;
+          xload = 0;
+        }
+        int n = chunks - pos;
+        n = n < seg_max ? n : seg_max;
+        if (x < kXcds - 1 && n > per_x - xload) n = per_x - xload;
         seg[4 * nseg] = e;
-        seg[4 * nseg + 1] = j == 0 ? -1 : used + j - 1;
-        seg[4 * nseg + 2] = (int32_t)(b * kTokPad);
-        seg[4 * nseg + 3] = (int32_t)(nc * kTokPad);
-        int best = 0;
-        for (int x = 1; x < kXcds; ++x) best = load[x] < load[best] ? x : best;
-        L.seg_x[nseg] = best;
-        L.seg_pos[nseg] = len[best];
-        len[best] += items;
-        load[best] += nc;
-        b += nc;
+        seg[4 * nseg + 1] = parts == 0 ? -1 : used++;
+        seg[4 * nseg + 2] = (int32_t)(pos * kTokPad);
+        seg[4 * nseg + 3] = (int32_t)(n * kTokPad);
+        L.seg_x[nseg] = x;
+        L.seg_pos[nseg] = len[x];
+        len[x] += items;
+        xload += n;
+        pos += n;
+        ++parts;
         ++nseg;
       }
-      used += (int)k - 1;
+      if (parts > 1) {
+        split[1 + 3 * nsplit] = e;
+        split[2 + 3 * nsplit] = first_part;
+        split[3 + 3 * nsplit] = parts - 1;
+        ++nsplit;
+      }
     }
     split[0] = nsplit;
     L.nseg = nseg;
@@ -214,7 +230,7 @@ __device__ void plan_gram(const int64_t* cnt, PlanLds& L, int slots, int64_t* __
     }
   }
   __syncthreads();
-  const int cap = kMaxSegs * items;
+  const int cap = (slots + max_partials) * items;
   for (int it = threadIdx.x; it < L.nseg * items; it += blockDim.x) {
     const int sg = it / items, t = it - sg * items;
     work[L.seg_x[sg] * cap + L.seg_pos[sg] + t] = sg * 1024 + t;
@@ -229,7 +245,7 @@ __global__ __launch_bounds__(256) void bucket_scan_kernel(
     int32_t* __restrict__ blockbase, int64_t* __restrict__ offsets, int64_t* __restrict__ pad_off,
     int32_t* __restrict__ slot_order, int64_t* __restrict__ layer_counts, int overwrite, int items,
     int32_t* __restrict__ work, int32_t* __restrict__ work_len, int32_t* __restrict__ work_next,
-    int32_t* __restrict__ seg, int32_t* __restrict__ split) {
+    int32_t* __restrict__ seg, int32_t* __restrict__ split, int max_partials) {
   __shared__ int64_t cnt[kMaxSlots];
   __shared__ PlanLds L;
   const int slots = E + has_shared;
@@ -262,7 +278,7 @@ __global__ __launch_bounds__(256) void bucket_scan_kernel(
     offsets[E] = o;
   }
   plan_gram(cnt, L, slots, pad_off, slot_order, layer_counts, overwrite, items, work, work_len, work_next, seg,
-            split);
+            split, max_partials);
 }
 
 // Plan of the down_proj inputs of one layer: slot e < E takes expert e's routed
@@ -273,14 +289,14 @@ __global__ __launch_bounds__(256) void down_scan_kernel(
     const int64_t* __restrict__ routed_offsets, int64_t n, int E, int slots, int64_t* __restrict__ pad_off,
     int32_t* __restrict__ slot_order, int64_t* __restrict__ layer_counts, int overwrite, int items,
     int32_t* __restrict__ work, int32_t* __restrict__ work_len, int32_t* __restrict__ work_next,
-    int32_t* __restrict__ seg, int32_t* __restrict__ split, int32_t* __restrict__ tile_off) {
+    int32_t* __restrict__ seg, int32_t* __restrict__ split, int32_t* __restrict__ tile_off, int max_partials) {
   __shared__ int64_t cnt[kMaxSlots];
   __shared__ PlanLds L;
   for (int e = threadIdx.x; e < slots; e += 256)
     cnt[e] = e < E ? routed_offsets[e + 1] - routed_offsets[e] : n;
   __syncthreads();
   plan_gram(cnt, L, slots, pad_off, slot_order, layer_counts, overwrite, items, work, work_len, work_next, seg,
-            split);
+            split, max_partials);
   if (threadIdx.x == 0) {
     int32_t t = 0;
     for (int e = 0; e < slots; ++e) {
@@ -295,7 +311,7 @@ void launch_down_scan(const int64_t* routed_offsets, int64_t n, int E, const Col
                       int64_t* layer_counts, int32_t* tile_off, hipStream_t s) {
   hipLaunchKernelGGL(down_scan_kernel, dim3(1), dim3(256), 0, s, routed_offsets, n, E, p.E, p.pad_off,
                      p.slot_order, layer_counts, p.overwrite, p.syrk_items, p.work, p.work_len, p.work_next,
-                     p.seg, p.split, tile_off);
+                     p.seg, p.split, tile_off, p.max_partials);
 }
 
 __global__ __launch_bounds__(256) void bucket_scatter_kernel(
@@ -343,7 +359,7 @@ void launch_bucket(const CollectPlan& p, int64_t* layer_counts, hipStream_t s) {
   hipLaunchKernelGGL(bucket_scan_kernel, dim3(1), dim3(256), 0, s, p.blockcounts, p.nblk,
                      p.n_tokens, p.E, p.has_shared, p.blockbase, p.offsets, p.pad_off,
                      p.slot_order, layer_counts, p.overwrite, p.syrk_items, p.work, p.work_len, p.work_next,
-                     p.seg, p.split);
+                     p.seg, p.split, p.max_partials);
   hipLaunchKernelGGL(bucket_scatter_kernel, dim3(p.nblk), dim3(256), 0, s, p.topk, p.n_tokens,
                      p.K, p.E, p.blockbase, p.offsets, p.token_ids);
 }
@@ -438,4 +454,17 @@ void launch_gather(const uint16_t* x, const CollectPlan& p, hipStream_t s) {
                      p.xgT);
 }
 
+}  // namespace clha
+
+namespace clha {
+int max_partials(int d, int64_t max_tokens, int top_k, int slots) {
+  // segments past each slot's first: at most rows / kSegTokens from the length
+  // cap, plus one at each boundary between two dies' runs
+  const int64_t rows = max_tokens * (top_k + 1) + (int64_t)kTokPad * slots;
+  int64_t need = rows / kSegTokens + kXcds;
+  const int64_t fit = ((int64_t)4 << 30) / ((int64_t)4 * d * d);
+  need = need < fit ? need : fit;
+  need = need < kMaxPartialsCap ? need : kMaxPartialsCap;
+  return (int)(need > 8 ? need : 8);
+}
 }  // namespace clha

@@ -12,16 +12,19 @@
 // pairs (p, nt-1-p): a diagonal tile's lower triangle is 36 of 64 32x32 blocks,
 // a pair is 72 blocks, 9 per wave, so every item is about one tile of work
 // (d = 2048: 28 + 4 = 32 items per slot, one per CU of an XCD).
-// The bucketing scan deals segments (token ranges of one slot) to per-XCD
-// lists, a segment's items consecutive, the diagonal pairs first.  Persistent
-// workgroups pull items from their die's list; since a segment's items take
-// about equally long, the 32 workgroups of a die run one segment's items side
-// by side and read its activations through one L2.  Every element of S is
+// The bucketing scan deals segments (token ranges of one slot, at most
+// kSegTokens = one flush interval long) to per-XCD lists, a segment's items
+// consecutive, the diagonal pairs first.  Persistent workgroups pull items
+// from their die's list, so the 32 workgroups of a die start a segment's items
+// together, run them side by side and read its activations through one L2;
+// short segments keep them from drifting apart (a diagonal pair takes 9/8 of
+// an off-diagonal tile's time, which over a long token range would leave the
+// pairs reading panels the die's L2 no longer holds).  Every element of S is
 // summed in a fixed order whichever workgroup takes the item, so results are
 // bit-identical run to run.  The running sum is added into S every
 // kFlushSteps token steps (two-level summation keeps the fp32 error
-// independent of the expert's size); for the later token ranges of a split
-// slot it goes to a partial buffer, added into S in part order afterwards.
+// independent of the expert's size); for the later segments of a slot it goes
+// to a partial buffer, added into S in part order afterwards.
 //
 // Tile pipeline: 512 threads = 8 waves.  Tokens advance 32 at a time through
 // four LDS stages filled by direct global-to-LDS loads (global_load_lds_dwordx4)
@@ -370,7 +373,7 @@ void launch_syrk(const CollectPlan& p, float* S, const int64_t* layer_counts, hi
     hipLaunchKernelGGL(zero_empty_slots_kernel, dim3(p.E + p.has_shared), dim3(256), 0, s, layer_counts, S,
                        p.d);
   hipLaunchKernelGGL(syrk_kernel, dim3(kXcds * kSyrkWgPerXcd), dim3(512), 0, s, p.xgT, p.pad_off, p.work,
-                     p.work_len, p.work_next, p.seg, kMaxSegs * p.syrk_items, p.d, S, p.partials,
+                     p.work_len, p.work_next, p.seg, p.max_segs * p.syrk_items, p.d, S, p.partials,
                      p.overwrite);
   hipLaunchKernelGGL(syrk_reduce_kernel, dim3((p.d + 1023) / 1024, p.d), dim3(256), 0, s, p.split,
                      p.partials, S, p.d);
