@@ -61,6 +61,9 @@ def parse():
                     help="write the options step's trace summary and bench line under profiles/ and exit")
     ap.add_argument("--summarize-down-profile", nargs=2, metavar=("DIR", "BENCH_JSON"),
                     help="write the down_proj profile summaries from DIR and the bench output file, and exit")
+    ap.add_argument("--experiment", choices=("drift", "sharpness"),
+                    help="run a section-4 experiment on the drift-stress shapes and write its table")
+    ap.add_argument("--out", help="JSON file of the experiment table (default under profiles/)")
     return ap.parse_args()
 
 
@@ -352,6 +355,74 @@ def summarize_profiles(d, wid):
     print(json.dumps(rec))
 
 
+EXPERIMENT_TAUS = (0.01, 0.03, 0.1, 0.3, 1.0, 3.0, 10.0)
+
+
+def experiment(args):
+    """The CLHA summary's section-4 experiments on the drift-stress shapes (d 4096,
+    128 routed experts top-8, 262,144 tokens per layer, 2048x4096 bf16 weights,
+    2-bit, group 64), every expert quantized under PLIC, CLHA-rt and CLHA-eq:
+      drift      layer b's activations (1 - t) x_a + t z for t in 0, .25, .5, .75, 1,
+                 router logits x R of each layer's own activations;
+      sharpness  the activations at t = 0.5 with sampled routing, logits
+                 x R / tau + Gumbel noise per layer, over a range of tau.
+    Each row: routing divergence (JSD of the expert loads, top-K overlap) and, per
+    weighting, the summed loss over the experts under the combined Hessian and
+    under each layer's own (the calibration-Hessian error).  Writes one JSON file."""
+    import numpy as np
+    import torch
+    import gen
+    import gptq_calibration_moe_amd as clha
+    from gptq_calibration_moe_amd.sweep import drift_sweep, sharpness_sweep
+
+    wl = gen.WORKLOADS[5]
+    dev = torch.device("cuda", 0)
+
+    def bits_dev(b):
+        return torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    ctx = clha.Context(wl.d, wl.n_routed, wl.top_k, 0, max_tokens=wl.n_tokens, device=dev)
+    weights = {e: bits_dev(w) for e, w in gen.all_expert_weights(wl, 0, range(wl.n_routed)).items()}
+    t0 = time.perf_counter()
+    if args.experiment == "drift":
+        def inputs_for(t):
+            inp = gen.pair_inputs(wl, 0, t=t)
+            log(f"drift t={t}: inputs after {time.perf_counter() - t0:.1f} s")
+            return (bits_dev(inp["x"][0]), bits_dev(inp["x"][1]),
+                    torch.from_numpy(inp["logits"][0]).to(dev), torch.from_numpy(inp["logits"][1]).to(dev))
+        rows = drift_sweep(ctx, inputs_for, wl.drift, weights, wl.bits, wl.group, wl.block, wl.damp)
+        what = "drift t"
+    else:
+        xa, xb = gen.activations(wl, 0, t=0.5)
+        rk = wl.scaled(logit_kind="router")
+        base = [gen.router_logits(rk, 0, 0, xa), gen.router_logits(rk, 0, 1, xb)]
+        x = [bits_dev(xa), bits_dev(xb)]
+
+        def logits_for(tau):
+            log(f"sharpness tau={tau}: logits after {time.perf_counter() - t0:.1f} s")
+            return [torch.from_numpy(gen.sharpness_logits(wl, 0, l, (xa, xb)[l], tau, base=base[l])).to(dev)
+                    for l in range(2)]
+        rows = sharpness_sweep(ctx, x, logits_for, EXPERIMENT_TAUS, weights, wl.bits, wl.group, wl.block,
+                               wl.damp)
+        what = "router temperature tau"
+    cmd = f"python3 bench.py --experiment {args.experiment}"
+    table = {"experiment": args.experiment, "command": cmd, "varied": what,
+             "workload": {"name": wl.name, "d": wl.d, "routed_experts": wl.n_routed, "top_k": wl.top_k,
+                          "tokens_per_layer": wl.n_tokens, "matrix_shape": [wl.rows, wl.d], "bits": wl.bits,
+                          "group": wl.group, "damp": wl.damp,
+                          "activations": "x_a ~ N(0,1); x_b = (1 - t) x_a + t z",
+                          "logits": ("x R per layer" if args.experiment == "drift"
+                                     else "x R / tau + Gumbel(0,1) per layer, t = 0.5")},
+             "losses": "sums over the experts of tr[(Wq - W) H (Wq - W)^T]: comb = the weighting's own "
+                       "H_comb, a / b = layer a's / b's Hessian",
+             "rows": rows}
+    out = args.out or os.path.join(ROOT, "profiles", f"experiment_{args.experiment}.json")
+    json.dump(table, open(out, "w"), indent=1)
+    log(f"wrote {out} after {time.perf_counter() - t0:.1f} s")
+    print(json.dumps({"experiment": args.experiment, "rows": len(rows), "out": out}), flush=True)
+    return 0
+
+
 def down_proj_bench(args):
     """The down_proj calibration step of the mid-MoE block (see the module docstring)."""
     import numpy as np
@@ -446,6 +517,8 @@ def main():
         return 2
     if args.down_proj:
         return down_proj_bench(args)
+    if args.experiment:
+        return experiment(args)
     return calibration_bench(args)
 
 

@@ -5,8 +5,9 @@ Both layers see the same activations; routing is sampled (Gumbel top-K of
 x R / tau), so tau sets how far the layers' routing diverges.  Checked: the
 divergence measures from the GPU's routing equal the oracle's (routing is
 bit-exact); at a tiny tau routing agrees in both layers, so CLHA-rt and -eq
-equal PLIC bit for bit; at a large tau the overlap falls toward K/E; the losses
-of CLHA-rt under each layer's Hessian against the oracle.
+equal PLIC bit for bit; at a large tau the overlap falls toward K/E; there the
+losses of PLIC, CLHA-rt and CLHA-eq under each layer's Hessian against the
+oracle.
 """
 import numpy as np
 import pytest
@@ -50,16 +51,23 @@ def test_sharpness_sweep():
     for tag in ("a", "b"):
         assert sharp[f"loss_rt_{tag}"] == sharp[f"loss_plic_{tag}"] == sharp[f"loss_eq_{tag}"]
     assert flat["topk_overlap"] < 0.5 and flat["load_divergence"] >= 0.0
-    # CLHA-rt at the large tau against the oracle, under each layer's own Hessian
+    # PLIC, CLHA-rt and CLHA-eq at the large tau against the oracle, each result
+    # under each layer's own Hessian
     tk = [oracle.route(logits[1e3][l], wl.top_k) for l in range(2)]
     S = [oracle.layer_hessians(xa, tk[l], wl.n_routed, 0) for l in range(2)]
-    for tag, l in (("a", 0), ("b", 1)):
-        want = 0.0
-        for e in experts:
-            H_rt, _ = oracle.aggregate([S[0][0][e], S[1][0][e]], [int(S[0][1][e]), int(S[1][1][e])], "rt")
-            H_l, _ = oracle.aggregate([S[l][0][e]], [int(S[l][1][e])], "rt")
-            wv = gen.weights_value(wl, w_host[e]).astype(np.float64)
-            ref = oracle.gptq(wv, H_rt, wl.bits, wl.group, 0.01, 128)
-            want += oracle.loss(wv, ref["wq"], H_l)
-        got = flat[f"loss_rt_{tag}"]
-        assert abs(got - want) <= LOSS_RTOL * abs(want), f"rt under H_{tag}: {got} vs {want}"
+    for name in ("plic", "rt", "eq"):
+        for tag, l in (("a", 0), ("b", 1)):
+            want = 0.0
+            for e in experts:
+                Se = [S[0][0][e], S[1][0][e]]
+                ne = [int(S[0][1][e]), int(S[1][1][e])]
+                if name == "plic":
+                    H_c, _ = oracle.aggregate(Se, ne, "explicit", alpha=[1.0, 0.0])
+                else:
+                    H_c, _ = oracle.aggregate(Se, ne, name)
+                H_l, _ = oracle.aggregate([Se[l]], [ne[l]], "rt")
+                wv = gen.weights_value(wl, w_host[e]).astype(np.float64)
+                ref = oracle.gptq(wv, H_c, wl.bits, wl.group, 0.01, 128)
+                want += oracle.loss(wv, ref["wq"], H_l)
+            got = flat[f"loss_{name}_{tag}"]
+            assert abs(got - want) <= LOSS_RTOL * abs(want), f"{name} under H_{tag}: {got} vs {want}"
