@@ -35,7 +35,7 @@ EXPORTS = (
     "clha_gptq_quantize_ex", "clha_inverse_cholesky_workspace_bytes",
     "clha_inverse_cholesky", "clha_loss_workspace_bytes", "clha_loss", "clha_set_timing",
     "clha_read_timing", "clha_sync", "clha_pack_codes", "clha_unpack_codes",
-    "clha_down_workspace_bytes", "clha_collect_down_hessians",
+    "clha_down_workspace_bytes", "clha_collect_down_hessians", "clha_loss_static",
 )
 STAGES = ("route", "bucket", "gather", "syrk", "aggregate", "factor", "gptq", "loss")
 
@@ -88,6 +88,7 @@ def _load() -> C.CDLL:
         "clha_inverse_cholesky": ([vp, i32, C.POINTER(vp), i32, f32, vp, vp, vp, vp, sz, vp], i32),
         "clha_loss_workspace_bytes": ([vp, i32, i32], sz),
         "clha_loss": ([vp, i32, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp], i32),
+        "clha_loss_static": ([vp, i32, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp], i32),
         "clha_set_timing": ([vp, i32], i32),
         "clha_read_timing": ([vp, C.POINTER(C.c_double), C.POINTER(i64), i32], i32),
         "clha_sync": ([vp, vp], i32),
@@ -415,6 +416,22 @@ class Context:
                                   BF16 if W.dtype == torch.bfloat16 else F32, _ptr(codes),
                                   _ptr(scales), _ptr(zeros), _ptr(H), _ptr(loss_out), _ptr(ws),
                                   ws.numel(), _stream(stream)))
+
+    def loss_static(self, W: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor,
+                    H: torch.Tensor, group: int, loss_out: torch.Tensor, stream=None):
+        """clha_loss_static: the loss of `loss` with the library's static scratch (no workspace,
+        no allocation)."""
+        rows, cols = W.shape
+        _check_dev("W", W, (torch.float32, torch.bfloat16), (rows, cols), self.device)
+        _check_dev("codes", codes, torch.uint8, (rows, cols), self.device)
+        _check_dev("scales", scales, torch.float32, (rows, cols // group), self.device)
+        _check_dev("zeros", zeros, torch.uint8, (rows, cols // group), self.device)
+        _check_dev("H", H, torch.float32, (cols, cols), self.device)
+        _check_dev("loss_out", loss_out, torch.float32, None, self.device)
+        self._raise(lib.clha_loss_static(self._h, rows, cols, group, _ptr(W),
+                                         BF16 if W.dtype == torch.bfloat16 else F32, _ptr(codes),
+                                         _ptr(scales), _ptr(zeros), _ptr(H), _ptr(loss_out),
+                                         _stream(stream)))
 
     def set_timing(self, enable: bool):
         self._raise(lib.clha_set_timing(self._h, 1 if enable else 0))

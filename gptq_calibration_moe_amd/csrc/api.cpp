@@ -362,7 +362,7 @@ CLHA_API clha_status clha_create(const clha_moe_desc* desc, clha_ctx** out) {
   if (!ctx) return CLHA_ERR_INVALID_ARG;
   ctx->desc = d;
   ctx->slots = d.n_routed + (d.n_shared > 0 ? 1 : 0);
-  if (hipGetDevice(&ctx->device) != hipSuccess ||
+  if (hipGetDevice(&ctx->device) != hipSuccess || !clha::loss_scratch_init(ctx->device) ||
       !(ctx->status_dev = clha::status_acquire(ctx->device, &ctx->status_slot)) ||
       hipEventCreateWithFlags(&ctx->pinned_done, hipEventDisableTiming) != hipSuccess) {
     if (ctx->status_dev) clha::status_release(ctx->device, ctx->status_slot);
@@ -896,6 +896,35 @@ CLHA_API clha_status clha_loss(clha_ctx* ctx, int32_t rows, int32_t cols, int32_
                       static_cast<float*>(workspace), loss_out, as_stream(stream));
   }
   return hip_check(ctx, "loss");
+}
+
+CLHA_API clha_status clha_loss_static(clha_ctx* ctx, int32_t rows, int32_t cols, int32_t group,
+                                      const void* W, int32_t w_dtype, const uint8_t* codes,
+                                      const float* scales, const uint8_t* zeros, const float* H,
+                                      float* loss_out, void* stream) {
+  if (!ctx) return CLHA_ERR_INVALID_ARG;
+  if (rows < 1 || cols < 64 || cols > 8192 || cols % 64 != 0 || group < 1 || cols % group != 0)
+    return fail(ctx, CLHA_ERR_SHAPE, "loss_static: bad shape");
+  if (!W || !codes || !scales || !zeros || !H || !loss_out)
+    return fail(ctx, CLHA_ERR_INVALID_ARG, "loss_static: null pointer");
+  if (w_dtype != CLHA_F32 && w_dtype != CLHA_BF16)
+    return fail(ctx, CLHA_ERR_INVALID_ARG, "loss_static: bad dtype");
+  if (!aligned16(W) || !aligned16(H) || !aligned4(scales) || !aligned4(loss_out))
+    return fail(ctx, CLHA_ERR_ALIGN, "loss_static: misaligned pointer");
+  const int64_t parts = clha::loss_partial_count(rows, cols);
+  if (parts > clha::kLossScratchPartials)
+    return fail(ctx, CLHA_ERR_WORKSPACE,
+                "loss_static: %lld tile partials (rows %d, cols %d) exceed the static scratch of %lld "
+                "(rows/64 rounded up times cols/64); use clha_loss with a workspace",
+                (long long)parts, rows, cols, (long long)clha::kLossScratchPartials);
+  double* scratch_ptr = clha::loss_scratch(ctx->device);
+  if (!scratch_ptr) return fail(ctx, CLHA_ERR_HIP, "loss_static: no scratch address for device %d", ctx->device);
+  {
+    StageTimer t(ctx, CLHA_STAGE_LOSS, as_stream(stream));
+    clha::launch_loss(rows, cols, group, W, w_dtype, codes, scales, zeros, H, nullptr,
+                      reinterpret_cast<float*>(scratch_ptr), loss_out, as_stream(stream));
+  }
+  return hip_check(ctx, "loss_static");
 }
 
 CLHA_API clha_status clha_set_timing(clha_ctx* ctx, int32_t enable) {

@@ -178,6 +178,11 @@ void launch_loss(int rows, int cols, int group, const void* W, int dtype, const 
                  const float* scales, const uint8_t* zeros, const float* H, const int* gidx,
                  float* partials, float* loss_out, hipStream_t s);
 int64_t loss_partial_count(int rows, int cols);
+// The allocation-free loss entry point's scratch: kLossScratchPartials fp64
+// partials (1 MiB) per device, in a file-scope device array of loss.hip.
+constexpr int64_t kLossScratchPartials = 131072;
+bool loss_scratch_init(int device);      // looks the array up on `device` (current); false on failure
+double* loss_scratch(int device);        // its address on `device`, or null before init
 
 // ---------------------------------------------------------------- packed codes
 void launch_pack_codes(const uint8_t* codes, uint8_t* packed, int64_t n_codes, int bits, hipStream_t s);

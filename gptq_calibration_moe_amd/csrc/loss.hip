@@ -11,6 +11,8 @@
 // a second kernel adds the partials in a fixed order.
 #include "kernels.h"
 
+#include <mutex>
+
 namespace clha {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -80,6 +82,35 @@ __global__ void loss_finish_kernel(const double* __restrict__ partials, int64_t 
 
 int64_t loss_partial_count(int rows, int cols) {
   return (int64_t)(cols / 64) * ((rows + 63) / 64);
+}
+
+// Scratch of the allocation-free loss entry point: the fp64 tile partials live
+// in this file-scope device array instead of a caller workspace.  Each device
+// holds its own copy; its address is looked up once per device (with that
+// device current) by loss_scratch_init, and only that address is ever passed to
+// kernels: in host code the array's name is not a device address.
+static __device__ __align__(256) double scratch[kLossScratchPartials];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mutex;
+double* g_scratch[kMaxScratchDevices] = {};
+}  // namespace
+
+bool loss_scratch_init(int device) {
+  if (device < 0 || device >= kMaxScratchDevices) return false;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch[device]) return true;
+  void* ptr = nullptr;
+  if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return false;
+  g_scratch[device] = static_cast<double*>(ptr);
+  return true;
+}
+
+double* loss_scratch(int device) {
+  if (device < 0 || device >= kMaxScratchDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  return g_scratch[device];
 }
 
 void launch_loss(int rows, int cols, int group, const void* W, int dtype, const uint8_t* codes,

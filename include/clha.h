@@ -292,6 +292,21 @@ CLHA_API clha_status clha_loss(clha_ctx* ctx, int32_t rows, int32_t cols, int32_
                                float* loss_out, void* workspace, size_t workspace_bytes,
                                void* stream);
 
+/* clha_loss for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation): the same loss, computed by the same
+ * kernels, with the tile partials in a static scratch array of the library (1 MiB per device,
+ * held until the process ends) instead of a workspace.  The call allocates nothing.
+ *   sizes: ceil(rows/64) * (cols/64) must be at most 131072 (e.g. rows <= 65536 at
+ *          cols 8192), else CLHA_ERR_WORKSPACE is returned and nothing is enqueued
+ *   Every call on one device shares that device's scratch: calls that overlap on one
+ *   device (e.g. on two streams) race; calls ordered on one stream do not.  The scratch
+ *   needs no clearing: every partial is written before it is read.
+ * Errors: as clha_loss, with WORKSPACE for sizes beyond the scratch. */
+CLHA_API clha_status clha_loss_static(clha_ctx* ctx, int32_t rows, int32_t cols, int32_t group,
+                                      const void* W, int32_t w_dtype, const uint8_t* codes,
+                                      const float* scales, const uint8_t* zeros, const float* H,
+                                      float* loss_out, void* stream);
+
 /* Inputs of the experts' second matrix (down_proj).  Section 2.2 collects the Hessian
  * of every shared weight over that weight's own input; the input of an expert's
  * down_proj is its SwiGLU intermediate
