@@ -37,7 +37,7 @@ EXPORTS = (
     "clha_read_timing", "clha_sync", "clha_pack_codes", "clha_unpack_codes",
     "clha_down_workspace_bytes", "clha_collect_down_hessians", "clha_loss_static",
 )
-STAGES = ("route", "bucket", "gather", "syrk", "aggregate", "factor", "gptq", "loss")
+STAGES = ("route", "bucket", "gather", "syrk", "aggregate", "factor", "gptq", "loss", "syrk_reduce")
 
 
 class ClhaError(RuntimeError):

@@ -170,6 +170,7 @@ struct CollectLayout {
   int32_t* topk;
   int32_t* blockcounts;
   int32_t* blockbase;
+  int32_t* tilebase;
   int64_t* offsets;
   int64_t* pad_off;
   int32_t* slot_order;
@@ -196,6 +197,7 @@ CollectLayout collect_layout(const clha_ctx* ctx, void* ws) {
   L.topk = c.take<int32_t>((size_t)n * d.top_k);
   L.blockcounts = c.take<int32_t>((size_t)nblk * d.n_routed);
   L.blockbase = c.take<int32_t>((size_t)nblk * d.n_routed);
+  L.tilebase = c.take<int32_t>((size_t)((n + clha::kGatherTok - 1) / clha::kGatherTok) * d.n_routed);
   L.offsets = c.take<int64_t>((size_t)d.n_routed + 1);
   L.pad_off = c.take<int64_t>((size_t)ctx->slots + 1);
   L.slot_order = c.take<int32_t>((size_t)ctx->slots);
@@ -483,6 +485,8 @@ CLHA_API clha_status clha_collect_hessians(clha_ctx* ctx, int32_t layer, int64_t
   p.topk = topk_out ? topk_out : L.topk;
   p.blockcounts = L.blockcounts;
   p.blockbase = L.blockbase;
+  p.tilebase = L.tilebase;
+  p.ntile = (int)((n_tokens + clha::kGatherTok - 1) / clha::kGatherTok);
   p.offsets = offsets_out ? offsets_out : L.offsets;
   p.pad_off = L.pad_off;
   p.slot_order = L.slot_order;
@@ -498,8 +502,6 @@ CLHA_API clha_status clha_collect_hessians(clha_ctx* ctx, int32_t layer, int64_t
   p.overwrite = it->second.fresh ? 1 : 0;
   p.token_ids = token_ids_out ? token_ids_out : L.token_ids;
   p.xgT = L.xgT;
-  p.xg_tiles = (n_tokens * d.top_k + clha::kTokPad - 1) / clha::kTokPad + d.n_routed +
-               (p.has_shared ? (n_tokens + clha::kTokPad - 1) / clha::kTokPad : 0);
   p.status = ctx->status_dev;
   p.layer = layer;
   const hipStream_t s = as_stream(stream);
@@ -517,7 +519,11 @@ CLHA_API clha_status clha_collect_hessians(clha_ctx* ctx, int32_t layer, int64_t
   }
   {
     StageTimer t(ctx, CLHA_STAGE_SYRK, s);
-    clha::launch_syrk(p, it->second.S, it->second.counts, s);
+    clha::launch_syrk(p, it->second.S, s);
+  }
+  {
+    StageTimer t(ctx, CLHA_STAGE_SYRK_REDUCE, s);
+    clha::launch_syrk_reduce(p, it->second.S, it->second.counts, s);
   }
   it->second.fresh = false;
   return hip_check(ctx, "collect_hessians");
@@ -1091,7 +1097,11 @@ CLHA_API clha_status clha_collect_down_hessians(clha_ctx* ctx, int32_t layer, in
   }
   {
     StageTimer t(ctx, CLHA_STAGE_SYRK, s);
-    clha::launch_syrk(p, it->second.S, it->second.counts, s);
+    clha::launch_syrk(p, it->second.S, s);
+  }
+  {
+    StageTimer t(ctx, CLHA_STAGE_SYRK_REDUCE, s);
+    clha::launch_syrk_reduce(p, it->second.S, it->second.counts, s);
   }
   it->second.fresh = false;
   return hip_check(ctx, "collect_down_hessians");

@@ -354,13 +354,23 @@ __global__ __launch_bounds__(256) void syrk_reduce_kernel(const int32_t* __restr
     const int slot = split[1 + 3 * sp], p0 = split[2 + 3 * sp], np = split[3 + 3 * sp];
     float* o = S + (int64_t)slot * dd + off;
     float4 v = *reinterpret_cast<const float4*>(o);
-    for (int k = 0; k < np; ++k) {
-      const float4 w = *reinterpret_cast<const float4*>(partials + (int64_t)(p0 + k) * dd + off);
+    const float* pp = partials + (int64_t)p0 * dd + off;
+    auto add = [&](const float4& w) {
       v.x += w.x;
       v.y += w.y;
       v.z += w.z;
       v.w += w.w;
+    };
+    // four parts' loads in flight together; the sums stay in part order
+    int k = 0;
+    for (; k + 4 <= np; k += 4) {
+      float4 w[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) w[u] = *reinterpret_cast<const float4*>(pp + (int64_t)(k + u) * dd);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) add(w[u]);
     }
+    for (; k < np; ++k) add(*reinterpret_cast<const float4*>(pp + (int64_t)k * dd));
     // columns above the diagonal keep their value (S's upper triangle is never written)
     if (j + 1 > i) v.y = o[1];
     if (j + 2 > i) v.z = o[2];
@@ -388,15 +398,20 @@ __global__ __launch_bounds__(256) void zero_empty_slots_kernel(const int64_t* __
     }
 }
 
-void launch_syrk(const CollectPlan& p, float* S, const int64_t* layer_counts, hipStream_t s) {
-  if (p.overwrite)
-    hipLaunchKernelGGL(zero_empty_slots_kernel, dim3(p.E + p.has_shared), dim3(256), 0, s, layer_counts, S,
-                       p.d);
+void launch_syrk(const CollectPlan& p, float* S, hipStream_t s) {
   hipLaunchKernelGGL(syrk_kernel, dim3(kXcds * kSyrkWgPerXcd), dim3(512), 0, s, p.xgT, p.pad_off, p.work,
                      p.work_len, p.work_next, p.seg, p.max_segs * p.syrk_items, p.d, S, p.partials,
                      p.overwrite);
+}
+
+// After the Gram-sum kernel.  The slots zeroed here received no token, so no
+// Gram-sum item or partial buffer touches them.
+void launch_syrk_reduce(const CollectPlan& p, float* S, const int64_t* layer_counts, hipStream_t s) {
   hipLaunchKernelGGL(syrk_reduce_kernel, dim3((p.d + 1023) / 1024, p.d), dim3(256), 0, s, p.split,
                      p.partials, S, p.d);
+  if (p.overwrite)
+    hipLaunchKernelGGL(zero_empty_slots_kernel, dim3(p.E + p.has_shared), dim3(256), 0, s, layer_counts, S,
+                       p.d);
 }
 
 int syrk_items_per_slot(int d) {

@@ -365,7 +365,8 @@ typedef enum clha_stage {
   CLHA_STAGE_FACTOR = 5,     /* damping, Cholesky and triangular inverse (clha_inverse_cholesky) */
   CLHA_STAGE_GPTQ = 6,       /* clha_gptq_quantize: factorisation and GPTQ, which overlap */
   CLHA_STAGE_LOSS = 7,       /* explicit loss kernels */
-  CLHA_NUM_STAGES = 8
+  CLHA_STAGE_SYRK_REDUCE = 8, /* Gram sums: partial sums of token-split slots into S, empty slots zeroed */
+  CLHA_NUM_STAGES = 9
 } clha_stage;
 
 /* Enables (1) or disables (0) per-stage timing: each stage of each later call records a
