@@ -3,7 +3,7 @@
 
 One step calibrates one CLWS pair (two layers that share their routed experts):
   reset the pair's accumulators -> collect layer a -> collect layer b (route,
-  bucket, gather, Gram sums) -> aggregate H_comb -> GPTQ of the pair's expert
+  bucket, Gram sums read straight from x) -> aggregate H_comb -> GPTQ of the pair's expert
   jobs (damping, factor of the inverse, column loop, lazy block updates, loss).
 Inputs are seeded synthetic arrays, every pair's resident in HBM before the
 timed region; steps cycle over the pairs.  Prints one JSON line.
@@ -626,23 +626,18 @@ def calibration_bench(args):
                 "flops_per_launch": flops_per_launch}
     stages_ms = {k: round(v[0] / args.steps, 4) for k, v in stages.items() if v[1]}
 
-    # gather rate on algorithmic bytes (each token read once, each routed row written once)
-    routed_per_step = wl.n_tokens * wl.top_k * 2
-    gather_bytes = 2 * wl.n_tokens * wl.d * 2 + routed_per_step * wl.d * 2
-    gather_gbs = gather_bytes / (stages_ms["gather"] / 1e3) / 1e9 if stages_ms.get("gather") else None
     # end-to-end roofline: each step's algorithmic work at the published peak of its bound
-    # (Gram sums on bf16 MFMA; inverse Cholesky (2/3)d^3 per distinct Hessian and GPTQ
-    # r c (c-1) per matrix on fp32 MFMA; the gather on HBM)
+    # (Gram sums on bf16 MFMA, their operands read straight from x; inverse Cholesky
+    # (2/3)d^3 per distinct Hessian and GPTQ r c (c-1) per matrix on fp32 MFMA)
     n_hess = wl.n_routed + (1 if wl.n_shared else 0)
     rows_total = sum(int(W[0][e].shape[0]) for e in experts)
     terms = {"gram_sums": 2 * flops_per_launch / (PEAK_BF16_TFLOPS * 1e12),
              "inverse_cholesky": n_hess * (2.0 / 3.0) * wl.d ** 3 / (PEAK_FP32_TFLOPS * 1e12),
-             "gptq": rows_total * wl.d * (wl.d - 1) / (PEAK_FP32_TFLOPS * 1e12),
-             "gather": gather_bytes / (PEAK_HBM_GBS * 1e9)}
+             "gptq": rows_total * wl.d * (wl.d - 1) / (PEAK_FP32_TFLOPS * 1e12)}
     t_roof_ms = sum(terms.values()) * 1e3
     end_to_end = {"t_roof_ms": round(t_roof_ms, 3), "frac": round(t_roof_ms / ms_per_step, 4),
                   "terms_ms": {k: round(v * 1e3, 3) for k, v in terms.items()},
-                  "peaks": "bf16 MFMA 2500 TFLOP/s, fp32 MFMA 157.3 TFLOP/s, HBM 8000 GB/s"}
+                  "peaks": "bf16 MFMA 2500 TFLOP/s, fp32 MFMA 157.3 TFLOP/s"}
 
     n_layers = 2 * (wl.n_pairs if not wl.drift else 1)
     config = {"workload": wl.name, "layers": n_layers, "clws_pairs": wl.n_pairs,
@@ -666,8 +661,7 @@ def calibration_bench(args):
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
            "data": "synthetic", "config": config,
-           "roofline": roofline, "stages_ms_per_step": stages_ms,
-           "gather_gbs": round(gather_gbs, 1) if gather_gbs else None, "end_to_end_roofline": end_to_end}
+           "roofline": roofline, "stages_ms_per_step": stages_ms, "end_to_end_roofline": end_to_end}
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(wl, host0[0], host0[1])

@@ -170,7 +170,6 @@ struct CollectLayout {
   int32_t* topk;
   int32_t* blockcounts;
   int32_t* blockbase;
-  int32_t* tilebase;
   int64_t* offsets;
   int64_t* pad_off;
   int32_t* slot_order;
@@ -182,7 +181,8 @@ struct CollectLayout {
   float* partials;
   int max_partials;
   int32_t* token_ids;
-  uint16_t* xgT;
+  int32_t* iota;
+  uint16_t* zero_row;
   size_t bytes;
 };
 
@@ -190,14 +190,11 @@ CollectLayout collect_layout(const clha_ctx* ctx, void* ws) {
   const clha_moe_desc& d = ctx->desc;
   const int64_t n = d.max_tokens;
   const int64_t nblk = (n + clha::kBucketTokens - 1) / clha::kBucketTokens;
-  const int64_t xg_tokens = n * d.top_k + (int64_t)clha::kTokPad * d.n_routed +
-                            (d.n_shared > 0 ? n + clha::kTokPad : 0);
   Carver c(ws);
   CollectLayout L;
   L.topk = c.take<int32_t>((size_t)n * d.top_k);
   L.blockcounts = c.take<int32_t>((size_t)nblk * d.n_routed);
   L.blockbase = c.take<int32_t>((size_t)nblk * d.n_routed);
-  L.tilebase = c.take<int32_t>((size_t)((n + clha::kGatherTok - 1) / clha::kGatherTok) * d.n_routed);
   L.offsets = c.take<int64_t>((size_t)d.n_routed + 1);
   L.pad_off = c.take<int64_t>((size_t)ctx->slots + 1);
   L.slot_order = c.take<int32_t>((size_t)ctx->slots);
@@ -210,7 +207,8 @@ CollectLayout collect_layout(const clha_ctx* ctx, void* ws) {
   L.split = c.take<int32_t>((size_t)1 + 3 * L.max_partials);
   L.partials = c.take<float>((size_t)L.max_partials * d.d * d.d);
   L.token_ids = c.take<int32_t>((size_t)n * d.top_k);
-  L.xgT = c.take<uint16_t>((size_t)xg_tokens * d.d);
+  L.iota = c.take<int32_t>((size_t)n);
+  L.zero_row = c.take<uint16_t>((size_t)d.d);
   L.bytes = c.off;
   return L;
 }
@@ -485,8 +483,6 @@ CLHA_API clha_status clha_collect_hessians(clha_ctx* ctx, int32_t layer, int64_t
   p.topk = topk_out ? topk_out : L.topk;
   p.blockcounts = L.blockcounts;
   p.blockbase = L.blockbase;
-  p.tilebase = L.tilebase;
-  p.ntile = (int)((n_tokens + clha::kGatherTok - 1) / clha::kGatherTok);
   p.offsets = offsets_out ? offsets_out : L.offsets;
   p.pad_off = L.pad_off;
   p.slot_order = L.slot_order;
@@ -501,7 +497,10 @@ CLHA_API clha_status clha_collect_hessians(clha_ctx* ctx, int32_t layer, int64_t
   p.syrk_items = clha::syrk_items_per_slot(d.d);
   p.overwrite = it->second.fresh ? 1 : 0;
   p.token_ids = token_ids_out ? token_ids_out : L.token_ids;
-  p.xgT = L.xgT;
+  p.xgT = nullptr;
+  p.x_rows = x;
+  p.iota = L.iota;
+  p.zero_row = L.zero_row;
   p.status = ctx->status_dev;
   p.layer = layer;
   const hipStream_t s = as_stream(stream);
@@ -512,10 +511,6 @@ CLHA_API clha_status clha_collect_hessians(clha_ctx* ctx, int32_t layer, int64_t
   {
     StageTimer t(ctx, CLHA_STAGE_BUCKET, s);
     clha::launch_bucket(p, it->second.counts, s);
-  }
-  {
-    StageTimer t(ctx, CLHA_STAGE_GATHER, s);
-    clha::launch_gather(x, p, s);
   }
   {
     StageTimer t(ctx, CLHA_STAGE_SYRK, s);

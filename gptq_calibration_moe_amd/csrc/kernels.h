@@ -12,7 +12,6 @@ namespace clha {
 // ---------------------------------------------------------------- constants
 constexpr int kBucketTokens = 1024;   // tokens per bucketing workgroup (16 groups of 64)
 constexpr int kTokPad = 64;           // expert token lists are padded to this multiple
-constexpr int kGatherTok = 256;       // tokens per gather tile (divides kBucketTokens)
 constexpr int kMaxExperts = 256;
 constexpr int kMaxTopK = 16;
 constexpr int kMaxLayers = 8;
@@ -61,8 +60,6 @@ struct CollectPlan {
   int32_t* topk;         // [n][K]
   int32_t* blockcounts;  // [nblk][E]
   int32_t* blockbase;    // [nblk][E]
-  int32_t* tilebase;     // [ntile][E] rank in each expert's list of the first token of gather tile t
-  int ntile;             // gather tiles: ceil(n / kGatherTok)
   int64_t* offsets;      // [E+1]
   int64_t* pad_off;      // [slots+1] padded starts of each slot's token list
   int32_t* slot_order;   // [slots] slots sorted by padded length, longest first
@@ -79,13 +76,17 @@ struct CollectPlan {
   int overwrite;         // first collection after a reset: S and counts are stored, not added
   int32_t* token_ids;    // [n*K]
   uint16_t* xgT;         // gathered activations: per slot, 32-token blocks of [d][32]
+  // Gram sums straight from the activations (non-null): x [n][d], the shared
+  // slot's token list 0 .. n-1 and d zero elements for padding positions
+  const uint16_t* x_rows;
+  int32_t* iota;
+  uint16_t* zero_row;
   int* status;           // the context's status record
   int layer;             // the collected layer (named by a non-finite logit)
 };
 
 void launch_route(const float* logits, const CollectPlan& p, hipStream_t s);
 void launch_bucket(const CollectPlan& p, int64_t* layer_counts, hipStream_t s);
-void launch_gather(const uint16_t* x, const CollectPlan& p, hipStream_t s);
 void launch_syrk(const CollectPlan& p, float* S, hipStream_t s);
 // partial sums of token-split slots into S; with p.overwrite, slots without tokens zeroed
 void launch_syrk_reduce(const CollectPlan& p, float* S, const int64_t* layer_counts, hipStream_t s);

@@ -1,5 +1,5 @@
 // Collection phase, first half: top-K routing, per-expert bucketing and the
-// gather of each expert's rows into a token-blocked, feature-major layout.
+// Gram-sum plan.
 //
 // CLHA summary, section 2.2 (collection): per calibration batch, every layer
 // accumulates a Hessian and a token count for each expert that is active for
@@ -10,31 +10,28 @@
 //   topk        int32 [N][K]        experts of each token, larger logit first
 //   offsets     int64 [E+1]         exclusive prefix sum of per-expert counts
 //   token_ids   int32 [N*K]         tokens of expert e at offsets[e].., ascending
-//   tilebase    int32 [ceil(N/256)][E] rank in expert e's list of the first
-//                                   token of each 256-token gather tile
-//   pad_off     int64 [slots+1]     start of slot e's token columns in xgT,
-//                                   each slot padded to a multiple of 64 tokens;
-//                                   slot E (if the block has shared experts) holds
-//                                   all N tokens in order
-//   xgT         bf16  per slot e, at xgT + pad_off[e]*d: npad_e/32 blocks of
-//                     32 tokens, each block [d][32] (feature-major inside the
-//                     block); element (f, t) at ((t/32)*d + f)*32 + t%32;
-//                     padding tokens are zero
-// Inside a block the Gram sum's contraction index (tokens) is contiguous, which
-// is the operand layout the matrix cores read, and the 32-token step of 256
-// features that one Gram-sum workgroup reads is one contiguous 16 KB run, so
-// every 128-byte line it fetches is used whole in one step.
+//   iota        int32 [N]           0 .. N-1, the shared slot's token list
+//   zero_row    bf16  [d]           zeros, the Gram sums' operand at padding positions
+//   pad_off     int64 [slots+1]     padded start of each slot's positions (each
+//                                   slot padded to a multiple of 64 tokens; slot E,
+//                                   if the block has shared experts, holds all N
+//                                   tokens in order), the Gram-sum segments and the
+//                                   per-XCD work lists
+// The Gram sums read each slot's rows of x straight through its token list.
 #include "kernels.h"
 
 namespace clha {
 
 // ------------------------------------------------------------------ routing
 
+// Also writes iota[t] = t, the shared slot's token list for the Gram sums.
 __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits, int64_t n,
                                                     int E, int K, int32_t* __restrict__ topk,
-                                                    int* __restrict__ status, int layer) {
+                                                    int* __restrict__ status, int layer,
+                                                    int32_t* __restrict__ iota) {
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (t >= n) return;
+  iota[t] = (int32_t)t;
   const float* row = logits + t * E;
   float val[kMaxTopK];
   int idx[kMaxTopK];
@@ -78,7 +75,7 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
 void launch_route(const float* logits, const CollectPlan& p, hipStream_t s) {
   const unsigned grid = (unsigned)((p.n_tokens + 255) / 256);
   hipLaunchKernelGGL(route_kernel, dim3(grid), dim3(256), 0, s, logits, p.n_tokens, p.E, p.K,
-                     p.topk, p.status, p.layer);
+                     p.topk, p.status, p.layer, p.iota);
 }
 
 // ------------------------------------------------------------------ bucketing
@@ -247,10 +244,13 @@ __global__ __launch_bounds__(256) void bucket_scan_kernel(
     int32_t* __restrict__ blockbase, int64_t* __restrict__ offsets, int64_t* __restrict__ pad_off,
     int32_t* __restrict__ slot_order, int64_t* __restrict__ layer_counts, int overwrite, int items,
     int32_t* __restrict__ work, int32_t* __restrict__ work_len, int32_t* __restrict__ work_next,
-    int32_t* __restrict__ seg, int32_t* __restrict__ split, int max_partials) {
+    int32_t* __restrict__ seg, int32_t* __restrict__ split, int max_partials, uint16_t* __restrict__ zero_row,
+    int d) {
   __shared__ int64_t cnt[kMaxSlots];
   __shared__ PlanLds L;
   const int slots = E + has_shared;
+  // the Gram sums' operand for padding positions
+  for (int f = threadIdx.x; f < d; f += 256) zero_row[f] = 0;
   // 16 blocks' counts are loaded together, so a thread waits for memory once
   // per 16 blocks rather than once per block
   constexpr int kScanBatch = 16;
@@ -316,23 +316,16 @@ void launch_down_scan(const int64_t* routed_offsets, int64_t n, int E, const Col
                      p.seg, p.split, tile_off, p.max_partials);
 }
 
-// Also the rank, in each expert's list, of the first token of every gather
-// tile (kGatherTok tokens: every fourth 64-token group) for the gather.
 __global__ __launch_bounds__(256) void bucket_scatter_kernel(
     const int32_t* __restrict__ topk, int64_t n, int K, int E,
     const int32_t* __restrict__ blockbase, const int64_t* __restrict__ offsets,
-    int32_t* __restrict__ token_ids, int32_t* __restrict__ tilebase, int ntile) {
+    int32_t* __restrict__ token_ids) {
   __shared__ unsigned long long mask[16 * kMaxExperts];
   __shared__ int32_t pre[16 * kMaxExperts];
-  constexpr int kGroupsPerTile = kGatherTok / 64;
   build_masks(topk, n, K, E, mask);
   for (int e = threadIdx.x; e < E; e += 256) {
     int run = blockbase[(int64_t)blockIdx.x * E + e];
     for (int g = 0; g < 16; ++g) {
-      if (g % kGroupsPerTile == 0) {
-        const int64_t tl = (int64_t)blockIdx.x * (kBucketTokens / kGatherTok) + g / kGroupsPerTile;
-        if (tl < ntile) tilebase[tl * E + e] = run;
-      }
       pre[g * E + e] = run;
       run += __popcll(mask[g * E + e]);
     }
@@ -368,233 +361,9 @@ void launch_bucket(const CollectPlan& p, int64_t* layer_counts, hipStream_t s) {
   hipLaunchKernelGGL(bucket_scan_kernel, dim3(1), dim3(256), 0, s, p.blockcounts, p.nblk,
                      p.n_tokens, p.E, p.has_shared, p.blockbase, p.offsets, p.pad_off,
                      p.slot_order, layer_counts, p.overwrite, p.syrk_items, p.work, p.work_len, p.work_next,
-                     p.seg, p.split, p.max_partials);
+                     p.seg, p.split, p.max_partials, p.zero_row, p.d);
   hipLaunchKernelGGL(bucket_scatter_kernel, dim3(p.nblk), dim3(256), 0, s, p.topk, p.n_tokens,
-                     p.K, p.E, p.blockbase, p.offsets, p.token_ids, p.tilebase, p.ntile);
-}
-
-// ------------------------------------------------------------------ gather
-// Token-major: each activation row is read from memory once.  A workgroup of
-// 512 threads takes a tile of kGatherTok consecutive tokens and a slice of
-// kGatherFeat features: it reads the slice of the tile's rows (256 B of each
-// row, 16 B per thread) into LDS, then writes that slice of every slot's rows
-// for those tokens.  Expert lists are sorted by token, so a tile's tokens form
-// one run [lo, hi) of each slot's positions; the bucketing gives lo and hi
-// (tilebase), and the shared slot's run is the tile itself.  Output is written
-// in 16-byte chunks, 8 consecutive positions of one feature, and every chunk
-// belongs to exactly one tile: the one holding its first position.  A tile
-// therefore writes the chunks that start in its run; the last of them may
-// reach past the run, and those few positions (at most 7 per slot) are read
-// straight from the activations through their token ids.  The tile that holds
-// a slot's last position also writes the slot's padding chunks as zeros.  A
-// wave takes one 32-token block at a time: lane (q, g) reads the 16-byte
-// pieces (features 8g .. 8g+7) of chunk q's 8 positions, transposes the 8x8
-// block in registers and stores 8 chunks, so each store instruction of the
-// wave writes 16 whole 64-byte feature rows where the block lies inside the
-// run.  Workgroups are dealt to the dies as contiguous runs of tiles taken
-// slice by slice, so the two tiles that share a 64-byte row run on one die at
-// the same time and its halves meet in that die's L2.
-
-__device__ __forceinline__ uint32_t lo_pair(uint32_t a, uint32_t b) {
-  return (a & 0xffffu) | (b << 16);
-}
-__device__ __forceinline__ uint32_t hi_pair(uint32_t a, uint32_t b) {
-  return (a >> 16) | (b & 0xffff0000u);
-}
-
-constexpr int kGatherFeat = 128;                    // features per gather tile
-constexpr int kGatherPitch = 2 * kGatherFeat + 16;  // LDS bytes per token row (16 B of padding)
-constexpr int kGatherThreads = 512;
-constexpr int kHalo = 7;                            // most positions of a chunk past the run
-constexpr uint16_t kFromHalo = 0x8000;              // entry: position past the run (halo index below)
-constexpr uint16_t kZeroPos = 0xffff;               // entry: padding position
-
-template <int SCAP, int KCAP>
-__global__ __launch_bounds__(kGatherThreads) void gather_kernel(
-    const uint16_t* __restrict__ x, int64_t n, int d, int E, int has_shared,
-    const int64_t* __restrict__ offsets, const int64_t* __restrict__ pad_off,
-    const int32_t* __restrict__ token_ids, const int32_t* __restrict__ tilebase, int ntile, int tpx,
-    uint16_t* __restrict__ xgT) {
-  __shared__ __attribute__((aligned(16))) char xt[kGatherTok * kGatherPitch];
-  // per slot: data run [lo, hi), position count, owned chunks [c0, c1), and
-  // exclusive prefixes of the blocks written and of the position entries
-  __shared__ int s_lo[SCAP], s_hi[SCAP], s_cnt[SCAP], s_c0[SCAP], s_c1[SCAP], s_pblk[SCAP + 1],
-      s_ppos[SCAP + 1];
-  __shared__ int s_halo[SCAP * kHalo];   // token ids of the positions hi .. hi + 6 (routed slots)
-  // one entry per position of a routed slot's owned chunks up to hi rounded up
-  // to 8 (at most hi - lo + 14 per slot): the local token index, or a halo
-  // index | kFromHalo, or kZeroPos; slot s's entries start at s_ppos[s] with
-  // position 8 c0, so every chunk's entries are one aligned 16-byte read
-  __shared__ __attribute__((aligned(16))) uint16_t ent[kGatherTok * KCAP + 16 * SCAP];
-  const int slots = E + has_shared;
-  const int xcd = (int)(blockIdx.x % kXcds), j = (int)(blockIdx.x / kXcds);
-  const int slice = j / tpx, tile = xcd * tpx + j % tpx;
-  if (tile >= ntile) return;
-  const int64_t t0 = (int64_t)tile * kGatherTok;
-  const int nt = (int)(n - t0 < kGatherTok ? n - t0 : kGatherTok);
-  const int fbase = slice * kGatherFeat;
-  const int tid = threadIdx.x;
-
-  // the tile's slice: kGatherTok rows x 16 chunks of 16 B
-  constexpr int kLoads = kGatherTok * 16 / kGatherThreads;
-  uint4 v[kLoads];
-#pragma unroll
-  for (int u = 0; u < kLoads; ++u) {
-    const int ch = u * kGatherThreads + tid, r = ch >> 4, c = ch & 15;
-    v[u] = make_uint4(0u, 0u, 0u, 0u);
-    if (r < nt) v[u] = *reinterpret_cast<const uint4*>(x + (t0 + r) * d + fbase + 8 * c);
-  }
-
-  for (int s = tid; s < slots; s += kGatherThreads) {
-    int lo, hi, cnt;
-    if (s < E) {
-      cnt = (int)(offsets[s + 1] - offsets[s]);
-      lo = tilebase[(int64_t)tile * E + s];
-      hi = tile + 1 < ntile ? tilebase[(int64_t)(tile + 1) * E + s] : cnt;
-    } else {
-      cnt = (int)n;
-      lo = (int)t0;
-      hi = (int)t0 + nt;
-    }
-    const int c0 = (lo + 7) >> 3;
-    int c1 = lo < hi ? ((hi - 1) >> 3) + 1 : c0;
-    if (lo < hi && hi == cnt) c1 = (int)((pad_off[s + 1] - pad_off[s]) >> 3);   // the slot's last tile
-    if (c1 < c0) c1 = c0;
-    s_lo[s] = lo;
-    s_hi[s] = hi;
-    s_cnt[s] = cnt;
-    s_c0[s] = c0;
-    s_c1[s] = c1;
-    s_pblk[s] = c0 < c1 ? ((c1 - 1) >> 2) - (c0 >> 2) + 1 : 0;
-    s_ppos[s] = (s < E && c0 < c1 && hi > 8 * c0) ? ((hi + 7) & ~7) - 8 * c0 : 0;
-    if (s < E)
-      for (int u = 0; u < kHalo; ++u)
-        s_halo[s * kHalo + u] = (c0 < c1 && hi + u < cnt && hi + u < 8 * c1) ? token_ids[offsets[s] + hi + u] : 0;
-  }
-  __syncthreads();
-  if (tid < 64) {
-    // exclusive prefix sums over the slots: lane l takes `per` consecutive slots
-    const int per = (slots + 63) / 64, s0 = tid * per;
-    int sb = 0, sp = 0;
-    for (int k = 0; k < per; ++k)
-      if (s0 + k < slots) {
-        sb += s_pblk[s0 + k];
-        sp += s_ppos[s0 + k];
-      }
-    int ib = sb, ip = sp;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int ob = __shfl_up(ib, off), op = __shfl_up(ip, off);
-      if (tid >= off) {
-        ib += ob;
-        ip += op;
-      }
-    }
-    int eb = ib - sb, ep = ip - sp;
-    for (int k = 0; k < per; ++k)
-      if (s0 + k < slots) {
-        const int b = s_pblk[s0 + k], q = s_ppos[s0 + k];
-        s_pblk[s0 + k] = eb;
-        s_ppos[s0 + k] = ep;
-        eb += b;
-        ep += q;
-      }
-    if (tid == 63) {
-      s_pblk[slots] = ib;
-      s_ppos[slots] = ip;
-    }
-  }
-  __syncthreads();
-  // position entries of the routed slots
-  const int ntot = s_ppos[slots];
-  for (int i = tid; i < ntot; i += kGatherThreads) {
-    int a = 0, b = slots;   // s_ppos[a] <= i < s_ppos[b]
-    while (b - a > 1) {
-      const int m = (a + b) >> 1;
-      if (s_ppos[m] <= i) a = m; else b = m;
-    }
-    const int p = 8 * s_c0[a] + (i - s_ppos[a]);
-    uint16_t e = kZeroPos;
-    if (p < s_hi[a]) e = (uint16_t)(token_ids[offsets[a] + p] - t0);
-    else if (p < s_cnt[a]) e = (uint16_t)(kFromHalo | (p - s_hi[a]));
-    ent[i] = e;
-  }
-#pragma unroll
-  for (int u = 0; u < kLoads; ++u) {
-    const int ch = u * kGatherThreads + tid, r = ch >> 4, c = ch & 15;
-    *reinterpret_cast<uint4*>(xt + r * kGatherPitch + 16 * c) = v[u];
-  }
-  __syncthreads();
-
-  // wave w writes blocks w, w + 8, ... of the list (slot-major).  Lane
-  // (q, g) = (lane % 4, lane / 4) takes chunk q of the block for features
-  // 8g .. 8g+7: it reads the 8 positions' 16-byte pieces of those features (from
-  // the LDS tile, or from memory for positions past the run), transposes the
-  // 8x8 block in registers and stores 8 chunks; for each of them the wave
-  // writes 16 feature rows of 64 B.
-  const int lane = tid & 63, wv = tid >> 6;
-  const int q = lane & 3, g = lane >> 2;
-  const int nb = s_pblk[slots];
-  for (int bi = wv; bi < nb; bi += kGatherThreads / 64) {
-    int s = 0, b = slots;   // s_pblk[s] <= bi < s_pblk[b]
-    while (b - s > 1) {
-      const int m = (s + b) >> 1;
-      if (s_pblk[m] <= bi) s = m; else b = m;
-    }
-    const int hi = s_hi[s], c0 = s_c0[s], c1 = s_c1[s];
-    const int blk = (c0 >> 2) + (bi - s_pblk[s]);
-    const int chunk = 4 * blk + q;
-    if (chunk < c0 || chunk >= c1) continue;
-    const int p0 = 8 * chunk;
-    uint4 rv[8];
-    if (s < E) {
-      const int pend = 8 * c0 + (s_ppos[s + 1] - s_ppos[s]);   // entries cover positions [8 c0, pend)
-      uint4 w = make_uint4(0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu);
-      if (p0 < pend) w = *reinterpret_cast<const uint4*>(ent + s_ppos[s] + (p0 - 8 * c0));
-      const int* halo = s_halo + s * kHalo;
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const uint32_t e = ((&w.x)[u >> 1] >> (16 * (u & 1))) & 0xffffu;
-        rv[u] = make_uint4(0u, 0u, 0u, 0u);
-        if (e < kFromHalo)
-          rv[u] = *reinterpret_cast<const uint4*>(xt + e * kGatherPitch + 16 * g);
-        else if (e != kZeroPos)
-          rv[u] = *reinterpret_cast<const uint4*>(x + (int64_t)halo[e & 7] * d + fbase + 8 * g);
-      }
-    } else {
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int p = p0 + u;
-        rv[u] = make_uint4(0u, 0u, 0u, 0u);
-        if (p < hi) rv[u] = *reinterpret_cast<const uint4*>(xt + (p - (int)t0) * kGatherPitch + 16 * g);
-      }
-    }
-    uint16_t* dst = xgT + (pad_off[s] + 32 * (int64_t)blk) * d + (int64_t)(fbase + 8 * g) * 32 + 8 * q;
-#pragma unroll
-    for (int fp = 0; fp < 4; ++fp) {       // feature pair (2fp, 2fp+1) of the group
-      uint32_t a[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) a[u] = (&rv[u].x)[fp];
-      *reinterpret_cast<uint4*>(dst + (2 * fp) * 32) =
-          make_uint4(lo_pair(a[0], a[1]), lo_pair(a[2], a[3]), lo_pair(a[4], a[5]), lo_pair(a[6], a[7]));
-      *reinterpret_cast<uint4*>(dst + (2 * fp + 1) * 32) =
-          make_uint4(hi_pair(a[0], a[1]), hi_pair(a[2], a[3]), hi_pair(a[4], a[5]), hi_pair(a[6], a[7]));
-    }
-  }
-}
-
-void launch_gather(const uint16_t* x, const CollectPlan& p, hipStream_t s) {
-  const int tpx = (p.ntile + kXcds - 1) / kXcds;
-  const dim3 grid((unsigned)(kXcds * tpx * (p.d / kGatherFeat)));
-  // the common shapes (up to 64 routed experts + 1 shared, top-8) get the small
-  // LDS tables, so two workgroups fit on a CU
-  if (p.E + p.has_shared <= 65 && p.K <= 8)
-    hipLaunchKernelGGL((gather_kernel<65, 8>), grid, dim3(kGatherThreads), 0, s, x, p.n_tokens, p.d, p.E,
-                       p.has_shared, p.offsets, p.pad_off, p.token_ids, p.tilebase, p.ntile, tpx, p.xgT);
-  else
-    hipLaunchKernelGGL((gather_kernel<kMaxSlots, kMaxTopK>), grid, dim3(kGatherThreads), 0, s, x, p.n_tokens,
-                       p.d, p.E, p.has_shared, p.offsets, p.pad_off, p.token_ids, p.tilebase, p.ntile, tpx,
-                       p.xgT);
+                     p.K, p.E, p.blockbase, p.offsets, p.token_ids);
 }
 
 }  // namespace clha

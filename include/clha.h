@@ -127,8 +127,7 @@ CLHA_API size_t clha_collect_workspace_bytes(const clha_ctx* ctx);
 /* Collection phase for one calibration batch of one layer (section 2.2, phase 1):
  *   1. routes each token to its top-K experts (larger logit first, ties to the lower index);
  *   2. buckets tokens per expert (counts, exclusive offsets, token lists ascending);
- *   3. gathers each expert's rows of X;
- *   4. S[e] += X_e^T X_e (fp32 accumulation of bf16 products) for every routed expert,
+ *   3. S[e] += X_e^T X_e (fp32 accumulation of bf16 products) for every routed expert,
  *      and S[E] += X^T X over all tokens when the block has shared experts;
  *      counts[e] += n_e, counts[E] += n_tokens (stored instead of added by the first
  *      collection with tokens after clha_reset_layer).
@@ -359,7 +358,7 @@ CLHA_API clha_status clha_unpack_codes(clha_ctx* ctx, int64_t n_codes, int32_t b
 typedef enum clha_stage {
   CLHA_STAGE_ROUTE = 0,      /* top-K routing kernel */
   CLHA_STAGE_BUCKET = 1,     /* histogram, scan and scatter kernels */
-  CLHA_STAGE_GATHER = 2,     /* gather of each expert's rows */
+  CLHA_STAGE_GATHER = 2,     /* down_proj inputs: the grouped SwiGLU GEMM (clha_collect_down_hessians) */
   CLHA_STAGE_SYRK = 3,       /* Gram-sum kernel (one launch per collect call) */
   CLHA_STAGE_AGGREGATE = 4,  /* aggregation kernel */
   CLHA_STAGE_FACTOR = 5,     /* damping, Cholesky and triangular inverse (clha_inverse_cholesky) */
