@@ -344,8 +344,9 @@ def summarize_profiles(d, wid):
                      f"{rate['F32']:.1f} | {rate['F64']:.2f} | {conf / act if act else 0.0:.4f} |")
     open(os.path.join(ROOT, "profiles", f"clha_step_{name}_mfma_lds_counters.md"), "w").write("\n".join(lines) + "\n")
 
-    sk = "clha::syrk_kernel"
-    rec = {"workload": name, "kernel": "syrk_kernel", "syrk_source_sha256_16": syrk_source_hash(),
+    # the collection's Gram-sum kernel (operands read from x by token id)
+    sk = "clha::syrk_kernel<true>"
+    rec = {"workload": name, "kernel": "syrk_kernel<true>", "syrk_source_sha256_16": syrk_source_hash(),
            "fetch_kib_per_launch": fetch[sk][0] / fetch[sk][1], "write_kib_per_launch": write[sk][0] / write[sk][1],
            "fetch_scale": f_scale, "write_scale": w_scale,
            "hbm_bytes_per_launch": (fetch[sk][0] / fetch[sk][1] * f_scale + write[sk][0] / write[sk][1] * w_scale) * 1024,
@@ -620,7 +621,7 @@ def calibration_bench(args):
         rec = json.load(open(tf))
         if rec.get("syrk_source_sha256_16") == syrk_source_hash():
             traffic = rec.get("hbm_bytes_per_launch")
-    roofline = {"kernel": "syrk_kernel", "bound": "mfma", "achieved": round(achieved, 2),
+    roofline = {"kernel": "syrk_kernel<true>", "bound": "mfma", "achieved": round(achieved, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": traffic, "avg_launch_ms": round(syrk_avg_ms, 4),
                 "flops_per_launch": flops_per_launch}
