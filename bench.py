@@ -179,31 +179,41 @@ def _short(name):
 
 
 def _trace_lines(trace_dir, title, cmd, notes, steps=4, timed=3, setup_free=False):
-    """Kernel-time table of a traced bench run (1 warm-up + `timed` steps).  Each
-    kernel's first launches (1/steps of them) belong to the warm-up step, whose
-    first touch of fresh device memory is slow; they are left out.  With
+    """Kernel-time table of a traced bench run (1 warm-up + `timed` steps).  When
+    the run routes each step's two layers (2 routing launches per step), only the
+    launches from the first timed step's routing on are counted, which leaves
+    out the set-up (buffer fills, input copies) and the warm-up step, whose first
+    touch of fresh device memory is slow.  Otherwise each kernel's first
+    launches (1/steps of them) are taken as the warm-up's and left out; with
     setup_free, kernels launched fewer than `steps` times ran only in the set-up
-    before the steps and are left out too."""
+    and are left out too."""
     trace = _csv(_find(trace_dir, "kernel_trace.csv"))
+    routes = sorted(int(r["Start_Timestamp"]) for r in trace if "route_kernel" in r["Kernel_Name"])
+    window = routes[2 * (steps - timed)] if len(routes) == 2 * steps else None
     by_name = {}
     for r in trace:
+        if window is not None and int(r["Start_Timestamp"]) < window:
+            continue
         by_name.setdefault(r["Kernel_Name"], []).append(
             (int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
     stats = []
     for name, ds in by_name.items():
         ds.sort()
-        if setup_free and len(ds) < steps:
-            continue
-        if setup_free:
-            ds = ds[len(ds) % steps:]          # launches before the steps
-        keep = [t for _, t in ds[len(ds) // steps:]] if len(ds) >= steps else [t for _, t in ds]
+        if window is not None:
+            keep = [t for _, t in ds]
+        else:
+            if setup_free and len(ds) < steps:
+                continue
+            if setup_free:
+                ds = ds[len(ds) % steps:]          # launches before the steps
+            keep = [t for _, t in ds[len(ds) // steps:]] if len(ds) >= steps else [t for _, t in ds]
         if keep:
             stats.append({"Name": name, "Calls": len(keep), "TotalDurationNs": sum(keep),
                           "AverageNs": sum(keep) / len(keep)})
     stats.sort(key=lambda r: -r["TotalDurationNs"])
     lines = [title, "", "Command (repository root):", "", f"    {cmd}", "",
-             f"{steps} steps traced (1 warm-up + {timed} timed); the warm-up step's launches are left out "
-             f"and per-step figures are totals / {timed}.", *notes, "",
+             f"{steps} steps traced (1 warm-up + {timed} timed); the set-up's and the warm-up step's launches "
+             f"are left out and per-step figures are totals / {timed}.", *notes, "",
              "| kernel | calls/step | ms/step | avg us/launch | % |", "|---|---:|---:|---:|---:|"]
     total = sum(float(r["TotalDurationNs"]) for r in stats)
     for r in stats:
