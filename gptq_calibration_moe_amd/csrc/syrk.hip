@@ -644,15 +644,17 @@ __global__ __launch_bounds__(512) void syrk_kernel(GramIn in, const int32_t* __r
 }
 
 // S[slot] (lower triangle) += the partial sums of each token-split slot, in
-// part order.  Row i per block row, four columns per thread.
+// part order.  Workgroup (x, i, z): row i, columns 1024x .. +1023 (four per
+// thread), split slots z, z + kReduceGroups, ...
+constexpr int kReduceGroups = 8;
 __global__ __launch_bounds__(256) void syrk_reduce_kernel(const int32_t* __restrict__ split,
                                                           const float* __restrict__ partials,
                                                           float* __restrict__ S, int d) {
   const int nsplit = split[0];
   const int i = blockIdx.y, j = 4 * (blockIdx.x * 256 + threadIdx.x);
-  if (nsplit == 0 || j > i || j >= d) return;
+  if (j > i || j >= d) return;
   const int64_t dd = (int64_t)d * d, off = (int64_t)i * d + j;
-  for (int sp = 0; sp < nsplit; ++sp) {
+  for (int sp = blockIdx.z; sp < nsplit; sp += kReduceGroups) {
     const int slot = split[1 + 3 * sp], p0 = split[2 + 3 * sp], np = split[3 + 3 * sp];
     float* o = S + (int64_t)slot * dd + off;
     float4 v = *reinterpret_cast<const float4*>(o);
@@ -713,7 +715,7 @@ void launch_syrk(const CollectPlan& p, float* S, hipStream_t s) {
 // After the Gram-sum kernel.  The slots zeroed here received no token, so no
 // Gram-sum item or partial buffer touches them.
 void launch_syrk_reduce(const CollectPlan& p, float* S, const int64_t* layer_counts, hipStream_t s) {
-  hipLaunchKernelGGL(syrk_reduce_kernel, dim3((p.d + 1023) / 1024, p.d), dim3(256), 0, s, p.split,
+  hipLaunchKernelGGL(syrk_reduce_kernel, dim3((p.d + 1023) / 1024, p.d, kReduceGroups), dim3(256), 0, s, p.split,
                      p.partials, S, p.d);
   if (p.overwrite)
     hipLaunchKernelGGL(zero_empty_slots_kernel, dim3(p.E + p.has_shared), dim3(256), 0, s, layer_counts, S,
