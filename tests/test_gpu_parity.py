@@ -190,14 +190,14 @@ def test_inverse_cholesky(c, dead):
     U, lam, dd = U.cpu().numpy(), lam.cpu().numpy(), dd.cpu().numpy()
     for i, H in enumerate(Hs):
         H32 = H.astype(np.float32).astype(np.float64)
+        # dead columns, lambda and U as the oracle's GPTQ makes them (one zero row)
+        ref = oracle.gptq(np.zeros((1, c)), H32, 2, 64, damp=0.01, block=64)
+        assert (dd[i].astype(bool) == ref["dead"]).all()
+        assert abs(lam[i] - ref["lam"]) <= 1e-6 * ref["lam"]
         hd = H32.copy()
-        dmask = np.diag(hd) == 0
-        assert (dd[i].astype(bool) == dmask).all()
-        hd[dmask, dmask] = 1.0
-        l_ref = 0.01 * np.mean(np.diag(hd))
-        assert abs(lam[i] - l_ref) <= 1e-6 * l_ref
-        hd += l_ref * np.eye(c)
-        Uref = oracle.inverse_cholesky_upper(hd)
+        hd[ref["dead"], ref["dead"]] = 1.0
+        hd += ref["lam"] * np.eye(c)
+        Uref = ref["U"]
         # the factor is computed in fp64 and rounded to fp32 once
         err = np.max(np.abs(np.triu(U[i]) - Uref)) / np.max(np.abs(Uref))
         assert err < 1e-6, err
