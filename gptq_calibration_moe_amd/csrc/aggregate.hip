@@ -139,32 +139,29 @@ __global__ __launch_bounds__(256) void aggregate_kernel(AggArgs g, float* __rest
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int idx = threadIdx.x + 256 * k, r = idx >> 4, c = 4 * (idx & 15);
-    if (diag && c > r) continue;
-    const int64_t e = (int64_t)(ti * 64 + r) * d + tj * 64 + c;
-    // on a diagonal tile, columns past the row are above the diagonal: S is not
-    // written there, so those values come from the mirror write below instead
 #pragma unroll
     for (int u = 0; u < 4; ++u) T[r][c + u] = v[k][u];
-    if (!diag || c + 3 <= r) {
-      *reinterpret_cast<float4*>(Hs + e) = make_float4(v[k][0], v[k][1], v[k][2], v[k][3]);
-    } else {
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (c + u <= r) Hs[e + u] = v[k][u];
-    }
+    // an off-diagonal tile is written here and mirrored below; a diagonal tile
+    // is written whole below (its upper half from the mirror of its lower half:
+    // S is not written above the diagonal)
+    if (!diag)
+      *reinterpret_cast<float4*>(Hs + (int64_t)(ti * 64 + r) * d + tj * 64 + c) =
+          make_float4(v[k][0], v[k][1], v[k][2], v[k][3]);
   }
   __syncthreads();
   for (int idx = threadIdx.x; idx < 64 * 16; idx += 256) {
     const int r = idx >> 4, c = 4 * (idx & 15);   // writes row tj*64 + r, columns ti*64 + c ..
-    if (diag && c + 3 <= r) continue;
     float* o = Hs + (int64_t)(tj * 64 + r) * d + ti * 64 + c;
+    float4 t;
     if (!diag) {
-      *reinterpret_cast<float4*>(o) = make_float4(T[c][r], T[c + 1][r], T[c + 2][r], T[c + 3][r]);
+      t = make_float4(T[c][r], T[c + 1][r], T[c + 2][r], T[c + 3][r]);
     } else {
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (c + u > r) o[u] = T[c + u][r];
+      t.x = c <= r ? T[r][c] : T[c][r];
+      t.y = c + 1 <= r ? T[r][c + 1] : T[c + 1][r];
+      t.z = c + 2 <= r ? T[r][c + 2] : T[c + 2][r];
+      t.w = c + 3 <= r ? T[r][c + 3] : T[c + 3][r];
     }
+    *reinterpret_cast<float4*>(o) = t;
   }
 }
 
