@@ -17,7 +17,7 @@ constexpr int kMaxTopK = 16;
 constexpr int kMaxLayers = 8;
 constexpr int kSyrkTile = 256;        // Gram-sum output tile
 constexpr int kMaxPartialsCap = 512;  // most partial Gram-sum buffers of token-split slots
-constexpr int kSegTokens = 8192;      // longest Gram-sum segment (one flush interval)
+constexpr int kSegTokens = 16384;     // longest Gram-sum segment (one flush interval)
 constexpr int kMaxSlots = kMaxExperts + 1;                // Hessian slots of one layer
 constexpr int kMaxSegsCap = kMaxSlots + kMaxPartialsCap;  // most Gram-sum segments per call
 // Partial buffers of a context: enough for every segment past each slot's first

@@ -25,6 +25,10 @@ namespace clha {
 // ------------------------------------------------------------------ routing
 
 // Also writes iota[t] = t, the shared slot's token list for the Gram sums.
+// KC >= K is the list length the insertion runs over (a compile-time bound, so
+// the list stays in registers with no per-entry test of K); VEC reads the row
+// 16 bytes at a time (E a multiple of 4 and the logits 16-byte aligned).
+template <int KC, bool VEC>
 __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits, int64_t n,
                                                     int E, int K, int32_t* __restrict__ topk,
                                                     int* __restrict__ status, int layer,
@@ -33,36 +37,44 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
   if (t >= n) return;
   iota[t] = (int32_t)t;
   const float* row = logits + t * E;
-  float val[kMaxTopK];
-  int idx[kMaxTopK];
+  float val[KC];
+  int idx[KC];
 #pragma unroll
-  for (int p = 0; p < kMaxTopK; ++p) {
+  for (int p = 0; p < KC; ++p) {
     val[p] = -INFINITY;
     idx[p] = 0x7fffffff;
   }
   bool bad = false;
-  for (int e = 0; e < E; ++e) {
-    float cv = row[e];
-    int ci = e;
+  // insertion into the list ordered by (logit descending, index ascending);
+  // an element pushed down keeps moving past entries it precedes, so equal
+  // logits always end up in index order.  Entries past K only ever hold
+  // elements pushed out of the first K, so the first K are the top K.
+  auto insert = [&](float cv, int ci) {
     bad |= !isfinite(cv);
-    // insertion into the list ordered by (logit descending, index ascending);
-    // an element pushed down keeps moving past entries it precedes, so equal
-    // logits always end up in index order
 #pragma unroll
-    for (int p = 0; p < kMaxTopK; ++p) {
-      if (p < K) {
-        const bool gt = cv > val[p] || (cv == val[p] && ci < idx[p]) || idx[p] == 0x7fffffff;
-        const float tv = val[p];
-        const int ti = idx[p];
-        val[p] = gt ? cv : tv;
-        idx[p] = gt ? ci : ti;
-        cv = gt ? tv : cv;
-        ci = gt ? ti : ci;
-      }
+    for (int p = 0; p < KC; ++p) {
+      const bool gt = cv > val[p] || (cv == val[p] && ci < idx[p]) || idx[p] == 0x7fffffff;
+      const float tv = val[p];
+      const int ti = idx[p];
+      val[p] = gt ? cv : tv;
+      idx[p] = gt ? ci : ti;
+      cv = gt ? tv : cv;
+      ci = gt ? ti : ci;
     }
+  };
+  if constexpr (VEC) {
+    for (int e = 0; e < E; e += 4) {
+      const float4 q = *reinterpret_cast<const float4*>(row + e);
+      insert(q.x, e);
+      insert(q.y, e + 1);
+      insert(q.z, e + 2);
+      insert(q.w, e + 3);
+    }
+  } else {
+    for (int e = 0; e < E; ++e) insert(row[e], e);
   }
 #pragma unroll
-  for (int p = 0; p < kMaxTopK; ++p)
+  for (int p = 0; p < KC; ++p)
     if (p < K) topk[t * K + p] = idx[p];
   if (bad) {
     atomicOr(status, kStatusNonfinite);
@@ -72,10 +84,22 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
   }
 }
 
-void launch_route(const float* logits, const CollectPlan& p, hipStream_t s) {
+template <int KC>
+static void launch_route_k(const float* logits, const CollectPlan& p, hipStream_t s) {
   const unsigned grid = (unsigned)((p.n_tokens + 255) / 256);
-  hipLaunchKernelGGL(route_kernel, dim3(grid), dim3(256), 0, s, logits, p.n_tokens, p.E, p.K,
-                     p.topk, p.status, p.layer, p.iota);
+  if (p.E % 4 == 0 && reinterpret_cast<uintptr_t>(logits) % 16 == 0)
+    hipLaunchKernelGGL((route_kernel<KC, true>), dim3(grid), dim3(256), 0, s, logits, p.n_tokens, p.E, p.K,
+                       p.topk, p.status, p.layer, p.iota);
+  else
+    hipLaunchKernelGGL((route_kernel<KC, false>), dim3(grid), dim3(256), 0, s, logits, p.n_tokens, p.E, p.K,
+                       p.topk, p.status, p.layer, p.iota);
+}
+
+void launch_route(const float* logits, const CollectPlan& p, hipStream_t s) {
+  if (p.K <= 2) launch_route_k<2>(logits, p, s);
+  else if (p.K <= 4) launch_route_k<4>(logits, p, s);
+  else if (p.K <= 8) launch_route_k<8>(logits, p, s);
+  else launch_route_k<kMaxTopK>(logits, p, s);
 }
 
 // ------------------------------------------------------------------ bucketing

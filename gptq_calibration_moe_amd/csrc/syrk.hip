@@ -54,7 +54,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kT = 256;              // output tile
 constexpr int kSK = 32;              // tokens per step
-constexpr int kFlushSteps = 256;     // 8192 tokens between partial-sum flushes (multiple of kStages)
+constexpr int kFlushSteps = 512;     // 16384 tokens between partial-sum flushes (multiple of kStages)
 constexpr int kStages = 4;           // LDS stages; loads run kStages - 1 steps ahead
 constexpr int kPanel = kT * kSK;     // one operand stage: 256 rows x 32 tokens (bf16 elements)
 
