@@ -40,6 +40,8 @@ PEAK_BF16_TFLOPS = 2500.0          # MI355X dense bf16 matrix peak
 PEAK_FP32_TFLOPS = 157.3           # MI355X fp32 matrix peak
 PEAK_HBM_GBS = 8000.0              # MI355X HBM3E bandwidth
 SYRK_SRC = os.path.join(ROOT, "gptq_calibration_moe_amd", "csrc", "syrk.hip")
+DOWN_SRC = os.path.join(ROOT, "gptq_calibration_moe_amd", "csrc", "down.hip")
+DOWN_TRAFFIC = os.path.join(ROOT, "profiles", "down_gemm_mid_moe_block_traffic.json")
 
 
 def parse():
@@ -61,6 +63,10 @@ def parse():
                     help="write the options step's trace summary and bench line under profiles/ and exit")
     ap.add_argument("--summarize-down-profile", nargs=2, metavar=("DIR", "BENCH_JSON"),
                     help="write the down_proj profile summaries from DIR and the bench output file, and exit")
+    ap.add_argument("--down-counter-commands", metavar="DIR",
+                    help="print the down_proj GEMM's counter command lines and exit")
+    ap.add_argument("--summarize-down-traffic", metavar="DIR",
+                    help="write the down_proj GEMM's traffic record from DIR and exit")
     ap.add_argument("--experiment", choices=("drift", "sharpness"),
                     help="run a section-4 experiment on the drift-stress shapes and write its table")
     ap.add_argument("--out", help="JSON file of the experiment table (default under profiles/)")
@@ -73,6 +79,10 @@ def log(msg):
 
 def syrk_source_hash():
     return hashlib.sha256(open(SYRK_SRC, "rb").read()).hexdigest()[:16]
+
+
+def down_source_hash():
+    return hashlib.sha256(open(DOWN_SRC, "rb").read()).hexdigest()[:16]
 
 
 def cpu_baseline(wl, inp, w_host, budget_s=10.0):
@@ -224,6 +234,54 @@ def _trace_lines(trace_dir, title, cmd, notes, steps=4, timed=3, setup_free=Fals
     return lines
 
 
+def down_traffic():
+    """HBM bytes per down_gemm launch from the committed counter record, while
+    down.hip is the source it was taken on (else None)."""
+    if not os.path.exists(DOWN_TRAFFIC):
+        return None
+    rec = json.load(open(DOWN_TRAFFIC))
+    return rec.get("hbm_bytes_per_launch") if rec.get("down_source_sha256_16") == down_source_hash() else None
+
+
+DOWN_COUNTER_RUNS = (
+    ("fetch", "timeout -s KILL 300 rocprofv3 --pmc FETCH_SIZE --output-format csv -d {dir}/fetch -o run "
+              "-- python3 bench.py --down-proj --steps 1 --warmup 1"),
+    ("write", "timeout -s KILL 300 rocprofv3 --pmc WRITE_SIZE --output-format csv -d {dir}/write -o run "
+              "-- python3 bench.py --down-proj --steps 1 --warmup 1"),
+    ("copy_fetch", "timeout -s KILL 60 rocprofv3 --pmc FETCH_SIZE --output-format csv -d {dir}/copy_fetch -o run "
+                   "-- python3 bench.py --copy-probe 1073741824"),
+    ("copy_write", "timeout -s KILL 60 rocprofv3 --pmc WRITE_SIZE --output-format csv -d {dir}/copy_write -o run "
+                   "-- python3 bench.py --copy-probe 1073741824"),
+)
+
+
+def summarize_down_traffic(d):
+    """down_gemm's HBM traffic per launch from the counter passes of DOWN_COUNTER_RUNS in
+    DIR (copy-probe scaled, as for the Gram sums), written to DOWN_TRAFFIC."""
+    def per_kernel(sub, counter, key):
+        tot, cnt = 0.0, 0
+        for r in _csv(_find(os.path.join(d, sub), "counter_collection.csv")):
+            if r["Counter_Name"] == counter and key in r["Kernel_Name"]:
+                tot += float(r["Counter_Value"])
+                cnt += 1
+        return tot, cnt
+    def copy_kib(sub, counter):
+        v, c = per_kernel(sub, counter, "copyBuffer")
+        return v / c if c else None
+    f_scale = COPY_BYTES / 1024 / copy_kib("copy_fetch", "FETCH_SIZE")
+    w_scale = COPY_BYTES / 1024 / copy_kib("copy_write", "WRITE_SIZE")
+    fv, fc = per_kernel("fetch", "FETCH_SIZE", "down_gemm_kernel")
+    wv, wc = per_kernel("write", "WRITE_SIZE", "down_gemm_kernel")
+    rec = {"workload": "mid_moe_block_down_proj", "kernel": "down_gemm_kernel",
+           "down_source_sha256_16": down_source_hash(),
+           "fetch_kib_per_launch": fv / fc, "write_kib_per_launch": wv / wc,
+           "fetch_scale": f_scale, "write_scale": w_scale,
+           "hbm_bytes_per_launch": (fv / fc * f_scale + wv / wc * w_scale) * 1024,
+           "commands": [c.format(dir=d) for _, c in DOWN_COUNTER_RUNS]}
+    json.dump(rec, open(DOWN_TRAFFIC, "w"), indent=1)
+    print(json.dumps(rec))
+
+
 DOWN_TRACE = ("timeout -k 10 400 rocprofv3 --kernel-trace --stats --output-format csv -d {dir}/trace -o run "
               "-- python3 bench.py --down-proj --steps 3 --warmup 1")
 
@@ -247,7 +305,8 @@ def summarize_down_profile(d, bench_json):
 
 
 OPTIONS_TRACE = ("timeout -k 10 400 rocprofv3 --kernel-trace --stats --output-format csv -d {dir}/trace -o run "
-                 "-- python3 bench.py --act-order --static-groups --steps 3 --warmup 1 --no-cpu-baseline")
+                 "-- python3 bench.py --workload 2 --act-order --static-groups --steps 3 --warmup 1 "
+                 "--no-cpu-baseline")
 
 
 def summarize_options_profile(d, bench_json):
@@ -264,7 +323,7 @@ def summarize_options_profile(d, bench_json):
     json.loads(line)
     out = ["# Bench line, mid MoE block with GPTQ activation order and static groups (MI355X)", "",
            "Command (repository root):", "",
-           "    timeout -k 10 400 python3 -u bench.py --act-order --static-groups --no-cpu-baseline", "",
+           "    timeout -k 10 400 python3 -u bench.py --workload 2 --act-order --static-groups --no-cpu-baseline", "",
            "Output:", "", "```json", line, "```", ""]
     open(os.path.join(ROOT, "profiles", "bench_gptq_options_mid_moe_block.md"), "w").write("\n".join(out))
 
@@ -498,7 +557,8 @@ def down_proj_bench(args):
             "roofline": {"kernel": "down_gemm_kernel", "bound": "mfma",
                          "achieved": round(achieved, 2) if achieved else None, "peak": PEAK_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4) if achieved else None,
-                         "traffic": None, "avg_launch_ms": round(gemm_ms, 4), "flops_per_launch": gemm_flops},
+                         "traffic": down_traffic(), "avg_launch_ms": round(gemm_ms, 4),
+                         "flops_per_launch": gemm_flops},
             "stages_ms_per_step": {k: round(v, 4) for k, v in stages.items()}}
     print(json.dumps(line), flush=True)
     return 0
@@ -518,6 +578,13 @@ def main():
         return 0
     if args.summarize_down_profile:
         summarize_down_profile(*args.summarize_down_profile)
+        return 0
+    if args.down_counter_commands:
+        for _, c in DOWN_COUNTER_RUNS:
+            print(c.format(dir=args.down_counter_commands))
+        return 0
+    if args.summarize_down_traffic:
+        summarize_down_traffic(args.summarize_down_traffic)
         return 0
     if args.copy_probe:
         copy_probe(args.copy_probe)
