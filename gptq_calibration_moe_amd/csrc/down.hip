@@ -33,6 +33,7 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 constexpr int kDF = 128;   // features per tile
 constexpr int kDT = 128;   // tokens per tile
 constexpr int kDK = 32;    // model dimension per chunk (64-byte rows)
+constexpr int kDG = 2;     // feature tiles per group of the tile order (see the kernel)
 
 __device__ __forceinline__ int down_off(int r, int c) { return r * 64 + ((c ^ ((r >> 2) & 3)) << 4); }
 
@@ -57,14 +58,26 @@ __global__ __launch_bounds__(256, 2) void down_gemm_kernel(const uint16_t* __res
   const int64_t per = (grid_tiles + kXcds - 1) / kXcds;
   const int64_t L = (int64_t)(blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
   if (L >= total) return;
-  const int tt = (int)(L / nft), ft = (int)(L - (int64_t)tt * nft);
+  // the slot owns workgroups [tile_off[e] nft, tile_off[e+1] nft); inside it the
+  // order is kDG feature tiles at a time, all token tiles per group, the kDG
+  // tiles of one token tile adjacent: the workgroups an XCD runs together share
+  // kDG weight slices (2 MB at kDG = 2) and read each x panel once per group,
+  // where a token-tile-major order cycled through the expert's whole 11.5 MB of
+  // weights, more than an XCD's L2 holds
+  const int ttg = (int)(L / nft);
   int lo = 0, hi = slots;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if (tile_off[mid] <= tt) lo = mid; else hi = mid;
+    if (tile_off[mid] <= ttg) lo = mid; else hi = mid;
   }
   const int e = lo;
-  const int t0 = (tt - tile_off[e]) * kDT;
+  const int T = tile_off[e + 1] - tile_off[e];
+  const int64_t l = L - (int64_t)tile_off[e] * nft;
+  const int g = (int)(l / ((int64_t)kDG * T));
+  const int gs = min(kDG, nft - g * kDG);
+  const int within = (int)(l - (int64_t)g * kDG * T);
+  const int tt = within / gs, ft = g * kDG + within % gs;
+  const int t0 = tt * kDT;
   const int64_t cnt = e < E ? roff[e + 1] - roff[e] : n;
   const int64_t npad = pad_off[e + 1] - pad_off[e];
   const int f0 = ft * kDF;
