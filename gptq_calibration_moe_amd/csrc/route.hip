@@ -263,7 +263,8 @@ __device__ void plan_gram(const int64_t* cnt, PlanLds& L, int slots, int64_t* __
 // One workgroup: per-expert exclusive scan over bucketing workgroups, expert
 // offsets, then the Gram-sum plan of the layer's slots (routed experts, and the
 // shared-expert slot with all tokens).
-__global__ __launch_bounds__(256) void bucket_scan_kernel(
+constexpr int kScanThreads = 1024;
+__global__ __launch_bounds__(kScanThreads) void bucket_scan_kernel(
     const int32_t* __restrict__ blockcounts, int nblk, int64_t n, int E, int has_shared,
     int32_t* __restrict__ blockbase, int64_t* __restrict__ offsets, int64_t* __restrict__ pad_off,
     int32_t* __restrict__ slot_order, int64_t* __restrict__ layer_counts, int overwrite, int items,
@@ -271,27 +272,48 @@ __global__ __launch_bounds__(256) void bucket_scan_kernel(
     int32_t* __restrict__ seg, int32_t* __restrict__ split, int max_partials, uint16_t* __restrict__ zero_row,
     int d) {
   __shared__ int64_t cnt[kMaxSlots];
+  __shared__ int64_t part[kScanThreads];
   __shared__ PlanLds L;
   const int slots = E + has_shared;
   // the Gram sums' operand for padding positions
-  for (int f = threadIdx.x; f < d; f += 256) zero_row[f] = 0;
-  // 16 blocks' counts are loaded together, so a thread waits for memory once
-  // per 16 blocks rather than once per block
+  for (int f = threadIdx.x; f < d; f += blockDim.x) zero_row[f] = 0;
+  // tpe threads per expert (a power of two, E * tpe <= the block), each over one
+  // run of consecutive token blocks: the runs' sums, an exclusive scan over an
+  // expert's runs, then each run's block bases.  16 blocks' counts are loaded
+  // together, so a thread waits for memory once per 16 blocks.
   constexpr int kScanBatch = 16;
-  for (int e = threadIdx.x; e < E; e += 256) {
-    int64_t run = 0;
-    for (int b0 = 0; b0 < nblk; b0 += kScanBatch) {
+  int tpe = 1;
+  while (tpe < 64 && 2 * tpe * E <= (int)blockDim.x) tpe *= 2;
+  const bool mine = (int)threadIdx.x < E * tpe;
+  const int e = threadIdx.x / tpe, t = threadIdx.x % tpe;
+  const int run_len = (nblk + tpe - 1) / tpe;
+  const int b_lo = min(t * run_len, nblk), b_hi = min(b_lo + run_len, nblk);
+  int64_t sum = 0;
+  if (mine) {
+    for (int b0 = b_lo; b0 < b_hi; b0 += kScanBatch) {
       int c[kScanBatch];
 #pragma unroll
-      for (int j = 0; j < kScanBatch; ++j)
-        c[j] = b0 + j < nblk ? blockcounts[(int64_t)(b0 + j) * E + e] : 0;
+      for (int j = 0; j < kScanBatch; ++j) c[j] = b0 + j < b_hi ? blockcounts[(int64_t)(b0 + j) * E + e] : 0;
+#pragma unroll
+      for (int j = 0; j < kScanBatch; ++j) sum += c[j];
+    }
+  }
+  part[threadIdx.x] = sum;
+  __syncthreads();
+  if (mine) {
+    int64_t run = 0;
+    for (int u = 0; u < t; ++u) run += part[e * tpe + u];
+    if (t == tpe - 1) cnt[e] = run + sum;
+    for (int b0 = b_lo; b0 < b_hi; b0 += kScanBatch) {
+      int c[kScanBatch];
+#pragma unroll
+      for (int j = 0; j < kScanBatch; ++j) c[j] = b0 + j < b_hi ? blockcounts[(int64_t)(b0 + j) * E + e] : 0;
 #pragma unroll
       for (int j = 0; j < kScanBatch; ++j) {
-        if (b0 + j < nblk) blockbase[(int64_t)(b0 + j) * E + e] = (int32_t)run;
+        if (b0 + j < b_hi) blockbase[(int64_t)(b0 + j) * E + e] = (int32_t)run;
         run += c[j];
       }
     }
-    cnt[e] = run;
   }
   if (threadIdx.x == 0 && has_shared) cnt[E] = n;
   __syncthreads();
@@ -382,7 +404,7 @@ void launch_zero_counts(int64_t* counts, int n, hipStream_t s) {
 void launch_bucket(const CollectPlan& p, int64_t* layer_counts, hipStream_t s) {
   hipLaunchKernelGGL(bucket_count_kernel, dim3(p.nblk), dim3(256), 0, s, p.topk, p.n_tokens, p.K,
                      p.E, p.blockcounts);
-  hipLaunchKernelGGL(bucket_scan_kernel, dim3(1), dim3(256), 0, s, p.blockcounts, p.nblk,
+  hipLaunchKernelGGL(bucket_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, p.blockcounts, p.nblk,
                      p.n_tokens, p.E, p.has_shared, p.blockbase, p.offsets, p.pad_off,
                      p.slot_order, layer_counts, p.overwrite, p.syrk_items, p.work, p.work_len, p.work_next,
                      p.seg, p.split, p.max_partials, p.zero_row, p.d);
