@@ -617,6 +617,22 @@ __global__ __launch_bounds__(512, 1) void gptq_trail_kernel(GptqPlan p, int c0, 
     fetch(a0, 0);
     fetch(a1, 1);
     const int cl = wc * 32 + 4 * hh;                  // lane's first result column in a tile
+    // The error digits of K step kc (the same for every tile) are read one step
+    // ahead of their products, into two register sets, so the LDS latency
+    // overlaps the previous step's products; the read after a tile's last
+    // step is step 0 of the next tile.
+    auto read_e = [&](i32x4 (&bq)[2][kTS], int kc) {
+      const int ch = 2 * kc + hh;
+#pragma unroll
+      for (int pp = 0; pp < kTS; ++pp)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          const int row = 32 * b + li;
+          bq[b][pp] = *reinterpret_cast<const i32x4*>(&Eq[pp][row][16 * (ch ^ (row & 15))]);
+        }
+    };
+    i32x4 e0[2][kTS], e1[2][kTS];
+    read_e(e0, 0);
     int g = 0;
     for (int t = 0; t < n_ct; ++t) {
       const int ncols = min(kGemmTile, c - (n0 + t * kGemmTile));   // 64 or 128
@@ -625,16 +641,7 @@ __global__ __launch_bounds__(512, 1) void gptq_trail_kernel(GptqPlan p, int c0, 
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int w = 0; w < kTS; ++w) acc[b][w] = i32x16{};
-      auto step = [&](const i32x4 (&a)[kTS], int kc) {
-        i32x4 bq[2][kTS];
-        const int ch = 2 * kc + hh;
-#pragma unroll
-        for (int pp = 0; pp < kTS; ++pp)
-#pragma unroll
-          for (int b = 0; b < 2; ++b) {
-            const int row = 32 * b + li;
-            bq[b][pp] = *reinterpret_cast<const i32x4*>(&Eq[pp][row][16 * (ch ^ (row & 15))]);
-          }
+      auto mul = [&](const i32x4 (&a)[kTS], const i32x4 (&bq)[2][kTS]) {
         // the two blocks alternate, so products into one accumulator are never adjacent
 #pragma unroll
         for (int pp = 0; pp < kTS; ++pp)
@@ -644,14 +651,24 @@ __global__ __launch_bounds__(512, 1) void gptq_trail_kernel(GptqPlan p, int c0, 
             for (int b = 0; b < 2; ++b)
               acc[b][pp + q] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[pp], bq[b][q], acc[b][pp + q], 0, 0, 0);
       };
-      // K steps in pairs: even steps use a0, odd ones a1, each refilled two steps ahead
-#pragma unroll 1
-      for (int kc = 0; kc < kSuper / kTK; kc += 2, g += 2) {
-        step(a0, kc);
-        fetch(a0, g + 2);
-        step(a1, kc + 1);
-        fetch(a1, g + 3);
+      // K steps in pairs: even steps use a0 and e0, odd ones a1 and e1; the U
+      // digits are refilled two steps ahead, the error digits one.  Unrolled,
+      // so that the waits for the U digits count the loads issued after them
+      // (across a loop edge the compiler waits for every load in flight).
+#pragma unroll
+      for (int kc = 0; kc < kSuper / kTK; kc += 2) {
+        read_e(e1, kc + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        mul(a0, e0);
+        fetch(a0, g + kc + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        read_e(e0, (kc + 2) % (kSuper / kTK));
+        __builtin_amdgcn_sched_barrier(0);
+        mul(a1, e1);
+        fetch(a1, g + kc + 3);
+        __builtin_amdgcn_sched_barrier(0);
       }
+      g += kSuper / kTK;
       if (wc * 32 < ncols) {
         // results r = 4q .. 4q+3 are columns cl + 8q .. +3 of row 32b + li
         float* Rt = R[t & 1];
