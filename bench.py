@@ -684,10 +684,11 @@ def calibration_bench(args):
     value = n_mats / (ms_per_step / 1e3)
     log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step")
 
-    # Gram-sum roofline: algorithmic flops = sum over slots of n_e d (d+1), averaged per launch
+    # Gram-sum roofline: algorithmic flops = sum over the routed slots of n_e d (d+1), averaged
+    # per launch (the shared slot's sums are formed from the routed ones, not by the kernel)
     launched = [i % len(units) for i in range(args.steps)]
     counts = {u: [cals[u].counts[l].cpu().numpy() for l in cals[u].layer_ids] for u in set(launched)}
-    rows_per_launch = sum(float(c.sum()) for u in launched for c in counts[u]) / (2 * args.steps)
+    rows_per_launch = sum(float(c[:wl.n_routed].sum()) for u in launched for c in counts[u]) / (2 * args.steps)
     flops_per_launch = rows_per_launch * wl.d * (wl.d + 1)
     syrk_ms, syrk_calls = stages["syrk"]
     syrk_avg_ms = syrk_ms / max(syrk_calls, 1)

@@ -503,6 +503,9 @@ CLHA_API clha_status clha_collect_hessians(clha_ctx* ctx, int32_t layer, int64_t
   p.zero_row = L.zero_row;
   p.status = ctx->status_dev;
   p.layer = layer;
+  // the shared slot's sums are derived from the routed ones (every token goes
+  // to exactly top_k routed experts): no Gram-sum items for it
+  p.derive_shared = p.has_shared ? 1 : 0;
   const hipStream_t s = as_stream(stream);
   {
     StageTimer t(ctx, CLHA_STAGE_ROUTE, s);

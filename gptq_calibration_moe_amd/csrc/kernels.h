@@ -83,6 +83,9 @@ struct CollectPlan {
   uint16_t* zero_row;
   int* status;           // the context's status record
   int layer;             // the collected layer (named by a non-finite logit)
+  // the shared slot's sums follow from the routed slots' (S_E = sum_e S_e / K):
+  // it gets no Gram-sum items and is formed after the partial-sum reduce
+  int derive_shared = 0;
 };
 
 void launch_route(const float* logits, const CollectPlan& p, hipStream_t s);

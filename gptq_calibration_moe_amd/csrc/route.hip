@@ -154,6 +154,7 @@ __global__ __launch_bounds__(256) void bucket_count_kernel(const int32_t* __rest
 // panels again).  The parts of a slot after its first go to partial buffers,
 // added into S in part order afterwards; when the buffers run short the
 // segments grow.  Longest slots first, each segment onto the least-loaded XCD.
+// Slot `derived` (or none, -1) keeps its counts but gets no Gram-sum items.
 struct PlanLds {
   int64_t padc[kMaxSlots];
   int32_t order[kMaxSlots];
@@ -166,7 +167,7 @@ __device__ void plan_gram(const int64_t* cnt, PlanLds& L, int slots, int64_t* __
                           int32_t* __restrict__ slot_order, int64_t* __restrict__ layer_counts, int overwrite,
                           int items, int32_t* __restrict__ work, int32_t* __restrict__ work_len,
                           int32_t* __restrict__ work_next, int32_t* __restrict__ seg, int32_t* __restrict__ split,
-                          int max_partials) {
+                          int max_partials, int derived) {
   for (int e = threadIdx.x; e < slots; e += blockDim.x) {
     L.padc[e] = (cnt[e] + kTokPad - 1) / kTokPad * kTokPad;
     if (layer_counts) layer_counts[e] = overwrite ? cnt[e] : layer_counts[e] + cnt[e];
@@ -190,7 +191,7 @@ __device__ void plan_gram(const int64_t* cnt, PlanLds& L, int slots, int64_t* __
   __syncthreads();
   if (threadIdx.x == 0) {
     int64_t total = 0;
-    for (int e = 0; e < slots; ++e) total += L.padc[e];
+    for (int e = 0; e < slots; ++e) total += e == derived ? 0 : L.padc[e];
     // In 64-token chunks (32-bit counts: 64-bit division is a long instruction
     // sequence).  The slots, longest first, are laid end to end and cut into
     // kXcds runs of per_x chunks, one run per die, so every die gets the same
@@ -208,7 +209,7 @@ __device__ void plan_gram(const int64_t* cnt, PlanLds& L, int slots, int64_t* __
     int x = 0, xload = 0, nseg = 0, nsplit = 0, used = 0;
     for (int r = 0; r < slots; ++r) {
       const int e = L.order[r];
-      const int chunks = (int)(L.padc[e] / kTokPad);
+      const int chunks = e == derived ? 0 : (int)(L.padc[e] / kTokPad);
       if (chunks == 0) continue;
       const int first_part = used;
       int pos = 0, parts = 0;
@@ -270,7 +271,7 @@ __global__ __launch_bounds__(kScanThreads) void bucket_scan_kernel(
     int32_t* __restrict__ slot_order, int64_t* __restrict__ layer_counts, int overwrite, int items,
     int32_t* __restrict__ work, int32_t* __restrict__ work_len, int32_t* __restrict__ work_next,
     int32_t* __restrict__ seg, int32_t* __restrict__ split, int max_partials, uint16_t* __restrict__ zero_row,
-    int d) {
+    int d, int derived) {
   __shared__ int64_t cnt[kMaxSlots];
   __shared__ int64_t part[kScanThreads];
   __shared__ PlanLds L;
@@ -326,7 +327,7 @@ __global__ __launch_bounds__(kScanThreads) void bucket_scan_kernel(
     offsets[E] = o;
   }
   plan_gram(cnt, L, slots, pad_off, slot_order, layer_counts, overwrite, items, work, work_len, work_next, seg,
-            split, max_partials);
+            split, max_partials, derived);
 }
 
 // Plan of the down_proj inputs of one layer: slot e < E takes expert e's routed
@@ -344,7 +345,7 @@ __global__ __launch_bounds__(256) void down_scan_kernel(
     cnt[e] = e < E ? routed_offsets[e + 1] - routed_offsets[e] : n;
   __syncthreads();
   plan_gram(cnt, L, slots, pad_off, slot_order, layer_counts, overwrite, items, work, work_len, work_next, seg,
-            split, max_partials);
+            split, max_partials, -1);
   if (threadIdx.x == 0) {
     int32_t t = 0;
     for (int e = 0; e < slots; ++e) {
@@ -407,7 +408,7 @@ void launch_bucket(const CollectPlan& p, int64_t* layer_counts, hipStream_t s) {
   hipLaunchKernelGGL(bucket_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, p.blockcounts, p.nblk,
                      p.n_tokens, p.E, p.has_shared, p.blockbase, p.offsets, p.pad_off,
                      p.slot_order, layer_counts, p.overwrite, p.syrk_items, p.work, p.work_len, p.work_next,
-                     p.seg, p.split, p.max_partials, p.zero_row, p.d);
+                     p.seg, p.split, p.max_partials, p.zero_row, p.d, p.derive_shared ? p.E : -1);
   hipLaunchKernelGGL(bucket_scatter_kernel, dim3(p.nblk), dim3(256), 0, s, p.topk, p.n_tokens,
                      p.K, p.E, p.blockbase, p.offsets, p.token_ids);
 }

@@ -702,6 +702,49 @@ __global__ __launch_bounds__(256) void zero_empty_slots_kernel(const int64_t* __
     }
 }
 
+// The shared slot's sums from the routed slots' (CLHA summary, section 2.2:
+// a shared expert's Hessian is accumulated over every token).  Top-K routing
+// sends each token to exactly K distinct routed experts, so
+//   sum_e S_e = sum_e sum_{t -> e} x_t x_t^T = K sum_t x_t x_t^T = K S_shared:
+// S_E = (sum_e S_e) / K, summed in fp64 in slot order and rounded once, for
+// the lower triangle.  The routed sums are cumulative over a layer's batches,
+// so S_E is formed anew after each batch.  Workgroup (x, i): row i, columns
+// 1024x .. +1023, four per thread.
+__global__ __launch_bounds__(256) void shared_from_routed_kernel(float* __restrict__ S, int E, int K, int d) {
+  const int i = blockIdx.y, j = 4 * (blockIdx.x * 256 + threadIdx.x);
+  if (j > i || j >= d) return;
+  const int64_t dd = (int64_t)d * d, off = (int64_t)i * d + j;
+  double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
+  int e = 0;
+  // eight slots' loads in flight together; the sums stay in slot order
+  for (; e + 8 <= E; e += 8) {
+    float4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const float4*>(S + (int64_t)(e + u) * dd + off);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      a0 += (double)v[u].x;
+      a1 += (double)v[u].y;
+      a2 += (double)v[u].z;
+      a3 += (double)v[u].w;
+    }
+  }
+  for (; e < E; ++e) {
+    const float4 v = *reinterpret_cast<const float4*>(S + (int64_t)e * dd + off);
+    a0 += (double)v.x;
+    a1 += (double)v.y;
+    a2 += (double)v.z;
+    a3 += (double)v.w;
+  }
+  float* o = S + (int64_t)E * dd + off;
+  float4 r = make_float4((float)(a0 / K), (float)(a1 / K), (float)(a2 / K), (float)(a3 / K));
+  // columns above the diagonal keep their value (S's upper triangle is never written)
+  if (j + 1 > i) r.y = o[1];
+  if (j + 2 > i) r.z = o[2];
+  if (j + 3 > i) r.w = o[3];
+  *reinterpret_cast<float4*>(o) = r;
+}
+
 void launch_syrk(const CollectPlan& p, float* S, hipStream_t s) {
   GramIn in{p.xgT, p.pad_off, p.x_rows, p.token_ids, p.offsets, p.iota, p.zero_row, p.n_tokens, p.E};
   if (p.x_rows)
@@ -713,12 +756,16 @@ void launch_syrk(const CollectPlan& p, float* S, hipStream_t s) {
 }
 
 // After the Gram-sum kernel.  The slots zeroed here received no token, so no
-// Gram-sum item or partial buffer touches them.
+// Gram-sum item or partial buffer touches them; the derived shared slot comes
+// last, from the finished routed sums.
 void launch_syrk_reduce(const CollectPlan& p, float* S, const int64_t* layer_counts, hipStream_t s) {
   hipLaunchKernelGGL(syrk_reduce_kernel, dim3((p.d + 1023) / 1024, p.d, kReduceGroups), dim3(256), 0, s, p.split,
                      p.partials, S, p.d);
   if (p.overwrite)
     hipLaunchKernelGGL(zero_empty_slots_kernel, dim3(p.E + p.has_shared), dim3(256), 0, s, layer_counts, S,
+                       p.d);
+  if (p.derive_shared)
+    hipLaunchKernelGGL(shared_from_routed_kernel, dim3((p.d + 1023) / 1024, p.d), dim3(256), 0, s, S, p.E, p.K,
                        p.d);
 }
 

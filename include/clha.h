@@ -128,9 +128,11 @@ CLHA_API size_t clha_collect_workspace_bytes(const clha_ctx* ctx);
  *   1. routes each token to its top-K experts (larger logit first, ties to the lower index);
  *   2. buckets tokens per expert (counts, exclusive offsets, token lists ascending);
  *   3. S[e] += X_e^T X_e (fp32 accumulation of bf16 products) for every routed expert,
- *      and S[E] += X^T X over all tokens when the block has shared experts;
- *      counts[e] += n_e, counts[E] += n_tokens (stored instead of added by the first
- *      collection with tokens after clha_reset_layer).
+ *      and S[E] = X^T X over all of the layer's tokens so far when the block has shared
+ *      experts; counts[e] += n_e, counts[E] += n_tokens (stored instead of added by the
+ *      first collection with tokens after clha_reset_layer).  Each token goes to exactly
+ *      K distinct routed experts, so X^T X = (sum_e S[e]) / K: S[E] is formed that way
+ *      from the routed sums (fp64 sum in slot order, one rounding) after each batch.
  *   x        device, bf16 bits [n_tokens][d]
  *   logits   device, float [n_tokens][E]
  *   topk_out, offsets_out, token_ids_out: optional device outputs of this batch's
