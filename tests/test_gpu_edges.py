@@ -9,7 +9,10 @@
   GPTQ of a 32-row matrix on a well-conditioned Hessian;
 * a reset accumulator (stale sums left in S, counts zeroed) collects exactly
   what a zeroed one does, an unrouted slot included, and a layer reset but
-  never collected drops out of the aggregation.
+  never collected drops out of the aggregation;
+* the shared-expert slot, formed from the routed slots' sums, equals the
+  oracle's X^T X over a reset layer with stale sums, an expert no token
+  chooses and two batches, also when every token goes to every expert.
 """
 import numpy as np
 import pytest
@@ -180,3 +183,33 @@ def test_reset_layer_matches_a_zeroed_accumulator():
     ctx.aggregate([1], "rt", H1)
     ctx.sync()
     assert torch.equal(H2, H1)
+
+
+@pytest.mark.parametrize("top_k", [2, 8])
+def test_shared_slot_from_routed_sums_after_reset(top_k):
+    """S_shared = (sum_e S_e) / K: every token goes to exactly K routed experts.
+    Stale sums in S, an expert no token chooses (its slot zeroed before the
+    shared slot is formed) and a second batch added to the first."""
+    import gptq_calibration_moe_amd as clha
+    wl = gen.WORKLOADS[1].scaled(n_tokens=4096, n_shared=1, top_k=top_k)
+    inp = gen.pair_inputs(wl)
+    lg = inp["logits"][0].copy()
+    if top_k < wl.n_routed:
+        lg[:, 5] = -100.0                    # expert 5 is never among the top K
+    ctx = clha.Context(wl.d, wl.n_routed, wl.top_k, wl.n_shared, wl.n_tokens, device=dev())
+    S, n = ctx.new_layer_buffers()
+    S.fill_(3.0)                             # stale sums and counts of an earlier run
+    n.fill_(7)
+    ctx.register_layer(0, S, n)
+    ctx.reset_layer(0)
+    half = wl.n_tokens // 2
+    for lo, hi in ((0, half), (half, wl.n_tokens)):
+        ctx.collect_hessians(0, bits_to_dev(inp["x"][0][lo:hi]), to_dev(lg[lo:hi]))
+    ctx.sync()
+    E = wl.n_routed
+    counts = n.cpu().numpy()
+    assert int(counts[E]) == wl.n_tokens and int(counts[:E].sum()) == top_k * wl.n_tokens
+    if top_k < wl.n_routed:
+        assert int(counts[5]) == 0
+    ref = oracle.gram_rows(inp["x"][0], np.arange(wl.d))
+    assert hess_err(S[E].cpu().numpy(), ref) <= HESS_TOL
